@@ -1,0 +1,140 @@
+/*
+ * KVTC reference oracle -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, single-threaded C implementation of KVTC-style transform
+ * coding of transformer KV caches.  It exists to check the HIP library and
+ * nothing else: only the tests, the smoke entry point and the benchmark's
+ * CPU-baseline leg may load it.  It shares no code, header, table or
+ * constant generator with the HIP library under tensor_compression_amd/.
+ *
+ * Sources (cited by page title and section):
+ *  [KVTC]  "KVTC: The Open-Source KV Cache Codec That Treats LLM Memory Like
+ *          Media" (repo explainer of OnlyTerp/kvtc): sections "How the
+ *          Pipeline Works", "Why RoPE Has to Be Reversed First", "Bit Budget
+ *          Is Not Fair, and That Is the Point", "rANS Makes the Last Mile
+ *          Smaller", "The Tradeoff Is Real".
+ *  [CG]    "Codec-Gauge: Learning Compression-Friendly Gauges for Transformer
+ *          KV Caches": "Problem Statement and Overview" (cache notation, the
+ *          Z=GX / C / D / G^-1 frame), "Compression Conditions" (uncentered
+ *          second-moment PCA/KLT, Hadamard control, KIVI-style ranges),
+ *          "Evaluation Design" (NRMSE, measured bits/value, sanity rows).
+ *  [TTAS]  "TTAS-X2: Extreme KV Cache Compression for Large Language Models":
+ *          2.1 K Compression (4-bit scalar, per-head scale), 2.2 V Compression
+ *          (per-vector RMS normalisation, Hadamard transform), 4 Memory
+ *          Analysis.
+ *  [AT1]   "Compress the most expensive bytes in AI" (AT-1 Memory), "KV &
+ *          tensor mode": token-major to channel-major reordering.
+ *
+ * Where the pages leave a step open, the oracle follows one stated reading;
+ * every reading is listed in the design notes of the repository.
+ */
+#ifndef KVTC_ORACLE_H
+#define KVTC_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORC_FP32 = 0, ORC_BF16 = 1 };
+enum { ORC_PCA = 0, ORC_WHT = 1 };
+enum { ORC_ROPE_HALF = 0, ORC_ROPE_INTERLEAVED = 1 };
+
+enum {
+  ORC_OK = 0,
+  ORC_ERR_INVALID_ARG = 1,
+  ORC_ERR_UNSUPPORTED = 2,
+  ORC_ERR_CAPACITY = 3,
+  ORC_ERR_CORRUPT = 4,
+  ORC_ERR_NONFINITE = 5
+};
+
+typedef struct {
+  int32_t layers, kv_heads, head_dim;
+  int32_t dtype;          /* ORC_FP32 / ORC_BF16: cache dtype = operand precision */
+  int32_t transform;      /* ORC_PCA / ORC_WHT */
+  int32_t sink_tokens, recent_tokens;
+  float bits_k, bits_v;   /* average bits per component */
+  int32_t max_bits;       /* 1..8 */
+  int32_t rope_keys;      /* 1: keys carry RoPE and are un-rotated first */
+  int32_t rope_style;     /* ORC_ROPE_HALF / ORC_ROPE_INTERLEAVED */
+  double rope_theta;
+  int32_t rans_scale_bits;/* 8..15 */
+  int32_t rans_lanes;     /* 1..64 */
+  int32_t chunk_tokens;   /* tokens sharing one frequency table */
+  int32_t tile_tokens;    /* tokens per packed tile = one rANS stream */
+  int32_t basis_per_head; /* 0: basis [L,2,D,D]; 1: [L,2,H,D,D] */
+  int32_t wht_keys;       /* WHT path: 1 = keys get RMS+WHT too */
+} orc_config;
+
+/* ---- numeric primitives ---------------------------------------------- */
+uint16_t orc_f32_to_bf16(float f);
+float orc_bf16_to_f32(uint16_t h);
+void orc_rope_table(int32_t T, int32_t D, double theta, float* cos_out, float* sin_out);
+void orc_rope_inverse(const float* y, float* x, int32_t D, int32_t style,
+                      const float* cos_row, const float* sin_row);
+void orc_rope_forward(const float* x, float* y, int32_t D, int32_t style,
+                      const float* cos_row, const float* sin_row);
+void orc_project(const float* x, const float* Bp, int32_t D, float* c);
+void orc_unproject(const float* chat, const float* Bp, int32_t D, float* x);
+float orc_rms(const float* x, int32_t D);
+void orc_wht(const float* x, int32_t D, float* y);
+
+/* ---- statistics, allocation, quantiser ------------------------------- */
+void orc_stats(const float* c, int64_t N, int32_t D, float* mu, float* var,
+               float* cmin, float* cmax);
+int32_t orc_budget(float bits, int32_t D);
+void orc_alloc_greedy(const float* var, int32_t D, int32_t budget, int32_t max_bits,
+                      uint8_t* bits);
+double orc_alloc_dp(const float* var, int32_t D, int32_t budget, int32_t max_bits,
+                    uint8_t* bits);
+double orc_distortion(const float* var, const uint8_t* bits, int32_t D);
+void orc_side_info(const uint8_t* bits, const float* mu, const float* cmin,
+                   const float* cmax, int32_t D, float* zero, float* scale, float* rcp);
+void orc_quantize(const float* c, int64_t N, int32_t D, const uint8_t* bits,
+                  const float* zero, const float* rcp, uint8_t* q, float* vpre);
+void orc_quantize_sym(const float* c, int64_t N, int32_t D, int32_t b, float rcp,
+                      uint8_t* q, float* vpre);
+
+/* ---- packing and entropy coding -------------------------------------- */
+int64_t orc_packed_bytes(const uint8_t* bits, int32_t D, int64_t ntok);
+void orc_pack(const uint8_t* q, int64_t ntok, int32_t D, const uint8_t* bits, uint8_t* out);
+void orc_unpack(const uint8_t* in, int64_t ntok, int32_t D, const uint8_t* bits, uint8_t* q);
+void orc_freq_normalize(const uint32_t* counts, int32_t scale_bits, uint16_t* freq);
+int64_t orc_rans_encode(const uint8_t* sym, int64_t N, const uint16_t* freq,
+                        int32_t scale_bits, int32_t lanes, uint32_t* states,
+                        uint16_t* words, int64_t words_cap);
+int orc_rans_decode(const uint32_t* states, const uint16_t* words, int64_t nwords,
+                    const uint16_t* freq, int32_t scale_bits, int32_t lanes,
+                    int64_t N, uint8_t* sym);
+
+/* ---- container ------------------------------------------------------- */
+int orc_check_config(const orc_config* cfg);
+uint64_t orc_fingerprint(const orc_config* cfg, const float* basis);
+int64_t orc_max_container_bytes(const orc_config* cfg, int32_t T);
+int orc_encode(const orc_config* cfg, const void* k, const void* v, int32_t T,
+               const float* basis, uint8_t* out, int64_t cap, int64_t* out_bytes);
+int orc_decode(const orc_config* cfg, const float* basis, const uint8_t* in,
+               int64_t in_bytes, void* k_out, void* v_out, int32_t out_dtype);
+/* Decode only sections [sec_begin, sec_end) of a container: the middle rows
+ * of each, after forward RoPE on keys and before the output cast, as
+ * [nsec, T_mid, D] fp32 (sampled cross-decode at full size). */
+int orc_decode_sections(const orc_config* cfg, const float* basis, const uint8_t* in,
+                        int64_t in_bytes, int32_t sec_begin, int32_t sec_end,
+                        float* mid_out);
+/* Rows t0..t1 of section u as the encoder sees them: keys un-rotated, all rows
+ * rounded to the operand precision.  x_out [t1-t0, D] fp32.  Used for basis
+ * calibration (the basis is an input of the method, fitted offline). */
+int orc_section_rows(const orc_config* cfg, const void* k, const void* v, int32_t T,
+                     int32_t section, int32_t t0, int32_t t1, float* x_out);
+/* Coefficients of one section's middle rows, as the encoder computes them.
+ * c_out [T_mid, D] fp32; r_out [T_mid] (WHT path, may be NULL). */
+int orc_section_coeffs(const orc_config* cfg, const void* k, const void* v, int32_t T,
+                       const float* basis, int32_t section, float* c_out, float* r_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
