@@ -109,6 +109,7 @@ def lib() -> ctypes.CDLL:
             "orc_decode": (ctypes.c_int, [P, P, P, i64, P, P, i32]),
             "orc_decode_sections": (ctypes.c_int, [P, P, P, i64, i32, i32, P]),
             "orc_section_rows": (ctypes.c_int, [P, P, P, i32, i32, i32, i32, P]),
+            "orc_section_codes": (ctypes.c_int, [P, P, P, i64, i32, P]),
             "orc_section_coeffs": (ctypes.c_int, [P, P, P, i32, P, i32, P, P]),
         }
         for name, (res, args) in sig.items():
@@ -441,6 +442,19 @@ def decode_sections(cfg: dict, data: bytes, basis, sec_begin: int, sec_end: int,
     if st != OK:
         raise OracleError(st, "decode_sections")
     return out[:, :T_mid]
+
+
+def section_codes(cfg: dict, data: bytes, basis, section: int, T: int) -> np.ndarray:
+    """Codes [T_mid, D] of one section, read back from a container."""
+    c = make_cfg(cfg)
+    lo = layout(cfg, T)
+    q = np.zeros((max(lo.T_mid, 1), cfg["head_dim"]), np.uint8)
+    buf = np.frombuffer(data, np.uint8).copy()
+    b = None if basis is None else np.ascontiguousarray(basis, np.float32)
+    st = lib().orc_section_codes(ctypes.byref(c), _p(b), _p(buf), buf.size, section, _p(q))
+    if st != OK:
+        raise OracleError(st, "section_codes")
+    return q[: lo.T_mid]
 
 
 def section_rows(cfg: dict, k, v, section: int, t0: int, t1: int) -> np.ndarray:

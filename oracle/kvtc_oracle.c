@@ -1269,3 +1269,28 @@ int orc_decode_sections(const orc_config* c, const float* basis, const uint8_t* 
   free(sin_t);
   return st;
 }
+
+int orc_section_codes(const orc_config* c, const float* basis, const uint8_t* in, int64_t n,
+                      int32_t u, uint8_t* q_out) {
+  int st = orc_check_config(c);
+  if (st != ORC_OK) return st;
+  layout_t lo;
+  st = parse_header(c, basis, in, n, &lo);
+  if (st != ORC_OK) return st;
+  if (u < 0 || u >= lo.n_sections) return ORC_ERR_INVALID_ARG;
+  int32_t D = c->head_dim;
+  int64_t total = (int64_t)get64(in + 168);
+  const uint8_t* rec = in + lo.side_off + (int64_t)u * SEC_REC(D);
+  uint8_t bits[256];
+  memcpy(bits, rec, (size_t)D);
+  for (int32_t i = 0; i < D; ++i)
+    if (bits[i] > c->max_bits) return ORC_ERR_CORRUPT;
+  uint8_t* packed = (uint8_t*)malloc((size_t)c->chunk_tokens * D + 64 * (size_t)D + 1);
+  uint8_t* syms = (uint8_t*)malloc((size_t)c->tile_tokens * D + 64 * (size_t)D + 1);
+  for (int32_t ch = 0; ch < lo.chunks_per_sec && st == ORC_OK; ++ch)
+    st = decode_chunk_codes(c, &lo, in, total, u, ch, bits,
+                            q_out + (int64_t)ch * c->chunk_tokens * D, packed, syms);
+  free(packed);
+  free(syms);
+  return st;
+}

@@ -124,6 +124,10 @@ int orc_decode(const orc_config* cfg, const float* basis, const uint8_t* in,
 int orc_decode_sections(const orc_config* cfg, const float* basis, const uint8_t* in,
                         int64_t in_bytes, int32_t sec_begin, int32_t sec_end,
                         float* mid_out);
+/* Quantisation codes of section u read back from a container (rANS decode
+ * and unpacking only): q_out [T_mid, D]. */
+int orc_section_codes(const orc_config* cfg, const float* basis, const uint8_t* in,
+                      int64_t in_bytes, int32_t section, uint8_t* q_out);
 /* Rows t0..t1 of section u as the encoder sees them: keys un-rotated, all rows
  * rounded to the operand precision.  x_out [t1-t0, D] fp32.  Used for basis
  * calibration (the basis is an input of the method, fitted offline). */

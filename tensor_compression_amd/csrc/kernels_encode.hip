@@ -1,0 +1,1049 @@
+// Encode-side kernels: raw windows, the RoPE-undo + MFMA projection with
+// per-component statistics, greedy bit allocation with side information,
+// and the fused quantise-and-pack pass.
+//
+// Projection layout (gfx950 v_mfma_f32_16x16x32_bf16, wave64): a wave
+// projects 16 tokens at a time.  Lane l = 16 g + r holds token r of the
+// block; its K-slice is the channel run [g D/8, (g+1) D/8) of the first
+// half and the matching run of the second half, so both members of every
+// half-split RoPE pair (j, j + D/2) sit in the same lane.  The basis of the
+// section is register-resident as B operands (component nb*16 + r, same
+// channel permutation).  The result lane l holds the coefficients of
+// component nb*16 + r for tokens 4g .. 4g+3 of the block: four consecutive
+// codes of one component, which is what channel-major packing wants.
+#include <string.h>
+
+#include <type_traits>
+
+#include "kvtc_internal.h"
+
+namespace kvtc {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct Geo {
+  static constexpr int HALF = D / 2;
+  static constexpr int PER = D / 8;  // channels per lane per half
+  static constexpr int NB = D / 16;  // 16-component output blocks
+  static constexpr int NKB = D / 32; // bf16 K blocks of 8 channels per lane
+};
+
+// channel of the e-th element of K-run position k (0 <= k < D/4) of lane group g
+template <int D>
+__device__ __forceinline__ int lane_channel(int g, int k) {
+  constexpr int PER = Geo<D>::PER;
+  return k < PER ? g * PER + k : Geo<D>::HALF + g * PER + (k - PER);
+}
+
+__device__ __forceinline__ void unpack_bf16x8(uint4 a, float* o) {
+  o[0] = __uint_as_float(a.x << 16); o[1] = __uint_as_float(a.x & 0xffff0000u);
+  o[2] = __uint_as_float(a.y << 16); o[3] = __uint_as_float(a.y & 0xffff0000u);
+  o[4] = __uint_as_float(a.z << 16); o[5] = __uint_as_float(a.z & 0xffff0000u);
+  o[6] = __uint_as_float(a.w << 16); o[7] = __uint_as_float(a.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// Load the lane's channel runs of one cache row (lo: first half, hi: second).
+template <int D, int DT>
+__device__ __forceinline__ void load_runs(const void* src, int64_t row, int g, bool valid,
+                                          float* lo, float* hi) {
+  constexpr int PER = Geo<D>::PER, HALF = Geo<D>::HALF;
+  if (DT == KVTC_BF16) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(src) + row;
+#pragma unroll
+    for (int q = 0; q < PER / 8; ++q) {
+      uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+      if (valid) {
+        a = *reinterpret_cast<const uint4*>(p + g * PER + q * 8);
+        b = *reinterpret_cast<const uint4*>(p + HALF + g * PER + q * 8);
+      }
+      unpack_bf16x8(a, lo + q * 8);
+      unpack_bf16x8(b, hi + q * 8);
+    }
+  } else {
+    const float* p = reinterpret_cast<const float*>(src) + row;
+#pragma unroll
+    for (int q = 0; q < PER / 4; ++q) {
+      float4 a = make_float4(0, 0, 0, 0), b = make_float4(0, 0, 0, 0);
+      if (valid) {
+        a = *reinterpret_cast<const float4*>(p + g * PER + q * 4);
+        b = *reinterpret_cast<const float4*>(p + HALF + g * PER + q * 4);
+      }
+      lo[q * 4 + 0] = a.x; lo[q * 4 + 1] = a.y; lo[q * 4 + 2] = a.z; lo[q * 4 + 3] = a.w;
+      hi[q * 4 + 0] = b.x; hi[q * 4 + 1] = b.y; hi[q * 4 + 2] = b.z; hi[q * 4 + 3] = b.w;
+    }
+  }
+}
+
+// Undo RoPE in place ("Why RoPE Has to Be Reversed First"):
+//   x_a = fma(y_a, c, y_b s),  x_b = fma(y_b, c, -(y_a s)).
+template <int D>
+__device__ __forceinline__ void rope_inverse_runs(const float2* rope_row, int g, int style,
+                                                  float* lo, float* hi) {
+  constexpr int PER = Geo<D>::PER, HALF = Geo<D>::HALF;
+  if (style == KVTC_ROPE_HALF) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      float2 cs = rope_row[g * PER + e];
+      float ya = lo[e], yb = hi[e];
+      float yb_s = __fmul_rn(yb, cs.y), ya_s = __fmul_rn(ya, cs.y);
+      lo[e] = __fmaf_rn(ya, cs.x, yb_s);
+      hi[e] = __fmaf_rn(yb, cs.x, -ya_s);
+    }
+  } else {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      float* v = half ? hi : lo;
+      int base = (half ? HALF : 0) + g * PER;
+#pragma unroll
+      for (int m = 0; m < PER / 2; ++m) {
+        float2 cs = rope_row[(base >> 1) + m];
+        float ya = v[2 * m], yb = v[2 * m + 1];
+        float yb_s = __fmul_rn(yb, cs.y), ya_s = __fmul_rn(ya, cs.y);
+        v[2 * m] = __fmaf_rn(ya, cs.x, yb_s);
+        v[2 * m + 1] = __fmaf_rn(yb, cs.x, -ya_s);
+      }
+    }
+  }
+}
+
+// Register-resident basis operands of one section.
+template <int D, int DT>
+struct BasisRegs;
+
+template <int D>
+struct BasisRegs<D, KVTC_BF16> {
+  uint4 b[Geo<D>::NB][Geo<D>::NKB];
+  __device__ __forceinline__ void load(const uint16_t* bt, int g, int r) {
+    constexpr int PER = Geo<D>::PER, HALF = Geo<D>::HALF, NKB = Geo<D>::NKB;
+#pragma unroll
+    for (int nb = 0; nb < Geo<D>::NB; ++nb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        int ch = kb < NKB / 2 ? g * PER + kb * 8 : HALF + g * PER + (kb - NKB / 2) * 8;
+        b[nb][kb] = *reinterpret_cast<const uint4*>(bt + (int64_t)(nb * 16 + r) * D + ch);
+      }
+  }
+};
+
+template <int D>
+struct BasisRegs<D, KVTC_FP32> {
+  float b[Geo<D>::NB][D / 4];
+  __device__ __forceinline__ void load(const float* bt, int g, int r) {
+#pragma unroll
+    for (int nb = 0; nb < Geo<D>::NB; ++nb)
+#pragma unroll
+      for (int k = 0; k < D / 4; ++k) b[nb][k] = bt[(int64_t)(nb * 16 + r) * D + lane_channel<D>(g, k)];
+  }
+};
+
+// c[token 4g+e][component nb*16+r] = acc[nb][e]
+template <int D, int DT>
+__device__ __forceinline__ void project_block(const BasisRegs<D, DT>& B, const float* lo,
+                                              const float* hi, f32x4_t* acc) {
+  constexpr int NB = Geo<D>::NB;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if constexpr (DT == KVTC_BF16) {
+    constexpr int NKB = Geo<D>::NKB, PER = Geo<D>::PER;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const float* src = kb < NKB / 2 ? lo + kb * 8 : hi + (kb - NKB / 2) * 8;
+      uint4 a;
+      a.x = pack2_bf16(src[0], src[1]); a.y = pack2_bf16(src[2], src[3]);
+      a.z = pack2_bf16(src[4], src[5]); a.w = pack2_bf16(src[6], src[7]);
+      bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, B.b[nb][kb]),
+                                                          acc[nb], 0, 0, 0);
+    }
+    (void)PER;
+  } else {
+    constexpr int PER = Geo<D>::PER;
+#pragma unroll
+    for (int k = 0; k < D / 4; ++k) {
+      float av = k < PER ? lo[k] : hi[k - PER];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, B.b[nb][k], acc[nb], 0, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ int64_t basis_index(const Params& p, int l, int s, int h) {
+  return p.basis_per_head ? ((int64_t)(l * 2 + s) * p.H + h) : (int64_t)(l * 2 + s);
+}
+
+// exclusive prefix sum over the lanes of one wave
+__device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) {
+  const int lane = threadIdx.x & 63;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  *total = __shfl(x, 63, 64);
+  return x - v;
+}
+
+// ---------------------------------------------------------------------------
+// raw windows: [sink K][recent K][sink V][recent V], each [L,H,n,D], copied
+// bit-exactly ("How the Pipeline Works": they stay in high fidelity)
+// ---------------------------------------------------------------------------
+
+__global__ void k_clear_status(uint8_t* ws, WsLayout w) {
+  if (threadIdx.x == 0) {
+    uint32_t* s = reinterpret_cast<uint32_t*>(ws + w.status);
+    s[0] = 0; s[1] = 0; s[2] = 0; s[3] = 0;
+  }
+}
+
+// to_container = 1: cache -> container (+ zero the side and raw padding);
+// 0: container -> output tensors in out_dtype.
+__global__ void k_copy_raw(const Params p, int to_container) {
+  const int64_t e = p.dtype == KVTC_BF16 ? 2 : 4;
+  const int64_t row_bytes = (int64_t)p.D * e;
+  const int64_t per_tensor_rows = (int64_t)p.L * p.H * (p.s0 + p.W_eff);
+  const int64_t total_rows = 2 * per_tensor_rows;
+  const int64_t words_per_row = row_bytes / 4;
+  const int64_t n = total_rows * words_per_row;
+  if (!to_container && (get_status(p.ws, p.w) & (1u << KVTC_ERR_CORRUPT))) return;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    int64_t row = idx / words_per_row, wi = idx % words_per_row;
+    int s = row >= per_tensor_rows;
+    int64_t rr = row - s * per_tensor_rows;
+    int64_t per_lh = p.s0 + p.W_eff;
+    int64_t lh = rr / per_lh, tt = rr % per_lh;
+    int64_t pos = tt < p.s0 ? tt : p.mid_end + (tt - p.s0);
+    // container order: region-major within each tensor
+    int64_t region = tt < p.s0 ? 0 : 1;
+    int64_t n_region = region == 0 ? p.s0 : p.W_eff;
+    int64_t off_region = region == 0 ? 0 : (int64_t)p.L * p.H * p.s0;
+    int64_t crow = (int64_t)s * per_tensor_rows + off_region + lh * n_region + (region == 0 ? tt : tt - p.s0);
+    int64_t tensor_elem = (lh * p.T + pos) * p.D;
+    if (to_container) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(s ? p.v : p.k);
+      reinterpret_cast<uint32_t*>(p.out + p.raw_off)[crow * words_per_row + wi] =
+          src[tensor_elem * e / 4 + wi];
+    } else {
+      const uint32_t word = reinterpret_cast<const uint32_t*>(p.in + p.raw_off)[crow * words_per_row + wi];
+      void* dst = s ? p.v_out : p.k_out;
+      if (p.out_dtype == p.dtype) {
+        reinterpret_cast<uint32_t*>(dst)[tensor_elem * e / 4 + wi] = word;
+      } else if (p.dtype == KVTC_BF16) {  // bf16 -> fp32: exact widening
+        float* d = reinterpret_cast<float*>(dst) + tensor_elem + 2 * wi;
+        d[0] = __uint_as_float(word << 16);
+        d[1] = __uint_as_float(word & 0xffff0000u);
+      } else {  // fp32 -> bf16 (RNE)
+        uint16_t* d = reinterpret_cast<uint16_t*>(dst) + tensor_elem + wi;
+        d[0] = f32_to_bf16(__uint_as_float(word));
+      }
+    }
+  }
+  if (to_container) {
+    // zero padding: [end of side records and r area, raw_off) and raw tail
+    int64_t side_used = p.r_off - p.side_off;  // section records
+    int64_t r_used = 0;
+    if (p.transform == KVTC_WHT) r_used = (int64_t)(p.wht_keys ? 2 : 1) * p.L * p.H * p.T_mid * 4;
+    int64_t a0 = p.side_off + side_used + r_used, a1 = p.raw_off;
+    int64_t b0 = p.raw_off + total_rows * row_bytes, b1 = p.raw_off + p.raw_bytes;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (a1 - a0) + (b1 - b0);
+         i += (int64_t)gridDim.x * blockDim.x) {
+      int64_t at = i < (a1 - a0) ? a0 + i : b0 + (i - (a1 - a0));
+      p.out[at] = 0;
+    }
+  }
+}
+
+hipError_t launch_copy_raw(const Params& p, int to_container, hipStream_t s) {
+  if (to_container) {
+    hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(64), 0, s, p.ws, p.w);
+  }
+  int64_t e = p.dtype == KVTC_BF16 ? 2 : 4;
+  int64_t words = 2 * (int64_t)p.L * p.H * (p.s0 + p.W_eff) * p.D * e / 4 + 64;
+  int64_t blocks = (words + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_copy_raw, dim3((unsigned)blocks), dim3(256), 0, s, p, to_container);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// projection passes over the middle region of every section
+//   mode 0: statistics per (section, chunk, component)
+//   mode 1: quantise and pack into channel-major tiles
+//   mode 2: write the coefficients (parity hook)
+// ---------------------------------------------------------------------------
+
+struct SideLds {
+  float zero[128];
+  float rcp[128];
+  uint32_t bits[128];
+  uint32_t row_w[129];  // word offset of each component's row in the current tile
+};
+
+template <int D, int DT, int MODE>
+__global__ __launch_bounds__(256) void k_enc_pca(const Params p, int sec0, float* coef_out) {
+  constexpr int NB = Geo<D>::NB, PER = Geo<D>::PER;
+  const int u = blockIdx.y + sec0, ch = blockIdx.x;
+  const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
+  const int t0 = ch * p.chunk_tokens;
+  const int n = min(p.chunk_tokens, p.T_mid - t0);
+  if (n <= 0) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
+  const void* src = s ? p.v : p.k;
+  const bool rope = (s == 0) && p.rope_keys;
+  const int64_t lh_row0 = ((int64_t)l * p.H + h) * p.T;
+
+  BasisRegs<D, DT> B;
+  {
+    const int64_t bi = basis_index(p, l, s, h) * D * D;
+    if constexpr (DT == KVTC_BF16)
+      B.load(reinterpret_cast<const uint16_t*>(p.basis_t) + bi, g, r);
+    else
+      B.load(reinterpret_cast<const float*>(p.basis_t) + bi, g, r);
+  }
+
+  float lo[PER], hi[PER];
+  f32x4_t acc[NB];
+
+  if constexpr (MODE == 0) {
+    double sum[NB], sq[NB];
+    float mn[NB], mx[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) { sum[nb] = 0.0; sq[nb] = 0.0; mn[nb] = INFINITY; mx[nb] = -INFINITY; }
+    for (int blk = wave; blk * 16 < n; blk += 4) {
+      const int tok = blk * 16 + r;
+      const bool valid = tok < n;
+      const int pos = p.mid_begin + t0 + tok;
+      load_runs<D, DT>(src, (lh_row0 + pos) * D, g, valid, lo, hi);
+      if (rope && valid) {
+        rope_inverse_runs<D>(p.rope + (int64_t)pos * Geo<D>::HALF, g, p.rope_style, lo, hi);
+        if (DT == KVTC_BF16) {
+#pragma unroll
+          for (int e2 = 0; e2 < PER; ++e2) { lo[e2] = round_bf16(lo[e2]); hi[e2] = round_bf16(hi[e2]); }
+        }
+      }
+      project_block<D, DT>(B, lo, hi, acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (blk * 16 + 4 * g + e < n) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            float c = acc[nb][e];
+            sum[nb] += (double)c;
+            sq[nb] = __fma_rn((double)c, (double)c, sq[nb]);
+            mn[nb] = fminf(mn[nb], c);
+            mx[nb] = fmaxf(mx[nb], c);
+          }
+        }
+      }
+    }
+    // combine the four lane groups, then the four waves, in a fixed order
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        sum[nb] += __shfl_xor(sum[nb], o, 64);
+        sq[nb] += __shfl_xor(sq[nb], o, 64);
+        mn[nb] = fminf(mn[nb], __shfl_xor(mn[nb], o, 64));
+        mx[nb] = fmaxf(mx[nb], __shfl_xor(mx[nb], o, 64));
+      }
+    }
+    __shared__ double s_sum[4][D], s_sq[4][D];
+    __shared__ float s_mn[4][D], s_mx[4][D];
+    if (g == 0) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        int i = nb * 16 + r;
+        s_sum[wave][i] = sum[nb]; s_sq[wave][i] = sq[nb]; s_mn[wave][i] = mn[nb]; s_mx[wave][i] = mx[nb];
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < D) {
+      int i = threadIdx.x;
+      double a = s_sum[0][i], b = s_sq[0][i];
+      float c = s_mn[0][i], d = s_mx[0][i];
+      for (int w2 = 1; w2 < 4; ++w2) {
+        a += s_sum[w2][i]; b += s_sq[w2][i];
+        c = fminf(c, s_mn[w2][i]); d = fmaxf(d, s_mx[w2][i]);
+      }
+      int64_t idx = ((int64_t)u * p.chunks_per_sec + ch) * D + i;
+      reinterpret_cast<double*>(p.ws + p.w.part_sum)[idx] = a;
+      reinterpret_cast<double*>(p.ws + p.w.part_sq)[idx] = b;
+      reinterpret_cast<float*>(p.ws + p.w.part_min)[idx] = c;
+      reinterpret_cast<float*>(p.ws + p.w.part_max)[idx] = d;
+    }
+  } else if constexpr (MODE == 1) {
+    if (get_status(p.ws, p.w) & (1u << KVTC_ERR_NONFINITE)) return;
+    __shared__ SideLds sd;
+    // dynamic LDS: [basis copy D x D][staged rows 4 x 16 x D][tile buffer]
+    using otype = typename std::conditional<DT == KVTC_BF16, uint16_t, float>::type;
+    extern __shared__ uint32_t dynlds[];
+    otype* bt_lds = reinterpret_cast<otype*>(dynlds);
+    otype* xs = bt_lds + D * D;
+    uint32_t* tilebuf = reinterpret_cast<uint32_t*>(xs + 4 * 16 * D);
+    {
+      const otype* bsrc = reinterpret_cast<const otype*>(p.basis_t) + basis_index(p, l, s, h) * D * D;
+      const int n4 = D * D * (int)sizeof(otype) / 16;
+      for (int i = threadIdx.x; i < n4; i += blockDim.x)
+        reinterpret_cast<uint4*>(bt_lds)[i] = reinterpret_cast<const uint4*>(bsrc)[i];
+    }
+    if (threadIdx.x < D) {
+      int i = threadIdx.x;
+      int64_t si = (int64_t)u * D + i;
+      sd.zero[i] = reinterpret_cast<const float*>(p.ws + p.w.side_zero)[si];
+      sd.rcp[i] = reinterpret_cast<const float*>(p.ws + p.w.side_rcp)[si];
+      sd.bits[i] = p.ws[p.w.side_bits + si];
+    }
+    __syncthreads();
+    // per-lane side information of the components this lane produces
+    float zr[NB], rc[NB], qmax[NB];
+    uint32_t bl[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      int i = nb * 16 + r;
+      zr[nb] = sd.zero[i]; rc[nb] = sd.rcp[i]; bl[nb] = sd.bits[i];
+      qmax[nb] = (float)((1u << bl[nb]) - 1u);
+    }
+    // bytes of a full tile (all but possibly the last tile of the section)
+    uint32_t full_words;
+    {
+      uint32_t v0 = 0;
+      if (threadIdx.x < 64) {
+        for (int i = lane; i < D; i += 64) v0 += (uint32_t)((p.tile_tokens * (int)sd.bits[i] + 31) >> 5);
+      }
+      __shared__ uint32_t s_full;
+      if (threadIdx.x < 64) {
+        uint32_t tot;
+        wave_excl_scan(v0, &tot);
+        if (lane == 0) s_full = tot;
+      }
+      __syncthreads();
+      full_words = s_full;
+    }
+    uint32_t* slot = reinterpret_cast<uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot);
+    const int ntiles = (n + p.tile_tokens - 1) / p.tile_tokens;
+    for (int tl = 0; tl < ntiles; ++tl) {
+      const int ta = tl * p.tile_tokens;
+      const int nt = min(p.tile_tokens, n - ta);
+      // row offsets of this tile
+      if (threadIdx.x < 64) {
+        uint32_t w0 = 0, w1 = 0;
+        int i0 = 2 * lane, i1 = 2 * lane + 1;
+        if (i0 < D) w0 = (uint32_t)((nt * (int)sd.bits[i0] + 31) >> 5);
+        if (i1 < D) w1 = (uint32_t)((nt * (int)sd.bits[i1] + 31) >> 5);
+        uint32_t tot;
+        uint32_t ex = wave_excl_scan(w0 + w1, &tot);
+        if (i0 < D) sd.row_w[i0] = ex;
+        if (i1 < D) sd.row_w[i1] = ex + w0;
+        if (lane == 0) sd.row_w[D] = tot;
+      }
+      __syncthreads();
+      const uint32_t tw = sd.row_w[D];
+      for (uint32_t i = threadIdx.x; i < tw; i += blockDim.x) tilebuf[i] = 0;
+      __syncthreads();
+      const int nblk = (nt + 15) / 16;
+      for (int blk = wave; blk < nblk; blk += 4) {
+        const int tok = ta + blk * 16 + r;
+        const bool valid = blk * 16 + r < nt;
+        const int pos = p.mid_begin + t0 + tok;
+        load_runs<D, DT>(src, (lh_row0 + pos) * D, g, valid, lo, hi);
+        if (rope && valid) {
+          rope_inverse_runs<D>(p.rope + (int64_t)pos * Geo<D>::HALF, g, p.rope_style, lo, hi);
+          if (DT == KVTC_BF16) {
+#pragma unroll
+            for (int e2 = 0; e2 < PER; ++e2) { lo[e2] = round_bf16(lo[e2]); hi[e2] = round_bf16(hi[e2]); }
+          }
+        }
+        project_block<D, DT>(B, lo, hi, acc);
+        const int tt = blk * 16 + 4 * g;  // first token of this lane's four within the tile
+        // stage this lane's channels of token r (operand precision) for the
+        // exact recomputation below
+        {
+          otype* xr = xs + (wave * 16 + r) * D;
+#pragma unroll
+          for (int e2 = 0; e2 < PER; ++e2) {
+            if constexpr (DT == KVTC_BF16) {
+              xr[g * PER + e2] = f32_to_bf16(lo[e2]);
+              xr[Geo<D>::HALF + g * PER + e2] = f32_to_bf16(hi[e2]);
+            } else {
+              xr[g * PER + e2] = lo[e2];
+              xr[Geo<D>::HALF + g * PER + e2] = hi[e2];
+            }
+          }
+        }
+        // |c_mfma - c_exact| <= mfma_err * ||x||_2 (fp32 accumulation of the D
+        // exact products; Cauchy-Schwarz with unit-norm basis columns scaled
+        // by the plan's largest column norm)
+        float n2 = 0.f;
+#pragma unroll
+        for (int e2 = 0; e2 < PER; ++e2) n2 = __fmaf_rn(lo[e2], lo[e2], __fmaf_rn(hi[e2], hi[e2], n2));
+        n2 += __shfl_xor(n2, 16, 64);
+        n2 += __shfl_xor(n2, 32, 64);
+        float ecm[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ecm[e] = p.mfma_err * __fsqrt_rn(__shfl(n2, 4 * g + e, 64));
+        uint32_t qv[NB];
+        uint32_t flags = 0;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          qv[nb] = 0;
+          const uint32_t b = bl[nb];
+          if (b == 0) continue;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // v = (c - zero) * rcp, rounded half to even, clamped to [0, 2^b - 1]
+            const float v = __fmul_rn(__fsub_rn(acc[nb][e], zr[nb]), rc[nb]);
+            const float rv = __builtin_rintf(v);
+            const float q = fminf(fmaxf(rv, 0.0f), qmax[nb]);
+            if (tt + e < nt) {
+              qv[nb] |= (uint32_t)q << (8 * e);
+              // within the error of v of a rounding boundary: recompute exactly
+              const float ev = __fmaf_rn(ecm[e], rc[nb], 3.0f * 0x1p-23f * fmaxf(fabsf(v), 1.0f));
+              if (fabsf(fabsf(__fsub_rn(v, rv)) - 0.5f) < ev) flags |= 1u << (nb * 4 + e);
+            }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+        uint64_t pend = __ballot(flags != 0);
+        while (pend) {
+          const int L = __ffsll((unsigned long long)pend) - 1;
+          const uint32_t fl = __shfl(flags, L, 64);
+          const int bit = __ffs(fl) - 1;
+          const int nbx = bit >> 2, ex = bit & 3;
+          const int tx = 4 * (L >> 4) + ex;   // token within the block
+          const int ix = nbx * 16 + (L & 15); // component
+          // exact products summed in fp64 over the wave in a fixed order
+          const otype* xrow = xs + (wave * 16 + tx) * D;
+          const otype* brow = bt_lds + ix * D;
+          double part = 0.0;
+#pragma unroll
+          for (int c2 = lane; c2 < D; c2 += 64) {
+            float xv, bv;
+            if constexpr (DT == KVTC_BF16) { xv = bf16_to_f32(xrow[c2]); bv = bf16_to_f32(brow[c2]); }
+            else { xv = xrow[c2]; bv = brow[c2]; }
+            part = __fma_rn((double)xv, (double)bv, part);
+          }
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+          if (lane == L) {
+            const float cex = (float)part;
+            const float v = __fmul_rn(__fsub_rn(cex, sd.zero[ix]), sd.rcp[ix]);
+            const float q = fminf(fmaxf(__builtin_rintf(v), 0.0f), (float)((1u << sd.bits[ix]) - 1u));
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              if (nb == nbx) qv[nb] = (qv[nb] & ~(0xffu << (8 * ex))) | ((uint32_t)q << (8 * ex));
+            flags &= ~(1u << bit);
+          }
+          pend = __ballot(flags != 0);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const uint32_t b = bl[nb];
+          if (b == 0 || tt >= nt) continue;
+          const uint32_t word = (qv[nb] & 0xffu) | (((qv[nb] >> 8) & 0xffu) << b) |
+                                (((qv[nb] >> 16) & 0xffu) << (2 * b)) | ((qv[nb] >> 24) << (3 * b));
+          const uint32_t bitpos = (uint32_t)tt * b;
+          const uint32_t wi = sd.row_w[nb * 16 + r] + (bitpos >> 5), sh = bitpos & 31;
+          atomicOr(&tilebuf[wi], word << sh);
+          // bits past the 32-bit boundary; codes of tokens past the tile end are
+          // zero, so a nonzero spill always lands inside this row
+          const uint32_t spill = sh + 4 * b > 32 ? word >> (32 - sh) : 0u;
+          if (spill) atomicOr(&tilebuf[wi + 1], spill);
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+      __syncthreads();
+      uint32_t* dst = slot + (int64_t)tl * full_words;
+      for (uint32_t i = threadIdx.x; i < tw; i += blockDim.x) dst[i] = tilebuf[i];
+      __syncthreads();
+    }
+  } else {
+    // mode 2: coefficients [section - sec0][T_mid][D]
+    for (int blk = wave; blk * 16 < n; blk += 4) {
+      const int tok = blk * 16 + r;
+      const bool valid = tok < n;
+      const int pos = p.mid_begin + t0 + tok;
+      load_runs<D, DT>(src, (lh_row0 + pos) * D, g, valid, lo, hi);
+      if (rope && valid) {
+        rope_inverse_runs<D>(p.rope + (int64_t)pos * Geo<D>::HALF, g, p.rope_style, lo, hi);
+        if (DT == KVTC_BF16) {
+#pragma unroll
+          for (int e2 = 0; e2 < PER; ++e2) { lo[e2] = round_bf16(lo[e2]); hi[e2] = round_bf16(hi[e2]); }
+        }
+      }
+      project_block<D, DT>(B, lo, hi, acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        int tk = blk * 16 + 4 * g + e;
+        if (tk < n) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            coef_out[((int64_t)(u - sec0) * p.T_mid + t0 + tk) * D + nb * 16 + r] = acc[nb][e];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// WHT path: per-token RMS normalisation and the orthonormal Walsh-Hadamard
+// transform in Sylvester order (TTAS-X2 2.2; the Hadamard control of
+// Codec-Gauge).  16 lanes per token, lane q holds channels 8q .. 8q+7; the
+// butterflies run in fp64, where every partial sum of bf16-rounded inputs is
+// exact, so the coefficients are the exactly rounded transform.
+// ---------------------------------------------------------------------------
+
+template <int MODE>
+__global__ __launch_bounds__(256) void k_enc_wht(const Params p, int sec0, float* coef_out, float* r_out) {
+  constexpr int D = 128;
+  const int u = blockIdx.y + sec0, ch = blockIdx.x;
+  const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
+  const int t0 = ch * p.chunk_tokens;
+  const int n = min(p.chunk_tokens, p.T_mid - t0);
+  if (n <= 0) return;
+  const int lane = threadIdx.x & 63, q = lane & 15, grp = threadIdx.x >> 4;  // 16 tokens per pass
+  const void* src = s ? p.v : p.k;
+  const bool rope = (s == 0) && p.rope_keys;
+  const bool transform = (s == 1) || p.wht_keys;
+  const int64_t lh_row0 = ((int64_t)l * p.H + h) * p.T;
+  const int64_t r_index = !transform ? -1 : (p.wht_keys ? (int64_t)u : (int64_t)l * p.H + h);
+
+  double sum[8], sq[8];
+  float mn[8], mx[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) { sum[e] = 0; sq[e] = 0; mn[e] = INFINITY; mx[e] = -INFINITY; }
+
+  __shared__ SideLds sd;
+  extern __shared__ uint32_t tilebuf[];
+  float zr[8], rc[8], qmax[8];
+  uint32_t bl = 0;
+  const bool sym = (s == 0);
+  if constexpr (MODE == 1) {
+    if (get_status(p.ws, p.w) & (1u << KVTC_ERR_NONFINITE)) return;
+    if (threadIdx.x < D) {
+      int64_t si = (int64_t)u * D + threadIdx.x;
+      sd.zero[threadIdx.x] = reinterpret_cast<const float*>(p.ws + p.w.side_zero)[si];
+      sd.rcp[threadIdx.x] = reinterpret_cast<const float*>(p.ws + p.w.side_rcp)[si];
+      sd.bits[threadIdx.x] = p.ws[p.w.side_bits + si];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int i = 8 * q + e;
+      zr[e] = sd.zero[i]; rc[e] = sd.rcp[i];
+    }
+    bl = sd.bits[0];  // uniform width on this path
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qmax[e] = (float)((1u << bl) - 1u);
+  }
+  const uint32_t row_words_full = (uint32_t)((p.tile_tokens * (int)bl + 31) >> 5);
+  const int ntiles = (n + p.tile_tokens - 1) / p.tile_tokens;
+  uint32_t* slot = MODE == 1 ? reinterpret_cast<uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot) : nullptr;
+
+  for (int tl = 0; tl < ntiles; ++tl) {
+    const int ta = tl * p.tile_tokens;
+    const int nt = min(p.tile_tokens, n - ta);
+    const uint32_t row_words = (uint32_t)((nt * (int)bl + 31) >> 5);
+    if constexpr (MODE == 1) {
+      for (uint32_t i = threadIdx.x; i < row_words * D; i += blockDim.x) tilebuf[i] = 0;
+      __syncthreads();
+    }
+    for (int tb = grp; tb < nt; tb += 16) {
+      const int tok = ta + tb;
+      const int pos = p.mid_begin + t0 + tok;
+      const uint16_t* rowp = nullptr;
+      float x[8];
+      if (p.dtype == KVTC_BF16) {
+        rowp = reinterpret_cast<const uint16_t*>(src) + (lh_row0 + pos) * D;
+        unpack_bf16x8(*reinterpret_cast<const uint4*>(rowp + 8 * q), x);
+      } else {
+        const float* fp = reinterpret_cast<const float*>(src) + (lh_row0 + pos) * D + 8 * q;
+        float4 a = *reinterpret_cast<const float4*>(fp), b = *reinterpret_cast<const float4*>(fp + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+      }
+      if (rope) {
+        const float2* rr = p.rope + (int64_t)pos * (D / 2);
+        if (p.rope_style == KVTC_ROPE_HALF) {
+          float pr[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pr[e] = __shfl_xor(x[e], 8, 16);
+          const bool lower = q < 8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            float2 cs = rr[8 * (q & 7) + e];
+            float ya = lower ? x[e] : pr[e], yb = lower ? pr[e] : x[e];
+            float yb_s = __fmul_rn(yb, cs.y), ya_s = __fmul_rn(ya, cs.y);
+            x[e] = lower ? __fmaf_rn(ya, cs.x, yb_s) : __fmaf_rn(yb, cs.x, -ya_s);
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            float2 cs = rr[4 * q + m];
+            float ya = x[2 * m], yb = x[2 * m + 1];
+            float yb_s = __fmul_rn(yb, cs.y), ya_s = __fmul_rn(ya, cs.y);
+            x[2 * m] = __fmaf_rn(ya, cs.x, yb_s);
+            x[2 * m + 1] = __fmaf_rn(yb, cs.x, -ya_s);
+          }
+        }
+        if (p.dtype == KVTC_BF16) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = round_bf16(x[e]);
+        }
+      }
+      float c[8];
+      if (transform) {
+        double ss = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = __fma_rn((double)x[e], (double)x[e], ss);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o, 16);
+        const float rt = (float)__dsqrt_rn(__ddiv_rn(ss, (double)D));
+        double y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = rt == 0.0f ? 0.0 : (double)__fdiv_rn(x[e], rt);
+        // in-lane stages (channel strides 1, 2, 4)
+#pragma unroll
+        for (int st = 1; st < 8; st <<= 1)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (!(e & st)) {
+              double a = y[e], b = y[e + st];
+              y[e] = a + b;
+              y[e + st] = a - b;
+            }
+        // cross-lane stages (channel strides 8, 16, 32, 64)
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            double other = __shfl_xor(y[e], o, 16);
+            y[e] = (q & o) ? other - y[e] : y[e] + other;
+          }
+        }
+        const double rs = __dsqrt_rn((double)D);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c[e] = (float)__ddiv_rn(y[e], rs);
+        if (q == 0) {
+          if (MODE == 0) reinterpret_cast<float*>(p.out + p.r_off)[r_index * p.T_mid + t0 + tok] = rt;
+          if (MODE == 2 && r_out) r_out[(int64_t)(u - sec0) * p.T_mid + t0 + tok] = rt;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c[e] = x[e];
+      }
+      if constexpr (MODE == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          sum[e] += (double)c[e];
+          sq[e] = __fma_rn((double)c[e], (double)c[e], sq[e]);
+          mn[e] = fminf(mn[e], c[e]);
+          mx[e] = fmaxf(mx[e], c[e]);
+        }
+      } else if constexpr (MODE == 1) {
+        if (bl > 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            uint32_t qi;
+            if (sym) {
+              // symmetric: clamp(rint(c * rcp), -Q, Q) + 2^(b-1)
+              const float Q = (float)((1 << (bl - 1)) - 1);
+              float v = __fmul_rn(c[e], rc[e]);
+              float qq = fminf(fmaxf(__builtin_rintf(v), -Q), Q);
+              qi = (uint32_t)((int)qq + (1 << (bl - 1)));
+            } else {
+              float v = __fmul_rn(__fsub_rn(c[e], zr[e]), rc[e]);
+              qi = (uint32_t)fminf(fmaxf(__builtin_rintf(v), 0.0f), qmax[e]);
+            }
+            const int i = 8 * q + e;
+            const uint32_t bitpos = (uint32_t)tb * bl;
+            const uint32_t wi = (uint32_t)i * row_words + (bitpos >> 5), sh = bitpos & 31;
+            atomicOr(&tilebuf[wi], qi << sh);
+            if (sh + bl > 32) atomicOr(&tilebuf[wi + 1], qi >> (32 - sh));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) coef_out[((int64_t)(u - sec0) * p.T_mid + t0 + tok) * D + 8 * q + e] = c[e];
+      }
+    }
+    if constexpr (MODE == 1) {
+      __syncthreads();
+      uint32_t* dst = slot + (int64_t)tl * row_words_full * D;
+      for (uint32_t i = threadIdx.x; i < row_words * D; i += blockDim.x) dst[i] = tilebuf[i];
+      __syncthreads();
+    }
+  }
+  if constexpr (MODE == 0) {
+    // reduce the 16 token groups of the block: lanes with equal q in the
+    // 16 groups (4 per wave, 4 waves), fixed order
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        sum[e] += __shfl_xor(sum[e], o, 64);
+        sq[e] += __shfl_xor(sq[e], o, 64);
+        mn[e] = fminf(mn[e], __shfl_xor(mn[e], o, 64));
+        mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], o, 64));
+      }
+    __shared__ double s_sum[4][D], s_sq[4][D];
+    __shared__ float s_mn[4][D], s_mx[4][D];
+    const int wave = threadIdx.x >> 6;
+    if ((lane >> 4) == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        int i = 8 * q + e;
+        s_sum[wave][i] = sum[e]; s_sq[wave][i] = sq[e]; s_mn[wave][i] = mn[e]; s_mx[wave][i] = mx[e];
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < D) {
+      int i = threadIdx.x;
+      double a = s_sum[0][i], b = s_sq[0][i];
+      float c = s_mn[0][i], d = s_mx[0][i];
+      for (int w2 = 1; w2 < 4; ++w2) {
+        a += s_sum[w2][i]; b += s_sq[w2][i];
+        c = fminf(c, s_mn[w2][i]); d = fmaxf(d, s_mx[w2][i]);
+      }
+      int64_t idx = ((int64_t)u * p.chunks_per_sec + ch) * D + i;
+      reinterpret_cast<double*>(p.ws + p.w.part_sum)[idx] = a;
+      reinterpret_cast<double*>(p.ws + p.w.part_sq)[idx] = b;
+      reinterpret_cast<float*>(p.ws + p.w.part_min)[idx] = c;
+      reinterpret_cast<float*>(p.ws + p.w.part_max)[idx] = d;
+    }
+  }
+}
+
+static size_t quant_lds_bytes(const Params& p, size_t tile) {
+  if (p.transform == KVTC_WHT) return tile;
+  const size_t os = p.dtype == KVTC_BF16 ? 2 : 4;
+  return (size_t)p.D * p.D * os + 4 * 16 * (size_t)p.D * os + tile;
+}
+
+static size_t tile_lds_bytes(const Params& p) {
+  int32_t bmax = p.budget_k > p.budget_v ? p.budget_k : p.budget_v;
+  if (p.transform == KVTC_WHT) {
+    int32_t b = p.bits_k_uniform > p.bits_v_uniform ? p.bits_k_uniform : p.bits_v_uniform;
+    return (size_t)((p.tile_tokens * b + 31) / 32) * p.D * 4;
+  }
+  int32_t nz = bmax < p.D ? bmax : p.D;
+  return (size_t)(((int64_t)p.tile_tokens * bmax + 31) / 32 + nz) * 4;
+}
+
+hipError_t launch_enc_transform(const Params& p, int mode, hipStream_t s) {
+  dim3 grid(p.chunks_per_sec, p.n_sections), block(256);
+  size_t lds = mode == 1 ? quant_lds_bytes(p, tile_lds_bytes(p)) : 0;
+  if (p.transform == KVTC_WHT) {
+    if (mode == 0) hipLaunchKernelGGL(k_enc_wht<0>, grid, block, 0, s, p, 0, (float*)nullptr, (float*)nullptr);
+    else hipLaunchKernelGGL(k_enc_wht<1>, grid, block, lds, s, p, 0, (float*)nullptr, (float*)nullptr);
+    return hipGetLastError();
+  }
+#define KVTC_LAUNCH_PCA(D_, DT_)                                                              \
+  if (p.D == D_ && p.dtype == DT_) {                                                          \
+    if (mode == 0) {                                                                          \
+      hipLaunchKernelGGL((k_enc_pca<D_, DT_, 0>), grid, block, 0, s, p, 0, (float*)nullptr);  \
+    } else {                                                                                  \
+      (void)hipFuncSetAttribute((const void*)k_enc_pca<D_, DT_, 1>,                          \
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);       \
+      hipLaunchKernelGGL((k_enc_pca<D_, DT_, 1>), grid, block, lds, s, p, 0, (float*)nullptr); \
+    }                                                                                         \
+    return hipGetLastError();                                                                 \
+  }
+  KVTC_LAUNCH_PCA(128, KVTC_BF16)
+  KVTC_LAUNCH_PCA(64, KVTC_BF16)
+  KVTC_LAUNCH_PCA(64, KVTC_FP32)
+#undef KVTC_LAUNCH_PCA
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_coeffs(const Params& p, int sec_begin, int sec_end, float* out, float* r_out,
+                         hipStream_t s) {
+  dim3 grid(p.chunks_per_sec, sec_end - sec_begin), block(256);
+  if (p.transform == KVTC_WHT) {
+    hipLaunchKernelGGL(k_enc_wht<2>, grid, block, 0, s, p, sec_begin, out, r_out);
+    return hipGetLastError();
+  }
+  if (p.D == 128 && p.dtype == KVTC_BF16)
+    hipLaunchKernelGGL((k_enc_pca<128, KVTC_BF16, 2>), grid, block, 0, s, p, sec_begin, out);
+  else if (p.D == 64 && p.dtype == KVTC_BF16)
+    hipLaunchKernelGGL((k_enc_pca<64, KVTC_BF16, 2>), grid, block, 0, s, p, sec_begin, out);
+  else if (p.D == 64 && p.dtype == KVTC_FP32)
+    hipLaunchKernelGGL((k_enc_pca<64, KVTC_FP32, 2>), grid, block, 0, s, p, sec_begin, out);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// allocation and side information, one workgroup (D threads) per section
+// ("Bit Budget Is Not Fair": uneven widths; CompressedSection: scales, zero
+// points, bit widths)
+// ---------------------------------------------------------------------------
+
+// Exact ordering key of var * 4^-k: (extended exponent, 24-bit significand),
+// then the component index reversed so that lower indices win ties.
+__device__ __forceinline__ uint64_t alloc_key(float var, int k, int i) {
+  uint32_t bits = __float_as_uint(var);
+  int32_t ex = (int32_t)(bits >> 23);
+  uint32_t man = bits & 0x7fffffu;
+  if (ex == 0) {  // subnormal: normalise the significand
+    int sh = __clz(man) - 8;
+    man = (man << sh) & 0x7fffffu;
+    ex = 1 - sh;
+  }
+  uint64_t e2 = (uint64_t)(ex - 2 * k + 256);  // > 0 for every fp32 value and k <= 8
+  return (((e2 << 23) | man) << 8) | (uint64_t)(255 - i);
+}
+
+__global__ __launch_bounds__(128) void k_enc_alloc(const Params p) {
+  const int u = blockIdx.x;
+  const int D = p.D;
+  const int i = threadIdx.x;
+  const int s = (u / p.H) & 1;
+  const bool active = i < D;
+  __shared__ uint32_t s_cnt[2];
+  __shared__ float s_amax[2];
+  uint8_t* rec = p.out + p.side_off + (int64_t)u * 9 * D;
+  const int64_t N = p.T_mid;
+  float mu = 0.f, var = 0.f, mn = 0.f, mx = 0.f;
+  bool nonfinite = false;
+  if (active && N > 0) {
+    double a = 0.0, b = 0.0;
+    float c = INFINITY, d = -INFINITY;
+    for (int ch = 0; ch < p.chunks_per_sec; ++ch) {
+      int64_t idx = ((int64_t)u * p.chunks_per_sec + ch) * D + i;
+      a += reinterpret_cast<const double*>(p.ws + p.w.part_sum)[idx];
+      b += reinterpret_cast<const double*>(p.ws + p.w.part_sq)[idx];
+      c = fminf(c, reinterpret_cast<const float*>(p.ws + p.w.part_min)[idx]);
+      d = fmaxf(d, reinterpret_cast<const float*>(p.ws + p.w.part_max)[idx]);
+    }
+    nonfinite = !isfinite(a) || !isfinite(b);
+    double m = a / (double)N;
+    double vv = (b - a * m) / (double)N;
+    if (vv < 0.0) vv = 0.0;
+    mu = (float)m;
+    var = (c != d) ? (float)vv : 0.0f;
+    mn = c;
+    mx = d;
+  }
+  if (nonfinite) set_status(p.ws, p.w, KVTC_ERR_NONFINITE);
+  // ---- bit widths ----
+  uint32_t bits = 0;
+  if (p.transform == KVTC_PCA) {
+    const int budget = s == 0 ? p.budget_k : p.budget_v;
+    // greedy marginal allocation == the `budget` largest var_i 4^-k (k < max_bits),
+    // ranked by exact value then lowest index: find the budget-th largest key
+    // by a bitwise search over the 41-bit keys
+    const bool cand = active && var > 0.0f;
+    auto count_ge = [&](uint64_t thr) -> uint32_t {
+      uint32_t cnt = 0;
+      if (cand)
+        for (int k = 0; k < p.max_bits; ++k) cnt += alloc_key(var, k, i) >= thr ? 1u : 0u;
+      // block sum (two waves)
+      for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+      __syncthreads();
+      if ((threadIdx.x & 63) == 0) s_cnt[threadIdx.x >> 6] = cnt;
+      __syncthreads();
+      return s_cnt[0] + (blockDim.x > 64 ? s_cnt[1] : 0u);
+    };
+    uint64_t thr = 1;  // every real candidate key is >= 1
+    if ((int)count_ge(1) > budget) {
+      uint64_t t = 0;
+      for (int bit = 40; bit >= 0; --bit) {
+        uint64_t c2 = t | (1ull << bit);
+        if ((int)count_ge(c2) >= budget) t = c2;
+      }
+      thr = t;
+    }
+    if (cand && budget > 0)
+      for (int k = 0; k < p.max_bits; ++k) bits += alloc_key(var, k, i) >= thr ? 1u : 0u;
+  } else {
+    bits = (uint32_t)(s == 0 ? p.bits_k_uniform : p.bits_v_uniform);
+  }
+  // ---- side information ----
+  float zero = 0.f, scale = 0.f, rcp = 0.f;
+  const bool sym = p.transform == KVTC_WHT && s == 0;
+  if (sym) {
+    float a = active ? fmaxf(fabsf(mn), fabsf(mx)) : 0.f;
+    if (N == 0) a = 0.f;
+    for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s_amax[threadIdx.x >> 6] = a;
+    __syncthreads();
+    float amax = fmaxf(s_amax[0], blockDim.x > 64 ? s_amax[1] : 0.f);
+    const int Q = (1 << (bits - 1)) - 1;
+    scale = (float)__ddiv_rn((double)amax, (double)Q);
+    rcp = scale > 0.f ? __fdiv_rn(1.0f, scale) : 0.f;
+    if (!(scale > 0.f) || isinf(rcp)) { scale = 0.f; rcp = 0.f; }
+  } else if (bits == 0) {
+    zero = mu;
+  } else {
+    zero = mn;
+    scale = (float)__ddiv_rn((double)mx - (double)mn, (double)((1u << bits) - 1u));
+    rcp = scale > 0.f ? __fdiv_rn(1.0f, scale) : 0.f;
+    if (!(scale > 0.f) || isinf(rcp)) { scale = 0.f; rcp = 0.f; }
+  }
+  if (N == 0) { bits = 0; zero = 0.f; scale = 0.f; rcp = 0.f; }
+  if (active) {
+    rec[i] = (uint8_t)bits;
+    reinterpret_cast<float*>(rec + D)[i] = zero;
+    reinterpret_cast<float*>(rec + 5 * (int64_t)D)[i] = scale;
+    int64_t si = (int64_t)u * D + i;
+    reinterpret_cast<float*>(p.ws + p.w.side_zero)[si] = zero;
+    reinterpret_cast<float*>(p.ws + p.w.side_rcp)[si] = rcp;
+    p.ws[p.w.side_bits + si] = (uint8_t)bits;
+    reinterpret_cast<float4*>(p.ws + p.w.sec_stats)[si] = make_float4(mu, var, mn, mx);
+  }
+}
+
+hipError_t launch_enc_alloc(const Params& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_enc_alloc, dim3(p.n_sections), dim3(p.D), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// plan: basis rounded to the operand precision, in both layouts
+// ---------------------------------------------------------------------------
+
+__global__ void k_prep_basis(const float* src, void* bt, void* b, int64_t n_basis, int D, int dtype,
+                             int32_t* bad) {
+  const int64_t total = n_basis * D * D;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    int64_t m = idx / ((int64_t)D * D), rem = idx % ((int64_t)D * D);
+    int j = (int)(rem / D), i = (int)(rem % D);  // src[m][j][i]: row j = channel, col i = component
+    float v = src[idx];
+    if (!isfinite(v)) atomicOr(bad, 1);
+    int64_t tpos = m * D * D + (int64_t)i * D + j;
+    if (dtype == KVTC_BF16) {
+      uint16_t hv = f32_to_bf16(v);
+      reinterpret_cast<uint16_t*>(b)[idx] = hv;
+      reinterpret_cast<uint16_t*>(bt)[tpos] = hv;
+    } else {
+      reinterpret_cast<float*>(b)[idx] = v;
+      reinterpret_cast<float*>(bt)[tpos] = v;
+    }
+  }
+}
+
+hipError_t launch_prep_basis(const float* src, void* basis_t, void* basis, int n_basis, int D,
+                             int dtype, int32_t* bad, hipStream_t s) {
+  int64_t total = (int64_t)n_basis * D * D;
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_prep_basis, dim3((unsigned)blocks), dim3(256), 0, s, src, basis_t, basis,
+                     (int64_t)n_basis, D, dtype, bad);
+  return hipGetLastError();
+}
+
+}  // namespace kvtc

@@ -1,0 +1,687 @@
+// Entropy coding ("rANS Makes the Last Mile Smaller"): per-chunk byte
+// histograms and 2^sb frequency tables, interleaved rANS streams with
+// `lanes` states each (one stream per packed tile, 64/lanes streams per
+// wave64), the prefix sum over record sizes, container assembly, and the
+// decoder with a slot lookup table in LDS.
+//
+// Stream format (one tile of P bytes): symbol i belongs to lane i % lanes
+// and step i / lanes; states live in [2^16, 2^32) and renormalise with
+// 16-bit words.  The encoder walks the steps backwards and, inside a step,
+// the lanes in descending order, storing words in emission order; the
+// decoder walks forward, lanes ascending, consuming words from the end.
+#include <string.h>
+
+#include "kvtc_internal.h"
+
+namespace kvtc {
+
+struct EncSym {
+  uint32_t f;
+  uint32_t cum;
+  double rcp;  // 1/f rounded to fp64; quotient = trunc(fma(x, rcp, 2^-20))
+};
+
+// ---- frequency table ------------------------------------------------------
+
+// Lane-local best of (value desc, symbol asc) across the wave.
+__device__ __forceinline__ void wave_argmax(uint64_t& v, int& s) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t ov = __shfl_xor(v, o, 64);
+    int os = __shfl_xor(s, o, 64);
+    if (ov > v || (ov == v && os < s)) { v = ov; s = os; }
+  }
+}
+
+__device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Counts -> frequencies summing to M = 2^sb (one wave; lane holds symbols
+// 4*lane .. 4*lane+3).  Each present symbol gets max(1, round(n M / N)); a
+// shortfall goes to the most frequent symbol, an excess is taken one unit at
+// a time from the largest frequency (lowest symbol on ties).  The excess loop
+// is evaluated in closed form: every frequency above a level tau is lowered
+// to tau, then the r lowest symbols at tau lose one more unit.
+__device__ void wave_freq_normalize(const uint32_t* counts, int sb, uint32_t* freq) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t M = 1ull << sb;
+  uint32_t n[4];
+  uint64_t f[4];
+  uint64_t N = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) { n[k] = counts[4 * lane + k]; N += n[k]; }
+  N = wave_sum64(N);
+  if (N == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) freq[4 * lane + k] = 0;
+    return;
+  }
+  uint64_t local = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (n[k] == 0) f[k] = 0;
+    else {
+      uint64_t r = ((uint64_t)n[k] * (2 * M) + N) / (2 * N);
+      f[k] = r < 1 ? 1 : r;
+    }
+    local += f[k];
+  }
+  const int64_t d = (int64_t)M - (int64_t)wave_sum64(local);
+  if (d > 0) {
+    uint64_t bv = 0;
+    int bs = 1 << 30;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if ((uint64_t)n[k] > bv || ((uint64_t)n[k] == bv && 4 * lane + k < bs)) { bv = n[k]; bs = 4 * lane + k; }
+    wave_argmax(bv, bs);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) if (4 * lane + k == bs) f[k] += (uint64_t)d;
+  } else if (d < 0) {
+    const uint64_t R = (uint64_t)(-d);
+    // smallest tau >= 1 with E(tau) = sum max(0, f - tau) <= R
+    uint64_t lo = 1, hi = M;  // E(M) = 0 <= R
+    while (lo < hi) {
+      uint64_t mid = (lo + hi) >> 1;
+      uint64_t e = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) e += f[k] > mid ? f[k] - mid : 0;
+      e = wave_sum64(e);
+      if (e <= R) hi = mid; else lo = mid + 1;
+    }
+    const uint64_t tau = lo;
+    uint64_t e = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) e += f[k] > tau ? f[k] - tau : 0;
+    e = wave_sum64(e);
+    uint64_t rem = R - e;
+    // symbols at level tau after lowering, in ascending symbol order
+    uint32_t at[4], cnt = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { at[k] = f[k] >= tau ? 1u : 0u; cnt += at[k]; }
+    uint32_t x = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      uint32_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    uint32_t before = x - cnt;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (f[k] > tau) f[k] = tau;
+      if (at[k]) {
+        if (before < rem) f[k] -= 1;
+        before += 1;
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) freq[4 * lane + k] = (uint32_t)f[k];
+}
+
+// Build the encoder table (wave 0 computes, the block shares it).
+__device__ void build_enc_table(const uint32_t* freq, EncSym* tab) {
+  const int lane = threadIdx.x & 63;
+  uint32_t f[4], s = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) { f[k] = freq[4 * lane + k]; s += f[k]; }
+  uint32_t x = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  uint32_t cum = x - s;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    EncSym e;
+    e.f = f[k];
+    e.cum = cum;
+    e.rcp = f[k] ? __ddiv_rn(1.0, (double)f[k]) : 0.0;
+    tab[4 * lane + k] = e;
+    cum += f[k];
+  }
+}
+
+// ---- stream coder ---------------------------------------------------------
+
+// Encode one stream per `lanes`-lane group of the wave.  sym: the tile's
+// bytes (any address space); words: output (emission order).  Returns the
+// word count (uniform within the group) or -1 when the capacity is exceeded.
+__device__ int64_t rans_encode_stream(const uint8_t* sym, int64_t Nt, bool valid, int steps_max,
+                                      const EncSym* tab, int sb, int lanes, uint16_t* words,
+                                      int64_t wcap, uint32_t* state_out) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane % lanes, grp = lane / lanes;
+  const uint64_t gmask = (lanes == 64) ? ~0ull : ((1ull << lanes) - 1ull);
+  const uint32_t M = 1u << sb;
+  uint32_t x = kRansL;
+  int64_t nw = 0;
+  bool overflow = false;
+  for (int k = steps_max - 1; k >= 0; --k) {
+    const int64_t i = (int64_t)k * lanes + j;
+    const bool active = valid && i < Nt;
+    EncSym e = tab[active ? sym[i] : 0];
+    const bool emit = active && ((uint64_t)x >= ((uint64_t)e.f << (32 - sb)));
+    const uint64_t m = (__ballot(emit) >> (grp * lanes)) & gmask;
+    if (emit) {
+      const int64_t at = nw + __popcll(m >> (j + 1));
+      if (at < wcap) words[at] = (uint16_t)(x & 0xffffu);
+      else overflow = true;
+      x >>= 16;
+    }
+    nw += __popcll(m);
+    if (active) {
+      // x = floor(x / f) * M + (x mod f) + cum, via an exact fp64 quotient
+      const uint32_t q = (uint32_t)__fma_rn((double)x, e.rcp, 0x1p-20);
+      x = x + e.cum + q * (M - e.f);
+    }
+  }
+  if (valid) state_out[j] = x;
+  const uint64_t ov = (__ballot(overflow) >> (grp * lanes)) & gmask;
+  return ov ? -1 : nw;
+}
+
+// Decode one stream per lane group.  lut: 2^sb entries of
+// sym | (f-1) << 8 | (slot-cum) << 20.  Returns false on a malformed stream.
+__device__ bool rans_decode_stream(const uint32_t* states, const uint16_t* words, int64_t nw,
+                                   int64_t Nt, bool valid, int steps_max, const uint32_t* lut,
+                                   int sb, int lanes, uint8_t* out) {
+  const int lane = threadIdx.x & 63;
+  const int j = lane % lanes, grp = lane / lanes;
+  const uint64_t gmask = (lanes == 64) ? ~0ull : ((1ull << lanes) - 1ull);
+  const uint32_t mask = (1u << sb) - 1u;
+  uint32_t x = valid ? states[j] : kRansL;
+  bool bad = valid && x < kRansL;
+  int64_t ptr = nw;
+  for (int k = 0; k < steps_max; ++k) {
+    const int64_t i = (int64_t)k * lanes + j;
+    const bool active = valid && i < Nt;
+    if (active) {
+      const uint32_t slot = x & mask;
+      const uint32_t e = lut[slot];
+      x = (((e >> 8) & 0xfffu) + 1u) * (x >> sb) + (e >> 20);
+      out[i] = (uint8_t)(e & 0xffu);
+    }
+    const bool need = active && x < kRansL;
+    const uint64_t m = (__ballot(need) >> (grp * lanes)) & gmask;
+    if (need) {
+      const int64_t at = ptr - 1 - __popcll(m & ((1ull << j) - 1ull));
+      if (at >= 0) x = (x << 16) | words[at];
+      else bad = true;
+      if (x < kRansL) bad = true;
+    }
+    ptr -= __popcll(m);
+  }
+  if (valid && (x != kRansL || ptr != 0)) bad = true;
+  return !bad;
+}
+
+// ---- per-chunk encoder ------------------------------------------------------
+
+__device__ __forceinline__ int64_t tile_bytes(const uint8_t* bits, int D, int ntok) {
+  int64_t P = 0;
+  for (int i = 0; i < D; ++i) P += 4 * (int64_t)((ntok * (int)bits[i] + 31) >> 5);
+  return P;
+}
+
+// record slot of chunk c: [freq u16 x256][nwords u32 x tiles][tile t: states, words]
+__device__ __forceinline__ int64_t slot_states_off(const Params& p, int t) {
+  return 512 + 4 * (int64_t)p.tiles_per_chunk + (int64_t)t * (4 * p.lanes + 2 * p.w.tile_words_max + 4);
+}
+
+__global__ void k_rans_enc_chunks(const Params p) {
+  const int c = blockIdx.x;
+  const int u = c / p.chunks_per_sec, ch = c % p.chunks_per_sec;
+  const int D = p.D;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (get_status(p.ws, p.w) & (1u << KVTC_ERR_NONFINITE)) return;
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t freq[256];
+  __shared__ EncSym tab[256];
+  __shared__ uint8_t bits[256];
+  __shared__ int64_t s_P[2];
+  if (threadIdx.x < 256) hist[threadIdx.x] = 0;
+  for (int i = threadIdx.x; i < D; i += blockDim.x) bits[i] = p.ws[p.w.side_bits + (int64_t)u * D + i];
+  __syncthreads();
+  const int n = min(p.chunk_tokens, p.T_mid - ch * p.chunk_tokens);
+  const int ntiles = (n + p.tile_tokens - 1) / p.tile_tokens;
+  const int n_last = n - (ntiles - 1) * p.tile_tokens;
+  if (threadIdx.x == 0) {
+    s_P[0] = tile_bytes(bits, D, p.tile_tokens);
+    s_P[1] = tile_bytes(bits, D, n_last);
+  }
+  __syncthreads();
+  const int64_t P_full = s_P[0], P_last = s_P[1];
+  const int64_t P = (ntiles - 1) * P_full + P_last;
+  uint32_t* rec_size = reinterpret_cast<uint32_t*>(p.ws + p.w.rec_size);
+  if (P == 0) {
+    if (threadIdx.x == 0) rec_size[c] = 0;
+    return;
+  }
+  const uint8_t* packed = p.ws + p.w.packed + (int64_t)c * p.w.packed_slot;
+  // histogram of the chunk's bytes (P is a multiple of 4)
+  for (int64_t i = threadIdx.x; i < P / 4; i += blockDim.x) {
+    uint32_t wv = reinterpret_cast<const uint32_t*>(packed)[i];
+    atomicAdd(&hist[wv & 0xff], 1u);
+    atomicAdd(&hist[(wv >> 8) & 0xff], 1u);
+    atomicAdd(&hist[(wv >> 16) & 0xff], 1u);
+    atomicAdd(&hist[wv >> 24], 1u);
+  }
+  __syncthreads();
+  if (wave == 0) {
+    wave_freq_normalize(hist, p.sb, freq);
+    __builtin_amdgcn_wave_barrier();
+    build_enc_table(freq, tab);
+  }
+  __syncthreads();
+  uint8_t* slot = p.ws + p.w.rec + (int64_t)c * p.w.rec_slot;
+  if (threadIdx.x < 256) reinterpret_cast<uint16_t*>(slot)[threadIdx.x] = (uint16_t)freq[threadIdx.x];
+  // streams: 64/lanes per wave
+  const int spw = 64 / p.lanes;
+  const int t = wave * spw + lane / p.lanes;
+  const bool valid = t < ntiles;
+  const int64_t Nt = valid ? (t == ntiles - 1 ? P_last : P_full) : 0;
+  const int steps = (int)((Nt + p.lanes - 1) / p.lanes);
+  int steps_max = steps;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) steps_max = max(steps_max, __shfl_xor(steps_max, o, 64));
+  const int tt = valid ? t : 0;
+  uint32_t* states = reinterpret_cast<uint32_t*>(slot + slot_states_off(p, tt));
+  uint16_t* words = reinterpret_cast<uint16_t*>(slot + slot_states_off(p, tt) + 4 * p.lanes);
+  int64_t nw = rans_encode_stream(packed + (int64_t)tt * P_full, Nt, valid, steps_max, tab, p.sb,
+                                  p.lanes, words, p.w.tile_words_max, states);
+  __shared__ int32_t s_nw[64];
+  if (valid && (lane % p.lanes) == 0) {
+    s_nw[t] = (int32_t)nw;
+    reinterpret_cast<uint32_t*>(slot + 512)[t] = (uint32_t)(nw < 0 ? 0 : nw);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int64_t size = 512 + 4 * (int64_t)ntiles;
+    bool over = false;
+    for (int k = 0; k < ntiles; ++k) {
+      if (s_nw[k] < 0) over = true;
+      int64_t w = s_nw[k] < 0 ? 0 : s_nw[k];
+      size += 4 * (int64_t)p.lanes + 2 * w + ((w & 1) ? 2 : 0);
+    }
+    if (over) set_status(p.ws, p.w, KVTC_ERR_CAPACITY);
+    rec_size[c] = (uint32_t)align16(size);
+  }
+}
+
+hipError_t launch_rans_encode_chunks(const Params& p, hipStream_t s) {
+  int streams = p.tiles_per_chunk;
+  int waves = (streams * p.lanes + 63) / 64;
+  if (waves < 4) waves = 4;  // 256 threads: histogram and table use 256
+  hipLaunchKernelGGL(k_rans_enc_chunks, dim3(p.n_chunks), dim3(64 * waves), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---- prefix sum, directory, header and record copy -------------------------
+
+struct HeaderBytes {
+  uint8_t b[kHeaderBytes];
+};
+
+__global__ __launch_bounds__(1024) void k_scan(const Params p, HeaderBytes hdr) {
+  __shared__ uint64_t s_part[1024];
+  const uint32_t* rec_size = reinterpret_cast<const uint32_t*>(p.ws + p.w.rec_size);
+  uint64_t* rec_pos = reinterpret_cast<uint64_t*>(p.ws + p.w.rec_pos);
+  const int64_t n = p.n_chunks;
+  const int tid = threadIdx.x;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t a = tid * per, b = min(n, a + per);
+  uint64_t local = 0;
+  for (int64_t i = a; i < b; ++i) local += rec_size[i];
+  s_part[tid] = local;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    uint64_t v = tid >= o ? s_part[tid - o] : 0;
+    __syncthreads();
+    s_part[tid] += v;
+    __syncthreads();
+  }
+  uint64_t run = s_part[tid] - local;
+  for (int64_t i = a; i < b; ++i) {
+    rec_pos[i] = run;
+    uint8_t* d = p.out + p.dir_off + i * kDirEntry;
+    uint64_t off = (uint64_t)p.chunks_off + run;
+    *reinterpret_cast<uint64_t*>(d) = off;
+    *reinterpret_cast<uint32_t*>(d + 8) = rec_size[i];
+    *reinterpret_cast<uint32_t*>(d + 12) = 0;
+    run += rec_size[i];
+  }
+  __syncthreads();
+  const uint64_t total = (uint64_t)p.chunks_off + s_part[1023];
+  if (tid < kHeaderBytes / 4) {
+    uint32_t wv = (uint32_t)hdr.b[4 * tid] | ((uint32_t)hdr.b[4 * tid + 1] << 8) |
+                  ((uint32_t)hdr.b[4 * tid + 2] << 16) | ((uint32_t)hdr.b[4 * tid + 3] << 24);
+    if (tid == 42) wv = (uint32_t)total;
+    if (tid == 43) wv = (uint32_t)(total >> 32);
+    reinterpret_cast<uint32_t*>(p.out)[tid] = wv;
+  }
+  if (tid == 0) {
+    uint64_t* st = reinterpret_cast<uint64_t*>(p.ws + p.w.status);
+    if (total > (uint64_t)p.cap) {
+      set_status(p.ws, p.w, KVTC_ERR_CAPACITY);
+      st[1] = 0;
+    } else {
+      st[1] = (get_status(p.ws, p.w) & ((1u << KVTC_ERR_NONFINITE) | (1u << KVTC_ERR_CAPACITY))) ? 0 : total;
+    }
+  }
+}
+
+__global__ void k_copy_records(const Params p) {
+  const int c = blockIdx.x;
+  if (get_status(p.ws, p.w) & ((1u << KVTC_ERR_CAPACITY) | (1u << KVTC_ERR_NONFINITE))) return;
+  const uint32_t size = reinterpret_cast<const uint32_t*>(p.ws + p.w.rec_size)[c];
+  if (size == 0) return;
+  const uint64_t pos = reinterpret_cast<const uint64_t*>(p.ws + p.w.rec_pos)[c];
+  const uint8_t* slot = p.ws + p.w.rec + (int64_t)c * p.w.rec_slot;
+  uint8_t* dst = p.out + p.chunks_off + pos;
+  const int ch = c % p.chunks_per_sec;
+  const int n = min(p.chunk_tokens, p.T_mid - ch * p.chunk_tokens);
+  const int ntiles = (n + p.tile_tokens - 1) / p.tile_tokens;
+  const uint32_t* nwv = reinterpret_cast<const uint32_t*>(slot + 512);
+  // table and word counts
+  const int head = (512 + 4 * ntiles) / 2;
+  for (int i = threadIdx.x; i < head; i += blockDim.x)
+    reinterpret_cast<uint16_t*>(dst)[i] = reinterpret_cast<const uint16_t*>(slot)[i];
+  int64_t at = 512 + 4 * (int64_t)ntiles;
+  for (int t = 0; t < ntiles; ++t) {
+    const uint32_t nw = nwv[t];
+    const int64_t so = slot_states_off(p, t);
+    const int64_t piece = 4 * (int64_t)p.lanes + 2 * (int64_t)nw;
+    const int64_t piece_padded = piece + ((nw & 1) ? 2 : 0);
+    for (int64_t i = threadIdx.x; i < piece_padded / 2; i += blockDim.x) {
+      uint16_t v = 2 * i < piece ? reinterpret_cast<const uint16_t*>(slot + so)[i] : 0;
+      reinterpret_cast<uint16_t*>(dst + at)[i] = v;
+    }
+    at += piece_padded;
+  }
+  for (int64_t i = at + threadIdx.x; i < size; i += blockDim.x) dst[i] = 0;
+}
+
+hipError_t launch_assemble(const Params& p, const uint8_t* hdr, hipStream_t s) {
+  HeaderBytes h;
+  memcpy(h.b, hdr, kHeaderBytes);
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, p, h);
+  if (p.n_chunks > 0) hipLaunchKernelGGL(k_copy_records, dim3(p.n_chunks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---- decoder ----------------------------------------------------------------
+
+__global__ void k_dec_check(const Params p, HeaderBytes hdr) {
+  const int tid = threadIdx.x;
+  __shared__ int s_bad;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  if (p.cap < p.chunks_off || p.cap < kHeaderBytes) {
+    if (tid == 0) s_bad = 1;
+  } else if (tid < kHeaderBytes / 4 && tid != 42 && tid != 43) {
+    const uint32_t want = (uint32_t)hdr.b[4 * tid] | ((uint32_t)hdr.b[4 * tid + 1] << 8) |
+                          ((uint32_t)hdr.b[4 * tid + 2] << 16) | ((uint32_t)hdr.b[4 * tid + 3] << 24);
+    if (reinterpret_cast<const uint32_t*>(p.in)[tid] != want) atomicOr(&s_bad, 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t* st = reinterpret_cast<uint32_t*>(p.ws + p.w.status);
+    uint32_t code = 0;
+    if (!s_bad) {
+      uint64_t total = *reinterpret_cast<const uint64_t*>(p.in + 168);
+      if (total < (uint64_t)p.chunks_off || total > (uint64_t)p.cap) s_bad = 1;
+    }
+    if (s_bad) code = 1u << KVTC_ERR_CORRUPT;
+    st[0] = code; st[1] = 0; st[2] = 0; st[3] = 0;
+  }
+}
+
+hipError_t launch_dec_check(const Params& p, const uint8_t* hdr, hipStream_t s) {
+  HeaderBytes h;
+  memcpy(h.b, hdr, kHeaderBytes);
+  hipLaunchKernelGGL(k_dec_check, dim3(1), dim3(64), 0, s, p, h);
+  return hipGetLastError();
+}
+
+// Validated bit widths of section u read from the container; false if
+// they cannot have been written by the encoder.
+__device__ bool load_section_bits(const Params& p, int u, uint8_t* bits, int64_t* P_full,
+                                  int64_t* P_last, int n_last) {
+  // called by thread 0 after bits[] was filled by the block
+  const int s = (u / p.H) & 1;
+  int sum = 0;
+  bool ok = true;
+  for (int i = 0; i < p.D; ++i) {
+    if (bits[i] > p.max_bits) ok = false;
+    sum += bits[i];
+    if (p.transform == KVTC_WHT && bits[i] != (s == 0 ? p.bits_k_uniform : p.bits_v_uniform)) ok = false;
+  }
+  if (p.transform == KVTC_PCA && sum > (s == 0 ? p.budget_k : p.budget_v)) ok = false;
+  if (ok) {
+    *P_full = tile_bytes(bits, p.D, p.tile_tokens);
+    *P_last = tile_bytes(bits, p.D, n_last);
+  }
+  return ok;
+}
+
+__global__ void k_rans_dec_chunks(const Params p, int64_t stage_cap) {
+  const int c = blockIdx.x;
+  const int u = c / p.chunks_per_sec, ch = c % p.chunks_per_sec;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (get_status(p.ws, p.w) & (1u << KVTC_ERR_CORRUPT)) return;
+  extern __shared__ uint32_t lds[];
+  uint32_t* lut = lds;                                    // 2^sb entries
+  uint8_t* stage = reinterpret_cast<uint8_t*>(lds + (1 << p.sb));
+  __shared__ uint8_t bits[256];
+  __shared__ int64_t s_info[4];
+  __shared__ uint32_t s_cum[257];
+  __shared__ int s_ok;
+  __shared__ int64_t s_toff[17];
+  const int n = min(p.chunk_tokens, p.T_mid - ch * p.chunk_tokens);
+  const int ntiles = (n + p.tile_tokens - 1) / p.tile_tokens;
+  const int n_last = n - (ntiles - 1) * p.tile_tokens;
+  for (int i = threadIdx.x; i < p.D; i += blockDim.x) bits[i] = p.in[p.side_off + (int64_t)u * 9 * p.D + i];
+  __syncthreads();
+  const uint8_t* dir = p.in + p.dir_off + (int64_t)c * kDirEntry;
+  const uint64_t off = *reinterpret_cast<const uint64_t*>(dir);
+  const uint32_t size = *reinterpret_cast<const uint32_t*>(dir + 8);
+  const uint32_t resv = *reinterpret_cast<const uint32_t*>(dir + 12);
+  const uint64_t total = *reinterpret_cast<const uint64_t*>(p.in + 168);
+  if (threadIdx.x == 0) {
+    int64_t Pf = 0, Pl = 0;
+    int ok = load_section_bits(p, u, bits, &Pf, &Pl, n_last) ? 1 : 0;
+    const int64_t P = ok ? (ntiles - 1) * Pf + Pl : 0;
+    if (ok && resv != 0) ok = 0;
+    if (ok && P == 0 && size != 0) ok = 0;
+    if (ok && P > 0) {
+      if (off < (uint64_t)p.chunks_off || (off & 15) || off + size > total ||
+          size < 512 + 4 * (uint32_t)ntiles)
+        ok = 0;
+    }
+    s_ok = ok;
+    s_info[0] = Pf; s_info[1] = Pl; s_info[2] = P;
+  }
+  __syncthreads();
+  if (!s_ok) { if (threadIdx.x == 0) set_status(p.ws, p.w, KVTC_ERR_CORRUPT); return; }
+  const int64_t P_full = s_info[0], P_last = s_info[1], P = s_info[2];
+  if (P == 0) return;
+  const uint8_t* rec = p.in + off;
+  // stage the record in LDS when it fits
+  const uint8_t* src = rec;
+  if ((int64_t)size <= stage_cap) {
+    for (uint32_t i = threadIdx.x; i < size / 4; i += blockDim.x)
+      reinterpret_cast<uint32_t*>(stage)[i] = reinterpret_cast<const uint32_t*>(rec)[i];
+    src = stage;
+  }
+  __syncthreads();
+  // frequency table -> cumulative -> slot lookup table
+  if (wave == 0) {
+    const uint16_t* fq = reinterpret_cast<const uint16_t*>(src);
+    uint32_t f[4], s = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { f[k] = fq[4 * lane + k]; s += f[k]; }
+    uint32_t x = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      uint32_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    uint32_t cum = x - s;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { s_cum[4 * lane + k] = cum; cum += f[k]; }
+    if (lane == 63) s_cum[256] = cum;
+  }
+  if (threadIdx.x == 0) {
+    // tile stream offsets inside the record
+    const uint32_t* nwv = reinterpret_cast<const uint32_t*>(src + 512);
+    int64_t at = 512 + 4 * (int64_t)ntiles;
+    for (int t = 0; t < ntiles; ++t) {
+      s_toff[t] = at;
+      uint32_t nw = nwv[t];
+      at += 4 * (int64_t)p.lanes + 2 * (int64_t)nw + ((nw & 1) ? 2 : 0);
+    }
+    s_toff[ntiles] = at;
+  }
+  __syncthreads();
+  if (s_cum[256] != (1u << p.sb) || align16(s_toff[ntiles]) != (int64_t)size) {
+    if (threadIdx.x == 0) set_status(p.ws, p.w, KVTC_ERR_CORRUPT);
+    return;
+  }
+  const uint16_t* fq = reinterpret_cast<const uint16_t*>(src);
+  for (int slot = threadIdx.x; slot < (1 << p.sb); slot += blockDim.x) {
+    int lo = 0, hi = 255;  // symbol s with cum[s] <= slot < cum[s+1]
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (s_cum[mid] <= (uint32_t)slot) lo = mid; else hi = mid - 1;
+    }
+    const uint32_t f = fq[lo];
+    lut[slot] = (uint32_t)lo | ((f - 1u) << 8) | (((uint32_t)slot - s_cum[lo]) << 20);
+  }
+  __syncthreads();
+  const int spw = 64 / p.lanes;
+  const int t = wave * spw + lane / p.lanes;
+  const bool valid = t < ntiles;
+  const int tt = valid ? t : 0;
+  const int64_t Nt = valid ? (t == ntiles - 1 ? P_last : P_full) : 0;
+  const int steps = (int)((Nt + p.lanes - 1) / p.lanes);
+  int steps_max = steps;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) steps_max = max(steps_max, __shfl_xor(steps_max, o, 64));
+  const uint32_t nw = reinterpret_cast<const uint32_t*>(src + 512)[tt];
+  const uint32_t* states = reinterpret_cast<const uint32_t*>(src + s_toff[tt]);
+  const uint16_t* words = reinterpret_cast<const uint16_t*>(src + s_toff[tt] + 4 * p.lanes);
+  uint8_t* out = p.ws + p.w.packed + (int64_t)c * p.w.packed_slot + (int64_t)tt * P_full;
+  const bool ok = rans_decode_stream(states, words, nw, Nt, valid, steps_max, lut, p.sb, p.lanes, out);
+  if (__ballot(!ok)) {
+    if (lane == 0) set_status(p.ws, p.w, KVTC_ERR_CORRUPT);
+  }
+}
+
+hipError_t launch_rans_decode_chunks(const Params& p, hipStream_t s) {
+  int streams = p.tiles_per_chunk;
+  int waves = (streams * p.lanes + 63) / 64;
+  if (waves < 1) waves = 1;
+  // stage records of up to 40 KiB in LDS next to the 2^sb-entry lookup table
+  // (larger records are decoded straight from global memory)
+  const int64_t stage_cap = 40 * 1024;
+  size_t lds = (size_t)(4u << p.sb) + (size_t)stage_cap;
+  hipLaunchKernelGGL(k_rans_dec_chunks, dim3(p.n_chunks), dim3(64 * waves), lds, s, p, stage_cap);
+  return hipGetLastError();
+}
+
+// ---- single-stream parity hooks ---------------------------------------------
+
+__global__ void k_test_rans_encode(const uint8_t* sym, int64_t N, const uint16_t* freq, int sb,
+                                   int lanes, uint32_t* states, uint16_t* words, int64_t cap,
+                                   int64_t* nwords) {
+  __shared__ uint32_t f32v[256];
+  __shared__ EncSym tab[256];
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) f32v[i] = freq[i];
+  __syncthreads();
+  build_enc_table(f32v, tab);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const bool valid = lane < lanes;  // one stream in the first lane group
+  const int steps = (int)((N + lanes - 1) / lanes);
+  int64_t nw = rans_encode_stream(sym, N, valid, steps, tab, sb, lanes, words, cap, states);
+  if (lane == 0) *nwords = nw;
+}
+
+hipError_t launch_test_rans_encode(const uint8_t* sym, int64_t N, const uint16_t* freq, int sb,
+                                   int lanes, uint32_t* states, uint16_t* words, int64_t cap,
+                                   int64_t* nwords, hipStream_t s) {
+  hipLaunchKernelGGL(k_test_rans_encode, dim3(1), dim3(64), 0, s, sym, N, freq, sb, lanes, states,
+                     words, cap, nwords);
+  return hipGetLastError();
+}
+
+__global__ void k_test_rans_decode(const uint32_t* states, const uint16_t* words, int64_t nwords,
+                                   const uint16_t* freq, int sb, int lanes, int64_t N, uint8_t* sym,
+                                   int32_t* status) {
+  extern __shared__ uint32_t lut[];
+  __shared__ uint32_t s_cum[257];
+  const int lane = threadIdx.x & 63;
+  uint32_t f[4], s = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) { f[k] = freq[4 * lane + k]; s += f[k]; }
+  uint32_t x = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  uint32_t cum = x - s;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) { s_cum[4 * lane + k] = cum; cum += f[k]; }
+  if (lane == 63) s_cum[256] = cum;
+  __syncthreads();
+  if (N > 0 && s_cum[256] != (1u << sb)) {
+    if (lane == 0) *status = KVTC_ERR_CORRUPT;
+    return;
+  }
+  for (int slot = threadIdx.x; slot < (1 << sb); slot += blockDim.x) {
+    int lo = 0, hi = 255;
+    while (lo < hi) {
+      int mid = (lo + hi + 1) >> 1;
+      if (s_cum[mid] <= (uint32_t)slot) lo = mid; else hi = mid - 1;
+    }
+    lut[slot] = (uint32_t)lo | (((uint32_t)freq[lo] - 1u) << 8) | (((uint32_t)slot - s_cum[lo]) << 20);
+  }
+  __syncthreads();
+  const bool valid = lane < lanes;
+  const int steps = (int)((N + lanes - 1) / lanes);
+  bool ok = rans_decode_stream(states, words, nwords, N, valid, steps, lut, sb, lanes, sym);
+  if (__ballot(!ok) != 0ull) {
+    if (lane == 0) *status = KVTC_ERR_CORRUPT;
+  } else if (lane == 0) {
+    *status = KVTC_OK;
+  }
+}
+
+hipError_t launch_test_rans_decode(const uint32_t* states, const uint16_t* words, int64_t nwords,
+                                   const uint16_t* freq, int sb, int lanes, int64_t N,
+                                   uint8_t* sym, int32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(k_test_rans_decode, dim3(1), dim3(64), (size_t)(4u << sb), s, states, words,
+                     nwords, freq, sb, lanes, N, sym, status);
+  return hipGetLastError();
+}
+
+__global__ void k_test_freq(const uint32_t* counts, int sb, uint16_t* freq) {
+  __shared__ uint32_t c[256], f[256];
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) c[i] = counts[i];
+  __syncthreads();
+  wave_freq_normalize(c, sb, f);
+  __syncthreads();
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) freq[i] = (uint16_t)f[i];
+}
+
+hipError_t launch_test_freq(const uint32_t* counts, int sb, uint16_t* freq, hipStream_t s) {
+  hipLaunchKernelGGL(k_test_freq, dim3(1), dim3(64), 0, s, counts, sb, freq);
+  return hipGetLastError();
+}
+
+}  // namespace kvtc

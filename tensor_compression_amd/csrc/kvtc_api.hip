@@ -1,0 +1,510 @@
+// C ABI of libkvtc: configuration checks, plans, workspace sizing and the
+// launch sequences of encode and decode.  Kernels live in kernels_*.hip.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "kvtc_internal.h"
+
+using namespace kvtc;
+
+#define HIP_TRY(x)                         \
+  do {                                     \
+    hipError_t e_ = (x);                   \
+    if (e_ != hipSuccess) return KVTC_ERR_HIP; \
+  } while (0)
+
+namespace kvtc {
+
+static int32_t floor_bits(float b) { return (int32_t)floorf(b); }
+
+static bool section_has_r(const kvtc_config& c, int s) {
+  return c.transform == KVTC_WHT && (s == 1 || c.wht_keys);
+}
+
+// Region split ("How the Pipeline Works": sink tokens at the front, a
+// compressed middle, a recent window kept at full fidelity) and the fixed
+// part of the container.
+Layout make_layout(const kvtc_config& c, int32_t T) {
+  Layout lo{};
+  lo.T = T;
+  lo.s0 = c.sink_tokens < T ? c.sink_tokens : T;
+  lo.mid_begin = lo.s0;
+  int32_t e = T - c.recent_tokens;
+  lo.mid_end = e > lo.s0 ? e : lo.s0;
+  lo.T_mid = lo.mid_end - lo.mid_begin;
+  lo.W_eff = T - lo.mid_end;
+  lo.n_sections = c.layers * 2 * c.kv_heads;
+  lo.chunks_per_sec = lo.T_mid > 0 ? (lo.T_mid + c.chunk_tokens - 1) / c.chunk_tokens : 0;
+  lo.n_chunks = lo.n_sections * lo.chunks_per_sec;
+  lo.tiles_per_chunk = c.chunk_tokens / c.tile_tokens;
+  lo.n_r_sections = 0;
+  for (int s = 0; s < 2; ++s)
+    if (section_has_r(c, s)) lo.n_r_sections += c.layers * c.kv_heads;
+  int64_t eb = c.dtype == KVTC_BF16 ? 2 : 4;
+  int64_t D = c.head_dim;
+  lo.side_off = kHeaderBytes;
+  lo.r_off = lo.side_off + (int64_t)lo.n_sections * 9 * D;
+  lo.side_bytes = align16((int64_t)lo.n_sections * 9 * D + (int64_t)lo.n_r_sections * lo.T_mid * 4);
+  lo.raw_off = lo.side_off + lo.side_bytes;
+  lo.raw_bytes = align16(2 * (int64_t)c.layers * c.kv_heads * (lo.s0 + lo.W_eff) * D * eb);
+  lo.dir_off = lo.raw_off + lo.raw_bytes;
+  lo.chunks_off = lo.dir_off + (int64_t)lo.n_chunks * kDirEntry;
+  if (c.transform == KVTC_PCA) {
+    lo.budget_k = (int32_t)floorf(c.bits_k * (float)c.head_dim);
+    lo.budget_v = (int32_t)floorf(c.bits_v * (float)c.head_dim);
+  } else {
+    lo.budget_k = floor_bits(c.bits_k) * c.head_dim;
+    lo.budget_v = floor_bits(c.bits_v) * c.head_dim;
+  }
+  return lo;
+}
+
+static int64_t max_tile_bytes(const kvtc_config& c, int32_t ntok, int32_t budget) {
+  int32_t nz = budget < c.head_dim ? budget : c.head_dim;
+  return ((int64_t)ntok * budget + 7) / 8 + 4 * (int64_t)nz;
+}
+
+static int64_t max_words(int64_t P, const kvtc_config& c) {
+  // each coded symbol grows the state by at most scale_bits bits and each
+  // emitted word removes 16
+  return (P * (c.rans_scale_bits + 1)) / 16 + 2 * (int64_t)c.rans_lanes + 2;
+}
+
+int64_t max_container_bytes(const kvtc_config& c, const Layout& lo) {
+  int64_t total = lo.chunks_off;
+  for (int s = 0; s < 2; ++s) {
+    int32_t budget = s == 0 ? lo.budget_k : lo.budget_v;
+    int64_t per_chunk_full = 0, per_chunk_last = 0;
+    for (int which = 0; which < 2; ++which) {
+      int32_t n = which == 0 ? c.chunk_tokens
+                             : lo.T_mid - (lo.chunks_per_sec - 1) * c.chunk_tokens;
+      if (lo.chunks_per_sec == 0) break;
+      int32_t ntiles = (n + c.tile_tokens - 1) / c.tile_tokens;
+      int64_t rec = 512 + 4 * (int64_t)ntiles;
+      for (int32_t t = 0; t < ntiles; ++t) {
+        int32_t m = n - t * c.tile_tokens;
+        if (m > c.tile_tokens) m = c.tile_tokens;
+        rec += 4 * (int64_t)c.rans_lanes + 2 * max_words(max_tile_bytes(c, m, budget), c) + 2;
+      }
+      (which == 0 ? per_chunk_full : per_chunk_last) = align16(rec);
+    }
+    int64_t secs = (int64_t)c.layers * c.kv_heads;
+    if (lo.chunks_per_sec > 0)
+      total += secs * ((lo.chunks_per_sec - 1) * per_chunk_full + per_chunk_last);
+  }
+  return total;
+}
+
+WsLayout make_ws_layout(const kvtc_config& c, const Layout& lo) {
+  WsLayout w{};
+  int64_t D = c.head_dim;
+  int64_t nsc = (int64_t)lo.n_sections * (lo.chunks_per_sec > 0 ? lo.chunks_per_sec : 1);
+  auto take = [](int64_t& at, int64_t bytes) {
+    int64_t o = at;
+    at += (bytes + 255) & ~(int64_t)255;
+    return o;
+  };
+  int64_t at = 0;
+  w.status = take(at, 16);
+  w.part_sum = take(at, nsc * D * 8);
+  w.part_sq = take(at, nsc * D * 8);
+  w.part_min = take(at, nsc * D * 4);
+  w.part_max = take(at, nsc * D * 4);
+  w.sec_stats = take(at, (int64_t)lo.n_sections * D * 16);
+  w.side_rcp = take(at, (int64_t)lo.n_sections * D * 4);
+  w.side_zero = take(at, (int64_t)lo.n_sections * D * 4);
+  w.side_bits = take(at, (int64_t)lo.n_sections * D);
+  int32_t bmax = lo.budget_k > lo.budget_v ? lo.budget_k : lo.budget_v;
+  int64_t tile_max = max_tile_bytes(c, c.tile_tokens, bmax);
+  w.packed_slot = align16(tile_max * lo.tiles_per_chunk);
+  w.packed = take(at, (int64_t)lo.n_chunks * w.packed_slot);
+  w.tile_words_max = max_words(tile_max, c);
+  w.rec_slot = align16(512 + 4 * (int64_t)lo.tiles_per_chunk +
+                       (int64_t)lo.tiles_per_chunk * (4 * c.rans_lanes + 2 * w.tile_words_max + 4));
+  w.rec = take(at, (int64_t)lo.n_chunks * w.rec_slot);
+  w.rec_size = take(at, (int64_t)lo.n_chunks * 4);
+  w.rec_pos = take(at, (int64_t)lo.n_chunks * 8 + 8);
+  w.total = at;
+  return w;
+}
+
+Params make_params(const PlanImpl& pl, const Layout& lo, const WsLayout& w) {
+  const kvtc_config& c = pl.cfg;
+  Params p{};
+  p.L = c.layers; p.H = c.kv_heads; p.D = c.head_dim; p.dtype = c.dtype;
+  p.transform = c.transform; p.rope_keys = c.rope_keys; p.rope_style = c.rope_style;
+  p.max_bits = c.max_bits; p.sb = c.rans_scale_bits; p.lanes = c.rans_lanes;
+  p.chunk_tokens = c.chunk_tokens; p.tile_tokens = c.tile_tokens;
+  p.basis_per_head = c.basis_per_head; p.wht_keys = c.wht_keys;
+  p.budget_k = lo.budget_k; p.budget_v = lo.budget_v;
+  p.T = lo.T; p.s0 = lo.s0; p.mid_begin = lo.mid_begin; p.mid_end = lo.mid_end;
+  p.T_mid = lo.T_mid; p.W_eff = lo.W_eff; p.n_sections = lo.n_sections;
+  p.chunks_per_sec = lo.chunks_per_sec; p.n_chunks = lo.n_chunks;
+  p.tiles_per_chunk = lo.tiles_per_chunk;
+  p.bits_k_uniform = floor_bits(c.bits_k); p.bits_v_uniform = floor_bits(c.bits_v);
+  p.side_off = lo.side_off; p.r_off = lo.r_off; p.raw_off = lo.raw_off;
+  p.raw_bytes = lo.raw_bytes; p.dir_off = lo.dir_off; p.chunks_off = lo.chunks_off;
+  p.basis_t = pl.basis_t; p.basis = pl.basis; p.rope = pl.rope;
+  // fp32 accumulation of D exact bf16 products (four chained 32-deep MFMA
+  // steps) stays within 8 * 2^-24 * sum|x_j B_ji| in measurements; 16 (bf16)
+  // and 64 (fp32 operands, products rounded too) leave a 2x margin, and
+  // sum|x_j B_ji| <= ||x||_2 ||B_i||_2 bounds the sum by the token norm
+  p.mfma_err = (c.dtype == KVTC_BF16 ? 16.0f : 64.0f) * 0x1p-24f * pl.max_col_norm;
+  p.w = w;
+  return p;
+}
+
+static void put32(uint8_t* p, uint32_t v) { memcpy(p, &v, 4); }
+static void put64(uint8_t* p, uint64_t v) { memcpy(p, &v, 8); }
+
+// Fixed 256-byte header (all fields little-endian); the total size at byte
+// 168 is filled in on the device once the chunk sizes are known.
+void build_header(const PlanImpl& pl, const Layout& lo, uint8_t* h) {
+  const kvtc_config& c = pl.cfg;
+  memset(h, 0, kHeaderBytes);
+  memcpy(h, "KVTC", 4);
+  put32(h + 4, 1);
+  put32(h + 8, kHeaderBytes);
+  put32(h + 16, c.layers); put32(h + 20, c.kv_heads); put32(h + 24, c.head_dim);
+  put32(h + 28, c.dtype); put32(h + 32, c.transform);
+  put32(h + 36, c.sink_tokens); put32(h + 40, c.recent_tokens);
+  memcpy(h + 44, &c.bits_k, 4); memcpy(h + 48, &c.bits_v, 4);
+  put32(h + 52, c.max_bits); put32(h + 56, c.rope_keys); put32(h + 60, c.rope_style);
+  memcpy(h + 64, &c.rope_theta, 8);
+  put32(h + 72, c.rans_scale_bits); put32(h + 76, c.rans_lanes);
+  put32(h + 80, c.chunk_tokens); put32(h + 84, c.tile_tokens);
+  put32(h + 88, c.basis_per_head); put32(h + 92, c.wht_keys);
+  put32(h + 96, lo.T); put32(h + 100, lo.s0); put32(h + 104, lo.mid_begin);
+  put32(h + 108, lo.mid_end); put32(h + 112, lo.n_sections); put32(h + 116, lo.chunks_per_sec);
+  put64(h + 120, lo.side_off); put64(h + 128, lo.side_bytes); put64(h + 136, lo.raw_off);
+  put64(h + 144, lo.raw_bytes); put64(h + 152, lo.dir_off); put64(h + 160, lo.chunks_off);
+  put64(h + 176, pl.fingerprint);
+  put32(h + 184, lo.budget_k); put32(h + 188, lo.budget_v);
+}
+
+}  // namespace kvtc
+
+// ---------------------------------------------------------------------------
+
+static kvtc_status check_config(const kvtc_config* c) {
+  if (!c) return KVTC_ERR_INVALID_ARG;
+  if (c->layers < 1 || c->kv_heads < 1 || c->max_tokens < 1) return KVTC_ERR_INVALID_ARG;
+  if (c->head_dim != 64 && c->head_dim != 128) return KVTC_ERR_UNSUPPORTED;
+  if (c->dtype != KVTC_BF16 && c->dtype != KVTC_FP32) return KVTC_ERR_INVALID_ARG;
+  if (c->transform != KVTC_PCA && c->transform != KVTC_WHT) return KVTC_ERR_INVALID_ARG;
+  if (c->transform == KVTC_PCA && c->dtype == KVTC_FP32 && c->head_dim != 64)
+    return KVTC_ERR_UNSUPPORTED;  // fp32 MFMA operands: the basis is register-resident
+  if (c->sink_tokens < 0 || c->recent_tokens < 0) return KVTC_ERR_INVALID_ARG;
+  if (c->max_bits < 1 || c->max_bits > 8) return KVTC_ERR_INVALID_ARG;
+  if (!(c->bits_k >= 0.0f) || !(c->bits_v >= 0.0f)) return KVTC_ERR_INVALID_ARG;
+  if (c->bits_k > (float)c->max_bits || c->bits_v > (float)c->max_bits) return KVTC_ERR_INVALID_ARG;
+  if (c->transform == KVTC_WHT && (c->bits_k < 2.0f || c->bits_v < 1.0f)) return KVTC_ERR_INVALID_ARG;
+  if (c->rope_style != KVTC_ROPE_HALF && c->rope_style != KVTC_ROPE_INTERLEAVED)
+    return KVTC_ERR_INVALID_ARG;
+  if (c->rope_keys != 0 && c->rope_keys != 1) return KVTC_ERR_INVALID_ARG;
+  if (c->rope_keys && !(c->rope_theta > 1.0)) return KVTC_ERR_INVALID_ARG;
+  if (c->rans_scale_bits < 8 || c->rans_scale_bits > 12) return KVTC_ERR_UNSUPPORTED;
+  if (c->rans_lanes != 16 && c->rans_lanes != 32) return KVTC_ERR_UNSUPPORTED;
+  if (c->tile_tokens < 16 || c->tile_tokens > 256 || (c->tile_tokens % 16)) return KVTC_ERR_UNSUPPORTED;
+  if (c->chunk_tokens < c->tile_tokens || (c->chunk_tokens % c->tile_tokens)) return KVTC_ERR_INVALID_ARG;
+  if (c->chunk_tokens / c->tile_tokens > 16) return KVTC_ERR_UNSUPPORTED;
+  if (c->basis_per_head != 0 && c->basis_per_head != 1) return KVTC_ERR_INVALID_ARG;
+  if (c->wht_keys != 0 && c->wht_keys != 1) return KVTC_ERR_INVALID_ARG;
+  return KVTC_OK;
+}
+
+static size_t plan_layout(const kvtc_config& c, size_t* off_bt, size_t* off_b, size_t* off_rope) {
+  size_t eb = c.dtype == KVTC_BF16 ? 2 : 4;
+  size_t nb = c.transform == KVTC_PCA
+                  ? (size_t)c.layers * 2 * (c.basis_per_head ? c.kv_heads : 1)
+                  : 0;
+  size_t bbytes = nb * c.head_dim * c.head_dim * eb;
+  size_t at = 0;
+  *off_bt = at; at += (bbytes + 255) & ~(size_t)255;
+  *off_b = at; at += (bbytes + 255) & ~(size_t)255;
+  *off_rope = at; at += (size_t)c.max_tokens * (c.head_dim / 2) * sizeof(float2);
+  at = (at + 255) & ~(size_t)255;
+  return at + 256;  // flag word used while the plan is built
+}
+
+extern "C" {
+
+const char* kvtc_status_str(kvtc_status s) {
+  switch (s) {
+    case KVTC_OK: return "KVTC_OK";
+    case KVTC_ERR_INVALID_ARG: return "KVTC_ERR_INVALID_ARG";
+    case KVTC_ERR_UNSUPPORTED: return "KVTC_ERR_UNSUPPORTED";
+    case KVTC_ERR_CAPACITY: return "KVTC_ERR_CAPACITY";
+    case KVTC_ERR_CORRUPT: return "KVTC_ERR_CORRUPT";
+    case KVTC_ERR_NONFINITE: return "KVTC_ERR_NONFINITE";
+    case KVTC_ERR_HIP: return "KVTC_ERR_HIP";
+  }
+  return "KVTC_ERR_UNKNOWN";
+}
+
+kvtc_status kvtc_plan_mem_size(const kvtc_config* cfg, size_t* bytes) {
+  kvtc_status st = check_config(cfg);
+  if (st != KVTC_OK) return st;
+  if (!bytes) return KVTC_ERR_INVALID_ARG;
+  size_t a, b, r;
+  *bytes = plan_layout(*cfg, &a, &b, &r);
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_plan(const kvtc_config* cfg, const float* basis_dev, void* plan_mem,
+                      size_t plan_mem_bytes, hipStream_t stream, kvtc_plan_t* out) {
+  kvtc_status st = check_config(cfg);
+  if (st != KVTC_OK) return st;
+  if (!out || !plan_mem) return KVTC_ERR_INVALID_ARG;
+  if (cfg->transform == KVTC_PCA && !basis_dev) return KVTC_ERR_INVALID_ARG;
+  size_t off_bt, off_b, off_rope;
+  size_t need = plan_layout(*cfg, &off_bt, &off_b, &off_rope);
+  if (plan_mem_bytes < need) return KVTC_ERR_CAPACITY;
+  PlanImpl* p = new (std::nothrow) PlanImpl();
+  if (!p) return KVTC_ERR_HIP;
+  p->cfg = *cfg;
+  p->mem = (uint8_t*)plan_mem;
+  p->basis_t = p->mem + off_bt;
+  p->basis = p->mem + off_b;
+  p->rope = (float2*)(p->mem + off_rope);
+  p->mem_bytes = need;
+  p->n_basis = cfg->transform == KVTC_PCA
+                   ? cfg->layers * 2 * (cfg->basis_per_head ? cfg->kv_heads : 1)
+                   : 0;
+  const int D = cfg->head_dim;
+  // RoPE table: angle t * theta^(-2j/D) in fp64, cos/sin from the C library,
+  // rounded to fp32 ("Why RoPE Has to Be Reversed First").
+  size_t nrope = (size_t)cfg->max_tokens * (D / 2);
+  float2* tab = (float2*)malloc(nrope * sizeof(float2));
+  if (!tab) { delete p; return KVTC_ERR_HIP; }
+  double* inv = (double*)malloc(sizeof(double) * (D / 2));
+  for (int j = 0; j < D / 2; ++j) inv[j] = pow(cfg->rope_theta, -2.0 * (double)j / (double)D);
+  for (int32_t t = 0; t < cfg->max_tokens; ++t)
+    for (int j = 0; j < D / 2; ++j) {
+      double a = (double)t * inv[j];
+      tab[(size_t)t * (D / 2) + j] = make_float2((float)cos(a), (float)sin(a));
+    }
+  free(inv);
+  hipError_t e = hipMemcpyAsync(p->rope, tab, nrope * sizeof(float2), hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  free(tab);
+  if (e != hipSuccess) { delete p; return KVTC_ERR_HIP; }
+  p->fingerprint = 0xcbf29ce484222325ull;
+  p->max_col_norm = 1.0f;
+  if (cfg->transform == KVTC_PCA) {
+    // operand-precision basis in both layouts; non-finite entries raise a
+    // flag word kept at the end of plan memory
+    int32_t* flag = (int32_t*)(p->mem + need - 256);
+    e = hipMemsetAsync(flag, 0, 4, stream);
+    if (e == hipSuccess)
+      e = launch_prep_basis(basis_dev, p->basis_t, p->basis, p->n_basis, D, cfg->dtype, flag, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    int32_t nonfinite = 0;
+    if (e == hipSuccess) e = hipMemcpy(&nonfinite, flag, 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) { delete p; return KVTC_ERR_HIP; }
+    if (nonfinite) { delete p; return KVTC_ERR_NONFINITE; }
+    // fingerprint: FNV-1a over the operand-precision basis bytes, row-major
+    size_t eb = cfg->dtype == KVTC_BF16 ? 2 : 4;
+    size_t nbytes = (size_t)p->n_basis * D * D * eb;
+    uint8_t* hb = (uint8_t*)malloc(nbytes);
+    if (!hb) { delete p; return KVTC_ERR_HIP; }
+    e = hipMemcpy(hb, p->basis, nbytes, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) { free(hb); delete p; return KVTC_ERR_HIP; }
+    uint64_t h = 0xcbf29ce484222325ull;
+    for (size_t i = 0; i < nbytes; ++i) { h ^= hb[i]; h *= 0x100000001b3ull; }
+    // largest column (component) norm, for the coefficient error bound
+    double mx = 0.0;
+    for (int m = 0; m < p->n_basis; ++m)
+      for (int i = 0; i < D; ++i) {
+        double acc = 0.0;
+        for (int j = 0; j < D; ++j) {
+          size_t idx = ((size_t)m * D + j) * D + i;
+          double v;
+          if (cfg->dtype == KVTC_BF16) {
+            uint16_t b16;
+            memcpy(&b16, hb + 2 * idx, 2);
+            uint32_t u32 = (uint32_t)b16 << 16;
+            float f;
+            memcpy(&f, &u32, 4);
+            v = f;
+          } else {
+            float f;
+            memcpy(&f, hb + 4 * idx, 4);
+            v = f;
+          }
+          acc += v * v;
+        }
+        if (acc > mx) mx = acc;
+      }
+    free(hb);
+    p->fingerprint = h;
+    p->max_col_norm = (float)(sqrt(mx) * (1.0 + 1e-6));
+  }
+  *out = (kvtc_plan_t)p;
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_plan_destroy(kvtc_plan_t plan) {
+  if (!plan) return KVTC_ERR_INVALID_ARG;
+  delete (PlanImpl*)plan;
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_plan_fingerprint(kvtc_plan_t plan, uint64_t* fp) {
+  if (!plan || !fp) return KVTC_ERR_INVALID_ARG;
+  *fp = ((PlanImpl*)plan)->fingerprint;
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_workspace_size(kvtc_plan_t plan, int32_t T, size_t* ws_bytes,
+                                size_t* max_container) {
+  if (!plan) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* p = (PlanImpl*)plan;
+  if (T < 0 || T > p->cfg.max_tokens) return KVTC_ERR_INVALID_ARG;
+  Layout lo = make_layout(p->cfg, T);
+  WsLayout w = make_ws_layout(p->cfg, lo);
+  if (ws_bytes) *ws_bytes = (size_t)w.total;
+  if (max_container) *max_container = (size_t)max_container_bytes(p->cfg, lo);
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_encode(kvtc_plan_t plan, const void* k, const void* v, int32_t T, void* out,
+                        size_t cap, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!plan || !out || !ws) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* pl = (PlanImpl*)plan;
+  if (T < 0 || T > pl->cfg.max_tokens) return KVTC_ERR_INVALID_ARG;
+  if (T > 0 && (!k || !v)) return KVTC_ERR_INVALID_ARG;
+  Layout lo = make_layout(pl->cfg, T);
+  WsLayout w = make_ws_layout(pl->cfg, lo);
+  if ((int64_t)ws_bytes < w.total) return KVTC_ERR_CAPACITY;
+  if ((int64_t)cap < lo.chunks_off) return KVTC_ERR_CAPACITY;
+  Params p = make_params(*pl, lo, w);
+  p.k = k; p.v = v; p.out = (uint8_t*)out; p.cap = (int64_t)cap; p.ws = (uint8_t*)ws;
+  uint8_t hdr[kHeaderBytes];
+  build_header(*pl, lo, hdr);
+  HIP_TRY(launch_copy_raw(p, 1, stream));  // also clears the status word
+  if (lo.n_chunks > 0) HIP_TRY(launch_enc_transform(p, 0, stream));
+  HIP_TRY(launch_enc_alloc(p, stream));
+  if (lo.n_chunks > 0) {
+    HIP_TRY(launch_enc_transform(p, 1, stream));
+    HIP_TRY(launch_rans_encode_chunks(p, stream));
+  }
+  HIP_TRY(launch_assemble(p, hdr, stream));
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_decode(kvtc_plan_t plan, const void* in, size_t in_bytes, int32_t T,
+                        void* k_out, void* v_out, int32_t out_dtype, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  if (!plan || !in || !ws) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* pl = (PlanImpl*)plan;
+  if (T < 0 || T > pl->cfg.max_tokens) return KVTC_ERR_INVALID_ARG;
+  if (T > 0 && (!k_out || !v_out)) return KVTC_ERR_INVALID_ARG;
+  if (out_dtype != KVTC_BF16 && out_dtype != KVTC_FP32) return KVTC_ERR_INVALID_ARG;
+  Layout lo = make_layout(pl->cfg, T);
+  WsLayout w = make_ws_layout(pl->cfg, lo);
+  if ((int64_t)ws_bytes < w.total) return KVTC_ERR_CAPACITY;
+  Params p = make_params(*pl, lo, w);
+  p.in = (const uint8_t*)in; p.cap = (int64_t)in_bytes; p.ws = (uint8_t*)ws;
+  p.k_out = k_out; p.v_out = v_out; p.out_dtype = out_dtype;
+  uint8_t hdr[kHeaderBytes];
+  build_header(*pl, lo, hdr);
+  HIP_TRY(launch_dec_check(p, hdr, stream));  // clears, then sets the status word
+  if (lo.n_chunks > 0) {
+    HIP_TRY(launch_rans_decode_chunks(p, stream));
+    HIP_TRY(launch_dec_transform(p, stream));
+  }
+  HIP_TRY(launch_copy_raw(p, 0, stream));
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_result(kvtc_plan_t plan, const void* ws, uint64_t* container_bytes,
+                        int32_t* device_status) {
+  if (!plan || !ws) return KVTC_ERR_INVALID_ARG;
+  uint32_t buf[4];
+  if (hipMemcpy(buf, ws, 16, hipMemcpyDeviceToHost) != hipSuccess) return KVTC_ERR_HIP;
+  uint32_t bits = buf[0];
+  int32_t st = KVTC_OK;
+  if (bits & (1u << KVTC_ERR_NONFINITE)) st = KVTC_ERR_NONFINITE;
+  else if (bits & (1u << KVTC_ERR_CORRUPT)) st = KVTC_ERR_CORRUPT;
+  else if (bits & (1u << KVTC_ERR_CAPACITY)) st = KVTC_ERR_CAPACITY;
+  else if (bits) st = KVTC_ERR_HIP;
+  if (device_status) *device_status = st;
+  if (container_bytes) {
+    uint64_t n;
+    memcpy(&n, &buf[2], 8);
+    *container_bytes = n;
+  }
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_test_section_stats(kvtc_plan_t plan, const void* ws, int32_t T, float* mu,
+                                    float* var, float* cmin, float* cmax) {
+  if (!plan || !ws || !mu || !var || !cmin || !cmax) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* pl = (PlanImpl*)plan;
+  if (T < 0 || T > pl->cfg.max_tokens) return KVTC_ERR_INVALID_ARG;
+  Layout lo = make_layout(pl->cfg, T);
+  WsLayout w = make_ws_layout(pl->cfg, lo);
+  size_t n = (size_t)lo.n_sections * pl->cfg.head_dim;
+  float* h = (float*)malloc(n * 16);
+  if (!h) return KVTC_ERR_HIP;
+  if (hipMemcpy(h, (const uint8_t*)ws + w.sec_stats, n * 16, hipMemcpyDeviceToHost) != hipSuccess) {
+    free(h);
+    return KVTC_ERR_HIP;
+  }
+  for (size_t i = 0; i < n; ++i) {
+    mu[i] = h[4 * i]; var[i] = h[4 * i + 1]; cmin[i] = h[4 * i + 2]; cmax[i] = h[4 * i + 3];
+  }
+  free(h);
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_test_coeffs(kvtc_plan_t plan, const void* k, const void* v, int32_t T,
+                             int32_t sec_begin, int32_t sec_end, float* out, float* r_out,
+                             hipStream_t stream) {
+  if (!plan || !k || !v || !out) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* pl = (PlanImpl*)plan;
+  if (T < 0 || T > pl->cfg.max_tokens) return KVTC_ERR_INVALID_ARG;
+  Layout lo = make_layout(pl->cfg, T);
+  if (sec_begin < 0 || sec_end > lo.n_sections || sec_begin > sec_end) return KVTC_ERR_INVALID_ARG;
+  WsLayout w = make_ws_layout(pl->cfg, lo);
+  Params p = make_params(*pl, lo, w);
+  p.k = k; p.v = v;
+  if (lo.T_mid == 0 || sec_end == sec_begin) return KVTC_OK;
+  HIP_TRY(launch_coeffs(p, sec_begin, sec_end, out, r_out, stream));
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_test_rans_encode(const uint8_t* sym, int64_t N, const uint16_t* freq,
+                                  int32_t scale_bits, int32_t lanes, uint32_t* states,
+                                  uint16_t* words, int64_t words_cap, int64_t* nwords,
+                                  hipStream_t stream) {
+  if ((N > 0 && !sym) || !freq || !states || !words || !nwords || N < 0) return KVTC_ERR_INVALID_ARG;
+  if (scale_bits < 8 || scale_bits > 12 || (lanes != 16 && lanes != 32)) return KVTC_ERR_UNSUPPORTED;
+  HIP_TRY(launch_test_rans_encode(sym, N, freq, scale_bits, lanes, states, words, words_cap,
+                                  nwords, stream));
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_test_rans_decode(const uint32_t* states, const uint16_t* words, int64_t nwords,
+                                  const uint16_t* freq, int32_t scale_bits, int32_t lanes,
+                                  int64_t N, uint8_t* sym, int32_t* status, hipStream_t stream) {
+  if (!states || !freq || !status || (N > 0 && !sym) || N < 0 || nwords < 0) return KVTC_ERR_INVALID_ARG;
+  if (scale_bits < 8 || scale_bits > 12 || (lanes != 16 && lanes != 32)) return KVTC_ERR_UNSUPPORTED;
+  HIP_TRY(launch_test_rans_decode(states, words, nwords, freq, scale_bits, lanes, N, sym, status,
+                                  stream));
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_test_freq_table(const uint32_t* counts, int32_t scale_bits, uint16_t* freq,
+                                 hipStream_t stream) {
+  if (!counts || !freq) return KVTC_ERR_INVALID_ARG;
+  if (scale_bits < 8 || scale_bits > 12) return KVTC_ERR_UNSUPPORTED;
+  HIP_TRY(launch_test_freq(counts, scale_bits, freq, stream));
+  return KVTC_OK;
+}
+
+}  // extern "C"

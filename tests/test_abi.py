@@ -1,0 +1,63 @@
+"""The C ABI (CPU only): the library loads, exports every entry point that
+include/kvtc.h declares, and validates configurations on the host."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tensor_compression_amd import kvtc, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "kvtc.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvtc_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("kvtc_plan", "kvtc_encode", "kvtc_decode", "kvtc_workspace_size",
+                     "kvtc_plan_mem_size", "kvtc_result", "kvtc_plan_destroy", "kvtc_status_str"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = kvtc.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert name in kvtc.EXPORTS, f"binding lacks {name}"
+
+
+def test_status_strings():
+    L = kvtc.lib()
+    for code, name in kvtc.STATUS.items():
+        want = "KVTC_OK" if code == 0 else f"KVTC_ERR_{name}"
+        assert L.kvtc_status_str(code).decode() == want
+
+
+def _mem_size(cfg, max_tokens=4096):
+    c = kvtc.make_config(cfg, max_tokens)
+    n = ctypes.c_size_t(0)
+    st = kvtc.lib().kvtc_plan_mem_size(ctypes.byref(c), ctypes.byref(n))
+    return st, n.value
+
+
+def test_plan_memory_size_and_validation():
+    w = synth.WORKLOADS["llama3_8b"]
+    cfg = synth.oracle_config(w)
+    st, n = _mem_size(cfg, 4096)
+    assert st == kvtc.OK
+    # two bf16 basis copies [32, 2, 128, 128] + fp32 (cos, sin) table [4096, 64]
+    assert n >= 2 * 32 * 2 * 128 * 128 * 2 + 4096 * 64 * 8
+    bad = [dict(cfg, head_dim=96), dict(cfg, max_bits=9), dict(cfg, bits_k=9.0),
+           dict(cfg, rans_lanes=7), dict(cfg, rans_scale_bits=13), dict(cfg, chunk_tokens=1000),
+           dict(cfg, tile_tokens=8), dict(cfg, dtype=5), dict(cfg, layers=0),
+           dict(cfg, rope_theta=0.5)]
+    for b in bad:
+        st, _ = _mem_size(b)
+        assert st in (kvtc.ERR_INVALID_ARG, kvtc.ERR_UNSUPPORTED), b
+    st, _ = _mem_size(cfg, 0)
+    assert st == kvtc.ERR_INVALID_ARG

@@ -1,0 +1,306 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle on the same
+seeded inputs.  Rules are in tests/parity.py."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import parity
+from tensor_compression_amd import kvtc, synth
+from tensor_compression_amd.calibrate import fit_pca_basis
+
+pytestmark = pytest.mark.gpu
+
+
+def _setup(name, tokens=None, layers=None, seed=None, **over):
+    w = synth.WORKLOADS[name]
+    K, V = synth.generate(w, device="cuda", tokens=tokens, layers=layers, seed=seed)
+    T = K.shape[2]
+    cfg = synth.oracle_config(w, layers=K.shape[0], **over)
+    k, v = synth.to_numpy_bits(K), synth.to_numpy_bits(V)
+    basis = None
+    if cfg["transform"] == 0:
+        lo = orc.layout(cfg, T)
+        t0, t1 = (0, T) if w.basis_from == "all" else (lo.mid_begin, max(lo.mid_end, lo.mid_begin + 1))
+        basis = orc.fit_pca_basis(cfg, k, v, t0, min(t1, T))
+    plan = kvtc.Plan(cfg, None if basis is None else torch.from_numpy(basis), max_tokens=max(T, 1))
+    return cfg, T, K, V, k, v, basis, plan
+
+
+def _encode(plan, K, V):
+    T = K.shape[2]
+    ws = plan.workspace(T)
+    data, st = plan.encode(K, V, ws)
+    return data.cpu().numpy().tobytes(), st, ws
+
+
+def _full_parity(cfg, T, K, V, k, v, basis, plan, sections=None, decode_check=True):
+    data, st, ws = _encode(plan, K, V)
+    assert st == kvtc.OK, kvtc.STATUS[st]
+    lo = orc.layout(cfg, T)
+    stats = plan.section_stats(ws, T, lo.n_sections)
+    secs = range(lo.n_sections) if sections is None else sections
+    report = []
+    for u in secs:
+        coef, _ = plan.coeffs(K, V, u, u + 1, lo.T_mid)
+        parity.compare_section(orc, cfg, T, k, v, basis, data, stats, u,
+                               gpu_coef=coef[0].cpu().numpy(), report=report)
+    total_codes = sum(r["codes"] for r in report)
+    boundary = sum(r["boundary_codes"] for r in report)
+    assert boundary <= parity.BOUNDARY_FRACTION * max(total_codes, 1)
+    if decode_check:
+        kd, vd, st2 = plan.decode(torch.frombuffer(bytearray(data), dtype=torch.uint8).cuda(), T, kvtc.FP32)
+        assert st2 == kvtc.OK
+        kd, vd = kd.cpu().numpy(), vd.cpu().numpy()
+        H = cfg["kv_heads"]
+        ref = orc.decode_sections(cfg, data, basis, 0, lo.n_sections, lo.T_mid) if sections is None else None
+        for u in secs:
+            l, s, h = u // (2 * H), (u // H) % 2, u % H
+            if ref is not None:
+                mid_ref = ref[u]
+            else:
+                mid_ref = orc.decode_sections(cfg, data, basis, u, u + 1, lo.T_mid)[0]
+            src = k if s == 0 else v
+            srcf = orc.bf16_bits_to_f32(src).reshape(src.shape) if cfg["dtype"] == 1 else src
+            rms = np.sqrt((srcf[l, h].astype(np.float64) ** 2).mean(axis=0))
+            got = (kd if s == 0 else vd)[l, h, lo.mid_begin: lo.mid_end]
+            parity.compare_decode(got, mid_ref, rms[None, :])
+        # raw windows restored bit-exactly (fp32 output of a bf16 cache widens exactly)
+        for a, b in ((k, kd), (v, vd)):
+            af = orc.bf16_bits_to_f32(a).reshape(a.shape) if cfg["dtype"] == 1 else a
+            assert np.array_equal(af[:, :, : lo.s0], b[:, :, : lo.s0])
+            assert np.array_equal(af[:, :, lo.mid_end:], b[:, :, lo.mid_end:])
+    return data, report
+
+
+# --------------------------------------------------------------------------- stages
+
+def test_freq_table_matches_oracle():
+    rng = np.random.default_rng(0)
+    cases = []
+    for _ in range(150):
+        k = int(rng.integers(1, 257))
+        c = np.zeros(256, np.uint32)
+        c[rng.choice(256, k, replace=False)] = rng.geometric(rng.uniform(0.0005, 0.9), k)
+        cases.append(c)
+    single = np.zeros(256, np.uint32)
+    single[200] = 77
+    cases += [single, np.full(256, 3, np.uint32), np.zeros(256, np.uint32)]
+    for sb in (8, 10, 12):
+        for c in cases:
+            g = kvtc.freq_table(torch.from_numpy(c.astype(np.int32)).cuda(), sb).cpu().numpy().view(np.uint16)
+            assert np.array_equal(g, orc.freq_normalize(c, sb)), (sb, c)
+
+
+@pytest.mark.parametrize("lanes", [16, 32])
+@pytest.mark.parametrize("sb", [8, 12])
+def test_rans_streams_bit_exact(lanes, sb):
+    rng = np.random.default_rng(lanes + sb)
+    for N in (0, 1, 2, lanes - 1, lanes, lanes + 1, 1000, 8192, 12345):
+        for dist in ("gauss", "skew", "uniform", "single"):
+            if dist == "gauss":
+                sym = np.clip(np.rint(rng.standard_normal(N) * 15 + 100), 0, 255).astype(np.uint8)
+            elif dist == "skew":
+                p = np.exp(-np.arange(256) / 6.0)
+                sym = rng.choice(256, N, p=p / p.sum()).astype(np.uint8)
+            elif dist == "uniform":
+                sym = rng.integers(0, 256, N).astype(np.uint8)
+            else:
+                sym = np.full(N, 9, np.uint8)
+            freq = orc.freq_normalize(orc.byte_histogram(sym) if N else np.eye(256, dtype=np.uint32)[9], sb)
+            st_o, wd_o = orc.rans_encode(sym, freq, sb, lanes)
+            ft = torch.from_numpy(freq.view(np.int16)).cuda()
+            st_g, wd_g, n = kvtc.rans_encode(torch.from_numpy(sym).cuda(), ft, sb, lanes)
+            assert n == wd_o.size
+            assert np.array_equal(st_g.cpu().numpy().view(np.uint32), st_o)
+            assert np.array_equal(wd_g.cpu().numpy().view(np.uint16), wd_o)
+            out, status = kvtc.rans_decode(torch.from_numpy(st_o.view(np.int32)).cuda(),
+                                           torch.from_numpy(wd_o.view(np.int16)).cuda(), ft, N, sb, lanes)
+            assert status == kvtc.OK and np.array_equal(out.cpu().numpy(), sym)
+            if wd_o.size > 1:  # a missing word is detected
+                _, status = kvtc.rans_decode(torch.from_numpy(st_o.view(np.int32)).cuda(),
+                                             torch.from_numpy(wd_o[1:].view(np.int16)).cuda(), ft, N, sb, lanes)
+                assert status == kvtc.ERR_CORRUPT
+
+
+# --------------------------------------------------------------------------- pipeline
+
+def test_tiny_workload_parity():
+    """1 layer, 1 head, head_dim 64, 256 tokens, fp32; fp32 MFMA path."""
+    cfg, T, K, V, k, v, basis, plan = _setup("tiny")
+    data, report = _full_parity(cfg, T, K, V, k, v, basis, plan)
+    # the GPU decoder reads the oracle's container as well
+    od = orc.encode(cfg, k, v, basis)
+    kd, vd, st = plan.decode(torch.frombuffer(bytearray(od), dtype=torch.uint8).cuda(), T, kvtc.FP32)
+    assert st == kvtc.OK
+    ko, vo = orc.decode(cfg, od, basis, T)
+    for a, b, src in ((kd.cpu().numpy(), ko, k), (vd.cpu().numpy(), vo, v)):
+        parity.compare_decode(a, b, parity.channel_rms(src))
+
+
+def test_llama_shaped_reduced_parity():
+    """2 layers x 8 heads x 1500 tokens bf16: two chunks per section, a
+    ragged last chunk and tile."""
+    cfg, T, K, V, k, v, basis, plan = _setup("llama3_8b", tokens=1500, layers=2)
+    _full_parity(cfg, T, K, V, k, v, basis, plan)
+
+
+@pytest.mark.parametrize("bits", [1.0, 1.6, 2.0, 4.0])
+def test_budget_sweep_parity(bits):
+    """Qwen3-32B-shaped generator, 1 layer, 2200 tokens, the budget sweep."""
+    cfg, T, K, V, k, v, basis, plan = _setup("qwen3_32b", tokens=2200, layers=1, bits_k=bits,
+                                             bits_v=bits, chunk_tokens=512, tile_tokens=128)
+    _full_parity(cfg, T, K, V, k, v, basis, plan)
+
+
+@pytest.mark.parametrize("wht_keys", [1, 0])
+def test_hadamard_path_parity(wht_keys):
+    cfg, T, K, V, k, v, basis, plan = _setup("hadamard_long", tokens=1300, layers=2, wht_keys=wht_keys)
+    _full_parity(cfg, T, K, V, k, v, basis, plan)
+
+
+def test_interleaved_rope_per_head_basis():
+    cfg, T, K, V, k, v, basis, plan = _setup("llama3_8b", tokens=700, layers=1, rope_style=1,
+                                             basis_per_head=1, chunk_tokens=256, tile_tokens=64,
+                                             rans_lanes=16)
+    _full_parity(cfg, T, K, V, k, v, basis, plan)
+
+
+@pytest.mark.parametrize("T", [0, 1, 20, 132, 133, 147, 148, 149, 1157])
+def test_edge_lengths(T):
+    """Empty, all-raw, one-token and ragged middles (sink 4, recent 128)."""
+    w = synth.WORKLOADS["llama3_8b"]
+    K, V = synth.generate(w, device="cuda", tokens=max(T, 1), layers=1)
+    K, V = K[:, :, :T].contiguous(), V[:, :, :T].contiguous()
+    cfg = synth.oracle_config(w, layers=1, head_dim=128, chunk_tokens=512, tile_tokens=128)
+    k, v = synth.to_numpy_bits(K), synth.to_numpy_bits(V)
+    Kb, Vb = synth.generate(w, device="cpu", tokens=600, layers=1)
+    basis = orc.fit_pca_basis(cfg, synth.to_numpy_bits(Kb), synth.to_numpy_bits(Vb), 4, 472)
+    plan = kvtc.Plan(cfg, torch.from_numpy(basis), max_tokens=2048)
+    if T == 0:
+        data, st, ws = _encode(plan, K, V)
+        assert st == kvtc.OK and data == orc.encode(cfg, k, v, basis)
+        return
+    _full_parity(cfg, T, K, V, k, v, basis, plan)
+
+
+def test_deterministic_container():
+    cfg, T, K, V, k, v, basis, plan = _setup("llama3_8b", tokens=900, layers=1)
+    d1, _, _ = _encode(plan, K, V)
+    d2, _, _ = _encode(plan, K, V)
+    assert d1 == d2
+
+
+def test_damaged_containers_are_refused():
+    cfg, T, K, V, k, v, basis, plan = _setup("llama3_8b", tokens=1200, layers=1)
+    data, st, ws = _encode(plan, K, V)
+    pc = orc.parse_container(data, cfg, T)
+    rec = int(pc["offsets"][0])
+
+    def status(d, n=None, TT=T):
+        t = torch.frombuffer(bytearray(d), dtype=torch.uint8).cuda()
+        shape = (1, cfg["kv_heads"], TT, cfg["head_dim"])
+        ko = torch.empty(shape, dtype=torch.float32, device="cuda")
+        vo = torch.empty(shape, dtype=torch.float32, device="cuda")
+        ws2 = plan.workspace(TT)
+        plan.decode_async(t, len(d) if n is None else n, TT, ko, vo, ws2, kvtc.FP32)
+        torch.cuda.synchronize()
+        return plan.result(ws2)[1]
+
+    assert status(data) == kvtc.OK
+    bad = bytearray(data); bad[1] ^= 0x20
+    assert status(bad) == kvtc.ERR_CORRUPT                 # magic
+    assert status(data, n=len(data) - 16) == kvtc.ERR_CORRUPT  # truncated
+    assert status(data, n=200) == kvtc.ERR_CORRUPT
+    assert status(data, TT=T - 1) == kvtc.ERR_CORRUPT      # header T mismatch
+    bad = bytearray(data); bad[176] ^= 1
+    assert status(bad) == kvtc.ERR_CORRUPT                 # basis fingerprint
+    bad = bytearray(data); bad[rec + 5] ^= 0x10
+    assert status(bad) == kvtc.ERR_CORRUPT                 # frequency table sum
+    bad = bytearray(data); bad[pc["layout"].n_sections * 0 + 256] = 9  # a width above max_bits
+    assert status(bad) == kvtc.ERR_CORRUPT
+    rng = np.random.default_rng(0)
+    caught = 0
+    for pos in rng.integers(rec + 700, rec + int(pc["sizes"][0]) - 8, 12):
+        bad = bytearray(data); bad[pos] ^= 0x5A
+        caught += status(bad) == kvtc.ERR_CORRUPT
+    assert caught >= 9
+    # the oracle agrees on the same damage
+    bad = bytearray(data); bad[rec + 5] ^= 0x10
+    assert orc.decode_status(cfg, bytes(bad), basis, T) == orc.ERR_CORRUPT
+
+
+def test_nonfinite_middle_is_reported():
+    cfg, T, K, V, k, v, basis, plan = _setup("llama3_8b", tokens=600, layers=1)
+    K2 = K.clone()
+    K2[0, 3, 200, 7] = float("nan")
+    _, st, _ = _encode(plan, K2, V)
+    assert st == kvtc.ERR_NONFINITE
+    K3 = K.clone()
+    K3[0, 1, 2, 5] = float("inf")  # sink window: passes through
+    K3[0, 2, T - 3, 6] = float("nan")  # recent window
+    data, st, _ = _encode(plan, K3, V)
+    assert st == kvtc.OK
+    kd, vd, st = plan.decode(torch.frombuffer(bytearray(data), dtype=torch.uint8).cuda(), T, kvtc.BF16)
+    assert st == kvtc.OK
+    assert torch.isinf(kd[0, 1, 2, 5]) and torch.isnan(kd[0, 2, T - 3, 6])
+
+
+def test_bf16_output_within_one_ulp():
+    cfg, T, K, V, k, v, basis, plan = _setup("llama3_8b", tokens=800, layers=1)
+    data, st, _ = _encode(plan, K, V)
+    t = torch.frombuffer(bytearray(data), dtype=torch.uint8).cuda()
+    k32, v32, _ = plan.decode(t, T, kvtc.FP32)
+    k16, v16, _ = plan.decode(t, T, kvtc.BF16)
+    assert torch.equal(k32.to(torch.bfloat16), k16) and torch.equal(v32.to(torch.bfloat16), v16)
+    ko, vo = orc.decode(cfg, data, basis, T, orc.BF16)
+    for g, o, src in ((k16, ko, k), (v16, vo, v)):
+        gf = g.float().cpu().numpy().astype(np.float64)
+        of = orc.bf16_bits_to_f32(o).reshape(o.shape).astype(np.float64)
+        rms = parity.channel_rms(orc.bf16_bits_to_f32(src).reshape(src.shape))
+        # the fp32 results agree to 1e-4 RMS; rounding each to bf16 adds at most one bf16 ulp
+        ulp = np.spacing(np.maximum(np.abs(gf), np.abs(of)).astype(np.float32)).astype(np.float64) * 2 ** 16
+        assert np.all(np.abs(gf - of) <= 1e-4 * rms + ulp)
+
+
+# --------------------------------------------------------------------------- full size
+
+def test_llama3_8b_full_size_sampled():
+    """32 layers x 8 heads x 4096 tokens bf16 at 2 bits/comp, the benchmark's
+    launch configuration; the oracle checks sampled sections."""
+    w = synth.WORKLOADS["llama3_8b"]
+    K, V = synth.generate(w, device="cuda")
+    T = K.shape[2]
+    cfg = synth.oracle_config(w)
+    lo = orc.layout(cfg, T)
+    basis_t = fit_pca_basis(K, V, cfg, lo.mid_begin, lo.mid_end)
+    basis = basis_t.cpu().numpy()
+    plan = kvtc.Plan(cfg, basis_t, max_tokens=T)
+    ws = plan.workspace(T)
+    data_t, st = plan.encode(K, V, ws)
+    assert st == kvtc.OK
+    data = data_t.cpu().numpy().tobytes()
+    stats = plan.section_stats(ws, T, lo.n_sections)
+    k, v = synth.to_numpy_bits(K), synth.to_numpy_bits(V)
+    rng = np.random.default_rng(7)
+    secs = sorted(set([0, 7, 8, 255, 256, 511] + [int(x) for x in rng.integers(0, lo.n_sections, 4)]))
+    kd, vd, st = plan.decode(data_t, T, kvtc.FP32)
+    assert st == kvtc.OK
+    report = []
+    for u in secs:
+        coef, _ = plan.coeffs(K, V, u, u + 1, lo.T_mid)
+        parity.compare_section(orc, cfg, T, k, v, basis, data, stats, u,
+                               gpu_coef=coef[0].cpu().numpy(), report=report)
+        mid_ref = orc.decode_sections(cfg, data, basis, u, u + 1, lo.T_mid)[0]
+        l, s, h = u // (2 * w.kv_heads), (u // w.kv_heads) % 2, u % w.kv_heads
+        src = k if s == 0 else v
+        srcf = orc.bf16_bits_to_f32(src[l, h]).reshape(T, -1)
+        rms = np.sqrt((srcf.astype(np.float64) ** 2).mean(axis=0))
+        got = (kd if s == 0 else vd)[l, h, lo.mid_begin: lo.mid_end].cpu().numpy()
+        parity.compare_decode(got, mid_ref, rms[None, :])
+    codes = sum(r["codes"] for r in report)
+    assert sum(r["boundary_codes"] for r in report) <= parity.BOUNDARY_FRACTION * codes
+    ratio = (K.numel() + V.numel()) * 2 / len(data)
+    assert 5.0 < ratio < 9.0, ratio
