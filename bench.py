@@ -1,0 +1,259 @@
+#!/usr/bin/env python
+"""Benchmark: KVTC-style encode + decode of a KV cache on one MI355X.
+
+One step = kvtc_encode + kvtc_decode of the whole cache (every phase of the
+coded path) with inputs resident in HBM.  Default workload: a
+Llama-3-8B-shaped cache, 32 layers x 8 KV heads x 4096 tokens x head_dim 128,
+bf16, 2 bits per component, sink 4 / recent 128, per-layer PCA basis.  The
+cache is synthetic (seeded low-rank latent + noise, RoPE on keys; see
+tensor_compression_amd/synth.py) and the basis is calibrated on it before
+timing.
+
+Prints one JSON line.  `value` is raw KV bytes / (encode + decode time) in
+GB/s.  `roofline` is the dominant kernel's algorithmic bytes per launch over
+its HIP-event-timed average duration against the 8 TB/s HBM3E peak;
+`path_roofline` does the same for the whole step (algorithmic bytes
+2 x (raw + container)).  `cpu_baseline` times the CPU oracle on a bounded
+slice of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "encode+decode GB/s of raw bf16 KV at 2 bits/comp; ratio; % HBM roofline"
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama3_8b")
+    ap.add_argument("--bits", type=float, default=None, help="bits per component (K and V)")
+    ap.add_argument("--tokens", type=int, default=None)
+    ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--chunk-tokens", type=int, default=1024)
+    ap.add_argument("--tile-tokens", type=int, default=256)
+    ap.add_argument("--cpu-layers", type=int, default=4,
+                    help="layers of the workload the CPU oracle baseline codes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-phase event pass")
+    return ap.parse_args()
+
+
+def layout(cfg, T):
+    s0 = min(cfg["sink_tokens"], T)
+    mid_end = max(s0, T - cfg["recent_tokens"])
+    return s0, mid_end
+
+
+def packed_bytes_total(bits, cfg, T_mid):
+    """Packed payload bytes of all sections from their bit widths [n_sec, D]."""
+    import numpy as np
+    ct, tt = cfg["chunk_tokens"], cfg["tile_tokens"]
+    tiles = []
+    for c0 in range(0, T_mid, ct):
+        n = min(ct, T_mid - c0)
+        for t0 in range(0, n, tt):
+            tiles.append(min(tt, n - t0))
+    total = 0
+    b = bits.astype(np.int64)
+    for m in set(tiles):
+        cnt = tiles.count(m)
+        total += cnt * int((4 * ((m * b + 31) // 32) * (b > 0)).sum())
+    return total
+
+
+def cpu_baseline(w, cfg, K, V, basis, layers):
+    """The oracle as it stands, single-threaded, on the first `layers` layers."""
+    import numpy as np
+
+    import oracle
+    from tensor_compression_amd import synth
+    layers = max(1, min(layers, K.shape[0]))
+    k = synth.to_numpy_bits(K[:layers])
+    v = synth.to_numpy_bits(V[:layers])
+    b = basis[:layers].cpu().numpy()
+    c1 = dict(cfg, layers=layers)
+    oracle.lib()
+    t0 = time.perf_counter()
+    data = oracle.encode(c1, k, v, b)
+    t1 = time.perf_counter()
+    oracle.decode(c1, data, b, K.shape[2], oracle.BF16)
+    t2 = time.perf_counter()
+    raw = k.nbytes + v.nbytes
+    return {
+        "value": raw / (t2 - t0) / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"{layers} of {K.shape[0]} layers ({layers * 2 * K.shape[1]} sections, "
+                  f"{raw} raw bytes): oracle encode {t1 - t0:.2f} s + decode {t2 - t1:.2f} s, "
+                  "single thread, throughput extrapolates linearly in sections",
+        "encode_s": t1 - t0, "decode_s": t2 - t1,
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} (world size {world}) "
+              "is not supported -- sections shard across GPUs without communication, see the "
+              "design notes", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from tensor_compression_amd import kvtc, synth
+    from tensor_compression_amd.calibrate import fit_pca_basis
+
+    kvtc.lib()  # fail loudly if the HIP library is missing
+    torch.cuda.init()
+    w = synth.WORKLOADS[args.workload]
+    over = dict(chunk_tokens=args.chunk_tokens, tile_tokens=args.tile_tokens)
+    if args.bits is not None:
+        over.update(bits_k=args.bits, bits_v=args.bits)
+    K, V = synth.generate(w, device="cuda", tokens=args.tokens, layers=args.layers)
+    L, H, T, D = K.shape
+    cfg = synth.oracle_config(w, layers=L, **over)
+    s0, mid_end = layout(cfg, T)
+    basis = fit_pca_basis(K, V, cfg, s0, mid_end) if cfg["transform"] == 0 else None
+    plan = kvtc.Plan(cfg, basis, max_tokens=T)
+    ws_bytes, cap = plan.sizes(T)
+    ws_e = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    ws_d = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    kd = torch.empty_like(K)
+    vd = torch.empty_like(V)
+    out_dtype = kvtc.BF16 if K.dtype == torch.bfloat16 else kvtc.FP32
+
+    def step():
+        plan.encode_async(K, V, out, ws_e)
+        plan.decode_async(out, cap, T, kd, vd, ws_d, out_dtype)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    nbytes, st_e = plan.result(ws_e)
+    _, st_d = plan.result(ws_d)
+    if st_e != kvtc.OK or st_d != kvtc.OK:
+        raise SystemExit(f"device status: encode {kvtc.STATUS[st_e]}, decode {kvtc.STATUS[st_d]}")
+
+    raw = (K.numel() + V.numel()) * K.element_size()
+    nvals = K.numel() + V.numel()
+
+    # per-phase HIP-event timing, encode and decode of every step separately
+    phases = {}
+    if not args.no_profile:
+        plan.profile(True)
+        for _ in range(args.steps):
+            plan.encode_async(K, V, out, ws_e)
+            for name, ms in plan.profile_read():
+                phases.setdefault(name, []).append(ms)
+            plan.decode_async(out, cap, T, kd, vd, ws_d, out_dtype)
+            for name, ms in plan.profile_read():
+                phases.setdefault(name, []).append(ms)
+        plan.profile(False)
+    ph_ms = {k: float(np.mean(v)) for k, v in phases.items()}
+    t_enc = sum(ph_ms.get(k, 0.0) for k in ("copy_raw", "enc_stats", "enc_alloc", "enc_quant_pack",
+                                             "rans_encode", "assemble"))
+    t_dec = sum(ph_ms.get(k, 0.0) for k in ("dec_check", "rans_decode", "dec_transform",
+                                             "copy_raw_out"))
+
+    # container accounting from the side records (bits) and the header
+    blob_head = out[: 256].cpu().numpy()
+    chunks_off = int(blob_head[160:168].view(np.uint64)[0])
+    side = out[256: 256 + L * 2 * H * 9 * D].cpu().numpy().reshape(L * 2 * H, 9 * D)
+    bits = side[:, :D]
+    T_mid = mid_end - s0
+    P = packed_bytes_total(bits, cfg, T_mid)
+    C_rec = nbytes - chunks_off
+    N_mid = L * 2 * H * T_mid * D
+    e = K.element_size()
+    alg = {  # minimum bytes each phase must move
+        "enc_stats": N_mid * e,
+        "enc_quant_pack": N_mid * e + P,
+        "rans_encode": P + C_rec,
+        "assemble": 2 * C_rec,
+        "rans_decode": C_rec + P,
+        "dec_transform": P + N_mid * e,
+    }
+    dom = max((k for k in alg if k in ph_ms), key=lambda k: ph_ms[k]) if ph_ms else None
+
+    # reconstruction quality on the GPU
+    def nrmse(a, b):
+        a = a.float()
+        b = b.float()
+        return math.sqrt(float(((a - b) ** 2).sum()) / max(float((a ** 2).sum()), 1e-300))
+
+    res = {
+        "metric": METRIC,
+        "value": raw / (ms_per_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if K.dtype == torch.bfloat16 else "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {L} layers x {H} KV heads x {T} tokens x head_dim {D}, "
+                        f"{w.dtype}, {cfg['bits_k']:g} bits/comp, sink {cfg['sink_tokens']}, "
+                        f"recent {cfg['recent_tokens']}, {'PCA' if cfg['transform'] == 0 else 'WHT'}",
+            "layers": L, "kv_heads": H, "tokens": T, "head_dim": D,
+            "bits_per_component": cfg["bits_k"], "chunk_tokens": cfg["chunk_tokens"],
+            "tile_tokens": cfg["tile_tokens"], "rans_lanes": cfg["rans_lanes"],
+            "rans_scale_bits": cfg["rans_scale_bits"],
+        },
+        "raw_bytes": raw,
+        "container_bytes": nbytes,
+        "compression_ratio": raw / nbytes,
+        "bits_per_value": 8.0 * nbytes / nvals,
+        "nrmse_k": nrmse(K, kd),
+        "nrmse_v": nrmse(V, vd),
+        "encode_gbps_events": raw / (t_enc * 1e-3) / 1e9 if t_enc else None,
+        "decode_gbps_events": raw / (t_dec * 1e-3) / 1e9 if t_dec else None,
+        "phases_ms": ph_ms,
+        "path_roofline": {
+            "bound": "hbm", "algorithmic_bytes": 2 * (raw + nbytes),
+            "achieved": 2 * (raw + nbytes) / (ms_per_step * 1e-3) / 1e9,
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": 2 * (raw + nbytes) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        },
+        "wall_s": wall,
+    }
+    if dom:
+        ach = alg[dom] / (ph_ms[dom] * 1e-3) / 1e9
+        res["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBPS,
+                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": None,
+                           "algorithmic_bytes": alg[dom], "avg_ms": ph_ms[dom]}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, cfg, K, V, basis, args.cpu_layers) \
+            if basis is not None else None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

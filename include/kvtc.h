@@ -175,6 +175,22 @@ kvtc_status kvtc_decode(kvtc_plan_t plan, const void* in, size_t in_bytes, int32
 kvtc_status kvtc_result(kvtc_plan_t plan, const void* ws, uint64_t* container_bytes,
                         int32_t* device_status);
 
+/* ---- profiling -------------------------------------------------------- */
+
+/* When on, kvtc_encode and kvtc_decode record a HIP event on the caller's
+ * stream before their first kernel and after each phase (one phase = one
+ * kernel launch of the path, except "copy_raw", "assemble" and
+ * "dec_check", which also clear or set the status word).  Events are created
+ * on first use.  A plan is then no longer safe to share between concurrent
+ * calls. */
+kvtc_status kvtc_profile_enable(kvtc_plan_t plan, int32_t on);
+
+/* Per-phase milliseconds of the last profiled encode or decode on this plan,
+ * in launch order: up to max_n entries into ms[] and names[] (static
+ * strings), the count to *n.  Synchronises on the last event. */
+kvtc_status kvtc_profile_read(kvtc_plan_t plan, int32_t max_n, float* ms, const char** names,
+                              int32_t* n);
+
 /* ---- stage entry points for parity tests (same kernels as the path) ---- */
 
 /* Per-section statistics left in ws by the last kvtc_encode: host arrays of

@@ -230,7 +230,56 @@ static size_t plan_layout(const kvtc_config& c, size_t* off_bt, size_t* off_b, s
   return at + 256;  // flag word used while the plan is built
 }
 
+// Phase markers for kvtc_profile_*: event i is recorded before phase i's
+// launch, the last one after the final phase.
+struct ProfScope {
+  PlanImpl* pl;
+  hipStream_t s;
+  explicit ProfScope(PlanImpl* p, hipStream_t st) : pl(p), s(st) {
+    if (pl->prof_on) {
+      pl->prof_n = 0;
+      (void)hipEventRecord(pl->prof_ev[0], s);
+      pl->prof_n = 1;
+    }
+  }
+  void phase(const char* name) {
+    if (!pl->prof_on || pl->prof_n >= 24) return;
+    pl->prof_name[pl->prof_n - 1] = name;
+    (void)hipEventRecord(pl->prof_ev[pl->prof_n], s);
+    pl->prof_n += 1;
+  }
+};
+
 extern "C" {
+
+kvtc_status kvtc_profile_enable(kvtc_plan_t plan, int32_t on) {
+  if (!plan) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* p = (PlanImpl*)plan;
+  if (on && !p->prof_created) {
+    for (int i = 0; i < 24; ++i)
+      if (hipEventCreate(&p->prof_ev[i]) != hipSuccess) return KVTC_ERR_HIP;
+    p->prof_created = 1;
+  }
+  p->prof_on = on ? 1 : 0;
+  p->prof_n = 0;
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_profile_read(kvtc_plan_t plan, int32_t max_n, float* ms, const char** names,
+                              int32_t* n) {
+  if (!plan || !n) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* p = (PlanImpl*)plan;
+  int32_t cnt = p->prof_n > 1 ? p->prof_n - 1 : 0;
+  if (cnt > 0 && hipEventSynchronize(p->prof_ev[cnt]) != hipSuccess) return KVTC_ERR_HIP;
+  for (int32_t i = 0; i < cnt && i < max_n; ++i) {
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, p->prof_ev[i], p->prof_ev[i + 1]) != hipSuccess) return KVTC_ERR_HIP;
+    if (ms) ms[i] = t;
+    if (names) names[i] = p->prof_name[i];
+  }
+  *n = cnt;
+  return KVTC_OK;
+}
 
 const char* kvtc_status_str(kvtc_status s) {
   switch (s) {
@@ -349,7 +398,10 @@ kvtc_status kvtc_plan(const kvtc_config* cfg, const float* basis_dev, void* plan
 
 kvtc_status kvtc_plan_destroy(kvtc_plan_t plan) {
   if (!plan) return KVTC_ERR_INVALID_ARG;
-  delete (PlanImpl*)plan;
+  PlanImpl* p = (PlanImpl*)plan;
+  if (p->prof_created)
+    for (int i = 0; i < 24; ++i) (void)hipEventDestroy(p->prof_ev[i]);
+  delete p;
   return KVTC_OK;
 }
 
@@ -385,14 +437,23 @@ kvtc_status kvtc_encode(kvtc_plan_t plan, const void* k, const void* v, int32_t 
   p.k = k; p.v = v; p.out = (uint8_t*)out; p.cap = (int64_t)cap; p.ws = (uint8_t*)ws;
   uint8_t hdr[kHeaderBytes];
   build_header(*pl, lo, hdr);
+  ProfScope prof(pl, stream);
   HIP_TRY(launch_copy_raw(p, 1, stream));  // also clears the status word
-  if (lo.n_chunks > 0) HIP_TRY(launch_enc_transform(p, 0, stream));
+  prof.phase("copy_raw");
+  if (lo.n_chunks > 0) {
+    HIP_TRY(launch_enc_transform(p, 0, stream));
+    prof.phase("enc_stats");
+  }
   HIP_TRY(launch_enc_alloc(p, stream));
+  prof.phase("enc_alloc");
   if (lo.n_chunks > 0) {
     HIP_TRY(launch_enc_transform(p, 1, stream));
+    prof.phase("enc_quant_pack");
     HIP_TRY(launch_rans_encode_chunks(p, stream));
+    prof.phase("rans_encode");
   }
   HIP_TRY(launch_assemble(p, hdr, stream));
+  prof.phase("assemble");
   return KVTC_OK;
 }
 
@@ -412,12 +473,17 @@ kvtc_status kvtc_decode(kvtc_plan_t plan, const void* in, size_t in_bytes, int32
   p.k_out = k_out; p.v_out = v_out; p.out_dtype = out_dtype;
   uint8_t hdr[kHeaderBytes];
   build_header(*pl, lo, hdr);
+  ProfScope prof(pl, stream);
   HIP_TRY(launch_dec_check(p, hdr, stream));  // clears, then sets the status word
+  prof.phase("dec_check");
   if (lo.n_chunks > 0) {
     HIP_TRY(launch_rans_decode_chunks(p, stream));
+    prof.phase("rans_decode");
     HIP_TRY(launch_dec_transform(p, stream));
+    prof.phase("dec_transform");
   }
   HIP_TRY(launch_copy_raw(p, 0, stream));
+  prof.phase("copy_raw_out");
   return KVTC_OK;
 }
 

@@ -55,6 +55,12 @@ struct PlanImpl {
   uint64_t fingerprint;
   float max_col_norm;  // largest column norm of the operand-precision basis
   size_t mem_bytes;
+  // profiling (kvtc_profile_*)
+  int32_t prof_on;
+  int32_t prof_n;  // events recorded by the last call
+  hipEvent_t prof_ev[24];
+  const char* prof_name[24];
+  int32_t prof_created;
 };
 
 // Everything a kernel needs about one call, passed by value.

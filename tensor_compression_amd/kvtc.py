@@ -61,6 +61,11 @@ EXPORTS = {
                                    ctypes.c_size_t, ctypes.c_void_p]),
     "kvtc_result": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint64),
                                    ctypes.POINTER(ctypes.c_int32)]),
+    "kvtc_profile_enable": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    "kvtc_profile_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_float),
+                                         ctypes.POINTER(ctypes.c_char_p),
+                                         ctypes.POINTER(ctypes.c_int32)]),
     "kvtc_test_section_stats": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                ctypes.c_void_p]),
@@ -211,6 +216,19 @@ class Plan:
         torch.cuda.current_stream().synchronize()
         _, st = self.result(ws)
         return k, v, st
+
+    # profiling
+    def profile(self, on: bool = True):
+        _check(lib().kvtc_profile_enable(self.handle, 1 if on else 0), "kvtc_profile_enable")
+
+    def profile_read(self):
+        """[(phase name, ms)] of the last encode or decode (synchronises)."""
+        ms = (ctypes.c_float * 24)()
+        names = (ctypes.c_char_p * 24)()
+        n = ctypes.c_int32(0)
+        _check(lib().kvtc_profile_read(self.handle, 24, ms, names, ctypes.byref(n)),
+               "kvtc_profile_read")
+        return [(names[i].decode(), float(ms[i])) for i in range(n.value)]
 
     # parity hooks
     def section_stats(self, ws: torch.Tensor, T: int, n_sections: int):
