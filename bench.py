@@ -154,6 +154,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = e0.elapsed_time(e1) / args.steps
     nbytes, st_e = plan.result(ws_e)
+    refined = plan.exact_recomputed(ws_e)
     _, st_d = plan.result(ws_d)
     if st_e != kvtc.OK or st_d != kvtc.OK:
         raise SystemExit(f"device status: encode {kvtc.STATUS[st_e]}, decode {kvtc.STATUS[st_d]}")
@@ -231,6 +232,7 @@ def main():
         "container_bytes": nbytes,
         "compression_ratio": raw / nbytes,
         "bits_per_value": 8.0 * nbytes / nvals,
+        "exact_recomputed_codes": refined,
         "nrmse_k": nrmse(K, kd),
         "nrmse_v": nrmse(V, vd),
         "encode_gbps_events": raw / (t_enc * 1e-3) / 1e9 if t_enc else None,

@@ -175,6 +175,11 @@ kvtc_status kvtc_decode(kvtc_plan_t plan, const void* in, size_t in_bytes, int32
 kvtc_status kvtc_result(kvtc_plan_t plan, const void* ws, uint64_t* container_bytes,
                         int32_t* device_status);
 
+/* After synchronising the stream of the last encode that used ws: how many
+ * quantisation codes that encode re-computed exactly because the MFMA
+ * coefficient lay within its error bound of a rounding boundary. */
+kvtc_status kvtc_encode_counters(kvtc_plan_t plan, const void* ws, uint64_t* exact_recomputed);
+
 /* ---- profiling -------------------------------------------------------- */
 
 /* When on, kvtc_encode and kvtc_decode record a HIP event on the caller's

@@ -359,6 +359,211 @@ __global__ __launch_bounds__(256) void k_dec_wht(const Params p) {
   }
 }
 
+// ---- head_dim 128, bf16 cache: the bandwidth-oriented decode pass -------------
+// Workgroup per chunk, 4 waves, 64-token sub-tiles.  Dequantisation: wave w
+// takes components [32w, 32w+32) with lane = token, so the bit width, scale
+// and zero point are wave-uniform; the codes come from the packed tile in
+// LDS (double-buffered: the next tile's bytes are loaded into registers while
+// the current one is decoded).  MFMA: wave w owns output channels
+// {16w .. 16w+15} and {64+16w .. 64+16w+15} -- both members of every
+// half-split RoPE pair -- with the basis rows in registers and the token rows
+// of c^ read from LDS.  Results go through an LDS tile to 16-byte stores.
+
+constexpr int kCS = 136;  // LDS row stride (bf16) of the c^ and output tiles
+
+__global__ __launch_bounds__(256) void k_dec128(const Params p) {
+  constexpr int D = 128;
+  const int u = blockIdx.y, ch = blockIdx.x;
+  const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
+  const int t0 = ch * p.chunk_tokens;
+  const int n = min(p.chunk_tokens, p.T_mid - t0);
+  if (n <= 0) return;
+  if (get_status(p.ws, p.w) & (1u << KVTC_ERR_CORRUPT)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
+  const bool rope = (s == 0) && p.rope_keys;
+  uint8_t* dst = reinterpret_cast<uint8_t*>(s ? p.v_out : p.k_out);
+  const int ob = p.out_dtype == KVTC_BF16 ? 2 : 4;
+  const int64_t lh_row0 = ((int64_t)l * p.H + h) * p.T;
+
+  __shared__ uint32_t s_bits[D], s_roww[D + 1];
+  __shared__ float s_zero[D], s_scale[D];
+  __shared__ __attribute__((aligned(16))) uint16_t C[64 * kCS];
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+  // dyn: [output tile 64 x 128 x ob (+pad)][packed tile buffers x 2]
+  uint8_t* O = reinterpret_cast<uint8_t*>(dyn);
+  const int orow = D * ob + 16;  // padded output row bytes
+  uint32_t* pk[2];
+  pk[0] = reinterpret_cast<uint32_t*>(O + 64 * orow);
+  const uint8_t* rec = p.in + p.side_off + (int64_t)u * 9 * D;
+  if (tid < D) {
+    s_bits[tid] = rec[tid];
+    s_zero[tid] = reinterpret_cast<const float*>(rec + D)[tid];
+    s_scale[tid] = reinterpret_cast<const float*>(rec + 5 * D)[tid];
+  }
+  __syncthreads();
+  uint32_t full_words = 0;
+  for (int i = 0; i < D; ++i) full_words += (uint32_t)((p.tile_tokens * (int)s_bits[i] + 31) >> 5);
+  pk[1] = pk[0] + full_words + 4;
+  const uint32_t* slot = reinterpret_cast<const uint32_t*>(
+      p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot);
+  const int ntiles = (n + p.tile_tokens - 1) / p.tile_tokens;
+
+  // basis rows j = 16(w + 4m) + r, components 32kb + 8g .. +7
+  const int64_t bi = (p.basis_per_head ? ((int64_t)(l * 2 + s) * p.H + h) : (int64_t)(l * 2 + s)) * D * D;
+  const uint16_t* B = reinterpret_cast<const uint16_t*>(p.basis) + bi;
+  uint4 bq[2][4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      bq[m][kb] = *reinterpret_cast<const uint4*>(B + (int64_t)((wave + 4 * m) * 16 + r) * D + kb * 32 + 8 * g);
+
+  // packed tile prefetch: up to 36 words per thread (8-bit budget, 256 tokens)
+  constexpr int kPF = 36;
+  uint32_t pf[kPF];
+  auto fetch_tile = [&](int tl) {
+    const int nt = min(p.tile_tokens, n - tl * p.tile_tokens);
+    uint32_t tw = 0;
+    for (int i = 0; i < D; ++i) tw += (uint32_t)((nt * (int)s_bits[i] + 31) >> 5);
+    const uint32_t* srcw = slot + (int64_t)tl * full_words;
+#pragma unroll
+    for (int k = 0; k < kPF; ++k) {
+      const uint32_t i = tid + 256 * k;
+      pf[k] = i < tw ? srcw[i] : 0u;
+    }
+    return tw;
+  };
+  auto commit_tile = [&](int buf, uint32_t tw) {
+#pragma unroll
+    for (int k = 0; k < kPF; ++k) {
+      const uint32_t i = tid + 256 * k;
+      if (i <= tw) pk[buf][i] = i < tw ? pf[k] : 0u;  // one zero word past the end
+    }
+  };
+
+  uint32_t tw_cur = fetch_tile(0);
+  commit_tile(0, tw_cur);
+  for (int tl = 0; tl < ntiles; ++tl) {
+    const int buf = tl & 1;
+    const int ta = tl * p.tile_tokens;
+    const int nt = min(p.tile_tokens, n - ta);
+    uint32_t tw_next = 0;
+    if (tl + 1 < ntiles) tw_next = fetch_tile(tl + 1);
+    // row offsets of this tile
+    if (tid < 64) {
+      const uint32_t w0 = (uint32_t)((nt * (int)s_bits[2 * lane] + 31) >> 5);
+      const uint32_t w1 = (uint32_t)((nt * (int)s_bits[2 * lane + 1] + 31) >> 5);
+      uint32_t x = w0 + w1;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      s_roww[2 * lane] = x - (w0 + w1);
+      s_roww[2 * lane + 1] = x - w1;
+    }
+    __syncthreads();
+    const uint32_t* P = pk[buf];
+    for (int sb0 = 0; sb0 < nt; sb0 += 64) {
+      const int ns = min(64, nt - sb0);
+      // ---- dequantise: wave w, components [32w, 32w+32), lane = token
+      {
+        const int tt = sb0 + lane;  // token within the tile
+        const bool valid = lane < ns;
+#pragma unroll 4
+        for (int c2 = 0; c2 < 32; c2 += 2) {
+          uint32_t packed2 = 0;
+#pragma unroll
+          for (int z = 0; z < 2; ++z) {
+            const int i = wave * 32 + c2 + z;
+            const uint32_t b = s_bits[i];
+            uint32_t q = 0;
+            if (b && valid) {
+              const uint32_t pos = (uint32_t)tt * b;
+              const uint32_t* rw = P + s_roww[i] + (pos >> 5);
+              const uint64_t v = (uint64_t)rw[0] | ((uint64_t)rw[1] << 32);
+              q = (uint32_t)(v >> (pos & 31)) & ((1u << b) - 1u);
+            }
+            const float c = __fmaf_rn((float)q, s_scale[i], s_zero[i]);
+            packed2 |= (uint32_t)f32_to_bf16(c) << (16 * z);
+          }
+          *reinterpret_cast<uint32_t*>(&C[lane * kCS + wave * 32 + c2]) = packed2;
+        }
+      }
+      __syncthreads();
+      // ---- inverse projection
+      f32x4_t acc[4][2];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        acc[kk][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        acc[kk][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const uint4 a = *reinterpret_cast<const uint4*>(&C[(kk * 16 + r) * kCS + kb * 32 + 8 * g]);
+          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            acc[kk][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bq[m][kb]),
+                                                                 acc[kk][m], 0, 0, 0);
+        }
+      }
+      // ---- RoPE on keys, output cast, into the output tile
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tk = kk * 16 + 4 * g + e;  // token within the sub-tile
+          float x0 = acc[kk][0][e], x1 = acc[kk][1][e];
+          if (rope && tk < ns) {
+            const int pos = p.mid_begin + t0 + ta + sb0 + tk;
+            const float2* rr = p.rope + (int64_t)pos * (D / 2);
+            if (p.rope_style == KVTC_ROPE_HALF) {
+              const float2 cs = rr[wave * 16 + r];  // pair (j, j + 64), j = 16w + r
+              const float xb_s = __fmul_rn(x1, cs.y), xb_c = __fmul_rn(x1, cs.x);
+              const float y0 = __fmaf_rn(x0, cs.x, -xb_s);
+              const float y1 = __fmaf_rn(x0, cs.y, xb_c);
+              x0 = y0;
+              x1 = y1;
+            } else {
+              const bool first = (r & 1) == 0;
+              const float o0 = __shfl_xor(x0, 1, 64), o1 = __shfl_xor(x1, 1, 64);
+              const float2 c0 = rr[(wave * 16 + r) >> 1], c1 = rr[(64 + wave * 16 + r) >> 1];
+              const float a0 = first ? x0 : o0, b0 = first ? o0 : x0;
+              const float a1 = first ? x1 : o1, b1 = first ? o1 : x1;
+              x0 = first ? __fmaf_rn(a0, c0.x, -__fmul_rn(b0, c0.y)) : __fmaf_rn(a0, c0.y, __fmul_rn(b0, c0.x));
+              x1 = first ? __fmaf_rn(a1, c1.x, -__fmul_rn(b1, c1.y)) : __fmaf_rn(a1, c1.y, __fmul_rn(b1, c1.x));
+            }
+          }
+          uint8_t* orow_p = O + tk * orow;
+          const int j0 = wave * 16 + r, j1 = 64 + wave * 16 + r;
+          if (ob == 2) {
+            reinterpret_cast<uint16_t*>(orow_p)[j0] = f32_to_bf16(x0);
+            reinterpret_cast<uint16_t*>(orow_p)[j1] = f32_to_bf16(x1);
+          } else {
+            reinterpret_cast<float*>(orow_p)[j0] = x0;
+            reinterpret_cast<float*>(orow_p)[j1] = x1;
+          }
+        }
+      }
+      __syncthreads();
+      // ---- coalesced stores: row bytes D * ob, 16 B per thread per step
+      {
+        const int per_row = D * ob / 16;
+        for (int idx = tid; idx < ns * per_row; idx += 256) {
+          const int tk = idx / per_row, cc = idx % per_row;
+          const int pos = p.mid_begin + t0 + ta + sb0 + tk;
+          uint8_t* drow = dst + (lh_row0 + pos) * (int64_t)D * ob;
+          reinterpret_cast<uint4*>(drow)[cc] = *reinterpret_cast<const uint4*>(O + tk * orow + 16 * cc);
+        }
+      }
+    }
+    if (tl + 1 < ntiles) {
+      commit_tile(buf ^ 1, tw_next);
+      __syncthreads();
+    }
+  }
+}
+
 hipError_t launch_dec_transform(const Params& p, hipStream_t s) {
   dim3 grid(p.chunks_per_sec, p.n_sections), block(256);
   if (p.transform == KVTC_WHT) {
@@ -369,6 +574,12 @@ hipError_t launch_dec_transform(const Params& p, hipStream_t s) {
   const int32_t bmax = p.budget_k > p.budget_v ? p.budget_k : p.budget_v;
   const int32_t nz = bmax < p.D ? bmax : p.D;
   const size_t tile_words = (size_t)(((int64_t)p.tile_tokens * bmax + 31) / 32 + nz) + 4;
+  if (p.D == 128 && p.dtype == KVTC_BF16 && tile_words <= 36 * 256) {
+    const size_t lds = 64 * (size_t)(128 * ob + 16) + 2 * (tile_words + 4) * 4;
+    (void)hipFuncSetAttribute((const void*)k_dec128, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(k_dec128, grid, block, lds, s, p);
+    return hipGetLastError();
+  }
   if (p.D == 128 && p.dtype == KVTC_BF16) {
     size_t lds = 64 * (128 + 8) * 2 + 4 * 16 * 128 * ob + tile_words * 4;
     hipLaunchKernelGGL((k_dec_pca<128, KVTC_BF16>), grid, block, lds, s, p);

@@ -823,6 +823,328 @@ __global__ __launch_bounds__(256) void k_enc_wht(const Params p, int sec0, float
   }
 }
 
+// ---------------------------------------------------------------------------
+// head_dim 128, bf16 cache: the bandwidth-oriented projection pass.
+//
+// A workgroup (4 waves) walks its chunk in 64-token sub-tiles.  Staging:
+// thread (token tid/4, quarter tid%4) loads the channel runs [16q, 16q+16)
+// and [64+16q, 64+16q+16) of its token -- both members of every RoPE pair --
+// undoes RoPE, rounds to bf16 and writes the row into a double-buffered LDS
+// tile; the loads of the next sub-tile are issued before the MFMA phase of
+// the current one.  MFMA: wave w owns components [32w, 32w+32) (its basis
+// rows, 32 VGPRs, stay in registers) and reads the token rows from LDS with
+// the K slice of lane group g = channels 32kb + 8g .. +7.  The result lane
+// (g, r) holds component (2w+m)*16 + r of tokens 16kk + 4g .. +3.
+// ---------------------------------------------------------------------------
+
+constexpr int kXS = 136;  // LDS row stride (bf16) of staged tokens: 16-B aligned, 4-bank shift
+
+template <int MODE>
+__global__ __launch_bounds__(256) void k_enc128(const Params p, int sec0, float* coef_out) {
+  constexpr int D = 128;
+  const int u = blockIdx.y + sec0, ch = blockIdx.x;
+  const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
+  const int t0 = ch * p.chunk_tokens;
+  const int n = min(p.chunk_tokens, p.T_mid - t0);
+  if (n <= 0) return;
+  if (MODE == 1 && (get_status(p.ws, p.w) & (1u << KVTC_ERR_NONFINITE))) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
+  const int st_t = tid >> 2, st_q = tid & 3;
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(s ? p.v : p.k);
+  const bool rope = (s == 0) && p.rope_keys;
+  const int64_t lh_row0 = ((int64_t)l * p.H + h) * p.T;
+  const int64_t bi = basis_index(p, l, s, h) * D * D;
+  const uint16_t* bt = reinterpret_cast<const uint16_t*>(p.basis_t) + bi;
+
+  __shared__ __attribute__((aligned(16))) uint16_t X[2][64 * kXS];
+  __shared__ SideLds sd;
+  extern __shared__ uint32_t tilebuf[];
+
+  uint4 bq[2][4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      bq[m][kb] = *reinterpret_cast<const uint4*>(bt + (int64_t)((2 * wave + m) * 16 + r) * D + kb * 32 + 8 * g);
+
+  // per-lane statistics / side information of the lane's two components
+  double sum[2] = {0.0, 0.0}, sq[2] = {0.0, 0.0};
+  float mn[2] = {INFINITY, INFINITY}, mx[2] = {-INFINITY, -INFINITY};
+  float zr[2] = {0.f, 0.f}, rc[2] = {0.f, 0.f}, qmax[2] = {0.f, 0.f};
+  uint32_t bl[2] = {0u, 0u};
+  uint32_t full_words = 0;
+  uint32_t* slot = nullptr;
+  if constexpr (MODE == 1) {
+    if (tid < D) {
+      const int64_t si = (int64_t)u * D + tid;
+      sd.zero[tid] = reinterpret_cast<const float*>(p.ws + p.w.side_zero)[si];
+      sd.rcp[tid] = reinterpret_cast<const float*>(p.ws + p.w.side_rcp)[si];
+      sd.bits[tid] = p.ws[p.w.side_bits + si];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int i = (2 * wave + m) * 16 + r;
+      zr[m] = sd.zero[i]; rc[m] = sd.rcp[i]; bl[m] = sd.bits[i];
+      qmax[m] = (float)((1u << bl[m]) - 1u);
+    }
+    for (int i = 0; i < D; ++i) full_words += (uint32_t)((p.tile_tokens * (int)sd.bits[i] + 31) >> 5);
+    slot = reinterpret_cast<uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot);
+  }
+
+  // ---- staging registers and helpers
+  uint4 ya0, ya1, yb0, yb1;
+  float4 cs[8];
+  auto load_sub = [&](int sub) {
+    const int tok = sub * 64 + st_t;
+    const bool valid = tok < n;
+    const int pos = p.mid_begin + t0 + tok;
+    ya0 = ya1 = yb0 = yb1 = make_uint4(0, 0, 0, 0);
+    if (valid) {
+      const uint16_t* row = src + (lh_row0 + pos) * D;
+      ya0 = *reinterpret_cast<const uint4*>(row + 16 * st_q);
+      ya1 = *reinterpret_cast<const uint4*>(row + 16 * st_q + 8);
+      yb0 = *reinterpret_cast<const uint4*>(row + 64 + 16 * st_q);
+      yb1 = *reinterpret_cast<const uint4*>(row + 64 + 16 * st_q + 8);
+    }
+    if (rope && valid) {
+      if (p.rope_style == KVTC_ROPE_HALF) {  // pairs [16q, 16q+16)
+        const float4* cr = reinterpret_cast<const float4*>(p.rope + (int64_t)pos * 64 + 16 * st_q);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) cs[k] = cr[k];
+      } else {  // interleaved: pairs [8q, 8q+8) and [32+8q, 32+8q+8)
+        const float4* cl = reinterpret_cast<const float4*>(p.rope + (int64_t)pos * 64 + 8 * st_q);
+        const float4* ch2 = reinterpret_cast<const float4*>(p.rope + (int64_t)pos * 64 + 32 + 8 * st_q);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { cs[k] = cl[k]; cs[4 + k] = ch2[k]; }
+      }
+    }
+  };
+  auto stage_sub = [&](int buf) {
+    float lo[16], hi[16];
+    unpack_bf16x8(ya0, lo); unpack_bf16x8(ya1, lo + 8);
+    unpack_bf16x8(yb0, hi); unpack_bf16x8(yb1, hi + 8);
+    uint4 o[4];
+    if (rope) {
+      if (p.rope_style == KVTC_ROPE_HALF) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float c = (e & 1) ? cs[e >> 1].z : cs[e >> 1].x;
+          const float sn = (e & 1) ? cs[e >> 1].w : cs[e >> 1].y;
+          const float ya = lo[e], yb = hi[e];
+          lo[e] = __fmaf_rn(ya, c, __fmul_rn(yb, sn));
+          hi[e] = __fmaf_rn(yb, c, -__fmul_rn(ya, sn));
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            float* v = half ? hi : lo;
+            const float4 q4 = cs[4 * half + (m >> 1)];
+            const float c = (m & 1) ? q4.z : q4.x;
+            const float sn = (m & 1) ? q4.w : q4.y;
+            const float ya = v[2 * m], yb = v[2 * m + 1];
+            v[2 * m] = __fmaf_rn(ya, c, __fmul_rn(yb, sn));
+            v[2 * m + 1] = __fmaf_rn(yb, c, -__fmul_rn(ya, sn));
+          }
+        }
+      }
+    }
+    o[0] = make_uint4(pack2_bf16(lo[0], lo[1]), pack2_bf16(lo[2], lo[3]), pack2_bf16(lo[4], lo[5]), pack2_bf16(lo[6], lo[7]));
+    o[1] = make_uint4(pack2_bf16(lo[8], lo[9]), pack2_bf16(lo[10], lo[11]), pack2_bf16(lo[12], lo[13]), pack2_bf16(lo[14], lo[15]));
+    o[2] = make_uint4(pack2_bf16(hi[0], hi[1]), pack2_bf16(hi[2], hi[3]), pack2_bf16(hi[4], hi[5]), pack2_bf16(hi[6], hi[7]));
+    o[3] = make_uint4(pack2_bf16(hi[8], hi[9]), pack2_bf16(hi[10], hi[11]), pack2_bf16(hi[12], hi[13]), pack2_bf16(hi[14], hi[15]));
+    uint16_t* xr = &X[buf][st_t * kXS];
+    *reinterpret_cast<uint4*>(xr + 16 * st_q) = o[0];
+    *reinterpret_cast<uint4*>(xr + 16 * st_q + 8) = o[1];
+    *reinterpret_cast<uint4*>(xr + 64 + 16 * st_q) = o[2];
+    *reinterpret_cast<uint4*>(xr + 64 + 16 * st_q + 8) = o[3];
+  };
+
+  const int nsub = (n + 63) / 64;
+  const int subs_per_tile = p.tile_tokens / 64 > 0 ? p.tile_tokens / 64 : 1;
+  uint32_t refined = 0;  // codes re-computed exactly (wave-uniform count)
+  load_sub(0);
+  for (int sub = 0; sub < nsub; ++sub) {
+    const int buf = sub & 1;
+    stage_sub(buf);
+    if (sub + 1 < nsub) load_sub(sub + 1);
+    // packed-tile bookkeeping (tile_tokens is a multiple of 64 on this path)
+    const int tl = (sub * 64) / p.tile_tokens;
+    const int ta = tl * p.tile_tokens;
+    const int nt = min(p.tile_tokens, n - ta);
+    if constexpr (MODE == 1) {
+      if (sub % subs_per_tile == 0) {
+        if (tid < 64) {
+          uint32_t w0 = (uint32_t)((nt * (int)sd.bits[2 * lane] + 31) >> 5);
+          uint32_t w1 = (uint32_t)((nt * (int)sd.bits[2 * lane + 1] + 31) >> 5);
+          uint32_t tot;
+          uint32_t ex = wave_excl_scan(w0 + w1, &tot);
+          sd.row_w[2 * lane] = ex;
+          sd.row_w[2 * lane + 1] = ex + w0;
+          if (lane == 0) sd.row_w[D] = tot;
+        }
+        __syncthreads();
+        for (uint32_t i = tid; i < sd.row_w[D]; i += 256) tilebuf[i] = 0;
+      }
+    }
+    __syncthreads();
+    f32x4_t acc[4][2];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      acc[kk][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      acc[kk][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&X[buf][(kk * 16 + r) * kXS + kb * 32 + 8 * g]);
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          acc[kk][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bq[m][kb]),
+                                                               acc[kk][m], 0, 0, 0);
+      }
+    }
+    if constexpr (MODE == 0) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (sub * 64 + kk * 16 + 4 * g + e < n) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+              const float c = acc[kk][m][e];
+              sum[m] += (double)c;
+              sq[m] = __fma_rn((double)c, (double)c, sq[m]);
+              mn[m] = fminf(mn[m], c);
+              mx[m] = fmaxf(mx[m], c);
+            }
+          }
+    } else if constexpr (MODE == 2) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tk = sub * 64 + kk * 16 + 4 * g + e;
+          if (tk < n) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+              coef_out[((int64_t)(u - sec0) * p.T_mid + t0 + tk) * D + (2 * wave + m) * 16 + r] = acc[kk][m][e];
+          }
+        }
+    } else {
+      // quantise; values within their error of a rounding boundary are
+      // recomputed exactly from the staged row (fp64 sum of exact products)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int tt = sub * 64 + kk * 16 + 4 * g - ta;  // first of the lane's 4 tokens, tile-relative
+        // token norms for the coefficient error bound
+        float ecm[4];
+        {
+          float n2 = 0.f;
+          const uint16_t* xr = &X[buf][(kk * 16 + r) * kXS];
+#pragma unroll
+          for (int c8 = 0; c8 < 4; ++c8) {
+            const uint4 a = *reinterpret_cast<const uint4*>(xr + c8 * 32 + 8 * g);
+            float f[8];
+            unpack_bf16x8(a, f);
+#pragma unroll
+            for (int z = 0; z < 8; ++z) n2 = __fmaf_rn(f[z], f[z], n2);
+          }
+          n2 += __shfl_xor(n2, 16, 64);
+          n2 += __shfl_xor(n2, 32, 64);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ecm[e] = p.mfma_err * __fsqrt_rn(__shfl(n2, 4 * g + e, 64));
+        }
+        uint32_t qv[2] = {0u, 0u};
+        uint32_t flags = 0;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          if (bl[m] == 0) continue;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v = __fmul_rn(__fsub_rn(acc[kk][m][e], zr[m]), rc[m]);
+            const float rv = __builtin_rintf(v);
+            const float q = fminf(fmaxf(rv, 0.0f), qmax[m]);
+            if (tt + e < nt) {
+              qv[m] |= (uint32_t)q << (8 * e);
+              const float ev = __fmaf_rn(ecm[e], rc[m], 3.0f * 0x1p-23f * fmaxf(fabsf(v), 1.0f));
+              if (fabsf(fabsf(__fsub_rn(v, rv)) - 0.5f) < ev) flags |= 1u << (m * 4 + e);
+            }
+          }
+        }
+        uint64_t pend = __ballot(flags != 0);
+        while (pend) {
+          const int L = __ffsll((unsigned long long)pend) - 1;
+          const uint32_t fl = __shfl(flags, L, 64);
+          const int bit = __ffs(fl) - 1;
+          const int mx_ = bit >> 2, ex = bit & 3;
+          ++refined;
+          const int tx = kk * 16 + 4 * (L >> 4) + ex;     // token within the sub-tile
+          const int ix = (2 * wave + mx_) * 16 + (L & 15);  // component
+          const uint32_t xw = *reinterpret_cast<const uint32_t*>(&X[buf][tx * kXS + 2 * lane]);
+          const uint32_t bw = *reinterpret_cast<const uint32_t*>(bt + (int64_t)ix * D + 2 * lane);
+          double part = __fma_rn((double)__uint_as_float(xw << 16), (double)__uint_as_float(bw << 16),
+                                 (double)__uint_as_float(xw & 0xffff0000u) *
+                                     (double)__uint_as_float(bw & 0xffff0000u));
+#pragma unroll
+          for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+          if (lane == L) {
+            const float cex = (float)part;
+            const float v = __fmul_rn(__fsub_rn(cex, sd.zero[ix]), sd.rcp[ix]);
+            const float q = fminf(fmaxf(__builtin_rintf(v), 0.0f), (float)((1u << sd.bits[ix]) - 1u));
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+              if (m == mx_) qv[m] = (qv[m] & ~(0xffu << (8 * ex))) | ((uint32_t)q << (8 * ex));
+            flags &= ~(1u << bit);
+          }
+          pend = __ballot(flags != 0);
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const uint32_t b = bl[m];
+          if (b == 0 || tt >= nt) continue;
+          const uint32_t word = (qv[m] & 0xffu) | (((qv[m] >> 8) & 0xffu) << b) |
+                                (((qv[m] >> 16) & 0xffu) << (2 * b)) | ((qv[m] >> 24) << (3 * b));
+          const uint32_t bitpos = (uint32_t)tt * b;
+          const uint32_t wi = sd.row_w[(2 * wave + m) * 16 + r] + (bitpos >> 5), sh = bitpos & 31;
+          atomicOr(&tilebuf[wi], word << sh);
+          const uint32_t spill = sh + 4 * b > 32 ? word >> (32 - sh) : 0u;
+          if (spill) atomicOr(&tilebuf[wi + 1], spill);
+        }
+      }
+      // flush a finished packed tile
+      if ((sub % subs_per_tile) == subs_per_tile - 1 || sub == nsub - 1) {
+        __syncthreads();
+        uint32_t* dst = slot + (int64_t)tl * full_words;
+        for (uint32_t i = tid; i < sd.row_w[D]; i += 256) dst[i] = tilebuf[i];
+        __syncthreads();
+      }
+    }
+  }
+  if (MODE == 1 && lane == 0 && refined)
+    atomicAdd(reinterpret_cast<uint32_t*>(p.ws + p.w.status) + 1, refined);
+  if constexpr (MODE == 0) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int o = 16; o <= 32; o <<= 1) {
+        sum[m] += __shfl_xor(sum[m], o, 64);
+        sq[m] += __shfl_xor(sq[m], o, 64);
+        mn[m] = fminf(mn[m], __shfl_xor(mn[m], o, 64));
+        mx[m] = fmaxf(mx[m], __shfl_xor(mx[m], o, 64));
+      }
+      if (g == 0) {
+        const int64_t idx = ((int64_t)u * p.chunks_per_sec + ch) * D + (2 * wave + m) * 16 + r;
+        reinterpret_cast<double*>(p.ws + p.w.part_sum)[idx] = sum[m];
+        reinterpret_cast<double*>(p.ws + p.w.part_sq)[idx] = sq[m];
+        reinterpret_cast<float*>(p.ws + p.w.part_min)[idx] = mn[m];
+        reinterpret_cast<float*>(p.ws + p.w.part_max)[idx] = mx[m];
+      }
+    }
+  }
+}
+
 static size_t quant_lds_bytes(const Params& p, size_t tile) {
   if (p.transform == KVTC_WHT) return tile;
   const size_t os = p.dtype == KVTC_BF16 ? 2 : 4;
@@ -845,6 +1167,16 @@ hipError_t launch_enc_transform(const Params& p, int mode, hipStream_t s) {
   if (p.transform == KVTC_WHT) {
     if (mode == 0) hipLaunchKernelGGL(k_enc_wht<0>, grid, block, 0, s, p, 0, (float*)nullptr, (float*)nullptr);
     else hipLaunchKernelGGL(k_enc_wht<1>, grid, block, lds, s, p, 0, (float*)nullptr, (float*)nullptr);
+    return hipGetLastError();
+  }
+  if (p.D == 128 && p.dtype == KVTC_BF16 && (p.tile_tokens % 64) == 0) {
+    if (mode == 0) {
+      hipLaunchKernelGGL(k_enc128<0>, grid, block, 0, s, p, 0, (float*)nullptr);
+    } else {
+      const size_t tl = tile_lds_bytes(p) + 16;
+      (void)hipFuncSetAttribute((const void*)k_enc128<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)tl);
+      hipLaunchKernelGGL(k_enc128<1>, grid, block, tl, s, p, 0, (float*)nullptr);
+    }
     return hipGetLastError();
   }
 #define KVTC_LAUNCH_PCA(D_, DT_)                                                              \
@@ -872,7 +1204,9 @@ hipError_t launch_coeffs(const Params& p, int sec_begin, int sec_end, float* out
     hipLaunchKernelGGL(k_enc_wht<2>, grid, block, 0, s, p, sec_begin, out, r_out);
     return hipGetLastError();
   }
-  if (p.D == 128 && p.dtype == KVTC_BF16)
+  if (p.D == 128 && p.dtype == KVTC_BF16 && (p.tile_tokens % 64) == 0)
+    hipLaunchKernelGGL(k_enc128<2>, grid, block, 0, s, p, sec_begin, out);
+  else if (p.D == 128 && p.dtype == KVTC_BF16)
     hipLaunchKernelGGL((k_enc_pca<128, KVTC_BF16, 2>), grid, block, 0, s, p, sec_begin, out);
   else if (p.D == 64 && p.dtype == KVTC_BF16)
     hipLaunchKernelGGL((k_enc_pca<64, KVTC_BF16, 2>), grid, block, 0, s, p, sec_begin, out);

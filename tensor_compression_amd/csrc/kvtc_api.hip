@@ -148,11 +148,11 @@ Params make_params(const PlanImpl& pl, const Layout& lo, const WsLayout& w) {
   p.side_off = lo.side_off; p.r_off = lo.r_off; p.raw_off = lo.raw_off;
   p.raw_bytes = lo.raw_bytes; p.dir_off = lo.dir_off; p.chunks_off = lo.chunks_off;
   p.basis_t = pl.basis_t; p.basis = pl.basis; p.rope = pl.rope;
-  // fp32 accumulation of D exact bf16 products (four chained 32-deep MFMA
-  // steps) stays within 8 * 2^-24 * sum|x_j B_ji| in measurements; 16 (bf16)
-  // and 64 (fp32 operands, products rounded too) leave a 2x margin, and
+  // fp32 MFMA accumulation of D exact bf16 products (four chained 32-deep
+  // steps) has measured up to 9.2 * 2^-24 * sum|x_j B_ji|; 24 (bf16) and 64
+  // (fp32 operands, whose products round too) leave margin, and
   // sum|x_j B_ji| <= ||x||_2 ||B_i||_2 bounds the sum by the token norm
-  p.mfma_err = (c.dtype == KVTC_BF16 ? 16.0f : 64.0f) * 0x1p-24f * pl.max_col_norm;
+  p.mfma_err = (c.dtype == KVTC_BF16 ? 24.0f : 64.0f) * 0x1p-24f * pl.max_col_norm;
   p.w = w;
   return p;
 }
@@ -504,6 +504,14 @@ kvtc_status kvtc_result(kvtc_plan_t plan, const void* ws, uint64_t* container_by
     memcpy(&n, &buf[2], 8);
     *container_bytes = n;
   }
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_encode_counters(kvtc_plan_t plan, const void* ws, uint64_t* exact_recomputed) {
+  if (!plan || !ws || !exact_recomputed) return KVTC_ERR_INVALID_ARG;
+  uint32_t buf[2];
+  if (hipMemcpy(buf, ws, 8, hipMemcpyDeviceToHost) != hipSuccess) return KVTC_ERR_HIP;
+  *exact_recomputed = buf[1];
   return KVTC_OK;
 }
 

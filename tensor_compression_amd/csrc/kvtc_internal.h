@@ -26,7 +26,7 @@ struct Layout {
 
 // Workspace carve-up (byte offsets from the workspace start).
 struct WsLayout {
-  int64_t status;      // u32 status, u32 pad, u64 container bytes
+  int64_t status;      // u32 status, u32 exact re-computations, u64 container bytes
   int64_t part_sum;    // f64 [n_sections][chunks][D]
   int64_t part_sq;     // f64 [n_sections][chunks][D]
   int64_t part_min;    // f32 [n_sections][chunks][D]

@@ -61,6 +61,8 @@ EXPORTS = {
                                    ctypes.c_size_t, ctypes.c_void_p]),
     "kvtc_result": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint64),
                                    ctypes.POINTER(ctypes.c_int32)]),
+    "kvtc_encode_counters": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.POINTER(ctypes.c_uint64)]),
     "kvtc_profile_enable": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     "kvtc_profile_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32,
                                          ctypes.POINTER(ctypes.c_float),
@@ -191,6 +193,12 @@ class Plan:
         _check(lib().kvtc_result(self.handle, _ptr(ws), ctypes.byref(n), ctypes.byref(st)),
                "kvtc_result")
         return n.value, st.value
+
+    def exact_recomputed(self, ws: torch.Tensor) -> int:
+        n = ctypes.c_uint64(0)
+        _check(lib().kvtc_encode_counters(self.handle, _ptr(ws), ctypes.byref(n)),
+               "kvtc_encode_counters")
+        return n.value
 
     # convenience wrappers (synchronising)
     def encode(self, K: torch.Tensor, V: torch.Tensor, ws: torch.Tensor | None = None):
