@@ -360,208 +360,397 @@ __global__ __launch_bounds__(256) void k_dec_wht(const Params p) {
 }
 
 // ---- head_dim 128, bf16 cache: the bandwidth-oriented decode pass -------------
-// Workgroup per chunk, 4 waves, 64-token sub-tiles.  Dequantisation: wave w
-// takes components [32w, 32w+32) with lane = token, so the bit width, scale
-// and zero point are wave-uniform; the codes come from the packed tile in
-// LDS (double-buffered: the next tile's bytes are loaded into registers while
-// the current one is decoded).  MFMA: wave w owns output channels
-// {16w .. 16w+15} and {64+16w .. 64+16w+15} -- both members of every
-// half-split RoPE pair -- with the basis rows in registers and the token rows
-// of c^ read from LDS.  Results go through an LDS tile to 16-byte stores.
+// One wave per chunk (four chunks of a section per workgroup), 64-token
+// sub-tiles.  The workgroup prologue reads the section's side information,
+// orders the components with codes (b > 0) by bit width -- the contraction
+// runs over this order, so every dequantisation step is wave-uniform in b --
+// and folds the b = 0 components, whose value is their zero point, into a
+// per-channel constant that seeds the accumulators.
+//
+// Dequantisation: lane = token, one component at a time, with the extraction
+// specialised per width; eight components pack into a bf16 K slice and a 4x4
+// exchange of lane groups (permlane swaps) turns "lane group = 16 tokens" into
+// the MFMA operand layout "lane group = 8 components".  MFMA: D^T = B^T C^T
+// with the basis rows (permuted component order) in registers, so the result
+// lane holds eight consecutive channels of one token -- both members of each
+// RoPE pair sit in the same lane -- and leaves with 16-byte stores.
 
-constexpr int kCS = 136;  // LDS row stride (bf16) of the c^ and output tiles
+constexpr int kBS = 136;  // LDS row stride (bf16) of the staged basis
 
-__global__ __launch_bounds__(256) void k_dec128(const Params p) {
+struct DecKInfo {  // per component in the sorted order
+  uint32_t b, idx;
+  float scale, zero;
+};
+
+__device__ __forceinline__ uint32_t lds_u32(const uint32_t* base, uint32_t byte_off) {
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(base) + byte_off);
+}
+
+// 4x4 exchange of (lane group g, register block c): afterwards block c of lane
+// group g holds what block g of lane group c held.
+__device__ __forceinline__ void xpose4(uint32_t (&v)[4][4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      auto r = __builtin_amdgcn_permlane32_swap(v[c][e], v[c + 2][e], false, false);
+      v[c][e] = r[0];
+      v[c + 2][e] = r[1];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; c += 2) {
+      auto r = __builtin_amdgcn_permlane16_swap(v[c][e], v[c + 1][e], false, false);
+      v[c][e] = r[0];
+      v[c + 1][e] = r[1];
+    }
+  }
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 values rounded to bf16 (nearest even) in one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
+// Per-wave part: chunk `ch` of section u with KB K slices of 32 sorted
+// components (entries past the coded components are zero).
+template <int KB, int KBS, int OB>
+__device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, const uint4* sA,
+                                             uint32_t* tb, uint4* kw, const DecKInfo* s_ki,
+                                             const uint8_t* s_rank, const uint32_t* s_b,
+                                             const float* s_const, uint32_t fw, int nnz, float4* brow) {
   constexpr int D = 128;
-  const int u = blockIdx.y, ch = blockIdx.x;
+  const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
   const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
   const int t0 = ch * p.chunk_tokens;
   const int n = min(p.chunk_tokens, p.T_mid - t0);
   if (n <= 0) return;
-  if (get_status(p.ws, p.w) & (1u << KVTC_ERR_CORRUPT)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
   const bool rope = (s == 0) && p.rope_keys;
-  uint8_t* dst = reinterpret_cast<uint8_t*>(s ? p.v_out : p.k_out);
-  const int ob = p.out_dtype == KVTC_BF16 ? 2 : 4;
+  const bool half_style = p.rope_style == KVTC_ROPE_HALF;
   const int64_t lh_row0 = ((int64_t)l * p.H + h) * p.T;
+  // the (layer, head) slab of the output as a buffer resource: stores of
+  // lanes past the section get an offset at the slab end and are dropped by
+  // the range check, so every store instruction is issued unconditionally
+  uint8_t* slab = reinterpret_cast<uint8_t*>(s ? p.v_out : p.k_out) + lh_row0 * D * OB;
+  const int32_t slab_bytes = p.T * D * OB;
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(slab, 0, slab_bytes, 0x00020000);
+  const uint32_t* slot = reinterpret_cast<const uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot);
 
-  __shared__ uint32_t s_bits[D], s_roww[D + 1];
-  __shared__ float s_zero[D], s_scale[D];
-  __shared__ __attribute__((aligned(16))) uint16_t C[64 * kCS];
-  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
-  // dyn: [output tile 64 x 128 x ob (+pad)][packed tile buffers x 2]
-  uint8_t* O = reinterpret_cast<uint8_t*>(dyn);
-  const int orow = D * ob + 16;  // padded output row bytes
-  uint32_t* pk[2];
-  pk[0] = reinterpret_cast<uint32_t*>(O + 64 * orow);
-  const uint8_t* rec = p.in + p.side_off + (int64_t)u * 9 * D;
-  if (tid < D) {
-    s_bits[tid] = rec[tid];
-    s_zero[tid] = reinterpret_cast<const float*>(rec + D)[tid];
-    s_scale[tid] = reinterpret_cast<const float*>(rec + 5 * D)[tid];
-  }
-  __syncthreads();
-  uint32_t full_words = 0;
-  for (int i = 0; i < D; ++i) full_words += (uint32_t)((p.tile_tokens * (int)s_bits[i] + 31) >> 5);
-  pk[1] = pk[0] + full_words + 4;
-  const uint32_t* slot = reinterpret_cast<const uint32_t*>(
-      p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot);
-  const int ntiles = (n + p.tile_tokens - 1) / p.tile_tokens;
-
-  // basis rows j = 16(w + 4m) + r, components 32kb + 8g .. +7
-  const int64_t bi = (p.basis_per_head ? ((int64_t)(l * 2 + s) * p.H + h) : (int64_t)(l * 2 + s)) * D * D;
-  const uint16_t* B = reinterpret_cast<const uint16_t*>(p.basis) + bi;
-  uint4 bq[2][4];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      bq[m][kb] = *reinterpret_cast<const uint4*>(B + (int64_t)((wave + 4 * m) * 16 + r) * D + kb * 32 + 8 * g);
-
-  // packed tile prefetch: up to 36 words per thread (8-bit budget, 256 tokens)
-  constexpr int kPF = 36;
-  uint32_t pf[kPF];
-  auto fetch_tile = [&](int tl) {
-    const int nt = min(p.tile_tokens, n - tl * p.tile_tokens);
-    uint32_t tw = 0;
-    for (int i = 0; i < D; ++i) tw += (uint32_t)((nt * (int)s_bits[i] + 31) >> 5);
-    const uint32_t* srcw = slot + (int64_t)tl * full_words;
-#pragma unroll
-    for (int k = 0; k < kPF; ++k) {
-      const uint32_t i = tid + 256 * k;
-      pf[k] = i < tw ? srcw[i] : 0u;
-    }
-    return tw;
+  // RoPE table rows (cos/sin of the first token of each 16-token group) of
+  // the next sub-tile, loaded a sub-tile ahead: lane l fetches 32 bytes of
+  // row l / 16 (sub-tiles are contiguous in tokens, tiles hold whole
+  // sub-tiles)
+  float4 nrow[2];
+  auto fetch_rows = [&](int tok0) {
+    const int row = min(p.mid_begin + t0 + tok0 + 16 * (lane >> 4), p.T - 1);
+    const float4* src = reinterpret_cast<const float4*>(p.rope + (int64_t)row * 64) + 2 * (lane & 15);
+    nrow[0] = src[0];
+    nrow[1] = src[1];
   };
-  auto commit_tile = [&](int buf, uint32_t tw) {
-#pragma unroll
-    for (int k = 0; k < kPF; ++k) {
-      const uint32_t i = tid + 256 * k;
-      if (i <= tw) pk[buf][i] = i < tw ? pf[k] : 0u;  // one zero word past the end
-    }
-  };
+  fetch_rows(0);
 
-  uint32_t tw_cur = fetch_tile(0);
-  commit_tile(0, tw_cur);
-  for (int tl = 0; tl < ntiles; ++tl) {
-    const int buf = tl & 1;
-    const int ta = tl * p.tile_tokens;
+  for (int ta = 0; ta < n; ta += p.tile_tokens) {
     const int nt = min(p.tile_tokens, n - ta);
-    uint32_t tw_next = 0;
-    if (tl + 1 < ntiles) tw_next = fetch_tile(tl + 1);
-    // row offsets of this tile
-    if (tid < 64) {
-      const uint32_t w0 = (uint32_t)((nt * (int)s_bits[2 * lane] + 31) >> 5);
-      const uint32_t w1 = (uint32_t)((nt * (int)s_bits[2 * lane + 1] + 31) >> 5);
+    // row offsets of this tile (natural order, scanned), stored by sorted
+    // position together with the width and the dequantisation constants;
+    // components without codes keep all-zero entries
+    uint32_t tw;
+    {
+      const uint32_t b0 = s_b[2 * lane], b1 = s_b[2 * lane + 1];
+      const uint32_t w0 = (uint32_t)(nt * (int)b0 + 31) >> 5, w1 = (uint32_t)(nt * (int)b1 + 31) >> 5;
       uint32_t x = w0 + w1;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const uint32_t y = __shfl_up(x, o, 64);
         if (lane >= o) x += y;
       }
-      s_roww[2 * lane] = x - (w0 + w1);
-      s_roww[2 * lane + 1] = x - w1;
+      tw = __shfl(x, 63, 64);
+      const uint32_t ex = x - (w0 + w1);
+      const uint32_t r0 = s_rank[2 * lane], r1 = s_rank[2 * lane + 1];
+      const DecKInfo i0 = s_ki[r0], i1 = s_ki[r1];
+      kw[r0] = b0 ? make_uint4(b0, 4u * ex, __float_as_uint(i0.scale), __float_as_uint(i0.zero)) : make_uint4(0, 0, 0, 0);
+      kw[r1] = b1 ? make_uint4(b1, 4u * (ex + w0), __float_as_uint(i1.scale), __float_as_uint(i1.zero)) : make_uint4(0, 0, 0, 0);
     }
-    __syncthreads();
-    const uint32_t* P = pk[buf];
-    for (int sb0 = 0; sb0 < nt; sb0 += 64) {
-      const int ns = min(64, nt - sb0);
-      // ---- dequantise: wave w, components [32w, 32w+32), lane = token
-      {
-        const int tt = sb0 + lane;  // token within the tile
-        const bool valid = lane < ns;
-#pragma unroll 4
-        for (int c2 = 0; c2 < 32; c2 += 2) {
-          uint32_t packed2 = 0;
+    // stage the packed tile (tile stride fw words in the slot)
+    {
+      const uint32_t* src = slot + (int64_t)(ta / p.tile_tokens) * fw;
+      if ((fw & 3u) == 0) {
+        const uint32_t n4 = tw >> 2;
+        for (uint32_t i = lane; i < n4; i += 64)
+          reinterpret_cast<uint4*>(tb)[i] = reinterpret_cast<const uint4*>(src)[i];
+        for (uint32_t i = 4 * n4 + lane; i < tw; i += 64) tb[i] = src[i];
+      } else {
+        for (uint32_t i = lane; i < tw; i += 64) tb[i] = src[i];
+      }
+      if (lane < 4) tb[tw + lane] = 0u;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+
+    for (int sub = 0; sub * 64 < nt; ++sub) {
+      brow[2 * lane] = nrow[0];
+      brow[2 * lane + 1] = nrow[1];
+      fetch_rows(ta + sub * 64 + 64);
+      // cos/sin of this lane's RoPE pairs, by angle addition: token
+      // base + r with base = the first token of the 16-token group, so
+      // cs(base + r) = cs(base) (x) cs(r).  The base row is one table row per
+      // load (shared by the 16 tokens), cs(r) comes from table rows 0..15.
+      // Rows past the section are clamped (their results are not stored).
+      // float4 (two pairs) x of this lane's pairs in half hf of a table row:
+      // half-split style pairs 32 hf + 8 g + 2 x, +1; interleaved style pairs
+      // 16 (hf + 2 (x >> 1)) + 4 g + 2 (x & 1), +1
+      auto pair_at = [&](int hf, int x) {
+        return half_style ? (32 * hf + 8 * g) / 2 + x : 8 * (hf + 2 * (x >> 1)) + 2 * g + (x & 1);
+      };
+      auto load_pairs = [&](int row, int hf, float4 (&c)[4]) {
+        const float4* rr = reinterpret_cast<const float4*>(p.rope + (int64_t)row * 64);
 #pragma unroll
-          for (int z = 0; z < 2; ++z) {
-            const int i = wave * 32 + c2 + z;
-            const uint32_t b = s_bits[i];
-            uint32_t q = 0;
-            if (b && valid) {
-              const uint32_t pos = (uint32_t)tt * b;
-              const uint32_t* rw = P + s_roww[i] + (pos >> 5);
-              const uint64_t v = (uint64_t)rw[0] | ((uint64_t)rw[1] << 32);
-              q = (uint32_t)(v >> (pos & 31)) & ((1u << b) - 1u);
-            }
-            const float c = __fmaf_rn((float)q, s_scale[i], s_zero[i]);
-            packed2 |= (uint32_t)f32_to_bf16(c) << (16 * z);
+        for (int x = 0; x < 4; ++x) c[x] = rr[pair_at(hf, x)];
+      };
+      // ---- dequantise: lane = token sub*64 + lane of the tile.  Branch-free
+      // per component (entries past the coded components are all zero and
+      // yield 0), so the table reads can be issued ahead of their use.
+      uint32_t cur[KB > 0 ? KB : 1][4][4];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (32 * kb + 8 * c >= nnz) {  // eight components without codes
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) cur[kb][c][q2] = 0u;
+            continue;
           }
-          *reinterpret_cast<uint32_t*>(&C[lane * kCS + wave * 32 + c2]) = packed2;
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) {
+            float v[2];
+#pragma unroll
+            for (int z = 0; z < 2; ++z) {
+              const uint4 ki = kw[32 * kb + 8 * c + 2 * q2 + z];
+              const uint32_t b = __builtin_amdgcn_readfirstlane(ki.x);
+              const uint32_t seg = __builtin_amdgcn_readfirstlane(ki.y) + 8u * b * (uint32_t)sub;
+              const uint32_t bp = __umul24((uint32_t)lane, b);
+              const uint32_t off = seg + ((bp >> 5) << 2);
+              const uint32_t lo = lds_u32(tb, off), hi = lds_u32(tb, off + 4);
+              const uint32_t q = __builtin_amdgcn_alignbit(hi, lo, bp) & ((1u << b) - 1u);
+              v[z] = __fmaf_rn((float)q, __uint_as_float(ki.z), __uint_as_float(ki.w));
+            }
+            cur[kb][c][q2] = pk_bf16(v[0], v[1]);
+          }
         }
+        xpose4(cur[kb]);
       }
-      __syncthreads();
-      // ---- inverse projection
-      f32x4_t acc[4][2];
+      // ---- MFMA, RoPE, store: two channel halves, four 16-token groups each
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        acc[kk][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        acc[kk][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int hf = 0; hf < 2; ++hf) {
+        uint4 A[4][KB > 0 ? KB : 1];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const uint4 a = *reinterpret_cast<const uint4*>(&C[(kk * 16 + r) * kCS + kb * 32 + 8 * g]);
-          const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
+        for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-          for (int m = 0; m < 2; ++m)
-            acc[kk][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bq[m][kb]),
-                                                                 acc[kk][m], 0, 0, 0);
-        }
-      }
-      // ---- RoPE on keys, output cast, into the output tile
+          for (int kb = 0; kb < KB; ++kb) A[mi][kb] = sA[((hf * 4 + mi) * KBS + kb) * 64 + lane];
+        float4 rot[4];  // cs(r) of this lane's pairs of the half
+        load_pairs(min(r, p.T - 1), hf, rot);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+        for (int kk = 0; kk < 4; ++kk) {
+          // keep each step's table reads and temporaries inside the step
+          __builtin_amdgcn_sched_barrier(0);
+          float4 base[4];  // cs of the group's first token
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tk = kk * 16 + 4 * g + e;  // token within the sub-tile
-          float x0 = acc[kk][0][e], x1 = acc[kk][1][e];
-          if (rope && tk < ns) {
-            const int pos = p.mid_begin + t0 + ta + sb0 + tk;
-            const float2* rr = p.rope + (int64_t)pos * (D / 2);
-            if (p.rope_style == KVTC_ROPE_HALF) {
-              const float2 cs = rr[wave * 16 + r];  // pair (j, j + 64), j = 16w + r
-              const float xb_s = __fmul_rn(x1, cs.y), xb_c = __fmul_rn(x1, cs.x);
-              const float y0 = __fmaf_rn(x0, cs.x, -xb_s);
-              const float y1 = __fmaf_rn(x0, cs.y, xb_c);
-              x0 = y0;
-              x1 = y1;
+          for (int x = 0; x < 4; ++x) base[x] = brow[kk * 32 + pair_at(hf, x)];
+          float4 c4p[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const float4 bq = base[x], rq = rot[x];
+            c4p[x] = make_float4(__fmaf_rn(bq.x, rq.x, -__fmul_rn(bq.y, rq.y)), __fmaf_rn(bq.y, rq.x, __fmul_rn(bq.x, rq.y)),
+                                 __fmaf_rn(bq.z, rq.z, -__fmul_rn(bq.w, rq.w)), __fmaf_rn(bq.w, rq.z, __fmul_rn(bq.z, rq.w)));
+          }
+          const int tok = sub * 64 + kk * 16 + r;  // tile-relative
+          const bool valid = tok < nt;
+          const int pos = p.mid_begin + t0 + ta + tok;
+          f32x4_t acc[4];
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi) {
+            const int pp = hf + 2 * (mi >> 1), a = mi & 1;
+            const float4 c4 = *reinterpret_cast<const float4*>(&s_const[32 * pp + 8 * g + 4 * a]);
+            acc[mi] = f32x4_t{c4.x, c4.y, c4.z, c4.w};
+          }
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, make_uint4(cur[kb][kk][0], cur[kb][kk][1], cur[kb][kk][2], cur[kb][kk][3]));
+#pragma unroll
+            for (int mi = 0; mi < 4; ++mi)
+              acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[mi][kb]), bop, acc[mi], 0, 0, 0);
+          }
+          if (rope) {
+            if (half_style) {
+              // pair j = 32 hf + 8 g + 4 a + e: x_a = acc[a][e], x_b = acc[2 + a][e]
+#pragma unroll
+              for (int a = 0; a < 2; ++a) {
+                const float4 c01 = c4p[2 * a], c23 = c4p[2 * a + 1];
+                const float cc[4] = {c01.x, c01.z, c23.x, c23.z}, ss[4] = {c01.y, c01.w, c23.y, c23.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const float xa = acc[a][e], xb = acc[2 + a][e];
+                  acc[a][e] = __fmaf_rn(xa, cc[e], -__fmul_rn(xb, ss[e]));
+                  acc[2 + a][e] = __fmaf_rn(xa, ss[e], __fmul_rn(xb, cc[e]));
+                }
+              }
             } else {
-              const bool first = (r & 1) == 0;
-              const float o0 = __shfl_xor(x0, 1, 64), o1 = __shfl_xor(x1, 1, 64);
-              const float2 c0 = rr[(wave * 16 + r) >> 1], c1 = rr[(64 + wave * 16 + r) >> 1];
-              const float a0 = first ? x0 : o0, b0 = first ? o0 : x0;
-              const float a1 = first ? x1 : o1, b1 = first ? o1 : x1;
-              x0 = first ? __fmaf_rn(a0, c0.x, -__fmul_rn(b0, c0.y)) : __fmaf_rn(a0, c0.y, __fmul_rn(b0, c0.x));
-              x1 = first ? __fmaf_rn(a1, c1.x, -__fmul_rn(b1, c1.y)) : __fmaf_rn(a1, c1.y, __fmul_rn(b1, c1.x));
+              // pairs (e, e + 1) of tile (p, a): index 16 p + 4 g + 2 a + e / 2
+#pragma unroll
+              for (int mi = 0; mi < 4; ++mi) {
+                const float4 c4 = c4p[mi];
+                const float cc[2] = {c4.x, c4.z}, ss[2] = {c4.y, c4.w};
+#pragma unroll
+                for (int e2 = 0; e2 < 2; ++e2) {
+                  const float xa = acc[mi][2 * e2], xb = acc[mi][2 * e2 + 1];
+                  acc[mi][2 * e2] = __fmaf_rn(xa, cc[e2], -__fmul_rn(xb, ss[e2]));
+                  acc[mi][2 * e2 + 1] = __fmaf_rn(xa, ss[e2], __fmul_rn(xb, cc[e2]));
+                }
+              }
             }
           }
-          uint8_t* orow_p = O + tk * orow;
-          const int j0 = wave * 16 + r, j1 = 64 + wave * 16 + r;
-          if (ob == 2) {
-            reinterpret_cast<uint16_t*>(orow_p)[j0] = f32_to_bf16(x0);
-            reinterpret_cast<uint16_t*>(orow_p)[j1] = f32_to_bf16(x1);
-          } else {
-            reinterpret_cast<float*>(orow_p)[j0] = x0;
-            reinterpret_cast<float*>(orow_p)[j1] = x1;
+          {
+            const int32_t vo = valid ? (int32_t)(((int64_t)pos * D) * OB) : slab_bytes;
+#pragma unroll
+            for (int pq = 0; pq < 2; ++pq) {
+              const int pp = hf + 2 * pq;
+              const f32x4_t x0 = acc[2 * pq], x1 = acc[2 * pq + 1];
+              const int c0 = 32 * pp + 8 * g;
+              if constexpr (OB == 2) {
+                const u32x4_t o = {pk_bf16(x0[0], x0[1]), pk_bf16(x0[2], x0[3]), pk_bf16(x1[0], x1[1]), pk_bf16(x1[2], x1[3])};
+                __builtin_amdgcn_raw_buffer_store_b128(o, orsrc, vo + 2 * c0, 0, 0);
+              } else {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x0), orsrc, vo + 4 * c0, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x1), orsrc, vo + 4 * c0 + 16, 0, 0);
+              }
+            }
           }
         }
       }
-      __syncthreads();
-      // ---- coalesced stores: row bytes D * ob, 16 B per thread per step
-      {
-        const int per_row = D * ob / 16;
-        for (int idx = tid; idx < ns * per_row; idx += 256) {
-          const int tk = idx / per_row, cc = idx % per_row;
-          const int pos = p.mid_begin + t0 + ta + sb0 + tk;
-          uint8_t* drow = dst + (lh_row0 + pos) * (int64_t)D * ob;
-          reinterpret_cast<uint4*>(drow)[cc] = *reinterpret_cast<const uint4*>(O + tk * orow + 16 * cc);
-        }
-      }
-    }
-    if (tl + 1 < ntiles) {
-      commit_tile(buf ^ 1, tw_next);
-      __syncthreads();
     }
   }
+}
+
+// KBMAX = 3 serves sections with at most 96 coded components, KBMAX = 4 the
+// rest; each instantiation leaves the other's sections alone.
+template <int KBMAX>
+__global__ __launch_bounds__(256, 2) void k_dec_pca128(const Params p) {
+  constexpr int D = 128;
+  const int u = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
+  const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
+
+  __shared__ DecKInfo s_ki[D];
+  __shared__ uint4 s_kw[4][D];       // per wave, sorted order: {b, row byte offset in its tile, scale, zero}
+  __shared__ uint8_t s_rank[D];      // natural component -> sorted position
+  __shared__ __attribute__((aligned(16))) float s_const[D];
+  __shared__ uint32_t s_b[D];
+  __shared__ int32_t s_misc[4];      // nnz, corrupt flag, full tile words
+  __shared__ float4 s_brow[4][4 * 32];  // per wave: RoPE table rows of the current sub-tile's 16-token groups
+  // dynamic: [basis operand fragments 2 x 4 x KBMAX x 64 lanes x 16 B][staged basis | tile buffers]
+  extern __shared__ __attribute__((aligned(16))) uint32_t dlds[];
+  uint4* sA = reinterpret_cast<uint4*>(dlds);
+  uint32_t* work = dlds + 2 * 4 * KBMAX * 64 * 4;
+
+  if (tid == 0) s_misc[1] = (int32_t)((get_status(p.ws, p.w) >> KVTC_ERR_CORRUPT) & 1u);
+  const uint8_t* rec = p.in + p.side_off + (int64_t)u * 9 * D;
+  if (tid < D) s_b[tid] = min((uint32_t)rec[tid], 8u);
+  __syncthreads();
+  if (s_misc[1]) return;
+  if (wave == 0) {
+    // counting sort of the components by width, b = 0 last
+    const uint32_t b0 = s_b[2 * lane], b1 = s_b[2 * lane + 1];
+    const uint32_t k0 = b0 ? b0 : 9u, k1 = b1 ? b1 : 9u;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    uint32_t base = 0, r0 = 0, r1 = 0, nnz = 0;
+    for (uint32_t v = 1; v <= 9; ++v) {
+      const uint64_t m0 = __ballot(k0 == v), m1 = __ballot(k1 == v);
+      const uint32_t before = base + __popcll(m0 & lt) + __popcll(m1 & lt);
+      if (k0 == v) r0 = before;
+      if (k1 == v) r1 = before + (k0 == v ? 1u : 0u);
+      base += __popcll(m0) + __popcll(m1);
+      if (v == 8) nnz = base;
+    }
+    s_rank[2 * lane] = (uint8_t)r0;
+    s_rank[2 * lane + 1] = (uint8_t)r1;
+    const float* zr = reinterpret_cast<const float*>(rec + D);
+    const float* sc = reinterpret_cast<const float*>(rec + 5 * D);
+    s_ki[r0] = DecKInfo{b0, (uint32_t)(2 * lane), sc[2 * lane], zr[2 * lane]};
+    s_ki[r1] = DecKInfo{b1, (uint32_t)(2 * lane + 1), sc[2 * lane + 1], zr[2 * lane + 1]};
+    uint32_t fw = ((uint32_t)(p.tile_tokens * (int)b0 + 31) >> 5) + ((uint32_t)(p.tile_tokens * (int)b1 + 31) >> 5);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) fw += __shfl_xor(fw, o, 64);
+    if (lane == 0) { s_misc[0] = (int32_t)nnz; s_misc[2] = (int32_t)fw; }
+  }
+  // stage the basis rows (channel-major, operand precision) for the gathers
+  const int64_t bidx = (p.basis_per_head ? ((int64_t)(l * 2 + s) * p.H + h) : (int64_t)(l * 2 + s)) * D * D;
+  const uint16_t* bsrc = reinterpret_cast<const uint16_t*>(p.basis) + bidx;
+  uint16_t* bst = reinterpret_cast<uint16_t*>(work);
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int row = it * 16 + (tid >> 4), c16 = tid & 15;
+    *reinterpret_cast<uint4*>(bst + row * kBS + c16 * 8) =
+        *reinterpret_cast<const uint4*>(bsrc + row * D + c16 * 8);
+  }
+  __syncthreads();
+  const int nnz = s_misc[0];
+  const int KB = (nnz + 31) >> 5;
+  if ((KBMAX == 3) != (KB <= 3)) return;
+  if (tid >= 128) {
+    // constant of the b = 0 components: sum_i B[j][i] bf16(zero_i), fp64, one rounding
+    const int j = tid - 128;
+    const float* zr = reinterpret_cast<const float*>(rec + D);
+    double acc = 0.0;
+    for (int i = 0; i < D; ++i)
+      if (s_b[i] == 0) acc = __fma_rn((double)bf16_to_f32(bst[j * kBS + i]), (double)round_bf16(zr[i]), acc);
+    s_const[j] = (float)acc;
+  }
+  // basis operand fragments [hf][mi][kb][lane]: lane (g, r) holds channel
+  // sigma(m, r) = 32 p + 8 (r >> 2) + 4 a + (r & 3), m = 2 p + a, p = hf + 2 (mi >> 1),
+  // a = mi & 1, of the sorted components 32 kb + 8 g .. +7
+  for (int f = wave; f < 2 * 4 * KB; f += 4) {
+    const int hf = f / (4 * KB), mi = (f / KB) % 4, kb = f % KB;
+    const int pp = hf + 2 * (mi >> 1), a = mi & 1;
+    const int chn = 32 * pp + 8 * (r >> 2) + 4 * a + (r & 3);
+    uint32_t w4[4];
+#pragma unroll
+    for (int q2 = 0; q2 < 4; ++q2) {
+      const int k0 = 32 * kb + 8 * g + 2 * q2;
+      const uint32_t lo = k0 < nnz ? bst[chn * kBS + s_ki[k0].idx] : 0u;
+      const uint32_t hi = k0 + 1 < nnz ? bst[chn * kBS + s_ki[k0 + 1].idx] : 0u;
+      w4[q2] = lo | (hi << 16);
+    }
+    sA[((hf * 4 + mi) * KBMAX + kb) * 64 + lane] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+  }
+  __syncthreads();  // the staged basis area becomes the tile buffers
+
+  const int ch = blockIdx.x * 4 + wave;
+  const uint32_t fw = (uint32_t)s_misc[2];
+  const int tbw = (int)(((int64_t)p.tile_tokens * (p.budget_k > p.budget_v ? p.budget_k : p.budget_v) + 31) / 32) + D + 20;
+  uint32_t* tb = work + wave * tbw;
+#define KVTC_DEC_CHUNK(KBV, OBV) dec_chunk128<KBV, KBMAX, OBV>(p, u, ch, sA, tb, s_kw[wave], s_ki, s_rank, s_b, s_const, fw, nnz, s_brow[wave])
+  if constexpr (KBMAX == 4) {
+    if (p.out_dtype == KVTC_BF16) KVTC_DEC_CHUNK(4, 2);
+    else KVTC_DEC_CHUNK(4, 4);
+  } else if (p.out_dtype == KVTC_BF16) {
+    switch (KB) {
+      case 0: KVTC_DEC_CHUNK(0, 2); break;
+      case 1: KVTC_DEC_CHUNK(1, 2); break;
+      case 2: KVTC_DEC_CHUNK(2, 2); break;
+      default: KVTC_DEC_CHUNK(3, 2); break;
+    }
+  } else {
+    switch (KB) {
+      case 0: KVTC_DEC_CHUNK(0, 4); break;
+      case 1: KVTC_DEC_CHUNK(1, 4); break;
+      case 2: KVTC_DEC_CHUNK(2, 4); break;
+      default: KVTC_DEC_CHUNK(3, 4); break;
+    }
+  }
+#undef KVTC_DEC_CHUNK
 }
 
 hipError_t launch_dec_transform(const Params& p, hipStream_t s) {
@@ -574,11 +763,19 @@ hipError_t launch_dec_transform(const Params& p, hipStream_t s) {
   const int32_t bmax = p.budget_k > p.budget_v ? p.budget_k : p.budget_v;
   const int32_t nz = bmax < p.D ? bmax : p.D;
   const size_t tile_words = (size_t)(((int64_t)p.tile_tokens * bmax + 31) / 32 + nz) + 4;
-  if (p.D == 128 && p.dtype == KVTC_BF16 && tile_words <= 36 * 256) {
-    const size_t lds = 64 * (size_t)(128 * ob + 16) + 2 * (tile_words + 4) * 4;
-    (void)hipFuncSetAttribute((const void*)k_dec128, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL(k_dec128, grid, block, lds, s, p);
-    return hipGetLastError();
+  if (p.D == 128 && p.dtype == KVTC_BF16 && p.tile_tokens % 64 == 0 && (int64_t)p.T * 128 * ob < (1ll << 31)) {
+    const int tbw = (int)(((int64_t)p.tile_tokens * bmax + 31) / 32) + 128 + 20;
+    size_t work = (size_t)4 * tbw * 4;
+    if (work < (size_t)128 * kBS * 2) work = (size_t)128 * kBS * 2;
+    const size_t lds3 = (size_t)2 * 4 * 3 * 64 * 16 + work, lds4 = (size_t)2 * 4 * 4 * 64 * 16 + work;
+    if (lds4 <= 140 * 1024) {
+      dim3 g4((p.chunks_per_sec + 3) / 4, p.n_sections);
+      (void)hipFuncSetAttribute((const void*)k_dec_pca128<3>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3);
+      (void)hipFuncSetAttribute((const void*)k_dec_pca128<4>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds4);
+      hipLaunchKernelGGL(k_dec_pca128<3>, g4, block, lds3, s, p);
+      hipLaunchKernelGGL(k_dec_pca128<4>, g4, block, lds4, s, p);
+      return hipGetLastError();
+    }
   }
   if (p.D == 128 && p.dtype == KVTC_BF16) {
     size_t lds = 64 * (128 + 8) * 2 + 4 * 16 * 128 * ob + tile_words * 4;
