@@ -184,39 +184,121 @@ __device__ int64_t rans_encode_stream(const uint8_t* sym, int64_t Nt, bool valid
   return ov ? -1 : nw;
 }
 
-// Decode one stream per lane group.  lut: 2^sb entries of
-// sym | (f-1) << 8 | (slot-cum) << 20.  Returns false on a malformed stream.
-__device__ bool rans_decode_stream(const uint32_t* states, const uint16_t* words, int64_t nw,
-                                   int64_t Nt, bool valid, int steps_max, const uint32_t* lut,
-                                   int sb, int lanes, uint8_t* out) {
-  const int lane = threadIdx.x & 63;
-  const int j = lane % lanes, grp = lane / lanes;
-  const uint64_t gmask = (lanes == 64) ? ~0ull : ((1ull << lanes) - 1ull);
-  const uint32_t mask = (1u << sb) - 1u;
-  uint32_t x = valid ? states[j] : kRansL;
-  bool bad = valid && x < kRansL;
-  int64_t ptr = nw;
-  for (int k = 0; k < steps_max; ++k) {
-    const int64_t i = (int64_t)k * lanes + j;
-    const bool active = valid && i < Nt;
-    if (active) {
-      const uint32_t slot = x & mask;
-      const uint32_t e = lut[slot];
-      x = (((e >> 8) & 0xfffu) + 1u) * (x >> sb) + (e >> 20);
-      out[i] = (uint8_t)(e & 0xffu);
-    }
-    const bool need = active && x < kRansL;
-    const uint64_t m = (__ballot(need) >> (grp * lanes)) & gmask;
-    if (need) {
-      const int64_t at = ptr - 1 - __popcll(m & ((1ull << j) - 1ull));
-      if (at >= 0) x = (x << 16) | words[at];
-      else bad = true;
-      if (x < kRansL) bad = true;
-    }
-    ptr -= __popcll(m);
+// Decoder tables from the cumulative frequencies (cum[256] = 2^sb): the
+// symbol of every slot (one byte each) and, per symbol, f | cum << 16.  Each
+// thread fills a run of consecutive slots, locating the run's first symbol
+// by binary search and walking on.
+__device__ __forceinline__ void build_dec_tables(const uint32_t* cum, int sb, uint8_t* sym_of, uint32_t* fc) {
+  for (int s = threadIdx.x; s < 256; s += blockDim.x) fc[s] = (cum[s + 1] - cum[s]) | (cum[s] << 16);
+  const int nslots = 1 << sb;
+  const int per = (nslots / 4 + (int)blockDim.x - 1) / (int)blockDim.x * 4;  // whole words
+  const int s0 = threadIdx.x * per, s1 = min(nslots, s0 + per);
+  if (s0 >= s1) return;
+  int lo = 0, hi = 255;  // symbol s with cum[s] <= s0 < cum[s+1]
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cum[mid] <= (uint32_t)s0) lo = mid; else hi = mid - 1;
   }
-  if (valid && (x != kRansL || ptr != 0)) bad = true;
-  return !bad;
+  uint32_t cnext = cum[lo + 1];
+  for (int slot = s0; slot < s1; slot += 4) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      while (cnext <= (uint32_t)(slot + b)) { ++lo; cnext = cum[lo + 1]; }
+      w |= (uint32_t)lo << (8 * b);
+    }
+    reinterpret_cast<uint32_t*>(sym_of)[slot >> 2] = w;
+  }
+}
+
+// Raw buffer resource over [base, base + bytes) with wave-uniform fields, so
+// the compiler keeps it in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(void* base, int32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* b = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(b, 0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+constexpr int kRing = 512;  // words of a stream's LDS ring
+constexpr int kUnit = 256;  // words per refill
+
+// Decode one interleaved stream: this lane runs state j = lane % LANES of
+// its group of LANES lanes; symbol i belongs to state i % LANES.  The stream's
+// 16-bit words (global memory, 4-byte aligned) are consumed from the end; a
+// ring of kRing words in LDS holds the next ones, refilled kUnit words at a
+// time from registers loaded one refill ahead, so no step waits on global
+// memory.  Returns false (for any lane) if the stream is not one the encoder
+// can have written.
+template <int LANES>
+__device__ __forceinline__ bool rans_decode_ring(const uint32_t* states, const uint16_t* words, int32_t nw,
+                                                 int32_t Nt, bool valid, int steps_max, const uint8_t* sym_of,
+                                                 const uint32_t* fc, int sb, uint16_t* ring, uint8_t* obase,
+                                                 int32_t out_off, int32_t out_end) {
+  const __amdgpu_buffer_rsrc_t orsrc = uniform_rsrc(obase, out_end);
+  const int lane = threadIdx.x & 63;
+  const int j = lane % LANES, grp = lane / LANES;
+  // this group's lanes as halves of the 64-bit lane mask
+  const uint64_t gm = (LANES == 64 ? ~0ull : ((1ull << LANES) - 1ull)) << (grp * LANES);
+  const uint32_t gm_lo = (uint32_t)gm, gm_hi = (uint32_t)(gm >> 32);
+  const uint32_t mask = (1u << sb) - 1u;
+  const uint32_t* wd = reinterpret_cast<const uint32_t*>(words);  // word pairs
+  uint32_t* ring32 = reinterpret_cast<uint32_t*>(ring);
+  uint32_t x = valid ? states[j] : kRansL;
+  const bool bad0 = valid && x < kRansL;
+  int32_t ptr = nw;
+  // committed words [clo, nw) (clo a multiple of 8), pending words [plo, clo)
+  int32_t clo = max(0, (nw - kRing + 7) & ~7);
+  if (valid) {
+    for (int32_t q = clo / 2 + j; 2 * q < nw; q += LANES)
+      ring32[q & (kRing / 2 - 1)] = (2 * q + 1 < nw) ? wd[q] : (uint32_t)words[2 * q];
+  }
+  int32_t plo = max(0, clo - kUnit);
+  constexpr int PER = kUnit / 2 / LANES;
+  uint32_t pend[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int32_t q = plo / 2 + j + LANES * k;
+    pend[k] = (valid && q < clo / 2) ? wd[q] : 0u;
+  }
+  __builtin_amdgcn_wave_barrier();
+  // Every step is branch-free apart from the (group-uniform) refill: a
+  // corrupt stream may read wrong ring words, which the final state and
+  // word-count checks then reject.
+  for (int k = 0; k < steps_max; ++k) {
+    if (valid && clo > 0 && ptr - clo <= kUnit) {
+      // the ring slots of [plo, clo) held words >= clo + kUnit >= ptr: consumed
+#pragma unroll
+      for (int q2 = 0; q2 < PER; ++q2) {
+        const int32_t q = plo / 2 + j + LANES * q2;
+        if (q < clo / 2) ring32[q & (kRing / 2 - 1)] = pend[q2];
+      }
+      clo = plo;
+      plo = max(0, clo - kUnit);
+#pragma unroll
+      for (int q2 = 0; q2 < PER; ++q2) {
+        const int32_t q = plo / 2 + j + LANES * q2;
+        pend[q2] = q < clo / 2 ? wd[q] : 0u;
+      }
+    }
+    const int32_t i = k * LANES + j;
+    const bool active = valid && i < Nt;
+    const uint32_t slot = x & mask;
+    const uint32_t sym = sym_of[slot];
+    const uint32_t e = fc[sym];
+    const uint32_t xn = __umul24(e & 0xffffu, x >> sb) + slot - (e >> 16);
+    x = active ? xn : x;
+    // lanes past the stream store out of the resource's range (dropped)
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sym, orsrc, active ? out_off + i : out_end, 0, 0);
+    const bool need = active && x < kRansL;
+    const uint64_t bl = __ballot(need);
+    const uint32_t mlo = (uint32_t)bl & gm_lo, mhi = (uint32_t)(bl >> 32) & gm_hi;
+    const uint32_t rank = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
+    const uint32_t w = ring[(uint32_t)(ptr - 1 - (int32_t)rank) & (kRing - 1)];
+    x = need ? ((x << 16) | w) : x;
+    ptr -= (int32_t)(__popc(mlo) + __popc(mhi));
+  }
+  return !(bad0 || (valid && (x != kRansL || ptr != 0)));
 }
 
 // ---- per-chunk encoder ------------------------------------------------------
@@ -447,80 +529,86 @@ hipError_t launch_dec_check(const Params& p, const uint8_t* hdr, hipStream_t s) 
   return hipGetLastError();
 }
 
-// Validated bit widths of section u read from the container; false if
-// they cannot have been written by the encoder.
-__device__ bool load_section_bits(const Params& p, int u, uint8_t* bits, int64_t* P_full,
-                                  int64_t* P_last, int n_last) {
-  // called by thread 0 after bits[] was filled by the block
-  const int s = (u / p.H) & 1;
-  int sum = 0;
-  bool ok = true;
-  for (int i = 0; i < p.D; ++i) {
-    if (bits[i] > p.max_bits) ok = false;
-    sum += bits[i];
-    if (p.transform == KVTC_WHT && bits[i] != (s == 0 ? p.bits_k_uniform : p.bits_v_uniform)) ok = false;
-  }
-  if (p.transform == KVTC_PCA && sum > (s == 0 ? p.budget_k : p.budget_v)) ok = false;
-  if (ok) {
-    *P_full = tile_bytes(bits, p.D, p.tile_tokens);
-    *P_last = tile_bytes(bits, p.D, n_last);
-  }
-  return ok;
-}
-
-__global__ void k_rans_dec_chunks(const Params p, int64_t stage_cap) {
+__global__ void k_rans_dec_chunks(const Params p) {
   const int c = blockIdx.x;
   const int u = c / p.chunks_per_sec, ch = c % p.chunks_per_sec;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (get_status(p.ws, p.w) & (1u << KVTC_ERR_CORRUPT)) return;
   extern __shared__ uint32_t lds[];
-  uint32_t* lut = lds;                                    // 2^sb entries
-  uint8_t* stage = reinterpret_cast<uint8_t*>(lds + (1 << p.sb));
-  __shared__ uint8_t bits[256];
+  uint32_t* fc = lds;                                                     // 256 entries
+  uint8_t* sym_of = reinterpret_cast<uint8_t*>(lds + 256);                // 2^sb bytes
+  uint16_t* rings = reinterpret_cast<uint16_t*>(sym_of + (1 << p.sb));    // kRing words per tile
   __shared__ int64_t s_info[4];
   __shared__ uint32_t s_cum[257];
   __shared__ int s_ok;
-  __shared__ int64_t s_toff[17];
+  __shared__ int32_t s_toff[17];
   const int n = min(p.chunk_tokens, p.T_mid - ch * p.chunk_tokens);
   const int ntiles = (n + p.tile_tokens - 1) / p.tile_tokens;
   const int n_last = n - (ntiles - 1) * p.tile_tokens;
-  for (int i = threadIdx.x; i < p.D; i += blockDim.x) bits[i] = p.in[p.side_off + (int64_t)u * 9 * p.D + i];
-  __syncthreads();
   const uint8_t* dir = p.in + p.dir_off + (int64_t)c * kDirEntry;
   const uint64_t off = *reinterpret_cast<const uint64_t*>(dir);
   const uint32_t size = *reinterpret_cast<const uint32_t*>(dir + 8);
   const uint32_t resv = *reinterpret_cast<const uint32_t*>(dir + 12);
   const uint64_t total = *reinterpret_cast<const uint64_t*>(p.in + 168);
-  if (threadIdx.x == 0) {
+  const uint8_t* rec = p.in + off;
+  if (wave == 0) {
+    // the section's widths: each no more than max_bits (and the uniform
+    // width on the WHT path), their sum within the budget; the packed tile
+    // sizes follow from them
+    const uint8_t* bits = p.in + p.side_off + (int64_t)u * 9 * p.D;
+    const int s = (u / p.H) & 1;
+    bool okl = true;
+    int sum = 0;
     int64_t Pf = 0, Pl = 0;
-    int ok = load_section_bits(p, u, bits, &Pf, &Pl, n_last) ? 1 : 0;
-    const int64_t P = ok ? (ntiles - 1) * Pf + Pl : 0;
-    if (ok && resv != 0) ok = 0;
-    if (ok && P == 0 && size != 0) ok = 0;
-    if (ok && P > 0) {
-      if (off < (uint64_t)p.chunks_off || (off & 15) || off + size > total ||
-          size < 512 + 4 * (uint32_t)ntiles)
-        ok = 0;
+    for (int i = lane; i < p.D; i += 64) {
+      const int b = bits[i];
+      if (b > p.max_bits) okl = false;
+      if (p.transform == KVTC_WHT && b != (s == 0 ? p.bits_k_uniform : p.bits_v_uniform)) okl = false;
+      sum += b;
+      Pf += 4 * (int64_t)((p.tile_tokens * b + 31) >> 5);
+      Pl += 4 * (int64_t)((n_last * b + 31) >> 5);
     }
-    s_ok = ok;
-    s_info[0] = Pf; s_info[1] = Pl; s_info[2] = P;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      sum += __shfl_xor(sum, o, 64);
+      Pf += __shfl_xor(Pf, o, 64);
+      Pl += __shfl_xor(Pl, o, 64);
+    }
+    bool ok = __ballot(!okl) == 0ull;
+    if (p.transform == KVTC_PCA && sum > (s == 0 ? p.budget_k : p.budget_v)) ok = false;
+    const int64_t P = ok ? (ntiles - 1) * Pf + Pl : 0;
+    if (ok && resv != 0) ok = false;
+    if (ok && P == 0 && size != 0) ok = false;
+    if (ok && P > 0 &&
+        (off < (uint64_t)p.chunks_off || (off & 15) || off + size > total || size < 512 + 4 * (uint32_t)ntiles))
+      ok = false;
+    // stream offsets inside the record (a prefix sum over its tiles)
+    int64_t piece = 0;
+    if (ok && P > 0 && lane < ntiles) {
+      const uint32_t nw = reinterpret_cast<const uint32_t*>(rec + 512)[lane];
+      piece = 4 * (int64_t)p.lanes + 2 * (int64_t)nw + ((nw & 1) ? 2 : 0);
+    }
+    int64_t xs = piece;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up(xs, o, 64);
+      if (lane >= o) xs += y;
+    }
+    const int64_t base = 512 + 4 * (int64_t)ntiles;
+    if (ok && P > 0 && align16(base + __shfl(xs, 63, 64)) != (int64_t)size) ok = false;
+    if (lane < ntiles) s_toff[lane] = (int32_t)(base + xs - piece);
+    if (lane == 0) {
+      s_ok = ok ? 1 : 0;
+      s_info[0] = Pf; s_info[1] = Pl; s_info[2] = P;
+    }
   }
   __syncthreads();
   if (!s_ok) { if (threadIdx.x == 0) set_status(p.ws, p.w, KVTC_ERR_CORRUPT); return; }
   const int64_t P_full = s_info[0], P_last = s_info[1], P = s_info[2];
   if (P == 0) return;
-  const uint8_t* rec = p.in + off;
-  // stage the record in LDS when it fits
-  const uint8_t* src = rec;
-  if ((int64_t)size <= stage_cap) {
-    for (uint32_t i = threadIdx.x; i < size / 4; i += blockDim.x)
-      reinterpret_cast<uint32_t*>(stage)[i] = reinterpret_cast<const uint32_t*>(rec)[i];
-    src = stage;
-  }
-  __syncthreads();
   // frequency table -> cumulative -> slot lookup table
   if (wave == 0) {
-    const uint16_t* fq = reinterpret_cast<const uint16_t*>(src);
+    const uint16_t* fq = reinterpret_cast<const uint16_t*>(rec);
     uint32_t f[4], s = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) { f[k] = fq[4 * lane + k]; s += f[k]; }
@@ -535,47 +623,31 @@ __global__ void k_rans_dec_chunks(const Params p, int64_t stage_cap) {
     for (int k = 0; k < 4; ++k) { s_cum[4 * lane + k] = cum; cum += f[k]; }
     if (lane == 63) s_cum[256] = cum;
   }
-  if (threadIdx.x == 0) {
-    // tile stream offsets inside the record
-    const uint32_t* nwv = reinterpret_cast<const uint32_t*>(src + 512);
-    int64_t at = 512 + 4 * (int64_t)ntiles;
-    for (int t = 0; t < ntiles; ++t) {
-      s_toff[t] = at;
-      uint32_t nw = nwv[t];
-      at += 4 * (int64_t)p.lanes + 2 * (int64_t)nw + ((nw & 1) ? 2 : 0);
-    }
-    s_toff[ntiles] = at;
-  }
   __syncthreads();
-  if (s_cum[256] != (1u << p.sb) || align16(s_toff[ntiles]) != (int64_t)size) {
+  if (s_cum[256] != (1u << p.sb)) {
     if (threadIdx.x == 0) set_status(p.ws, p.w, KVTC_ERR_CORRUPT);
     return;
   }
-  const uint16_t* fq = reinterpret_cast<const uint16_t*>(src);
-  for (int slot = threadIdx.x; slot < (1 << p.sb); slot += blockDim.x) {
-    int lo = 0, hi = 255;  // symbol s with cum[s] <= slot < cum[s+1]
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (s_cum[mid] <= (uint32_t)slot) lo = mid; else hi = mid - 1;
-    }
-    const uint32_t f = fq[lo];
-    lut[slot] = (uint32_t)lo | ((f - 1u) << 8) | (((uint32_t)slot - s_cum[lo]) << 20);
-  }
+  build_dec_tables(s_cum, p.sb, sym_of, fc);
   __syncthreads();
   const int spw = 64 / p.lanes;
   const int t = wave * spw + lane / p.lanes;
   const bool valid = t < ntiles;
   const int tt = valid ? t : 0;
-  const int64_t Nt = valid ? (t == ntiles - 1 ? P_last : P_full) : 0;
-  const int steps = (int)((Nt + p.lanes - 1) / p.lanes);
+  const int32_t Nt = valid ? (int32_t)(t == ntiles - 1 ? P_last : P_full) : 0;
+  const int steps = (Nt + p.lanes - 1) / p.lanes;
   int steps_max = steps;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) steps_max = max(steps_max, __shfl_xor(steps_max, o, 64));
-  const uint32_t nw = reinterpret_cast<const uint32_t*>(src + 512)[tt];
-  const uint32_t* states = reinterpret_cast<const uint32_t*>(src + s_toff[tt]);
-  const uint16_t* words = reinterpret_cast<const uint16_t*>(src + s_toff[tt] + 4 * p.lanes);
-  uint8_t* out = p.ws + p.w.packed + (int64_t)c * p.w.packed_slot + (int64_t)tt * P_full;
-  const bool ok = rans_decode_stream(states, words, nw, Nt, valid, steps_max, lut, p.sb, p.lanes, out);
+  uint8_t* slot = p.ws + p.w.packed + (int64_t)c * p.w.packed_slot;
+  const int32_t nw = (int32_t)reinterpret_cast<const uint32_t*>(rec + 512)[tt];
+  const uint32_t* states = reinterpret_cast<const uint32_t*>(rec + s_toff[tt]);
+  const uint16_t* words = reinterpret_cast<const uint16_t*>(rec + s_toff[tt] + 4 * p.lanes);
+  uint16_t* ring = rings + tt * kRing;
+  const int32_t oo = (int32_t)(tt * P_full);
+  const bool ok = p.lanes == 16
+      ? rans_decode_ring<16>(states, words, nw, Nt, valid, steps_max, sym_of, fc, p.sb, ring, slot, oo, (int32_t)P)
+      : rans_decode_ring<32>(states, words, nw, Nt, valid, steps_max, sym_of, fc, p.sb, ring, slot, oo, (int32_t)P);
   if (__ballot(!ok)) {
     if (lane == 0) set_status(p.ws, p.w, KVTC_ERR_CORRUPT);
   }
@@ -585,11 +657,9 @@ hipError_t launch_rans_decode_chunks(const Params& p, hipStream_t s) {
   int streams = p.tiles_per_chunk;
   int waves = (streams * p.lanes + 63) / 64;
   if (waves < 1) waves = 1;
-  // stage records of up to 40 KiB in LDS next to the 2^sb-entry lookup table
-  // (larger records are decoded straight from global memory)
-  const int64_t stage_cap = 40 * 1024;
-  size_t lds = (size_t)(4u << p.sb) + (size_t)stage_cap;
-  hipLaunchKernelGGL(k_rans_dec_chunks, dim3(p.n_chunks), dim3(64 * waves), lds, s, p, stage_cap);
+  // LDS: the symbol tables and one word ring per tile
+  const size_t lds = 1024 + (size_t)(1u << p.sb) + (size_t)p.tiles_per_chunk * kRing * 2;
+  hipLaunchKernelGGL(k_rans_dec_chunks, dim3(p.n_chunks), dim3(64 * waves), lds, s, p);
   return hipGetLastError();
 }
 
@@ -643,18 +713,15 @@ __global__ void k_test_rans_decode(const uint32_t* states, const uint16_t* words
     if (lane == 0) *status = KVTC_ERR_CORRUPT;
     return;
   }
-  for (int slot = threadIdx.x; slot < (1 << sb); slot += blockDim.x) {
-    int lo = 0, hi = 255;
-    while (lo < hi) {
-      int mid = (lo + hi + 1) >> 1;
-      if (s_cum[mid] <= (uint32_t)slot) lo = mid; else hi = mid - 1;
-    }
-    lut[slot] = (uint32_t)lo | (((uint32_t)freq[lo] - 1u) << 8) | (((uint32_t)slot - s_cum[lo]) << 20);
-  }
+  uint32_t* fc = lut;
+  uint8_t* sym_of = reinterpret_cast<uint8_t*>(lut + 256);
+  build_dec_tables(s_cum, sb, sym_of, fc);
   __syncthreads();
   const bool valid = lane < lanes;
   const int steps = (int)((N + lanes - 1) / lanes);
-  bool ok = rans_decode_stream(states, words, nwords, N, valid, steps, lut, sb, lanes, sym);
+  uint16_t* ring = reinterpret_cast<uint16_t*>(sym_of + (1 << sb));
+  const bool ok = lanes == 16 ? rans_decode_ring<16>(states, words, (int32_t)nwords, (int32_t)N, valid, steps, sym_of, fc, sb, ring, sym, 0, (int32_t)N)
+                              : rans_decode_ring<32>(states, words, (int32_t)nwords, (int32_t)N, valid, steps, sym_of, fc, sb, ring, sym, 0, (int32_t)N);
   if (__ballot(!ok) != 0ull) {
     if (lane == 0) *status = KVTC_ERR_CORRUPT;
   } else if (lane == 0) {
@@ -665,7 +732,7 @@ __global__ void k_test_rans_decode(const uint32_t* states, const uint16_t* words
 hipError_t launch_test_rans_decode(const uint32_t* states, const uint16_t* words, int64_t nwords,
                                    const uint16_t* freq, int sb, int lanes, int64_t N,
                                    uint8_t* sym, int32_t* status, hipStream_t s) {
-  hipLaunchKernelGGL(k_test_rans_decode, dim3(1), dim3(64), (size_t)(4u << sb), s, states, words,
+  hipLaunchKernelGGL(k_test_rans_decode, dim3(1), dim3(64), 1024 + (size_t)(1u << sb) + kRing * 2, s, states, words,
                      nwords, freq, sb, lanes, N, sym, status);
   return hipGetLastError();
 }
