@@ -824,6 +824,73 @@ __global__ __launch_bounds__(256) void k_enc_wht(const Params p, int sec0, float
 }
 
 // ---------------------------------------------------------------------------
+// head_dim 128, bf16 cache: RoPE removed from the mid-region keys ahead of the
+// projection passes (Codec-Gauge "Problem Statement and Overview"; KVTC
+// undoes the rotation before the transform).  x_a = fma(y_a, c, fp32(y_b s)),
+// x_b = fma(y_b, c, -fp32(y_a s)), rounded to bf16, into a copy laid out
+// [layer][head][mid token][channel] in the workspace.  A workgroup takes 16
+// positions of one layer: their table rows are read once into LDS with
+// coalesced loads and applied to every head.  Lane q of a row's 8 lanes holds
+// channels [8q, 8q+8) and [64+8q, 64+8q+8), which contain both members of
+// each of its RoPE pairs in either pairing style.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_unrope128(const Params p) {
+  constexpr int D = 128;
+  const int l = blockIdx.y, t0 = blockIdx.x * 16;
+  const int nt = min(16, p.T_mid - t0);
+  if (nt <= 0) return;
+  const int tid = threadIdx.x;
+  __shared__ float2 cs[16 * 64];
+  {
+    const float4* srow = reinterpret_cast<const float4*>(p.rope + (int64_t)(p.mid_begin + t0) * 64);
+    for (int i = tid; i < nt * 32; i += 256) reinterpret_cast<float4*>(cs)[i] = srow[i];
+  }
+  __syncthreads();
+  const int q = tid & 7;
+  const bool half = p.rope_style == KVTC_ROPE_HALF;
+  const uint16_t* kin = reinterpret_cast<const uint16_t*>(p.k);
+  uint16_t* kout = reinterpret_cast<uint16_t*>(p.ws + p.w.kprime);
+  for (int ri = tid >> 3; ri < p.H * nt; ri += 32) {
+    const int h = ri / nt, t = ri % nt;
+    const uint16_t* in = kin + (((int64_t)l * p.H + h) * p.T + p.mid_begin + t0 + t) * D;
+    const uint4 a = *reinterpret_cast<const uint4*>(in + 8 * q);
+    const uint4 b = *reinterpret_cast<const uint4*>(in + 64 + 8 * q);
+    float ya[8], yb[8];
+    unpack_bf16x8(a, ya);
+    unpack_bf16x8(b, yb);
+    const float2* row = cs + t * 64;
+    if (half) {
+      // pair j = 8q + e: (channel j, channel j + 64)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float2 c = row[8 * q + e];
+        const float xa = __fmaf_rn(ya[e], c.x, __fmul_rn(yb[e], c.y));
+        const float xb = __fmaf_rn(yb[e], c.x, -__fmul_rn(ya[e], c.y));
+        ya[e] = xa;
+        yb[e] = xb;
+      }
+    } else {
+      // pairs (2m, 2m + 1): m = 4q + e/2 in the low run, 32 + 4q + e/2 in the high run
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float2 cl = row[4 * q + m], ch = row[32 + 4 * q + m];
+        const float a0 = ya[2 * m], a1 = ya[2 * m + 1], b0 = yb[2 * m], b1 = yb[2 * m + 1];
+        ya[2 * m] = __fmaf_rn(a0, cl.x, __fmul_rn(a1, cl.y));
+        ya[2 * m + 1] = __fmaf_rn(a1, cl.x, -__fmul_rn(a0, cl.y));
+        yb[2 * m] = __fmaf_rn(b0, ch.x, __fmul_rn(b1, ch.y));
+        yb[2 * m + 1] = __fmaf_rn(b1, ch.x, -__fmul_rn(b0, ch.y));
+      }
+    }
+    uint16_t* o = kout + (((int64_t)l * p.H + h) * p.T_mid + t0 + t) * D;
+    *reinterpret_cast<uint4*>(o + 8 * q) =
+        make_uint4(pack2_bf16(ya[0], ya[1]), pack2_bf16(ya[2], ya[3]), pack2_bf16(ya[4], ya[5]), pack2_bf16(ya[6], ya[7]));
+    *reinterpret_cast<uint4*>(o + 64 + 8 * q) =
+        make_uint4(pack2_bf16(yb[0], yb[1]), pack2_bf16(yb[2], yb[3]), pack2_bf16(yb[4], yb[5]), pack2_bf16(yb[6], yb[7]));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // head_dim 128, bf16 cache: the bandwidth-oriented projection pass.
 //
 // A workgroup (4 waves) walks its chunk in 64-token sub-tiles.  Staging:
@@ -850,9 +917,14 @@ __global__ __launch_bounds__(256) void k_enc128(const Params p, int sec0, float*
   if (MODE == 1 && (get_status(p.ws, p.w) & (1u << KVTC_ERR_NONFINITE))) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
   const int st_t = tid >> 2, st_q = tid & 3;
-  const uint16_t* src = reinterpret_cast<const uint16_t*>(s ? p.v : p.k);
-  const bool rope = (s == 0) && p.rope_keys;
-  const int64_t lh_row0 = ((int64_t)l * p.H + h) * p.T;
+  // keys with RoPE come from the workspace copy with the rotation removed
+  // (k_unrope128), except for the coefficient export, which has no workspace
+  const bool pre = MODE != 2 && s == 0 && p.rope_keys;
+  const uint16_t* src = pre ? reinterpret_cast<const uint16_t*>(p.ws + p.w.kprime)
+                            : reinterpret_cast<const uint16_t*>(s ? p.v : p.k);
+  const bool rope = !pre && (s == 0) && p.rope_keys;
+  const int64_t lh_row0 = ((int64_t)l * p.H + h) * (pre ? p.T_mid : p.T);
+  const int pos_base = pre ? 0 : p.mid_begin;
   const int64_t bi = basis_index(p, l, s, h) * D * D;
   const uint16_t* bt = reinterpret_cast<const uint16_t*>(p.basis_t) + bi;
 
@@ -901,7 +973,7 @@ __global__ __launch_bounds__(256) void k_enc128(const Params p, int sec0, float*
     const int pos = p.mid_begin + t0 + tok;
     ya0 = ya1 = yb0 = yb1 = make_uint4(0, 0, 0, 0);
     if (valid) {
-      const uint16_t* row = src + (lh_row0 + pos) * D;
+      const uint16_t* row = src + (lh_row0 + pos_base + t0 + tok) * D;
       ya0 = *reinterpret_cast<const uint4*>(row + 16 * st_q);
       ya1 = *reinterpret_cast<const uint4*>(row + 16 * st_q + 8);
       yb0 = *reinterpret_cast<const uint4*>(row + 64 + 16 * st_q);
@@ -1171,11 +1243,10 @@ hipError_t launch_enc_transform(const Params& p, int mode, hipStream_t s) {
   }
   if (p.D == 128 && p.dtype == KVTC_BF16 && (p.tile_tokens % 64) == 0) {
     if (mode == 0) {
+      if (p.rope_keys) hipLaunchKernelGGL(k_unrope128, dim3((p.T_mid + 15) / 16, p.L), dim3(256), 0, s, p);
       hipLaunchKernelGGL(k_enc128<0>, grid, block, 0, s, p, 0, (float*)nullptr);
     } else {
-      const size_t tl = tile_lds_bytes(p) + 16;
-      (void)hipFuncSetAttribute((const void*)k_enc128<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)tl);
-      hipLaunchKernelGGL(k_enc128<1>, grid, block, tl, s, p, 0, (float*)nullptr);
+      return launch_quant128(p, s);
     }
     return hipGetLastError();
   }

@@ -127,6 +127,9 @@ WsLayout make_ws_layout(const kvtc_config& c, const Layout& lo) {
   w.rec = take(at, (int64_t)lo.n_chunks * w.rec_slot);
   w.rec_size = take(at, (int64_t)lo.n_chunks * 4);
   w.rec_pos = take(at, (int64_t)lo.n_chunks * 8 + 8);
+  const bool fast128 = c.head_dim == 128 && c.dtype == KVTC_BF16 && c.transform == KVTC_PCA &&
+                       c.tile_tokens % 64 == 0 && c.rope_keys;
+  w.kprime = take(at, fast128 ? (int64_t)c.layers * c.kv_heads * lo.T_mid * D * 2 : 0);
   w.total = at;
   return w;
 }

@@ -42,6 +42,7 @@ struct WsLayout {
   int64_t tile_words_max;  // words capacity of one tile stream in a slot
   int64_t rec_size;    // u32 [n_chunks]
   int64_t rec_pos;     // u64 [n_chunks]
+  int64_t kprime;      // bf16 [L][H][T_mid][D]: mid-region keys with RoPE removed (head_dim 128 bf16 path)
   int64_t total;
 };
 
@@ -104,6 +105,7 @@ void build_header(const PlanImpl& p, const Layout& lo, uint8_t* hdr);
 hipError_t launch_copy_raw(const Params& p, int to_container, hipStream_t s);
 hipError_t launch_enc_transform(const Params& p, int mode, hipStream_t s);  // 0 stats, 1 quant
 hipError_t launch_enc_alloc(const Params& p, hipStream_t s);
+hipError_t launch_quant128(const Params& p, hipStream_t s);  // head_dim 128 bf16 PCA, tile % 64 == 0
 hipError_t launch_rans_encode_chunks(const Params& p, hipStream_t s);
 hipError_t launch_assemble(const Params& p, const uint8_t* hdr, hipStream_t s);
 hipError_t launch_dec_check(const Params& p, const uint8_t* hdr, hipStream_t s);
