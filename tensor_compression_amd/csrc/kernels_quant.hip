@@ -2,23 +2,24 @@
 // (KVTC "Quantization and bit allocation"; Codec-Gauge "Problem Statement
 // and Overview": B_c = Q(Z_c), channel-major packing of the codes).
 //
-// Workgroup = one chunk of one section, one wave per packed tile.  Only the
+// Workgroup = eight packed tiles of one section, one wave per tile.  Only the
 // components with codes (b > 0) are projected: they are ordered by width and
 // their basis columns are staged in LDS as MFMA B fragments of 16 components.
-// A wave walks its tile in 64-token sub-tiles with the token rows loaded
+// A wave walks its tile in 16-token groups with the token rows loaded
 // straight from global memory as MFMA A operands (lane (g, r) of group kk
-// holds token 16 kk + r, channels 32 kb + 8 g .. +7).  For each 16-component
-// tile the result lane (g, r) holds tokens 16 kk + 4 g .. +3 of component
-// 16 m + r, i.e. four consecutive codes of one channel-major row.
+// holds token 16 kk + r, channels 32 kb + 8 g .. +7; the next two groups'
+// rows are in flight meanwhile).  For each 16-component tile the result lane
+// (g, r) holds tokens 16 kk + 4 g .. +3 of component 16 m + r, i.e. four
+// consecutive codes of one channel-major row.
 //
 // Quantisation: v = (c - zero) * rcp, clamped to [0, 2^b - 1] and rounded to
 // nearest even by adding 2^23, whose float bits then carry the code.  The
 // four codes of a lane fold into one 4b-bit piece that is OR-ed into the
 // wave's LDS segment buffer (the sub-tile's slice of every row); the buffer
-// is then copied to the packed tile.  A code is recomputed from the exact
-// dot product (fp64 sum of the exact bf16 products, over the four lanes that
-// hold the token) when v lies within the coefficient's error bound of a
-// rounding boundary: |c_mfma - c| <= mfma_err ||x||_2 (fp32 accumulation of
+// is copied to the packed tile after every 64 tokens.  A code is recomputed
+// on the spot from the exact dot product (fp64 sum of the exact bf16
+// products, over the four lanes that hold the token) when v lies within the
+// coefficient's error bound of a rounding boundary: |c_mfma - c| <= mfma_err ||x||_2 (fp32 accumulation of
 // the exact products; Cauchy-Schwarz), with ||x||_2 from a bf16 dot product
 // of the token with itself, taken 1% high.
 #include <string.h>
@@ -41,16 +42,12 @@ struct QInfo {     // per component, sorted order (b > 0 first, by width)
   uint32_t pad;    // fp32 bits of mfma_err * rcp: error of v per unit token norm
 };
 
-constexpr int kQWaves = 4;
-constexpr uint32_t kQList = 128;  // queued recomputations per wave
+constexpr int kQWaves = 8;  // one packed tile per wave
 
-__global__ __launch_bounds__(256) void k_quant128(const Params p) {
+__global__ __launch_bounds__(64 * kQWaves) void k_quant128(const Params p) {
   constexpr int D = 128;
-  const int u = blockIdx.y, ch = blockIdx.x;
+  const int u = blockIdx.y;
   const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
-  const int t0 = ch * p.chunk_tokens;
-  const int n = min(p.chunk_tokens, p.T_mid - t0);
-  if (n <= 0) return;
   if (get_status(p.ws, p.w) & (1u << KVTC_ERR_NONFINITE)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
 
@@ -140,22 +137,22 @@ __global__ __launch_bounds__(256) void k_quant128(const Params p) {
   }
   __syncthreads();
 
-  const uint16_t* bt = reinterpret_cast<const uint16_t*>(p.basis_t) +
-                       (p.basis_per_head ? ((int64_t)(l * 2 + s) * p.H + h) : (int64_t)(l * 2 + s)) * D * D;
-  __shared__ uint2 s_qlist[kQWaves][kQList];
-  uint2* qlist = s_qlist[wave];
   // token rows: keys with RoPE come from the workspace copy with the rotation removed
   const bool pre = s == 0 && p.rope_keys;
   const uint16_t* src = pre ? reinterpret_cast<const uint16_t*>(p.ws + p.w.kprime)
                             : reinterpret_cast<const uint16_t*>(s ? p.v : p.k);
-  const int64_t row0 = ((int64_t)l * p.H + h) * (pre ? p.T_mid : p.T) + (pre ? 0 : p.mid_begin) + t0;
-  uint32_t* slot = reinterpret_cast<uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot);
   uint32_t refined = 0;
-  const int ntiles = (n + p.tile_tokens - 1) / p.tile_tokens;
-
-  for (int tl = wave; tl < ntiles; tl += kQWaves) {
-    const int ta = tl * p.tile_tokens;
+  // this wave's tile: the f-th tile of the section
+  const int f = blockIdx.x * kQWaves + wave;
+  const int ch = f / p.tiles_per_chunk, tl = f % p.tiles_per_chunk;
+  const int t0 = ch * p.chunk_tokens;
+  const int n = min(p.chunk_tokens, p.T_mid - t0);
+  const int ta = tl * p.tile_tokens;
+  if (ch < p.chunks_per_sec && ta < n) {
     const int nt = min(p.tile_tokens, n - ta);
+    const int64_t row0 = ((int64_t)l * p.H + h) * (pre ? p.T_mid : p.T) + (pre ? 0 : p.mid_begin) + t0 + ta;
+    uint32_t* tile = reinterpret_cast<uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot) +
+                     (int64_t)tl * fw;
     // row offsets of this tile (natural order scan), by sorted position
     {
       const uint32_t b0 = s_bs[s_rank[2 * lane]], b1 = s_bs[s_rank[2 * lane + 1]];
@@ -170,143 +167,120 @@ __global__ __launch_bounds__(256) void k_quant128(const Params p) {
       s_row[wave][s_rank[2 * lane]] = ex;
       s_row[wave][s_rank[2 * lane + 1]] = ex + w0;
     }
-    uint32_t* tile = slot + (int64_t)tl * fw;
+    // A operands of a 16-token group: lane (g, r) holds token 16 kk + r (rows
+    // past the tile repeat its last token), channels 32 kb + 8 g .. +7
+    auto load_group = [&](int sub, int kk, uint4 (&a)[4]) {
+      const int tok = min(sub * 64 + kk * 16 + r, nt - 1);
+      const uint16_t* rowp = src + (row0 + tok) * D;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) a[kb] = *reinterpret_cast<const uint4*>(rowp + 32 * kb + 8 * g);
+    };
+    // two groups in flight ahead of the one being projected
+    uint4 An[4], An2[4];
+    load_group(0, 0, An);
+    load_group(0, 1, An2);
     for (int sub = 0; sub * 64 < nt; ++sub) {
-      // exact recomputation of the queued codes, one per lane: fp64 sum of the
-      // exact bf16 products in channel order, then the corrected code is
-      // XOR-ed into the segment buffer (codes occupy disjoint bits)
-      uint32_t nq = 0;
-      auto drain = [&]() {
-        for (uint32_t q0 = 0; q0 < nq; q0 += 64) {
-          if (q0 + lane < nq) {
-            const uint2 en = qlist[q0 + lane];
-            const uint32_t t = en.x & 0xffu, k = (en.x >> 8) & 0xffu, oldc = (en.x >> 16) & 0xffu;
-            const QInfo& qk = s_q[k];
-            const uint16_t* xr = src + (row0 + ta + sub * 64 + (int)t) * D;
-            const uint16_t* br = bt + (int64_t)qk.idx * D;
-            double acc = 0.0;
-            for (int c8 = 0; c8 < D / 8; ++c8) {
-              const uint4 xa = *reinterpret_cast<const uint4*>(xr + 8 * c8);
-              const uint4 ba = *reinterpret_cast<const uint4*>(br + 8 * c8);
-              const uint32_t xw[4] = {xa.x, xa.y, xa.z, xa.w}, bw[4] = {ba.x, ba.y, ba.z, ba.w};
-#pragma unroll
-              for (int z = 0; z < 4; ++z) {
-                acc = __fma_rn((double)__uint_as_float(xw[z] << 16), (double)__uint_as_float(bw[z] << 16), acc);
-                acc = __fma_rn((double)__uint_as_float(xw[z] & 0xffff0000u), (double)__uint_as_float(bw[z] & 0xffff0000u), acc);
-              }
-            }
-            const float qm = (float)((1u << qk.b) - 1u);
-            const float v = __fmul_rn(__fsub_rn((float)acc, qk.zero), qk.rcp);
-            const uint32_t newc = (__float_as_uint(__fadd_rn(__builtin_amdgcn_fmed3f(v, 0.0f, qm), 0x1p23f)) & 0xffu);
-            const uint32_t delta = oldc ^ newc;
-            if (delta) {
-              const uint32_t bitoff = t * qk.b;
-              const uint32_t wi = qk.seg + (bitoff >> 5), sh = bitoff & 31;
-              atomicXor(&segbuf[wi], delta << sh);
-              if (sh + qk.b > 32) atomicXor(&segbuf[wi + 1], delta >> (32 - sh));
-            }
-          }
-        }
-        refined += nq;
-        nq = 0;
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-      };
       for (uint32_t w = lane; w < segw + 4; w += 64) segbuf[w] = 0u;
-      // A operands of the four 16-token groups (rows past the tile repeat its last token)
-      uint4 A[4][4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int tok = min(sub * 64 + kk * 16 + r, nt - 1);
-        const uint16_t* rowp = src + (row0 + ta + tok) * D;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) A[kk][kb] = *reinterpret_cast<const uint4*>(rowp + 32 * kb + 8 * g);
-      }
-      // norm bound of the token of output element (group kk, row 4 g + e)
-      float tnorm[4][4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        float n2 = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const uint32_t w4[4] = {A[kk][kb].x, A[kk][kb].y, A[kk][kb].z, A[kk][kb].w};
-#pragma unroll
-          for (int z = 0; z < 4; ++z) {
-            const bf16x2_t h2 = __builtin_bit_cast(bf16x2_t, w4[z]);
-            n2 = __builtin_amdgcn_fdot2_f32_bf16(h2, h2, n2, false);
-          }
-        }
-        n2 += __shfl_xor(n2, 16, 64);
-        n2 += __shfl_xor(n2, 32, 64);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) tnorm[kk][e] = 1.01f * __fsqrt_rn(__shfl(n2, 4 * g + e, 64));
-      }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
-      for (int m = 0; m < NT; ++m) {
-        uint4 Bm[4];
+      for (int kk = 0; kk < 4; ++kk) {
+        uint4 A[4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) Bm[kb] = sB[(m * 4 + kb) * 64 + lane];
-        const QInfo qi = s_q[16 * m + r];
-        const uint32_t b = qi.b;
-        const float qmax = (float)((1u << b) - 1u);
-        uint32_t uq[4][4];   // float bits of 2^23 + code, [group][element]
-        uint32_t flags = 0;  // bit 4 kk + e: recompute exactly
+        for (int kb = 0; kb < 4; ++kb) { A[kb] = An[kb]; An[kb] = An2[kb]; }
+        // group kk + 2 of this sub-tile or of the next (the loads of groups
+        // past the tile are clamped to its last token and never used)
+        load_group(sub + ((kk + 2) >> 2), (kk + 2) & 3, An2);
+        // norm bound of the token of output element (row 4 g + e of the group)
+        float tn[4];
+        {
+          float n2 = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
+          for (int kb = 0; kb < 4; ++kb) {
+            const uint32_t w4[4] = {A[kb].x, A[kb].y, A[kb].z, A[kb].w};
+#pragma unroll
+            for (int z = 0; z < 4; ++z) {
+              const bf16x2_t h2 = __builtin_bit_cast(bf16x2_t, w4[z]);
+              n2 = __builtin_amdgcn_fdot2_f32_bf16(h2, h2, n2, false);
+            }
+          }
+          n2 += __shfl_xor(n2, 16, 64);
+          n2 += __shfl_xor(n2, 32, 64);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) tn[e] = 1.01f * __fsqrt_rn(__shfl(n2, 4 * g + e, 64));
+        }
+        const int tb0 = sub * 64 + kk * 16 + 4 * g;  // tile-relative token of element 0
+        for (int m = 0; m < NT; ++m) {
+          uint4 Bm[4];
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) Bm[kb] = sB[(m * 4 + kb) * 64 + lane];
+          const QInfo qi = s_q[16 * m + r];
+          const uint32_t b = qi.b;
+          const float qmax = (float)((1u << b) - 1u);
           f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[kk][kb]),
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[kb]),
                                                           __builtin_bit_cast(bf16x8_t, Bm[kb]), acc, 0, 0, 0);
-          const int tb0 = sub * 64 + kk * 16 + 4 * g;  // tile-relative token of element 0
+          uint32_t uq[4];
+          uint32_t flags = 0;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const bool valid = b > 0 && tb0 + e < nt;
             const float v = __fmul_rn(__fsub_rn(acc[e], qi.zero), qi.rcp);
             const float vc = valid ? __builtin_amdgcn_fmed3f(v, 0.0f, qmax) : 0.0f;
             const float sv = __fadd_rn(vc, 0x1p23f);  // rint(vc), nearest even, in the low bits
-            uq[kk][e] = __float_as_uint(sv);
+            uq[e] = __float_as_uint(sv);
             const float d = __fsub_rn(vc, __fsub_rn(sv, 0x1p23f));
-            if (fabsf(d) > __fmaf_rn(-__uint_as_float(qi.pad), tnorm[kk][e], qi.thr)) flags |= 1u << (4 * kk + e);
+            if (fabsf(d) > __fmaf_rn(-__uint_as_float(qi.pad), tn[e], qi.thr)) flags |= 1u << e;
           }
-        }
-        if (b > 0) {
+          uint64_t pend = __ballot(flags != 0);
+          while (pend) {
+            // exact coefficient of (row rho of the group, component of lane L):
+            // fp64 sum of the exact products over the four lanes holding the row
+            const int L = __ffsll((unsigned long long)pend) - 1;
+            const int e = __ffs(__shfl(flags, L, 64)) - 1;
+            const int rho = 4 * (L >> 4) + e, r0 = L & 15;
+            double part = 0.0;
+            if (r == rho) {
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            // four codes -> one 4b-bit piece (the exponent bits cancel in kb)
-            const uint32_t piece = uq[kk][0] + (uq[kk][1] << b) + (uq[kk][2] << (2 * b)) + (uq[kk][3] << (3 * b)) - qi.kb;
-            if (piece != 0u) {
-              const uint32_t bitoff = (uint32_t)(kk * 16 + 4 * g) * b;
-              const uint32_t wi = qi.seg + (bitoff >> 5), sh = bitoff & 31;
-              atomicOr(&segbuf[wi], piece << sh);
-              if (sh + 4 * b > 32) atomicOr(&segbuf[wi + 1], piece >> (32 - sh));
+              for (int kb = 0; kb < 4; ++kb) {
+                const uint4 bv = sB[(m * 4 + kb) * 64 + (lane & 48) + r0];
+                uint32_t aw[4] = {A[kb].x, A[kb].y, A[kb].z, A[kb].w};
+                // keep the unpacking of this rarely taken path inside the loop
+                asm volatile("" : "+v"(aw[0]), "+v"(aw[1]), "+v"(aw[2]), "+v"(aw[3]));
+                const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+                for (int z = 0; z < 4; ++z) {
+                  // bf16 x bf16 products are exact in fp32
+                  part += (double)__fmul_rn(__uint_as_float(aw[z] << 16), __uint_as_float(bw[z] << 16));
+                  part += (double)__fmul_rn(__uint_as_float(aw[z] & 0xffff0000u), __uint_as_float(bw[z] & 0xffff0000u));
+                }
+              }
             }
+            part += __shfl_xor(part, 16, 64);
+            part += __shfl_xor(part, 32, 64);
+            const double cex = __shfl(part, rho, 64);
+            if (lane == L) {
+              const float v = __fmul_rn(__fsub_rn((float)cex, qi.zero), qi.rcp);
+              const uint32_t un = __float_as_uint(__fadd_rn(__builtin_amdgcn_fmed3f(v, 0.0f, qmax), 0x1p23f));
+#pragma unroll
+              for (int z = 0; z < 4; ++z)
+                if (z == e) uq[z] = un;
+              flags &= ~(1u << e);
+            }
+            ++refined;
+            pend = __ballot(flags != 0);
           }
-        }
-        // codes near a rounding boundary: queue (token, component, old code)
-        if (__ballot(flags != 0)) {
-          uint32_t fl = flags;
-          while (__ballot(fl != 0)) {
-            const bool has = fl != 0;
-            const int bit = has ? __ffs(fl) - 1 : 0;
-            const uint64_t bm = __ballot(has);
-            if (has) {
-              uint32_t code = 0;
-#pragma unroll
-              for (int z = 0; z < 16; ++z)
-                if (z == bit) code = uq[z >> 2][z & 3] & 0xffu;
-              const uint32_t t = (uint32_t)(16 * (bit >> 2) + 4 * g + (bit & 3));
-              const uint32_t at = nq + __builtin_amdgcn_mbcnt_hi((uint32_t)(bm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bm, 0u));
-              qlist[at] = make_uint2(t | ((uint32_t)(16 * m + r) << 8) | (code << 16), 0u);
-              fl &= ~(1u << bit);
-            }
-            nq += (uint32_t)__popcll(bm);
-            if (nq + 64 > kQList) drain();
+          // four codes -> one 4b-bit piece (the exponent bits cancel in kb)
+          const uint32_t piece = uq[0] + (uq[1] << b) + (uq[2] << (2 * b)) + (uq[3] << (3 * b)) - qi.kb;
+          if (b > 0 && piece != 0u) {
+            const uint32_t bitoff = (uint32_t)(kk * 16 + 4 * g) * b;
+            const uint32_t wi = qi.seg + (bitoff >> 5), sh = bitoff & 31;
+            atomicOr(&segbuf[wi], piece << sh);
+            if (sh + 4 * b > 32) atomicOr(&segbuf[wi + 1], piece >> (32 - sh));
           }
         }
       }
-      drain();
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
       // segment buffer -> the rows of the packed tile
@@ -317,6 +291,7 @@ __global__ __launch_bounds__(256) void k_quant128(const Params p) {
         const int32_t rw = (int32_t)((nt * (int)qk.b + 31) >> 5) - (int32_t)(2 * qk.b * sub);
         if ((int32_t)idx < rw) tile[s_row[wave][k] + 2 * qk.b * sub + idx] = segbuf[w];
       }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
     }
   }
@@ -330,8 +305,9 @@ hipError_t launch_quant128(const Params& p, hipStream_t s) {
   if (segw > 2048) return hipErrorInvalidValue;
   const int segstride = (segw + 4 + 3) & ~3;
   const size_t lds = (size_t)8 * 4 * 64 * 16 + (size_t)kQWaves * segstride * 4;
+  const int tiles = p.chunks_per_sec * p.tiles_per_chunk;
   (void)hipFuncSetAttribute((const void*)k_quant128, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL(k_quant128, dim3(p.chunks_per_sec, p.n_sections), dim3(64 * kQWaves), lds, s, p);
+  hipLaunchKernelGGL(k_quant128, dim3((tiles + kQWaves - 1) / kQWaves, p.n_sections), dim3(64 * kQWaves), lds, s, p);
   return hipGetLastError();
 }
 
