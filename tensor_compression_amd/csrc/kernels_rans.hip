@@ -18,8 +18,17 @@ namespace kvtc {
 struct EncSym {
   uint32_t f;
   uint32_t cum;
-  double rcp;  // 1/f rounded to fp64; quotient = trunc(fma(x, rcp, 2^-20))
+  double rcp;     // 1/f rounded to fp64; quotient = trunc(fma(x, rcp, 2^-20))
 };
+
+// Raw buffer resource over [base, base + bytes) with wave-uniform fields, so
+// the compiler keeps it in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(void* base, int32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* b = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(b, 0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
 
 // ---- frequency table ------------------------------------------------------
 
@@ -150,37 +159,73 @@ __device__ void build_enc_table(const uint32_t* freq, EncSym* tab) {
 // Encode one stream per `lanes`-lane group of the wave.  sym: the tile's
 // bytes (any address space); words: output (emission order).  Returns the
 // word count (uniform within the group) or -1 when the capacity is exceeded.
-__device__ int64_t rans_encode_stream(const uint8_t* sym, int64_t Nt, bool valid, int steps_max,
-                                      const EncSym* tab, int sb, int lanes, uint16_t* words,
-                                      int64_t wcap, uint32_t* state_out) {
+__device__ __forceinline__ int64_t rans_encode_stream(const uint8_t* sbase, int32_t sbytes, int32_t soff, int32_t Nt,
+                                                      bool valid, int steps_max, const EncSym* tab, int sb, int lanes,
+                                                      uint8_t* wbase, int32_t wbytes, int32_t woff, int64_t wcap,
+                                                      uint32_t* state_out) {
+  // Symbols come from sbase + soff + i and words go to wbase + woff + 2 at,
+  // both through buffer resources whose range check turns the accesses of
+  // lanes without work into no-ops, so every step issues exactly one load
+  // and one store (the waits for the prefetched symbols then never cover an
+  // unknown number of stores).  The symbol of step k is loaded PF steps
+  // ahead into slot k % PF of a register ring that is consumed in place.
+  const __amdgpu_buffer_rsrc_t srsrc = uniform_rsrc(const_cast<uint8_t*>(sbase), sbytes);
+  const __amdgpu_buffer_rsrc_t wrsrc = uniform_rsrc(wbase, wbytes);
   const int lane = threadIdx.x & 63;
   const int j = lane % lanes, grp = lane / lanes;
-  const uint64_t gmask = (lanes == 64) ? ~0ull : ((1ull << lanes) - 1ull);
+  // this group's lanes as halves of the 64-bit lane mask
+  const uint64_t gm = ((lanes == 64) ? ~0ull : ((1ull << lanes) - 1ull)) << (grp * lanes);
+  const uint32_t gm_lo = (uint32_t)gm, gm_hi = (uint32_t)(gm >> 32);
   const uint32_t M = 1u << sb;
   uint32_t x = kRansL;
-  int64_t nw = 0;
+  int32_t nw = 0;
   bool overflow = false;
-  for (int k = steps_max - 1; k >= 0; --k) {
-    const int64_t i = (int64_t)k * lanes + j;
-    const bool active = valid && i < Nt;
-    EncSym e = tab[active ? sym[i] : 0];
-    const bool emit = active && ((uint64_t)x >= ((uint64_t)e.f << (32 - sb)));
-    const uint64_t m = (__ballot(emit) >> (grp * lanes)) & gmask;
-    if (emit) {
-      const int64_t at = nw + __popcll(m >> (j + 1));
-      if (at < wcap) words[at] = (uint16_t)(x & 0xffffu);
-      else overflow = true;
-      x >>= 16;
-    }
-    nw += __popcll(m);
-    if (active) {
-      // x = floor(x / f) * M + (x mod f) + cum, via an exact fp64 quotient
-      const uint32_t q = (uint32_t)__fma_rn((double)x, e.rcp, 0x1p-20);
-      x = x + e.cum + q * (M - e.f);
+  constexpr int PF = 8;
+  auto fetch = [&](int k) -> uint32_t {
+    const int32_t i = k * lanes + j;
+    return __builtin_amdgcn_raw_buffer_load_b8(srsrc, (valid && k >= 0 && i < Nt) ? soff + i : sbytes, 0, 0);
+  };
+  // Steps are padded up to a multiple of PF (the padding steps hold no
+  // symbol for any lane) so that the unrolled body has no branch: a branch
+  // would make the ring registers merge across it and wait on their loads.
+  const int kt = (__builtin_amdgcn_readfirstlane(steps_max) + PF - 1) / PF * PF;
+  uint32_t ring[PF];
+#pragma unroll
+  for (int d = 0; d < PF; ++d) ring[d] = fetch(kt - 1 - d);
+  for (int k0 = kt - 1; k0 >= 0; k0 -= PF) {
+#pragma unroll
+    for (int d = 0; d < PF; ++d) {
+      const int k = k0 - d;
+      {
+        const int32_t i = k * lanes + j;
+        const bool active = valid && i < Nt;
+        const EncSym e = tab[ring[d]];
+        // refill after the last use so the load can reuse the same register
+        ring[d] = fetch(k - PF);
+        // renormalise while x >= f 2^(32 - sb): one 16-bit word at most
+        const bool emit = active && (x >> (32 - sb)) >= e.f;
+        const uint64_t bl = __ballot(emit);
+        const uint32_t mlo = (uint32_t)bl & gm_lo, mhi = (uint32_t)(bl >> 32) & gm_hi;
+        const int32_t cnt = (int32_t)(__popc(mlo) + __popc(mhi));
+        // words are written in emission order, higher lanes first
+        const int32_t below = (int32_t)__builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
+        const int32_t at = nw + cnt - 1 - below;
+        const bool fits = at < wcap;
+        overflow |= emit && !fits;
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(x & 0xffffu), wrsrc, (emit && fits) ? woff + 2 * at : wbytes, 0, 0);
+        if (emit) x >>= 16;
+        nw += cnt;
+        // x = floor(x / f) * M + (x mod f) + cum, via an exact fp64 quotient
+        const uint32_t q = (uint32_t)__fma_rn((double)x, e.rcp, 0x1p-20);
+        const uint32_t xn = x + e.cum + q * (M - e.f);
+        x = active ? xn : x;
+        // keep the steps in order so that each ring register is refilled in place
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
   if (valid) state_out[j] = x;
-  const uint64_t ov = (__ballot(overflow) >> (grp * lanes)) & gmask;
+  const uint64_t ov = __ballot(overflow) & gm;
   return ov ? -1 : nw;
 }
 
@@ -209,15 +254,6 @@ __device__ __forceinline__ void build_dec_tables(const uint32_t* cum, int sb, ui
     }
     reinterpret_cast<uint32_t*>(sym_of)[slot >> 2] = w;
   }
-}
-
-// Raw buffer resource over [base, base + bytes) with wave-uniform fields, so
-// the compiler keeps it in scalar registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(void* base, int32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  void* b = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(b, 0, __builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
 constexpr int kRing = 512;  // words of a stream's LDS ring
@@ -325,7 +361,6 @@ __global__ void k_rans_enc_chunks(const Params p) {
   __shared__ EncSym tab[256];
   __shared__ uint8_t bits[256];
   __shared__ int64_t s_P[2];
-  if (threadIdx.x < 256) hist[threadIdx.x] = 0;
   for (int i = threadIdx.x; i < D; i += blockDim.x) bits[i] = p.ws[p.w.side_bits + (int64_t)u * D + i];
   __syncthreads();
   const int n = min(p.chunk_tokens, p.T_mid - ch * p.chunk_tokens);
@@ -344,13 +379,28 @@ __global__ void k_rans_enc_chunks(const Params p) {
     return;
   }
   const uint8_t* packed = p.ws + p.w.packed + (int64_t)c * p.w.packed_slot;
-  // histogram of the chunk's bytes (P is a multiple of 4)
-  for (int64_t i = threadIdx.x; i < P / 4; i += blockDim.x) {
-    uint32_t wv = reinterpret_cast<const uint32_t*>(packed)[i];
-    atomicAdd(&hist[wv & 0xff], 1u);
-    atomicAdd(&hist[(wv >> 8) & 0xff], 1u);
-    atomicAdd(&hist[(wv >> 16) & 0xff], 1u);
-    atomicAdd(&hist[wv >> 24], 1u);
+  // histogram of the chunk's bytes (P is a multiple of 4), in eight
+  // interleaved copies (bin b of copy c at 8 b + c, lane l counts into copy
+  // l % 8) so that lanes hitting a popular byte value spread over banks
+  __shared__ uint32_t hist8[256 * 8];
+  for (int i = threadIdx.x; i < 256 * 8; i += blockDim.x) hist8[i] = 0;
+  __syncthreads();
+  {
+    const uint32_t cpy = lane & 7;
+    for (int64_t i = threadIdx.x; i < P / 4; i += blockDim.x) {
+      const uint32_t wv = reinterpret_cast<const uint32_t*>(packed)[i];
+      atomicAdd(&hist8[8 * (wv & 0xff) + cpy], 1u);
+      atomicAdd(&hist8[8 * ((wv >> 8) & 0xff) + cpy], 1u);
+      atomicAdd(&hist8[8 * ((wv >> 16) & 0xff) + cpy], 1u);
+      atomicAdd(&hist8[8 * (wv >> 24) + cpy], 1u);
+    }
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < 256; b += blockDim.x) {
+    uint32_t sum = 0;
+#pragma unroll
+    for (int c2 = 0; c2 < 8; ++c2) sum += hist8[8 * b + c2];
+    hist[b] = sum;
   }
   __syncthreads();
   if (wave == 0) {
@@ -360,7 +410,7 @@ __global__ void k_rans_enc_chunks(const Params p) {
   }
   __syncthreads();
   uint8_t* slot = p.ws + p.w.rec + (int64_t)c * p.w.rec_slot;
-  if (threadIdx.x < 256) reinterpret_cast<uint16_t*>(slot)[threadIdx.x] = (uint16_t)freq[threadIdx.x];
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) reinterpret_cast<uint16_t*>(slot)[i] = (uint16_t)freq[i];
   // streams: 64/lanes per wave
   const int spw = 64 / p.lanes;
   const int t = wave * spw + lane / p.lanes;
@@ -372,9 +422,9 @@ __global__ void k_rans_enc_chunks(const Params p) {
   for (int o = 32; o > 0; o >>= 1) steps_max = max(steps_max, __shfl_xor(steps_max, o, 64));
   const int tt = valid ? t : 0;
   uint32_t* states = reinterpret_cast<uint32_t*>(slot + slot_states_off(p, tt));
-  uint16_t* words = reinterpret_cast<uint16_t*>(slot + slot_states_off(p, tt) + 4 * p.lanes);
-  int64_t nw = rans_encode_stream(packed + (int64_t)tt * P_full, Nt, valid, steps_max, tab, p.sb,
-                                  p.lanes, words, p.w.tile_words_max, states);
+  const int64_t nw = rans_encode_stream(packed, (int32_t)P, (int32_t)(tt * P_full), (int32_t)Nt, valid, steps_max, tab,
+                                        p.sb, p.lanes, slot, (int32_t)p.w.rec_slot,
+                                        (int32_t)(slot_states_off(p, tt) + 4 * p.lanes), p.w.tile_words_max, states);
   __shared__ int32_t s_nw[64];
   if (valid && (lane % p.lanes) == 0) {
     s_nw[t] = (int32_t)nw;
@@ -397,7 +447,7 @@ __global__ void k_rans_enc_chunks(const Params p) {
 hipError_t launch_rans_encode_chunks(const Params& p, hipStream_t s) {
   int streams = p.tiles_per_chunk;
   int waves = (streams * p.lanes + 63) / 64;
-  if (waves < 4) waves = 4;  // 256 threads: histogram and table use 256
+  if (waves < 1) waves = 1;
   hipLaunchKernelGGL(k_rans_enc_chunks, dim3(p.n_chunks), dim3(64 * waves), 0, s, p);
   return hipGetLastError();
 }
@@ -677,7 +727,8 @@ __global__ void k_test_rans_encode(const uint8_t* sym, int64_t N, const uint16_t
   const int lane = threadIdx.x & 63;
   const bool valid = lane < lanes;  // one stream in the first lane group
   const int steps = (int)((N + lanes - 1) / lanes);
-  int64_t nw = rans_encode_stream(sym, N, valid, steps, tab, sb, lanes, words, cap, states);
+  int64_t nw = rans_encode_stream(sym, (int32_t)N, 0, (int32_t)N, valid, steps, tab, sb, lanes,
+                                  reinterpret_cast<uint8_t*>(words), (int32_t)(2 * cap), 0, cap, states);
   if (lane == 0) *nwords = nw;
 }
 
