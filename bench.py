@@ -44,11 +44,113 @@ def parse():
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--chunk-tokens", type=int, default=1024)
     ap.add_argument("--tile-tokens", type=int, default=256)
-    ap.add_argument("--cpu-layers", type=int, default=4,
+    ap.add_argument("--cpu-layers", type=int, default=8,
                     help="layers of the workload the CPU oracle baseline codes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-phase event pass")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain copy kernel of known size (for scaling HBM counters)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a per-kernel table from a rocprofv3 --stats output folder and exit")
+    ap.add_argument("--summarize-pmc", metavar="DIR",
+                    help="print per-kernel mean counters from a rocprofv3 --pmc csv folder and exit")
     return ap.parse_args()
+
+
+# Phase -> (kernels, sources they are built from).  The roofline's `traffic`
+# is taken from the committed counter summary only while these sources are
+# unchanged since the counters were read.
+PHASE_KERNELS = {
+    "enc_stats": (("k_unrope128", "k_enc128"), ("kernels_encode.hip",)),
+    "enc_quant_pack": (("k_quant128",), ("kernels_quant.hip",)),
+    "rans_encode": (("k_rans_enc_chunks",), ("kernels_rans.hip",)),
+    "assemble": (("k_scan", "k_copy_records"), ("kernels_rans.hip",)),
+    "rans_decode": (("k_rans_dec_chunks",), ("kernels_rans.hip",)),
+    "dec_transform": (("k_dec_pca128",), ("kernels_decode.hip",)),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_llama3_8b.md")
+COPY_CAL_BYTES = 1 << 28  # fp32 elements read and written by the calibration copy
+
+
+def source_digest(files) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in tuple(files) + ("kvtc_internal.h",):
+        with open(os.path.join(ROOT, "tensor_compression_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(phase):
+    """HBM bytes per launch of the phase's kernels from the committed counter
+    summary (rows `| phase | ... | bytes | digest |`), or None when absent or
+    taken on different kernel sources."""
+    if phase not in PHASE_KERNELS or not os.path.exists(TRAFFIC_FILE):
+        return None
+    want = source_digest(PHASE_KERNELS[phase][1])
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) >= 6 and cells[0] == phase:
+                try:
+                    nbytes = float(cells[4])
+                except ValueError:
+                    return None
+                return nbytes if cells[5] == want else None
+    return None
+
+
+def _short_kernel(name: str) -> str:
+    n = name.split("(")[0].replace("void ", "")
+    return n.replace("kvtc::", "")
+
+
+def summarize_trace(d):
+    """Per-kernel calls / mean / min / max (us) from rocprofv3 --stats."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                rows.append((_short_kernel(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                             float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    rows.sort(key=lambda r: -r[1] * r[2])
+    print("| kernel | calls | avg (us) | min (us) | max (us) | % time |")
+    print("|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| {r[0]} | {r[1]} | {r[2]:.1f} | {r[3]:.1f} | {r[4]:.1f} | {r[5]:.1f} |")
+
+
+def summarize_pmc(d):
+    """Mean counter value per dispatch, per kernel, from rocprofv3 --pmc csv."""
+    import collections
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    acc = collections.defaultdict(lambda: collections.defaultdict(float))
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                acc[(_short_kernel(r["Kernel_Name"]), r["Counter_Name"])][r["Dispatch_Id"]] += \
+                    float(r["Counter_Value"])
+    print("| kernel | counter | dispatches | mean per dispatch |")
+    print("|---|---|---|---|")
+    for (k, c), per in sorted(acc.items()):
+        print(f"| {k} | {c} | {len(per)} | {sum(per.values()) / len(per):.6g} |")
+
+
+def copy_calibration():
+    """A plain copy-like kernel of known traffic: out = ~x over 2^28 bytes of
+    int32, read once and written once (torch's bitwise_not kernel, which
+    nothing else here launches)."""
+    import torch
+    x = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.int32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.bitwise_not(x, out=y)
+    torch.cuda.synchronize()
 
 
 def layout(cfg, T):
@@ -103,6 +205,12 @@ def cpu_baseline(w, cfg, K, V, basis, layers):
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} (world size {world}) "
@@ -118,6 +226,8 @@ def main():
 
     kvtc.lib()  # fail loudly if the HIP library is missing
     torch.cuda.init()
+    if args.copy_calibration:
+        copy_calibration()
     w = synth.WORKLOADS[args.workload]
     over = dict(chunk_tokens=args.chunk_tokens, tile_tokens=args.tile_tokens)
     if args.bits is not None:
@@ -248,8 +358,9 @@ def main():
     }
     if dom:
         ach = alg[dom] / (ph_ms[dom] * 1e-3) / 1e9
-        res["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBPS,
-                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": None,
+        res["roofline"] = {"bound": "hbm", "kernel": dom, "kernels": list(PHASE_KERNELS[dom][0]),
+                           "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                           "frac": ach / HBM_PEAK_GBPS, "traffic": traffic_from_profile(dom),
                            "algorithmic_bytes": alg[dom], "avg_ms": ph_ms[dom]}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, cfg, K, V, basis, args.cpu_layers) \

@@ -22,6 +22,9 @@
  * Conventions for every entry point:
  *  - Tensors are contiguous [layers, kv_heads, tokens, head_dim] in the cache
  *    dtype (bf16 or fp32), little-endian, in device memory.
+ *  - Every device pointer passed to encode or decode must be 16-byte aligned
+ *    (allocations from hipMalloc or PyTorch are); otherwise the call returns
+ *    KVTC_ERR_INVALID_ARG.
  *  - The caller owns every buffer (device memory from any allocator, e.g.
  *    PyTorch).  The library never allocates device memory: plan memory and
  *    workspaces are passed in, sized by the *_size queries.

@@ -207,59 +207,56 @@ __global__ void k_clear_status(uint8_t* ws, WsLayout w) {
 
 // to_container = 1: cache -> container (+ zero the side and raw padding);
 // 0: container -> output tensors in out_dtype.
-__global__ void k_copy_raw(const Params p, int to_container) {
-  const int64_t e = p.dtype == KVTC_BF16 ? 2 : 4;
-  const int64_t row_bytes = (int64_t)p.D * e;
-  const int64_t per_tensor_rows = (int64_t)p.L * p.H * (p.s0 + p.W_eff);
-  const int64_t total_rows = 2 * per_tensor_rows;
-  const int64_t words_per_row = row_bytes / 4;
-  const int64_t n = total_rows * words_per_row;
+// Raw regions as contiguous runs: for every (tensor, region, layer x head) the
+// n_region rows are consecutive both in the cache ([L,H,T,D]) and in the
+// container ([L,H,n_region,D] per tensor and region).  Workgroup y = run,
+// x = 4 KiB piece of the run; one 16-byte unit per thread (rows are whole
+// 16-byte units for head_dim 64 and 128).
+__global__ __launch_bounds__(256) void k_copy_raw(const Params p, int to_container) {
+  const int e = p.dtype == KVTC_BF16 ? 2 : 4;
+  const int row_units = p.D * e / 16;
+  const int LH = p.L * p.H;
+  const int run = blockIdx.y;
+  const int s = run / (2 * LH), region = (run / LH) & 1, lh = run % LH;
+  const int n_region = region == 0 ? p.s0 : p.W_eff;
+  const int units = n_region * row_units;
+  const int i = blockIdx.x * 256 + threadIdx.x;
   if (!to_container && (get_status(p.ws, p.w) & (1u << KVTC_ERR_CORRUPT))) return;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    int64_t row = idx / words_per_row, wi = idx % words_per_row;
-    int s = row >= per_tensor_rows;
-    int64_t rr = row - s * per_tensor_rows;
-    int64_t per_lh = p.s0 + p.W_eff;
-    int64_t lh = rr / per_lh, tt = rr % per_lh;
-    int64_t pos = tt < p.s0 ? tt : p.mid_end + (tt - p.s0);
-    // container order: region-major within each tensor
-    int64_t region = tt < p.s0 ? 0 : 1;
-    int64_t n_region = region == 0 ? p.s0 : p.W_eff;
-    int64_t off_region = region == 0 ? 0 : (int64_t)p.L * p.H * p.s0;
-    int64_t crow = (int64_t)s * per_tensor_rows + off_region + lh * n_region + (region == 0 ? tt : tt - p.s0);
-    int64_t tensor_elem = (lh * p.T + pos) * p.D;
+  if (i < units) {
+    const int64_t row_bytes = (int64_t)p.D * e;
+    const int64_t per_tensor = (int64_t)LH * (p.s0 + p.W_eff) * row_bytes;
+    const int64_t coff = (int64_t)s * per_tensor + (region == 0 ? 0 : (int64_t)LH * p.s0 * row_bytes) +
+                         (int64_t)lh * n_region * row_bytes + (int64_t)i * 16;
+    const int64_t pos0 = region == 0 ? 0 : p.mid_end;
+    const int64_t telem = ((int64_t)lh * p.T + pos0) * p.D + (int64_t)i * (16 / e);  // first element of the unit
     if (to_container) {
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(s ? p.v : p.k);
-      reinterpret_cast<uint32_t*>(p.out + p.raw_off)[crow * words_per_row + wi] =
-          src[tensor_elem * e / 4 + wi];
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(s ? p.v : p.k);
+      *reinterpret_cast<uint4*>(p.out + p.raw_off + coff) = *reinterpret_cast<const uint4*>(src + telem * e);
     } else {
-      const uint32_t word = reinterpret_cast<const uint32_t*>(p.in + p.raw_off)[crow * words_per_row + wi];
+      const uint4 w = *reinterpret_cast<const uint4*>(p.in + p.raw_off + coff);
       void* dst = s ? p.v_out : p.k_out;
       if (p.out_dtype == p.dtype) {
-        reinterpret_cast<uint32_t*>(dst)[tensor_elem * e / 4 + wi] = word;
-      } else if (p.dtype == KVTC_BF16) {  // bf16 -> fp32: exact widening
-        float* d = reinterpret_cast<float*>(dst) + tensor_elem + 2 * wi;
-        d[0] = __uint_as_float(word << 16);
-        d[1] = __uint_as_float(word & 0xffff0000u);
-      } else {  // fp32 -> bf16 (RNE)
-        uint16_t* d = reinterpret_cast<uint16_t*>(dst) + tensor_elem + wi;
-        d[0] = f32_to_bf16(__uint_as_float(word));
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(dst) + telem * e) = w;
+      } else if (p.dtype == KVTC_BF16) {  // bf16 -> fp32: exact widening of 8 values
+        uint4* d = reinterpret_cast<uint4*>(reinterpret_cast<float*>(dst) + telem);
+        d[0] = make_uint4(w.x << 16, w.x & 0xffff0000u, w.y << 16, w.y & 0xffff0000u);
+        d[1] = make_uint4(w.z << 16, w.z & 0xffff0000u, w.w << 16, w.w & 0xffff0000u);
+      } else {  // fp32 -> bf16 (RNE) of 4 values
+        const uint32_t lo = (uint32_t)f32_to_bf16(__uint_as_float(w.x)) | ((uint32_t)f32_to_bf16(__uint_as_float(w.y)) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16(__uint_as_float(w.z)) | ((uint32_t)f32_to_bf16(__uint_as_float(w.w)) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dst) + telem) = make_uint2(lo, hi);
       }
     }
   }
-  if (to_container) {
-    // zero padding: [end of side records and r area, raw_off) and raw tail
-    int64_t side_used = p.r_off - p.side_off;  // section records
+  if (to_container && run == 0 && blockIdx.x == 0 && threadIdx.x < 64) {
+    // zero padding: the gap between the side records (and r area) and
+    // raw_off, and the raw area's tail; each is shorter than 16 bytes
     int64_t r_used = 0;
     if (p.transform == KVTC_WHT) r_used = (int64_t)(p.wht_keys ? 2 : 1) * p.L * p.H * p.T_mid * 4;
-    int64_t a0 = p.side_off + side_used + r_used, a1 = p.raw_off;
-    int64_t b0 = p.raw_off + total_rows * row_bytes, b1 = p.raw_off + p.raw_bytes;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (a1 - a0) + (b1 - b0);
-         i += (int64_t)gridDim.x * blockDim.x) {
-      int64_t at = i < (a1 - a0) ? a0 + i : b0 + (i - (a1 - a0));
-      p.out[at] = 0;
-    }
+    const int64_t a0 = p.r_off + r_used, a1 = p.raw_off;
+    const int64_t b0 = p.raw_off + 2 * (int64_t)LH * (p.s0 + p.W_eff) * p.D * e, b1 = p.raw_off + p.raw_bytes;
+    const int64_t na = a1 - a0, nb = b1 - b0;
+    for (int64_t k = threadIdx.x; k < na + nb; k += 64) p.out[k < na ? a0 + k : b0 + (k - na)] = 0;
   }
 }
 
@@ -267,12 +264,13 @@ hipError_t launch_copy_raw(const Params& p, int to_container, hipStream_t s) {
   if (to_container) {
     hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(64), 0, s, p.ws, p.w);
   }
-  int64_t e = p.dtype == KVTC_BF16 ? 2 : 4;
-  int64_t words = 2 * (int64_t)p.L * p.H * (p.s0 + p.W_eff) * p.D * e / 4 + 64;
-  int64_t blocks = (words + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(k_copy_raw, dim3((unsigned)blocks), dim3(256), 0, s, p, to_container);
+  const int e = p.dtype == KVTC_BF16 ? 2 : 4;
+  if ((p.D * e) % 16) return hipErrorInvalidValue;
+  const int64_t units = (int64_t)(p.s0 > p.W_eff ? p.s0 : p.W_eff) * (p.D * e / 16);
+  const int64_t bx = units > 0 ? (units + 255) / 256 : 1;
+  const int64_t runs = 4 * (int64_t)p.L * p.H;
+  if (bx > 65535 || runs > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_copy_raw, dim3((unsigned)bx, (unsigned)runs), dim3(256), 0, s, p, to_container);
   return hipGetLastError();
 }
 
@@ -835,58 +833,77 @@ __global__ __launch_bounds__(256) void k_enc_wht(const Params p, int sec0, float
 // each of its RoPE pairs in either pairing style.
 // ---------------------------------------------------------------------------
 
+// LDS image of a table row: pair j at float offset 18 (j / 8) + 2 (j % 8), so
+// the 8 lanes of a row read 8 distinct bank pairs in either pairing style.
+__device__ __forceinline__ int cs_at(int t, int j) { return t * 144 + 18 * (j >> 3) + 2 * (j & 7); }
+
 __global__ __launch_bounds__(256) void k_unrope128(const Params p) {
   constexpr int D = 128;
   const int l = blockIdx.y, t0 = blockIdx.x * 16;
   const int nt = min(16, p.T_mid - t0);
   if (nt <= 0) return;
   const int tid = threadIdx.x;
-  __shared__ float2 cs[16 * 64];
+  __shared__ __attribute__((aligned(16))) float cs[16 * 144];
   {
-    const float4* srow = reinterpret_cast<const float4*>(p.rope + (int64_t)(p.mid_begin + t0) * 64);
-    for (int i = tid; i < nt * 32; i += 256) reinterpret_cast<float4*>(cs)[i] = srow[i];
+    const float2* srow = p.rope + (int64_t)(p.mid_begin + t0) * 64;
+    for (int i = tid; i < nt * 64; i += 256)
+      *reinterpret_cast<float2*>(cs + cs_at(i >> 6, i & 63)) = srow[i];
   }
   __syncthreads();
   const int q = tid & 7;
   const bool half = p.rope_style == KVTC_ROPE_HALF;
   const uint16_t* kin = reinterpret_cast<const uint16_t*>(p.k);
   uint16_t* kout = reinterpret_cast<uint16_t*>(p.ws + p.w.kprime);
-  for (int ri = tid >> 3; ri < p.H * nt; ri += 32) {
-    const int h = ri / nt, t = ri % nt;
-    const uint16_t* in = kin + (((int64_t)l * p.H + h) * p.T + p.mid_begin + t0 + t) * D;
-    const uint4 a = *reinterpret_cast<const uint4*>(in + 8 * q);
-    const uint4 b = *reinterpret_cast<const uint4*>(in + 64 + 8 * q);
-    float ya[8], yb[8];
-    unpack_bf16x8(a, ya);
-    unpack_bf16x8(b, yb);
-    const float2* row = cs + t * 64;
-    if (half) {
-      // pair j = 8q + e: (channel j, channel j + 64)
+  const int rows = p.H * nt;
+  // row ri = (token t = ri / H, head h = ri % H): the lanes of a wave share a
+  // token (table reads broadcast); each thread loads four rows before using them
+  for (int ri0 = tid >> 3; ri0 < rows; ri0 += 4 * 32) {
+    uint4 a[4], b[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float2 c = row[8 * q + e];
-        const float xa = __fmaf_rn(ya[e], c.x, __fmul_rn(yb[e], c.y));
-        const float xb = __fmaf_rn(yb[e], c.x, -__fmul_rn(ya[e], c.y));
-        ya[e] = xa;
-        yb[e] = xb;
-      }
-    } else {
-      // pairs (2m, 2m + 1): m = 4q + e/2 in the low run, 32 + 4q + e/2 in the high run
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float2 cl = row[4 * q + m], ch = row[32 + 4 * q + m];
-        const float a0 = ya[2 * m], a1 = ya[2 * m + 1], b0 = yb[2 * m], b1 = yb[2 * m + 1];
-        ya[2 * m] = __fmaf_rn(a0, cl.x, __fmul_rn(a1, cl.y));
-        ya[2 * m + 1] = __fmaf_rn(a1, cl.x, -__fmul_rn(a0, cl.y));
-        yb[2 * m] = __fmaf_rn(b0, ch.x, __fmul_rn(b1, ch.y));
-        yb[2 * m + 1] = __fmaf_rn(b1, ch.x, -__fmul_rn(b0, ch.y));
-      }
+    for (int k = 0; k < 4; ++k) {
+      const int ri = min(ri0 + 32 * k, rows - 1);
+      const int t = ri / p.H, h = ri % p.H;
+      const uint16_t* in = kin + (((int64_t)l * p.H + h) * p.T + p.mid_begin + t0 + t) * D;
+      a[k] = *reinterpret_cast<const uint4*>(in + 8 * q);
+      b[k] = *reinterpret_cast<const uint4*>(in + 64 + 8 * q);
     }
-    uint16_t* o = kout + (((int64_t)l * p.H + h) * p.T_mid + t0 + t) * D;
-    *reinterpret_cast<uint4*>(o + 8 * q) =
-        make_uint4(pack2_bf16(ya[0], ya[1]), pack2_bf16(ya[2], ya[3]), pack2_bf16(ya[4], ya[5]), pack2_bf16(ya[6], ya[7]));
-    *reinterpret_cast<uint4*>(o + 64 + 8 * q) =
-        make_uint4(pack2_bf16(yb[0], yb[1]), pack2_bf16(yb[2], yb[3]), pack2_bf16(yb[4], yb[5]), pack2_bf16(yb[6], yb[7]));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int ri = ri0 + 32 * k;
+      if (ri >= rows) break;
+      const int t = ri / p.H, h = ri % p.H;
+      float ya[8], yb[8];
+      unpack_bf16x8(a[k], ya);
+      unpack_bf16x8(b[k], yb);
+      if (half) {
+        // pair j = 8q + e: (channel j, channel j + 64)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float2 c = *reinterpret_cast<const float2*>(cs + cs_at(t, 8 * q + e));
+          const float xa = __fmaf_rn(ya[e], c.x, __fmul_rn(yb[e], c.y));
+          const float xb = __fmaf_rn(yb[e], c.x, -__fmul_rn(ya[e], c.y));
+          ya[e] = xa;
+          yb[e] = xb;
+        }
+      } else {
+        // pairs (2m, 2m + 1): m = 4q + e/2 in the low run, 32 + 4q + e/2 in the high run
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float2 cl = *reinterpret_cast<const float2*>(cs + cs_at(t, 4 * q + m));
+          const float2 ch = *reinterpret_cast<const float2*>(cs + cs_at(t, 32 + 4 * q + m));
+          const float a0 = ya[2 * m], a1 = ya[2 * m + 1], b0 = yb[2 * m], b1 = yb[2 * m + 1];
+          ya[2 * m] = __fmaf_rn(a0, cl.x, __fmul_rn(a1, cl.y));
+          ya[2 * m + 1] = __fmaf_rn(a1, cl.x, -__fmul_rn(a0, cl.y));
+          yb[2 * m] = __fmaf_rn(b0, ch.x, __fmul_rn(b1, ch.y));
+          yb[2 * m + 1] = __fmaf_rn(b1, ch.x, -__fmul_rn(b0, ch.y));
+        }
+      }
+      uint16_t* o = kout + (((int64_t)l * p.H + h) * p.T_mid + t0 + t) * D;
+      *reinterpret_cast<uint4*>(o + 8 * q) =
+          make_uint4(pack2_bf16(ya[0], ya[1]), pack2_bf16(ya[2], ya[3]), pack2_bf16(ya[4], ya[5]), pack2_bf16(ya[6], ya[7]));
+      *reinterpret_cast<uint4*>(o + 64 + 8 * q) =
+          make_uint4(pack2_bf16(yb[0], yb[1]), pack2_bf16(yb[2], yb[3]), pack2_bf16(yb[4], yb[5]), pack2_bf16(yb[6], yb[7]));
+    }
   }
 }
 

@@ -347,7 +347,9 @@ __device__ __forceinline__ int64_t tile_bytes(const uint8_t* bits, int D, int nt
 
 // record slot of chunk c: [freq u16 x256][nwords u32 x tiles][tile t: states, words]
 __device__ __forceinline__ int64_t slot_states_off(const Params& p, int t) {
-  return 512 + 4 * (int64_t)p.tiles_per_chunk + (int64_t)t * (4 * p.lanes + 2 * p.w.tile_words_max + 4);
+  // 16-byte aligned: 4 lanes and 2 tile_words_max + 4 are multiples of 16
+  return ((512 + 4 * (int64_t)p.tiles_per_chunk + 15) & ~(int64_t)15) +
+         (int64_t)t * (4 * p.lanes + 2 * p.w.tile_words_max + 4);
 }
 
 __global__ void k_rans_enc_chunks(const Params p) {
@@ -506,35 +508,47 @@ __global__ __launch_bounds__(1024) void k_scan(const Params p, HeaderBytes hdr) 
   }
 }
 
-__global__ void k_copy_records(const Params p) {
+__global__ __launch_bounds__(256) void k_copy_records(const Params p) {
   const int c = blockIdx.x;
   if (get_status(p.ws, p.w) & ((1u << KVTC_ERR_CAPACITY) | (1u << KVTC_ERR_NONFINITE))) return;
   const uint32_t size = reinterpret_cast<const uint32_t*>(p.ws + p.w.rec_size)[c];
   if (size == 0) return;
   const uint64_t pos = reinterpret_cast<const uint64_t*>(p.ws + p.w.rec_pos)[c];
   const uint8_t* slot = p.ws + p.w.rec + (int64_t)c * p.w.rec_slot;
-  uint8_t* dst = p.out + p.chunks_off + pos;
+  uint8_t* dst = p.out + p.chunks_off + pos;  // 16-byte aligned record
   const int ch = c % p.chunks_per_sec;
   const int n = min(p.chunk_tokens, p.T_mid - ch * p.chunk_tokens);
   const int ntiles = (n + p.tile_tokens - 1) / p.tile_tokens;
   const uint32_t* nwv = reinterpret_cast<const uint32_t*>(slot + 512);
+  const int tid = threadIdx.x;
+  // dword copy of n_dw dwords; the last one keeps only its low half when
+  // `half_last` (an odd word count padded with zeros)
+  auto copy_dw = [&](const uint32_t* src, uint32_t* d, int n_dw, bool half_last) {
+    for (int i0 = 0; i0 < n_dw; i0 += 4 * 256) {
+      uint32_t v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = i0 + k * 256 + tid;
+        v[k] = i < n_dw ? src[i] : 0u;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = i0 + k * 256 + tid;
+        if (i < n_dw) d[i] = (half_last && i == n_dw - 1) ? (v[k] & 0xffffu) : v[k];
+      }
+    }
+  };
   // table and word counts
-  const int head = (512 + 4 * ntiles) / 2;
-  for (int i = threadIdx.x; i < head; i += blockDim.x)
-    reinterpret_cast<uint16_t*>(dst)[i] = reinterpret_cast<const uint16_t*>(slot)[i];
+  copy_dw(reinterpret_cast<const uint32_t*>(slot), reinterpret_cast<uint32_t*>(dst), 128 + ntiles, false);
   int64_t at = 512 + 4 * (int64_t)ntiles;
   for (int t = 0; t < ntiles; ++t) {
     const uint32_t nw = nwv[t];
-    const int64_t so = slot_states_off(p, t);
-    const int64_t piece = 4 * (int64_t)p.lanes + 2 * (int64_t)nw;
-    const int64_t piece_padded = piece + ((nw & 1) ? 2 : 0);
-    for (int64_t i = threadIdx.x; i < piece_padded / 2; i += blockDim.x) {
-      uint16_t v = 2 * i < piece ? reinterpret_cast<const uint16_t*>(slot + so)[i] : 0;
-      reinterpret_cast<uint16_t*>(dst + at)[i] = v;
-    }
-    at += piece_padded;
+    const int n_dw = p.lanes + (int)((nw + 1) >> 1);  // states, words, zero pad to 4 bytes
+    copy_dw(reinterpret_cast<const uint32_t*>(slot + slot_states_off(p, t)), reinterpret_cast<uint32_t*>(dst + at),
+            n_dw, (nw & 1) != 0);
+    at += 4 * (int64_t)n_dw;
   }
-  for (int64_t i = at + threadIdx.x; i < size; i += blockDim.x) dst[i] = 0;
+  for (int64_t i = at + tid; i < size; i += 256) dst[i] = 0;
 }
 
 hipError_t launch_assemble(const Params& p, const uint8_t* hdr, hipStream_t s) {

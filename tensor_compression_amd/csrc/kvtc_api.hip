@@ -121,8 +121,9 @@ WsLayout make_ws_layout(const kvtc_config& c, const Layout& lo) {
   int64_t tile_max = max_tile_bytes(c, c.tile_tokens, bmax);
   w.packed_slot = align16(tile_max * lo.tiles_per_chunk);
   w.packed = take(at, (int64_t)lo.n_chunks * w.packed_slot);
-  w.tile_words_max = max_words(tile_max, c);
-  w.rec_slot = align16(512 + 4 * (int64_t)lo.tiles_per_chunk +
+  // capacity rounded so that every tile piece of a slot starts 16-byte aligned
+  w.tile_words_max = ((max_words(tile_max, c) + 2 + 7) & ~(int64_t)7) - 2;
+  w.rec_slot = align16(align16(512 + 4 * (int64_t)lo.tiles_per_chunk) +
                        (int64_t)lo.tiles_per_chunk * (4 * c.rans_lanes + 2 * w.tile_words_max + 4));
   w.rec = take(at, (int64_t)lo.n_chunks * w.rec_slot);
   w.rec_size = take(at, (int64_t)lo.n_chunks * 4);
@@ -426,12 +427,16 @@ kvtc_status kvtc_workspace_size(kvtc_plan_t plan, int32_t T, size_t* ws_bytes,
   return KVTC_OK;
 }
 
+// Kernels move 16-byte units of every buffer.
+static bool misaligned(const void* ptr) { return ((uintptr_t)ptr & 15u) != 0; }
+
 kvtc_status kvtc_encode(kvtc_plan_t plan, const void* k, const void* v, int32_t T, void* out,
                         size_t cap, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (!plan || !out || !ws) return KVTC_ERR_INVALID_ARG;
   PlanImpl* pl = (PlanImpl*)plan;
   if (T < 0 || T > pl->cfg.max_tokens) return KVTC_ERR_INVALID_ARG;
   if (T > 0 && (!k || !v)) return KVTC_ERR_INVALID_ARG;
+  if (misaligned(k) || misaligned(v) || misaligned(out) || misaligned(ws)) return KVTC_ERR_INVALID_ARG;
   Layout lo = make_layout(pl->cfg, T);
   WsLayout w = make_ws_layout(pl->cfg, lo);
   if ((int64_t)ws_bytes < w.total) return KVTC_ERR_CAPACITY;
@@ -468,6 +473,7 @@ kvtc_status kvtc_decode(kvtc_plan_t plan, const void* in, size_t in_bytes, int32
   if (T < 0 || T > pl->cfg.max_tokens) return KVTC_ERR_INVALID_ARG;
   if (T > 0 && (!k_out || !v_out)) return KVTC_ERR_INVALID_ARG;
   if (out_dtype != KVTC_BF16 && out_dtype != KVTC_FP32) return KVTC_ERR_INVALID_ARG;
+  if (misaligned(in) || misaligned(k_out) || misaligned(v_out) || misaligned(ws)) return KVTC_ERR_INVALID_ARG;
   Layout lo = make_layout(pl->cfg, T);
   WsLayout w = make_ws_layout(pl->cfg, lo);
   if ((int64_t)ws_bytes < w.total) return KVTC_ERR_CAPACITY;
