@@ -172,6 +172,50 @@ kvtc_status kvtc_decode(kvtc_plan_t plan, const void* in, size_t in_bytes, int32
                         void* k_out, void* v_out, int32_t out_dtype, void* ws, size_t ws_bytes,
                         hipStream_t stream);
 
+/* ---- paged ragged batches ---------------------------------------------- */
+
+/* A batch of n_seqs independent sequences whose K and V live in page pools
+ * [layers, pool_pages, kv_heads, 16, head_dim] (cache dtype): token t of
+ * sequence z is row t % 16 of page page_table[z * max_pages + t / 16].  Each
+ * sequence is coded on its own, exactly as kvtc_encode codes a contiguous
+ * cache of its length (regions, sections and chunks are per sequence, as in
+ * "KVTC: The Open-Source KV Cache Codec That Treats LLM Memory Like Media",
+ * "How the Pipeline Works"); the batch container holds the sequence
+ * containers in order:
+ *   bytes 0..63: "KVTB", u32 version 1, u32 n_seqs, u32 header bytes,
+ *                u64 total bytes, zeros;
+ *   then per sequence u64 offset, u64 size of its container;
+ *   sequence containers start 256-byte aligned, gaps are zero.
+ * Every phase is one launch over the whole batch.  Supported for the bf16,
+ * head_dim 128, PCA configurations with tile_tokens % 64 == 0 (otherwise
+ * KVTC_ERR_UNSUPPORTED).
+ *
+ * seq_lens_host and seq_lens_dev hold the same n_seqs lengths (host copy for
+ * sizing the launches, device copy for the kernels); page_table and
+ * seq_lens_dev are device int32 arrays (4-byte aligned).  The device checks
+ * the lengths against the host's (sum and maximum) and every page index
+ * against pool_pages; a mismatch sets KVTC_ERR_INVALID_ARG in the status and
+ * codes nothing.  Page pools must not overlap the container or workspace. */
+
+/* Workspace and worst-case container bytes of a batch. */
+kvtc_status kvtc_workspace_size_paged(kvtc_plan_t plan, int32_t n_seqs, const int32_t* seq_lens_host,
+                                      size_t* ws_bytes, size_t* max_container_bytes);
+
+/* Encode a paged batch into `out` (device, cap bytes).  Asynchronous; read
+ * the total size and status with kvtc_result(). */
+kvtc_status kvtc_encode_paged(kvtc_plan_t plan, const void* k_pool, const void* v_pool, int32_t pool_pages,
+                              const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens_dev,
+                              const int32_t* seq_lens_host, int32_t n_seqs, void* out, size_t cap, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
+/* Decode a batch container into the pages of k_pool and v_pool (cache dtype)
+ * named by the page table; only the pages of the sequences' tokens are
+ * written.  Asynchronous; a damaged container sets KVTC_ERR_CORRUPT. */
+kvtc_status kvtc_decode_paged(kvtc_plan_t plan, const void* in, size_t in_bytes, void* k_pool, void* v_pool,
+                              int32_t pool_pages, const int32_t* page_table, int32_t max_pages,
+                              const int32_t* seq_lens_dev, const int32_t* seq_lens_host, int32_t n_seqs, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
 /* After synchronising the stream of the last encode/decode that used ws:
  * the container size of that encode (0 after a decode) and the status the
  * device recorded.  Blocking device-to-host copy of 16 bytes. */

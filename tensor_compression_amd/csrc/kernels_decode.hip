@@ -417,7 +417,9 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 
 // Per-wave part: chunk `ch` of section u with KB K slices of 32 sorted
 // components (entries past the coded components are zero).
-template <int KB, int KBS, int OB>
+// PG: the output is a paged pool (bf16); rows are addressed through the page
+// table and lanes past the section store to a scratch row of the workspace.
+template <int KB, int KBS, int OB, bool PG>
 __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, const uint4* sA,
                                              uint32_t* tb, uint4* kw, const DecKInfo* s_ki,
                                              const uint8_t* s_rank, const uint32_t* s_b,
@@ -434,8 +436,10 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
   // the (layer, head) slab of the output as a buffer resource: stores of
   // lanes past the section get an offset at the slab end and are dropped by
   // the range check, so every store instruction is issued unconditionally
-  uint8_t* slab = reinterpret_cast<uint8_t*>(s ? p.v_out : p.k_out) + lh_row0 * D * OB;
-  const int32_t slab_bytes = p.T * D * OB;
+  uint8_t* obase = reinterpret_cast<uint8_t*>(s ? p.v_out : p.k_out);
+  uint8_t* slab = obase + (PG ? 0 : lh_row0 * D * OB);
+  const int32_t slab_bytes = PG ? 0 : p.T * D * OB;
+  uint8_t* const dummy = p.ws + p.w.fixed;  // PG: scratch row for lanes past the section
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(slab, 0, slab_bytes, 0x00020000);
   const uint32_t* slot = reinterpret_cast<const uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot);
 
@@ -491,6 +495,9 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
     __builtin_amdgcn_wave_barrier();
 
     for (int sub = 0; sub * 64 < nt; ++sub) {
+      // PG: page of token `lane` of the sub-tile (clamped into the sequence)
+      int32_t pg = 0;
+      if constexpr (PG) pg = p.page_row[min(p.mid_begin + t0 + ta + sub * 64 + lane, p.T - 1) >> 4];
       brow[2 * lane] = nrow[0];
       brow[2 * lane + 1] = nrow[1];
       fetch_rows(ta + sub * 64 + 64);
@@ -612,7 +619,19 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
               }
             }
           }
-          {
+          if constexpr (PG) {
+            const int64_t page = __shfl(pg, kk * 16 + r, 64);
+            uint8_t* rowp = valid ? obase + ((((page + (int64_t)l * p.pool_pages) * p.H + h) << 4) + (pos & 15)) * D * 2
+                                  : dummy;
+#pragma unroll
+            for (int pq = 0; pq < 2; ++pq) {
+              const int pp = hf + 2 * pq;
+              const f32x4_t x0 = acc[2 * pq], x1 = acc[2 * pq + 1];
+              const int c0 = 32 * pp + 8 * g;
+              *reinterpret_cast<u32x4_t*>(rowp + 2 * c0) =
+                  u32x4_t{pk_bf16(x0[0], x0[1]), pk_bf16(x0[2], x0[3]), pk_bf16(x1[0], x1[1]), pk_bf16(x1[2], x1[3])};
+            }
+          } else {
             const int32_t vo = valid ? (int32_t)(((int64_t)pos * D) * OB) : slab_bytes;
 #pragma unroll
             for (int pq = 0; pq < 2; ++pq) {
@@ -636,8 +655,9 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
 
 // KBMAX = 3 serves sections with at most 96 coded components, KBMAX = 4 the
 // rest; each instantiation leaves the other's sections alone.
-template <int KBMAX>
-__global__ __launch_bounds__(256, 2) void k_dec_pca128(const Params p) {
+template <int KBMAX, bool PG>
+__global__ __launch_bounds__(256, 2) void k_dec_pca128(const Params p0) {
+  const Params p = at_seq(p0, blockIdx.z);
   constexpr int D = 128;
   const int u = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
@@ -731,8 +751,19 @@ __global__ __launch_bounds__(256, 2) void k_dec_pca128(const Params p) {
   const uint32_t fw = (uint32_t)s_misc[2];
   const int tbw = (int)(((int64_t)p.tile_tokens * (p.budget_k > p.budget_v ? p.budget_k : p.budget_v) + 31) / 32) + D + 20;
   uint32_t* tb = work + wave * tbw;
-#define KVTC_DEC_CHUNK(KBV, OBV) dec_chunk128<KBV, KBMAX, OBV>(p, u, ch, sA, tb, s_kw[wave], s_ki, s_rank, s_b, s_const, fw, nnz, s_brow[wave])
-  if constexpr (KBMAX == 4) {
+#define KVTC_DEC_CHUNK(KBV, OBV) dec_chunk128<KBV, KBMAX, OBV, PG>(p, u, ch, sA, tb, s_kw[wave], s_ki, s_rank, s_b, s_const, fw, nnz, s_brow[wave])
+  if constexpr (PG) {  // pools hold the cache dtype: bf16
+    if constexpr (KBMAX == 4) {
+      KVTC_DEC_CHUNK(4, 2);
+    } else {
+      switch (KB) {
+        case 0: KVTC_DEC_CHUNK(0, 2); break;
+        case 1: KVTC_DEC_CHUNK(1, 2); break;
+        case 2: KVTC_DEC_CHUNK(2, 2); break;
+        default: KVTC_DEC_CHUNK(3, 2); break;
+      }
+    }
+  } else if constexpr (KBMAX == 4) {
     if (p.out_dtype == KVTC_BF16) KVTC_DEC_CHUNK(4, 2);
     else KVTC_DEC_CHUNK(4, 4);
   } else if (p.out_dtype == KVTC_BF16) {
@@ -763,17 +794,26 @@ hipError_t launch_dec_transform(const Params& p, hipStream_t s) {
   const int32_t bmax = p.budget_k > p.budget_v ? p.budget_k : p.budget_v;
   const int32_t nz = bmax < p.D ? bmax : p.D;
   const size_t tile_words = (size_t)(((int64_t)p.tile_tokens * bmax + 31) / 32 + nz) + 4;
-  if (p.D == 128 && p.dtype == KVTC_BF16 && p.tile_tokens % 64 == 0 && (int64_t)p.T * 128 * ob < (1ll << 31)) {
+  if (p.D == 128 && p.dtype == KVTC_BF16 && p.tile_tokens % 64 == 0 &&
+      (p.n_seqs > 0 || (int64_t)p.T * 128 * ob < (1ll << 31))) {
     const int tbw = (int)(((int64_t)p.tile_tokens * bmax + 31) / 32) + 128 + 20;
     size_t work = (size_t)4 * tbw * 4;
     if (work < (size_t)128 * kBS * 2) work = (size_t)128 * kBS * 2;
     const size_t lds3 = (size_t)2 * 4 * 3 * 64 * 16 + work, lds4 = (size_t)2 * 4 * 4 * 64 * 16 + work;
     if (lds4 <= 140 * 1024) {
-      dim3 g4((p.chunks_per_sec + 3) / 4, p.n_sections);
-      (void)hipFuncSetAttribute((const void*)k_dec_pca128<3>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3);
-      (void)hipFuncSetAttribute((const void*)k_dec_pca128<4>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds4);
-      hipLaunchKernelGGL(k_dec_pca128<3>, g4, block, lds3, s, p);
-      hipLaunchKernelGGL(k_dec_pca128<4>, g4, block, lds4, s, p);
+      dim3 g4((p.chunks_per_sec + 3) / 4, p.n_sections, seq_grid(p));
+      if (p.n_seqs > 0) {
+        if (ob != 2) return hipErrorInvalidValue;
+        (void)hipFuncSetAttribute((const void*)k_dec_pca128<3, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3);
+        (void)hipFuncSetAttribute((const void*)k_dec_pca128<4, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds4);
+        hipLaunchKernelGGL((k_dec_pca128<3, true>), g4, block, lds3, s, p);
+        hipLaunchKernelGGL((k_dec_pca128<4, true>), g4, block, lds4, s, p);
+        return hipGetLastError();
+      }
+      (void)hipFuncSetAttribute((const void*)k_dec_pca128<3, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3);
+      (void)hipFuncSetAttribute((const void*)k_dec_pca128<4, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds4);
+      hipLaunchKernelGGL((k_dec_pca128<3, false>), g4, block, lds3, s, p);
+      hipLaunchKernelGGL((k_dec_pca128<4, false>), g4, block, lds4, s, p);
       return hipGetLastError();
     }
   }

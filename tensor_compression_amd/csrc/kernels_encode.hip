@@ -212,7 +212,8 @@ __global__ void k_clear_status(uint8_t* ws, WsLayout w) {
 // container ([L,H,n_region,D] per tensor and region).  Workgroup y = run,
 // x = 4 KiB piece of the run; one 16-byte unit per thread (rows are whole
 // 16-byte units for head_dim 64 and 128).
-__global__ __launch_bounds__(256) void k_copy_raw(const Params p, int to_container) {
+__global__ __launch_bounds__(256) void k_copy_raw(const Params p0, int to_container) {
+  const Params p = at_seq(p0, blockIdx.z);
   const int e = p.dtype == KVTC_BF16 ? 2 : 4;
   const int row_units = p.D * e / 16;
   const int LH = p.L * p.H;
@@ -227,8 +228,10 @@ __global__ __launch_bounds__(256) void k_copy_raw(const Params p, int to_contain
     const int64_t per_tensor = (int64_t)LH * (p.s0 + p.W_eff) * row_bytes;
     const int64_t coff = (int64_t)s * per_tensor + (region == 0 ? 0 : (int64_t)LH * p.s0 * row_bytes) +
                          (int64_t)lh * n_region * row_bytes + (int64_t)i * 16;
-    const int64_t pos0 = region == 0 ? 0 : p.mid_end;
-    const int64_t telem = ((int64_t)lh * p.T + pos0) * p.D + (int64_t)i * (16 / e);  // first element of the unit
+    const int pos0 = region == 0 ? 0 : p.mid_end;
+    const int row = i / row_units, ui = i - row * row_units;
+    // first element of the unit
+    const int64_t telem = cache_row(p, lh / p.H, lh % p.H, pos0 + row) + (int64_t)ui * (16 / e);
     if (to_container) {
       const uint8_t* src = reinterpret_cast<const uint8_t*>(s ? p.v : p.k);
       *reinterpret_cast<uint4*>(p.out + p.raw_off + coff) = *reinterpret_cast<const uint4*>(src + telem * e);
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(256) void k_copy_raw(const Params p, int to_contain
 }
 
 hipError_t launch_copy_raw(const Params& p, int to_container, hipStream_t s) {
-  if (to_container) {
+  if (to_container && p.n_seqs == 0) {
     hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(64), 0, s, p.ws, p.w);
   }
   const int e = p.dtype == KVTC_BF16 ? 2 : 4;
@@ -270,7 +273,7 @@ hipError_t launch_copy_raw(const Params& p, int to_container, hipStream_t s) {
   const int64_t bx = units > 0 ? (units + 255) / 256 : 1;
   const int64_t runs = 4 * (int64_t)p.L * p.H;
   if (bx > 65535 || runs > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_copy_raw, dim3((unsigned)bx, (unsigned)runs), dim3(256), 0, s, p, to_container);
+  hipLaunchKernelGGL(k_copy_raw, dim3((unsigned)bx, (unsigned)runs, seq_grid(p)), dim3(256), 0, s, p, to_container);
   return hipGetLastError();
 }
 
@@ -837,7 +840,8 @@ __global__ __launch_bounds__(256) void k_enc_wht(const Params p, int sec0, float
 // the 8 lanes of a row read 8 distinct bank pairs in either pairing style.
 __device__ __forceinline__ int cs_at(int t, int j) { return t * 144 + 18 * (j >> 3) + 2 * (j & 7); }
 
-__global__ __launch_bounds__(256) void k_unrope128(const Params p) {
+__global__ __launch_bounds__(256) void k_unrope128(const Params p0) {
+  const Params p = at_seq(p0, blockIdx.z);
   constexpr int D = 128;
   const int l = blockIdx.y, t0 = blockIdx.x * 16;
   const int nt = min(16, p.T_mid - t0);
@@ -863,7 +867,7 @@ __global__ __launch_bounds__(256) void k_unrope128(const Params p) {
     for (int k = 0; k < 4; ++k) {
       const int ri = min(ri0 + 32 * k, rows - 1);
       const int t = ri / p.H, h = ri % p.H;
-      const uint16_t* in = kin + (((int64_t)l * p.H + h) * p.T + p.mid_begin + t0 + t) * D;
+      const uint16_t* in = kin + cache_row(p, l, h, p.mid_begin + t0 + t);
       a[k] = *reinterpret_cast<const uint4*>(in + 8 * q);
       b[k] = *reinterpret_cast<const uint4*>(in + 64 + 8 * q);
     }
@@ -924,7 +928,8 @@ __global__ __launch_bounds__(256) void k_unrope128(const Params p) {
 constexpr int kXS = 136;  // LDS row stride (bf16) of staged tokens: 16-B aligned, 4-bank shift
 
 template <int MODE>
-__global__ __launch_bounds__(256) void k_enc128(const Params p, int sec0, float* coef_out) {
+__global__ __launch_bounds__(256) void k_enc128(const Params p0, int sec0, float* coef_out) {
+  const Params p = at_seq(p0, blockIdx.z);
   constexpr int D = 128;
   const int u = blockIdx.y + sec0, ch = blockIdx.x;
   const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
@@ -990,7 +995,7 @@ __global__ __launch_bounds__(256) void k_enc128(const Params p, int sec0, float*
     const int pos = p.mid_begin + t0 + tok;
     ya0 = ya1 = yb0 = yb1 = make_uint4(0, 0, 0, 0);
     if (valid) {
-      const uint16_t* row = src + (lh_row0 + pos_base + t0 + tok) * D;
+      const uint16_t* row = src + (pre ? (lh_row0 + pos_base + t0 + tok) * D : cache_row(p, l, h, pos));
       ya0 = *reinterpret_cast<const uint4*>(row + 16 * st_q);
       ya1 = *reinterpret_cast<const uint4*>(row + 16 * st_q + 8);
       yb0 = *reinterpret_cast<const uint4*>(row + 64 + 16 * st_q);
@@ -1251,7 +1256,7 @@ static size_t tile_lds_bytes(const Params& p) {
 }
 
 hipError_t launch_enc_transform(const Params& p, int mode, hipStream_t s) {
-  dim3 grid(p.chunks_per_sec, p.n_sections), block(256);
+  dim3 grid(p.chunks_per_sec, p.n_sections, seq_grid(p)), block(256);
   size_t lds = mode == 1 ? quant_lds_bytes(p, tile_lds_bytes(p)) : 0;
   if (p.transform == KVTC_WHT) {
     if (mode == 0) hipLaunchKernelGGL(k_enc_wht<0>, grid, block, 0, s, p, 0, (float*)nullptr, (float*)nullptr);
@@ -1260,7 +1265,7 @@ hipError_t launch_enc_transform(const Params& p, int mode, hipStream_t s) {
   }
   if (p.D == 128 && p.dtype == KVTC_BF16 && (p.tile_tokens % 64) == 0) {
     if (mode == 0) {
-      if (p.rope_keys) hipLaunchKernelGGL(k_unrope128, dim3((p.T_mid + 15) / 16, p.L), dim3(256), 0, s, p);
+      if (p.rope_keys) hipLaunchKernelGGL(k_unrope128, dim3((p.T_mid + 15) / 16, p.L, seq_grid(p)), dim3(256), 0, s, p);
       hipLaunchKernelGGL(k_enc128<0>, grid, block, 0, s, p, 0, (float*)nullptr);
     } else {
       return launch_quant128(p, s);
@@ -1326,7 +1331,8 @@ __device__ __forceinline__ uint64_t alloc_key(float var, int k, int i) {
   return (((e2 << 23) | man) << 8) | (uint64_t)(255 - i);
 }
 
-__global__ __launch_bounds__(128) void k_enc_alloc(const Params p) {
+__global__ __launch_bounds__(128) void k_enc_alloc(const Params p0) {
+  const Params p = at_seq(p0, blockIdx.z);
   const int u = blockIdx.x;
   const int D = p.D;
   const int i = threadIdx.x;
@@ -1428,7 +1434,7 @@ __global__ __launch_bounds__(128) void k_enc_alloc(const Params p) {
 }
 
 hipError_t launch_enc_alloc(const Params& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_enc_alloc, dim3(p.n_sections), dim3(p.D), 0, s, p);
+  hipLaunchKernelGGL(k_enc_alloc, dim3(p.n_sections, 1, seq_grid(p)), dim3(p.D), 0, s, p);
   return hipGetLastError();
 }
 

@@ -44,7 +44,8 @@ struct QInfo {     // per component, sorted order (b > 0 first, by width)
 
 constexpr int kQWaves = 8;  // one packed tile per wave
 
-__global__ __launch_bounds__(64 * kQWaves) void k_quant128(const Params p) {
+__global__ __launch_bounds__(64 * kQWaves) void k_quant128(const Params p0) {
+  const Params p = at_seq(p0, blockIdx.z);
   constexpr int D = 128;
   const int u = blockIdx.y;
   const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(64 * kQWaves) void k_quant128(const Params p) {
     // past the tile repeat its last token), channels 32 kb + 8 g .. +7
     auto load_group = [&](int sub, int kk, uint4 (&a)[4]) {
       const int tok = min(sub * 64 + kk * 16 + r, nt - 1);
-      const uint16_t* rowp = src + (row0 + tok) * D;
+      const uint16_t* rowp = src + (pre ? (row0 + tok) * D : cache_row(p, l, h, p.mid_begin + t0 + ta + tok));
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) a[kb] = *reinterpret_cast<const uint4*>(rowp + 32 * kb + 8 * g);
     };
@@ -307,7 +308,7 @@ hipError_t launch_quant128(const Params& p, hipStream_t s) {
   const size_t lds = (size_t)8 * 4 * 64 * 16 + (size_t)kQWaves * segstride * 4;
   const int tiles = p.chunks_per_sec * p.tiles_per_chunk;
   (void)hipFuncSetAttribute((const void*)k_quant128, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL(k_quant128, dim3((tiles + kQWaves - 1) / kQWaves, p.n_sections), dim3(64 * kQWaves), lds, s, p);
+  hipLaunchKernelGGL(k_quant128, dim3((tiles + kQWaves - 1) / kQWaves, p.n_sections, seq_grid(p)), dim3(64 * kQWaves), lds, s, p);
   return hipGetLastError();
 }
 

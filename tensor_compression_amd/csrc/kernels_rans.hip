@@ -352,8 +352,10 @@ __device__ __forceinline__ int64_t slot_states_off(const Params& p, int t) {
          (int64_t)t * (4 * p.lanes + 2 * p.w.tile_words_max + 4);
 }
 
-__global__ void k_rans_enc_chunks(const Params p) {
+__global__ void k_rans_enc_chunks(const Params p0) {
+  const Params p = at_seq(p0, blockIdx.z);
   const int c = blockIdx.x;
+  if (c >= p.n_chunks) return;
   const int u = c / p.chunks_per_sec, ch = c % p.chunks_per_sec;
   const int D = p.D;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -450,7 +452,7 @@ hipError_t launch_rans_encode_chunks(const Params& p, hipStream_t s) {
   int streams = p.tiles_per_chunk;
   int waves = (streams * p.lanes + 63) / 64;
   if (waves < 1) waves = 1;
-  hipLaunchKernelGGL(k_rans_enc_chunks, dim3(p.n_chunks), dim3(64 * waves), 0, s, p);
+  hipLaunchKernelGGL(k_rans_enc_chunks, dim3(p.n_chunks, 1, seq_grid(p)), dim3(64 * waves), 0, s, p);
   return hipGetLastError();
 }
 
@@ -460,7 +462,37 @@ struct HeaderBytes {
   uint8_t b[kHeaderBytes];
 };
 
-__global__ __launch_bounds__(1024) void k_scan(const Params p, HeaderBytes hdr) {
+// Header word i: the plan's template with the fields that depend on T taken
+// from this call's (or this sequence's) layout.
+__device__ inline uint32_t header_word(const Params& p, const HeaderBytes& hdr, int i) {
+  auto lo32 = [](int64_t v) { return (uint32_t)v; };
+  auto hi32 = [](int64_t v) { return (uint32_t)((uint64_t)v >> 32); };
+  switch (i) {
+    case 24: return (uint32_t)p.T;
+    case 25: return (uint32_t)p.s0;
+    case 26: return (uint32_t)p.mid_begin;
+    case 27: return (uint32_t)p.mid_end;
+    case 29: return (uint32_t)p.chunks_per_sec;
+    case 30: return lo32(p.side_off);
+    case 31: return hi32(p.side_off);
+    case 32: return lo32(p.raw_off - p.side_off);
+    case 33: return hi32(p.raw_off - p.side_off);
+    case 34: return lo32(p.raw_off);
+    case 35: return hi32(p.raw_off);
+    case 36: return lo32(p.raw_bytes);
+    case 37: return hi32(p.raw_bytes);
+    case 38: return lo32(p.dir_off);
+    case 39: return hi32(p.dir_off);
+    case 40: return lo32(p.chunks_off);
+    case 41: return hi32(p.chunks_off);
+    default:
+      return (uint32_t)hdr.b[4 * i] | ((uint32_t)hdr.b[4 * i + 1] << 8) | ((uint32_t)hdr.b[4 * i + 2] << 16) |
+             ((uint32_t)hdr.b[4 * i + 3] << 24);
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_scan(const Params p0, HeaderBytes hdr) {
+  const Params p = at_seq(p0, blockIdx.z);
   __shared__ uint64_t s_part[1024];
   const uint32_t* rec_size = reinterpret_cast<const uint32_t*>(p.ws + p.w.rec_size);
   uint64_t* rec_pos = reinterpret_cast<uint64_t*>(p.ws + p.w.rec_pos);
@@ -491,8 +523,7 @@ __global__ __launch_bounds__(1024) void k_scan(const Params p, HeaderBytes hdr) 
   __syncthreads();
   const uint64_t total = (uint64_t)p.chunks_off + s_part[1023];
   if (tid < kHeaderBytes / 4) {
-    uint32_t wv = (uint32_t)hdr.b[4 * tid] | ((uint32_t)hdr.b[4 * tid + 1] << 8) |
-                  ((uint32_t)hdr.b[4 * tid + 2] << 16) | ((uint32_t)hdr.b[4 * tid + 3] << 24);
+    uint32_t wv = header_word(p, hdr, tid);
     if (tid == 42) wv = (uint32_t)total;
     if (tid == 43) wv = (uint32_t)(total >> 32);
     reinterpret_cast<uint32_t*>(p.out)[tid] = wv;
@@ -508,14 +539,16 @@ __global__ __launch_bounds__(1024) void k_scan(const Params p, HeaderBytes hdr) 
   }
 }
 
-__global__ __launch_bounds__(256) void k_copy_records(const Params p) {
+__global__ __launch_bounds__(256) void k_copy_records(const Params p0) {
+  const Params p = at_seq(p0, blockIdx.z);
   const int c = blockIdx.x;
+  if (c >= p.n_chunks) return;
   if (get_status(p.ws, p.w) & ((1u << KVTC_ERR_CAPACITY) | (1u << KVTC_ERR_NONFINITE))) return;
   const uint32_t size = reinterpret_cast<const uint32_t*>(p.ws + p.w.rec_size)[c];
   if (size == 0) return;
   const uint64_t pos = reinterpret_cast<const uint64_t*>(p.ws + p.w.rec_pos)[c];
   const uint8_t* slot = p.ws + p.w.rec + (int64_t)c * p.w.rec_slot;
-  uint8_t* dst = p.out + p.chunks_off + pos;  // 16-byte aligned record
+  uint8_t* dst = p.out_final + p.chunks_off + pos;  // 16-byte aligned record
   const int ch = c % p.chunks_per_sec;
   const int n = min(p.chunk_tokens, p.T_mid - ch * p.chunk_tokens);
   const int ntiles = (n + p.tile_tokens - 1) / p.tile_tokens;
@@ -554,14 +587,20 @@ __global__ __launch_bounds__(256) void k_copy_records(const Params p) {
 hipError_t launch_assemble(const Params& p, const uint8_t* hdr, hipStream_t s) {
   HeaderBytes h;
   memcpy(h.b, hdr, kHeaderBytes);
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, p, h);
-  if (p.n_chunks > 0) hipLaunchKernelGGL(k_copy_records, dim3(p.n_chunks), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(k_scan, dim3(1, 1, seq_grid(p)), dim3(1024), 0, s, p, h);
+  if (p.n_seqs > 0) {
+    // place the sequences, then move each one's staged fixed part and records
+    const hipError_t e = launch_batch_place(p, s);
+    if (e != hipSuccess) return e;
+  }
+  if (p.n_chunks > 0) hipLaunchKernelGGL(k_copy_records, dim3(p.n_chunks, 1, seq_grid(p)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 // ---- decoder ----------------------------------------------------------------
 
-__global__ void k_dec_check(const Params p, HeaderBytes hdr) {
+__global__ void k_dec_check(const Params p0, HeaderBytes hdr) {
+  const Params p = at_seq(p0, blockIdx.z);
   const int tid = threadIdx.x;
   __shared__ int s_bad;
   if (tid == 0) s_bad = 0;
@@ -569,8 +608,7 @@ __global__ void k_dec_check(const Params p, HeaderBytes hdr) {
   if (p.cap < p.chunks_off || p.cap < kHeaderBytes) {
     if (tid == 0) s_bad = 1;
   } else if (tid < kHeaderBytes / 4 && tid != 42 && tid != 43) {
-    const uint32_t want = (uint32_t)hdr.b[4 * tid] | ((uint32_t)hdr.b[4 * tid + 1] << 8) |
-                          ((uint32_t)hdr.b[4 * tid + 2] << 16) | ((uint32_t)hdr.b[4 * tid + 3] << 24);
+    const uint32_t want = header_word(p, hdr, tid);
     if (reinterpret_cast<const uint32_t*>(p.in)[tid] != want) atomicOr(&s_bad, 1);
   }
   __syncthreads();
@@ -589,12 +627,14 @@ __global__ void k_dec_check(const Params p, HeaderBytes hdr) {
 hipError_t launch_dec_check(const Params& p, const uint8_t* hdr, hipStream_t s) {
   HeaderBytes h;
   memcpy(h.b, hdr, kHeaderBytes);
-  hipLaunchKernelGGL(k_dec_check, dim3(1), dim3(64), 0, s, p, h);
+  hipLaunchKernelGGL(k_dec_check, dim3(1, 1, seq_grid(p)), dim3(64), 0, s, p, h);
   return hipGetLastError();
 }
 
-__global__ void k_rans_dec_chunks(const Params p) {
+__global__ void k_rans_dec_chunks(const Params p0) {
+  const Params p = at_seq(p0, blockIdx.z);
   const int c = blockIdx.x;
+  if (c >= p.n_chunks) return;
   const int u = c / p.chunks_per_sec, ch = c % p.chunks_per_sec;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (get_status(p.ws, p.w) & (1u << KVTC_ERR_CORRUPT)) return;
@@ -723,7 +763,7 @@ hipError_t launch_rans_decode_chunks(const Params& p, hipStream_t s) {
   if (waves < 1) waves = 1;
   // LDS: the symbol tables and one word ring per tile
   const size_t lds = 1024 + (size_t)(1u << p.sb) + (size_t)p.tiles_per_chunk * kRing * 2;
-  hipLaunchKernelGGL(k_rans_dec_chunks, dim3(p.n_chunks), dim3(64 * waves), lds, s, p);
+  hipLaunchKernelGGL(k_rans_dec_chunks, dim3(p.n_chunks, 1, seq_grid(p)), dim3(64 * waves), lds, s, p);
   return hipGetLastError();
 }
 

@@ -18,61 +18,6 @@ using namespace kvtc;
 
 namespace kvtc {
 
-static int32_t floor_bits(float b) { return (int32_t)floorf(b); }
-
-static bool section_has_r(const kvtc_config& c, int s) {
-  return c.transform == KVTC_WHT && (s == 1 || c.wht_keys);
-}
-
-// Region split ("How the Pipeline Works": sink tokens at the front, a
-// compressed middle, a recent window kept at full fidelity) and the fixed
-// part of the container.
-Layout make_layout(const kvtc_config& c, int32_t T) {
-  Layout lo{};
-  lo.T = T;
-  lo.s0 = c.sink_tokens < T ? c.sink_tokens : T;
-  lo.mid_begin = lo.s0;
-  int32_t e = T - c.recent_tokens;
-  lo.mid_end = e > lo.s0 ? e : lo.s0;
-  lo.T_mid = lo.mid_end - lo.mid_begin;
-  lo.W_eff = T - lo.mid_end;
-  lo.n_sections = c.layers * 2 * c.kv_heads;
-  lo.chunks_per_sec = lo.T_mid > 0 ? (lo.T_mid + c.chunk_tokens - 1) / c.chunk_tokens : 0;
-  lo.n_chunks = lo.n_sections * lo.chunks_per_sec;
-  lo.tiles_per_chunk = c.chunk_tokens / c.tile_tokens;
-  lo.n_r_sections = 0;
-  for (int s = 0; s < 2; ++s)
-    if (section_has_r(c, s)) lo.n_r_sections += c.layers * c.kv_heads;
-  int64_t eb = c.dtype == KVTC_BF16 ? 2 : 4;
-  int64_t D = c.head_dim;
-  lo.side_off = kHeaderBytes;
-  lo.r_off = lo.side_off + (int64_t)lo.n_sections * 9 * D;
-  lo.side_bytes = align16((int64_t)lo.n_sections * 9 * D + (int64_t)lo.n_r_sections * lo.T_mid * 4);
-  lo.raw_off = lo.side_off + lo.side_bytes;
-  lo.raw_bytes = align16(2 * (int64_t)c.layers * c.kv_heads * (lo.s0 + lo.W_eff) * D * eb);
-  lo.dir_off = lo.raw_off + lo.raw_bytes;
-  lo.chunks_off = lo.dir_off + (int64_t)lo.n_chunks * kDirEntry;
-  if (c.transform == KVTC_PCA) {
-    lo.budget_k = (int32_t)floorf(c.bits_k * (float)c.head_dim);
-    lo.budget_v = (int32_t)floorf(c.bits_v * (float)c.head_dim);
-  } else {
-    lo.budget_k = floor_bits(c.bits_k) * c.head_dim;
-    lo.budget_v = floor_bits(c.bits_v) * c.head_dim;
-  }
-  return lo;
-}
-
-static int64_t max_tile_bytes(const kvtc_config& c, int32_t ntok, int32_t budget) {
-  int32_t nz = budget < c.head_dim ? budget : c.head_dim;
-  return ((int64_t)ntok * budget + 7) / 8 + 4 * (int64_t)nz;
-}
-
-static int64_t max_words(int64_t P, const kvtc_config& c) {
-  // each coded symbol grows the state by at most scale_bits bits and each
-  // emitted word removes 16
-  return (P * (c.rans_scale_bits + 1)) / 16 + 2 * (int64_t)c.rans_lanes + 2;
-}
-
 int64_t max_container_bytes(const kvtc_config& c, const Layout& lo) {
   int64_t total = lo.chunks_off;
   for (int s = 0; s < 2; ++s) {
@@ -98,43 +43,6 @@ int64_t max_container_bytes(const kvtc_config& c, const Layout& lo) {
   return total;
 }
 
-WsLayout make_ws_layout(const kvtc_config& c, const Layout& lo) {
-  WsLayout w{};
-  int64_t D = c.head_dim;
-  int64_t nsc = (int64_t)lo.n_sections * (lo.chunks_per_sec > 0 ? lo.chunks_per_sec : 1);
-  auto take = [](int64_t& at, int64_t bytes) {
-    int64_t o = at;
-    at += (bytes + 255) & ~(int64_t)255;
-    return o;
-  };
-  int64_t at = 0;
-  w.status = take(at, 16);
-  w.part_sum = take(at, nsc * D * 8);
-  w.part_sq = take(at, nsc * D * 8);
-  w.part_min = take(at, nsc * D * 4);
-  w.part_max = take(at, nsc * D * 4);
-  w.sec_stats = take(at, (int64_t)lo.n_sections * D * 16);
-  w.side_rcp = take(at, (int64_t)lo.n_sections * D * 4);
-  w.side_zero = take(at, (int64_t)lo.n_sections * D * 4);
-  w.side_bits = take(at, (int64_t)lo.n_sections * D);
-  int32_t bmax = lo.budget_k > lo.budget_v ? lo.budget_k : lo.budget_v;
-  int64_t tile_max = max_tile_bytes(c, c.tile_tokens, bmax);
-  w.packed_slot = align16(tile_max * lo.tiles_per_chunk);
-  w.packed = take(at, (int64_t)lo.n_chunks * w.packed_slot);
-  // capacity rounded so that every tile piece of a slot starts 16-byte aligned
-  w.tile_words_max = ((max_words(tile_max, c) + 2 + 7) & ~(int64_t)7) - 2;
-  w.rec_slot = align16(align16(512 + 4 * (int64_t)lo.tiles_per_chunk) +
-                       (int64_t)lo.tiles_per_chunk * (4 * c.rans_lanes + 2 * w.tile_words_max + 4));
-  w.rec = take(at, (int64_t)lo.n_chunks * w.rec_slot);
-  w.rec_size = take(at, (int64_t)lo.n_chunks * 4);
-  w.rec_pos = take(at, (int64_t)lo.n_chunks * 8 + 8);
-  const bool fast128 = c.head_dim == 128 && c.dtype == KVTC_BF16 && c.transform == KVTC_PCA &&
-                       c.tile_tokens % 64 == 0 && c.rope_keys;
-  w.kprime = take(at, fast128 ? (int64_t)c.layers * c.kv_heads * lo.T_mid * D * 2 : 0);
-  w.total = at;
-  return w;
-}
-
 Params make_params(const PlanImpl& pl, const Layout& lo, const WsLayout& w) {
   const kvtc_config& c = pl.cfg;
   Params p{};
@@ -158,6 +66,7 @@ Params make_params(const PlanImpl& pl, const Layout& lo, const WsLayout& w) {
   // sum|x_j B_ji| <= ||x||_2 ||B_i||_2 bounds the sum by the token norm
   p.mfma_err = (c.dtype == KVTC_BF16 ? 24.0f : 64.0f) * 0x1p-24f * pl.max_col_norm;
   p.w = w;
+  p.cfg = c;
   return p;
 }
 
@@ -442,7 +351,7 @@ kvtc_status kvtc_encode(kvtc_plan_t plan, const void* k, const void* v, int32_t 
   if ((int64_t)ws_bytes < w.total) return KVTC_ERR_CAPACITY;
   if ((int64_t)cap < lo.chunks_off) return KVTC_ERR_CAPACITY;
   Params p = make_params(*pl, lo, w);
-  p.k = k; p.v = v; p.out = (uint8_t*)out; p.cap = (int64_t)cap; p.ws = (uint8_t*)ws;
+  p.k = k; p.v = v; p.out = (uint8_t*)out; p.out_final = p.out; p.cap = (int64_t)cap; p.ws = (uint8_t*)ws;
   uint8_t hdr[kHeaderBytes];
   build_header(*pl, lo, hdr);
   ProfScope prof(pl, stream);
@@ -496,6 +405,147 @@ kvtc_status kvtc_decode(kvtc_plan_t plan, const void* in, size_t in_bytes, int32
   return KVTC_OK;
 }
 
+// ---- paged ragged batches ----------------------------------------------------
+
+// Host-side sizes of a batch from the host copy of the lengths; false when a
+// length is out of range.  `lo_max` is the layout of the longest sequence,
+// which bounds every launch grid.
+static bool batch_sizes(const PlanImpl& pl, int32_t n_seqs, const int32_t* lens, int64_t* ws_total,
+                        int64_t* cont_total, int64_t* sum_t, int32_t* max_t) {
+  int64_t ws = batch_ws_head(n_seqs), cont = batch_header_bytes(n_seqs), st = 0;
+  int32_t mt = 0;
+  for (int32_t z = 0; z < n_seqs; ++z) {
+    const int32_t T = lens[z];
+    if (T < 0 || T > pl.cfg.max_tokens) return false;
+    const Layout lo = make_layout(pl.cfg, T);
+    ws += align256(make_ws_layout(pl.cfg, lo, true).total);
+    cont += align256(max_container_bytes(pl.cfg, lo));
+    st += T;
+    if (T > mt) mt = T;
+  }
+  if (ws_total) *ws_total = ws;
+  if (cont_total) *cont_total = cont;
+  if (sum_t) *sum_t = st;
+  if (max_t) *max_t = mt;
+  return true;
+}
+
+// The paged path runs on the bf16 head_dim-128 PCA kernels.
+static bool paged_supported(const kvtc_config& c) {
+  return c.head_dim == 128 && c.dtype == KVTC_BF16 && c.transform == KVTC_PCA && c.tile_tokens % 64 == 0;
+}
+
+kvtc_status kvtc_workspace_size_paged(kvtc_plan_t plan, int32_t n_seqs, const int32_t* seq_lens_host,
+                                      size_t* ws_bytes, size_t* max_container) {
+  if (!plan || n_seqs < 1 || n_seqs > 65535 || !seq_lens_host) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* pl = (PlanImpl*)plan;
+  if (!paged_supported(pl->cfg)) return KVTC_ERR_UNSUPPORTED;
+  int64_t ws = 0, cont = 0;
+  if (!batch_sizes(*pl, n_seqs, seq_lens_host, &ws, &cont, nullptr, nullptr)) return KVTC_ERR_INVALID_ARG;
+  if (ws_bytes) *ws_bytes = (size_t)ws;
+  if (max_container) *max_container = (size_t)cont;
+  return KVTC_OK;
+}
+
+// Batch parameters: the layout of the longest sequence (grids) plus the pool,
+// page table and sequence table.
+static kvtc_status paged_params(PlanImpl* pl, int32_t pool_pages, const int32_t* page_table, int32_t max_pages,
+                                const int32_t* seq_lens_dev, const int32_t* seq_lens_host, int32_t n_seqs,
+                                void* ws, size_t ws_bytes, Params* out_p, int64_t* sum_t, int32_t* max_t) {
+  if (n_seqs < 1 || n_seqs > 65535 || !seq_lens_host || !seq_lens_dev || !page_table || !ws)
+    return KVTC_ERR_INVALID_ARG;
+  if (pool_pages < 1 || max_pages < 1) return KVTC_ERR_INVALID_ARG;
+  if (!paged_supported(pl->cfg)) return KVTC_ERR_UNSUPPORTED;
+  if (misaligned(ws) || ((uintptr_t)page_table & 3u) || ((uintptr_t)seq_lens_dev & 3u)) return KVTC_ERR_INVALID_ARG;
+  int64_t ws_total = 0;
+  if (!batch_sizes(*pl, n_seqs, seq_lens_host, &ws_total, nullptr, sum_t, max_t)) return KVTC_ERR_INVALID_ARG;
+  for (int32_t z = 0; z < n_seqs; ++z)
+    if ((seq_lens_host[z] + kPageTokens - 1) / kPageTokens > max_pages) return KVTC_ERR_INVALID_ARG;
+  if ((int64_t)ws_bytes < ws_total) return KVTC_ERR_CAPACITY;
+  const Layout lo = make_layout(pl->cfg, *max_t);
+  Params p = make_params(*pl, lo, make_ws_layout(pl->cfg, lo, true));
+  p.ws = (uint8_t*)ws;
+  p.n_seqs = n_seqs;
+  p.pool_pages = pool_pages;
+  p.max_pages = max_pages;
+  p.page_table = page_table;
+  p.seqs = reinterpret_cast<SeqInfo*>((uint8_t*)ws + batch_seqinfo_off());
+  *out_p = p;
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_encode_paged(kvtc_plan_t plan, const void* k_pool, const void* v_pool, int32_t pool_pages,
+                              const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens_dev,
+                              const int32_t* seq_lens_host, int32_t n_seqs, void* out, size_t cap, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  if (!plan || !k_pool || !v_pool || !out) return KVTC_ERR_INVALID_ARG;
+  if (misaligned(k_pool) || misaligned(v_pool) || misaligned(out)) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* pl = (PlanImpl*)plan;
+  Params p;
+  int64_t sum_t = 0;
+  int32_t max_t = 0;
+  kvtc_status st = paged_params(pl, pool_pages, page_table, max_pages, seq_lens_dev, seq_lens_host, n_seqs, ws,
+                                ws_bytes, &p, &sum_t, &max_t);
+  if (st != KVTC_OK) return st;
+  if ((int64_t)cap < batch_header_bytes(n_seqs)) return KVTC_ERR_CAPACITY;
+  p.k = k_pool; p.v = v_pool; p.out = (uint8_t*)out; p.cap = (int64_t)cap;
+  uint8_t hdr[kHeaderBytes];
+  build_header(*pl, make_layout(pl->cfg, max_t), hdr);  // T-dependent fields are set per sequence
+  ProfScope prof(pl, stream);
+  HIP_TRY(launch_seq_setup(p, seq_lens_dev, sum_t, max_t, (int64_t)ws_bytes, 0, stream));
+  HIP_TRY(launch_copy_raw(p, 1, stream));
+  prof.phase("copy_raw");
+  if (p.n_chunks > 0) {
+    HIP_TRY(launch_enc_transform(p, 0, stream));
+    prof.phase("enc_stats");
+  }
+  HIP_TRY(launch_enc_alloc(p, stream));
+  prof.phase("enc_alloc");
+  if (p.n_chunks > 0) {
+    HIP_TRY(launch_enc_transform(p, 1, stream));
+    prof.phase("enc_quant_pack");
+    HIP_TRY(launch_rans_encode_chunks(p, stream));
+    prof.phase("rans_encode");
+  }
+  HIP_TRY(launch_assemble(p, hdr, stream));
+  HIP_TRY(launch_batch_finish(p, stream));
+  prof.phase("assemble");
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_decode_paged(kvtc_plan_t plan, const void* in, size_t in_bytes, void* k_pool, void* v_pool,
+                              int32_t pool_pages, const int32_t* page_table, int32_t max_pages,
+                              const int32_t* seq_lens_dev, const int32_t* seq_lens_host, int32_t n_seqs, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  if (!plan || !in || !k_pool || !v_pool) return KVTC_ERR_INVALID_ARG;
+  if (misaligned(in) || misaligned(k_pool) || misaligned(v_pool)) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* pl = (PlanImpl*)plan;
+  Params p;
+  int64_t sum_t = 0;
+  int32_t max_t = 0;
+  kvtc_status st = paged_params(pl, pool_pages, page_table, max_pages, seq_lens_dev, seq_lens_host, n_seqs, ws,
+                                ws_bytes, &p, &sum_t, &max_t);
+  if (st != KVTC_OK) return st;
+  p.in = (const uint8_t*)in; p.cap = (int64_t)in_bytes;
+  p.k_out = k_pool; p.v_out = v_pool; p.out_dtype = pl->cfg.dtype;
+  uint8_t hdr[kHeaderBytes];
+  build_header(*pl, make_layout(pl->cfg, max_t), hdr);
+  ProfScope prof(pl, stream);
+  HIP_TRY(launch_seq_setup(p, seq_lens_dev, sum_t, max_t, (int64_t)ws_bytes, 1, stream));
+  HIP_TRY(launch_dec_check(p, hdr, stream));
+  prof.phase("dec_check");
+  if (p.n_chunks > 0) {
+    HIP_TRY(launch_rans_decode_chunks(p, stream));
+    prof.phase("rans_decode");
+    HIP_TRY(launch_dec_transform(p, stream));
+    prof.phase("dec_transform");
+  }
+  HIP_TRY(launch_copy_raw(p, 0, stream));
+  HIP_TRY(launch_batch_finish(p, stream));
+  prof.phase("copy_raw_out");
+  return KVTC_OK;
+}
+
 kvtc_status kvtc_result(kvtc_plan_t plan, const void* ws, uint64_t* container_bytes,
                         int32_t* device_status) {
   if (!plan || !ws) return KVTC_ERR_INVALID_ARG;
@@ -503,7 +553,8 @@ kvtc_status kvtc_result(kvtc_plan_t plan, const void* ws, uint64_t* container_by
   if (hipMemcpy(buf, ws, 16, hipMemcpyDeviceToHost) != hipSuccess) return KVTC_ERR_HIP;
   uint32_t bits = buf[0];
   int32_t st = KVTC_OK;
-  if (bits & (1u << KVTC_ERR_NONFINITE)) st = KVTC_ERR_NONFINITE;
+  if (bits & (1u << KVTC_ERR_INVALID_ARG)) st = KVTC_ERR_INVALID_ARG;
+  else if (bits & (1u << KVTC_ERR_NONFINITE)) st = KVTC_ERR_NONFINITE;
   else if (bits & (1u << KVTC_ERR_CORRUPT)) st = KVTC_ERR_CORRUPT;
   else if (bits & (1u << KVTC_ERR_CAPACITY)) st = KVTC_ERR_CAPACITY;
   else if (bits) st = KVTC_ERR_HIP;

@@ -43,8 +43,110 @@ struct WsLayout {
   int64_t rec_size;    // u32 [n_chunks]
   int64_t rec_pos;     // u64 [n_chunks]
   int64_t kprime;      // bf16 [L][H][T_mid][D]: mid-region keys with RoPE removed (head_dim 128 bf16 path)
+  int64_t fixed;       // paged batch: staging of the container's fixed part [chunks_off]
   int64_t total;
 };
+
+#define KVTC_HD __host__ __device__
+
+KVTC_HD inline int64_t align16(int64_t x) { return (x + 15) & ~(int64_t)15; }
+KVTC_HD inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+KVTC_HD inline int32_t floor_bits(float b) { return (int32_t)floorf(b); }
+
+KVTC_HD inline bool section_has_r(const kvtc_config& c, int s) {
+  return c.transform == KVTC_WHT && (s == 1 || c.wht_keys);
+}
+
+// Region split ("How the Pipeline Works": sink tokens at the front, a
+// compressed middle, a recent window kept at full fidelity) and the fixed
+// part of the container.
+KVTC_HD inline Layout make_layout(const kvtc_config& c, int32_t T) {
+  Layout lo{};
+  lo.T = T;
+  lo.s0 = c.sink_tokens < T ? c.sink_tokens : T;
+  lo.mid_begin = lo.s0;
+  int32_t e = T - c.recent_tokens;
+  lo.mid_end = e > lo.s0 ? e : lo.s0;
+  lo.T_mid = lo.mid_end - lo.mid_begin;
+  lo.W_eff = T - lo.mid_end;
+  lo.n_sections = c.layers * 2 * c.kv_heads;
+  lo.chunks_per_sec = lo.T_mid > 0 ? (lo.T_mid + c.chunk_tokens - 1) / c.chunk_tokens : 0;
+  lo.n_chunks = lo.n_sections * lo.chunks_per_sec;
+  lo.tiles_per_chunk = c.chunk_tokens / c.tile_tokens;
+  lo.n_r_sections = 0;
+  for (int s = 0; s < 2; ++s)
+    if (section_has_r(c, s)) lo.n_r_sections += c.layers * c.kv_heads;
+  int64_t eb = c.dtype == KVTC_BF16 ? 2 : 4;
+  int64_t D = c.head_dim;
+  lo.side_off = kHeaderBytes;
+  lo.r_off = lo.side_off + (int64_t)lo.n_sections * 9 * D;
+  lo.side_bytes = align16((int64_t)lo.n_sections * 9 * D + (int64_t)lo.n_r_sections * lo.T_mid * 4);
+  lo.raw_off = lo.side_off + lo.side_bytes;
+  lo.raw_bytes = align16(2 * (int64_t)c.layers * c.kv_heads * (lo.s0 + lo.W_eff) * D * eb);
+  lo.dir_off = lo.raw_off + lo.raw_bytes;
+  lo.chunks_off = lo.dir_off + (int64_t)lo.n_chunks * kDirEntry;
+  if (c.transform == KVTC_PCA) {
+    lo.budget_k = (int32_t)floorf(c.bits_k * (float)c.head_dim);
+    lo.budget_v = (int32_t)floorf(c.bits_v * (float)c.head_dim);
+  } else {
+    lo.budget_k = floor_bits(c.bits_k) * c.head_dim;
+    lo.budget_v = floor_bits(c.bits_v) * c.head_dim;
+  }
+  return lo;
+}
+
+KVTC_HD inline int64_t max_tile_bytes(const kvtc_config& c, int32_t ntok, int32_t budget) {
+  int32_t nz = budget < c.head_dim ? budget : c.head_dim;
+  return ((int64_t)ntok * budget + 7) / 8 + 4 * (int64_t)nz;
+}
+
+KVTC_HD inline int64_t max_words(int64_t P, const kvtc_config& c) {
+  // each coded symbol grows the state by at most scale_bits bits and each
+  // emitted word removes 16
+  return (P * (c.rans_scale_bits + 1)) / 16 + 2 * (int64_t)c.rans_lanes + 2;
+}
+
+// `paged`: the workspace of one sequence of a paged batch, which also stages
+// the fixed part of its container (everything before chunks_off).
+KVTC_HD inline WsLayout make_ws_layout(const kvtc_config& c, const Layout& lo, bool paged = false) {
+  WsLayout w{};
+  int64_t D = c.head_dim;
+  int64_t nsc = (int64_t)lo.n_sections * (lo.chunks_per_sec > 0 ? lo.chunks_per_sec : 1);
+  auto take = [](int64_t& at, int64_t bytes) {
+    int64_t o = at;
+    at += (bytes + 255) & ~(int64_t)255;
+    return o;
+  };
+  int64_t at = 0;
+  w.status = take(at, 16);
+  w.part_sum = take(at, nsc * D * 8);
+  w.part_sq = take(at, nsc * D * 8);
+  w.part_min = take(at, nsc * D * 4);
+  w.part_max = take(at, nsc * D * 4);
+  w.sec_stats = take(at, (int64_t)lo.n_sections * D * 16);
+  w.side_rcp = take(at, (int64_t)lo.n_sections * D * 4);
+  w.side_zero = take(at, (int64_t)lo.n_sections * D * 4);
+  w.side_bits = take(at, (int64_t)lo.n_sections * D);
+  int32_t bmax = lo.budget_k > lo.budget_v ? lo.budget_k : lo.budget_v;
+  int64_t tile_max = max_tile_bytes(c, c.tile_tokens, bmax);
+  w.packed_slot = align16(tile_max * lo.tiles_per_chunk);
+  w.packed = take(at, (int64_t)lo.n_chunks * w.packed_slot);
+  // capacity rounded so that every tile piece of a slot starts 16-byte aligned
+  w.tile_words_max = ((max_words(tile_max, c) + 2 + 7) & ~(int64_t)7) - 2;
+  w.rec_slot = align16(align16(512 + 4 * (int64_t)lo.tiles_per_chunk) +
+                       (int64_t)lo.tiles_per_chunk * (4 * c.rans_lanes + 2 * w.tile_words_max + 4));
+  w.rec = take(at, (int64_t)lo.n_chunks * w.rec_slot);
+  w.rec_size = take(at, (int64_t)lo.n_chunks * 4);
+  w.rec_pos = take(at, (int64_t)lo.n_chunks * 8 + 8);
+  const bool fast128 = c.head_dim == 128 && c.dtype == KVTC_BF16 && c.transform == KVTC_PCA &&
+                       c.tile_tokens % 64 == 0 && c.rope_keys;
+  w.kprime = take(at, fast128 ? (int64_t)c.layers * c.kv_heads * lo.T_mid * D * 2 : 0);
+  w.fixed = take(at, paged ? lo.chunks_off : 0);
+  w.total = at;
+  return w;
+}
+
 
 struct PlanImpl {
   kvtc_config cfg;
@@ -92,11 +194,77 @@ struct Params {
   // workspace
   uint8_t* ws;
   WsLayout w;
+  // paged batch (n_seqs > 0): blockIdx.z selects a sequence; at_seq() turns
+  // the batch parameters into that sequence's
+  kvtc_config cfg;
+  int32_t n_seqs;
+  int32_t pool_pages;           // pages in each pool [L, pool_pages, H, 16, D]
+  int32_t max_pages;            // length of a page-table row
+  const int32_t* page_table;    // [n_seqs][max_pages]
+  const int32_t* page_row;      // this sequence's row (null: contiguous cache)
+  struct SeqInfo* seqs;         // [n_seqs], in the batch workspace
+  uint8_t* out_final;           // where this sequence's records go (encode)
 };
 
+constexpr int kPageTokens = 16;
+
+// Per-sequence placement of a paged batch, written on the device.
+struct SeqInfo {
+  int32_t T;        // tokens of the sequence
+  int32_t pad;
+  int64_t ws_off;   // its workspace, from the batch workspace start
+  int64_t out_off;  // its container, from the batch container start
+  int64_t cap;      // decode: bytes of its container
+};
+
+// Batch workspace: a status block in the contiguous-call format (status bits,
+// exact re-computations, total bytes), the SeqInfo table, then one workspace
+// per sequence.
+KVTC_HD inline int64_t batch_seqinfo_off() { return 256; }
+KVTC_HD inline int64_t batch_ws_head(int32_t n_seqs) {
+  return align256(batch_seqinfo_off() + (int64_t)n_seqs * (int64_t)sizeof(SeqInfo));
+}
+// Batch container: "KVTB", version, n_seqs, header bytes, u64 total, then
+// u64 offset and u64 size per sequence; sequence containers start 256-byte
+// aligned and are each what kvtc_encode writes for that sequence alone.
+constexpr int kBatchFixedBytes = 64;
+KVTC_HD inline int64_t batch_header_bytes(int32_t n_seqs) {
+  return align256(kBatchFixedBytes + 16 * (int64_t)n_seqs);
+}
+
+// This sequence's parameters (identity for a contiguous call).
+__device__ inline Params at_seq(const Params& p0, int z) {
+  if (p0.n_seqs == 0) return p0;
+  Params p = p0;
+  const SeqInfo si = p0.seqs[z];
+  const Layout lo = make_layout(p0.cfg, si.T);
+  p.T = lo.T; p.s0 = lo.s0; p.mid_begin = lo.mid_begin; p.mid_end = lo.mid_end;
+  p.T_mid = lo.T_mid; p.W_eff = lo.W_eff; p.chunks_per_sec = lo.chunks_per_sec; p.n_chunks = lo.n_chunks;
+  p.side_off = lo.side_off; p.r_off = lo.r_off; p.raw_off = lo.raw_off; p.raw_bytes = lo.raw_bytes;
+  p.dir_off = lo.dir_off; p.chunks_off = lo.chunks_off;
+  p.w = make_ws_layout(p0.cfg, lo, true);
+  p.ws = p0.ws + si.ws_off;
+  p.out = p.ws + p.w.fixed;  // the fixed part is staged until the sequence is placed
+  p.out_final = p0.out + si.out_off;
+  p.in = p0.in + si.out_off;
+  p.cap = si.cap;
+  p.page_row = p0.page_table + (int64_t)z * p0.max_pages;
+  return p;
+}
+
+// gridDim.z of a launch: one slice per sequence of a paged batch.
+inline unsigned seq_grid(const Params& p) { return p.n_seqs > 0 ? (unsigned)p.n_seqs : 1u; }
+
+// Element offset of the row (layer l, head h, token pos) of K or V: the
+// contiguous [L, H, T, D] cache, or a pool [L, P, H, 16, D] through the page
+// table.
+__device__ inline int64_t cache_row(const Params& p, int l, int h, int pos) {
+  if (p.page_row == nullptr) return (((int64_t)l * p.H + h) * p.T + pos) * p.D;
+  const int64_t page = p.page_row[pos >> 4];
+  return (((((int64_t)l * p.pool_pages + page) * p.H + h) << 4) + (pos & 15)) * p.D;
+}
+
 // host helpers (kvtc_api.hip)
-Layout make_layout(const kvtc_config& c, int32_t T);
-WsLayout make_ws_layout(const kvtc_config& c, const Layout& lo);
 int64_t max_container_bytes(const kvtc_config& c, const Layout& lo);
 Params make_params(const PlanImpl& p, const Layout& lo, const WsLayout& w);
 void build_header(const PlanImpl& p, const Layout& lo, uint8_t* hdr);
@@ -113,6 +281,10 @@ hipError_t launch_rans_decode_chunks(const Params& p, hipStream_t s);
 hipError_t launch_dec_transform(const Params& p, hipStream_t s);
 hipError_t launch_coeffs(const Params& p, int sec_begin, int sec_end, float* out, float* r_out,
                          hipStream_t s);
+hipError_t launch_seq_setup(const Params& p, const int32_t* seq_lens, int64_t sum_t, int32_t max_t, int64_t ws_bytes,
+                            int mode, hipStream_t s);  // mode 0 encode, 1 decode
+hipError_t launch_batch_place(const Params& p, hipStream_t s);
+hipError_t launch_batch_finish(const Params& p, hipStream_t s);
 hipError_t launch_test_rans_encode(const uint8_t* sym, int64_t N, const uint16_t* freq, int sb,
                                    int lanes, uint32_t* states, uint16_t* words, int64_t cap,
                                    int64_t* nwords, hipStream_t s);
@@ -126,8 +298,6 @@ hipError_t launch_prep_basis(const float* src, void* basis_t, void* basis, int n
 // ---------------------------------------------------------------------------
 // device helpers shared by the kernels
 // ---------------------------------------------------------------------------
-
-__host__ __device__ inline int64_t align16(int64_t x) { return (x + 15) & ~(int64_t)15; }
 
 // Bytes of one packed tile of `ntok` tokens: a row of ceil(ntok*b/32) words
 // per component with b > 0.

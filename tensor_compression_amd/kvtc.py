@@ -59,6 +59,17 @@ EXPORTS = {
     "kvtc_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                    ctypes.c_size_t, ctypes.c_void_p]),
+    "kvtc_workspace_size_paged": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                                 ctypes.POINTER(ctypes.c_size_t),
+                                                 ctypes.POINTER(ctypes.c_size_t)]),
+    "kvtc_encode_paged": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]),
+    "kvtc_decode_paged": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_size_t, ctypes.c_void_p]),
     "kvtc_result": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint64),
                                    ctypes.POINTER(ctypes.c_int32)]),
     "kvtc_encode_counters": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p,
@@ -224,6 +235,36 @@ class Plan:
         torch.cuda.current_stream().synchronize()
         _, st = self.result(ws)
         return k, v, st
+
+    # paged ragged batches: pools [L, P, H, 16, D], page_table [n_seqs, max_pages]
+    # int32 on the device, seq_lens as a host list (copied to the device here)
+    def sizes_paged(self, seq_lens):
+        lens = (ctypes.c_int32 * len(seq_lens))(*[int(x) for x in seq_lens])
+        ws = ctypes.c_size_t(0)
+        mc = ctypes.c_size_t(0)
+        _check(lib().kvtc_workspace_size_paged(self.handle, len(seq_lens), lens, ctypes.byref(ws),
+                                               ctypes.byref(mc)), "kvtc_workspace_size_paged")
+        return ws.value, mc.value
+
+    @staticmethod
+    def _paged_args(k_pool, page_table, seq_lens, seq_lens_dev):
+        lens = (ctypes.c_int32 * len(seq_lens))(*[int(x) for x in seq_lens])
+        assert page_table.dtype == torch.int32 and page_table.dim() == 2 and page_table.is_contiguous()
+        assert seq_lens_dev.dtype == torch.int32 and seq_lens_dev.numel() == len(seq_lens)
+        return k_pool.shape[1], page_table.shape[1], lens
+
+    def encode_paged_async(self, k_pool, v_pool, page_table, seq_lens, seq_lens_dev, out, ws, stream=None):
+        P, max_pages, lens = self._paged_args(k_pool, page_table, seq_lens, seq_lens_dev)
+        _check(lib().kvtc_encode_paged(self.handle, _ptr(k_pool), _ptr(v_pool), P, _ptr(page_table), max_pages,
+                                       _ptr(seq_lens_dev), lens, len(seq_lens), _ptr(out), out.numel(), _ptr(ws),
+                                       ws.numel(), _stream(stream)), "kvtc_encode_paged")
+
+    def decode_paged_async(self, data, nbytes, k_pool, v_pool, page_table, seq_lens, seq_lens_dev, ws,
+                           stream=None):
+        P, max_pages, lens = self._paged_args(k_pool, page_table, seq_lens, seq_lens_dev)
+        _check(lib().kvtc_decode_paged(self.handle, _ptr(data), nbytes, _ptr(k_pool), _ptr(v_pool), P,
+                                       _ptr(page_table), max_pages, _ptr(seq_lens_dev), lens, len(seq_lens),
+                                       _ptr(ws), ws.numel(), _stream(stream)), "kvtc_decode_paged")
 
     # profiling
     def profile(self, on: bool = True):

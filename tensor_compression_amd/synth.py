@@ -154,6 +154,61 @@ def page_permutation(n_pages: int, seed: int = 2):
     return torch.randperm(n_pages, generator=gen)
 
 
+def generate_paged(w: Workload, device: str = "cpu", lengths=None, layers: int | None = None,
+                   seed: int | None = None, spare_pages: int = 0):
+    """A ragged batch in 16-token pages: pools [L, P, H, 16, D] (workload
+    dtype, zero where no token lives), page_table [n_seqs, max_pages] int32
+    (-1 past a sequence's pages) and the lengths.
+
+    The per-layer mixing and channel scales are drawn first (layer-major, K
+    before V) and shared by every sequence and head, as a shared per-layer
+    basis implies; then each sequence draws its latents and noise in order.
+    Pages are handed out by a seeded permutation of the pool."""
+    lens = list(ragged_lengths(w) if lengths is None else lengths)
+    L = w.layers if layers is None else layers
+    H, D, r, pt = w.kv_heads, w.head_dim, w.rank, w.page_tokens
+    gen = torch.Generator(device=device)
+    gen.manual_seed(w.seed if seed is None else seed)
+    dt = torch_dtype(w.dtype)
+    params = [[_layer_params(gen, D, r, w.scales, w.outliers, device) for _ in range(2)] for _ in range(L)]
+    n_pg = [(T + pt - 1) // pt for T in lens]
+    n_pages = sum(n_pg) + spare_pages
+    perm = page_permutation(max(n_pages, 1))
+    max_pages = max(max(n_pg), 1)
+    table = torch.full((len(lens), max_pages), -1, dtype=torch.int32)
+    at = 0
+    for z, n in enumerate(n_pg):
+        table[z, :n] = perm[at: at + n].to(torch.int32)
+        at += n
+    pools = [torch.zeros(L, max(n_pages, 1), H, pt, D, dtype=dt, device=device) for _ in range(2)]
+    for z, T in enumerate(lens):
+        if T == 0:
+            continue
+        pages = table[z, : n_pg[z]].to(device=device, dtype=torch.long)
+        pos = torch.arange(T, device=device)
+        for l in range(L):
+            for s in range(2):
+                M, g = params[l][s]
+                zl = torch.randn(H, T, r, generator=gen, device=device, dtype=torch.float32)
+                eps = torch.randn(H, T, D, generator=gen, device=device, dtype=torch.float32) * w.noise
+                x = (zl @ M.T + eps) * g
+                if s == 0:
+                    x = model_rope(x, pos, w.theta)
+                xp = torch.zeros(H, n_pg[z] * pt, D, dtype=dt, device=device)
+                xp[:, :T] = x.to(dt)
+                pools[s][l, pages] = xp.view(H, n_pg[z], pt, D).permute(1, 0, 2, 3)
+    return pools[0], pools[1], table, lens
+
+
+def gather_paged(pool: torch.Tensor, table: torch.Tensor, z: int, T: int) -> torch.Tensor:
+    """Sequence z of a page pool as a contiguous [L, H, T, D] tensor."""
+    L, _, H, pt, D = pool.shape
+    n = (T + pt - 1) // pt
+    pages = table[z, :n].to(device=pool.device, dtype=torch.long)
+    x = pool[:, pages].permute(0, 2, 1, 3, 4).reshape(L, H, n * pt, D)
+    return x[:, :, :T].contiguous()
+
+
 def to_numpy_bits(x: torch.Tensor):
     """Host copy for the oracle: fp32 as float32, bf16 as its uint16 bit pattern."""
     x = x.detach().contiguous().cpu()
