@@ -48,6 +48,7 @@ def parse():
                     help="layers of the workload the CPU oracle baseline codes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-phase event pass")
+    ap.add_argument("--seqs", type=int, default=None, help="sequences of a paged workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain copy kernel of known size (for scaling HBM counters)")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -203,6 +204,122 @@ def cpu_baseline(w, cfg, K, V, basis, layers):
     }
 
 
+def run_paged(args, w):
+    """The paged ragged batch: one step = kvtc_encode_paged + kvtc_decode_paged
+    of the whole batch (decode writes back into the same pools, which a
+    second copy of would not fit next to the workspace)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from tensor_compression_amd import kvtc, synth
+    from tensor_compression_amd.calibrate import fit_pca_basis
+
+    n_seqs = args.seqs if args.seqs is not None else w.n_seqs
+    lens = synth.ragged_lengths(w, n_seqs)
+    over = dict(chunk_tokens=args.chunk_tokens, tile_tokens=args.tile_tokens)
+    if args.bits is not None:
+        over.update(bits_k=args.bits, bits_v=args.bits)
+    kp, vp, table, lens = synth.generate_paged(w, device="cuda", lengths=lens, layers=args.layers)
+    L, P, H, _, D = kp.shape
+    cfg = synth.oracle_config(w, layers=L, **over)
+    # shared per-layer basis, fitted on the longest of the first eight sequences
+    z0 = int(np.argmax(lens[:8]))
+    Kz, Vz = synth.gather_paged(kp, table, z0, lens[z0]), synth.gather_paged(vp, table, z0, lens[z0])
+    s0, mid_end = layout(cfg, lens[z0])
+    basis = fit_pca_basis(Kz, Vz, cfg, s0, mid_end)
+    del Kz, Vz
+    plan = kvtc.Plan(cfg, basis, max_tokens=max(lens))
+    ws_bytes, cap = plan.sizes_paged(lens)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    # the worst-case container capacity assumes every rANS stream expands; when
+    # that does not fit next to the pools and the workspace, take what is free
+    # (an encode that overflows reports KVTC_ERR_CAPACITY)
+    free = torch.cuda.mem_get_info()[0] - (2 << 30)
+    cap = int(min(cap, free))
+    out = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    table_d = table.cuda()
+    lens_d = torch.tensor(lens, dtype=torch.int32, device="cuda")
+
+    def step():
+        plan.encode_paged_async(kp, vp, table_d, lens, lens_d, out, ws)
+        plan.decode_paged_async(out, cap, kp, vp, table_d, lens, lens_d, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    plan.encode_paged_async(kp, vp, table_d, lens, lens_d, out, ws)
+    torch.cuda.synchronize()
+    nbytes, st = plan.result(ws)
+    if st != kvtc.OK:
+        raise SystemExit(f"device status: {kvtc.STATUS[st]}")
+    phases = {}
+    if not args.no_profile:
+        plan.profile(True)
+        for _ in range(max(1, min(args.steps, 3))):
+            plan.encode_paged_async(kp, vp, table_d, lens, lens_d, out, ws)
+            for name, ms in plan.profile_read():
+                phases.setdefault(name, []).append(ms)
+            plan.decode_paged_async(out, cap, kp, vp, table_d, lens, lens_d, ws)
+            for name, ms in plan.profile_read():
+                phases.setdefault(name, []).append(ms)
+        plan.profile(False)
+    ph_ms = {k: float(np.mean(v)) for k, v in phases.items()}
+    tok = int(sum(lens))
+    raw = tok * L * H * D * 2 * kp.element_size()
+    res = {
+        "metric": METRIC + " (paged ragged batch)",
+        "value": raw / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {n_seqs} sequences, lengths U[{w.min_len}, {w.max_len}] ({tok} tokens), "
+                        f"16-token pages, {L} layers x {H} KV heads x head_dim {D}, bf16, {cfg['bits_k']:g} "
+                        f"bits/comp, shared per-layer PCA basis",
+            "sequences": n_seqs, "tokens": tok, "layers": L, "kv_heads": H, "head_dim": D,
+            "pool_pages": P, "bits_per_component": cfg["bits_k"],
+        },
+        "raw_bytes": raw, "container_bytes": nbytes, "compression_ratio": raw / nbytes,
+        "bits_per_value": 8.0 * nbytes / (raw / kp.element_size()),
+        "phases_ms": ph_ms,
+        "path_roofline": {
+            "bound": "hbm", "algorithmic_bytes": 2 * (raw + nbytes),
+            "achieved": 2 * (raw + nbytes) / (ms_per_step * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": 2 * (raw + nbytes) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        },
+        "workspace_bytes": ws_bytes, "container_capacity": cap, "wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        # the oracle on the first two layers of the first sequence
+        T0 = lens[0]
+        k = synth.to_numpy_bits(synth.gather_paged(kp[:2], table, 0, T0))
+        v = synth.to_numpy_bits(synth.gather_paged(vp[:2], table, 0, T0))
+        c1 = dict(cfg, layers=2)
+        b = basis[:2].cpu().numpy()
+        oracle.lib()
+        t_a = time.perf_counter()
+        data = oracle.encode(c1, k, v, b)
+        t_b = time.perf_counter()
+        oracle.decode(c1, data, b, T0, oracle.BF16)
+        t_c = time.perf_counter()
+        res["cpu_baseline"] = {
+            "value": (k.nbytes + v.nbytes) / (t_c - t_a) / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"sequence 0 ({T0} tokens), layers 0-1 of {L}: oracle encode {t_b - t_a:.2f} s + decode "
+                      f"{t_c - t_b:.2f} s, single thread; the decode overwrote the pools, so the sample is the "
+                      "reconstruction of the first step",
+        }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -229,6 +346,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
     w = synth.WORKLOADS[args.workload]
+    if w.n_seqs > 0:
+        run_paged(args, w)
+        return
     over = dict(chunk_tokens=args.chunk_tokens, tile_tokens=args.tile_tokens)
     if args.bits is not None:
         over.update(bits_k=args.bits, bits_v=args.bits)

@@ -37,6 +37,27 @@ __device__ inline int64_t block_exclusive_scan(int64_t v, int64_t* s_tmp, int64_
 
 }  // namespace
 
+// Clears the batch status block (k_seq_check reports into word 3).
+__global__ void k_batch_clear(const Params p0) {
+  if (threadIdx.x < 4) reinterpret_cast<uint32_t*>(p0.ws)[threadIdx.x] = 0u;
+}
+
+// One workgroup per sequence: its length and every page index it uses.
+__global__ __launch_bounds__(256) void k_seq_check(const Params p0, const int32_t* seq_lens, int32_t max_t_host) {
+  const int z = blockIdx.x;
+  const int32_t T = seq_lens[z];
+  uint32_t* bst = reinterpret_cast<uint32_t*>(p0.ws);
+  const int32_t np = (T + kPageTokens - 1) / kPageTokens;
+  if (T < 0 || T > max_t_host || np > p0.max_pages) {
+    if (threadIdx.x == 0) atomicOr(bst + 3, 1u);
+    return;
+  }
+  const int32_t* row = p0.page_table + (int64_t)z * p0.max_pages;
+  bool bad = false;
+  for (int i = threadIdx.x; i < np; i += 256) bad |= row[i] < 0 || row[i] >= p0.pool_pages;
+  if (bad) atomicOr(bst + 3, 1u);
+}
+
 // mode 0 (encode): lengths and page table checked, workspaces placed, status
 // words cleared.  mode 1 (decode): the same, plus the batch container header
 // checked and each sequence's container located.  Anything inconsistent with
@@ -50,21 +71,10 @@ __global__ __launch_bounds__(1024) void k_seq_setup(const Params p0, const int32
   const int tid = threadIdx.x, n = p0.n_seqs;
   SeqInfo* si = reinterpret_cast<SeqInfo*>(p0.ws + batch_seqinfo_off());
   uint32_t* bst = reinterpret_cast<uint32_t*>(p0.ws);
-  if (tid == 0) { s_bad = 0; s_corrupt = 0; }
+  if (tid == 0) { s_bad = bst[3] != 0u; s_corrupt = 0; }  // k_seq_check's verdict on lengths and pages
   __syncthreads();
-  // sequences tid, tid + 1024, ...: lengths and pages
   int64_t sum_t = 0;
-  for (int z = tid; z < n; z += 1024) {
-    const int32_t T = seq_lens[z];
-    if (T < 0 || T > max_t_host || (T + kPageTokens - 1) / kPageTokens > p0.max_pages) {
-      s_bad = 1;
-      continue;
-    }
-    sum_t += T;
-    const int32_t* row = p0.page_table + (int64_t)z * p0.max_pages;
-    for (int i = 0; i < (T + kPageTokens - 1) / kPageTokens; ++i)
-      if (row[i] < 0 || row[i] >= p0.pool_pages) s_bad = 1;
-  }
+  for (int z = tid; z < n; z += 1024) sum_t += seq_lens[z];
   int64_t tot_t;
   (void)block_exclusive_scan(sum_t, s_tmp, tot_t);
   if (tid == 0 && tot_t != sum_t_host) s_bad = 1;
@@ -264,6 +274,8 @@ __global__ __launch_bounds__(1024) void k_batch_finish(const Params p0) {
 
 hipError_t launch_seq_setup(const Params& p, const int32_t* seq_lens, int64_t sum_t, int32_t max_t, int64_t ws_bytes,
                             int mode, hipStream_t s) {
+  hipLaunchKernelGGL(k_batch_clear, dim3(1), dim3(64), 0, s, p);
+  hipLaunchKernelGGL(k_seq_check, dim3(p.n_seqs), dim3(256), 0, s, p, seq_lens, max_t);
   hipLaunchKernelGGL(k_seq_setup, dim3(1), dim3(1024), 0, s, p, seq_lens, sum_t, max_t, ws_bytes, mode);
   return hipGetLastError();
 }

@@ -136,12 +136,17 @@ KVTC_HD inline WsLayout make_ws_layout(const kvtc_config& c, const Layout& lo, b
   w.tile_words_max = ((max_words(tile_max, c) + 2 + 7) & ~(int64_t)7) - 2;
   w.rec_slot = align16(align16(512 + 4 * (int64_t)lo.tiles_per_chunk) +
                        (int64_t)lo.tiles_per_chunk * (4 * c.rans_lanes + 2 * w.tile_words_max + 4));
-  w.rec = take(at, (int64_t)lo.n_chunks * w.rec_slot);
-  w.rec_size = take(at, (int64_t)lo.n_chunks * 4);
-  w.rec_pos = take(at, (int64_t)lo.n_chunks * 8 + 8);
   const bool fast128 = c.head_dim == 128 && c.dtype == KVTC_BF16 && c.transform == KVTC_PCA &&
                        c.tile_tokens % 64 == 0 && c.rope_keys;
-  w.kprime = take(at, fast128 ? (int64_t)c.layers * c.kv_heads * lo.T_mid * D * 2 : 0);
+  const int64_t kprime_bytes = fast128 ? (int64_t)c.layers * c.kv_heads * lo.T_mid * D * 2 : 0;
+  const int64_t rec_bytes = (int64_t)lo.n_chunks * w.rec_slot;
+  w.kprime = take(at, kprime_bytes);
+  // the record slots are written by the rANS encoder, after the last reader
+  // of the un-rotated keys (the quantiser): they share its memory when it is
+  // large enough
+  w.rec = (kprime_bytes > 0 && rec_bytes <= kprime_bytes) ? w.kprime : take(at, rec_bytes);
+  w.rec_size = take(at, (int64_t)lo.n_chunks * 4);
+  w.rec_pos = take(at, (int64_t)lo.n_chunks * 8 + 8);
   w.fixed = take(at, paged ? lo.chunks_off : 0);
   w.total = at;
   return w;
