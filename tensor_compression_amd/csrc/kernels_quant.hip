@@ -24,6 +24,8 @@
 // of the token with itself, taken 1% high.
 #include <string.h>
 
+#include <type_traits>
+
 #include "kvtc_internal.h"
 
 namespace kvtc {
@@ -43,8 +45,15 @@ struct QInfo {     // per component, sorted order (b > 0 first, by width)
 };
 
 constexpr int kQWaves = 8;  // one packed tile per wave
+// Per-wave queue of codes to recompute exactly.  The hot loop only notes, in a
+// scalar bitmask, which 16 x 16 steps of a 16-token group had a code within
+// its error bound of a rounding boundary; after the group those steps are
+// redone and their codes queued (one step adds at most 256 entries, and the
+// queue is drained once it holds kQDrain or more).
+constexpr int kQDrain = 64;
+constexpr int kQCap = kQDrain + 256;
 
-__global__ __launch_bounds__(64 * kQWaves) void k_quant128(const Params p0) {
+__global__ __launch_bounds__(64 * kQWaves, 4) void k_quant128(const Params p0) {
   const Params p = at_seq(p0, blockIdx.z);
   constexpr int D = 128;
   const int u = blockIdx.y;
@@ -58,6 +67,7 @@ __global__ __launch_bounds__(64 * kQWaves) void k_quant128(const Params p0) {
   __shared__ uint32_t s_row[kQWaves][D];  // per wave: row offset (words) in its tile, sorted order
   __shared__ uint8_t s_wmap[2048 + 64];   // segment-buffer word -> sorted component
   __shared__ int32_t s_misc[4];           // nnz, segment words, full tile words
+  __shared__ uint32_t s_queue[kQWaves][kQCap];  // (sub-tile token << 16) | (sorted component << 8) | code
   extern __shared__ __attribute__((aligned(16))) uint32_t dq[];  // [B fragments][segment buffers]
 
   const int64_t si0 = (int64_t)u * D;
@@ -176,21 +186,128 @@ __global__ __launch_bounds__(64 * kQWaves) void k_quant128(const Params p0) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) a[kb] = *reinterpret_cast<const uint4*>(rowp + 32 * kb + 8 * g);
     };
-    // two groups in flight ahead of the one being projected
-    uint4 An[4], An2[4];
-    load_group(0, 0, An);
-    load_group(0, 1, An2);
+    // four group buffers: group kk of a sub-tile lives in Ab[kk]; the loads of
+    // group kk + 2 are issued while group kk is projected
+    uint4 Ab[4][4];
+    load_group(0, 0, Ab[0]);
+    load_group(0, 1, Ab[1]);
+    // Exact re-computation of the queued codes, one per lane: the fp64 sum of
+    // the 128 exact bf16 products (four independent partial sums), rounded to
+    // fp32 once, then the code; a changed code is XOR-ed into the segment
+    // buffer over the provisional one.
+    uint32_t* queue = s_queue[wave];
+    int qn = 0;
+    auto drain = [&](int sub) {
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      for (int q0 = 0; q0 < qn; q0 += 64) {
+        if (q0 + lane < qn) {
+          const uint32_t ent = queue[q0 + lane];
+          const int t = (int)(ent >> 16), k = (int)((ent >> 8) & 0xffu);
+          const uint32_t old = ent & 0xffu;
+          const QInfo qk = s_q[k];
+          const int tt = sub * 64 + t;  // tile-relative token
+          const uint16_t* rowp = src + (pre ? (row0 + tt) * D : cache_row(p, l, h, p.mid_begin + t0 + ta + tt));
+          const int mk = k >> 4, rk = k & 15;
+          double part[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 1
+          for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll 1
+            for (int gq = 0; gq < 4; ++gq) {
+              // channels 32 kb + 8 gq .. +7: the token row and the component's basis fragment
+              const uint4 xv = *reinterpret_cast<const uint4*>(rowp + 32 * kb + 8 * gq);
+              const uint4 bv = sB[(mk * 4 + kb) * 64 + 16 * gq + rk];
+              const uint32_t aw[4] = {xv.x, xv.y, xv.z, xv.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+              for (int z = 0; z < 4; ++z) {
+                part[z] += (double)__fmul_rn(__uint_as_float(aw[z] << 16), __uint_as_float(bw[z] << 16));
+                part[z] += (double)__fmul_rn(__uint_as_float(aw[z] & 0xffff0000u), __uint_as_float(bw[z] & 0xffff0000u));
+              }
+            }
+          }
+          const double cex = (part[0] + part[1]) + (part[2] + part[3]);
+          const float v = __fmul_rn(__fsub_rn((float)cex, qk.zero), qk.rcp);
+          const uint32_t code = __float_as_uint(__fadd_rn(__builtin_amdgcn_fmed3f(v, 0.0f, (float)((1u << qk.b) - 1u)),
+                                                          0x1p23f)) & 0xffu;
+          const uint64_t dx = (uint64_t)(code ^ old) << ((t * qk.b) & 31);
+          const uint32_t wi = qk.seg + (((uint32_t)t * qk.b) >> 5);
+          if (dx) {
+            atomicXor(&segbuf[wi], (uint32_t)dx);
+            if (dx >> 32) atomicXor(&segbuf[wi + 1], (uint32_t)(dx >> 32));
+          }
+        }
+      }
+      refined += (uint32_t)qn;
+      qn = 0;
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    };
+    // The 16 x 16 (token x component) steps of one 16-token group: project,
+    // quantise, queue the codes within their error bound of a rounding
+    // boundary, OR the provisional codes into segbuf.  FULL: the tile has
+    // every token (no tail masking).
+    auto group = [&](auto full_tag, const uint4 (&A)[4], const float (&tn)[4], int kk, int tb0, int sub) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      for (int m = 0; m < NT; ++m) {
+        uint4 Bm[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) Bm[kb] = sB[(m * 4 + kb) * 64 + lane];
+        const QInfo qi = s_q[16 * m + r];
+        const uint32_t b = qi.b;
+        const float qmax = (float)((1u << b) - 1u);
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[kb]),
+                                                        __builtin_bit_cast(bf16x8_t, Bm[kb]), acc, 0, 0, 0);
+        uint32_t uq[4];
+        uint64_t near[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // components without codes (b = 0, rcp = 0, qmax = 0) give v = 0 and
+          // code 0, so only the token tail needs masking
+          const float v = __fmul_rn(__fsub_rn(acc[e], qi.zero), qi.rcp);
+          const float vc = (FULL || tb0 + e < nt) ? __builtin_amdgcn_fmed3f(v, 0.0f, qmax) : 0.0f;
+          const float sv = __fadd_rn(vc, 0x1p23f);  // rint(vc), nearest even, in the low bits
+          uq[e] = __float_as_uint(sv);
+          const float d = __fsub_rn(vc, __fsub_rn(sv, 0x1p23f));
+          near[e] = __ballot(fabsf(d) > __fmaf_rn(-__uint_as_float(qi.pad), tn[e], qi.thr));
+        }
+        if (near[0] | near[1] | near[2] | near[3]) {
+          // queue them: (sub-tile token, sorted component, provisional code)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (near[e]) {
+              const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(near[e] >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)near[e], 0u));
+              if ((near[e] >> lane) & 1ull)
+                queue[qn + below] = ((uint32_t)((tb0 & 63) + e) << 16) | ((uint32_t)(16 * m + r) << 8) | (uq[e] & 0xffu);
+              qn += (int)__popcll(near[e]);
+            }
+          }
+        }
+        // four codes -> one 4b-bit piece (the exponent bits cancel in kb)
+        const uint32_t piece = uq[0] + (uq[1] << b) + (uq[2] << (2 * b)) + (uq[3] << (3 * b)) - qi.kb;
+        if (piece != 0u) {
+          const uint32_t bitoff = (uint32_t)(kk * 16 + 4 * g) * b;
+          const uint32_t wi = qi.seg + (bitoff >> 5), sh = bitoff & 31;
+          atomicOr(&segbuf[wi], piece << sh);
+          if (sh + 4 * b > 32) atomicOr(&segbuf[wi + 1], piece >> (32 - sh));
+        }
+        if (qn >= kQDrain) drain(sub);
+      }
+    };
+    const bool full = nt == p.tile_tokens;
     for (int sub = 0; sub * 64 < nt; ++sub) {
       for (uint32_t w = lane; w < segw + 4; w += 64) segbuf[w] = 0u;
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
-      for (int kk = 0; kk < 4; ++kk) {
-        uint4 A[4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) { A[kb] = An[kb]; An[kb] = An2[kb]; }
+      for (int kk = 0; kk < 4; ++kk) {
         // group kk + 2 of this sub-tile or of the next (the loads of groups
         // past the tile are clamped to its last token and never used)
-        load_group(sub + ((kk + 2) >> 2), (kk + 2) & 3, An2);
+        load_group(sub + ((kk + 2) >> 2), (kk + 2) & 3, Ab[(kk + 2) & 3]);
+        const uint4 (&A)[4] = Ab[kk];
         // norm bound of the token of output element (row 4 g + e of the group)
         float tn[4];
         {
@@ -210,78 +327,10 @@ __global__ __launch_bounds__(64 * kQWaves) void k_quant128(const Params p0) {
           for (int e = 0; e < 4; ++e) tn[e] = 1.01f * __fsqrt_rn(__shfl(n2, 4 * g + e, 64));
         }
         const int tb0 = sub * 64 + kk * 16 + 4 * g;  // tile-relative token of element 0
-        for (int m = 0; m < NT; ++m) {
-          uint4 Bm[4];
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb) Bm[kb] = sB[(m * 4 + kb) * 64 + lane];
-          const QInfo qi = s_q[16 * m + r];
-          const uint32_t b = qi.b;
-          const float qmax = (float)((1u << b) - 1u);
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[kb]),
-                                                          __builtin_bit_cast(bf16x8_t, Bm[kb]), acc, 0, 0, 0);
-          uint32_t uq[4];
-          uint32_t flags = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bool valid = b > 0 && tb0 + e < nt;
-            const float v = __fmul_rn(__fsub_rn(acc[e], qi.zero), qi.rcp);
-            const float vc = valid ? __builtin_amdgcn_fmed3f(v, 0.0f, qmax) : 0.0f;
-            const float sv = __fadd_rn(vc, 0x1p23f);  // rint(vc), nearest even, in the low bits
-            uq[e] = __float_as_uint(sv);
-            const float d = __fsub_rn(vc, __fsub_rn(sv, 0x1p23f));
-            if (fabsf(d) > __fmaf_rn(-__uint_as_float(qi.pad), tn[e], qi.thr)) flags |= 1u << e;
-          }
-          uint64_t pend = __ballot(flags != 0);
-          while (pend) {
-            // exact coefficient of (row rho of the group, component of lane L):
-            // fp64 sum of the exact products over the four lanes holding the row
-            const int L = __ffsll((unsigned long long)pend) - 1;
-            const int e = __ffs(__shfl(flags, L, 64)) - 1;
-            const int rho = 4 * (L >> 4) + e, r0 = L & 15;
-            double part = 0.0;
-            if (r == rho) {
-#pragma unroll
-              for (int kb = 0; kb < 4; ++kb) {
-                const uint4 bv = sB[(m * 4 + kb) * 64 + (lane & 48) + r0];
-                uint32_t aw[4] = {A[kb].x, A[kb].y, A[kb].z, A[kb].w};
-                // keep the unpacking of this rarely taken path inside the loop
-                asm volatile("" : "+v"(aw[0]), "+v"(aw[1]), "+v"(aw[2]), "+v"(aw[3]));
-                const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
-#pragma unroll
-                for (int z = 0; z < 4; ++z) {
-                  // bf16 x bf16 products are exact in fp32
-                  part += (double)__fmul_rn(__uint_as_float(aw[z] << 16), __uint_as_float(bw[z] << 16));
-                  part += (double)__fmul_rn(__uint_as_float(aw[z] & 0xffff0000u), __uint_as_float(bw[z] & 0xffff0000u));
-                }
-              }
-            }
-            part += __shfl_xor(part, 16, 64);
-            part += __shfl_xor(part, 32, 64);
-            const double cex = __shfl(part, rho, 64);
-            if (lane == L) {
-              const float v = __fmul_rn(__fsub_rn((float)cex, qi.zero), qi.rcp);
-              const uint32_t un = __float_as_uint(__fadd_rn(__builtin_amdgcn_fmed3f(v, 0.0f, qmax), 0x1p23f));
-#pragma unroll
-              for (int z = 0; z < 4; ++z)
-                if (z == e) uq[z] = un;
-              flags &= ~(1u << e);
-            }
-            ++refined;
-            pend = __ballot(flags != 0);
-          }
-          // four codes -> one 4b-bit piece (the exponent bits cancel in kb)
-          const uint32_t piece = uq[0] + (uq[1] << b) + (uq[2] << (2 * b)) + (uq[3] << (3 * b)) - qi.kb;
-          if (b > 0 && piece != 0u) {
-            const uint32_t bitoff = (uint32_t)(kk * 16 + 4 * g) * b;
-            const uint32_t wi = qi.seg + (bitoff >> 5), sh = bitoff & 31;
-            atomicOr(&segbuf[wi], piece << sh);
-            if (sh + 4 * b > 32) atomicOr(&segbuf[wi + 1], piece >> (32 - sh));
-          }
-        }
+        if (full) group(std::true_type{}, A, tn, kk, tb0, sub);
+        else group(std::false_type{}, A, tn, kk, tb0, sub);
       }
+      if (qn > 0) drain(sub);
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
       // segment buffer -> the rows of the packed tile
