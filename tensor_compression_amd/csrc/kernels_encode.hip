@@ -928,7 +928,7 @@ __global__ __launch_bounds__(256) void k_unrope128(const Params p0) {
 constexpr int kXS = 136;  // LDS row stride (bf16) of staged tokens: 16-B aligned, 4-bank shift
 
 template <int MODE>
-__global__ __launch_bounds__(256) void k_enc128(const Params p0, int sec0, float* coef_out) {
+__global__ __launch_bounds__(256, MODE == 0 ? 4 : 1) void k_enc128(const Params p0, int sec0, float* coef_out) {
   const Params p = at_seq(p0, blockIdx.z);
   constexpr int D = 128;
   const int u = blockIdx.y + sec0, ch = blockIdx.x;
@@ -944,7 +944,8 @@ __global__ __launch_bounds__(256) void k_enc128(const Params p0, int sec0, float
   const bool pre = MODE != 2 && s == 0 && p.rope_keys;
   const uint16_t* src = pre ? reinterpret_cast<const uint16_t*>(p.ws + p.w.kprime)
                             : reinterpret_cast<const uint16_t*>(s ? p.v : p.k);
-  const bool rope = !pre && (s == 0) && p.rope_keys;
+  // only the coefficient export rotates in place (the passes read un-rotated keys)
+  const bool rope = MODE == 2 && !pre && (s == 0) && p.rope_keys;
   const int64_t lh_row0 = ((int64_t)l * p.H + h) * (pre ? p.T_mid : p.T);
   const int pos_base = pre ? 0 : p.mid_begin;
   const int64_t bi = basis_index(p, l, s, h) * D * D;
@@ -1100,20 +1101,31 @@ __global__ __launch_bounds__(256) void k_enc128(const Params p0, int sec0, float
       }
     }
     if constexpr (MODE == 0) {
+      // min / max as med3 against -inf / +inf: one instruction each (finite
+      // coefficients; non-finite inputs are caught by the fp64 sums)
+      auto accumulate = [&](float c, int m) {
+        sum[m] += (double)c;
+        sq[m] = __fma_rn((double)c, (double)c, sq[m]);
+        mn[m] = __builtin_amdgcn_fmed3f(c, mn[m], -INFINITY);
+        mx[m] = __builtin_amdgcn_fmed3f(c, mx[m], INFINITY);
+      };
+      if (sub * 64 + 64 <= n) {  // a full sub-tile
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (sub * 64 + kk * 16 + 4 * g + e < n) {
+          for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-              const float c = acc[kk][m][e];
-              sum[m] += (double)c;
-              sq[m] = __fma_rn((double)c, (double)c, sq[m]);
-              mn[m] = fminf(mn[m], c);
-              mx[m] = fmaxf(mx[m], c);
+            for (int m = 0; m < 2; ++m) accumulate(acc[kk][m][e], m);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (sub * 64 + kk * 16 + 4 * g + e < n) {
+#pragma unroll
+              for (int m = 0; m < 2; ++m) accumulate(acc[kk][m][e], m);
             }
-          }
+      }
     } else if constexpr (MODE == 2) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
