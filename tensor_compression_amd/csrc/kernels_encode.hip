@@ -1343,110 +1343,123 @@ __device__ __forceinline__ uint64_t alloc_key(float var, int k, int i) {
   return (((e2 << 23) | man) << 8) | (uint64_t)(255 - i);
 }
 
-__global__ __launch_bounds__(128) void k_enc_alloc(const Params p0) {
+// One wave per section; lane l holds components l and l + 64 (head_dim 128).
+__global__ __launch_bounds__(64) void k_enc_alloc(const Params p0) {
   const Params p = at_seq(p0, blockIdx.z);
   const int u = blockIdx.x;
   const int D = p.D;
-  const int i = threadIdx.x;
+  const int lane = threadIdx.x;
+  const int NC = D / 64;  // components per lane
   const int s = (u / p.H) & 1;
-  const bool active = i < D;
-  __shared__ uint32_t s_cnt[2];
-  __shared__ float s_amax[2];
   uint8_t* rec = p.out + p.side_off + (int64_t)u * 9 * D;
   const int64_t N = p.T_mid;
-  float mu = 0.f, var = 0.f, mn = 0.f, mx = 0.f;
+  float mu[2] = {0.f, 0.f}, var[2] = {0.f, 0.f}, mn[2] = {0.f, 0.f}, mx[2] = {0.f, 0.f};
   bool nonfinite = false;
-  if (active && N > 0) {
-    double a = 0.0, b = 0.0;
-    float c = INFINITY, d = -INFINITY;
-    for (int ch = 0; ch < p.chunks_per_sec; ++ch) {
-      int64_t idx = ((int64_t)u * p.chunks_per_sec + ch) * D + i;
-      a += reinterpret_cast<const double*>(p.ws + p.w.part_sum)[idx];
-      b += reinterpret_cast<const double*>(p.ws + p.w.part_sq)[idx];
-      c = fminf(c, reinterpret_cast<const float*>(p.ws + p.w.part_min)[idx]);
-      d = fmaxf(d, reinterpret_cast<const float*>(p.ws + p.w.part_max)[idx]);
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int i = lane + 64 * c;
+    if (c < NC && N > 0) {
+      double a = 0.0, b = 0.0;
+      float lo = INFINITY, hi = -INFINITY;
+      for (int ch = 0; ch < p.chunks_per_sec; ++ch) {
+        const int64_t idx = ((int64_t)u * p.chunks_per_sec + ch) * D + i;
+        a += reinterpret_cast<const double*>(p.ws + p.w.part_sum)[idx];
+        b += reinterpret_cast<const double*>(p.ws + p.w.part_sq)[idx];
+        lo = fminf(lo, reinterpret_cast<const float*>(p.ws + p.w.part_min)[idx]);
+        hi = fmaxf(hi, reinterpret_cast<const float*>(p.ws + p.w.part_max)[idx]);
+      }
+      nonfinite |= !isfinite(a) || !isfinite(b);
+      const double m = a / (double)N;
+      double vv = (b - a * m) / (double)N;
+      if (vv < 0.0) vv = 0.0;
+      mu[c] = (float)m;
+      var[c] = (lo != hi) ? (float)vv : 0.0f;
+      mn[c] = lo;
+      mx[c] = hi;
     }
-    nonfinite = !isfinite(a) || !isfinite(b);
-    double m = a / (double)N;
-    double vv = (b - a * m) / (double)N;
-    if (vv < 0.0) vv = 0.0;
-    mu = (float)m;
-    var = (c != d) ? (float)vv : 0.0f;
-    mn = c;
-    mx = d;
   }
-  if (nonfinite) set_status(p.ws, p.w, KVTC_ERR_NONFINITE);
+  if (__ballot(nonfinite) && lane == 0) set_status(p.ws, p.w, KVTC_ERR_NONFINITE);
   // ---- bit widths ----
-  uint32_t bits = 0;
+  uint32_t bits[2] = {0u, 0u};
   if (p.transform == KVTC_PCA) {
     const int budget = s == 0 ? p.budget_k : p.budget_v;
     // greedy marginal allocation == the `budget` largest var_i 4^-k (k < max_bits),
     // ranked by exact value then lowest index: find the budget-th largest key
-    // by a bitwise search over the 41-bit keys
-    const bool cand = active && var > 0.0f;
-    auto count_ge = [&](uint64_t thr) -> uint32_t {
-      uint32_t cnt = 0;
-      if (cand)
-        for (int k = 0; k < p.max_bits; ++k) cnt += alloc_key(var, k, i) >= thr ? 1u : 0u;
-      // block sum (two waves)
-      for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
-      __syncthreads();
-      if ((threadIdx.x & 63) == 0) s_cnt[threadIdx.x >> 6] = cnt;
-      __syncthreads();
-      return s_cnt[0] + (blockDim.x > 64 ? s_cnt[1] : 0u);
+    // by a bitwise search over the 41-bit keys.  The keys are formed once
+    // (0 for no candidate, below every real key) and counted with ballots.
+    uint64_t key[2][8];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        key[c][k] = (c < NC && var[c] > 0.0f && k < p.max_bits) ? alloc_key(var[c], k, lane + 64 * c) : 0ull;
+    auto count_ge = [&](uint64_t thr) -> int {
+      int cnt = 0;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) cnt += (int)__popcll(__ballot(key[c][k] >= thr));
+      return cnt;
     };
     uint64_t thr = 1;  // every real candidate key is >= 1
-    if ((int)count_ge(1) > budget) {
+    if (count_ge(1) > budget) {
       uint64_t t = 0;
       for (int bit = 40; bit >= 0; --bit) {
-        uint64_t c2 = t | (1ull << bit);
-        if ((int)count_ge(c2) >= budget) t = c2;
+        const uint64_t c2 = t | (1ull << bit);
+        if (count_ge(c2) >= budget) t = c2;
       }
       thr = t;
     }
-    if (cand && budget > 0)
-      for (int k = 0; k < p.max_bits; ++k) bits += alloc_key(var, k, i) >= thr ? 1u : 0u;
+    if (budget > 0)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) bits[c] += key[c][k] >= thr ? 1u : 0u;
   } else {
-    bits = (uint32_t)(s == 0 ? p.bits_k_uniform : p.bits_v_uniform);
+    bits[0] = bits[1] = (uint32_t)(s == 0 ? p.bits_k_uniform : p.bits_v_uniform);
   }
   // ---- side information ----
-  float zero = 0.f, scale = 0.f, rcp = 0.f;
   const bool sym = p.transform == KVTC_WHT && s == 0;
+  float amax = 0.f;
   if (sym) {
-    float a = active ? fmaxf(fabsf(mn), fabsf(mx)) : 0.f;
-    if (N == 0) a = 0.f;
-    for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o, 64));
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) s_amax[threadIdx.x >> 6] = a;
-    __syncthreads();
-    float amax = fmaxf(s_amax[0], blockDim.x > 64 ? s_amax[1] : 0.f);
-    const int Q = (1 << (bits - 1)) - 1;
-    scale = (float)__ddiv_rn((double)amax, (double)Q);
-    rcp = scale > 0.f ? __fdiv_rn(1.0f, scale) : 0.f;
-    if (!(scale > 0.f) || isinf(rcp)) { scale = 0.f; rcp = 0.f; }
-  } else if (bits == 0) {
-    zero = mu;
-  } else {
-    zero = mn;
-    scale = (float)__ddiv_rn((double)mx - (double)mn, (double)((1u << bits) - 1u));
-    rcp = scale > 0.f ? __fdiv_rn(1.0f, scale) : 0.f;
-    if (!(scale > 0.f) || isinf(rcp)) { scale = 0.f; rcp = 0.f; }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      if (c < NC && N > 0) amax = fmaxf(amax, fmaxf(fabsf(mn[c]), fabsf(mx[c])));
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
   }
-  if (N == 0) { bits = 0; zero = 0.f; scale = 0.f; rcp = 0.f; }
-  if (active) {
-    rec[i] = (uint8_t)bits;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    if (c >= NC) continue;
+    const int i = lane + 64 * c;
+    uint32_t b = bits[c];
+    float zero = 0.f, scale = 0.f, rcp = 0.f;
+    if (sym) {
+      const int Q = (1 << (b - 1)) - 1;
+      scale = (float)__ddiv_rn((double)amax, (double)Q);
+      rcp = scale > 0.f ? __fdiv_rn(1.0f, scale) : 0.f;
+      if (!(scale > 0.f) || isinf(rcp)) { scale = 0.f; rcp = 0.f; }
+    } else if (b == 0) {
+      zero = mu[c];
+    } else {
+      zero = mn[c];
+      scale = (float)__ddiv_rn((double)mx[c] - (double)mn[c], (double)((1u << b) - 1u));
+      rcp = scale > 0.f ? __fdiv_rn(1.0f, scale) : 0.f;
+      if (!(scale > 0.f) || isinf(rcp)) { scale = 0.f; rcp = 0.f; }
+    }
+    if (N == 0) { b = 0; zero = 0.f; scale = 0.f; rcp = 0.f; }
+    rec[i] = (uint8_t)b;
     reinterpret_cast<float*>(rec + D)[i] = zero;
     reinterpret_cast<float*>(rec + 5 * (int64_t)D)[i] = scale;
-    int64_t si = (int64_t)u * D + i;
+    const int64_t si = (int64_t)u * D + i;
     reinterpret_cast<float*>(p.ws + p.w.side_zero)[si] = zero;
     reinterpret_cast<float*>(p.ws + p.w.side_rcp)[si] = rcp;
-    p.ws[p.w.side_bits + si] = (uint8_t)bits;
-    reinterpret_cast<float4*>(p.ws + p.w.sec_stats)[si] = make_float4(mu, var, mn, mx);
+    p.ws[p.w.side_bits + si] = (uint8_t)b;
+    reinterpret_cast<float4*>(p.ws + p.w.sec_stats)[si] = make_float4(mu[c], var[c], mn[c], mx[c]);
   }
 }
 
 hipError_t launch_enc_alloc(const Params& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_enc_alloc, dim3(p.n_sections, 1, seq_grid(p)), dim3(p.D), 0, s, p);
+  hipLaunchKernelGGL(k_enc_alloc, dim3(p.n_sections, 1, seq_grid(p)), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
