@@ -198,60 +198,78 @@ __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) 
 // bit-exactly ("How the Pipeline Works": they stay in high fidelity)
 // ---------------------------------------------------------------------------
 
-__global__ void k_clear_status(uint8_t* ws, WsLayout w) {
-  if (threadIdx.x == 0) {
-    uint32_t* s = reinterpret_cast<uint32_t*>(ws + w.status);
-    s[0] = 0; s[1] = 0; s[2] = 0; s[3] = 0;
-  }
-}
-
 // to_container = 1: cache -> container (+ zero the side and raw padding);
 // 0: container -> output tensors in out_dtype.
 // Raw regions as contiguous runs: for every (tensor, region, layer x head) the
 // n_region rows are consecutive both in the cache ([L,H,T,D]) and in the
-// container ([L,H,n_region,D] per tensor and region).  Workgroup y = run,
-// x = 4 KiB piece of the run; one 16-byte unit per thread (rows are whole
-// 16-byte units for head_dim 64 and 128).
+// container ([L,H,n_region,D] per tensor and region).  One workgroup per run;
+// each thread moves up to eight 16-byte units (rows are whole 16-byte units
+// for head_dim 64 and 128), all loads issued before the stores.  Encode: the
+// first workgroup also clears the status block.
 __global__ __launch_bounds__(256) void k_copy_raw(const Params p0, int to_container) {
   const Params p = at_seq(p0, blockIdx.z);
   const int e = p.dtype == KVTC_BF16 ? 2 : 4;
   const int row_units = p.D * e / 16;
   const int LH = p.L * p.H;
-  const int run = blockIdx.y;
+  const int run = blockIdx.x;
   const int s = run / (2 * LH), region = (run / LH) & 1, lh = run % LH;
   const int n_region = region == 0 ? p.s0 : p.W_eff;
   const int units = n_region * row_units;
-  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (to_container && p0.n_seqs == 0 && run == 0 && threadIdx.x < 4)
+    reinterpret_cast<uint32_t*>(p.ws + p.w.status)[threadIdx.x] = 0u;
   if (!to_container && (get_status(p.ws, p.w) & (1u << KVTC_ERR_CORRUPT))) return;
-  if (i < units) {
-    const int64_t row_bytes = (int64_t)p.D * e;
-    const int64_t per_tensor = (int64_t)LH * (p.s0 + p.W_eff) * row_bytes;
-    const int64_t coff = (int64_t)s * per_tensor + (region == 0 ? 0 : (int64_t)LH * p.s0 * row_bytes) +
-                         (int64_t)lh * n_region * row_bytes + (int64_t)i * 16;
-    const int pos0 = region == 0 ? 0 : p.mid_end;
+  const int64_t row_bytes = (int64_t)p.D * e;
+  const int64_t per_tensor = (int64_t)LH * (p.s0 + p.W_eff) * row_bytes;
+  const int64_t cbase = (int64_t)s * per_tensor + (region == 0 ? 0 : (int64_t)LH * p.s0 * row_bytes) +
+                        (int64_t)lh * n_region * row_bytes;
+  const int pos0 = region == 0 ? 0 : p.mid_end;
+  // first element of unit i of the run in the cache
+  auto telem = [&](int i) {
     const int row = i / row_units, ui = i - row * row_units;
-    // first element of the unit
-    const int64_t telem = cache_row(p, lh / p.H, lh % p.H, pos0 + row) + (int64_t)ui * (16 / e);
+    return cache_row(p, lh / p.H, lh % p.H, pos0 + row) + (int64_t)ui * (16 / e);
+  };
+  for (int i0 = 0; i0 < units; i0 += 8 * 256) {
+    uint4 v[8];
     if (to_container) {
       const uint8_t* src = reinterpret_cast<const uint8_t*>(s ? p.v : p.k);
-      *reinterpret_cast<uint4*>(p.out + p.raw_off + coff) = *reinterpret_cast<const uint4*>(src + telem * e);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k * 256 + (int)threadIdx.x;
+        if (i < units) v[k] = *reinterpret_cast<const uint4*>(src + telem(i) * e);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k * 256 + (int)threadIdx.x;
+        if (i < units) *reinterpret_cast<uint4*>(p.out + p.raw_off + cbase + (int64_t)i * 16) = v[k];
+      }
     } else {
-      const uint4 w = *reinterpret_cast<const uint4*>(p.in + p.raw_off + coff);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k * 256 + (int)threadIdx.x;
+        if (i < units) v[k] = *reinterpret_cast<const uint4*>(p.in + p.raw_off + cbase + (int64_t)i * 16);
+      }
       void* dst = s ? p.v_out : p.k_out;
-      if (p.out_dtype == p.dtype) {
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(dst) + telem * e) = w;
-      } else if (p.dtype == KVTC_BF16) {  // bf16 -> fp32: exact widening of 8 values
-        uint4* d = reinterpret_cast<uint4*>(reinterpret_cast<float*>(dst) + telem);
-        d[0] = make_uint4(w.x << 16, w.x & 0xffff0000u, w.y << 16, w.y & 0xffff0000u);
-        d[1] = make_uint4(w.z << 16, w.z & 0xffff0000u, w.w << 16, w.w & 0xffff0000u);
-      } else {  // fp32 -> bf16 (RNE) of 4 values
-        const uint32_t lo = (uint32_t)f32_to_bf16(__uint_as_float(w.x)) | ((uint32_t)f32_to_bf16(__uint_as_float(w.y)) << 16);
-        const uint32_t hi = (uint32_t)f32_to_bf16(__uint_as_float(w.z)) | ((uint32_t)f32_to_bf16(__uint_as_float(w.w)) << 16);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dst) + telem) = make_uint2(lo, hi);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k * 256 + (int)threadIdx.x;
+        if (i >= units) continue;
+        const uint4 w = v[k];
+        const int64_t te = telem(i);
+        if (p.out_dtype == p.dtype) {
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(dst) + te * e) = w;
+        } else if (p.dtype == KVTC_BF16) {  // bf16 -> fp32: exact widening of 8 values
+          uint4* d = reinterpret_cast<uint4*>(reinterpret_cast<float*>(dst) + te);
+          d[0] = make_uint4(w.x << 16, w.x & 0xffff0000u, w.y << 16, w.y & 0xffff0000u);
+          d[1] = make_uint4(w.z << 16, w.z & 0xffff0000u, w.w << 16, w.w & 0xffff0000u);
+        } else {  // fp32 -> bf16 (RNE) of 4 values
+          const uint32_t lo = (uint32_t)f32_to_bf16(__uint_as_float(w.x)) | ((uint32_t)f32_to_bf16(__uint_as_float(w.y)) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16(__uint_as_float(w.z)) | ((uint32_t)f32_to_bf16(__uint_as_float(w.w)) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dst) + te) = make_uint2(lo, hi);
+        }
       }
     }
   }
-  if (to_container && run == 0 && blockIdx.x == 0 && threadIdx.x < 64) {
+  if (to_container && run == 0 && threadIdx.x < 64) {
     // zero padding: the gap between the side records (and r area) and
     // raw_off, and the raw area's tail; each is shorter than 16 bytes
     int64_t r_used = 0;
@@ -264,16 +282,11 @@ __global__ __launch_bounds__(256) void k_copy_raw(const Params p0, int to_contai
 }
 
 hipError_t launch_copy_raw(const Params& p, int to_container, hipStream_t s) {
-  if (to_container && p.n_seqs == 0) {
-    hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(64), 0, s, p.ws, p.w);
-  }
   const int e = p.dtype == KVTC_BF16 ? 2 : 4;
   if ((p.D * e) % 16) return hipErrorInvalidValue;
-  const int64_t units = (int64_t)(p.s0 > p.W_eff ? p.s0 : p.W_eff) * (p.D * e / 16);
-  const int64_t bx = units > 0 ? (units + 255) / 256 : 1;
   const int64_t runs = 4 * (int64_t)p.L * p.H;
-  if (bx > 65535 || runs > 65535) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_copy_raw, dim3((unsigned)bx, (unsigned)runs, seq_grid(p)), dim3(256), 0, s, p, to_container);
+  if (runs > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_copy_raw, dim3((unsigned)runs, 1, seq_grid(p)), dim3(256), 0, s, p, to_container);
   return hipGetLastError();
 }
 
