@@ -55,6 +55,9 @@ def parse():
                     help="print a per-kernel table from a rocprofv3 --stats output folder and exit")
     ap.add_argument("--summarize-pmc", metavar="DIR",
                     help="print per-kernel mean counters from a rocprofv3 --pmc csv folder and exit")
+    ap.add_argument("--traffic-table", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the per-phase HBM traffic table from FETCH_SIZE and WRITE_SIZE "
+                         "rocprofv3 --pmc csv folders of a --copy-calibration run and exit")
     return ap.parse_args()
 
 
@@ -122,6 +125,50 @@ def summarize_trace(d):
     print("|---|---|---|---|---|---|")
     for r in rows:
         print(f"| {r[0]} | {r[1]} | {r[2]:.1f} | {r[3]:.1f} | {r[4]:.1f} | {r[5]:.1f} |")
+
+
+def pmc_means(d, counter):
+    """Mean of `counter` per dispatch, per kernel, from a rocprofv3 --pmc csv folder."""
+    import collections
+    import csv
+    import glob
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    per[_short_kernel(r["Kernel_Name"])][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def traffic_table(fetch_dir, write_dir):
+    """Per-phase HBM bytes per launch: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) of the phase's kernels, each scaled by the ratio of the known
+    bytes of the calibration copy to what the same counter read for it."""
+    fetch, write = pmc_means(fetch_dir, "FETCH_SIZE"), pmc_means(write_dir, "WRITE_SIZE")
+    cal = [k for k in fetch if "bitwise_not" in k]
+    if not cal or cal[0] not in write:
+        raise SystemExit("no calibration copy kernel in the counter folders (run with --copy-calibration)")
+    known_kib = COPY_CAL_BYTES / 1024.0
+    ff, fw = known_kib / fetch[cal[0]], known_kib / write[cal[0]]
+    print(f"Calibration: the copy kernel moves {COPY_CAL_BYTES} B each way; FETCH_SIZE read "
+          f"{fetch[cal[0]]:.1f} KiB (factor {ff:.4f}), WRITE_SIZE read {write[cal[0]]:.1f} KiB "
+          f"(factor {fw:.4f}).")
+    print()
+    print("| kernel | FETCH_SIZE (KiB/dispatch) | WRITE_SIZE (KiB/dispatch) |")
+    print("|---|---|---|")
+    for k in sorted(fetch):
+        if k.startswith("k_"):
+            print(f"| {k} | {fetch[k]:.1f} | {write.get(k, 0.0):.1f} |")
+    print()
+    print("| phase | kernels | fetch bytes | write bytes | traffic bytes | sources digest |")
+    print("|---|---|---|---|---|---|")
+    for ph, (kernels, files) in PHASE_KERNELS.items():
+        names = [k for k in fetch if any(k == b or k.startswith(b + "<") for b in kernels)]
+        fb = sum(fetch[k] for k in names) * ff * 1024
+        wb = sum(write.get(k, 0.0) for k in names) * fw * 1024
+        print(f"| {ph} | {' + '.join(sorted(names))} | {fb:.0f} | {wb:.0f} | {fb + wb:.0f} | "
+              f"{source_digest(files)} |")
 
 
 def summarize_pmc(d):
@@ -327,6 +374,9 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
+        return
+    if args.traffic_table:
+        traffic_table(*args.traffic_table)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
