@@ -267,40 +267,68 @@ def test_bf16_output_within_one_ulp():
 
 # --------------------------------------------------------------------------- full size
 
-def test_llama3_8b_full_size_sampled():
-    """32 layers x 8 heads x 4096 tokens bf16 at 2 bits/comp, the benchmark's
-    launch configuration; the oracle checks sampled sections."""
-    w = synth.WORKLOADS["llama3_8b"]
+def _full_size_sampled(name, fixed_secs, n_random, ratio_range, seed=7, **over):
+    """A workload at its full size in the benchmark's launch configuration:
+    the whole cache is coded and decoded on the GPU and the oracle checks
+    sampled sections (statistics, widths, side information, coefficients,
+    codes, rANS records and the decoded middle)."""
+    w = synth.WORKLOADS[name]
     K, V = synth.generate(w, device="cuda")
     T = K.shape[2]
-    cfg = synth.oracle_config(w)
+    cfg = synth.oracle_config(w, **over)
     lo = orc.layout(cfg, T)
-    basis_t = fit_pca_basis(K, V, cfg, lo.mid_begin, lo.mid_end)
-    basis = basis_t.cpu().numpy()
+    basis_t = fit_pca_basis(K, V, cfg, lo.mid_begin, lo.mid_end) if cfg["transform"] == 0 else None
+    basis = None if basis_t is None else basis_t.cpu().numpy()
     plan = kvtc.Plan(cfg, basis_t, max_tokens=T)
     ws = plan.workspace(T)
     data_t, st = plan.encode(K, V, ws)
-    assert st == kvtc.OK
+    assert st == kvtc.OK, kvtc.STATUS[st]
     data = data_t.cpu().numpy().tobytes()
     stats = plan.section_stats(ws, T, lo.n_sections)
     k, v = synth.to_numpy_bits(K), synth.to_numpy_bits(V)
-    rng = np.random.default_rng(7)
-    secs = sorted(set([0, 7, 8, 255, 256, 511] + [int(x) for x in rng.integers(0, lo.n_sections, 4)]))
+    rng = np.random.default_rng(seed)
+    secs = sorted(set(fixed_secs + [int(x) for x in rng.integers(0, lo.n_sections, n_random)]))
     kd, vd, st = plan.decode(data_t, T, kvtc.FP32)
-    assert st == kvtc.OK
+    assert st == kvtc.OK, kvtc.STATUS[st]
+    H = w.kv_heads
     report = []
     for u in secs:
         coef, _ = plan.coeffs(K, V, u, u + 1, lo.T_mid)
         parity.compare_section(orc, cfg, T, k, v, basis, data, stats, u,
                                gpu_coef=coef[0].cpu().numpy(), report=report)
+        del coef
         mid_ref = orc.decode_sections(cfg, data, basis, u, u + 1, lo.T_mid)[0]
-        l, s, h = u // (2 * w.kv_heads), (u // w.kv_heads) % 2, u % w.kv_heads
+        l, s, h = u // (2 * H), (u // H) % 2, u % H
         src = k if s == 0 else v
         srcf = orc.bf16_bits_to_f32(src[l, h]).reshape(T, -1)
         rms = np.sqrt((srcf.astype(np.float64) ** 2).mean(axis=0))
         got = (kd if s == 0 else vd)[l, h, lo.mid_begin: lo.mid_end].cpu().numpy()
         parity.compare_decode(got, mid_ref, rms[None, :])
+        # raw windows of the sampled head restored bit-exactly
+        srcw = orc.bf16_bits_to_f32(src[l, h]).reshape(T, -1)
+        dec = (kd if s == 0 else vd)[l, h]
+        assert np.array_equal(srcw[: lo.s0], dec[: lo.s0].cpu().numpy())
+        assert np.array_equal(srcw[lo.mid_end:], dec[lo.mid_end:].cpu().numpy())
     codes = sum(r["codes"] for r in report)
     assert sum(r["boundary_codes"] for r in report) <= parity.BOUNDARY_FRACTION * codes
     ratio = (K.numel() + V.numel()) * 2 / len(data)
-    assert 5.0 < ratio < 9.0, ratio
+    assert ratio_range[0] < ratio < ratio_range[1], ratio
+
+
+def test_llama3_8b_full_size_sampled():
+    """32 layers x 8 heads x 4096 tokens bf16 at 2 bits/comp."""
+    _full_size_sampled("llama3_8b", [0, 7, 8, 255, 256, 511], 4, (5.0, 9.0))
+
+
+@pytest.mark.timeout(900)
+def test_qwen3_32b_full_size_sampled():
+    """64 layers x 8 heads x 32768 tokens bf16 at 2 bits/comp (the 8.6 GB
+    cache); first, last and layer-boundary sections plus random ones."""
+    _full_size_sampled("qwen3_32b", [0, 15, 16, 1023], 2, (5.0, 9.0), seed=3)
+
+
+@pytest.mark.timeout(900)
+def test_hadamard_long_full_size_sampled():
+    """32 layers x 8 heads x 131072 tokens bf16 on the Hadamard path (keys 4
+    bits, values 2 bits); WHT coefficients and codes are exact."""
+    _full_size_sampled("hadamard_long", [0, 8, 511], 2, (3.0, 9.0), seed=5)
