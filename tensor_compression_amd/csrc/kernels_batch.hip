@@ -149,6 +149,8 @@ __global__ __launch_bounds__(1024) void k_seq_setup(const Params p0, const int32
       uint32_t* st = reinterpret_cast<uint32_t*>(p0.ws + si[z].ws_off);
       st[0] = 0; st[1] = 0; st[2] = 0; st[3] = 0;
     }
+    for (int i = tid; i < n * kCountSlots; i += 1024)
+      *reinterpret_cast<uint32_t*>(p0.ws + si[i / kCountSlots].ws_off + kCountOff + kCountStride * (i % kCountSlots)) = 0u;
   }
   if (tid == 0) {
     bst[0] = (s_bad ? (1u << KVTC_ERR_INVALID_ARG) : 0u) | (corrupt ? (1u << KVTC_ERR_CORRUPT) : 0u);
@@ -259,6 +261,9 @@ __global__ __launch_bounds__(1024) void k_batch_finish(const Params p0) {
     bits |= st[0];
     refined += st[1];
   }
+  for (int i = tid; i < n * kCountSlots; i += 1024)
+    refined += *reinterpret_cast<const uint32_t*>(p0.ws + si[i / kCountSlots].ws_off + kCountOff +
+                                                  kCountStride * (i % kCountSlots));
   __shared__ uint32_t s_bits, s_ref;
   if (tid == 0) { s_bits = 0; s_ref = 0; }
   __syncthreads();

@@ -205,7 +205,7 @@ __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, uint32_t* total) 
 // container ([L,H,n_region,D] per tensor and region).  One workgroup per run;
 // each thread moves up to eight 16-byte units (rows are whole 16-byte units
 // for head_dim 64 and 128), all loads issued before the stores.  Encode: the
-// first workgroup also clears the status block.
+// first workgroup also clears the status word and the count slots.
 __global__ __launch_bounds__(256) void k_copy_raw(const Params p0, int to_container) {
   const Params p = at_seq(p0, blockIdx.z);
   const int e = p.dtype == KVTC_BF16 ? 2 : 4;
@@ -215,8 +215,11 @@ __global__ __launch_bounds__(256) void k_copy_raw(const Params p0, int to_contai
   const int s = run / (2 * LH), region = (run / LH) & 1, lh = run % LH;
   const int n_region = region == 0 ? p.s0 : p.W_eff;
   const int units = n_region * row_units;
-  if (to_container && p0.n_seqs == 0 && run == 0 && threadIdx.x < 4)
-    reinterpret_cast<uint32_t*>(p.ws + p.w.status)[threadIdx.x] = 0u;
+  if (to_container && p0.n_seqs == 0 && run == 0) {
+    if (threadIdx.x < 4) reinterpret_cast<uint32_t*>(p.ws + p.w.status)[threadIdx.x] = 0u;
+    if (threadIdx.x < kCountSlots)
+      *reinterpret_cast<uint32_t*>(p.ws + p.w.status + kCountOff + kCountStride * threadIdx.x) = 0u;
+  }
   if (!to_container && (get_status(p.ws, p.w) & (1u << KVTC_ERR_CORRUPT))) return;
   const int64_t row_bytes = (int64_t)p.D * e;
   const int64_t per_tensor = (int64_t)LH * (p.s0 + p.W_eff) * row_bytes;
@@ -1241,8 +1244,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? 4 : 1) void k_enc128(const Params 
       }
     }
   }
-  if (MODE == 1 && lane == 0 && refined)
-    atomicAdd(reinterpret_cast<uint32_t*>(p.ws + p.w.status) + 1, refined);
+  if (MODE == 1 && lane == 0 && refined) atomicAdd(count_slot(p.ws, p.w), refined);
   if constexpr (MODE == 0) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {

@@ -17,11 +17,11 @@
 // four codes of a lane fold into one 4b-bit piece that is OR-ed into the
 // wave's LDS segment buffer (the sub-tile's slice of every row); the buffer
 // is copied to the packed tile after every 64 tokens.  A code is recomputed
-// on the spot from the exact dot product (fp64 sum of the exact bf16
-// products, over the four lanes that hold the token) when v lies within the
-// coefficient's error bound of a rounding boundary: |c_mfma - c| <= mfma_err ||x||_2 (fp32 accumulation of
-// the exact products; Cauchy-Schwarz), with ||x||_2 from a bf16 dot product
-// of the token with itself, taken 1% high.
+// from the exact dot product (fp64 sum of the exact bf16 products) when v
+// lies within the coefficient's error bound of a rounding boundary:
+// |c_mfma - c| <= mfma_err ||x||_2 (fp32 accumulation of the exact products;
+// Cauchy-Schwarz), with ||x||_2 from a bf16 dot product of the token with
+// itself, taken 1% high.
 #include <string.h>
 
 #include <type_traits>
@@ -45,29 +45,40 @@ struct QInfo {     // per component, sorted order (b > 0 first, by width)
 };
 
 constexpr int kQWaves = 8;  // one packed tile per wave
-// Per-wave queue of codes to recompute exactly.  The hot loop only notes, in a
-// scalar bitmask, which 16 x 16 steps of a 16-token group had a code within
-// its error bound of a rounding boundary; after the group those steps are
-// redone and their codes queued (one step adds at most 256 entries, and the
-// queue is drained once it holds kQDrain or more).
-constexpr int kQDrain = 64;
-constexpr int kQCap = kQDrain + 256;
 
+// The lane index, formed anew at each use: lane-derived addresses are then
+// recomputed where they are needed instead of held in registers across the
+// projection loop.
+__device__ __forceinline__ int fresh_lane() {
+  int x;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+  return x;
+}
+// Per-wave queue of codes to recompute exactly.  The hot loop only sets, per
+// lane, one bit for every code of its pair that lies within its error bound
+// of a rounding boundary; after every 64 tokens (once they are in the packed
+// tile) the flagged codes are queued, and the queue is worked off at the end
+// of the tile, or when it fills up, with all its loads in flight together.
+constexpr int kQCap = 128;
 __global__ __launch_bounds__(64 * kQWaves, 4) void k_quant128(const Params p0) {
   const Params p = at_seq(p0, blockIdx.z);
   constexpr int D = 128;
   const int u = blockIdx.y;
   const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
   if (get_status(p.ws, p.w) & (1u << KVTC_ERR_NONFINITE)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in scalar registers
 
   __shared__ QInfo s_q[D];
+  __shared__ float4 s_hf[D];            // hot loop: rcp, -zero rcp, 2^b - 1, margin
+  __shared__ uint4 s_hu[D];             // hot loop: b, kb, seg, pad
   __shared__ uint8_t s_rank[D];
   __shared__ uint32_t s_bs[D];          // widths in sorted order
   __shared__ uint32_t s_row[kQWaves][D];  // per wave: row offset (words) in its tile, sorted order
   __shared__ uint8_t s_wmap[2048 + 64];   // segment-buffer word -> sorted component
   __shared__ int32_t s_misc[4];           // nnz, segment words, full tile words
-  __shared__ uint32_t s_queue[kQWaves][kQCap];  // (sub-tile token << 16) | (sorted component << 8) | code
+  __shared__ uint32_t s_flags[kQWaves][4][64];    // per wave: flags of the sub-tile's pairs and halves
+  __shared__ uint32_t s_queue[kQWaves][kQCap];  // (tile token << 16) | (sorted component << 8)
   extern __shared__ __attribute__((aligned(16))) uint32_t dq[];  // [B fragments][segment buffers]
 
   const int64_t si0 = (int64_t)u * D;
@@ -121,6 +132,17 @@ __global__ __launch_bounds__(64 * kQWaves, 4) void k_quant128(const Params p0) {
     __builtin_amdgcn_wave_barrier();
     s_q[2 * lane].seg = seg0;
     s_q[2 * lane + 1].seg = seg1;
+#pragma unroll
+    for (int z = 0; z < 2; ++z) {
+      // the hot loop forms v as one fma, c rcp + (-zero rcp); against the
+      // two roundings of (c - zero) rcp that adds the rounding of -zero rcp
+      // and of the fma to the margin to the rounding boundary
+      const QInfo& q = s_q[2 * lane + z];
+      const float nzr = __fmul_rn(-q.zero, q.rcp);
+      const float thr = q.thr - 0x1p-23f * fabsf(nzr);
+      s_hf[2 * lane + z] = make_float4(q.rcp, nzr, (float)((1u << q.b) - 1u), thr);
+      s_hu[2 * lane + z] = make_uint4(q.b, q.kb, z ? seg1 : seg0, q.pad);
+    }
     // word -> component map of the segment buffer
     for (uint32_t w = 0; w < 2 * sb0; ++w) s_wmap[seg0 + w] = (uint8_t)(2 * lane);
     for (uint32_t w = 0; w < 2 * sb1; ++w) s_wmap[seg1 + w] = (uint8_t)(2 * lane + 1);
@@ -178,174 +200,261 @@ __global__ __launch_bounds__(64 * kQWaves, 4) void k_quant128(const Params p0) {
       s_row[wave][s_rank[2 * lane]] = ex;
       s_row[wave][s_rank[2 * lane + 1]] = ex + w0;
     }
-    // A operands of a 16-token group: lane (g, r) holds token 16 kk + r (rows
-    // past the tile repeat its last token), channels 32 kb + 8 g .. +7
-    auto load_group = [&](int sub, int kk, uint4 (&a)[4]) {
-      const int tok = min(sub * 64 + kk * 16 + r, nt - 1);
-      const uint16_t* rowp = src + (pre ? (row0 + tok) * D : cache_row(p, l, h, p.mid_begin + t0 + ta + tok));
+    // A operands of a 32-token pair, two 16-row halves h: row 4 i + e of half
+    // h holds token 8 i + 4 h + e, so that result lane (g, r) holds tokens
+    // 8 g .. 8 g + 7 of one component, eight consecutive codes of one row.
+    // Lane (g, r) loads rows r of both halves, channels 32 kb + 8 g .. +7
+    // (rows past the tile repeat its last token).
+    auto load_pair = [&](int pr, uint4 (&a)[2][4]) {
+      const int ln = fresh_lane(), g = ln >> 4, r = ln & 15;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) a[kb] = *reinterpret_cast<const uint4*>(rowp + 32 * kb + 8 * g);
+      for (int hh = 0; hh < 2; ++hh) {
+        const int tok = min(pr * 32 + 8 * (r >> 2) + 4 * hh + (r & 3), nt - 1);
+        const uint16_t* rowp = src + (pre ? (row0 + tok) * D : cache_row(p, l, h, p.mid_begin + t0 + ta + tok));
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) a[hh][kb] = *reinterpret_cast<const uint4*>(rowp + 32 * kb + 8 * g);
+      }
     };
-    // four group buffers: group kk of a sub-tile lives in Ab[kk]; the loads of
-    // group kk + 2 are issued while group kk is projected
-    uint4 Ab[4][4];
-    load_group(0, 0, Ab[0]);
-    load_group(0, 1, Ab[1]);
-    // Exact re-computation of the queued codes, one per lane: the fp64 sum of
-    // the 128 exact bf16 products (four independent partial sums), rounded to
-    // fp32 once, then the code; a changed code is XOR-ed into the segment
-    // buffer over the provisional one.
+    // two pair buffers: pair P + 1 is in flight while pair P is projected
+    uint4 Ab[2][2][4];
+    load_pair(0, Ab[0]);
+    // Exact re-computation of the queued codes, 16 Z at a time: four lanes per
+    // code each take 32 channels of the token row (four 16-byte loads; the
+    // loads of all 16 Z codes, and of the packed words that hold their
+    // provisional values, are issued together) and the matching basis
+    // fragments, sum the exact bf16 products in fp64 and reduce across the
+    // four; the sum is rounded to fp32 once and quantised, and a changed code
+    // is XOR-ed into the packed tile over the provisional one.
     uint32_t* queue = s_queue[wave];
-    int qn = 0;
-    auto drain = [&](int sub) {
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    auto drain = [&](auto z_tag, int qn) {
+      constexpr int Z = decltype(z_tag)::value;
+      const int lane = fresh_lane();
+      // the packed words are stored before they are read back
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_wave_barrier();
-      for (int q0 = 0; q0 < qn; q0 += 64) {
-        if (q0 + lane < qn) {
-          const uint32_t ent = queue[q0 + lane];
-          const int t = (int)(ent >> 16), k = (int)((ent >> 8) & 0xffu);
-          const uint32_t old = ent & 0xffu;
-          const QInfo qk = s_q[k];
-          const int tt = sub * 64 + t;  // tile-relative token
-          const uint16_t* rowp = src + (pre ? (row0 + tt) * D : cache_row(p, l, h, p.mid_begin + t0 + ta + tt));
-          const int mk = k >> 4, rk = k & 15;
-          double part[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 1
-          for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll 1
-            for (int gq = 0; gq < 4; ++gq) {
-              // channels 32 kb + 8 gq .. +7: the token row and the component's basis fragment
-              const uint4 xv = *reinterpret_cast<const uint4*>(rowp + 32 * kb + 8 * gq);
-              const uint4 bv = sB[(mk * 4 + kb) * 64 + 16 * gq + rk];
-              const uint32_t aw[4] = {xv.x, xv.y, xv.z, xv.w}, bw[4] = {bv.x, bv.y, bv.z, bv.w};
+      const int j = lane & 3;
+      for (int q0 = 0; q0 < qn; q0 += 16 * Z) {
+        uint32_t ent[Z], wd[Z][2];
+        uint4 xv[Z][4];
 #pragma unroll
-              for (int z = 0; z < 4; ++z) {
-                part[z] += (double)__fmul_rn(__uint_as_float(aw[z] << 16), __uint_as_float(bw[z] << 16));
-                part[z] += (double)__fmul_rn(__uint_as_float(aw[z] & 0xffff0000u), __uint_as_float(bw[z] & 0xffff0000u));
-              }
+        for (int z = 0; z < Z; ++z) {
+          const int qe = q0 + 16 * z + (lane >> 2);
+          ent[z] = queue[qe < qn ? qe : q0];
+          const int t = (int)(ent[z] >> 16), k = (int)((ent[z] >> 8) & 0xffu);  // tile-relative token
+          const uint16_t* rowp = src + (pre ? (row0 + t) * D : cache_row(p, l, h, p.mid_begin + t0 + ta + t));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xv[z][q] = *reinterpret_cast<const uint4*>(rowp + 32 * j + 8 * q);
+          // the one or two packed words of the code (the second read only
+          // when the code crosses into it)
+          const uint32_t b = s_bs[k], bitpos = (uint32_t)t * b;
+          uint32_t* wp = tile + s_row[wave][k] + (bitpos >> 5);
+          wd[z][0] = __hip_atomic_load(wp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          wd[z][1] = __hip_atomic_load(wp + ((bitpos & 31) + b > 32 ? 1 : 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int z = 0; z < Z; ++z) {
+          const int k = (int)((ent[z] >> 8) & 0xffu);
+          double part[2] = {0.0, 0.0};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            // channels 32 j + 8 q .. +7 of the component's basis column
+            const uint4 bv = sB[((k >> 4) * 4 + j) * 64 + 16 * q + (k & 15)];
+            const uint32_t aw[4] = {xv[z][q].x, xv[z][q].y, xv[z][q].z, xv[z][q].w};
+            const uint32_t bw[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+              part[0] += (double)__fmul_rn(__uint_as_float(aw[y] << 16), __uint_as_float(bw[y] << 16));
+              part[1] += (double)__fmul_rn(__uint_as_float(aw[y] & 0xffff0000u), __uint_as_float(bw[y] & 0xffff0000u));
             }
           }
-          const double cex = (part[0] + part[1]) + (part[2] + part[3]);
-          const float v = __fmul_rn(__fsub_rn((float)cex, qk.zero), qk.rcp);
-          const uint32_t code = __float_as_uint(__fadd_rn(__builtin_amdgcn_fmed3f(v, 0.0f, (float)((1u << qk.b) - 1u)),
-                                                          0x1p23f)) & 0xffu;
-          const uint64_t dx = (uint64_t)(code ^ old) << ((t * qk.b) & 31);
-          const uint32_t wi = qk.seg + (((uint32_t)t * qk.b) >> 5);
-          if (dx) {
-            atomicXor(&segbuf[wi], (uint32_t)dx);
-            if (dx >> 32) atomicXor(&segbuf[wi + 1], (uint32_t)(dx >> 32));
+          double cex = part[0] + part[1];
+          cex += __shfl_xor(cex, 1, 64);
+          cex += __shfl_xor(cex, 2, 64);
+          if (j == 0 && q0 + 16 * z + (lane >> 2) < qn) {
+            const QInfo qk = s_q[k];
+            const int t = (int)(ent[z] >> 16);
+            const float v = __fmul_rn(__fsub_rn((float)cex, qk.zero), qk.rcp);
+            const uint32_t code = __float_as_uint(__fadd_rn(__builtin_amdgcn_fmed3f(v, 0.0f, (float)((1u << qk.b) - 1u)),
+                                                            0x1p23f)) & 0xffu;
+            const uint32_t bitpos = (uint32_t)t * qk.b, sh = bitpos & 31;
+            const uint64_t cur = (uint64_t)wd[z][0] | ((uint64_t)wd[z][1] << 32);
+            const uint32_t old = (uint32_t)(cur >> sh) & ((1u << qk.b) - 1u);
+            const uint64_t dx = (uint64_t)(code ^ old) << sh;
+            uint32_t* wp = tile + s_row[wave][k] + (bitpos >> 5);
+            if (dx) {
+              atomicXor(wp, (uint32_t)dx);
+              if (dx >> 32) atomicXor(wp + 1, (uint32_t)(dx >> 32));
+            }
           }
         }
       }
       refined += (uint32_t)qn;
-      qn = 0;
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
     };
-    // The 16 x 16 (token x component) steps of one 16-token group: project,
-    // quantise, queue the codes within their error bound of a rounding
-    // boundary, OR the provisional codes into segbuf.  FULL: the tile has
-    // every token (no tail masking).
-    auto group = [&](auto full_tag, const uint4 (&A)[4], const float (&tn)[4], int kk, int tb0, int sub) {
+    // The 32 x 16 (token x component) steps of one pair: project, quantise,
+    // OR the provisional codes into segbuf and shift into fl[h] one flag per
+    // code (step m, element e at bit 4 (NT - 1 - m) + 3 - e) for the codes
+    // within their error bound of a rounding boundary.  No LDS access here
+    // depends on the data, so every wait on LDS stays exact.  FULL: the tile
+    // has every token (no tail masking).
+    auto pair = [&](auto full_tag, const uint4 (&A)[2][4], float tnmax, int P, int tb0, uint32_t (&fl)[2]) {
       constexpr bool FULL = decltype(full_tag)::value;
+      const int lane = fresh_lane(), g = lane >> 4, r = lane & 15;
       for (int m = 0; m < NT; ++m) {
         uint4 Bm[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) Bm[kb] = sB[(m * 4 + kb) * 64 + lane];
-        const QInfo qi = s_q[16 * m + r];
-        const uint32_t b = qi.b;
-        const float qmax = (float)((1u << b) - 1u);
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        const float4 qf = s_hf[16 * m + r];  // rcp, -zero rcp, 2^b - 1, margin
+        const uint4 qu = s_hu[16 * m + r];   // b, kb, seg, pad
+        const uint32_t b = qu.x;
+        f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[kb]),
-                                                        __builtin_bit_cast(bf16x8_t, Bm[kb]), acc, 0, 0, 0);
-        uint32_t uq[4];
-        uint64_t near[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // components without codes (b = 0, rcp = 0, qmax = 0) give v = 0 and
-          // code 0, so only the token tail needs masking
-          const float v = __fmul_rn(__fsub_rn(acc[e], qi.zero), qi.rcp);
-          const float vc = (FULL || tb0 + e < nt) ? __builtin_amdgcn_fmed3f(v, 0.0f, qmax) : 0.0f;
-          const float sv = __fadd_rn(vc, 0x1p23f);  // rint(vc), nearest even, in the low bits
-          uq[e] = __float_as_uint(sv);
-          const float d = __fsub_rn(vc, __fsub_rn(sv, 0x1p23f));
-          near[e] = __ballot(fabsf(d) > __fmaf_rn(-__uint_as_float(qi.pad), tn[e], qi.thr));
-        }
-        if (near[0] | near[1] | near[2] | near[3]) {
-          // queue them: (sub-tile token, sorted component, provisional code)
+          for (int hh = 0; hh < 2; ++hh)
+            acc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[hh][kb]),
+                                                              __builtin_bit_cast(bf16x8_t, Bm[kb]), acc[hh], 0, 0, 0);
+        // bound on |v - v_exact| away from the rounding boundary
+        const float bnd = __fmaf_rn(-__uint_as_float(qu.w), tnmax, qf.w);
+        uint32_t pc[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          uint32_t uq[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            if (near[e]) {
-              const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(near[e] >> 32),
-                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)near[e], 0u));
-              if ((near[e] >> lane) & 1ull)
-                queue[qn + below] = ((uint32_t)((tb0 & 63) + e) << 16) | ((uint32_t)(16 * m + r) << 8) | (uq[e] & 0xffu);
-              qn += (int)__popcll(near[e]);
-            }
+            // components without codes (b = 0, rcp = 0, qmax = 0) give v = 0
+            // and code 0, so only the token tail needs masking
+            const float v = __fmaf_rn(acc[hh][e], qf.x, qf.y);
+            const bool in = FULL || tb0 + 4 * hh + e < nt;
+            const float vc = in ? __builtin_amdgcn_fmed3f(v, 0.0f, qf.z) : 0.0f;
+            const float sv = __fadd_rn(vc, 0x1p23f);  // rint(vc), nearest even, in the low bits
+            uq[e] = __float_as_uint(sv);
+            const float d = __fsub_rn(vc, __fsub_rn(sv, 0x1p23f));
+            const bool nr = in && fabsf(d) > bnd;
+            fl[hh] = fl[hh] + fl[hh] + (nr ? 1u : 0u);
           }
+          // four codes -> one 4b-bit piece (the exponent bits cancel in kb)
+          pc[hh] = uq[0] + (uq[1] << b) + (uq[2] << (2 * b)) + (uq[3] << (3 * b)) - qu.y;
         }
-        // four codes -> one 4b-bit piece (the exponent bits cancel in kb)
-        const uint32_t piece = uq[0] + (uq[1] << b) + (uq[2] << (2 * b)) + (uq[3] << (3 * b)) - qi.kb;
-        if (piece != 0u) {
-          const uint32_t bitoff = (uint32_t)(kk * 16 + 4 * g) * b;
-          const uint32_t wi = qi.seg + (bitoff >> 5), sh = bitoff & 31;
-          atomicOr(&segbuf[wi], piece << sh);
-          if (sh + 4 * b > 32) atomicOr(&segbuf[wi + 1], piece >> (32 - sh));
-        }
-        if (qn >= kQDrain) drain(sub);
+        // eight codes (8b bits) at bit (32 P + 8 g) b of the component's row
+        const uint64_t piece = (uint64_t)pc[0] | ((uint64_t)pc[1] << (4 * b));
+        const uint32_t bitoff = (uint32_t)(32 * P + 8 * g) * b, sh = bitoff & 31;
+        const uint32_t wi = qu.z + (bitoff >> 5);
+        const uint64_t w01 = piece << sh;
+        const uint32_t w2 = (uint32_t)(((piece >> 32) << sh) >> 32);
+        atomicOr(&segbuf[wi], (uint32_t)w01);
+        atomicOr(&segbuf[wi + 1], (uint32_t)(w01 >> 32));
+        atomicOr(&segbuf[wi + 2], w2);
       }
     };
     const bool full = nt == p.tile_tokens;
+    int qn = 0;  // queued codes
     for (int sub = 0; sub * 64 < nt; ++sub) {
-      for (uint32_t w = lane; w < segw + 4; w += 64) segbuf[w] = 0u;
+      for (uint32_t w = fresh_lane(); w < segw + 4; w += 64) segbuf[w] = 0u;
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        // group kk + 2 of this sub-tile or of the next (the loads of groups
-        // past the tile are clamped to its last token and never used)
-        load_group(sub + ((kk + 2) >> 2), (kk + 2) & 3, Ab[(kk + 2) & 3]);
-        const uint4 (&A)[4] = Ab[kk];
-        // norm bound of the token of output element (row 4 g + e of the group)
-        float tn[4];
+      for (int P = 0; P < 2; ++P) {
+        // the next pair (of this sub-tile or the next; loads past the tile
+        // are clamped to its last token and never used)
+        load_pair(2 * sub + P + 1, Ab[P ^ 1]);
+        const uint4 (&A)[2][4] = Ab[P];
+        // bound on the norms of the pair's 32 tokens: the sum over the four
+        // channel quarters of the largest partial norm of each, 1% high
+        float tnmax;
         {
-          float n2 = 0.f;
+          float n2[2] = {0.f, 0.f};
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            const uint32_t w4[4] = {A[kb].x, A[kb].y, A[kb].z, A[kb].w};
+          for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-            for (int z = 0; z < 4; ++z) {
-              const bf16x2_t h2 = __builtin_bit_cast(bf16x2_t, w4[z]);
-              n2 = __builtin_amdgcn_fdot2_f32_bf16(h2, h2, n2, false);
+            for (int kb = 0; kb < 4; ++kb) {
+              const uint32_t w4[4] = {A[hh][kb].x, A[hh][kb].y, A[hh][kb].z, A[hh][kb].w};
+#pragma unroll
+              for (int z = 0; z < 4; ++z) {
+                const bf16x2_t h2 = __builtin_bit_cast(bf16x2_t, w4[z]);
+                n2[hh] = __builtin_amdgcn_fdot2_f32_bf16(h2, h2, n2[hh], false);
+              }
             }
-          }
-          n2 += __shfl_xor(n2, 16, 64);
-          n2 += __shfl_xor(n2, 32, 64);
+          // non-negative floats order as their bit patterns
+          uint32_t mx = max(__float_as_uint(n2[0]), __float_as_uint(n2[1]));
 #pragma unroll
-          for (int e = 0; e < 4; ++e) tn[e] = 1.01f * __fsqrt_rn(__shfl(n2, 4 * g + e, 64));
+          for (int o = 1; o < 16; o <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+          const float s01 = __uint_as_float(__builtin_amdgcn_readlane(mx, 0)) +
+                            __uint_as_float(__builtin_amdgcn_readlane(mx, 16));
+          const float s23 = __uint_as_float(__builtin_amdgcn_readlane(mx, 32)) +
+                            __uint_as_float(__builtin_amdgcn_readlane(mx, 48));
+          tnmax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(1.01f * __fsqrt_rn(s01 + s23))));
         }
-        const int tb0 = sub * 64 + kk * 16 + 4 * g;  // tile-relative token of element 0
-        if (full) group(std::true_type{}, A, tn, kk, tb0, sub);
-        else group(std::false_type{}, A, tn, kk, tb0, sub);
+        const int tb0 = sub * 64 + 32 * P + 8 * g;  // tile-relative token of element (0, 0)
+        uint32_t fl[2] = {0u, 0u};
+        if (full) pair(std::true_type{}, A, tnmax, P, tb0, fl);
+        else pair(std::false_type{}, A, tnmax, P, tb0, fl);
+        const int ln = fresh_lane();
+        s_flags[wave][2 * P][ln] = fl[0];
+        s_flags[wave][2 * P + 1][ln] = fl[1];
       }
-      if (qn > 0) drain(sub);
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
       // segment buffer -> the rows of the packed tile
-      for (uint32_t w = lane; w < segw; w += 64) {
+      for (uint32_t w = fresh_lane(); w < segw; w += 64) {
         const uint32_t k = s_wmap[w];
         const QInfo& qk = s_q[k];
         const uint32_t idx = w - qk.seg;
         const int32_t rw = (int32_t)((nt * (int)qk.b + 31) >> 5) - (int32_t)(2 * qk.b * sub);
         if ((int32_t)idx < rw) tile[s_row[wave][k] + 2 * qk.b * sub + idx] = segbuf[w];
       }
+      // queue every flagged code of the sub-tile (all lanes at once, at the
+      // offsets of a wave-wide scan of their counts); a full queue is worked
+      // off first
+      const int lane = fresh_lane(), g = lane >> 4, r = lane & 15;
+      uint32_t fl[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) fl[q] = s_flags[wave][q][lane];
+      for (;;) {
+        const uint32_t cnt = __popc(fl[0]) + __popc(fl[1]) + __popc(fl[2]) + __popc(fl[3]);
+        uint32_t incl = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = (uint32_t)__shfl_up((int)incl, o, 64);
+          if (lane >= o) incl += y;
+        }
+        const int total = (int)__builtin_amdgcn_readlane(incl, 63);
+        if (total == 0) break;
+        if (qn > 0 && qn + total > kQCap) {
+          drain(std::integral_constant<int, 1>{}, qn);  // the next pair's loads hold registers
+          qn = 0;
+        }
+        const int room = kQCap - qn;
+        int idx = (int)(incl - cnt);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          while (fl[q] != 0u && idx < room) {
+            const uint32_t bit = (uint32_t)__builtin_ctz(fl[q]);
+            fl[q] &= fl[q] - 1u;
+            const uint32_t m = (uint32_t)(NT - 1) - (bit >> 2), e = 3u - (bit & 3u);
+            const uint32_t t = (uint32_t)(sub * 64 + 32 * (q >> 1) + 8 * g + 4 * (q & 1)) + e;
+            queue[qn + idx] = (t << 16) | ((16u * m + (uint32_t)r) << 8);
+            ++idx;
+          }
+        }
+        if (total <= room) {
+          qn += total;
+          break;
+        }
+        drain(std::integral_constant<int, 1>{}, kQCap);
+        qn = 0;
+      }
       __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
       __builtin_amdgcn_wave_barrier();
     }
+    if (qn > 0) drain(std::integral_constant<int, 2>{}, qn);
   }
-  if (lane == 0 && refined) atomicAdd(reinterpret_cast<uint32_t*>(p.ws + p.w.status) + 1, refined);
+  // one count per workgroup, into the workgroup's slot
+  __shared__ uint32_t s_refined;
+  if (tid == 0) s_refined = 0u;
+  __syncthreads();
+  if (lane == 0 && refined) atomicAdd(&s_refined, refined);
+  __syncthreads();
+  if (tid == 0 && s_refined) atomicAdd(count_slot(p.ws, p.w), s_refined);
 }
 
 hipError_t launch_quant128(const Params& p, hipStream_t s) {

@@ -569,9 +569,12 @@ kvtc_status kvtc_result(kvtc_plan_t plan, const void* ws, uint64_t* container_by
 
 kvtc_status kvtc_encode_counters(kvtc_plan_t plan, const void* ws, uint64_t* exact_recomputed) {
   if (!plan || !ws || !exact_recomputed) return KVTC_ERR_INVALID_ARG;
-  uint32_t buf[2];
-  if (hipMemcpy(buf, ws, 8, hipMemcpyDeviceToHost) != hipSuccess) return KVTC_ERR_HIP;
-  *exact_recomputed = buf[1];
+  static_assert(kStatusBlockBytes % 4 == 0, "status block in words");
+  uint32_t buf[kStatusBlockBytes / 4];
+  if (hipMemcpy(buf, ws, sizeof(buf), hipMemcpyDeviceToHost) != hipSuccess) return KVTC_ERR_HIP;
+  uint64_t n = buf[1];
+  for (int i = 0; i < kCountSlots; ++i) n += buf[(kCountOff + kCountStride * i) / 4];
+  *exact_recomputed = n;
   return KVTC_OK;
 }
 

@@ -107,6 +107,16 @@ KVTC_HD inline int64_t max_words(int64_t P, const kvtc_config& c) {
   return (P * (c.rans_scale_bits + 1)) / 16 + 2 * (int64_t)c.rans_lanes + 2;
 }
 
+// Status block at the start of every workspace: the status word (error
+// bits), the exact re-computation count and the container size in its first
+// 16 bytes, then kCountSlots counters on lines of their own that workgroups
+// add their re-computation counts to (spread so that the adds do not queue
+// on one line); the count is word 1 plus the slots.
+constexpr int kCountSlots = 64;
+constexpr int64_t kCountOff = 256;
+constexpr int64_t kCountStride = 128;
+constexpr int64_t kStatusBlockBytes = kCountOff + kCountSlots * kCountStride;
+
 // `paged`: the workspace of one sequence of a paged batch, which also stages
 // the fixed part of its container (everything before chunks_off).
 KVTC_HD inline WsLayout make_ws_layout(const kvtc_config& c, const Layout& lo, bool paged = false) {
@@ -119,7 +129,7 @@ KVTC_HD inline WsLayout make_ws_layout(const kvtc_config& c, const Layout& lo, b
     return o;
   };
   int64_t at = 0;
-  w.status = take(at, 16);
+  w.status = take(at, kStatusBlockBytes);
   w.part_sum = take(at, nsc * D * 8);
   w.part_sq = take(at, nsc * D * 8);
   w.part_min = take(at, nsc * D * 4);
@@ -323,6 +333,12 @@ __device__ inline void set_status(uint8_t* ws, const WsLayout& w, uint32_t code)
 
 __device__ inline uint32_t get_status(const uint8_t* ws, const WsLayout& w) {
   return __atomic_load_n(reinterpret_cast<const uint32_t*>(ws + w.status), __ATOMIC_RELAXED);
+}
+
+// The counter slot of a workgroup (x, y).
+__device__ inline uint32_t* count_slot(uint8_t* ws, const WsLayout& w) {
+  const uint32_t i = (blockIdx.x + blockIdx.y * gridDim.x) % kCountSlots;
+  return reinterpret_cast<uint32_t*>(ws + w.status + kCountOff + kCountStride * i);
 }
 
 }  // namespace kvtc
