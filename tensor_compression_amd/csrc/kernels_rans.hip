@@ -192,6 +192,9 @@ __device__ __forceinline__ int64_t rans_encode_stream(const uint8_t* sbase, int3
   uint32_t ring[PF];
 #pragma unroll
   for (int d = 0; d < PF; ++d) ring[d] = fetch(kt - 1 - d);
+  // the table entry of the next step is read a step ahead (ring slot d + 1
+  // holds the next step's symbol, slot 0 the next block's after its refill)
+  EncSym en = tab[ring[0]];
   for (int k0 = kt - 1; k0 >= 0; k0 -= PF) {
 #pragma unroll
     for (int d = 0; d < PF; ++d) {
@@ -199,9 +202,10 @@ __device__ __forceinline__ int64_t rans_encode_stream(const uint8_t* sbase, int3
       {
         const int32_t i = k * lanes + j;
         const bool active = valid && i < Nt;
-        const EncSym e = tab[ring[d]];
+        const EncSym e = en;
         // refill after the last use so the load can reuse the same register
         ring[d] = fetch(k - PF);
+        en = tab[ring[(d + 1) % PF]];
         // renormalise while x >= f 2^(32 - sb): one 16-bit word at most
         const bool emit = active && (x >> (32 - sb)) >= e.f;
         const uint64_t bl = __ballot(emit);
@@ -390,14 +394,36 @@ __global__ void k_rans_enc_chunks(const Params p0) {
   for (int i = threadIdx.x; i < 256 * 8; i += blockDim.x) hist8[i] = 0;
   __syncthreads();
   {
+    // 16-byte loads, eight in flight per thread before their bytes are
+    // counted (the slot is 16-byte aligned; a tail of 4-byte words follows)
     const uint32_t cpy = lane & 7;
-    for (int64_t i = threadIdx.x; i < P / 4; i += blockDim.x) {
-      const uint32_t wv = reinterpret_cast<const uint32_t*>(packed)[i];
+    auto count = [&](uint32_t wv) {
       atomicAdd(&hist8[8 * (wv & 0xff) + cpy], 1u);
       atomicAdd(&hist8[8 * ((wv >> 8) & 0xff) + cpy], 1u);
       atomicAdd(&hist8[8 * ((wv >> 16) & 0xff) + cpy], 1u);
       atomicAdd(&hist8[8 * (wv >> 24) + cpy], 1u);
+    };
+    const int64_t n16 = P / 16;
+    const uint4* p16 = reinterpret_cast<const uint4*>(packed);
+    for (int64_t i0 = 0; i0 < n16; i0 += 8 * (int64_t)blockDim.x) {
+      uint4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t i = i0 + k * (int64_t)blockDim.x + threadIdx.x;
+        v[k] = i < n16 ? p16[i] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (i0 + k * (int64_t)blockDim.x + threadIdx.x < n16) {
+          count(v[k].x);
+          count(v[k].y);
+          count(v[k].z);
+          count(v[k].w);
+        }
+      }
     }
+    for (int64_t i = 4 * n16 + threadIdx.x; i < P / 4; i += blockDim.x)
+      count(reinterpret_cast<const uint32_t*>(packed)[i]);
   }
   __syncthreads();
   for (int b = threadIdx.x; b < 256; b += blockDim.x) {
