@@ -360,20 +360,24 @@ __global__ __launch_bounds__(256) void k_dec_wht(const Params p) {
 }
 
 // ---- head_dim 128, bf16 cache: the bandwidth-oriented decode pass -------------
-// One wave per chunk (four chunks of a section per workgroup), 64-token
-// sub-tiles.  The workgroup prologue reads the section's side information,
-// orders the components with codes (b > 0) by bit width -- the contraction
-// runs over this order, so every dequantisation step is wave-uniform in b --
-// and folds the b = 0 components, whose value is their zero point, into a
-// per-channel constant that seeds the accumulators.
+// A workgroup (four waves) per chunk; the chunk's packed tiles are staged in
+// LDS one at a time and decoded in 64-token sub-tiles, all four waves on the
+// same sub-tile.  The workgroup prologue reads the section's side
+// information, orders the components with codes (b > 0) by bit width (the
+// contraction runs over this order) and folds the b = 0 components, whose
+// value is their zero point, into a per-channel constant that seeds the
+// accumulators.
 //
-// Dequantisation: lane = token, one component at a time, with the extraction
-// specialised per width; eight components pack into a bf16 K slice and a 4x4
-// exchange of lane groups (permlane swaps) turns "lane group = 16 tokens" into
-// the MFMA operand layout "lane group = 8 components".  MFMA: D^T = B^T C^T
-// with the basis rows (permuted component order) in registers, so the result
-// lane holds eight consecutive channels of one token -- both members of each
-// RoPE pair sit in the same lane -- and leaves with 16-byte stores.
+// Dequantisation (all 256 threads): lane = token, one component octet per
+// wave at a time, so the width and constants of each component are
+// wave-uniform; the eight bf16 values of the octet go to LDS as one 16-byte
+// MFMA operand, laid out [K slice][16-token group][lane group][token].
+//
+// MFMA: D^T = B^T C^T with the basis rows (permuted channel order) in
+// registers.  Wave w takes the channel half hf = w & 1 (channel runs hf and
+// hf + 2 of 32, so both members of every RoPE pair) and the 16-token groups
+// 2 (w >> 1), +1 of the sub-tile; the result lane holds eight consecutive
+// channels of one token per run and leaves with 16-byte stores.
 
 constexpr int kBS = 136;  // LDS row stride (bf16) of the staged basis
 
@@ -386,26 +390,6 @@ __device__ __forceinline__ uint32_t lds_u32(const uint32_t* base, uint32_t byte_
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(base) + byte_off);
 }
 
-// 4x4 exchange of (lane group g, register block c): afterwards block c of lane
-// group g holds what block g of lane group c held.
-__device__ __forceinline__ void xpose4(uint32_t (&v)[4][4]) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      auto r = __builtin_amdgcn_permlane32_swap(v[c][e], v[c + 2][e], false, false);
-      v[c][e] = r[0];
-      v[c + 2][e] = r[1];
-    }
-#pragma unroll
-    for (int c = 0; c < 4; c += 2) {
-      auto r = __builtin_amdgcn_permlane16_swap(v[c][e], v[c + 1][e], false, false);
-      v[c][e] = r[0];
-      v[c + 1][e] = r[1];
-    }
-  }
-}
-
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -415,49 +399,49 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
-// Per-wave part: chunk `ch` of section u with KB K slices of 32 sorted
-// components (entries past the coded components are zero).
-// PG: the output is a paged pool (bf16); rows are addressed through the page
-// table and lanes past the section store to a scratch row of the workspace.
-template <int KB, int KBS, int OB, bool PG>
-__device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, const uint4* sA,
-                                             uint32_t* tb, uint4* kw, const DecKInfo* s_ki,
-                                             const uint8_t* s_rank, const uint32_t* s_b,
-                                             const float* s_const, uint32_t fw, int nnz, float4* brow) {
+// Words of the LDS tile buffer: the packed tile and four zero words past it.
+__host__ __device__ inline int dec_tile_words(const Params& p) {
+  const int32_t bmax = p.budget_k > p.budget_v ? p.budget_k : p.budget_v;
+  return (int)(((int64_t)p.tile_tokens * bmax + 31) / 32) + 4;
+}
+
+// The section's coded components by width: KB K slices of 32 (entries past
+// the coded components are zero).  KBMAX = 3 serves sections with at most 96
+// coded components, KBMAX = 4 the rest; each instantiation leaves the other's
+// sections alone.  PG: the output is a paged pool (bf16) addressed through
+// the page table; lanes past the section store to a scratch row of the
+// workspace.  OB: output bytes per element.
+template <int KB, int KBMAX, int OB, bool PG>
+__device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, const uint4 (&A)[4][KBMAX],
+                                             uint4* cq, uint32_t* tb, uint4* s_kw, const DecKInfo* s_ki,
+                                             const uint8_t* s_rank, const uint32_t* s_b, const float* s_const,
+                                             uint32_t fw, uint4* stage) {
   constexpr int D = 128;
-  const int lane = threadIdx.x & 63, g = lane >> 4, r = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = wave & 1, th = wave >> 1;
   const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
   const int t0 = ch * p.chunk_tokens;
   const int n = min(p.chunk_tokens, p.T_mid - t0);
-  if (n <= 0) return;
   const bool rope = (s == 0) && p.rope_keys;
   const bool half_style = p.rope_style == KVTC_ROPE_HALF;
   const int64_t lh_row0 = ((int64_t)l * p.H + h) * p.T;
   // the (layer, head) slab of the output as a buffer resource: stores of
-  // lanes past the section get an offset at the slab end and are dropped by
+  // tokens past the section get an offset at the slab end and are dropped by
   // the range check, so every store instruction is issued unconditionally
   uint8_t* obase = reinterpret_cast<uint8_t*>(s ? p.v_out : p.k_out);
   uint8_t* slab = obase + (PG ? 0 : lh_row0 * D * OB);
   const int32_t slab_bytes = PG ? 0 : p.T * D * OB;
-  uint8_t* const dummy = p.ws + p.w.fixed;  // PG: scratch row for lanes past the section
+  uint8_t* const dummy = p.ws + p.w.fixed;  // PG: scratch row for tokens past the section
   const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(slab, 0, slab_bytes, 0x00020000);
+  // the RoPE table as a buffer resource (one offset register per load)
+  const __amdgpu_buffer_rsrc_t rrsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float2*>(p.rope), 0, rope ? p.T * 512 : 0, 0x00020000);
   const uint32_t* slot = reinterpret_cast<const uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot);
-
-  // RoPE table rows (cos/sin of the first token of each 16-token group) of
-  // the next sub-tile, loaded a sub-tile ahead: lane l fetches 32 bytes of
-  // row l / 16 (sub-tiles are contiguous in tokens, tiles hold whole
-  // sub-tiles)
-  float4 nrow[2];
-  auto fetch_rows = [&](int tok0) {
-    const int row = min(p.mid_begin + t0 + tok0 + 16 * (lane >> 4), p.T - 1);
-    const float4* src = reinterpret_cast<const float4*>(p.rope + (int64_t)row * 64) + 2 * (lane & 15);
-    nrow[0] = src[0];
-    nrow[1] = src[1];
-  };
-  fetch_rows(0);
 
   for (int ta = 0; ta < n; ta += p.tile_tokens) {
     const int nt = min(p.tile_tokens, n - ta);
+    lds_barrier();  // the previous tile's buffer and operands are consumed
     // row offsets of this tile (natural order, scanned), stored by sorted
     // position together with the width and the dequantisation constants;
     // components without codes keep all-zero entries
@@ -472,208 +456,211 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
         if (lane >= o) x += y;
       }
       tw = __shfl(x, 63, 64);
-      const uint32_t ex = x - (w0 + w1);
-      const uint32_t r0 = s_rank[2 * lane], r1 = s_rank[2 * lane + 1];
-      const DecKInfo i0 = s_ki[r0], i1 = s_ki[r1];
-      kw[r0] = b0 ? make_uint4(b0, 4u * ex, __float_as_uint(i0.scale), __float_as_uint(i0.zero)) : make_uint4(0, 0, 0, 0);
-      kw[r1] = b1 ? make_uint4(b1, 4u * (ex + w0), __float_as_uint(i1.scale), __float_as_uint(i1.zero)) : make_uint4(0, 0, 0, 0);
+      if (wave == 0) {
+        const uint32_t ex = x - (w0 + w1);
+        const uint32_t r0 = s_rank[2 * lane], r1 = s_rank[2 * lane + 1];
+        const DecKInfo i0 = s_ki[r0], i1 = s_ki[r1];
+        s_kw[r0] = b0 ? make_uint4(b0, 4u * ex, __float_as_uint(i0.scale), __float_as_uint(i0.zero)) : make_uint4(0, 0, 0, 0);
+        s_kw[r1] = b1 ? make_uint4(b1, 4u * (ex + w0), __float_as_uint(i1.scale), __float_as_uint(i1.zero)) : make_uint4(0, 0, 0, 0);
+      }
     }
-    // stage the packed tile (tile stride fw words in the slot)
+    // stage the packed tile (tile stride fw words in the slot; tw is a
+    // multiple of 4 when the tile is full, whose slots are 16-byte aligned)
     {
       const uint32_t* src = slot + (int64_t)(ta / p.tile_tokens) * fw;
-      if ((fw & 3u) == 0) {
-        const uint32_t n4 = tw >> 2;
-        for (uint32_t i = lane; i < n4; i += 64)
-          reinterpret_cast<uint4*>(tb)[i] = reinterpret_cast<const uint4*>(src)[i];
-        for (uint32_t i = 4 * n4 + lane; i < tw; i += 64) tb[i] = src[i];
-      } else {
-        for (uint32_t i = lane; i < tw; i += 64) tb[i] = src[i];
-      }
-      if (lane < 4) tb[tw + lane] = 0u;
+      const bool al = ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
+      const uint32_t n4 = al ? tw >> 2 : 0u;
+      for (uint32_t i = tid; i < n4; i += 256) reinterpret_cast<uint4*>(tb)[i] = reinterpret_cast<const uint4*>(src)[i];
+      for (uint32_t i = 4 * n4 + tid; i < tw; i += 256) tb[i] = src[i];
+      if (tid < 4) tb[tw + tid] = 0u;
     }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+    lds_barrier();
 
     for (int sub = 0; sub * 64 < nt; ++sub) {
-      // PG: page of token `lane` of the sub-tile (clamped into the sequence)
-      int32_t pg = 0;
-      if constexpr (PG) pg = p.page_row[min(p.mid_begin + t0 + ta + sub * 64 + lane, p.T - 1) >> 4];
-      brow[2 * lane] = nrow[0];
-      brow[2 * lane + 1] = nrow[1];
-      fetch_rows(ta + sub * 64 + 64);
-      // cos/sin of this lane's RoPE pairs, by angle addition: token
-      // base + r with base = the first token of the 16-token group, so
-      // cs(base + r) = cs(base) (x) cs(r).  The base row is one table row per
-      // load (shared by the 16 tokens), cs(r) comes from table rows 0..15.
-      // Rows past the section are clamped (their results are not stored).
-      // float4 (two pairs) x of this lane's pairs in half hf of a table row:
-      // half-split style pairs 32 hf + 8 g + 2 x, +1; interleaved style pairs
-      // 16 (hf + 2 (x >> 1)) + 4 g + 2 (x & 1), +1
-      auto pair_at = [&](int hf, int x) {
-        return half_style ? (32 * hf + 8 * g) / 2 + x : 8 * (hf + 2 * (x >> 1)) + 2 * g + (x & 1);
-      };
-      auto load_pairs = [&](int row, int hf, float4 (&c)[4]) {
-        const float4* rr = reinterpret_cast<const float4*>(p.rope + (int64_t)row * 64);
+      // RoPE table entries of this wave's two 16-token groups, in flight
+      // during the dequantisation (a row is 64 pairs of cos, sin: 512 bytes;
+      // half style: pairs 32 hf + 8 g + 2 x, +1; interleaved: pairs
+      // 16 pp + 4 g + 2 (x & 1), +1 with pp = hf + 2 (x >> 1))
+      float4 cs[2][4];
+      if (rope) {
 #pragma unroll
-        for (int x = 0; x < 4; ++x) c[x] = rr[pair_at(hf, x)];
-      };
-      // ---- dequantise: lane = token sub*64 + lane of the tile.  Branch-free
-      // per component (entries past the coded components are all zero and
-      // yield 0), so the table reads can be issued ahead of their use.
-      uint32_t cur[KB > 0 ? KB : 1][4][4];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (32 * kb + 8 * c >= nnz) {  // eight components without codes
-#pragma unroll
-            for (int q2 = 0; q2 < 4; ++q2) cur[kb][c][q2] = 0u;
-            continue;
-          }
-#pragma unroll
-          for (int q2 = 0; q2 < 4; ++q2) {
-            float v[2];
-#pragma unroll
-            for (int z = 0; z < 2; ++z) {
-              const uint4 ki = kw[32 * kb + 8 * c + 2 * q2 + z];
-              const uint32_t b = __builtin_amdgcn_readfirstlane(ki.x);
-              const uint32_t seg = __builtin_amdgcn_readfirstlane(ki.y) + 8u * b * (uint32_t)sub;
-              const uint32_t bp = __umul24((uint32_t)lane, b);
-              const uint32_t off = seg + ((bp >> 5) << 2);
-              const uint32_t lo = lds_u32(tb, off), hi = lds_u32(tb, off + 4);
-              const uint32_t q = __builtin_amdgcn_alignbit(hi, lo, bp) & ((1u << b) - 1u);
-              v[z] = __fmaf_rn((float)q, __uint_as_float(ki.z), __uint_as_float(ki.w));
-            }
-            cur[kb][c][q2] = pk_bf16(v[0], v[1]);
-          }
-        }
-        xpose4(cur[kb]);
-      }
-      // ---- MFMA, RoPE, store: two channel halves, four 16-token groups each
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        uint4 A[4][KB > 0 ? KB : 1];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) A[mi][kb] = sA[((hf * 4 + mi) * KBS + kb) * 64 + lane];
-        float4 rot[4];  // cs(r) of this lane's pairs of the half
-        load_pairs(min(r, p.T - 1), hf, rot);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          // keep each step's table reads and temporaries inside the step
-          __builtin_amdgcn_sched_barrier(0);
-          float4 base[4];  // cs of the group's first token
-#pragma unroll
-          for (int x = 0; x < 4; ++x) base[x] = brow[kk * 32 + pair_at(hf, x)];
-          float4 c4p[4];
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const int pos = p.mid_begin + t0 + ta + sub * 64 + (2 * th + k2) * 16 + r;
+          const int32_t crow = min(pos, p.T - 1) * 512;
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
-            const float4 bq = base[x], rq = rot[x];
-            c4p[x] = make_float4(__fmaf_rn(bq.x, rq.x, -__fmul_rn(bq.y, rq.y)), __fmaf_rn(bq.y, rq.x, __fmul_rn(bq.x, rq.y)),
-                                 __fmaf_rn(bq.z, rq.z, -__fmul_rn(bq.w, rq.w)), __fmaf_rn(bq.w, rq.z, __fmul_rn(bq.z, rq.w)));
+            const int pr = half_style ? 32 * hf + 8 * g + 2 * x : 16 * (hf + 2 * (x >> 1)) + 4 * g + 2 * (x & 1);
+            cs[k2][x] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rrsrc, crow + 8 * pr, 0, 0));
           }
-          const int tok = sub * 64 + kk * 16 + r;  // tile-relative
-          const bool valid = tok < nt;
-          const int pos = p.mid_begin + t0 + ta + tok;
-          f32x4_t acc[4];
+        }
+      }
+      // ---- dequantise: lane = token sub*64 + lane of the tile, octets w, w+4, ...
+      // Branch-free per component (entries past the coded components are
+      // all zero and yield 0), so the table reads can be issued ahead.
+#pragma unroll 1
+      for (int j8 = 0; j8 < KB; ++j8) {
+        const int c8 = 4 * j8 + wave;
+        // the octet's widths, row offsets and constants (wave-uniform), then
+        // all eight code-word pairs in flight before any is used
+        uint32_t bw[8], bp[8], lo[8], hi[8];
+        float sc[8], zr[8];
 #pragma unroll
-          for (int mi = 0; mi < 4; ++mi) {
-            const int pp = hf + 2 * (mi >> 1), a = mi & 1;
-            const float4 c4 = *reinterpret_cast<const float4*>(&s_const[32 * pp + 8 * g + 4 * a]);
-            acc[mi] = f32x4_t{c4.x, c4.y, c4.z, c4.w};
+        for (int z = 0; z < 8; ++z) {
+          const uint4 ki = s_kw[8 * c8 + z];
+          bw[z] = __builtin_amdgcn_readfirstlane(ki.x);
+          const uint32_t seg = __builtin_amdgcn_readfirstlane(ki.y) + 8u * bw[z] * (uint32_t)sub;
+          sc[z] = __uint_as_float(ki.z);
+          zr[z] = __uint_as_float(ki.w);
+          bp[z] = __umul24((uint32_t)lane, bw[z]);
+          const uint32_t off = seg + ((bp[z] >> 5) << 2);
+          lo[z] = lds_u32(tb, off);
+          hi[z] = lds_u32(tb, off + 4);
+        }
+        uint32_t w4[4];
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          float v[2];
+#pragma unroll
+          for (int z2 = 0; z2 < 2; ++z2) {
+            const int z = 2 * q2 + z2;
+            const uint32_t q = __builtin_amdgcn_alignbit(hi[z], lo[z], bp[z]) & ((1u << bw[z]) - 1u);
+            v[z2] = __fmaf_rn((float)q, sc[z], zr[z]);
           }
+          w4[q2] = pk_bf16(v[0], v[1]);
+        }
+        // operand slot [kb = c8 / 4][kk = lane / 16][g = c8 % 4][r = lane % 16]
+        cq[((c8 >> 2) * 4 + (lane >> 4)) * 64 + (c8 & 3) * 16 + (lane & 15)] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      }
+      lds_barrier();
+      // ---- MFMA, RoPE, store: this wave's two 16-token groups
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, make_uint4(cur[kb][kk][0], cur[kb][kk][1], cur[kb][kk][2], cur[kb][kk][3]));
+      for (int k2 = 0; k2 < 2; ++k2) {
+        // one group at a time (bounds the registers in flight)
+        __builtin_amdgcn_sched_barrier(0);
+        const int kk = 2 * th + k2;
+        const int tok = sub * 64 + kk * 16 + r;  // tile-relative
+        const bool valid = tok < nt;
+        const int pos = p.mid_begin + t0 + ta + tok;
+        // RoPE table entries of this lane's eight pairs (token clamped into the cache)
+        // accumulator seeds: channel 32 pp + 8 g + 4 a + e of tile mi = (pp, a)
+        f32x4_t acc[4];
 #pragma unroll
-            for (int mi = 0; mi < 4; ++mi)
-              acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[mi][kb]), bop, acc[mi], 0, 0, 0);
-          }
-          if (rope) {
-            if (half_style) {
-              // pair j = 32 hf + 8 g + 4 a + e: x_a = acc[a][e], x_b = acc[2 + a][e]
+        for (int mi = 0; mi < 4; ++mi) {
+          const int pp = hf + 2 * (mi >> 1), a = mi & 1;
+          const float4 c4 = *reinterpret_cast<const float4*>(&s_const[32 * pp + 8 * g + 4 * a]);
+          acc[mi] = f32x4_t{c4.x, c4.y, c4.z, c4.w};
+        }
 #pragma unroll
-              for (int a = 0; a < 2; ++a) {
-                const float4 c01 = c4p[2 * a], c23 = c4p[2 * a + 1];
-                const float cc[4] = {c01.x, c01.z, c23.x, c23.z}, ss[4] = {c01.y, c01.w, c23.y, c23.w};
+        for (int kb = 0; kb < KB; ++kb) {
+          const uint4 bq = cq[(kb * 4 + kk) * 64 + lane];
+          const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, bq);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                  const float xa = acc[a][e], xb = acc[2 + a][e];
-                  acc[a][e] = __fmaf_rn(xa, cc[e], -__fmul_rn(xb, ss[e]));
-                  acc[2 + a][e] = __fmaf_rn(xa, ss[e], __fmul_rn(xb, cc[e]));
-                }
+          for (int mi = 0; mi < 4; ++mi)
+            acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, A[mi][kb]), bop, acc[mi], 0, 0, 0);
+        }
+        if (rope) {
+          if (half_style) {
+            // pair j = 32 hf + 8 g + 4 a + e: x_a = acc[a][e], x_b = acc[2 + a][e]
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+              const float4 c01 = cs[k2][2 * a], c23 = cs[k2][2 * a + 1];
+              const float cc[4] = {c01.x, c01.z, c23.x, c23.z}, ss[4] = {c01.y, c01.w, c23.y, c23.w};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float xa = acc[a][e], xb = acc[2 + a][e];
+                acc[a][e] = __fmaf_rn(xa, cc[e], -__fmul_rn(xb, ss[e]));
+                acc[2 + a][e] = __fmaf_rn(xa, ss[e], __fmul_rn(xb, cc[e]));
               }
-            } else {
-              // pairs (e, e + 1) of tile (p, a): index 16 p + 4 g + 2 a + e / 2
-#pragma unroll
-              for (int mi = 0; mi < 4; ++mi) {
-                const float4 c4 = c4p[mi];
-                const float cc[2] = {c4.x, c4.z}, ss[2] = {c4.y, c4.w};
-#pragma unroll
-                for (int e2 = 0; e2 < 2; ++e2) {
-                  const float xa = acc[mi][2 * e2], xb = acc[mi][2 * e2 + 1];
-                  acc[mi][2 * e2] = __fmaf_rn(xa, cc[e2], -__fmul_rn(xb, ss[e2]));
-                  acc[mi][2 * e2 + 1] = __fmaf_rn(xa, ss[e2], __fmul_rn(xb, cc[e2]));
-                }
-              }
-            }
-          }
-          if constexpr (PG) {
-            const int64_t page = __shfl(pg, kk * 16 + r, 64);
-            uint8_t* rowp = valid ? obase + ((((page + (int64_t)l * p.pool_pages) * p.H + h) << 4) + (pos & 15)) * D * 2
-                                  : dummy;
-#pragma unroll
-            for (int pq = 0; pq < 2; ++pq) {
-              const int pp = hf + 2 * pq;
-              const f32x4_t x0 = acc[2 * pq], x1 = acc[2 * pq + 1];
-              const int c0 = 32 * pp + 8 * g;
-              *reinterpret_cast<u32x4_t*>(rowp + 2 * c0) =
-                  u32x4_t{pk_bf16(x0[0], x0[1]), pk_bf16(x0[2], x0[3]), pk_bf16(x1[0], x1[1]), pk_bf16(x1[2], x1[3])};
             }
           } else {
-            const int32_t vo = valid ? (int32_t)(((int64_t)pos * D) * OB) : slab_bytes;
+            // pairs (e, e + 1) of tile (pp, a): index 16 pp + 4 g + 2 a + e / 2
 #pragma unroll
-            for (int pq = 0; pq < 2; ++pq) {
-              const int pp = hf + 2 * pq;
-              const f32x4_t x0 = acc[2 * pq], x1 = acc[2 * pq + 1];
-              const int c0 = 32 * pp + 8 * g;
-              if constexpr (OB == 2) {
-                const u32x4_t o = {pk_bf16(x0[0], x0[1]), pk_bf16(x0[2], x0[3]), pk_bf16(x1[0], x1[1]), pk_bf16(x1[2], x1[3])};
-                __builtin_amdgcn_raw_buffer_store_b128(o, orsrc, vo + 2 * c0, 0, 0);
-              } else {
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x0), orsrc, vo + 4 * c0, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x1), orsrc, vo + 4 * c0 + 16, 0, 0);
+            for (int mi = 0; mi < 4; ++mi) {
+              const float4 c4 = cs[k2][mi];
+              const float cc[2] = {c4.x, c4.z}, ss[2] = {c4.y, c4.w};
+#pragma unroll
+              for (int e2 = 0; e2 < 2; ++e2) {
+                const float xa = acc[mi][2 * e2], xb = acc[mi][2 * e2 + 1];
+                acc[mi][2 * e2] = __fmaf_rn(xa, cc[e2], -__fmul_rn(xb, ss[e2]));
+                acc[mi][2 * e2 + 1] = __fmaf_rn(xa, ss[e2], __fmul_rn(xb, cc[e2]));
               }
             }
           }
         }
+        if constexpr (OB == 2) {
+          // bf16 rows go through LDS (row = 16 units of 16 bytes, stride 17
+          // units against bank conflicts): this
+          // wave's two 64-byte runs per token now, whole rows below
+#pragma unroll
+          for (int pq = 0; pq < 2; ++pq) {
+            const int pp = hf + 2 * pq;
+            const f32x4_t x0 = acc[2 * pq], x1 = acc[2 * pq + 1];
+            stage[(kk * 16 + r) * 17 + 4 * pp + g] =
+                make_uint4(pk_bf16(x0[0], x0[1]), pk_bf16(x0[2], x0[3]), pk_bf16(x1[0], x1[1]), pk_bf16(x1[2], x1[3]));
+          }
+        } else {
+          const int32_t vo = valid ? (int32_t)(((int64_t)pos * D) * OB) : slab_bytes;
+#pragma unroll
+          for (int pq = 0; pq < 2; ++pq) {
+            const int pp = hf + 2 * pq;
+            const f32x4_t x0 = acc[2 * pq], x1 = acc[2 * pq + 1];
+            const int c0 = 32 * pp + 8 * g;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x0), orsrc, vo + 4 * c0, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x1), orsrc, vo + 4 * c0 + 16, 0, 0);
+          }
+        }
       }
+      if constexpr (OB == 2) {
+        lds_barrier();  // the sub-tile's rows are complete in LDS
+        // whole rows: wave w stores tokens 16 w .. 16 w + 15, four rows per
+        // instruction (lane = row l / 16, unit l % 16)
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const int rr = 16 * wave + 4 * it + (lane >> 4), un = lane & 15;
+          const uint4 v = stage[rr * 17 + un];
+          const int tok = sub * 64 + rr;
+          const bool valid = tok < nt;
+          const int pos = p.mid_begin + t0 + ta + tok;
+          if constexpr (PG) {
+            const int64_t page = p.page_row[min(pos, p.T - 1) >> 4];
+            uint8_t* rowp = valid ? obase + ((((page + (int64_t)l * p.pool_pages) * p.H + h) << 4) + (pos & 15)) * D * 2
+                                  : dummy;
+            *reinterpret_cast<uint4*>(rowp + 16 * un) = v;
+          } else {
+            const int32_t vo = valid ? (int32_t)((int64_t)pos * D * 2) : slab_bytes;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), orsrc, vo + 16 * un, 0, 0);
+          }
+        }
+      }
+      lds_barrier();  // the operands of this sub-tile are consumed
     }
   }
 }
 
-// KBMAX = 3 serves sections with at most 96 coded components, KBMAX = 4 the
-// rest; each instantiation leaves the other's sections alone.
 template <int KBMAX, bool PG>
-__global__ __launch_bounds__(256, 2) void k_dec_pca128(const Params p0) {
+__global__ __launch_bounds__(256, 3) void k_dec_pca128(const Params p0) {
   const Params p = at_seq(p0, blockIdx.z);
   constexpr int D = 128;
-  const int u = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
+  const int u = blockIdx.y, ch = blockIdx.x;
+  if (ch >= p.chunks_per_sec) return;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
+  if (min(p.chunk_tokens, p.T_mid - ch * p.chunk_tokens) <= 0) return;
 
   __shared__ DecKInfo s_ki[D];
-  __shared__ uint4 s_kw[4][D];       // per wave, sorted order: {b, row byte offset in its tile, scale, zero}
+  __shared__ uint4 s_kw[D];          // sorted order: {b, row byte offset in the tile, scale, zero}
   __shared__ uint8_t s_rank[D];      // natural component -> sorted position
   __shared__ __attribute__((aligned(16))) float s_const[D];
   __shared__ uint32_t s_b[D];
   __shared__ int32_t s_misc[4];      // nnz, corrupt flag, full tile words
-  __shared__ float4 s_brow[4][4 * 32];  // per wave: RoPE table rows of the current sub-tile's 16-token groups
-  // dynamic: [basis operand fragments 2 x 4 x KBMAX x 64 lanes x 16 B][staged basis | tile buffers]
+  // dynamic: [MFMA operands of the sub-tile: KBMAX x 4 KB][tile buffer][bf16
+  // output rows of the sub-tile: 64 x 272 bytes], the staged basis (prologue)
+  // overlaying them
   extern __shared__ __attribute__((aligned(16))) uint32_t dlds[];
-  uint4* sA = reinterpret_cast<uint4*>(dlds);
-  uint32_t* work = dlds + 2 * 4 * KBMAX * 64 * 4;
+  uint4* cq = reinterpret_cast<uint4*>(dlds);
+  uint32_t* tb = dlds + KBMAX * 4 * 64 * 4;
+  uint4* stage = reinterpret_cast<uint4*>(tb + ((dec_tile_words(p) + 3) & ~3));  // 64 rows x 17 units
 
   if (tid == 0) s_misc[1] = (int32_t)((get_status(p.ws, p.w) >> KVTC_ERR_CORRUPT) & 1u);
   const uint8_t* rec = p.in + p.side_off + (int64_t)u * 9 * D;
@@ -708,7 +695,7 @@ __global__ __launch_bounds__(256, 2) void k_dec_pca128(const Params p0) {
   // stage the basis rows (channel-major, operand precision) for the gathers
   const int64_t bidx = (p.basis_per_head ? ((int64_t)(l * 2 + s) * p.H + h) : (int64_t)(l * 2 + s)) * D * D;
   const uint16_t* bsrc = reinterpret_cast<const uint16_t*>(p.basis) + bidx;
-  uint16_t* bst = reinterpret_cast<uint16_t*>(work);
+  uint16_t* bst = reinterpret_cast<uint16_t*>(dlds);
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int row = it * 16 + (tid >> 4), c16 = tid & 15;
@@ -720,38 +707,55 @@ __global__ __launch_bounds__(256, 2) void k_dec_pca128(const Params p0) {
   const int KB = (nnz + 31) >> 5;
   if ((KBMAX == 3) != (KB <= 3)) return;
   if (tid >= 128) {
-    // constant of the b = 0 components: sum_i B[j][i] bf16(zero_i), fp64, one rounding
+    // constant of the b = 0 components (sorted positions nnz .. D-1):
+    // sum_i B[j][i] bf16(zero_i), fp64, one rounding
     const int j = tid - 128;
-    const float* zr = reinterpret_cast<const float*>(rec + D);
     double acc = 0.0;
-    for (int i = 0; i < D; ++i)
-      if (s_b[i] == 0) acc = __fma_rn((double)bf16_to_f32(bst[j * kBS + i]), (double)round_bf16(zr[i]), acc);
+    for (int k = nnz; k < D; ++k) {
+      const DecKInfo ki = s_ki[k];
+      acc = __fma_rn((double)bf16_to_f32(bst[j * kBS + ki.idx]), (double)round_bf16(ki.zero), acc);
+    }
     s_const[j] = (float)acc;
   }
-  // basis operand fragments [hf][mi][kb][lane]: lane (g, r) holds channel
-  // sigma(m, r) = 32 p + 8 (r >> 2) + 4 a + (r & 3), m = 2 p + a, p = hf + 2 (mi >> 1),
-  // a = mi & 1, of the sorted components 32 kb + 8 g .. +7
-  for (int f = wave; f < 2 * 4 * KB; f += 4) {
-    const int hf = f / (4 * KB), mi = (f / KB) % 4, kb = f % KB;
-    const int pp = hf + 2 * (mi >> 1), a = mi & 1;
-    const int chn = 32 * pp + 8 * (r >> 2) + 4 * a + (r & 3);
-    uint32_t w4[4];
+  // this wave's basis operand fragments A[mi][kb]: lane (g, r) holds channel
+  // 32 pp + 8 (r >> 2) + 4 a + (r & 3), pp = hf + 2 (mi >> 1), a = mi & 1,
+  // hf = wave & 1, of the sorted components 32 kb + 8 g .. +7
+  uint4 A[4][KBMAX];
+  {
+    const int hf = wave & 1;
+    // natural index of the lane's sorted components 32 kb + 8 g .. +7 (-1: none)
+    int idx[KBMAX][8];
 #pragma unroll
-    for (int q2 = 0; q2 < 4; ++q2) {
-      const int k0 = 32 * kb + 8 * g + 2 * q2;
-      const uint32_t lo = k0 < nnz ? bst[chn * kBS + s_ki[k0].idx] : 0u;
-      const uint32_t hi = k0 + 1 < nnz ? bst[chn * kBS + s_ki[k0 + 1].idx] : 0u;
-      w4[q2] = lo | (hi << 16);
+    for (int kb = 0; kb < KBMAX; ++kb)
+#pragma unroll
+      for (int z = 0; z < 8; ++z) {
+        const int k = 32 * kb + 8 * g + z;
+        idx[kb][z] = k < nnz ? (int)s_ki[k].idx : -1;
+      }
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int pp = hf + 2 * (mi >> 1), a = mi & 1;
+      const uint16_t* brow = bst + (32 * pp + 8 * (r >> 2) + 4 * a + (r & 3)) * kBS;
+#pragma unroll
+      for (int kb = 0; kb < KBMAX; ++kb) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+          const int i0 = idx[kb][2 * q2], i1 = idx[kb][2 * q2 + 1];
+          const uint32_t lo = i0 >= 0 ? brow[i0] : 0u;
+          const uint32_t hi = i1 >= 0 ? brow[i1] : 0u;
+          w4[q2] = lo | (hi << 16);
+        }
+        A[mi][kb] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      }
+      // one channel tile's gathers at a time (bounds the registers in flight)
+      __builtin_amdgcn_sched_barrier(0);
     }
-    sA[((hf * 4 + mi) * KBMAX + kb) * 64 + lane] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
   }
-  __syncthreads();  // the staged basis area becomes the tile buffers
-
-  const int ch = blockIdx.x * 4 + wave;
+  __syncthreads();  // the staged basis area becomes the operand and tile buffers
   const uint32_t fw = (uint32_t)s_misc[2];
-  const int tbw = (int)(((int64_t)p.tile_tokens * (p.budget_k > p.budget_v ? p.budget_k : p.budget_v) + 31) / 32) + D + 20;
-  uint32_t* tb = work + wave * tbw;
-#define KVTC_DEC_CHUNK(KBV, OBV) dec_chunk128<KBV, KBMAX, OBV, PG>(p, u, ch, sA, tb, s_kw[wave], s_ki, s_rank, s_b, s_const, fw, nnz, s_brow[wave])
+
+#define KVTC_DEC_CHUNK(KBV, OBV) dec_chunk128<KBV, KBMAX, OBV, PG>(p, u, ch, A, cq, tb, s_kw, s_ki, s_rank, s_b, s_const, fw, stage)
   if constexpr (PG) {  // pools hold the cache dtype: bf16
     if constexpr (KBMAX == 4) {
       KVTC_DEC_CHUNK(4, 2);
@@ -796,12 +800,13 @@ hipError_t launch_dec_transform(const Params& p, hipStream_t s) {
   const size_t tile_words = (size_t)(((int64_t)p.tile_tokens * bmax + 31) / 32 + nz) + 4;
   if (p.D == 128 && p.dtype == KVTC_BF16 && p.tile_tokens % 64 == 0 &&
       (p.n_seqs > 0 || (int64_t)p.T * 128 * ob < (1ll << 31))) {
-    const int tbw = (int)(((int64_t)p.tile_tokens * bmax + 31) / 32) + 128 + 20;
-    size_t work = (size_t)4 * tbw * 4;
-    if (work < (size_t)128 * kBS * 2) work = (size_t)128 * kBS * 2;
-    const size_t lds3 = (size_t)2 * 4 * 3 * 64 * 16 + work, lds4 = (size_t)2 * 4 * 4 * 64 * 16 + work;
+    // dynamic LDS: operands + tile buffer, at least the staged basis
+    const size_t tbytes = (size_t)((dec_tile_words(p) + 3) & ~3) * 4 + (size_t)64 * 17 * 16, bbytes = (size_t)128 * kBS * 2;
+    size_t lds3 = (size_t)3 * 4 * 64 * 16 + tbytes, lds4 = (size_t)4 * 4 * 64 * 16 + tbytes;
+    if (lds3 < bbytes) lds3 = bbytes;
+    if (lds4 < bbytes) lds4 = bbytes;
     if (lds4 <= 140 * 1024) {
-      dim3 g4((p.chunks_per_sec + 3) / 4, p.n_sections, seq_grid(p));
+      dim3 g4(p.chunks_per_sec, p.n_sections, seq_grid(p));
       if (p.n_seqs > 0) {
         if (ob != 2) return hipErrorInvalidValue;
         (void)hipFuncSetAttribute((const void*)k_dec_pca128<3, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3);

@@ -1100,7 +1100,10 @@ __global__ __launch_bounds__(256, MODE == 0 ? 4 : 1) void k_enc128(const Params 
         for (uint32_t i = tid; i < sd.row_w[D]; i += 256) tilebuf[i] = 0;
       }
     }
-    __syncthreads();
+    // the staged rows are complete (an LDS-only barrier: the next sub-tile's
+    // loads stay in flight)
+    if constexpr (MODE == 1) __syncthreads();
+    else lds_barrier();
     f32x4_t acc[4][2];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {

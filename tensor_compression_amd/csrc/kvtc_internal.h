@@ -335,6 +335,15 @@ __device__ inline uint32_t get_status(const uint8_t* ws, const WsLayout& w) {
   return __atomic_load_n(reinterpret_cast<const uint32_t*>(ws + w.status), __ATOMIC_RELAXED);
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its global loads and stores (which a plain
+// __syncthreads also drains, so prefetches in flight would stall it).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // The counter slot of a workgroup (x, y).
 __device__ inline uint32_t* count_slot(uint8_t* ws, const WsLayout& w) {
   const uint32_t i = (blockIdx.x + blockIdx.y * gridDim.x) % kCountSlots;
