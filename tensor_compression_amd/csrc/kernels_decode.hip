@@ -386,6 +386,9 @@ struct DecKInfo {  // per component in the sorted order
   float scale, zero;
 };
 
+typedef __attribute__((address_space(3))) const uint32_t lds_word_t;
+typedef __attribute__((address_space(3))) const uint8_t lds_byte_t;
+
 __device__ __forceinline__ uint32_t lds_u32(const uint32_t* base, uint32_t byte_off) {
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(base) + byte_off);
 }
@@ -476,6 +479,7 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
     }
     lds_barrier();
 
+    lds_byte_t* const tb3 = (lds_byte_t*)tb;  // the tile buffer in the LDS address space
     for (int sub = 0; sub * 64 < nt; ++sub) {
       // RoPE table entries of this wave's two 16-token groups, in flight
       // during the dequantisation (a row is 64 pairs of cos, sin: 512 bytes;
@@ -509,12 +513,13 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
           const uint4 ki = s_kw[8 * c8 + z];
           bw[z] = __builtin_amdgcn_readfirstlane(ki.x);
           const uint32_t seg = __builtin_amdgcn_readfirstlane(ki.y) + 8u * bw[z] * (uint32_t)sub;
-          sc[z] = __uint_as_float(ki.z);
-          zr[z] = __uint_as_float(ki.w);
+          sc[z] = __uint_as_float(__builtin_amdgcn_readfirstlane(ki.z));
+          zr[z] = __uint_as_float(ki.w);  // uniform; the fma takes it from a vector register
           bp[z] = __umul24((uint32_t)lane, bw[z]);
-          const uint32_t off = seg + ((bp[z] >> 5) << 2);
-          lo[z] = lds_u32(tb, off);
-          hi[z] = lds_u32(tb, off + 4);
+          // the row segment's first word (uniform LDS address) plus this lane's word
+          const lds_word_t* wp = (const lds_word_t*)(tb3 + seg) + (bp[z] >> 5);
+          lo[z] = wp[0];
+          hi[z] = wp[1];
         }
         uint32_t w4[4];
 #pragma unroll
@@ -523,7 +528,7 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
 #pragma unroll
           for (int z2 = 0; z2 < 2; ++z2) {
             const int z = 2 * q2 + z2;
-            const uint32_t q = __builtin_amdgcn_alignbit(hi[z], lo[z], bp[z]) & ((1u << bw[z]) - 1u);
+            const uint32_t q = __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(hi[z], lo[z], bp[z]), 0u, bw[z]);
             v[z2] = __fmaf_rn((float)q, sc[z], zr[z]);
           }
           w4[q2] = pk_bf16(v[0], v[1]);

@@ -356,10 +356,16 @@ __device__ __forceinline__ int64_t slot_states_off(const Params& p, int t) {
          (int64_t)t * (4 * p.lanes + 2 * p.w.tile_words_max + 4);
 }
 
-__global__ void k_rans_enc_chunks(const Params p0) {
+// raw_runs > 0 (contiguous cache): workgroups past the chunks copy the raw
+// sink and recent runs into the container, on the bandwidth this
+// latency-bound pass leaves idle.
+__global__ void k_rans_enc_chunks(const Params p0, int raw_runs) {
   const Params p = at_seq(p0, blockIdx.z);
   const int c = blockIdx.x;
-  if (c >= p.n_chunks) return;
+  if (c >= p.n_chunks) {
+    if (c - p.n_chunks < raw_runs) copy_raw_run(p, c - p.n_chunks, 1, false);
+    return;
+  }
   const int u = c / p.chunks_per_sec, ch = c % p.chunks_per_sec;
   const int D = p.D;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -474,11 +480,12 @@ __global__ void k_rans_enc_chunks(const Params p0) {
   }
 }
 
-hipError_t launch_rans_encode_chunks(const Params& p, hipStream_t s) {
+hipError_t launch_rans_encode_chunks(const Params& p, hipStream_t s, bool with_raw) {
   int streams = p.tiles_per_chunk;
   int waves = (streams * p.lanes + 63) / 64;
   if (waves < 1) waves = 1;
-  hipLaunchKernelGGL(k_rans_enc_chunks, dim3(p.n_chunks, 1, seq_grid(p)), dim3(64 * waves), 0, s, p);
+  const int raw_runs = with_raw && p.n_seqs == 0 ? 4 * p.L * p.H : 0;
+  hipLaunchKernelGGL(k_rans_enc_chunks, dim3(p.n_chunks + raw_runs, 1, seq_grid(p)), dim3(64 * waves), 0, s, p, raw_runs);
   return hipGetLastError();
 }
 
@@ -657,10 +664,16 @@ hipError_t launch_dec_check(const Params& p, const uint8_t* hdr, hipStream_t s) 
   return hipGetLastError();
 }
 
-__global__ void k_rans_dec_chunks(const Params p0) {
+// raw_runs > 0 (contiguous cache): workgroups past the chunks copy the raw
+// sink and recent runs of the container to the outputs, which costs the
+// bandwidth this latency-bound pass leaves idle.
+__global__ void k_rans_dec_chunks(const Params p0, int raw_runs) {
   const Params p = at_seq(p0, blockIdx.z);
   const int c = blockIdx.x;
-  if (c >= p.n_chunks) return;
+  if (c >= p.n_chunks) {
+    if (c - p.n_chunks < raw_runs) copy_raw_run(p, c - p.n_chunks, 0, false);
+    return;
+  }
   const int u = c / p.chunks_per_sec, ch = c % p.chunks_per_sec;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (get_status(p.ws, p.w) & (1u << KVTC_ERR_CORRUPT)) return;
@@ -783,13 +796,14 @@ __global__ void k_rans_dec_chunks(const Params p0) {
   }
 }
 
-hipError_t launch_rans_decode_chunks(const Params& p, hipStream_t s) {
+hipError_t launch_rans_decode_chunks(const Params& p, hipStream_t s, bool with_raw) {
   int streams = p.tiles_per_chunk;
   int waves = (streams * p.lanes + 63) / 64;
   if (waves < 1) waves = 1;
   // LDS: the symbol tables and one word ring per tile
   const size_t lds = 1024 + (size_t)(1u << p.sb) + (size_t)p.tiles_per_chunk * kRing * 2;
-  hipLaunchKernelGGL(k_rans_dec_chunks, dim3(p.n_chunks, 1, seq_grid(p)), dim3(64 * waves), lds, s, p);
+  const int raw_runs = with_raw && p.n_seqs == 0 ? 4 * p.L * p.H : 0;
+  hipLaunchKernelGGL(k_rans_dec_chunks, dim3(p.n_chunks + raw_runs, 1, seq_grid(p)), dim3(64 * waves), lds, s, p, raw_runs);
   return hipGetLastError();
 }
 

@@ -355,18 +355,21 @@ kvtc_status kvtc_encode(kvtc_plan_t plan, const void* k, const void* v, int32_t 
   uint8_t hdr[kHeaderBytes];
   build_header(*pl, lo, hdr);
   ProfScope prof(pl, stream);
-  HIP_TRY(launch_copy_raw(p, 1, stream));  // also clears the status word
-  prof.phase("copy_raw");
   if (lo.n_chunks > 0) {
+    // the first pass clears the status block; the raw runs are copied by
+    // extra workgroups of the rANS encoder
     HIP_TRY(launch_enc_transform(p, 0, stream));
     prof.phase("enc_stats");
+  } else {
+    HIP_TRY(launch_copy_raw(p, 1, stream));  // also clears the status block
+    prof.phase("copy_raw");
   }
   HIP_TRY(launch_enc_alloc(p, stream));
   prof.phase("enc_alloc");
   if (lo.n_chunks > 0) {
     HIP_TRY(launch_enc_transform(p, 1, stream));
     prof.phase("enc_quant_pack");
-    HIP_TRY(launch_rans_encode_chunks(p, stream));
+    HIP_TRY(launch_rans_encode_chunks(p, stream, true));
     prof.phase("rans_encode");
   }
   HIP_TRY(launch_assemble(p, hdr, stream));
@@ -395,13 +398,15 @@ kvtc_status kvtc_decode(kvtc_plan_t plan, const void* in, size_t in_bytes, int32
   HIP_TRY(launch_dec_check(p, hdr, stream));  // clears, then sets the status word
   prof.phase("dec_check");
   if (lo.n_chunks > 0) {
-    HIP_TRY(launch_rans_decode_chunks(p, stream));
+    // the raw runs are copied by extra workgroups of the rANS decoder
+    HIP_TRY(launch_rans_decode_chunks(p, stream, true));
     prof.phase("rans_decode");
     HIP_TRY(launch_dec_transform(p, stream));
     prof.phase("dec_transform");
+  } else {
+    HIP_TRY(launch_copy_raw(p, 0, stream));
+    prof.phase("copy_raw_out");
   }
-  HIP_TRY(launch_copy_raw(p, 0, stream));
-  prof.phase("copy_raw_out");
   return KVTC_OK;
 }
 

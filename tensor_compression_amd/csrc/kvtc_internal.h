@@ -289,10 +289,10 @@ hipError_t launch_copy_raw(const Params& p, int to_container, hipStream_t s);
 hipError_t launch_enc_transform(const Params& p, int mode, hipStream_t s);  // 0 stats, 1 quant
 hipError_t launch_enc_alloc(const Params& p, hipStream_t s);
 hipError_t launch_quant128(const Params& p, hipStream_t s);  // head_dim 128 bf16 PCA, tile % 64 == 0
-hipError_t launch_rans_encode_chunks(const Params& p, hipStream_t s);
+hipError_t launch_rans_encode_chunks(const Params& p, hipStream_t s, bool with_raw = false);
 hipError_t launch_assemble(const Params& p, const uint8_t* hdr, hipStream_t s);
 hipError_t launch_dec_check(const Params& p, const uint8_t* hdr, hipStream_t s);
-hipError_t launch_rans_decode_chunks(const Params& p, hipStream_t s);
+hipError_t launch_rans_decode_chunks(const Params& p, hipStream_t s, bool with_raw = false);
 hipError_t launch_dec_transform(const Params& p, hipStream_t s);
 hipError_t launch_coeffs(const Params& p, int sec_begin, int sec_end, float* out, float* r_out,
                          hipStream_t s);
@@ -344,10 +344,107 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Encode of a contiguous cache: the first workgroup of the first pass over
+// the middle clears the status word and the count slots (no workgroup of that
+// pass reads or sets them).
+__device__ inline void clear_status_block(const Params& p) {
+  if (threadIdx.x < 4) reinterpret_cast<uint32_t*>(p.ws + p.w.status)[threadIdx.x] = 0u;
+  if (threadIdx.x < kCountSlots)
+    *reinterpret_cast<uint32_t*>(p.ws + p.w.status + kCountOff + kCountStride * threadIdx.x) = 0u;
+}
+
 // The counter slot of a workgroup (x, y).
 __device__ inline uint32_t* count_slot(uint8_t* ws, const WsLayout& w) {
   const uint32_t i = (blockIdx.x + blockIdx.y * gridDim.x) % kCountSlots;
   return reinterpret_cast<uint32_t*>(ws + w.status + kCountOff + kCountStride * i);
+}
+
+// ---- raw sink / recent regions ------------------------------------------------
+// to_container = 1: cache -> container (+ zero the side and raw padding);
+// 0: container -> output tensors in out_dtype.
+// Raw regions as contiguous runs: for every (tensor, region, layer x head) the
+// n_region rows are consecutive both in the cache ([L,H,T,D]) and in the
+// container ([L,H,n_region,D] per tensor and region).  A workgroup per run;
+// each thread moves up to eight 16-byte units (rows are whole 16-byte units
+// for head_dim 64 and 128), all loads issued before the stores.
+// One run by the calling workgroup (any size; the rANS decoder's extra
+// workgroups also use it).  first: clears the status block (encode,
+// contiguous cache).
+__device__ inline void copy_raw_run(const Params& p, int run, int to_container, bool first) {
+  const int nth = (int)blockDim.x;
+  const int e = p.dtype == KVTC_BF16 ? 2 : 4;
+  const int row_units = p.D * e / 16;
+  const int LH = p.L * p.H;
+  const int s = run / (2 * LH), region = (run / LH) & 1, lh = run % LH;
+  const int n_region = region == 0 ? p.s0 : p.W_eff;
+  const int units = n_region * row_units;
+  if (to_container && first && run == 0) {
+    if (threadIdx.x < 4) reinterpret_cast<uint32_t*>(p.ws + p.w.status)[threadIdx.x] = 0u;
+    if (threadIdx.x < kCountSlots)
+      *reinterpret_cast<uint32_t*>(p.ws + p.w.status + kCountOff + kCountStride * threadIdx.x) = 0u;
+  }
+  if (!to_container && (get_status(p.ws, p.w) & (1u << KVTC_ERR_CORRUPT))) return;
+  const int64_t row_bytes = (int64_t)p.D * e;
+  const int64_t per_tensor = (int64_t)LH * (p.s0 + p.W_eff) * row_bytes;
+  const int64_t cbase = (int64_t)s * per_tensor + (region == 0 ? 0 : (int64_t)LH * p.s0 * row_bytes) +
+                        (int64_t)lh * n_region * row_bytes;
+  const int pos0 = region == 0 ? 0 : p.mid_end;
+  // first element of unit i of the run in the cache
+  auto telem = [&](int i) {
+    const int row = i / row_units, ui = i - row * row_units;
+    return cache_row(p, lh / p.H, lh % p.H, pos0 + row) + (int64_t)ui * (16 / e);
+  };
+  for (int i0 = 0; i0 < units; i0 += 8 * nth) {
+    uint4 v[8];
+    if (to_container) {
+      const uint8_t* src = reinterpret_cast<const uint8_t*>(s ? p.v : p.k);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k * nth + (int)threadIdx.x;
+        if (i < units) v[k] = *reinterpret_cast<const uint4*>(src + telem(i) * e);
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k * nth + (int)threadIdx.x;
+        if (i < units) *reinterpret_cast<uint4*>(p.out + p.raw_off + cbase + (int64_t)i * 16) = v[k];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k * nth + (int)threadIdx.x;
+        if (i < units) v[k] = *reinterpret_cast<const uint4*>(p.in + p.raw_off + cbase + (int64_t)i * 16);
+      }
+      void* dst = s ? p.v_out : p.k_out;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k * nth + (int)threadIdx.x;
+        if (i >= units) continue;
+        const uint4 w = v[k];
+        const int64_t te = telem(i);
+        if (p.out_dtype == p.dtype) {
+          *reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(dst) + te * e) = w;
+        } else if (p.dtype == KVTC_BF16) {  // bf16 -> fp32: exact widening of 8 values
+          uint4* d = reinterpret_cast<uint4*>(reinterpret_cast<float*>(dst) + te);
+          d[0] = make_uint4(w.x << 16, w.x & 0xffff0000u, w.y << 16, w.y & 0xffff0000u);
+          d[1] = make_uint4(w.z << 16, w.z & 0xffff0000u, w.w << 16, w.w & 0xffff0000u);
+        } else {  // fp32 -> bf16 (RNE) of 4 values
+          const uint32_t lo = (uint32_t)f32_to_bf16(__uint_as_float(w.x)) | ((uint32_t)f32_to_bf16(__uint_as_float(w.y)) << 16);
+          const uint32_t hi = (uint32_t)f32_to_bf16(__uint_as_float(w.z)) | ((uint32_t)f32_to_bf16(__uint_as_float(w.w)) << 16);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(dst) + te) = make_uint2(lo, hi);
+        }
+      }
+    }
+  }
+  if (to_container && run == 0 && threadIdx.x < 64) {
+    // zero padding: the gap between the side records (and r area) and
+    // raw_off, and the raw area's tail; each is shorter than 16 bytes
+    int64_t r_used = 0;
+    if (p.transform == KVTC_WHT) r_used = (int64_t)(p.wht_keys ? 2 : 1) * p.L * p.H * p.T_mid * 4;
+    const int64_t a0 = p.r_off + r_used, a1 = p.raw_off;
+    const int64_t b0 = p.raw_off + 2 * (int64_t)LH * (p.s0 + p.W_eff) * p.D * e, b1 = p.raw_off + p.raw_bytes;
+    const int64_t na = a1 - a0, nb = b1 - b0;
+    for (int64_t k = threadIdx.x; k < na + nb; k += 64) p.out[k < na ? a0 + k : b0 + (k - na)] = 0;
+  }
 }
 
 }  // namespace kvtc
