@@ -1304,12 +1304,28 @@ __global__ __launch_bounds__(64) void k_enc_alloc(const Params p0) {
     if (c < NC && N > 0) {
       double a = 0.0, b = 0.0;
       float lo = INFINITY, hi = -INFINITY;
-      for (int ch = 0; ch < p.chunks_per_sec; ++ch) {
-        const int64_t idx = ((int64_t)u * p.chunks_per_sec + ch) * D + i;
-        a += reinterpret_cast<const double*>(p.ws + p.w.part_sum)[idx];
-        b += reinterpret_cast<const double*>(p.ws + p.w.part_sq)[idx];
-        lo = fminf(lo, reinterpret_cast<const float*>(p.ws + p.w.part_min)[idx]);
-        hi = fmaxf(hi, reinterpret_cast<const float*>(p.ws + p.w.part_max)[idx]);
+      // the chunks' partials, eight chunks' loads in flight at a time
+      for (int c0 = 0; c0 < p.chunks_per_sec; c0 += 8) {
+        double pa[8], pb[8];
+        float pl[8], ph[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int ch = min(c0 + k, p.chunks_per_sec - 1);
+          const int64_t idx = ((int64_t)u * p.chunks_per_sec + ch) * D + i;
+          pa[k] = reinterpret_cast<const double*>(p.ws + p.w.part_sum)[idx];
+          pb[k] = reinterpret_cast<const double*>(p.ws + p.w.part_sq)[idx];
+          pl[k] = reinterpret_cast<const float*>(p.ws + p.w.part_min)[idx];
+          ph[k] = reinterpret_cast<const float*>(p.ws + p.w.part_max)[idx];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (c0 + k < p.chunks_per_sec) {
+            a += pa[k];
+            b += pb[k];
+            lo = fminf(lo, pl[k]);
+            hi = fmaxf(hi, ph[k]);
+          }
+        }
       }
       nonfinite |= !isfinite(a) || !isfinite(b);
       const double m = a / (double)N;
