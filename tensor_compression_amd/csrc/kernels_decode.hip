@@ -504,34 +504,77 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
 #pragma unroll 1
       for (int j8 = 0; j8 < KB; ++j8) {
         const int c8 = 4 * j8 + wave;
-        // the octet's widths, row offsets and constants (wave-uniform), then
-        // all eight code-word pairs in flight before any is used
-        uint32_t bw[8], bp[8], lo[8], hi[8];
-        float sc[8], zr[8];
+        // widths ascend along the sorted order with the uncoded entries (all
+        // zero) last, so the first and last width of the octet tell whether
+        // it has a single width
+        const uint32_t bf = __builtin_amdgcn_readfirstlane(s_kw[8 * c8].x);
+        const uint32_t bl = __builtin_amdgcn_readfirstlane(s_kw[8 * c8 + 7].x);
+        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+        if (bf == bl && bf != 0u) {
+          // one width: the lane's bit position and word offset are shared by
+          // the eight rows; per code one add, one or two LDS words, extract,
+          // convert, fma (offsets and constants stay in vector registers)
+          const uint32_t bpos = __umul24((uint32_t)lane, bf);
+          const lds_byte_t* const lb = tb3 + 8u * bf * (uint32_t)sub + ((bpos >> 5) << 2);
+          uint32_t x[8];
+          float sc[8], zr[8];
+          if ((bf & (bf - 1u)) == 0u) {  // 1, 2, 4, 8 bits: a code never straddles two words
 #pragma unroll
-        for (int z = 0; z < 8; ++z) {
-          const uint4 ki = s_kw[8 * c8 + z];
-          bw[z] = __builtin_amdgcn_readfirstlane(ki.x);
-          const uint32_t seg = __builtin_amdgcn_readfirstlane(ki.y) + 8u * bw[z] * (uint32_t)sub;
-          sc[z] = __uint_as_float(__builtin_amdgcn_readfirstlane(ki.z));
-          zr[z] = __uint_as_float(ki.w);  // uniform; the fma takes it from a vector register
-          bp[z] = __umul24((uint32_t)lane, bw[z]);
-          // the row segment's first word (uniform LDS address) plus this lane's word
-          const lds_word_t* wp = (const lds_word_t*)(tb3 + seg) + (bp[z] >> 5);
-          lo[z] = wp[0];
-          hi[z] = wp[1];
-        }
-        uint32_t w4[4];
+            for (int z = 0; z < 8; ++z) {
+              const uint4 ki = s_kw[8 * c8 + z];
+              x[z] = *(const lds_word_t*)(lb + ki.y);
+              sc[z] = __uint_as_float(ki.z);
+              zr[z] = __uint_as_float(ki.w);
+            }
 #pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          float v[2];
+            for (int z = 0; z < 8; ++z) x[z] = __builtin_amdgcn_ubfe(x[z], bpos & 31u, bf);
+          } else {
+            uint32_t hi[8];
 #pragma unroll
-          for (int z2 = 0; z2 < 2; ++z2) {
-            const int z = 2 * q2 + z2;
-            const uint32_t q = __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(hi[z], lo[z], bp[z]), 0u, bw[z]);
-            v[z2] = __fmaf_rn((float)q, sc[z], zr[z]);
+            for (int z = 0; z < 8; ++z) {
+              const uint4 ki = s_kw[8 * c8 + z];
+              const lds_word_t* wp = (const lds_word_t*)(lb + ki.y);
+              x[z] = wp[0];
+              hi[z] = wp[1];
+              sc[z] = __uint_as_float(ki.z);
+              zr[z] = __uint_as_float(ki.w);
+            }
+#pragma unroll
+            for (int z = 0; z < 8; ++z) x[z] = __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(hi[z], x[z], bpos), 0u, bf);
           }
-          w4[q2] = pk_bf16(v[0], v[1]);
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2)
+            w4[q2] = pk_bf16(__fmaf_rn((float)x[2 * q2], sc[2 * q2], zr[2 * q2]),
+                             __fmaf_rn((float)x[2 * q2 + 1], sc[2 * q2 + 1], zr[2 * q2 + 1]));
+        } else if (bf != 0u) {
+          // mixed widths: per row width, offsets and constants (wave-uniform),
+          // then all eight code-word pairs in flight before any is used
+          uint32_t bw[8], bp[8], lo[8], hi[8];
+          float sc[8], zr[8];
+#pragma unroll
+          for (int z = 0; z < 8; ++z) {
+            const uint4 ki = s_kw[8 * c8 + z];
+            bw[z] = __builtin_amdgcn_readfirstlane(ki.x);
+            const uint32_t seg = __builtin_amdgcn_readfirstlane(ki.y) + 8u * bw[z] * (uint32_t)sub;
+            sc[z] = __uint_as_float(__builtin_amdgcn_readfirstlane(ki.z));
+            zr[z] = __uint_as_float(ki.w);  // uniform; the fma takes it from a vector register
+            bp[z] = __umul24((uint32_t)lane, bw[z]);
+            // the row segment's first word (uniform LDS address) plus this lane's word
+            const lds_word_t* wp = (const lds_word_t*)(tb3 + seg) + (bp[z] >> 5);
+            lo[z] = wp[0];
+            hi[z] = wp[1];
+          }
+#pragma unroll
+          for (int q2 = 0; q2 < 4; ++q2) {
+            float v[2];
+#pragma unroll
+            for (int z2 = 0; z2 < 2; ++z2) {
+              const int z = 2 * q2 + z2;
+              const uint32_t q = __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(hi[z], lo[z], bp[z]), 0u, bw[z]);
+              v[z2] = __fmaf_rn((float)q, sc[z], zr[z]);
+            }
+            w4[q2] = pk_bf16(v[0], v[1]);
+          }
         }
         // operand slot [kb = c8 / 4][kk = lane / 16][g = c8 % 4][r = lane % 16]
         cq[((c8 >> 2) * 4 + (lane >> 4)) * 64 + (c8 & 3) * 16 + (lane & 15)] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
