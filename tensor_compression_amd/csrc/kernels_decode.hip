@@ -442,6 +442,19 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float2*>(p.rope), 0, rope ? p.T * 512 : 0, 0x00020000);
   const uint32_t* slot = reinterpret_cast<const uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot);
 
+  // widths of this wave's octets (sorted positions 8 c8 .. +7, c8 = 4 j8 +
+  // wave), one byte each: the single width of the octet, 0 when it holds no
+  // coded component, 0xff when its widths differ.  Widths ascend along the
+  // sorted order with the uncoded entries last, so the first and last entry
+  // decide.
+  uint32_t oct_w = 0u;
+#pragma unroll
+  for (int j8 = 0; j8 < KB; ++j8) {
+    const int c8 = 4 * j8 + wave;
+    const uint32_t bf = __builtin_amdgcn_readfirstlane(s_ki[8 * c8].b);
+    const uint32_t bl = __builtin_amdgcn_readfirstlane(s_ki[8 * c8 + 7].b);
+    oct_w |= (bf == bl ? bf : 0xffu) << (8 * j8);
+  }
   for (int ta = 0; ta < n; ta += p.tile_tokens) {
     const int nt = min(p.tile_tokens, n - ta);
     lds_barrier();  // the previous tile's buffer and operands are consumed
@@ -504,13 +517,9 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
 #pragma unroll 1
       for (int j8 = 0; j8 < KB; ++j8) {
         const int c8 = 4 * j8 + wave;
-        // widths ascend along the sorted order with the uncoded entries (all
-        // zero) last, so the first and last width of the octet tell whether
-        // it has a single width
-        const uint32_t bf = __builtin_amdgcn_readfirstlane(s_kw[8 * c8].x);
-        const uint32_t bl = __builtin_amdgcn_readfirstlane(s_kw[8 * c8 + 7].x);
+        const uint32_t bf = (oct_w >> (8 * j8)) & 0xffu;
         uint32_t w4[4] = {0u, 0u, 0u, 0u};
-        if (bf == bl && bf != 0u) {
+        if (bf != 0xffu && bf != 0u) {
           // one width: the lane's bit position and word offset are shared by
           // the eight rows; per code one add, one or two LDS words, extract,
           // convert, fma (offsets and constants stay in vector registers)
@@ -546,7 +555,7 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
           for (int q2 = 0; q2 < 4; ++q2)
             w4[q2] = pk_bf16(__fmaf_rn((float)x[2 * q2], sc[2 * q2], zr[2 * q2]),
                              __fmaf_rn((float)x[2 * q2 + 1], sc[2 * q2 + 1], zr[2 * q2 + 1]));
-        } else if (bf != 0u) {
+        } else if (bf == 0xffu) {
           // mixed widths: per row width, offsets and constants (wave-uniform),
           // then all eight code-word pairs in flight before any is used
           uint32_t bw[8], bp[8], lo[8], hi[8];
