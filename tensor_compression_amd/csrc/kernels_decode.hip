@@ -710,7 +710,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_pca128(const Params p0) {
   __shared__ uint8_t s_rank[D];      // natural component -> sorted position
   __shared__ __attribute__((aligned(16))) float s_const[D];
   __shared__ uint32_t s_b[D];
-  __shared__ int32_t s_misc[4];      // nnz, corrupt flag, full tile words
+  __shared__ int32_t s_misc[4];      // [1] corrupt flag, [2] full tile words
   // dynamic: [MFMA operands of the sub-tile: KBMAX x 4 KB][tile buffer][bf16
   // output rows of the sub-tile: 64 x 272 bytes], the staged basis (prologue)
   // overlaying them
@@ -724,19 +724,29 @@ __global__ __launch_bounds__(256, 3) void k_dec_pca128(const Params p0) {
   if (tid < D) s_b[tid] = min((uint32_t)rec[tid], 8u);
   __syncthreads();
   if (s_misc[1]) return;
+  // coded components (every wave counts them): the variant for this section
+  const int nnz = (int)(__popcll(__ballot(s_b[lane] != 0u)) + __popcll(__ballot(s_b[lane + 64] != 0u)));
+  const int KB = (nnz + 31) >> 5;
+  if ((KBMAX == 3) != (KB <= 3)) return;
+  // the basis rows (channel-major, operand precision) in flight during the sort
+  const int64_t bidx = (p.basis_per_head ? ((int64_t)(l * 2 + s) * p.H + h) : (int64_t)(l * 2 + s)) * D * D;
+  const uint16_t* bsrc = reinterpret_cast<const uint16_t*>(p.basis) + bidx;
+  uint4 brow8[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it)
+    brow8[it] = *reinterpret_cast<const uint4*>(bsrc + (it * 16 + (tid >> 4)) * D + (tid & 15) * 8);
   if (wave == 0) {
     // counting sort of the components by width, b = 0 last
     const uint32_t b0 = s_b[2 * lane], b1 = s_b[2 * lane + 1];
     const uint32_t k0 = b0 ? b0 : 9u, k1 = b1 ? b1 : 9u;
     const uint64_t lt = (1ull << lane) - 1ull;
-    uint32_t base = 0, r0 = 0, r1 = 0, nnz = 0;
+    uint32_t base = 0, r0 = 0, r1 = 0;
     for (uint32_t v = 1; v <= 9; ++v) {
       const uint64_t m0 = __ballot(k0 == v), m1 = __ballot(k1 == v);
       const uint32_t before = base + __popcll(m0 & lt) + __popcll(m1 & lt);
       if (k0 == v) r0 = before;
       if (k1 == v) r1 = before + (k0 == v ? 1u : 0u);
       base += __popcll(m0) + __popcll(m1);
-      if (v == 8) nnz = base;
     }
     s_rank[2 * lane] = (uint8_t)r0;
     s_rank[2 * lane + 1] = (uint8_t)r1;
@@ -747,66 +757,53 @@ __global__ __launch_bounds__(256, 3) void k_dec_pca128(const Params p0) {
     uint32_t fw = ((uint32_t)(p.tile_tokens * (int)b0 + 31) >> 5) + ((uint32_t)(p.tile_tokens * (int)b1 + 31) >> 5);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) fw += __shfl_xor(fw, o, 64);
-    if (lane == 0) { s_misc[0] = (int32_t)nnz; s_misc[2] = (int32_t)fw; }
-  }
-  // stage the basis rows (channel-major, operand precision) for the gathers
-  const int64_t bidx = (p.basis_per_head ? ((int64_t)(l * 2 + s) * p.H + h) : (int64_t)(l * 2 + s)) * D * D;
-  const uint16_t* bsrc = reinterpret_cast<const uint16_t*>(p.basis) + bidx;
-  uint16_t* bst = reinterpret_cast<uint16_t*>(dlds);
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int row = it * 16 + (tid >> 4), c16 = tid & 15;
-    *reinterpret_cast<uint4*>(bst + row * kBS + c16 * 8) =
-        *reinterpret_cast<const uint4*>(bsrc + row * D + c16 * 8);
+    if (lane == 0) s_misc[2] = (int32_t)fw;
   }
   __syncthreads();
-  const int nnz = s_misc[0];
-  const int KB = (nnz + 31) >> 5;
-  if ((KBMAX == 3) != (KB <= 3)) return;
+  // stage the basis with its columns in sorted component order:
+  // bst[channel][sorted position]
+  uint16_t* bst = reinterpret_cast<uint16_t*>(dlds);
+  {
+    uint32_t rk[8];
+#pragma unroll
+    for (int z = 0; z < 8; ++z) rk[z] = s_rank[(tid & 15) * 8 + z];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      uint16_t* brow = bst + (it * 16 + (tid >> 4)) * kBS;
+      const uint32_t w[4] = {brow8[it].x, brow8[it].y, brow8[it].z, brow8[it].w};
+#pragma unroll
+      for (int z = 0; z < 8; ++z) brow[rk[z]] = (uint16_t)(w[z >> 1] >> (16 * (z & 1)));
+    }
+  }
+  __syncthreads();
   if (tid >= 128) {
     // constant of the b = 0 components (sorted positions nnz .. D-1):
-    // sum_i B[j][i] bf16(zero_i), fp64, one rounding
+    // sum_i B[j][i] bf16(zero_i), fp64 (four partial sums), one rounding
     const int j = tid - 128;
-    double acc = 0.0;
-    for (int k = nnz; k < D; ++k) {
-      const DecKInfo ki = s_ki[k];
-      acc = __fma_rn((double)bf16_to_f32(bst[j * kBS + ki.idx]), (double)round_bf16(ki.zero), acc);
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int k = nnz; k < D; k += 4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kk = min(k + e, D - 1);
+        const double t = (double)bf16_to_f32(bst[j * kBS + kk]) * (double)round_bf16(s_ki[kk].zero);
+        acc[e] += (k + e < D) ? t : 0.0;
+      }
     }
-    s_const[j] = (float)acc;
+    s_const[j] = (float)((acc[0] + acc[1]) + (acc[2] + acc[3]));
   }
   // this wave's basis operand fragments A[mi][kb]: lane (g, r) holds channel
   // 32 pp + 8 (r >> 2) + 4 a + (r & 3), pp = hf + 2 (mi >> 1), a = mi & 1,
-  // hf = wave & 1, of the sorted components 32 kb + 8 g .. +7
+  // hf = wave & 1, of the sorted components 32 kb + 8 g .. +7.  Positions past
+  // the coded components multiply dequantised zeros (the basis is finite).
   uint4 A[4][KBMAX];
   {
     const int hf = wave & 1;
-    // natural index of the lane's sorted components 32 kb + 8 g .. +7 (-1: none)
-    int idx[KBMAX][8];
-#pragma unroll
-    for (int kb = 0; kb < KBMAX; ++kb)
-#pragma unroll
-      for (int z = 0; z < 8; ++z) {
-        const int k = 32 * kb + 8 * g + z;
-        idx[kb][z] = k < nnz ? (int)s_ki[k].idx : -1;
-      }
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       const int pp = hf + 2 * (mi >> 1), a = mi & 1;
       const uint16_t* brow = bst + (32 * pp + 8 * (r >> 2) + 4 * a + (r & 3)) * kBS;
 #pragma unroll
-      for (int kb = 0; kb < KBMAX; ++kb) {
-        uint32_t w4[4];
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          const int i0 = idx[kb][2 * q2], i1 = idx[kb][2 * q2 + 1];
-          const uint32_t lo = i0 >= 0 ? brow[i0] : 0u;
-          const uint32_t hi = i1 >= 0 ? brow[i1] : 0u;
-          w4[q2] = lo | (hi << 16);
-        }
-        A[mi][kb] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-      }
-      // one channel tile's gathers at a time (bounds the registers in flight)
-      __builtin_amdgcn_sched_barrier(0);
+      for (int kb = 0; kb < KBMAX; ++kb) A[mi][kb] = *reinterpret_cast<const uint4*>(brow + 32 * kb + 8 * g);
     }
   }
   __syncthreads();  // the staged basis area becomes the operand and tile buffers
