@@ -957,6 +957,14 @@ __global__ __launch_bounds__(256, MODE == 0 ? 4 : 1) void k_enc128(const Params 
     }
   };
   auto stage_sub = [&](int buf) {
+    uint16_t* xr = &X[buf][st_t * kXS];
+    if (!rope) {  // the loaded bf16 words as they are
+      *reinterpret_cast<uint4*>(xr + 16 * st_q) = ya0;
+      *reinterpret_cast<uint4*>(xr + 16 * st_q + 8) = ya1;
+      *reinterpret_cast<uint4*>(xr + 64 + 16 * st_q) = yb0;
+      *reinterpret_cast<uint4*>(xr + 64 + 16 * st_q + 8) = yb1;
+      return;
+    }
     float lo[16], hi[16];
     unpack_bf16x8(ya0, lo); unpack_bf16x8(ya1, lo + 8);
     unpack_bf16x8(yb0, hi); unpack_bf16x8(yb1, hi + 8);
@@ -991,7 +999,6 @@ __global__ __launch_bounds__(256, MODE == 0 ? 4 : 1) void k_enc128(const Params 
     o[1] = make_uint4(pack2_bf16(lo[8], lo[9]), pack2_bf16(lo[10], lo[11]), pack2_bf16(lo[12], lo[13]), pack2_bf16(lo[14], lo[15]));
     o[2] = make_uint4(pack2_bf16(hi[0], hi[1]), pack2_bf16(hi[2], hi[3]), pack2_bf16(hi[4], hi[5]), pack2_bf16(hi[6], hi[7]));
     o[3] = make_uint4(pack2_bf16(hi[8], hi[9]), pack2_bf16(hi[10], hi[11]), pack2_bf16(hi[12], hi[13]), pack2_bf16(hi[14], hi[15]));
-    uint16_t* xr = &X[buf][st_t * kXS];
     *reinterpret_cast<uint4*>(xr + 16 * st_q) = o[0];
     *reinterpret_cast<uint4*>(xr + 16 * st_q + 8) = o[1];
     *reinterpret_cast<uint4*>(xr + 64 + 16 * st_q) = o[2];
