@@ -868,7 +868,7 @@ __global__ __launch_bounds__(256) void k_unrope128(const Params p0) {
 constexpr int kXS = 136;  // LDS row stride (bf16) of staged tokens: 16-B aligned, 4-bank shift
 
 template <int MODE>
-__global__ __launch_bounds__(256, MODE == 0 ? 4 : 1) void k_enc128(const Params p0, int sec0, float* coef_out) {
+__global__ __launch_bounds__(256, MODE == 0 ? 3 : 1) void k_enc128(const Params p0, int sec0, float* coef_out) {
   const Params p = at_seq(p0, blockIdx.z);
   if (MODE == 0 && p0.n_seqs == 0 && !p.rope_keys && blockIdx.x == 0 && blockIdx.y == 0) clear_status_block(p);
   constexpr int D = 128;
@@ -929,19 +929,18 @@ __global__ __launch_bounds__(256, MODE == 0 ? 4 : 1) void k_enc128(const Params 
   }
 
   // ---- staging registers and helpers
-  uint4 ya0, ya1, yb0, yb1;
   float4 cs[8];
-  auto load_sub = [&](int sub) {
+  auto load_sub = [&](int sub, uint4 (&y)[4]) {
     const int tok = sub * 64 + st_t;
     const bool valid = tok < n;
     const int pos = p.mid_begin + t0 + tok;
-    ya0 = ya1 = yb0 = yb1 = make_uint4(0, 0, 0, 0);
+    y[0] = y[1] = y[2] = y[3] = make_uint4(0, 0, 0, 0);
     if (valid) {
       const uint16_t* row = src + (pre ? (lh_row0 + pos_base + t0 + tok) * D : cache_row(p, l, h, pos));
-      ya0 = *reinterpret_cast<const uint4*>(row + 16 * st_q);
-      ya1 = *reinterpret_cast<const uint4*>(row + 16 * st_q + 8);
-      yb0 = *reinterpret_cast<const uint4*>(row + 64 + 16 * st_q);
-      yb1 = *reinterpret_cast<const uint4*>(row + 64 + 16 * st_q + 8);
+      y[0] = *reinterpret_cast<const uint4*>(row + 16 * st_q);
+      y[1] = *reinterpret_cast<const uint4*>(row + 16 * st_q + 8);
+      y[2] = *reinterpret_cast<const uint4*>(row + 64 + 16 * st_q);
+      y[3] = *reinterpret_cast<const uint4*>(row + 64 + 16 * st_q + 8);
     }
     if (rope && valid) {
       if (p.rope_style == KVTC_ROPE_HALF) {  // pairs [16q, 16q+16)
@@ -956,18 +955,18 @@ __global__ __launch_bounds__(256, MODE == 0 ? 4 : 1) void k_enc128(const Params 
       }
     }
   };
-  auto stage_sub = [&](int buf) {
+  auto stage_sub = [&](int buf, const uint4 (&y)[4]) {
     uint16_t* xr = &X[buf][st_t * kXS];
     if (!rope) {  // the loaded bf16 words as they are
-      *reinterpret_cast<uint4*>(xr + 16 * st_q) = ya0;
-      *reinterpret_cast<uint4*>(xr + 16 * st_q + 8) = ya1;
-      *reinterpret_cast<uint4*>(xr + 64 + 16 * st_q) = yb0;
-      *reinterpret_cast<uint4*>(xr + 64 + 16 * st_q + 8) = yb1;
+      *reinterpret_cast<uint4*>(xr + 16 * st_q) = y[0];
+      *reinterpret_cast<uint4*>(xr + 16 * st_q + 8) = y[1];
+      *reinterpret_cast<uint4*>(xr + 64 + 16 * st_q) = y[2];
+      *reinterpret_cast<uint4*>(xr + 64 + 16 * st_q + 8) = y[3];
       return;
     }
     float lo[16], hi[16];
-    unpack_bf16x8(ya0, lo); unpack_bf16x8(ya1, lo + 8);
-    unpack_bf16x8(yb0, hi); unpack_bf16x8(yb1, hi + 8);
+    unpack_bf16x8(y[0], lo); unpack_bf16x8(y[1], lo + 8);
+    unpack_bf16x8(y[2], hi); unpack_bf16x8(y[3], hi + 8);
     uint4 o[4];
     if (rope) {
       if (p.rope_style == KVTC_ROPE_HALF) {
@@ -1008,11 +1007,9 @@ __global__ __launch_bounds__(256, MODE == 0 ? 4 : 1) void k_enc128(const Params 
   const int nsub = (n + 63) / 64;
   const int subs_per_tile = p.tile_tokens / 64 > 0 ? p.tile_tokens / 64 : 1;
   uint32_t refined = 0;  // codes re-computed exactly (wave-uniform count)
-  load_sub(0);
-  for (int sub = 0; sub < nsub; ++sub) {
+  // the loop body after staging (sub-tile sub in X[sub & 1])
+  auto body = [&](int sub) {
     const int buf = sub & 1;
-    stage_sub(buf);
-    if (sub + 1 < nsub) load_sub(sub + 1);
     // packed-tile bookkeeping (tile_tokens is a multiple of 64 on this path)
     const int tl = (sub * 64) / p.tile_tokens;
     const int ta = tl * p.tile_tokens;
@@ -1177,6 +1174,30 @@ __global__ __launch_bounds__(256, MODE == 0 ? 4 : 1) void k_enc128(const Params 
         for (uint32_t i = tid; i < sd.row_w[D]; i += 256) dst[i] = tilebuf[i];
         __syncthreads();
       }
+    }
+  };
+  uint4 yA[4], yB[4];
+  if constexpr (MODE == 0) {
+    // rows two sub-tiles ahead in flight: the sub-tile after next is loaded
+    // into the registers just staged
+    load_sub(0, yA);
+    if (1 < nsub) load_sub(1, yB);
+    for (int sub = 0; sub < nsub; sub += 2) {
+      stage_sub(0, yA);
+      if (sub + 2 < nsub) load_sub(sub + 2, yA);
+      body(sub);
+      if (sub + 1 < nsub) {
+        stage_sub(1, yB);
+        if (sub + 3 < nsub) load_sub(sub + 3, yB);
+        body(sub + 1);
+      }
+    }
+  } else {
+    load_sub(0, yA);
+    for (int sub = 0; sub < nsub; ++sub) {
+      stage_sub(sub & 1, yA);
+      if (sub + 1 < nsub) load_sub(sub + 1, yA);
+      body(sub);
     }
   }
   if (MODE == 1 && lane == 0 && refined) atomicAdd(count_slot(p.ws, p.w), refined);
