@@ -535,15 +535,30 @@ __global__ __launch_bounds__(1024) void k_scan(const Params p0, HeaderBytes hdr)
   const int64_t a = tid * per, b = min(n, a + per);
   uint64_t local = 0;
   for (int64_t i = a; i < b; ++i) local += rec_size[i];
-  s_part[tid] = local;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    uint64_t v = tid >= o ? s_part[tid - o] : 0;
-    __syncthreads();
-    s_part[tid] += v;
-    __syncthreads();
+  // inclusive scan: within each wave by shuffles, then over the 16 wave totals
+  const int lane = tid & 63, wave = tid >> 6;
+  uint64_t incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
   }
-  uint64_t run = s_part[tid] - local;
+  __shared__ uint64_t s_wave[16];
+  if (lane == 63) s_wave[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    uint64_t w = lane < 16 ? s_wave[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const uint64_t v = __shfl_up(w, o, 64);
+      if (lane >= o) w += v;
+    }
+    if (lane < 16) s_wave[lane] = w;  // inclusive wave totals
+  }
+  __syncthreads();
+  incl += wave > 0 ? s_wave[wave - 1] : 0;
+  s_part[tid] = incl;
+  uint64_t run = incl - local;
   for (int64_t i = a; i < b; ++i) {
     rec_pos[i] = run;
     uint8_t* d = p.out + p.dir_off + i * kDirEntry;
