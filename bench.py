@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-phase event pass")
     ap.add_argument("--seqs", type=int, default=None, help="sequences of a paged workload")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="time plain read, write and copy kernels over 520 MB (the practical HBM ceilings) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain copy kernel of known size (for scaling HBM counters)")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -199,6 +201,32 @@ def copy_calibration():
     for _ in range(3):
         torch.bitwise_not(x, out=y)
     torch.cuda.synchronize()
+
+
+def ceilings():
+    """Practical HBM rates of plain torch kernels over 520 MiB (about the bytes
+    of one pass over the Llama-3-8B middle): a fill (write) and a copy (read +
+    write, both counted).  Printed as a markdown table."""
+    import torch
+    n = 520 << 20
+    x = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    cases = [("write (fill_)", n, lambda: y.fill_(7)),
+             ("copy (copy_, read + write)", 2 * n, lambda: y.copy_(x))]
+    print("| kernel | bytes moved | us | TB/s |")
+    print("|---|---|---|---|")
+    for name, moved, fn in cases:
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(20):
+            fn()
+        b.record()
+        b.synchronize()
+        us = a.elapsed_time(b) / 20 * 1e3
+        print(f"| {name} | {moved / 1e6:.0f} MB | {us:.1f} | {moved / us / 1e6:.2f} |")
 
 
 def layout(cfg, T):
@@ -393,6 +421,9 @@ def main():
 
     kvtc.lib()  # fail loudly if the HIP library is missing
     torch.cuda.init()
+    if args.ceilings:
+        ceilings()
+        return
     if args.copy_calibration:
         copy_calibration()
     w = synth.WORKLOADS[args.workload]
