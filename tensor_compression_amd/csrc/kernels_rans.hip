@@ -305,7 +305,53 @@ __device__ __forceinline__ bool rans_decode_ring(const uint32_t* states, const u
   // Every step is branch-free apart from the (group-uniform) refill: a
   // corrupt stream may read wrong ring words, which the final state and
   // word-count checks then reject.
-  for (int k = 0; k < steps_max; ++k) {
+  //
+  // Main phase: steps at which every valid lane of the wave decodes a
+  // symbol (no per-lane masks; lanes of an absent tile compute values that
+  // are never used and store past the output's range, where the stores are
+  // dropped).  The refill test runs once per four steps: a group takes at
+  // most LANES words a step, so the ring cannot run short between tests.
+  int kfull = valid ? Nt / LANES : steps_max;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) kfull = min(kfull, __shfl_xor(kfull, o, 64));
+  kfull = __builtin_amdgcn_readfirstlane(min(kfull, steps_max));
+  const int steps_u = __builtin_amdgcn_readfirstlane(steps_max);
+  int32_t voff = valid ? out_off + j : out_end;
+  int k = 0;
+  for (; k + 4 <= kfull; k += 4) {
+    if (valid && clo > 0 && ptr - clo <= kUnit) {
+#pragma unroll
+      for (int q2 = 0; q2 < PER; ++q2) {
+        const int32_t q = plo / 2 + j + LANES * q2;
+        if (q < clo / 2) ring32[q & (kRing / 2 - 1)] = pend[q2];
+      }
+      clo = plo;
+      plo = max(0, clo - kUnit);
+#pragma unroll
+      for (int q2 = 0; q2 < PER; ++q2) {
+        const int32_t q = plo / 2 + j + LANES * q2;
+        pend[q2] = q < clo / 2 ? wd[q] : 0u;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t slot = x & mask;
+      const uint32_t sym = sym_of[slot];
+      const uint32_t e = fc[sym];
+      x = __umul24(e & 0xffffu, x >> sb) + slot - (e >> 16);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sym, orsrc, voff, 0, 0);
+      voff += LANES;
+      const bool need = x < kRansL;
+      const uint64_t bl = __ballot(need);
+      const uint32_t mlo = (uint32_t)bl & gm_lo, mhi = (uint32_t)(bl >> 32) & gm_hi;
+      const uint32_t rank = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
+      const uint32_t w = ring[(uint32_t)(ptr - 1 - (int32_t)rank) & (kRing - 1)];
+      x = need ? ((x << 16) | w) : x;
+      ptr -= (int32_t)(__popc(mlo) + __popc(mhi));
+    }
+  }
+  // the remaining steps, masked per lane
+  for (; k < steps_u; ++k) {
     if (valid && clo > 0 && ptr - clo <= kUnit) {
       // the ring slots of [plo, clo) held words >= clo + kUnit >= ptr: consumed
 #pragma unroll
