@@ -11,6 +11,8 @@
 // decoder walks forward, lanes ascending, consuming words from the end.
 #include <string.h>
 
+#include <type_traits>
+
 #include "kvtc_internal.h"
 
 namespace kvtc {
@@ -195,13 +197,22 @@ __device__ __forceinline__ int64_t rans_encode_stream(const uint8_t* sbase, int3
   // the table entry of the next step is read a step ahead (ring slot d + 1
   // holds the next step's symbol, slot 0 the next block's after its refill)
   EncSym en = tab[ring[0]];
-  for (int k0 = kt - 1; k0 >= 0; k0 -= PF) {
+  // Blocks of PF steps from the last step down.  Steps below kfull have a
+  // symbol for every lane of a present tile, so their blocks skip the
+  // per-lane step masks (lanes of an absent tile never emit, and their state
+  // is not stored).
+  int kfull = valid ? Nt / lanes : kt;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) kfull = min(kfull, __shfl_xor(kfull, o, 64));
+  kfull = __builtin_amdgcn_readfirstlane(kfull);
+  auto block = [&](auto masked_tag, int k0) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
 #pragma unroll
     for (int d = 0; d < PF; ++d) {
       const int k = k0 - d;
       {
         const int32_t i = k * lanes + j;
-        const bool active = valid && i < Nt;
+        const bool active = MASKED ? (valid && i < Nt) : valid;
         const EncSym e = en;
         // refill after the last use so the load can reuse the same register
         ring[d] = fetch(k - PF);
@@ -222,12 +233,15 @@ __device__ __forceinline__ int64_t rans_encode_stream(const uint8_t* sbase, int3
         // x = floor(x / f) * M + (x mod f) + cum, via an exact fp64 quotient
         const uint32_t q = (uint32_t)__fma_rn((double)x, e.rcp, 0x1p-20);
         const uint32_t xn = x + e.cum + q * (M - e.f);
-        x = active ? xn : x;
+        x = MASKED ? (active ? xn : x) : xn;
         // keep the steps in order so that each ring register is refilled in place
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-  }
+  };
+  int k0 = kt - 1;
+  for (; k0 >= 0 && k0 >= kfull; k0 -= PF) block(std::true_type{}, k0);
+  for (; k0 >= 0; k0 -= PF) block(std::false_type{}, k0);
   if (valid) state_out[j] = x;
   const uint64_t ov = __ballot(overflow) & gm;
   return ov ? -1 : nw;
