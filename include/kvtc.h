@@ -259,7 +259,8 @@ kvtc_status kvtc_test_coeffs(kvtc_plan_t plan, const void* k, const void* v, int
 /* One interleaved rANS stream with the device coder: encode N bytes `sym`
  * with table `freq` (u16[256], sums to 2^scale_bits) into states u32[lanes]
  * and words u16[words_cap] (emission order), word count to *nwords (device
- * int64).  All pointers are device memory. */
+ * int64).  All pointers are device memory.  N must be below 2^30
+ * (KVTC_ERR_INVALID_ARG otherwise); a words_cap above 2^30 acts as 2^30. */
 kvtc_status kvtc_test_rans_encode(const uint8_t* sym, int64_t N, const uint16_t* freq,
                                   int32_t scale_bits, int32_t lanes, uint32_t* states,
                                   uint16_t* words, int64_t words_cap, int64_t* nwords,

@@ -163,7 +163,7 @@ __device__ void build_enc_table(const uint32_t* freq, EncSym* tab) {
 // word count (uniform within the group) or -1 when the capacity is exceeded.
 __device__ __forceinline__ int64_t rans_encode_stream(const uint8_t* sbase, int32_t sbytes, int32_t soff, int32_t Nt,
                                                       bool valid, int steps_max, const EncSym* tab, int sb, int lanes,
-                                                      uint8_t* wbase, int32_t wbytes, int32_t woff, int64_t wcap,
+                                                      uint8_t* wbase, int32_t wbytes, int32_t woff, int32_t wcap,
                                                       uint32_t* state_out) {
   // Symbols come from sbase + soff + i and words go to wbase + woff + 2 at,
   // both through buffer resources whose range check turns the accesses of
@@ -186,6 +186,10 @@ __device__ __forceinline__ int64_t rans_encode_stream(const uint8_t* sbase, int3
   auto fetch = [&](int k) -> uint32_t {
     const int32_t i = k * lanes + j;
     return __builtin_amdgcn_raw_buffer_load_b8(srsrc, (valid && k >= 0 && i < Nt) ? soff + i : sbytes, 0, 0);
+  };
+  // the same for a step below kfull (every lane of a present tile has a symbol)
+  auto fetch_full = [&](int k) -> uint32_t {
+    return __builtin_amdgcn_raw_buffer_load_b8(srsrc, (valid && k >= 0) ? soff + k * lanes + j : sbytes, 0, 0);
   };
   // Steps are padded up to a multiple of PF (the padding steps hold no
   // symbol for any lane) so that the unrolled body has no branch: a branch
@@ -215,7 +219,7 @@ __device__ __forceinline__ int64_t rans_encode_stream(const uint8_t* sbase, int3
         const bool active = MASKED ? (valid && i < Nt) : valid;
         const EncSym e = en;
         // refill after the last use so the load can reuse the same register
-        ring[d] = fetch(k - PF);
+        ring[d] = MASKED ? fetch(k - PF) : fetch_full(k - PF);
         en = tab[ring[(d + 1) % PF]];
         // renormalise while x >= f 2^(32 - sb): one 16-bit word at most
         const bool emit = active && (x >> (32 - sb)) >= e.f;
@@ -232,7 +236,8 @@ __device__ __forceinline__ int64_t rans_encode_stream(const uint8_t* sbase, int3
         nw += cnt;
         // x = floor(x / f) * M + (x mod f) + cum, via an exact fp64 quotient
         const uint32_t q = (uint32_t)__fma_rn((double)x, e.rcp, 0x1p-20);
-        const uint32_t xn = x + e.cum + q * (M - e.f);
+        // q < 2^(32 - sb) <= 2^24 and M - f < 2^12: a 24-bit product
+        const uint32_t xn = x + e.cum + __umul24(q, M - e.f);
         x = MASKED ? (active ? xn : x) : xn;
         // keep the steps in order so that each ring register is refilled in place
         __builtin_amdgcn_sched_barrier(0);
@@ -897,7 +902,7 @@ __global__ void k_test_rans_encode(const uint8_t* sym, int64_t N, const uint16_t
   const bool valid = lane < lanes;  // one stream in the first lane group
   const int steps = (int)((N + lanes - 1) / lanes);
   int64_t nw = rans_encode_stream(sym, (int32_t)N, 0, (int32_t)N, valid, steps, tab, sb, lanes,
-                                  reinterpret_cast<uint8_t*>(words), (int32_t)(2 * cap), 0, cap, states);
+                                  reinterpret_cast<uint8_t*>(words), (int32_t)(2 * cap), 0, (int32_t)cap, states);
   if (lane == 0) *nwords = nw;
 }
 

@@ -626,6 +626,9 @@ kvtc_status kvtc_test_rans_encode(const uint8_t* sym, int64_t N, const uint16_t*
                                   hipStream_t stream) {
   if ((N > 0 && !sym) || !freq || !states || !words || !nwords || N < 0) return KVTC_ERR_INVALID_ARG;
   if (scale_bits < 8 || scale_bits > 12 || (lanes != 16 && lanes != 32)) return KVTC_ERR_UNSUPPORTED;
+  if (N >= (1ll << 30) || words_cap < 0) return KVTC_ERR_INVALID_ARG;
+  // the capacity is an upper bound on the words written: larger values act as 2^30
+  if (words_cap > (1ll << 30)) words_cap = 1ll << 30;
   HIP_TRY(launch_test_rans_encode(sym, N, freq, scale_bits, lanes, states, words, words_cap,
                                   nwords, stream));
   return KVTC_OK;
