@@ -71,11 +71,19 @@ __device__ void wave_freq_normalize(const uint32_t* counts, int sb, uint32_t* fr
     return;
   }
   uint64_t local = 0;
+  // floor((n 2M + N) / 2N): the quotient from one fp64 reciprocal of the
+  // common divisor (numerator < 2^53, so exact in fp64), off by at most one
+  // and corrected in integers
+  const uint64_t div = 2 * N;
+  const double inv = 1.0 / (double)div;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     if (n[k] == 0) f[k] = 0;
     else {
-      uint64_t r = ((uint64_t)n[k] * (2 * M) + N) / (2 * N);
+      const uint64_t a = (uint64_t)n[k] * (2 * M) + N;
+      uint64_t r = (uint64_t)((double)a * inv);
+      if (r * div > a) --r;
+      else if ((r + 1) * div <= a) ++r;
       f[k] = r < 1 ? 1 : r;
     }
     local += f[k];
@@ -93,13 +101,15 @@ __device__ void wave_freq_normalize(const uint32_t* counts, int sb, uint32_t* fr
   } else if (d < 0) {
     const uint64_t R = (uint64_t)(-d);
     // smallest tau >= 1 with E(tau) = sum max(0, f - tau) <= R
-    uint64_t lo = 1, hi = M;  // E(M) = 0 <= R
+    // (f <= 2^13, so E <= 2^21 sums in 32 bits)
+    uint32_t lo = 1, hi = (uint32_t)M;  // E(M) = 0 <= R
     while (lo < hi) {
-      uint64_t mid = (lo + hi) >> 1;
-      uint64_t e = 0;
+      const uint32_t mid = (lo + hi) >> 1;
+      uint32_t e = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) e += f[k] > mid ? f[k] - mid : 0;
-      e = wave_sum64(e);
+      for (int k = 0; k < 4; ++k) e += (uint32_t)f[k] > mid ? (uint32_t)f[k] - mid : 0u;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) e += (uint32_t)__shfl_xor((int)e, o, 64);
       if (e <= R) hi = mid; else lo = mid + 1;
     }
     const uint64_t tau = lo;
@@ -408,12 +418,6 @@ __device__ __forceinline__ bool rans_decode_ring(const uint32_t* states, const u
 
 // ---- per-chunk encoder ------------------------------------------------------
 
-__device__ __forceinline__ int64_t tile_bytes(const uint8_t* bits, int D, int ntok) {
-  int64_t P = 0;
-  for (int i = 0; i < D; ++i) P += 4 * (int64_t)((ntok * (int)bits[i] + 31) >> 5);
-  return P;
-}
-
 // record slot of chunk c: [freq u16 x256][nwords u32 x tiles][tile t: states, words]
 __device__ __forceinline__ int64_t slot_states_off(const Params& p, int t) {
   // 16-byte aligned: 4 lanes and 2 tile_words_max + 4 are multiples of 16
@@ -445,9 +449,15 @@ __global__ void k_rans_enc_chunks(const Params p0, int raw_runs) {
   const int n = min(p.chunk_tokens, p.T_mid - ch * p.chunk_tokens);
   const int ntiles = (n + p.tile_tokens - 1) / p.tile_tokens;
   const int n_last = n - (ntiles - 1) * p.tile_tokens;
-  if (threadIdx.x == 0) {
-    s_P[0] = tile_bytes(bits, D, p.tile_tokens);
-    s_P[1] = tile_bytes(bits, D, n_last);
+  if (wave == 0) {  // packed bytes of a full and of the last tile
+    int64_t pf = 0, pl = 0;
+    for (int i = lane; i < D; i += 64) {
+      pf += 4 * (int64_t)((p.tile_tokens * (int)bits[i] + 31) >> 5);
+      pl += 4 * (int64_t)((n_last * (int)bits[i] + 31) >> 5);
+    }
+    pf = (int64_t)wave_sum64((uint64_t)pf);
+    pl = (int64_t)wave_sum64((uint64_t)pl);
+    if (lane == 0) { s_P[0] = pf; s_P[1] = pl; }
   }
   __syncthreads();
   const int64_t P_full = s_P[0], P_last = s_P[1];
