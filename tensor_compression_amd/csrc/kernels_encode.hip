@@ -1033,22 +1033,22 @@ __global__ __launch_bounds__(256, MODE == 0 ? 3 : 1) void k_enc128(const Params 
     // loads stay in flight)
     if constexpr (MODE == 1) __syncthreads();
     else lds_barrier();
-    f32x4_t acc[4][2];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      acc[kk][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      acc[kk][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // the 16-token groups kk of the sub-tile: tokens 16 kk + r as A rows
+    auto project = [&](int kk, f32x4_t (&a2)[2]) {
+      a2[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      a2[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const uint4 a = *reinterpret_cast<const uint4*>(&X[buf][(kk * 16 + r) * kXS + kb * 32 + 8 * g]);
         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
 #pragma unroll
         for (int m = 0; m < 2; ++m)
-          acc[kk][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bq[m][kb]),
-                                                               acc[kk][m], 0, 0, 0);
+          a2[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bq[m][kb]), a2[m], 0, 0, 0);
       }
-    }
+    };
     if constexpr (MODE == 0) {
+      // each group is folded into the statistics right after its products
+      // (eight accumulator registers live, not 32), in the same order
       // min / max as med3 against -inf / +inf: one instruction each (finite
       // coefficients; non-finite inputs are caught by the fp64 sums)
       auto accumulate = [&](float c, int m) {
@@ -1057,24 +1057,31 @@ __global__ __launch_bounds__(256, MODE == 0 ? 3 : 1) void k_enc128(const Params 
         mn[m] = __builtin_amdgcn_fmed3f(c, mn[m], -INFINITY);
         mx[m] = __builtin_amdgcn_fmed3f(c, mx[m], INFINITY);
       };
-      if (sub * 64 + 64 <= n) {  // a full sub-tile
+      const bool full_sub = sub * 64 + 64 <= n;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+      for (int kk = 0; kk < 4; ++kk) {
+        f32x4_t a2[2];
+        project(kk, a2);
+        if (full_sub) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int m = 0; m < 2; ++m) accumulate(acc[kk][m][e], m);
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+            for (int m = 0; m < 2; ++m) accumulate(a2[m][e], m);
+        } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             if (sub * 64 + kk * 16 + 4 * g + e < n) {
 #pragma unroll
-              for (int m = 0; m < 2; ++m) accumulate(acc[kk][m][e], m);
+              for (int m = 0; m < 2; ++m) accumulate(a2[m][e], m);
             }
+        }
       }
-    } else if constexpr (MODE == 2) {
+      return;
+    }
+    f32x4_t acc[4][2];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) project(kk, acc[kk]);
+    if constexpr (MODE == 2) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
