@@ -60,6 +60,14 @@ __device__ __forceinline__ int fresh_lane() {
 // tile) the flagged codes are queued, and the queue is worked off at the end
 // of the tile, or when it fills up, with all its loads in flight together.
 constexpr int kQCap = 128;
+// fl * 2 + (|d| > bnd): the compare's lane mask is the carry-in of one
+// add-with-carry (false for a NaN d, like the C comparison)
+__device__ __forceinline__ uint32_t shift_in_flag(uint32_t fl, float d, float bnd) {
+  uint32_t r;
+  asm("v_cmp_gt_f32_e64 vcc, |%1|, %2\n\tv_addc_co_u32_e32 %0, vcc, %3, %3, vcc" : "=v"(r) : "v"(d), "v"(bnd), "v"(fl) : "vcc");
+  return r;
+}
+
 __global__ __launch_bounds__(64 * kQWaves, 4) void k_quant128(const Params p0) {
   const Params p = at_seq(p0, blockIdx.z);
   constexpr int D = 128;
@@ -329,15 +337,19 @@ __global__ __launch_bounds__(64 * kQWaves, 4) void k_quant128(const Params p0) {
             const float sv = __fadd_rn(vc, 0x1p23f);  // rint(vc), nearest even, in the low bits
             uq[e] = __float_as_uint(sv);
             const float d = __fsub_rn(vc, __fsub_rn(sv, 0x1p23f));
-            const bool nr = in && fabsf(d) > bnd;
-            fl[hh] = fl[hh] + fl[hh] + (nr ? 1u : 0u);
+            if constexpr (FULL) {
+              fl[hh] = shift_in_flag(fl[hh], d, bnd);
+            } else {
+              const bool nr = in && fabsf(d) > bnd;
+              fl[hh] = fl[hh] + fl[hh] + (nr ? 1u : 0u);
+            }
           }
           // four codes -> one 4b-bit piece (the exponent bits cancel in kb)
           pc[hh] = uq[0] + (uq[1] << b) + (uq[2] << (2 * b)) + (uq[3] << (3 * b)) - qu.y;
         }
         // eight codes (8b bits) at bit (32 P + 8 g) b of the component's row
         const uint64_t piece = (uint64_t)pc[0] | ((uint64_t)pc[1] << (4 * b));
-        const uint32_t bitoff = (uint32_t)(32 * P + 8 * g) * b, sh = bitoff & 31;
+        const uint32_t bitoff = __umul24((uint32_t)(32 * P + 8 * g), b), sh = bitoff & 31;
         const uint32_t wi = qu.z + (bitoff >> 5);
         const uint64_t w01 = piece << sh;
         const uint32_t w2 = (uint32_t)(((piece >> 32) << sh) >> 32);
