@@ -767,10 +767,13 @@ __global__ void k_rans_dec_chunks(const Params p0, int raw_runs) {
   const int u = c / p.chunks_per_sec, ch = c % p.chunks_per_sec;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (get_status(p.ws, p.w) & (1u << KVTC_ERR_CORRUPT)) return;
+  // the decode tables at fixed LDS addresses (their base folds into the
+  // instructions' offsets); the word rings in dynamic LDS
+  __shared__ uint32_t fc[256];
+  __shared__ uint32_t s_sym[1024];  // one byte per slot, 2^sb <= 4096 slots
+  uint8_t* sym_of = reinterpret_cast<uint8_t*>(s_sym);
   extern __shared__ uint32_t lds[];
-  uint32_t* fc = lds;                                                     // 256 entries
-  uint8_t* sym_of = reinterpret_cast<uint8_t*>(lds + 256);                // 2^sb bytes
-  uint16_t* rings = reinterpret_cast<uint16_t*>(sym_of + (1 << p.sb));    // kRing words per tile
+  uint16_t* rings = reinterpret_cast<uint16_t*>(lds);                     // kRing words per tile
   __shared__ int64_t s_info[4];
   __shared__ uint32_t s_cum[257];
   __shared__ int s_ok;
@@ -890,8 +893,8 @@ hipError_t launch_rans_decode_chunks(const Params& p, hipStream_t s, bool with_r
   int streams = p.tiles_per_chunk;
   int waves = (streams * p.lanes + 63) / 64;
   if (waves < 1) waves = 1;
-  // LDS: the symbol tables and one word ring per tile
-  const size_t lds = 1024 + (size_t)(1u << p.sb) + (size_t)p.tiles_per_chunk * kRing * 2;
+  // dynamic LDS: one word ring per tile (the symbol tables are static)
+  const size_t lds = (size_t)p.tiles_per_chunk * kRing * 2;
   const int raw_runs = with_raw && p.n_seqs == 0 ? 4 * p.L * p.H : 0;
   hipLaunchKernelGGL(k_rans_dec_chunks, dim3(p.n_chunks + raw_runs, 1, seq_grid(p)), dim3(64 * waves), lds, s, p, raw_runs);
   return hipGetLastError();
