@@ -662,14 +662,60 @@ __global__ __launch_bounds__(1024) void k_scan(const Params p0, HeaderBytes hdr)
   }
 }
 
-__global__ __launch_bounds__(256) void k_copy_records(const Params p0) {
+// scan = 1 (a contiguous call with chunks): each workgroup sums the sizes of
+// the records before its own (at most a few KB, cached) instead of reading
+// k_scan's offsets, writes its directory entry, and the last one writes the
+// header, the container size and the status word, as k_scan does.
+__global__ __launch_bounds__(256) void k_copy_records(const Params p0, HeaderBytes hdr, int scan) {
   const Params p = at_seq(p0, blockIdx.z);
   const int c = blockIdx.x;
   if (c >= p.n_chunks) return;
+  const uint32_t* rec_size = reinterpret_cast<const uint32_t*>(p.ws + p.w.rec_size);
+  const uint32_t size = rec_size[c];
+  uint64_t pos;
+  if (scan) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint64_t part = 0;
+    for (int i = tid; i < c; i += 256) part += rec_size[i];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+    __shared__ uint64_t s_part[4];
+    if (lane == 0) s_part[wave] = part;
+    __syncthreads();
+    pos = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+    if (tid == 0) {
+      reinterpret_cast<uint64_t*>(p.ws + p.w.rec_pos)[c] = pos;
+      uint8_t* d = p.out + p.dir_off + (int64_t)c * kDirEntry;
+      *reinterpret_cast<uint64_t*>(d) = (uint64_t)p.chunks_off + pos;
+      *reinterpret_cast<uint32_t*>(d + 8) = size;
+      *reinterpret_cast<uint32_t*>(d + 12) = 0;
+    }
+    if (c == p.n_chunks - 1) {
+      const uint64_t total = (uint64_t)p.chunks_off + pos + size;
+      if (tid < kHeaderBytes / 4) {
+        uint32_t wv = header_word(p, hdr, tid);
+        if (tid == 42) wv = (uint32_t)total;
+        if (tid == 43) wv = (uint32_t)(total >> 32);
+        reinterpret_cast<uint32_t*>(p.out)[tid] = wv;
+      }
+      if (tid == 0) {
+        uint64_t* st = reinterpret_cast<uint64_t*>(p.ws + p.w.status);
+        if (total > (uint64_t)p.cap) {
+          set_status(p.ws, p.w, KVTC_ERR_CAPACITY);
+          st[1] = 0;
+        } else {
+          st[1] = (get_status(p.ws, p.w) & ((1u << KVTC_ERR_NONFINITE) | (1u << KVTC_ERR_CAPACITY))) ? 0 : total;
+        }
+      }
+    }
+    // a record that does not fit is not copied (the last workgroup reports
+    // the capacity error)
+    if ((uint64_t)p.chunks_off + pos + size > (uint64_t)p.cap) return;
+  } else {
+    pos = reinterpret_cast<const uint64_t*>(p.ws + p.w.rec_pos)[c];
+  }
   if (get_status(p.ws, p.w) & ((1u << KVTC_ERR_CAPACITY) | (1u << KVTC_ERR_NONFINITE))) return;
-  const uint32_t size = reinterpret_cast<const uint32_t*>(p.ws + p.w.rec_size)[c];
   if (size == 0) return;
-  const uint64_t pos = reinterpret_cast<const uint64_t*>(p.ws + p.w.rec_pos)[c];
   const uint8_t* slot = p.ws + p.w.rec + (int64_t)c * p.w.rec_slot;
   uint8_t* dst = p.out_final + p.chunks_off + pos;  // 16-byte aligned record
   const int ch = c % p.chunks_per_sec;
@@ -710,13 +756,18 @@ __global__ __launch_bounds__(256) void k_copy_records(const Params p0) {
 hipError_t launch_assemble(const Params& p, const uint8_t* hdr, hipStream_t s) {
   HeaderBytes h;
   memcpy(h.b, hdr, kHeaderBytes);
+  if (p.n_seqs == 0 && p.n_chunks > 0) {
+    // one launch: offsets, directory, header and records
+    hipLaunchKernelGGL(k_copy_records, dim3(p.n_chunks), dim3(256), 0, s, p, h, 1);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_scan, dim3(1, 1, seq_grid(p)), dim3(1024), 0, s, p, h);
   if (p.n_seqs > 0) {
     // place the sequences, then move each one's staged fixed part and records
     const hipError_t e = launch_batch_place(p, s);
     if (e != hipSuccess) return e;
   }
-  if (p.n_chunks > 0) hipLaunchKernelGGL(k_copy_records, dim3(p.n_chunks, 1, seq_grid(p)), dim3(256), 0, s, p);
+  if (p.n_chunks > 0) hipLaunchKernelGGL(k_copy_records, dim3(p.n_chunks, 1, seq_grid(p)), dim3(256), 0, s, p, h, 0);
   return hipGetLastError();
 }
 
