@@ -232,6 +232,35 @@ def test_damaged_containers_are_refused():
     assert orc.decode_status(cfg, bytes(bad), basis, T) == orc.ERR_CORRUPT
 
 
+def test_short_output_reports_capacity():
+    """An output with room for the header, directory and raw windows but not
+    for every record: the device reports KVTC_ERR_CAPACITY and no container
+    size, and writes nothing past the capacity it was given."""
+    cfg, T, K, V, k, v, basis, plan = _setup("llama3_8b", tokens=1200, layers=1)
+    data, st, ws = _encode(plan, K, V)
+    assert st == kvtc.OK
+    pc = orc.parse_container(data, cfg, T)
+    chunks_off = int(pc["chunks_off"])
+    assert len(data) > chunks_off + 64
+    for cap in (chunks_off, (chunks_off + len(data)) // 2, len(data) - 1):
+        buf = torch.full((len(data) + 4096,), 0xA5, dtype=torch.uint8, device="cuda")
+        ws2 = plan.workspace(T)
+        plan.encode_async(K, V, buf[:cap], ws2)
+        torch.cuda.synchronize()
+        n, st2 = plan.result(ws2)
+        assert st2 == kvtc.ERR_CAPACITY, (cap, st2)
+        assert n == 0
+        assert bool((buf[cap:] == 0xA5).all()), cap
+    # the full capacity still encodes the same container
+    buf = torch.full((len(data),), 0xA5, dtype=torch.uint8, device="cuda")
+    ws3 = plan.workspace(T)
+    plan.encode_async(K, V, buf, ws3)
+    torch.cuda.synchronize()
+    n, st3 = plan.result(ws3)
+    assert st3 == kvtc.OK and n == len(data)
+    assert buf.cpu().numpy().tobytes() == data
+
+
 def test_nonfinite_middle_is_reported():
     cfg, T, K, V, k, v, basis, plan = _setup("llama3_8b", tokens=600, layers=1)
     K2 = K.clone()
