@@ -17,7 +17,7 @@
 
 namespace kvtc {
 
-struct EncSym {
+struct alignas(16) EncSym {  // one 16-byte LDS read per lookup
   uint32_t f;
   uint32_t cum;
   double rcp;     // 1/f rounded to fp64; quotient = trunc(fma(x, rcp, 2^-20))
@@ -210,7 +210,16 @@ __device__ __forceinline__ int64_t rans_encode_stream(const uint8_t* sbase, int3
   for (int d = 0; d < PF; ++d) ring[d] = fetch(kt - 1 - d);
   // the table entry of the next step is read a step ahead (ring slot d + 1
   // holds the next step's symbol, slot 0 the next block's after its refill)
-  EncSym en = tab[ring[0]];
+  // table entries as one 16-byte LDS read (its offset field takes the table's base)
+  auto entry = [&](uint32_t sym) -> EncSym {
+    const uint4 q = reinterpret_cast<const uint4*>(tab)[sym];
+    EncSym e;
+    e.f = q.x;
+    e.cum = q.y;
+    e.rcp = __hiloint2double((int)q.w, (int)q.z);
+    return e;
+  };
+  EncSym en = entry(ring[0]);
   // Blocks of PF steps from the last step down.  Steps below kfull have a
   // symbol for every lane of a present tile, so their blocks skip the
   // per-lane step masks (lanes of an absent tile never emit, and their state
@@ -230,7 +239,7 @@ __device__ __forceinline__ int64_t rans_encode_stream(const uint8_t* sbase, int3
         const EncSym e = en;
         // refill after the last use so the load can reuse the same register
         ring[d] = MASKED ? fetch(k - PF) : fetch_full(k - PF);
-        en = tab[ring[(d + 1) % PF]];
+        en = entry(ring[(d + 1) % PF]);
         // renormalise while x >= f 2^(32 - sb): one 16-bit word at most
         const bool emit = active && (x >> (32 - sb)) >= e.f;
         const uint64_t bl = __ballot(emit);
