@@ -272,29 +272,51 @@ __device__ __forceinline__ int64_t rans_encode_stream(const uint8_t* sbase, int3
 }
 
 // Decoder tables from the cumulative frequencies (cum[256] = 2^sb): the
-// symbol of every slot (one byte each) and, per symbol, f | cum << 16.  Each
-// thread fills a run of consecutive slots, locating the run's first symbol
-// by binary search and walking on.
+// symbol of every slot (one byte each) and, per symbol, f | cum << 16.  Every
+// present symbol marks the first slot of its range; since symbols ascend
+// with their ranges, the symbol of a slot is the running maximum of the marks
+// up to it.  Each thread takes a run of whole words, and the maxima of the
+// earlier runs come from a block scan, so no step depends on the data.
+// Called by every thread of the block (it synchronises the block).
 __device__ __forceinline__ void build_dec_tables(const uint32_t* cum, int sb, uint8_t* sym_of, uint32_t* fc) {
-  for (int s = threadIdx.x; s < 256; s += blockDim.x) fc[s] = (cum[s + 1] - cum[s]) | (cum[s] << 16);
-  const int nslots = 1 << sb;
-  const int per = (nslots / 4 + (int)blockDim.x - 1) / (int)blockDim.x * 4;  // whole words
-  const int s0 = threadIdx.x * per, s1 = min(nslots, s0 + per);
-  if (s0 >= s1) return;
-  int lo = 0, hi = 255;  // symbol s with cum[s] <= s0 < cum[s+1]
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cum[mid] <= (uint32_t)s0) lo = mid; else hi = mid - 1;
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
+  for (int s = tid; s < 256; s += nt) fc[s] = (cum[s + 1] - cum[s]) | (cum[s] << 16);
+  const int nw = (1 << sb) >> 2;  // words of the slot table
+  uint32_t* w = reinterpret_cast<uint32_t*>(sym_of);
+  for (int i = tid; i < nw; i += nt) w[i] = 0u;
+  __syncthreads();
+  for (int s = tid; s < 256; s += nt)
+    if (cum[s + 1] > cum[s]) sym_of[cum[s]] = (uint8_t)s;
+  __syncthreads();
+  const int per = (nw + nt - 1) / nt;
+  const int w0 = min(nw, tid * per), w1 = min(nw, w0 + per);
+  uint32_t m = 0;
+  for (int i = w0; i < w1; ++i) {
+    const uint32_t v = w[i];
+    m = max(m, max(max(v & 0xffu, (v >> 8) & 0xffu), max((v >> 16) & 0xffu, v >> 24)));
   }
-  uint32_t cnext = cum[lo + 1];
-  for (int slot = s0; slot < s1; slot += 4) {
-    uint32_t w = 0;
+  // the maximum over the runs before this thread's
+  uint32_t inc = m;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc = max(inc, y);
+  }
+  __shared__ uint32_t s_wmax[16];
+  if (lane == 63) s_wmax[wave] = inc;
+  __syncthreads();
+  uint32_t run = __shfl_up(inc, 1, 64);
+  if (lane == 0) run = 0u;
+  for (int v2 = 0; v2 < wave; ++v2) run = max(run, s_wmax[v2]);
+  for (int i = w0; i < w1; ++i) {
+    const uint32_t v = w[i];
+    uint32_t o4 = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      while (cnext <= (uint32_t)(slot + b)) { ++lo; cnext = cum[lo + 1]; }
-      w |= (uint32_t)lo << (8 * b);
+      run = max(run, (v >> (8 * b)) & 0xffu);
+      o4 |= run << (8 * b);
     }
-    reinterpret_cast<uint32_t*>(sym_of)[slot >> 2] = w;
+    w[i] = o4;
   }
 }
 
