@@ -191,7 +191,6 @@ __device__ __forceinline__ int64_t rans_encode_stream(const uint8_t* sbase, int3
   const uint32_t M = 1u << sb;
   uint32_t x = kRansL;
   int32_t nw = 0;
-  bool overflow = false;
   constexpr int PF = 8;
   auto fetch = [&](int k) -> uint32_t {
     const int32_t i = k * lanes + j;
@@ -249,7 +248,6 @@ __device__ __forceinline__ int64_t rans_encode_stream(const uint8_t* sbase, int3
         const int32_t below = (int32_t)__builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
         const int32_t at = nw + cnt - 1 - below;
         const bool fits = at < wcap;
-        overflow |= emit && !fits;
         __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(x & 0xffffu), wrsrc, (emit && fits) ? woff + 2 * at : wbytes, 0, 0);
         if (emit) x >>= 16;
         nw += cnt;
@@ -267,8 +265,9 @@ __device__ __forceinline__ int64_t rans_encode_stream(const uint8_t* sbase, int3
   for (; k0 >= 0 && k0 >= kfull; k0 -= PF) block(std::true_type{}, k0);
   for (; k0 >= 0; k0 -= PF) block(std::false_type{}, k0);
   if (valid) state_out[j] = x;
-  const uint64_t ov = __ballot(overflow) & gm;
-  return ov ? -1 : nw;
+  // every word of the group went below its final count nw, so one went past
+  // the capacity exactly when nw exceeds it (those stores were dropped)
+  return nw > wcap ? -1 : nw;
 }
 
 // Decoder tables from the cumulative frequencies (cum[256] = 2^sb): the
