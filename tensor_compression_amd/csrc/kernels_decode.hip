@@ -512,8 +512,10 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
         }
       }
       // ---- dequantise: lane = token sub*64 + lane of the tile, octets w, w+4, ...
-      // Branch-free per component (entries past the coded components are
-      // all zero and yield 0), so the table reads can be issued ahead.
+      // One wave-uniform branch per octet on its width class (one width,
+      // mixed widths, no coded component); inside an octet every component
+      // is branch-free (entries past the coded components are all zero and
+      // yield 0), so its table and code-word reads are issued together.
 #pragma unroll 1
       for (int j8 = 0; j8 < KB; ++j8) {
         const int c8 = 4 * j8 + wave;
