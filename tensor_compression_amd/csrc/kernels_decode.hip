@@ -455,8 +455,20 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
     const uint32_t bl = __builtin_amdgcn_readfirstlane(s_ki[8 * c8 + 7].b);
     oct_w |= (bf == bl ? bf : 0xffu) << (8 * j8);
   }
+  // Two tile buffers: the next tile is loaded straight into the other one
+  // (no registers) once the current tile's last dequantisation is done, and
+  // waited for at its start.
+  uint32_t* const tb2 = reinterpret_cast<uint32_t*>(stage + 64 * 17);
+  bool pf = false;  // the current tile's 16-byte words were loaded ahead
+  auto tile_words = [&](int ntok) -> uint32_t {
+    uint32_t w = ((uint32_t)(ntok * (int)s_b[2 * lane] + 31) >> 5) + ((uint32_t)(ntok * (int)s_b[2 * lane + 1] + 31) >> 5);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) w += __shfl_xor(w, o, 64);
+    return w;
+  };
   for (int ta = 0; ta < n; ta += p.tile_tokens) {
     const int nt = min(p.tile_tokens, n - ta);
+    uint32_t* const tbc = ((ta / p.tile_tokens) & 1) ? tb2 : tb;
     lds_barrier();  // the previous tile's buffer and operands are consumed
     // row offsets of this tile (natural order, scanned), stored by sorted
     // position together with the width and the dequantisation constants;
@@ -486,13 +498,18 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
       const uint32_t* src = slot + (int64_t)(ta / p.tile_tokens) * fw;
       const bool al = ((reinterpret_cast<uintptr_t>(src) & 15u) == 0);
       const uint32_t n4 = al ? tw >> 2 : 0u;
-      for (uint32_t i = tid; i < n4; i += 256) reinterpret_cast<uint4*>(tb)[i] = reinterpret_cast<const uint4*>(src)[i];
-      for (uint32_t i = 4 * n4 + tid; i < tw; i += 256) tb[i] = src[i];
-      if (tid < 4) tb[tw + tid] = 0u;
+      if (pf) {
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of the tile have landed
+      } else {
+        for (uint32_t i = tid; i < n4; i += 256) reinterpret_cast<uint4*>(tbc)[i] = reinterpret_cast<const uint4*>(src)[i];
+      }
+      for (uint32_t i = 4 * n4 + tid; i < tw; i += 256) tbc[i] = src[i];
+      if (tid < 4) tbc[tw + tid] = 0u;
     }
+    pf = false;
     lds_barrier();
 
-    lds_byte_t* const tb3 = (lds_byte_t*)tb;  // the tile buffer in the LDS address space
+    lds_byte_t* const tb3 = (lds_byte_t*)tbc;  // the tile buffer in the LDS address space
     for (int sub = 0; sub * 64 < nt; ++sub) {
       // RoPE table entries of this wave's two 16-token groups, in flight
       // during the dequantisation (a row is 64 pairs of cos, sin: 512 bytes;
@@ -591,6 +608,21 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
         cq[((c8 >> 2) * 4 + (lane >> 4)) * 64 + (c8 & 3) * 16 + (lane & 15)] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
       }
       lds_barrier();
+      if ((sub + 1) * 64 >= nt && ta + p.tile_tokens < n) {
+        // the other buffer held the previous tile, consumed before this one
+        // started: the next tile's 16-byte words go there directly
+        const uint32_t* nsrc = slot + (int64_t)(ta / p.tile_tokens + 1) * fw;
+        if ((reinterpret_cast<uintptr_t>(nsrc) & 15u) == 0) {
+          const uint32_t n4n = tile_words(min(p.tile_tokens, n - ta - p.tile_tokens)) >> 2;
+          uint32_t* const tbn = tbc == tb ? tb2 : tb;
+          for (uint32_t c = (uint32_t)wave; c * 64 < n4n; c += 4)
+            if (c * 64 + (uint32_t)lane < n4n)
+              __builtin_amdgcn_global_load_lds(
+                  (const void __attribute__((address_space(1)))*)(nsrc + 4 * (c * 64 + lane)),
+                  (void __attribute__((address_space(3)))*)(tbn + 256 * c), 16, 0, 0);
+          pf = true;
+        }
+      }
       // ---- MFMA, RoPE, store: this wave's two 16-token groups
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
@@ -857,7 +889,8 @@ hipError_t launch_dec_transform(const Params& p, hipStream_t s) {
   if (p.D == 128 && p.dtype == KVTC_BF16 && p.tile_tokens % 64 == 0 &&
       (p.n_seqs > 0 || (int64_t)p.T * 128 * ob < (1ll << 31))) {
     // dynamic LDS: operands + tile buffer, at least the staged basis
-    const size_t tbytes = (size_t)((dec_tile_words(p) + 3) & ~3) * 4 + (size_t)64 * 17 * 16, bbytes = (size_t)128 * kBS * 2;
+    // two tile buffers around the row staging
+    const size_t tbytes = (size_t)((dec_tile_words(p) + 3) & ~3) * 4 * 2 + (size_t)64 * 17 * 16, bbytes = (size_t)128 * kBS * 2;
     size_t lds3 = (size_t)3 * 4 * 64 * 16 + tbytes, lds4 = (size_t)4 * 4 * 64 * 16 + tbytes;
     if (lds3 < bbytes) lds3 = bbytes;
     if (lds4 < bbytes) lds4 = bbytes;
