@@ -418,7 +418,7 @@ template <int KB, int KBMAX, int OB, bool PG>
 __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, const uint4 (&A)[4][KBMAX],
                                              uint4* cq, uint32_t* tb, uint4* s_kw, const DecKInfo* s_ki,
                                              const uint8_t* s_rank, const uint32_t* s_b, const float* s_const,
-                                             uint32_t fw, uint4* stage) {
+                                             uint32_t fw, uint4* stage, bool pf0) {
   constexpr int D = 128;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -458,8 +458,10 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
   // Two tile buffers: the next tile is loaded straight into the other one
   // (no registers) once the current tile's last dequantisation is done, and
   // waited for at its start.
+  // (tile 0 in the second buffer: it may have been loaded during the set-up,
+  // pf0)
   uint32_t* const tb2 = reinterpret_cast<uint32_t*>(stage + 64 * 17);
-  bool pf = false;  // the current tile's 16-byte words were loaded ahead
+  bool pf = pf0;  // the current tile's 16-byte words were loaded ahead
   auto tile_words = [&](int ntok) -> uint32_t {
     uint32_t w = ((uint32_t)(ntok * (int)s_b[2 * lane] + 31) >> 5) + ((uint32_t)(ntok * (int)s_b[2 * lane + 1] + 31) >> 5);
 #pragma unroll
@@ -468,7 +470,7 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
   };
   for (int ta = 0; ta < n; ta += p.tile_tokens) {
     const int nt = min(p.tile_tokens, n - ta);
-    uint32_t* const tbc = ((ta / p.tile_tokens) & 1) ? tb2 : tb;
+    uint32_t* const tbc = ((ta / p.tile_tokens) & 1) ? tb : tb2;
     lds_barrier();  // the previous tile's buffer and operands are consumed
     // row offsets of this tile (natural order, scanned), stored by sorted
     // position together with the width and the dequantisation constants;
@@ -794,6 +796,27 @@ __global__ __launch_bounds__(256, 3) void k_dec_pca128(const Params p0) {
     if (lane == 0) s_misc[2] = (int32_t)fw;
   }
   __syncthreads();
+  // the chunk's first packed tile straight into the second tile buffer
+  // (past the staged basis) while the set-up goes on
+  bool pf0 = false;
+  {
+    uint32_t* const tb2 = reinterpret_cast<uint32_t*>(stage + 64 * 17);
+    const uint32_t* slot0 =
+        reinterpret_cast<const uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot);
+    const bool clear = reinterpret_cast<uint8_t*>(tb2) - reinterpret_cast<uint8_t*>(dlds) >= 128 * kBS * 2;
+    if (clear && (reinterpret_cast<uintptr_t>(slot0) & 15u) == 0) {
+      const int nt0 = min(p.tile_tokens, min(p.chunk_tokens, p.T_mid - ch * p.chunk_tokens));
+      uint32_t w = ((uint32_t)(nt0 * (int)s_b[2 * lane] + 31) >> 5) + ((uint32_t)(nt0 * (int)s_b[2 * lane + 1] + 31) >> 5);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) w += __shfl_xor(w, o, 64);
+      const uint32_t n4 = w >> 2;
+      for (uint32_t c = (uint32_t)wave; c * 64 < n4; c += 4)
+        if (c * 64 + (uint32_t)lane < n4)
+          __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(slot0 + 4 * (c * 64 + lane)),
+                                           (void __attribute__((address_space(3)))*)(tb2 + 256 * c), 16, 0, 0);
+      pf0 = true;
+    }
+  }
   // stage the basis with its columns in sorted component order:
   // bst[channel][sorted position]
   uint16_t* bst = reinterpret_cast<uint16_t*>(dlds);
@@ -843,7 +866,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_pca128(const Params p0) {
   __syncthreads();  // the staged basis area becomes the operand and tile buffers
   const uint32_t fw = (uint32_t)s_misc[2];
 
-#define KVTC_DEC_CHUNK(KBV, OBV) dec_chunk128<KBV, KBMAX, OBV, PG>(p, u, ch, A, cq, tb, s_kw, s_ki, s_rank, s_b, s_const, fw, stage)
+#define KVTC_DEC_CHUNK(KBV, OBV) dec_chunk128<KBV, KBMAX, OBV, PG>(p, u, ch, A, cq, tb, s_kw, s_ki, s_rank, s_b, s_const, fw, stage, pf0)
   if constexpr (PG) {  // pools hold the cache dtype: bf16
     if constexpr (KBMAX == 4) {
       KVTC_DEC_CHUNK(4, 2);
