@@ -103,6 +103,7 @@ def lib() -> ctypes.CDLL:
             "orc_rans_encode": (i64, [P, i64, P, i32, i32, P, P, i64]),
             "orc_rans_decode": (ctypes.c_int, [P, P, i64, P, i32, i32, i64, P]),
             "orc_check_config": (ctypes.c_int, [P]),
+            "orc_fnv1a64": (u64, [u64, P, i64]),
             "orc_fingerprint": (u64, [P, P]),
             "orc_max_container_bytes": (i64, [P, i32]),
             "orc_encode": (ctypes.c_int, [P, P, P, i32, P, P, i64, P]),
@@ -377,6 +378,11 @@ def _tensor_ptr(x: np.ndarray, dtype: int):
 def check_config(cfg: dict) -> int:
     c = make_cfg(cfg)
     return int(lib().orc_check_config(ctypes.byref(c)))
+
+
+def fnv1a64(data: bytes, h: int = 0xCBF29CE484222325) -> int:
+    buf = np.frombuffer(bytes(data), np.uint8).copy()
+    return int(lib().orc_fnv1a64(h, _p(buf) if buf.size else None, buf.size))
 
 
 def fingerprint(cfg: dict, basis: np.ndarray | None) -> int:

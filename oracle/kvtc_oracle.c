@@ -144,7 +144,8 @@ float orc_rms(const float* x, int32_t D) {
 }
 
 /* Orthonormal Walsh-Hadamard transform in Sylvester (natural) order
- * ([TTAS] 2.2 "Hadamard transform to spread energy"; [CG] Hadamard control):
+ * ([TTAS] 2.2: values pass through a Hadamard transform before quantisation;
+ * [CG] Hadamard control):
  * H[i][j] = (-1)^popcount(i & j); y = H x / sqrt(D), sum in fp64, one
  * rounding.  H/sqrt(D) is symmetric and orthogonal, so it is its own inverse. */
 void orc_wht(const float* x, int32_t D, float* y) {
@@ -609,6 +610,17 @@ static const float* basis_of(const orc_config* c, const float* basis, int32_t l,
   return basis + ((int64_t)l * 2 + s) * DD;
 }
 
+/* 64-bit FNV-1a (offset basis 0xcbf29ce484222325, prime 2^40 + 0x1b3):
+ * for each byte, XOR it in, then multiply by the prime modulo 2^64.  `h`
+ * carries a running hash (start with the offset basis). */
+uint64_t orc_fnv1a64(uint64_t h, const uint8_t* bytes, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) {
+    h ^= bytes[i];
+    h *= 0x100000001b3ull;
+  }
+  return h;
+}
+
 /* 64-bit FNV-1a over the operand-precision basis bytes (bf16: 2 bytes,
  * fp32: 4 bytes per entry, little-endian), in storage order. */
 uint64_t orc_fingerprint(const orc_config* c, const float* basis) {
@@ -627,10 +639,7 @@ uint64_t orc_fingerprint(const orc_config* c, const float* basis) {
       memcpy(b, &basis[i], 4);
       nb = 4;
     }
-    for (int k = 0; k < nb; ++k) {
-      h ^= b[k];
-      h *= 0x100000001b3ull;
-    }
+    h = orc_fnv1a64(h, b, nb);
   }
   return h;
 }
@@ -1081,7 +1090,8 @@ static int decode_chunk_codes(const orc_config* c, const layout_t* lo, const uin
     for (int64_t i = 0; i < (int64_t)n * D; ++i) q[i] = 0;
     return ORC_OK;
   }
-  if (off < (uint64_t)lo->chunks_off || (off & 15) || off + size > (uint64_t)total) return ORC_ERR_CORRUPT;
+  if (off < (uint64_t)lo->chunks_off || (off & 15) || off > (uint64_t)total || size > (uint64_t)total - off)
+    return ORC_ERR_CORRUPT;
   const uint8_t* rec = in + off;
   if (size < 512 + 4 * (uint32_t)ntiles) return ORC_ERR_CORRUPT;
   uint16_t freq[256];

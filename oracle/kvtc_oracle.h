@@ -112,6 +112,7 @@ int orc_rans_decode(const uint32_t* states, const uint16_t* words, int64_t nword
 
 /* ---- container ------------------------------------------------------- */
 int orc_check_config(const orc_config* cfg);
+uint64_t orc_fnv1a64(uint64_t h, const uint8_t* bytes, int64_t n);
 uint64_t orc_fingerprint(const orc_config* cfg, const float* basis);
 int64_t orc_max_container_bytes(const orc_config* cfg, int32_t T);
 int orc_encode(const orc_config* cfg, const void* k, const void* v, int32_t T,

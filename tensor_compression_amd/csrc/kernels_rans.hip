@@ -897,7 +897,8 @@ __global__ void k_rans_dec_chunks(const Params p0, int raw_runs) {
     if (ok && resv != 0) ok = false;
     if (ok && P == 0 && size != 0) ok = false;
     if (ok && P > 0 &&
-        (off < (uint64_t)p.chunks_off || (off & 15) || off + size > total || size < 512 + 4 * (uint32_t)ntiles))
+        (off < (uint64_t)p.chunks_off || (off & 15) || off > total || size > total - off ||
+         size < 512 + 4 * (uint32_t)ntiles))
       ok = false;
     // stream offsets inside the record (a prefix sum over its tiles)
     int64_t piece = 0;

@@ -110,6 +110,8 @@ static kvtc_status check_config(const kvtc_config* c) {
   if (c->transform != KVTC_PCA && c->transform != KVTC_WHT) return KVTC_ERR_INVALID_ARG;
   if (c->transform == KVTC_PCA && c->dtype == KVTC_FP32 && c->head_dim != 64)
     return KVTC_ERR_UNSUPPORTED;  // fp32 MFMA operands: the basis is register-resident
+  if (c->transform == KVTC_WHT && c->head_dim != 128)
+    return KVTC_ERR_UNSUPPORTED;  // the WHT kernels run 16 lanes x 8 components per token
   if (c->sink_tokens < 0 || c->recent_tokens < 0) return KVTC_ERR_INVALID_ARG;
   if (c->max_bits < 1 || c->max_bits > 8) return KVTC_ERR_INVALID_ARG;
   if (!(c->bits_k >= 0.0f) || !(c->bits_v >= 0.0f)) return KVTC_ERR_INVALID_ARG;

@@ -61,3 +61,15 @@ def test_plan_memory_size_and_validation():
         assert st in (kvtc.ERR_INVALID_ARG, kvtc.ERR_UNSUPPORTED), b
     st, _ = _mem_size(cfg, 0)
     assert st == kvtc.ERR_INVALID_ARG
+
+
+def test_hadamard_path_needs_head_dim_128():
+    """The WHT kernels hold 8 components per lane for 16 lanes per token; a
+    head_dim-64 WHT configuration is refused before anything is launched."""
+    w = synth.WORKLOADS["hadamard_long"]
+    for dtype in (0, 1):
+        cfg = synth.oracle_config(w, dtype=dtype)
+        assert _mem_size(cfg)[0] == kvtc.OK
+        st, _ = _mem_size(dict(cfg, head_dim=64))
+        assert st == kvtc.ERR_UNSUPPORTED
+

@@ -14,8 +14,8 @@ from tensor_compression_amd.calibrate import fit_pca_basis
 pytestmark = pytest.mark.gpu
 
 
-def _setup(name, tokens=None, layers=None, seed=None, **over):
-    w = synth.WORKLOADS[name]
+def _setup(name, tokens=None, layers=None, seed=None, workload=None, **over):
+    w = synth.WORKLOADS[name] if workload is None else workload
     K, V = synth.generate(w, device="cuda", tokens=tokens, layers=layers, seed=seed)
     T = K.shape[2]
     cfg = synth.oracle_config(w, layers=K.shape[0], **over)
@@ -186,6 +186,25 @@ def test_edge_lengths(T):
     _full_parity(cfg, T, K, V, k, v, basis, plan)
 
 
+@pytest.mark.parametrize("case", ["bf16_head_dim_64", "bf16_tile_32", "fp32_hadamard"])
+def test_generic_kernel_configurations(case):
+    """Configurations served by the generic transform kernels rather than the
+    bf16 head_dim-128 ones: a bf16 head_dim-64 cache, 32-token tiles, and the
+    Hadamard path on an fp32 cache."""
+    import dataclasses
+    if case == "bf16_head_dim_64":
+        w = dataclasses.replace(synth.WORKLOADS["llama3_8b"], head_dim=64, rank=16)
+        args = dict(tokens=900, layers=1, workload=w, head_dim=64, chunk_tokens=512, tile_tokens=128)
+    elif case == "bf16_tile_32":
+        args = dict(tokens=700, layers=1, chunk_tokens=256, tile_tokens=32)
+    else:
+        w = dataclasses.replace(synth.WORKLOADS["hadamard_long"], dtype="fp32")
+        args = dict(tokens=900, layers=1, workload=w, dtype=0)
+    name = "hadamard_long" if case == "fp32_hadamard" else "llama3_8b"
+    cfg, T, K, V, k, v, basis, plan = _setup(name, **args)
+    _full_parity(cfg, T, K, V, k, v, basis, plan)
+
+
 def test_deterministic_container():
     cfg, T, K, V, k, v, basis, plan = _setup("llama3_8b", tokens=900, layers=1)
     d1, _, _ = _encode(plan, K, V)
@@ -227,9 +246,20 @@ def test_damaged_containers_are_refused():
         bad = bytearray(data); bad[pos] ^= 0x5A
         caught += status(bad) == kvtc.ERR_CORRUPT
     assert caught >= 9
+    # a directory offset near 2^64 (16-byte aligned) would wrap an
+    # offset + size bound; it is refused before the record is read
+    bad = bytearray(data)
+    bad[orc_dir_off(data): orc_dir_off(data) + 8] = np.uint64(2 ** 64 - 256).tobytes()
+    assert status(bad) == kvtc.ERR_CORRUPT
+    assert orc.decode_status(cfg, bytes(bad), basis, T) == orc.ERR_CORRUPT
     # the oracle agrees on the same damage
     bad = bytearray(data); bad[rec + 5] ^= 0x10
     assert orc.decode_status(cfg, bytes(bad), basis, T) == orc.ERR_CORRUPT
+
+
+def orc_dir_off(data):
+    """Byte offset of the chunk directory, from the container header."""
+    return int(np.frombuffer(data[152:160], np.uint64)[0])
 
 
 def test_short_output_reports_capacity():

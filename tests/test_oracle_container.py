@@ -251,3 +251,24 @@ def test_nonfinite_input(orc):
     data = orc.encode(cfg, k3, v, B)
     kd, _ = orc.decode(cfg, data, B, 256)
     assert np.isnan(kd[0, 0, 1, 3]) and kd[0, 0, 250, 5] == np.inf
+
+
+def test_fnv1a64_known_answers(orc):
+    """Published FNV-1a 64-bit test vectors (offset basis 0xcbf29ce484222325,
+    prime 0x100000001b3), then the container fingerprint as that hash over the
+    operand-precision basis bytes in storage order."""
+    assert orc.fnv1a64(b"") == 0xCBF29CE484222325
+    assert orc.fnv1a64(b"a") == 0xAF63DC4C8601EC8C
+    assert orc.fnv1a64(b"foobar") == 0x85944171F73967E8
+    # the running form continues a hash across pieces
+    assert orc.fnv1a64(b"bar", orc.fnv1a64(b"foo")) == 0x85944171F73967E8
+    rng = np.random.default_rng(3)
+    cfg = dict(layers=1, kv_heads=2, head_dim=16, dtype=1, transform=0, sink_tokens=0,
+               recent_tokens=0, bits_k=2.0, bits_v=2.0, max_bits=8, rope_keys=0, rope_style=0,
+               rope_theta=1e4, rans_scale_bits=12, rans_lanes=32, chunk_tokens=256,
+               tile_tokens=256, basis_per_head=0, wht_keys=1)
+    basis = rng.standard_normal((1, 2, 16, 16)).astype(np.float32)
+    assert orc.fingerprint(cfg, basis) == orc.fnv1a64(orc.f32_to_bf16_bits(basis).tobytes())
+    cfg32 = dict(cfg, dtype=0)
+    assert orc.fingerprint(cfg32, basis) == orc.fnv1a64(basis.tobytes())
+

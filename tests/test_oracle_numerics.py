@@ -181,10 +181,22 @@ def test_wht_is_involution(orc):
 
 
 def test_rms(orc):
+    """Closed forms of the root mean square over the D entries of a row: a
+    constant row gives its magnitude, a single spike of a in D entries gives
+    |a| / sqrt(D), an alternating row +-a gives |a|, (3, 4) gives 5/sqrt(2),
+    and scaling by a power of two scales the result exactly."""
+    assert orc.rms(np.full(128, 3.0, np.float32)) == np.float32(3.0)
+    assert orc.rms(np.full(64, -0.75, np.float32)) == np.float32(0.75)
+    spike = np.zeros(64, np.float32)
+    spike[17] = -24.0
+    assert orc.rms(spike) == np.float32(3.0)  # 24 / sqrt(64)
+    alt = np.array([5.5, -5.5] * 64, np.float32)
+    assert orc.rms(alt) == np.float32(5.5)
+    assert orc.rms(np.array([3.0, 4.0], np.float32)) == np.float32(5.0 / math.sqrt(2.0))
+    assert orc.rms(np.zeros(128, np.float32)) == 0.0
     rng = np.random.default_rng(8)
     x = _bf16_values(rng, 128, 3.0)
-    assert orc.rms(x) == np.float32(math.sqrt((x.astype(np.float64) ** 2).sum() / 128))
-    assert orc.rms(np.zeros(128, np.float32)) == 0.0
+    assert orc.rms(x * np.float32(8.0)) == np.float32(8.0) * orc.rms(x)
 
 
 # --------------------------------------------------------------- stats ----

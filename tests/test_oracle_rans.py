@@ -42,6 +42,16 @@ def _round_trip(orc, sym, freq, lanes, sb=12):
     return states, words
 
 
+def test_freq_normalize_rounds_half_up(orc):
+    """Counts (2, 5, 2) of N = 9 at M = 256: n M / N = 56.9, 142.2, 56.9 round
+    to 57, 142, 57, which already sum to M.  (Flooring would give 56, 142, 56
+    and hand the deficit of 2 to the most frequent symbol: 56, 144, 56.)"""
+    c = np.zeros(256, np.uint32)
+    c[[3, 4, 5]] = [2, 5, 2]
+    f = orc.freq_normalize(c, 8)
+    assert list(f[[3, 4, 5]]) == [57, 142, 57] and int(f.sum()) == 256
+
+
 def test_rans_exhaustive_tiny_alphabets(orc):
     """Every sequence of length 0..8 over alphabets of 1..3 symbols, with
     several tables and lane counts, round-trips exactly."""
