@@ -99,7 +99,13 @@ def lib() -> ctypes.CDLL:
             "orc_packed_bytes": (i64, [P, i32, i64]),
             "orc_pack": (None, [P, i64, i32, P, P]),
             "orc_unpack": (None, [P, i64, i32, P, P]),
-            "orc_freq_normalize": (None, [P, i32, P]),
+            "orc_freq_normalize": (None, [P, i32, i32, P]),
+            "orc_sym_bits": (i32, [i32]),
+            "orc_raw_bits": (i32, [i32]),
+            "orc_rans_encode_seq": (i64, [i64, P, P, P, P, P, i32, i32, P, P, i64]),
+            "orc_rans_decode_seq": (ctypes.c_int, [i64, P, P, P, P, i32, i32, P, P, i64, P]),
+            "orc_chunk_encode": (i64, [P, P, P, i32, P, i64, P]),
+            "orc_chunk_decode": (ctypes.c_int, [P, P, P, i64, i32, i32, P]),
             "orc_rans_encode": (i64, [P, i64, P, i32, i32, P, P, i64]),
             "orc_rans_decode": (ctypes.c_int, [P, P, i64, P, i32, i32, i64, P]),
             "orc_check_config": (ctypes.c_int, [P]),
@@ -319,11 +325,87 @@ def unpack(data: np.ndarray, ntok: int, bits) -> np.ndarray:
 
 
 def freq_normalize(counts, scale_bits: int = 12) -> np.ndarray:
+    """Frequencies (sum 2^scale_bits) of an alphabet of len(counts) <= 256 symbols."""
     counts = np.ascontiguousarray(counts, np.uint32)
-    assert counts.shape == (256,)
-    f = np.zeros(256, np.uint16)
-    lib().orc_freq_normalize(_p(counts), scale_bits, _p(f))
+    assert counts.ndim == 1 and 1 <= counts.size <= 256
+    f = np.zeros(counts.size, np.uint16)
+    lib().orc_freq_normalize(_p(counts), counts.size, scale_bits, _p(f))
     return f
+
+
+def sym_bits(b: int) -> int:
+    return int(lib().orc_sym_bits(int(b)))
+
+
+def raw_bits(b: int) -> int:
+    return int(lib().orc_raw_bits(int(b)))
+
+
+def rans_encode_seq(sym, lane, tab, n_sym, freqs, scale_bits: int = 12, lanes: int = 32):
+    """Interleaved rANS over a symbol sequence in decoding order, with a lane
+    and a table (offset into `freqs`, n_sym entries) per symbol."""
+    sym = np.ascontiguousarray(sym, np.uint8)
+    N = sym.size
+    lane = np.ascontiguousarray(lane, np.uint8)
+    tab = np.ascontiguousarray(tab, np.int32)
+    n_sym = np.ascontiguousarray(n_sym, np.int32)
+    freqs = np.ascontiguousarray(freqs, np.uint16)
+    states = np.zeros(lanes, np.uint32)
+    cap = rans_words_cap(N, lanes, scale_bits)
+    words = np.zeros(max(cap, 1), np.uint16)
+    one8, one32 = np.zeros(1, np.uint8), np.zeros(1, np.int32)
+    n = lib().orc_rans_encode_seq(N, _p(sym if N else one8), _p(lane if N else one8),
+                                  _p(tab if N else one32), _p(n_sym if N else one32), _p(freqs),
+                                  scale_bits, lanes, _p(states), _p(words), cap)
+    if n < 0:
+        raise OracleError(ERR_CAPACITY, "rans_encode_seq")
+    return states, words[:n].copy()
+
+
+def rans_decode_seq(states, words, lane, tab, n_sym, freqs, scale_bits: int = 12, lanes: int = 32):
+    lane = np.ascontiguousarray(lane, np.uint8)
+    N = lane.size
+    tab = np.ascontiguousarray(tab, np.int32)
+    n_sym = np.ascontiguousarray(n_sym, np.int32)
+    states = np.ascontiguousarray(states, np.uint32)
+    words = np.ascontiguousarray(words, np.uint16)
+    wbuf = words if words.size else np.zeros(1, np.uint16)
+    out = np.zeros(max(N, 1), np.uint8)
+    one8, one32 = np.zeros(1, np.uint8), np.zeros(1, np.int32)
+    st = lib().orc_rans_decode_seq(N, _p(lane if N else one8), _p(tab if N else one32),
+                                   _p(n_sym if N else one32), _p(np.ascontiguousarray(freqs, np.uint16)),
+                                   scale_bits, lanes, _p(states), _p(wbuf), words.size, _p(out))
+    if st != OK:
+        raise OracleError(st, "rans_decode_seq")
+    return out[:N]
+
+
+def chunk_encode(cfg: dict, bits, q) -> tuple:
+    """(record bytes, mode) of one chunk's codes q[n, D] (mode 0 coded, 1 packed)."""
+    c = make_cfg(cfg)
+    q = np.ascontiguousarray(q, np.uint8)
+    n, D = q.shape
+    bits = np.ascontiguousarray(bits, np.uint8)
+    cap = 4 * n * D + 4096
+    out = np.zeros(cap, np.uint8)
+    mode = ctypes.c_int32(0)
+    size = lib().orc_chunk_encode(ctypes.byref(c), _p(bits), _p(q if q.size else np.zeros(1, np.uint8)),
+                                  n, _p(out), cap, ctypes.byref(mode))
+    if size < 0:
+        raise OracleError(ERR_CAPACITY, "chunk_encode")
+    return out[:size].tobytes(), mode.value
+
+
+def chunk_decode(cfg: dict, bits, rec: bytes, mode: int, n: int) -> np.ndarray:
+    c = make_cfg(cfg)
+    D = cfg["head_dim"]
+    buf = np.frombuffer(bytes(rec), np.uint8).copy()
+    q = np.zeros((max(n, 1), D), np.uint8)
+    st = lib().orc_chunk_decode(ctypes.byref(c), _p(np.ascontiguousarray(bits, np.uint8)),
+                                _p(buf if buf.size else np.zeros(1, np.uint8)), buf.size, mode, n, _p(q))
+    if st != OK:
+        raise OracleError(st, "chunk_decode")
+    return q[:n]
 
 
 def byte_histogram(sym: np.ndarray) -> np.ndarray:
@@ -533,7 +615,8 @@ def parse_container(data: bytes, cfg: dict, T: int) -> dict:
     d = buf[dir_off: dir_off + 16 * nch].reshape(max(nch, 0), 16)
     offs = d[:, :8].copy().view(np.uint64).ravel()
     sizes = d[:, 8:12].copy().view(np.uint32).ravel()
-    return dict(bits=bits, zero=zero, scale=scale, offsets=offs, sizes=sizes,
+    modes = d[:, 12:16].copy().view(np.uint32).ravel()
+    return dict(bits=bits, zero=zero, scale=scale, offsets=offs, sizes=sizes, modes=modes,
                 chunks_off=chunks_off, total=total, layout=lo,
                 fingerprint=int(hdr[176:184].view(np.uint64)[0]))
 

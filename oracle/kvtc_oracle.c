@@ -15,6 +15,12 @@
 
 #define ORC_RANS_L 65536u /* lower bound of the normalised rANS state interval */
 
+/* little-endian field access (the host is little-endian) */
+static void put32(uint8_t* p, uint32_t v) { memcpy(p, &v, 4); }
+static void put64(uint8_t* p, uint64_t v) { memcpy(p, &v, 8); }
+static uint32_t get32(const uint8_t* p) { uint32_t v; memcpy(&v, p, 4); return v; }
+static uint64_t get64(const uint8_t* p) { uint64_t v; memcpy(&v, p, 8); return v; }
+
 /* ===================================================================== */
 /* bf16 <-> fp32                                                          */
 /* ===================================================================== */
@@ -392,21 +398,22 @@ void orc_unpack(const uint8_t* in, int64_t ntok, int32_t D, const uint8_t* bits,
 /* rANS ([KVTC] "rANS Makes the Last Mile Smaller"; rans_encode)           */
 /* ===================================================================== */
 
-/* Frequencies summing to M = 2^scale_bits from byte counts: each present
- * symbol gets max(1, round-half-up(n_s M / N)); a positive remainder goes to
- * the most frequent symbol, an excess is removed one unit at a time from the
- * symbol with the largest frequency above 1 (lowest symbol on ties). */
-void orc_freq_normalize(const uint32_t* counts, int32_t scale_bits, uint16_t* freq) {
+/* Frequencies summing to M = 2^scale_bits from the counts of an alphabet of
+ * n_sym symbols: each present symbol gets max(1, round-half-up(n_s M / N));
+ * a positive remainder goes to the most frequent symbol (lowest symbol on
+ * ties), an excess is removed one unit at a time from the symbol with the
+ * largest frequency above 1 (lowest symbol on ties).  All zero when N = 0. */
+void orc_freq_normalize(const uint32_t* counts, int32_t n_sym, int32_t scale_bits, uint16_t* freq) {
   uint64_t N = 0;
-  for (int s = 0; s < 256; ++s) N += counts[s];
+  for (int s = 0; s < n_sym; ++s) N += counts[s];
   int64_t M = (int64_t)1 << scale_bits;
   if (N == 0) {
-    for (int s = 0; s < 256; ++s) freq[s] = 0;
+    for (int s = 0; s < n_sym; ++s) freq[s] = 0;
     return;
   }
   int64_t f[256];
   int64_t sum = 0;
-  for (int s = 0; s < 256; ++s) {
+  for (int s = 0; s < n_sym; ++s) {
     if (counts[s] == 0) {
       f[s] = 0;
     } else {
@@ -418,95 +425,391 @@ void orc_freq_normalize(const uint32_t* counts, int32_t scale_bits, uint16_t* fr
   int64_t d = M - sum;
   if (d > 0) {
     int best = 0;
-    for (int s = 1; s < 256; ++s)
+    for (int s = 1; s < n_sym; ++s)
       if (counts[s] > counts[best]) best = s;
     f[best] += d;
   }
   while (d < 0) {
     int best = -1;
-    for (int s = 0; s < 256; ++s)
+    for (int s = 0; s < n_sym; ++s)
       if (f[s] > 1 && (best < 0 || f[s] > f[best])) best = s;
     f[best] -= 1;
     d += 1;
   }
-  for (int s = 0; s < 256; ++s) freq[s] = (uint16_t)f[s];
+  for (int s = 0; s < n_sym; ++s) freq[s] = (uint16_t)f[s];
 }
 
-/* Interleaved rANS with `lanes` 32-bit states (state interval [2^16, 2^32),
- * 16-bit renormalisation words).  Symbol i belongs to lane i mod lanes and
- * step i / lanes.  Encoding walks the steps backwards and, inside a step,
- * the lanes in descending order; words are stored in the order they are
- * emitted.  The decoder walks the steps forwards and the lanes in ascending
- * order, consuming the words from the last one to the first.  Returns the
- * number of words, or -1 when words_cap is too small or a symbol has
- * frequency 0. */
-int64_t orc_rans_encode(const uint8_t* sym, int64_t N, const uint16_t* freq,
-                        int32_t scale_bits, int32_t lanes, uint32_t* states,
-                        uint16_t* words, int64_t words_cap) {
-  uint32_t cum[257];
-  cum[0] = 0;
-  for (int s = 0; s < 256; ++s) cum[s + 1] = cum[s] + freq[s];
+/* Interleaved rANS over a sequence of N symbols given in decoding order
+ * (Duda's range variant of ANS; interleaving after Giesen).  Symbol p is
+ * coded by state lane[p] (of `lanes` 32-bit states in [2^16, 2^32), 16-bit
+ * renormalisation words) with the frequency table that starts at
+ * freqs[tab[p]] and has n_sym[p] entries summing to M = 2^scale_bits.
+ *
+ * Encoding walks the sequence from the last symbol to the first.  Before a
+ * symbol of frequency f is coded, a state x >= f 2^(32 - scale_bits) emits
+ * its low 16 bits as one word and shifts them out; then
+ * x = floor(x / f) M + (x mod f) + cum, cum being the sum of the
+ * frequencies of the smaller symbols.  Words are stored in emission order.
+ * Decoding walks the sequence forwards: slot = x mod M selects the symbol
+ * whose cumulative range holds it, x = f floor(x / M) + slot - cum, and a
+ * state below 2^16 takes the last unread word as its new low 16 bits.
+ *
+ * Returns the number of words, or -1 when words_cap is too small or a
+ * symbol has frequency 0. */
+int64_t orc_rans_encode_seq(int64_t N, const uint8_t* sym, const uint8_t* lane, const int32_t* tab,
+                            const int32_t* n_sym, const uint16_t* freqs, int32_t scale_bits,
+                            int32_t lanes, uint32_t* states, uint16_t* words, int64_t words_cap) {
   for (int32_t j = 0; j < lanes; ++j) states[j] = ORC_RANS_L;
-  int64_t steps = (N + lanes - 1) / lanes;
   int64_t n = 0;
-  for (int64_t k = steps - 1; k >= 0; --k) {
-    for (int32_t j = lanes - 1; j >= 0; --j) {
-      int64_t i = k * lanes + j;
-      if (i >= N) continue;
-      uint32_t s = sym[i];
-      uint32_t f = freq[s];
-      if (f == 0) return -1;
-      uint32_t x = states[j];
-      if ((uint64_t)x >= ((uint64_t)f << (32 - scale_bits))) {
-        if (n >= words_cap) return -1;
-        words[n++] = (uint16_t)(x & 0xffffu);
-        x >>= 16;
-      }
-      x = ((x / f) << scale_bits) + (x % f) + cum[s];
-      states[j] = x;
+  for (int64_t p = N - 1; p >= 0; --p) {
+    const uint16_t* fr = freqs + tab[p];
+    uint32_t s = sym[p];
+    if ((int32_t)s >= n_sym[p]) return -1;
+    uint32_t f = fr[s];
+    if (f == 0) return -1;
+    uint32_t cum = 0;
+    for (uint32_t k = 0; k < s; ++k) cum += fr[k];
+    uint32_t x = states[lane[p]];
+    if ((uint64_t)x >= ((uint64_t)f << (32 - scale_bits))) {
+      if (n >= words_cap) return -1;
+      words[n++] = (uint16_t)(x & 0xffffu);
+      x >>= 16;
     }
+    x = ((x / f) << scale_bits) + (x % f) + cum;
+    states[lane[p]] = x;
   }
   return n;
 }
 
-/* Inverse of orc_rans_encode.  Returns ORC_OK, or ORC_ERR_CORRUPT when the
- * table is invalid, the words run out or are left over, or a final state
- * differs from the initial state 2^16. */
-int orc_rans_decode(const uint32_t* states, const uint16_t* words, int64_t nwords,
-                    const uint16_t* freq, int32_t scale_bits, int32_t lanes,
-                    int64_t N, uint8_t* sym) {
+/* Inverse of orc_rans_encode_seq.  Returns ORC_OK, or ORC_ERR_CORRUPT when a
+ * table does not sum to M, the words run out or are left over, or a final
+ * state differs from the initial state 2^16. */
+int orc_rans_decode_seq(int64_t N, const uint8_t* lane, const int32_t* tab, const int32_t* n_sym,
+                        const uint16_t* freqs, int32_t scale_bits, int32_t lanes,
+                        const uint32_t* states, const uint16_t* words, int64_t nwords,
+                        uint8_t* sym) {
   uint32_t M = 1u << scale_bits;
-  uint32_t cum[257];
-  cum[0] = 0;
-  for (int s = 0; s < 256; ++s) cum[s + 1] = cum[s] + freq[s];
-  if (N > 0 && cum[256] != M) return ORC_ERR_CORRUPT;
   uint32_t x[64];
   for (int32_t j = 0; j < lanes; ++j) {
     x[j] = states[j];
     if (x[j] < ORC_RANS_L) return ORC_ERR_CORRUPT;
   }
   int64_t ptr = nwords; /* words are consumed from the last one backwards */
-  int64_t steps = (N + lanes - 1) / lanes;
-  for (int64_t k = 0; k < steps; ++k) {
-    for (int32_t j = 0; j < lanes; ++j) {
-      int64_t i = k * lanes + j;
-      if (i >= N) break;
-      uint32_t slot = x[j] & (M - 1);
-      int s = 0;
-      while (!(slot < cum[s + 1])) ++s; /* the symbol whose range holds slot */
-      sym[i] = (uint8_t)s;
-      x[j] = freq[s] * (x[j] >> scale_bits) + slot - cum[s];
-      if (x[j] < ORC_RANS_L) {
-        if (ptr <= 0) return ORC_ERR_CORRUPT;
-        x[j] = (x[j] << 16) | words[--ptr];
-        if (x[j] < ORC_RANS_L) return ORC_ERR_CORRUPT;
-      }
+  for (int64_t p = 0; p < N; ++p) {
+    const uint16_t* fr = freqs + tab[p];
+    uint32_t total = 0;
+    for (int32_t k = 0; k < n_sym[p]; ++k) total += fr[k];
+    if (total != M) return ORC_ERR_CORRUPT;
+    uint32_t j = lane[p];
+    uint32_t slot = x[j] & (M - 1);
+    uint32_t cum = 0;
+    int s = 0;
+    while (!(slot < cum + fr[s])) cum += fr[s++]; /* the symbol whose range holds slot */
+    sym[p] = (uint8_t)s;
+    x[j] = fr[s] * (x[j] >> scale_bits) + slot - cum;
+    if (x[j] < ORC_RANS_L) {
+      if (ptr <= 0) return ORC_ERR_CORRUPT;
+      x[j] = (x[j] << 16) | words[--ptr];
+      if (x[j] < ORC_RANS_L) return ORC_ERR_CORRUPT;
     }
   }
   if (ptr != 0) return ORC_ERR_CORRUPT;
   for (int32_t j = 0; j < lanes; ++j)
     if (x[j] != ORC_RANS_L) return ORC_ERR_CORRUPT;
   return ORC_OK;
+}
+
+/* One stream of N byte symbols with a single 256-entry table, symbol i on
+ * lane i mod lanes: the sequence coder with uniform lanes and table. */
+static void single_table_seq(int64_t N, int32_t lanes, uint8_t* lane, int32_t* tab, int32_t* n_sym) {
+  for (int64_t i = 0; i < N; ++i) {
+    lane[i] = (uint8_t)(i % lanes);
+    tab[i] = 0;
+    n_sym[i] = 256;
+  }
+}
+
+int64_t orc_rans_encode(const uint8_t* sym, int64_t N, const uint16_t* freq,
+                        int32_t scale_bits, int32_t lanes, uint32_t* states,
+                        uint16_t* words, int64_t words_cap) {
+  uint8_t* lane = (uint8_t*)malloc((size_t)N + 1);
+  int32_t* tab = (int32_t*)malloc(sizeof(int32_t) * ((size_t)N + 1));
+  int32_t* ns = (int32_t*)malloc(sizeof(int32_t) * ((size_t)N + 1));
+  single_table_seq(N, lanes, lane, tab, ns);
+  int64_t n = orc_rans_encode_seq(N, sym, lane, tab, ns, freq, scale_bits, lanes, states, words, words_cap);
+  free(lane); free(tab); free(ns);
+  return n;
+}
+
+int orc_rans_decode(const uint32_t* states, const uint16_t* words, int64_t nwords,
+                    const uint16_t* freq, int32_t scale_bits, int32_t lanes,
+                    int64_t N, uint8_t* sym) {
+  uint8_t* lane = (uint8_t*)malloc((size_t)N + 1);
+  int32_t* tab = (int32_t*)malloc(sizeof(int32_t) * ((size_t)N + 1));
+  int32_t* ns = (int32_t*)malloc(sizeof(int32_t) * ((size_t)N + 1));
+  single_table_seq(N, lanes, lane, tab, ns);
+  int st = orc_rans_decode_seq(N, lane, tab, ns, freq, scale_bits, lanes, states, words, nwords, sym);
+  free(lane); free(tab); free(ns);
+  return st;
+}
+
+/* ===================================================================== */
+/* Chunk records: what the entropy coder models ([KVTC] "rANS Makes the    */
+/* Last Mile Smaller": codes that occur more often should cost less)       */
+/* ===================================================================== */
+
+/* A component of width b >= 2 contributes one symbol per token: the top
+ * min(b, 4) bits of its code, coded with that component's own frequency
+ * table over the chunk (2^min(b,4) entries).  The remaining low bits of a
+ * wider code (b - 4 of them when b >= 5) and the whole code of a 1-bit
+ * component are stored as raw bits. */
+int32_t orc_sym_bits(int32_t b) { return b >= 2 ? (b < 4 ? b : 4) : 0; }
+int32_t orc_raw_bits(int32_t b) { return b == 1 ? 1 : (b >= 5 ? b - 4 : 0); }
+
+/* Bytes of a record's frequency tables (u16 each), padded to 4 bytes. */
+static int64_t table_bytes(const uint8_t* bits, int32_t D) {
+  int64_t n = 0;
+  for (int32_t i = 0; i < D; ++i)
+    if (orc_sym_bits(bits[i]) > 0) n += (int64_t)1 << orc_sym_bits(bits[i]);
+  return (2 * n + 3) & ~(int64_t)3;
+}
+
+/* Bytes of a tile's raw rows: per component with raw bits r > 0, in index
+ * order, ceil(m r / 32) little-endian words, bits LSB-first. */
+static int64_t raw_row_bytes(const uint8_t* bits, int32_t D, int64_t m) {
+  int64_t n = 0;
+  for (int32_t i = 0; i < D; ++i) {
+    int32_t r = orc_raw_bits(bits[i]);
+    if (r > 0) n += 4 * ((m * r + 31) / 32);
+  }
+  return n;
+}
+
+/* Symbols of one tile of m tokens (codes q[m][D]) in decoding order: the
+ * components with symbol bits in index order, and within a component the
+ * tokens in order; the k-th symbol of a component goes to lane k mod lanes
+ * and uses that component's table (tab_off[i] into the record's tables). */
+static int64_t tile_sequence(const uint8_t* q, int32_t m, int32_t D, const uint8_t* bits, int32_t lanes,
+                             const int32_t* tab_off, uint8_t* sym, uint8_t* lane, int32_t* tab,
+                             int32_t* n_sym) {
+  int64_t p = 0;
+  for (int32_t i = 0; i < D; ++i) {
+    int32_t h = orc_sym_bits(bits[i]);
+    if (h == 0) continue;
+    int32_t r = bits[i] - h;
+    for (int32_t k = 0; k < m; ++k) {
+      if (sym) sym[p] = (uint8_t)(q[(int64_t)k * D + i] >> r);
+      lane[p] = (uint8_t)(k % lanes);
+      tab[p] = tab_off[i];
+      n_sym[p] = 1 << h;
+      ++p;
+    }
+  }
+  return p;
+}
+
+static void put_bits(uint8_t* row, int64_t at, uint32_t v, int32_t nb) {
+  for (int32_t bit = 0; bit < nb; ++bit)
+    if ((v >> bit) & 1u) row[(at + bit) / 8] |= (uint8_t)(1u << ((at + bit) % 8));
+}
+
+static uint32_t get_bits(const uint8_t* row, int64_t at, int32_t nb) {
+  uint32_t v = 0;
+  for (int32_t bit = 0; bit < nb; ++bit)
+    if ((row[(at + bit) / 8] >> ((at + bit) % 8)) & 1u) v |= 1u << bit;
+  return v;
+}
+
+static int64_t seq_words_cap(int64_t nsym, int32_t lanes, int32_t sb) {
+  /* each symbol adds at most sb bits of state, each word removes 16 */
+  return (nsym * (sb + 1)) / 16 + 2 * (int64_t)lanes + 2;
+}
+
+/* Packed size of a chunk of n tokens: its tiles' packed rows back to back. */
+static int64_t chunk_packed_bytes(const orc_config* c, const uint8_t* bits, int32_t n) {
+  int64_t P = 0;
+  for (int32_t a = 0; a < n; a += c->tile_tokens) {
+    int32_t m = n - a < c->tile_tokens ? n - a : c->tile_tokens;
+    P += orc_packed_bytes(bits, c->head_dim, m);
+  }
+  return P;
+}
+
+/* Encode the record of one chunk (codes q[n][D] of widths bits[D]).
+ *
+ * Coded record (mode 0):
+ *   tables: for each component with symbol bits h > 0, in index order, 2^h
+ *           u16 frequencies of its symbols over the chunk (sum 2^sb), then
+ *           zero padding to 4 bytes;
+ *   u32 word count of each tile's stream;
+ *   per tile (tile_tokens tokens, the last one shorter): u32 final state of
+ *           each lane (lane 0 first), the stream's u16 words in emission
+ *           order (a zero u16 after an odd count), then its raw rows;
+ *   zero padding to 16 bytes.
+ * Packed record (mode 1): the packed tiles back to back, zero padding to 16
+ * bytes.  The packed form is written when the coded record would not be
+ * smaller (the never-worse rule of the AT-1 Memory page, "KV & tensor
+ * mode": keep the smaller of the coded and the plain form).  A chunk whose
+ * components all have width 0 has an empty record.
+ *
+ * Returns the record size (a multiple of 16), or -1 when cap is too small. */
+int64_t orc_chunk_encode(const orc_config* c, const uint8_t* bits, const uint8_t* q, int32_t n,
+                         uint8_t* rec, int64_t cap, int32_t* mode) {
+  int32_t D = c->head_dim, lanes = c->rans_lanes, sb = c->rans_scale_bits;
+  int32_t ntiles = (n + c->tile_tokens - 1) / c->tile_tokens;
+  int64_t P = chunk_packed_bytes(c, bits, n);
+  *mode = 0;
+  if (P == 0) return 0;
+  /* packed form, kept in case it wins */
+  int64_t Pa = (P + 15) & ~(int64_t)15;
+  uint8_t* packed = (uint8_t*)calloc((size_t)Pa, 1);
+  int64_t at = 0;
+  for (int32_t t = 0; t < ntiles; ++t) {
+    int32_t a = t * c->tile_tokens, m = n - a < c->tile_tokens ? n - a : c->tile_tokens;
+    orc_pack(q + (int64_t)a * D, m, D, bits, packed + at);
+    at += orc_packed_bytes(bits, D, m);
+  }
+  /* coded form */
+  int32_t tab_off[256];
+  int64_t ntab = 0;
+  for (int32_t i = 0; i < D; ++i) {
+    tab_off[i] = (int32_t)ntab;
+    int32_t h = orc_sym_bits(bits[i]);
+    if (h > 0) ntab += (int64_t)1 << h;
+  }
+  int64_t tb = table_bytes(bits, D);
+  int64_t cap_coded = tb + 4 * (int64_t)ntiles;
+  for (int32_t t = 0; t < ntiles; ++t) {
+    int32_t a = t * c->tile_tokens, m = n - a < c->tile_tokens ? n - a : c->tile_tokens;
+    int64_t nsym = (int64_t)m * (ntab > 0 ? D : 0);
+    cap_coded += 4 * (int64_t)lanes + 2 * seq_words_cap(nsym, lanes, sb) + 2 + raw_row_bytes(bits, D, m);
+  }
+  uint8_t* buf = (uint8_t*)calloc((size_t)cap_coded + 16, 1);
+  uint16_t* freqs = (uint16_t*)buf; /* the tables sit at the start of the record */
+  for (int32_t i = 0; i < D; ++i) {
+    int32_t h = orc_sym_bits(bits[i]);
+    if (h == 0) continue;
+    uint32_t counts[16] = {0};
+    for (int32_t k = 0; k < n; ++k) counts[q[(int64_t)k * D + i] >> (bits[i] - h)]++;
+    orc_freq_normalize(counts, 1 << h, sb, freqs + tab_off[i]);
+  }
+  int64_t p = tb + 4 * (int64_t)ntiles;
+  int64_t maxsym = (int64_t)c->tile_tokens * D;
+  uint8_t* sym = (uint8_t*)malloc((size_t)maxsym + 1);
+  uint8_t* lane = (uint8_t*)malloc((size_t)maxsym + 1);
+  int32_t* tab = (int32_t*)malloc(sizeof(int32_t) * ((size_t)maxsym + 1));
+  int32_t* ns = (int32_t*)malloc(sizeof(int32_t) * ((size_t)maxsym + 1));
+  uint16_t* words = (uint16_t*)malloc(sizeof(uint16_t) * ((size_t)seq_words_cap(maxsym, lanes, sb) + 1));
+  int ok = 1;
+  for (int32_t t = 0; t < ntiles && ok; ++t) {
+    int32_t a = t * c->tile_tokens, m = n - a < c->tile_tokens ? n - a : c->tile_tokens;
+    const uint8_t* qt = q + (int64_t)a * D;
+    int64_t N = tile_sequence(qt, m, D, bits, lanes, tab_off, sym, lane, tab, ns);
+    uint32_t states[64];
+    int64_t nw = orc_rans_encode_seq(N, sym, lane, tab, ns, freqs, sb, lanes, states, words,
+                                     seq_words_cap(N, lanes, sb));
+    if (nw < 0) { ok = 0; break; }
+    put32(buf + tb + 4 * (int64_t)t, (uint32_t)nw);
+    memcpy(buf + p, states, 4 * (size_t)lanes);
+    p += 4 * (int64_t)lanes;
+    memcpy(buf + p, words, 2 * (size_t)nw);
+    p += 2 * nw + ((nw & 1) ? 2 : 0);
+    for (int32_t i = 0; i < D; ++i) {
+      int32_t r = orc_raw_bits(bits[i]);
+      if (r == 0) continue;
+      for (int32_t k = 0; k < m; ++k)
+        put_bits(buf + p, (int64_t)k * r, qt[(int64_t)k * D + i] & ((1u << r) - 1u), r);
+      p += 4 * (((int64_t)m * r + 31) / 32);
+    }
+  }
+  int64_t size;
+  int64_t coded = (p + 15) & ~(int64_t)15;
+  if (ok && coded < Pa) {
+    size = coded;
+    if (size <= cap) memcpy(rec, buf, (size_t)size);
+  } else {
+    size = Pa;
+    *mode = 1;
+    if (size <= cap) memcpy(rec, packed, (size_t)size);
+  }
+  free(buf); free(packed); free(sym); free(lane); free(tab); free(ns); free(words);
+  return size <= cap ? size : -1;
+}
+
+/* Decode one chunk record (mode 0 coded, 1 packed) of n tokens into codes
+ * q[n][D].  Returns ORC_OK or ORC_ERR_CORRUPT (sizes, tables, streams). */
+int orc_chunk_decode(const orc_config* c, const uint8_t* bits, const uint8_t* rec, int64_t size,
+                     int32_t mode, int32_t n, uint8_t* q) {
+  int32_t D = c->head_dim, lanes = c->rans_lanes, sb = c->rans_scale_bits;
+  int32_t ntiles = (n + c->tile_tokens - 1) / c->tile_tokens;
+  int64_t P = chunk_packed_bytes(c, bits, n);
+  if (P == 0) {
+    if (size != 0 || mode != 0) return ORC_ERR_CORRUPT;
+    memset(q, 0, (size_t)n * D);
+    return ORC_OK;
+  }
+  if (mode == 1) {
+    if (size != ((P + 15) & ~(int64_t)15)) return ORC_ERR_CORRUPT;
+    int64_t at = 0;
+    for (int32_t t = 0; t < ntiles; ++t) {
+      int32_t a = t * c->tile_tokens, m = n - a < c->tile_tokens ? n - a : c->tile_tokens;
+      orc_unpack(rec + at, m, D, bits, q + (int64_t)a * D);
+      at += orc_packed_bytes(bits, D, m);
+    }
+    return ORC_OK;
+  }
+  if (mode != 0) return ORC_ERR_CORRUPT;
+  int32_t tab_off[256];
+  int64_t ntab = 0;
+  for (int32_t i = 0; i < D; ++i) {
+    tab_off[i] = (int32_t)ntab;
+    int32_t h = orc_sym_bits(bits[i]);
+    if (h > 0) ntab += (int64_t)1 << h;
+  }
+  int64_t tb = table_bytes(bits, D);
+  if (size < tb + 4 * (int64_t)ntiles) return ORC_ERR_CORRUPT;
+  const uint16_t* freqs = (const uint16_t*)rec; /* little-endian host */
+  int64_t p = tb + 4 * (int64_t)ntiles;
+  int64_t maxsym = (int64_t)c->tile_tokens * D;
+  uint8_t* sym = (uint8_t*)malloc((size_t)maxsym + 1);
+  uint8_t* lane = (uint8_t*)malloc((size_t)maxsym + 1);
+  int32_t* tab = (int32_t*)malloc(sizeof(int32_t) * ((size_t)maxsym + 1));
+  int32_t* ns = (int32_t*)malloc(sizeof(int32_t) * ((size_t)maxsym + 1));
+  int st = ORC_OK;
+  for (int32_t t = 0; t < ntiles && st == ORC_OK; ++t) {
+    int32_t a = t * c->tile_tokens, m = n - a < c->tile_tokens ? n - a : c->tile_tokens;
+    uint8_t* qt = q + (int64_t)a * D;
+    uint32_t nw = get32(rec + tb + 4 * (int64_t)t);
+    int64_t need = 4 * (int64_t)lanes + 2 * (int64_t)nw + ((nw & 1) ? 2 : 0);
+    if (p + need > size) { st = ORC_ERR_CORRUPT; break; }
+    int64_t N = tile_sequence(NULL, m, D, bits, lanes, tab_off, NULL, lane, tab, ns);
+    uint32_t states[64];
+    memcpy(states, rec + p, 4 * (size_t)lanes);
+    uint16_t* w = (uint16_t*)malloc(sizeof(uint16_t) * ((size_t)nw + 1));
+    memcpy(w, rec + p + 4 * (int64_t)lanes, 2 * (size_t)nw);
+    st = orc_rans_decode_seq(N, lane, tab, ns, freqs, sb, lanes, states, w, nw, sym);
+    free(w);
+    if (st != ORC_OK) break;
+    p += need;
+    int64_t rb = raw_row_bytes(bits, D, m);
+    if (p + rb > size) { st = ORC_ERR_CORRUPT; break; }
+    /* symbols back into codes, then the raw bits */
+    int64_t s_at = 0;
+    for (int32_t i = 0; i < D; ++i) {
+      int32_t h = orc_sym_bits(bits[i]);
+      for (int32_t k = 0; k < m; ++k) qt[(int64_t)k * D + i] = h > 0 ? (uint8_t)(sym[s_at + k] << (bits[i] - h)) : 0;
+      if (h > 0) s_at += m;
+    }
+    for (int32_t i = 0; i < D; ++i) {
+      int32_t r = orc_raw_bits(bits[i]);
+      if (r == 0) continue;
+      for (int32_t k = 0; k < m; ++k) qt[(int64_t)k * D + i] |= (uint8_t)get_bits(rec + p, (int64_t)k * r, r);
+      p += 4 * (((int64_t)m * r + 31) / 32);
+    }
+  }
+  free(sym); free(lane); free(tab); free(ns);
+  if (st == ORC_OK && ((p + 15) & ~(int64_t)15) != size) st = ORC_ERR_CORRUPT;
+  return st;
 }
 
 /* ===================================================================== */
@@ -599,10 +902,6 @@ static int64_t r_index(const orc_config* c, int32_t u) {
   return (int64_t)l * H + h; /* only value sections carry r */
 }
 
-static void put32(uint8_t* p, uint32_t v) { memcpy(p, &v, 4); }
-static void put64(uint8_t* p, uint64_t v) { memcpy(p, &v, 8); }
-static uint32_t get32(const uint8_t* p) { uint32_t v; memcpy(&v, p, 4); return v; }
-static uint64_t get64(const uint8_t* p) { uint64_t v; memcpy(&v, p, 8); return v; }
 
 static const float* basis_of(const orc_config* c, const float* basis, int32_t l, int32_t s, int32_t h) {
   int64_t DD = (int64_t)c->head_dim * c->head_dim;
@@ -644,23 +943,20 @@ uint64_t orc_fingerprint(const orc_config* c, const float* basis) {
   return h;
 }
 
-static int64_t max_words(int64_t P, int32_t lanes, int32_t sb) {
-  /* each symbol adds at most sb bits of state, each word removes 16 */
-  return (P * (sb + 1)) / 16 + 2 * (int64_t)lanes + 2;
-}
-
+/* Largest record of a chunk of ntok tokens: never above its packed size
+ * (records fall back to the packed form), which is at most ntok budget / 8
+ * bytes plus a padding word per component row of each tile. */
 static int64_t max_record(const orc_config* c, int32_t ntok, int32_t budget) {
   int32_t D = c->head_dim;
   int32_t ntiles = (ntok + c->tile_tokens - 1) / c->tile_tokens;
   int32_t nz = budget < D ? budget : D; /* components with >= 1 bit */
-  int64_t rec = 512 + 4 * (int64_t)ntiles;
+  int64_t P = 0;
   for (int32_t t = 0; t < ntiles; ++t) {
     int32_t n = ntok - t * c->tile_tokens;
     if (n > c->tile_tokens) n = c->tile_tokens;
-    int64_t P = ((int64_t)n * budget + 7) / 8 + 4 * (int64_t)nz;
-    rec += 4 * (int64_t)c->rans_lanes + 2 * max_words(P, c->rans_lanes, c->rans_scale_bits) + 2;
+    P += ((int64_t)n * budget + 7) / 8 + 4 * (int64_t)nz;
   }
-  return align16(rec);
+  return align16(P);
 }
 
 int64_t orc_max_container_bytes(const orc_config* c, int32_t T) {
@@ -744,7 +1040,7 @@ static void write_header(const orc_config* c, const layout_t* lo, uint64_t fp,
                          int64_t total, uint8_t* out) {
   memset(out, 0, HDR_BYTES);
   memcpy(out + 0, "KVTC", 4);
-  put32(out + 4, 1);
+  put32(out + 4, 2);
   put32(out + 8, HDR_BYTES);
   put32(out + 12, 0);
   put32(out + 16, (uint32_t)c->layers);
@@ -928,9 +1224,6 @@ int orc_encode(const orc_config* c, const void* k, const void* v, int32_t T,
   float* coef = (float*)malloc(sizeof(float) * ((size_t)lo.T_mid * D + 1));
   float* r = (float*)malloc(sizeof(float) * ((size_t)lo.T_mid + 1));
   uint8_t* q = (uint8_t*)malloc((size_t)c->chunk_tokens * D + 1);
-  uint8_t* packed = (uint8_t*)malloc((size_t)c->chunk_tokens * D + 64 * (size_t)D + 1);
-  int64_t wcap = max_words((int64_t)c->tile_tokens * D + 4 * D, c->rans_lanes, c->rans_scale_bits);
-  uint16_t* words = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)wcap);
   int64_t pos = lo.chunks_off;
   side_t si;
   for (int32_t u = 0; u < lo.n_sections && st == ORC_OK; ++u) {
@@ -953,54 +1246,14 @@ int orc_encode(const orc_config* c, const void* k, const void* v, int32_t T,
         orc_quantize_sym(coef + (int64_t)t0 * D, n, D, si.bits[0], si.rcp[0], q, NULL);
       else
         orc_quantize(coef + (int64_t)t0 * D, n, D, si.bits, si.zero, si.rcp, q, NULL);
-      int32_t ntiles = (n + c->tile_tokens - 1) / c->tile_tokens;
-      int64_t tile_off[1024 + 1];
-      if (ntiles > 1024) { st = ORC_ERR_UNSUPPORTED; break; }
-      tile_off[0] = 0;
-      for (int32_t tl = 0; tl < ntiles; ++tl) {
-        int32_t a = tl * c->tile_tokens;
-        int32_t m = n - a < c->tile_tokens ? n - a : c->tile_tokens;
-        orc_pack(q + (int64_t)a * D, m, D, si.bits, packed + tile_off[tl]);
-        tile_off[tl + 1] = tile_off[tl] + orc_packed_bytes(si.bits, D, m);
-      }
-      int64_t P = tile_off[ntiles];
+      int32_t mode = 0;
+      int64_t size = orc_chunk_encode(c, si.bits, q, n, out + pos, cap - pos, &mode);
+      if (size < 0) { st = ORC_ERR_CAPACITY; break; }
       int64_t dir = lo.dir_off + ((int64_t)u * lo.chunks_per_sec + ch) * DIR_ENTRY;
-      if (P == 0) { /* every component at 0 bits: empty record */
-        if (cap < lo.chunks_off) { st = ORC_ERR_CAPACITY; break; }
-        put64(out + dir, (uint64_t)pos);
-        put32(out + dir + 8, 0);
-        put32(out + dir + 12, 0);
-        continue;
-      }
-      uint32_t counts[256] = {0};
-      for (int64_t b = 0; b < P; ++b) counts[packed[b]]++;
-      uint16_t freq[256];
-      orc_freq_normalize(counts, c->rans_scale_bits, freq);
-      int64_t start = pos;
-      int64_t p = pos + 512 + 4 * (int64_t)ntiles;
-      if (p > cap) { st = ORC_ERR_CAPACITY; break; }
-      memcpy(out + pos, freq, 512);
-      for (int32_t tl = 0; tl < ntiles && st == ORC_OK; ++tl) {
-        uint32_t states[64];
-        int64_t nw = orc_rans_encode(packed + tile_off[tl], tile_off[tl + 1] - tile_off[tl], freq,
-                                     c->rans_scale_bits, c->rans_lanes, states, words, wcap);
-        if (nw < 0) { st = ORC_ERR_CAPACITY; break; }
-        int64_t need = 4 * (int64_t)c->rans_lanes + 2 * nw + (nw & 1 ? 2 : 0);
-        if (p + need > cap) { st = ORC_ERR_CAPACITY; break; }
-        put32(out + pos + 512 + 4 * (int64_t)tl, (uint32_t)nw);
-        memcpy(out + p, states, 4 * (size_t)c->rans_lanes);
-        memcpy(out + p + 4 * (int64_t)c->rans_lanes, words, 2 * (size_t)nw);
-        if (nw & 1) memset(out + p + 4 * (int64_t)c->rans_lanes + 2 * nw, 0, 2);
-        p += need;
-      }
-      if (st != ORC_OK) break;
-      int64_t end = align16(p);
-      if (end > cap) { st = ORC_ERR_CAPACITY; break; }
-      memset(out + p, 0, (size_t)(end - p));
-      put64(out + dir, (uint64_t)start);
-      put32(out + dir + 8, (uint32_t)(end - start));
-      put32(out + dir + 12, 0);
-      pos = end;
+      put64(out + dir, (uint64_t)pos);
+      put32(out + dir + 8, (uint32_t)size);
+      put32(out + dir + 12, (uint32_t)mode);
+      pos += size;
     }
   }
   if (st == ORC_OK) {
@@ -1008,7 +1261,7 @@ int orc_encode(const orc_config* c, const void* k, const void* v, int32_t T,
     write_header(c, &lo, orc_fingerprint(c, basis), pos, out);
     *out_bytes = pos;
   }
-  free(x); free(coef); free(r); free(q); free(packed); free(words);
+  free(x); free(coef); free(r); free(q);
   free(cos_t); free(sin_t);
   return st;
 }
@@ -1018,7 +1271,7 @@ int orc_encode(const orc_config* c, const void* k, const void* v, int32_t T,
 static int parse_header(const orc_config* c, const float* basis, const uint8_t* in,
                         int64_t n, layout_t* lo) {
   if (n < HDR_BYTES) return ORC_ERR_CORRUPT;
-  if (memcmp(in, "KVTC", 4) != 0 || get32(in + 4) != 1 || get32(in + 8) != HDR_BYTES)
+  if (memcmp(in, "KVTC", 4) != 0 || get32(in + 4) != 2 || get32(in + 8) != HDR_BYTES)
     return ORC_ERR_CORRUPT;
   orc_config h;
   memset(&h, 0, sizeof h);
@@ -1071,54 +1324,18 @@ static int parse_header(const orc_config* c, const float* basis, const uint8_t* 
 /* Decode the codes of chunk ch of section u into q[n][D]. */
 static int decode_chunk_codes(const orc_config* c, const layout_t* lo, const uint8_t* in,
                               int64_t total, int32_t u, int32_t ch, const uint8_t* bits,
-                              uint8_t* q, uint8_t* packed, uint8_t* syms) {
-  int32_t D = c->head_dim;
+                              uint8_t* q) {
   int32_t t0 = ch * c->chunk_tokens;
   int32_t n = lo->T_mid - t0 < c->chunk_tokens ? lo->T_mid - t0 : c->chunk_tokens;
-  int32_t ntiles = (n + c->tile_tokens - 1) / c->tile_tokens;
   int64_t dir = lo->dir_off + ((int64_t)u * lo->chunks_per_sec + ch) * DIR_ENTRY;
   uint64_t off = get64(in + dir);
   uint32_t size = get32(in + dir + 8);
-  if (get32(in + dir + 12) != 0) return ORC_ERR_CORRUPT;
-  int64_t P = 0;
-  for (int32_t tl = 0; tl < ntiles; ++tl) {
-    int32_t m = n - tl * c->tile_tokens < c->tile_tokens ? n - tl * c->tile_tokens : c->tile_tokens;
-    P += orc_packed_bytes(bits, D, m);
-  }
-  if (P == 0) {
-    if (size != 0) return ORC_ERR_CORRUPT;
-    for (int64_t i = 0; i < (int64_t)n * D; ++i) q[i] = 0;
-    return ORC_OK;
-  }
-  if (off < (uint64_t)lo->chunks_off || (off & 15) || off > (uint64_t)total || size > (uint64_t)total - off)
+  uint32_t mode = get32(in + dir + 12);
+  if (mode > 1) return ORC_ERR_CORRUPT;
+  if (size > 0 && (off < (uint64_t)lo->chunks_off || (off & 15) || off > (uint64_t)total ||
+                   size > (uint64_t)total - off))
     return ORC_ERR_CORRUPT;
-  const uint8_t* rec = in + off;
-  if (size < 512 + 4 * (uint32_t)ntiles) return ORC_ERR_CORRUPT;
-  uint16_t freq[256];
-  memcpy(freq, rec, 512);
-  int64_t p = 512 + 4 * (int64_t)ntiles;
-  int64_t done = 0;
-  for (int32_t tl = 0; tl < ntiles; ++tl) {
-    int32_t a = tl * c->tile_tokens;
-    int32_t m = n - a < c->tile_tokens ? n - a : c->tile_tokens;
-    int64_t Pt = orc_packed_bytes(bits, D, m);
-    uint32_t nw = get32(rec + 512 + 4 * (int64_t)tl);
-    int64_t need = 4 * (int64_t)c->rans_lanes + 2 * (int64_t)nw + (nw & 1 ? 2 : 0);
-    if (p + need > (int64_t)size) return ORC_ERR_CORRUPT;
-    uint32_t states[64];
-    memcpy(states, rec + p, 4 * (size_t)c->rans_lanes);
-    uint16_t* w = (uint16_t*)malloc(sizeof(uint16_t) * ((size_t)nw + 1));
-    memcpy(w, rec + p + 4 * (int64_t)c->rans_lanes, 2 * (size_t)nw);
-    int st = orc_rans_decode(states, w, nw, freq, c->rans_scale_bits, c->rans_lanes, Pt, syms);
-    free(w);
-    if (st != ORC_OK) return st;
-    memcpy(packed + done, syms, (size_t)Pt);
-    orc_unpack(packed + done, m, D, bits, q + (int64_t)a * D);
-    done += Pt;
-    p += need;
-  }
-  if (align16(p) != (int64_t)size) return ORC_ERR_CORRUPT;
-  return ORC_OK;
+  return orc_chunk_decode(c, bits, size > 0 ? in + off : in, size, (int32_t)mode, n, q);
 }
 
 /* Reconstruct the middle rows of section u (before RoPE and the output
@@ -1145,8 +1362,6 @@ static int decode_section_mid(const orc_config* c, const float* basis, const lay
     for (int64_t i = 0; i < (int64_t)D * D; ++i) Bp[i] = round_p(B[i], c->dtype);
   }
   uint8_t* q = (uint8_t*)malloc((size_t)c->chunk_tokens * D + 1);
-  uint8_t* packed = (uint8_t*)malloc((size_t)c->chunk_tokens * D + 64 * (size_t)D + 1);
-  uint8_t* syms = (uint8_t*)malloc((size_t)c->tile_tokens * D + 64 * (size_t)D + 1);
   float chat[256], tmp[256];
   int st = ORC_OK;
   int sym = sym_section(c, u);
@@ -1154,7 +1369,7 @@ static int decode_section_mid(const orc_config* c, const float* basis, const lay
   for (int32_t ch = 0; ch < lo->chunks_per_sec && st == ORC_OK; ++ch) {
     int32_t t0 = ch * c->chunk_tokens;
     int32_t n = lo->T_mid - t0 < c->chunk_tokens ? lo->T_mid - t0 : c->chunk_tokens;
-    st = decode_chunk_codes(c, lo, in, total, u, ch, bits, q, packed, syms);
+    st = decode_chunk_codes(c, lo, in, total, u, ch, bits, q);
     if (st != ORC_OK) break;
     for (int32_t t = 0; t < n; ++t) {
       const uint8_t* qr = q + (int64_t)t * D;
@@ -1178,7 +1393,7 @@ static int decode_section_mid(const orc_config* c, const float* basis, const lay
       }
     }
   }
-  free(q); free(packed); free(syms); free(Bp);
+  free(q); free(Bp);
   return st;
 }
 
@@ -1295,12 +1510,7 @@ int orc_section_codes(const orc_config* c, const float* basis, const uint8_t* in
   memcpy(bits, rec, (size_t)D);
   for (int32_t i = 0; i < D; ++i)
     if (bits[i] > c->max_bits) return ORC_ERR_CORRUPT;
-  uint8_t* packed = (uint8_t*)malloc((size_t)c->chunk_tokens * D + 64 * (size_t)D + 1);
-  uint8_t* syms = (uint8_t*)malloc((size_t)c->tile_tokens * D + 64 * (size_t)D + 1);
   for (int32_t ch = 0; ch < lo.chunks_per_sec && st == ORC_OK; ++ch)
-    st = decode_chunk_codes(c, &lo, in, total, u, ch, bits,
-                            q_out + (int64_t)ch * c->chunk_tokens * D, packed, syms);
-  free(packed);
-  free(syms);
+    st = decode_chunk_codes(c, &lo, in, total, u, ch, bits, q_out + (int64_t)ch * c->chunk_tokens * D);
   return st;
 }

@@ -102,13 +102,30 @@ void orc_quantize_sym(const float* c, int64_t N, int32_t D, int32_t b, float rcp
 int64_t orc_packed_bytes(const uint8_t* bits, int32_t D, int64_t ntok);
 void orc_pack(const uint8_t* q, int64_t ntok, int32_t D, const uint8_t* bits, uint8_t* out);
 void orc_unpack(const uint8_t* in, int64_t ntok, int32_t D, const uint8_t* bits, uint8_t* q);
-void orc_freq_normalize(const uint32_t* counts, int32_t scale_bits, uint16_t* freq);
+void orc_freq_normalize(const uint32_t* counts, int32_t n_sym, int32_t scale_bits, uint16_t* freq);
+int64_t orc_rans_encode_seq(int64_t N, const uint8_t* sym, const uint8_t* lane, const int32_t* tab,
+                            const int32_t* n_sym, const uint16_t* freqs, int32_t scale_bits,
+                            int32_t lanes, uint32_t* states, uint16_t* words, int64_t words_cap);
+int orc_rans_decode_seq(int64_t N, const uint8_t* lane, const int32_t* tab, const int32_t* n_sym,
+                        const uint16_t* freqs, int32_t scale_bits, int32_t lanes,
+                        const uint32_t* states, const uint16_t* words, int64_t nwords,
+                        uint8_t* sym);
 int64_t orc_rans_encode(const uint8_t* sym, int64_t N, const uint16_t* freq,
                         int32_t scale_bits, int32_t lanes, uint32_t* states,
                         uint16_t* words, int64_t words_cap);
 int orc_rans_decode(const uint32_t* states, const uint16_t* words, int64_t nwords,
                     const uint16_t* freq, int32_t scale_bits, int32_t lanes,
                     int64_t N, uint8_t* sym);
+/* Entropy-coding classes of a component of width b: symbol bits (the top
+ * min(b, 4) bits of codes of width >= 2) and raw bits (the rest). */
+int32_t orc_sym_bits(int32_t b);
+int32_t orc_raw_bits(int32_t b);
+/* One chunk record from its codes q[n][D]; *mode = 0 coded, 1 packed.
+ * Returns the size (multiple of 16) or -1 when cap is too small. */
+int64_t orc_chunk_encode(const orc_config* cfg, const uint8_t* bits, const uint8_t* q, int32_t n,
+                         uint8_t* rec, int64_t cap, int32_t* mode);
+int orc_chunk_decode(const orc_config* cfg, const uint8_t* bits, const uint8_t* rec, int64_t size,
+                     int32_t mode, int32_t n, uint8_t* q);
 
 /* ---- container ------------------------------------------------------- */
 int orc_check_config(const orc_config* cfg);

@@ -225,7 +225,7 @@ def oracle_config(w: Workload, **over) -> dict:
         dtype=0 if w.dtype == "fp32" else 1, transform=0 if w.transform == "pca" else 1,
         sink_tokens=w.sink, recent_tokens=w.recent, bits_k=w.bits_k, bits_v=w.bits_v,
         max_bits=8, rope_keys=1, rope_style=0, rope_theta=w.theta, rans_scale_bits=12,
-        rans_lanes=w.lanes, chunk_tokens=1024, tile_tokens=256, basis_per_head=0, wht_keys=1,
+        rans_lanes=w.lanes, chunk_tokens=4096, tile_tokens=256, basis_per_head=0, wht_keys=1,
     )
     cfg.update(over)
     return cfg

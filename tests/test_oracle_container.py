@@ -202,9 +202,13 @@ def test_wht_path(orc):
 
 
 def test_damaged_containers_are_refused(orc):
-    cfg, k, v, B = _tiny(orc)
+    w = synth.WORKLOADS["tiny"]
+    T = 2048  # long enough that the chunk records are coded rather than packed
+    K, V = synth.generate(w, tokens=T)
+    k, v = synth.to_numpy_bits(K), synth.to_numpy_bits(V)
+    cfg = synth.oracle_config(w)
+    B = orc.fit_pca_basis(cfg, k, v)
     data = bytearray(orc.encode(cfg, k, v, B))
-    T = 256
 
     def status(d, basis=B):
         return orc.decode_status(cfg, bytes(d), basis, T)
@@ -213,19 +217,31 @@ def test_damaged_containers_are_refused(orc):
     bad = bytearray(data)
     bad[0] ^= 1
     assert status(bad) == orc.ERR_CORRUPT  # magic
+    bad = bytearray(data)
+    bad[4] = 1
+    assert status(bad) == orc.ERR_CORRUPT  # container version
     assert status(data[:-16]) == orc.ERR_CORRUPT  # truncated
     assert status(data[:100]) == orc.ERR_CORRUPT
     assert status(data, B * -1.0) == orc.ERR_CORRUPT  # another basis: fingerprint
     pc = orc.parse_container(bytes(data), cfg, T)
+    assert list(pc["modes"]) == [0, 0]
     rec = int(pc["offsets"][0])
     bad = bytearray(data)
-    bad[rec + 3] ^= 0x40  # frequency table no longer sums to 4096
+    bad[rec + 3] ^= 0x40  # the first frequency table no longer sums to 4096
+    assert status(bad) == orc.ERR_CORRUPT
+    d0 = int(np.frombuffer(bytes(data[152:160]), np.uint64)[0])  # the chunk directory
+    for mode in (1, 2):  # a record mode that disagrees with the record, or no mode at all
+        bad = bytearray(data)
+        bad[d0 + 12: d0 + 16] = np.uint32(mode).tobytes()
+        assert status(bad) == orc.ERR_CORRUPT
+    bad = bytearray(data)
+    bad[d0: d0 + 8] = np.uint64(2 ** 64 - 256).tobytes()  # an offset that would wrap a bound
     assert status(bad) == orc.ERR_CORRUPT
     # flipped stream words: rejected by the final-state check, or at least not silent
     kd, vd = orc.decode(cfg, bytes(data), B, T)
     hits = 0
     rng = np.random.default_rng(0)
-    for pos in rng.integers(rec + 700, rec + int(pc["sizes"][0]) - 8, 20):
+    for pos in rng.integers(rec + 2000, rec + int(pc["sizes"][0]) - 8, 20):
         bad = bytearray(data)
         bad[pos] ^= 0x5A
         st = status(bad)
@@ -234,7 +250,7 @@ def test_damaged_containers_are_refused(orc):
         else:
             kb, _ = orc.decode(cfg, bytes(bad), B, T)
             assert not np.array_equal(kb, kd)
-    assert hits >= 15
+    assert hits >= 10
 
 
 def test_nonfinite_input(orc):
