@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--bits", type=float, default=None, help="bits per component (K and V)")
     ap.add_argument("--tokens", type=int, default=None)
     ap.add_argument("--layers", type=int, default=None)
-    ap.add_argument("--chunk-tokens", type=int, default=1024)
+    ap.add_argument("--chunk-tokens", type=int, default=4096)
     ap.add_argument("--tile-tokens", type=int, default=256)
     ap.add_argument("--cpu-layers", type=int, default=8,
                     help="layers of the workload the CPU oracle baseline codes")
@@ -270,8 +270,18 @@ def cpu_baseline(w, cfg, K, V, basis, layers):
     oracle.decode(c1, data, b, K.shape[2], oracle.BF16)
     t2 = time.perf_counter()
     raw = k.nbytes + v.nbytes
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": raw / (t2 - t0) / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "host_cpus": os.cpu_count(), "host_cpu_model": model,
         "sample": f"{layers} of {K.shape[0]} layers ({layers * 2 * K.shape[1]} sections, "
                   f"{raw} raw bytes): oracle encode {t1 - t0:.2f} s + decode {t2 - t1:.2f} s, "
                   "single thread, throughput extrapolates linearly in sections",

@@ -90,9 +90,11 @@ enum { KVTC_ROPE_HALF = 0, KVTC_ROPE_INTERLEAVED = 1 };
  *                   t * theta^(-2j/D) in fp64, cos/sin rounded to fp32
  *  rans_scale_bits  frequency precision, 8..12 (M = 2^bits)
  *  rans_lanes       interleaved rANS states per stream, 16 or 32
- *  chunk_tokens     tokens of a section sharing one frequency table
+ *  chunk_tokens     tokens of a section's chunk: one container record with
+ *                   a frequency table per coded component; at most 32
+ *                   tiles, and a multiple of 1024 when longer than 1024
  *  tile_tokens      tokens per packed tile = one rANS stream; divides
- *                   chunk_tokens
+ *                   chunk_tokens (and 1024 when the chunk is longer)
  *  basis_per_head   0: basis [L,2,D,D]; 1: [L,2,H,D,D]
  *  wht_keys         WHT path: 1 = keys are normalised and transformed too,
  *                   0 = keys are quantised directly
@@ -256,26 +258,27 @@ kvtc_status kvtc_test_coeffs(kvtc_plan_t plan, const void* k, const void* v, int
                              int32_t sec_begin, int32_t sec_end, float* out, float* r_out,
                              hipStream_t stream);
 
-/* One interleaved rANS stream with the device coder: encode N bytes `sym`
- * with table `freq` (u16[256], sums to 2^scale_bits) into states u32[lanes]
- * and words u16[words_cap] (emission order), word count to *nwords (device
- * int64).  All pointers are device memory.  N must be below 2^30
- * (KVTC_ERR_INVALID_ARG otherwise); a words_cap above 2^30 acts as 2^30. */
-kvtc_status kvtc_test_rans_encode(const uint8_t* sym, int64_t N, const uint16_t* freq,
-                                  int32_t scale_bits, int32_t lanes, uint32_t* states,
-                                  uint16_t* words, int64_t words_cap, int64_t* nwords,
-                                  hipStream_t stream);
+/* Frequency tables with the record encoder's normaliser ("KVTC: The
+ * Open-Source KV Cache Codec That Treats LLM Memory Like Media", rANS Makes
+ * the Last Mile Smaller): n tables, counts u32 [n][16] with alphabet[i]
+ * (1..16) meaningful entries each -> freq u16 [n][16] summing to
+ * 2^scale_bits (entries past the alphabet are 0).  Present symbols get
+ * max(1, round-half-up(count M / N)); a shortfall goes to the most frequent
+ * symbol, an excess is taken one unit at a time from the largest frequency
+ * above 1 (lowest symbol on ties).  All pointers are device memory. */
+kvtc_status kvtc_test_freq_tables(const uint32_t* counts, const int32_t* alphabet, int32_t n,
+                                  int32_t scale_bits, uint16_t* freq, hipStream_t stream);
 
-/* Decode one stream; status (device int32) gets KVTC_OK or KVTC_ERR_CORRUPT. */
-kvtc_status kvtc_test_rans_decode(const uint32_t* states, const uint16_t* words,
-                                  int64_t nwords, const uint16_t* freq, int32_t scale_bits,
-                                  int32_t lanes, int64_t N, uint8_t* sym, int32_t* status,
-                                  hipStream_t stream);
-
-/* Frequency table of a byte histogram with the device normaliser:
- * counts u32[256] -> freq u16[256] (device). */
-kvtc_status kvtc_test_freq_table(const uint32_t* counts, int32_t scale_bits, uint16_t* freq,
-                                 hipStream_t stream);
+/* The packed tiles of one section as the last kvtc_encode (or kvtc_decode)
+ * that used ws left them in the workspace: *blocks work blocks of
+ * *slot_bytes bytes each (the tiles of a block back to back, each tile the
+ * channel-major rows of its codes, "Compress the most expensive bytes in
+ * AI", KV & tensor mode).  With out = NULL only the sizes are returned;
+ * otherwise out (device, out_bytes >= blocks * slot_bytes) receives them
+ * (asynchronous on `stream`). */
+kvtc_status kvtc_test_packed_tiles(kvtc_plan_t plan, const void* ws, int32_t T, int32_t section,
+                                   void* out, size_t out_bytes, int32_t* blocks, size_t* slot_bytes,
+                                   hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -47,8 +47,8 @@ __global__ __launch_bounds__(256) void k_dec_pca(const Params p) {
   constexpr int NB = DecGeo<D, DT>::NB, KPL = DecGeo<D, DT>::KPL, CS = DecGeo<D, DT>::CS;
   const int u = blockIdx.y, ch = blockIdx.x;
   const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
-  const int t0 = ch * p.chunk_tokens;
-  const int n = min(p.chunk_tokens, p.T_mid - t0);
+  const int t0 = ch * p.blk_tokens;
+  const int n = min(p.blk_tokens, p.T_mid - t0);
   if (n <= 0) return;
   if (get_status(p.ws, p.w) & (1u << KVTC_ERR_CORRUPT)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void k_dec_pca(const Params p) {
     if (lane == 0) s_full = v0;
   }
   __syncthreads();
-  const uint32_t* slot = reinterpret_cast<const uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot);
+  const uint32_t* slot = reinterpret_cast<const uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.blks_per_sec + ch) * p.w.packed_slot);
   // dequantisation role: fixed component per thread
   const int di = tid % D;
   const uint32_t db = s_bits[di];
@@ -244,8 +244,8 @@ __global__ __launch_bounds__(256) void k_dec_wht(const Params p) {
   constexpr int D = 128;
   const int u = blockIdx.y, ch = blockIdx.x;
   const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
-  const int t0 = ch * p.chunk_tokens;
-  const int n = min(p.chunk_tokens, p.T_mid - t0);
+  const int t0 = ch * p.blk_tokens;
+  const int n = min(p.blk_tokens, p.T_mid - t0);
   if (n <= 0) return;
   if (get_status(p.ws, p.w) & (1u << KVTC_ERR_CORRUPT)) return;
   const int tid = threadIdx.x, q = tid & 15, grp = tid >> 4;
@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void k_dec_wht(const Params p) {
   }
   const int64_t r_index = !transform ? -1 : (p.wht_keys ? (int64_t)u : (int64_t)l * p.H + h);
   const float* rarea = reinterpret_cast<const float*>(p.in + p.r_off);
-  const uint32_t* slot = reinterpret_cast<const uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot);
+  const uint32_t* slot = reinterpret_cast<const uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.blks_per_sec + ch) * p.w.packed_slot);
   const uint32_t full_row = (uint32_t)((p.tile_tokens * (int)b + 31) >> 5);
   const int ntiles = (n + p.tile_tokens - 1) / p.tile_tokens;
   for (int tl = 0; tl < ntiles; ++tl) {
@@ -424,8 +424,8 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = wave & 1, th = wave >> 1;
   const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
-  const int t0 = ch * p.chunk_tokens;
-  const int n = min(p.chunk_tokens, p.T_mid - t0);
+  const int t0 = ch * p.blk_tokens;
+  const int n = min(p.blk_tokens, p.T_mid - t0);
   const bool rope = (s == 0) && p.rope_keys;
   const bool half_style = p.rope_style == KVTC_ROPE_HALF;
   const int64_t lh_row0 = ((int64_t)l * p.H + h) * p.T;
@@ -440,7 +440,7 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
   // the RoPE table as a buffer resource (one offset register per load)
   const __amdgpu_buffer_rsrc_t rrsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float2*>(p.rope), 0, rope ? p.T * 512 : 0, 0x00020000);
-  const uint32_t* slot = reinterpret_cast<const uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot);
+  const uint32_t* slot = reinterpret_cast<const uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.blks_per_sec + ch) * p.w.packed_slot);
 
   // widths of this wave's octets (sorted positions 8 c8 .. +7, c8 = 4 j8 +
   // wave), one byte each: the single width of the octet, 0 when it holds no
@@ -735,11 +735,11 @@ __global__ __launch_bounds__(256, 3) void k_dec_pca128(const Params p0) {
   const Params p = at_seq(p0, blockIdx.z);
   constexpr int D = 128;
   const int u = blockIdx.y, ch = blockIdx.x;
-  if (ch >= p.chunks_per_sec) return;
+  if (ch >= p.blks_per_sec) return;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
-  if (min(p.chunk_tokens, p.T_mid - ch * p.chunk_tokens) <= 0) return;
+  if (min(p.blk_tokens, p.T_mid - ch * p.blk_tokens) <= 0) return;
 
   __shared__ DecKInfo s_ki[D];
   __shared__ uint4 s_kw[D];          // sorted order: {b, row byte offset in the tile, scale, zero}
@@ -802,10 +802,10 @@ __global__ __launch_bounds__(256, 3) void k_dec_pca128(const Params p0) {
   {
     uint32_t* const tb2 = reinterpret_cast<uint32_t*>(stage + 64 * 17);
     const uint32_t* slot0 =
-        reinterpret_cast<const uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot);
+        reinterpret_cast<const uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.blks_per_sec + ch) * p.w.packed_slot);
     const bool clear = reinterpret_cast<uint8_t*>(tb2) - reinterpret_cast<uint8_t*>(dlds) >= 128 * kBS * 2;
     if (clear && (reinterpret_cast<uintptr_t>(slot0) & 15u) == 0) {
-      const int nt0 = min(p.tile_tokens, min(p.chunk_tokens, p.T_mid - ch * p.chunk_tokens));
+      const int nt0 = min(p.tile_tokens, min(p.blk_tokens, p.T_mid - ch * p.blk_tokens));
       uint32_t w = ((uint32_t)(nt0 * (int)s_b[2 * lane] + 31) >> 5) + ((uint32_t)(nt0 * (int)s_b[2 * lane + 1] + 31) >> 5);
 #pragma unroll
       for (int o = 32; o > 0; o >>= 1) w += __shfl_xor(w, o, 64);
@@ -900,7 +900,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_pca128(const Params p0) {
 }
 
 hipError_t launch_dec_transform(const Params& p, hipStream_t s) {
-  dim3 grid(p.chunks_per_sec, p.n_sections), block(256);
+  dim3 grid(p.blks_per_sec, p.n_sections), block(256);
   if (p.transform == KVTC_WHT) {
     hipLaunchKernelGGL(k_dec_wht, grid, block, 0, s, p);
     return hipGetLastError();
@@ -918,7 +918,7 @@ hipError_t launch_dec_transform(const Params& p, hipStream_t s) {
     if (lds3 < bbytes) lds3 = bbytes;
     if (lds4 < bbytes) lds4 = bbytes;
     if (lds4 <= 140 * 1024) {
-      dim3 g4(p.chunks_per_sec, p.n_sections, seq_grid(p));
+      dim3 g4(p.blks_per_sec, p.n_sections, seq_grid(p));
       if (p.n_seqs > 0) {
         if (ob != 2) return hipErrorInvalidValue;
         (void)hipFuncSetAttribute((const void*)k_dec_pca128<3, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3);

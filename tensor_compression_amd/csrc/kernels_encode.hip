@@ -234,8 +234,8 @@ __global__ __launch_bounds__(256) void k_enc_pca(const Params p, int sec0, float
   if (MODE == 0 && p.n_seqs == 0 && blockIdx.x == 0 && blockIdx.y == 0) clear_status_block(p);
   const int u = blockIdx.y + sec0, ch = blockIdx.x;
   const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
-  const int t0 = ch * p.chunk_tokens;
-  const int n = min(p.chunk_tokens, p.T_mid - t0);
+  const int t0 = ch * p.blk_tokens;
+  const int n = min(p.blk_tokens, p.T_mid - t0);
   if (n <= 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, r = lane & 15;
   const void* src = s ? p.v : p.k;
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(256) void k_enc_pca(const Params p, int sec0, float
         a += s_sum[w2][i]; b += s_sq[w2][i];
         c = fminf(c, s_mn[w2][i]); d = fmaxf(d, s_mx[w2][i]);
       }
-      int64_t idx = ((int64_t)u * p.chunks_per_sec + ch) * D + i;
+      int64_t idx = ((int64_t)u * p.blks_per_sec + ch) * D + i;
       reinterpret_cast<double*>(p.ws + p.w.part_sum)[idx] = a;
       reinterpret_cast<double*>(p.ws + p.w.part_sq)[idx] = b;
       reinterpret_cast<float*>(p.ws + p.w.part_min)[idx] = c;
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256) void k_enc_pca(const Params p, int sec0, float
       __syncthreads();
       full_words = s_full;
     }
-    uint32_t* slot = reinterpret_cast<uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot);
+    uint32_t* slot = reinterpret_cast<uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.blks_per_sec + ch) * p.w.packed_slot);
     const int ntiles = (n + p.tile_tokens - 1) / p.tile_tokens;
     for (int tl = 0; tl < ntiles; ++tl) {
       const int ta = tl * p.tile_tokens;
@@ -548,8 +548,8 @@ __global__ __launch_bounds__(256) void k_enc_wht(const Params p, int sec0, float
   if (MODE == 0 && p.n_seqs == 0 && blockIdx.x == 0 && blockIdx.y == 0) clear_status_block(p);
   const int u = blockIdx.y + sec0, ch = blockIdx.x;
   const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
-  const int t0 = ch * p.chunk_tokens;
-  const int n = min(p.chunk_tokens, p.T_mid - t0);
+  const int t0 = ch * p.blk_tokens;
+  const int n = min(p.blk_tokens, p.T_mid - t0);
   if (n <= 0) return;
   const int lane = threadIdx.x & 63, q = lane & 15, grp = threadIdx.x >> 4;  // 16 tokens per pass
   const void* src = s ? p.v : p.k;
@@ -588,7 +588,7 @@ __global__ __launch_bounds__(256) void k_enc_wht(const Params p, int sec0, float
   }
   const uint32_t row_words_full = (uint32_t)((p.tile_tokens * (int)bl + 31) >> 5);
   const int ntiles = (n + p.tile_tokens - 1) / p.tile_tokens;
-  uint32_t* slot = MODE == 1 ? reinterpret_cast<uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot) : nullptr;
+  uint32_t* slot = MODE == 1 ? reinterpret_cast<uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.blks_per_sec + ch) * p.w.packed_slot) : nullptr;
 
   for (int tl = 0; tl < ntiles; ++tl) {
     const int ta = tl * p.tile_tokens;
@@ -754,7 +754,7 @@ __global__ __launch_bounds__(256) void k_enc_wht(const Params p, int sec0, float
         a += s_sum[w2][i]; b += s_sq[w2][i];
         c = fminf(c, s_mn[w2][i]); d = fmaxf(d, s_mx[w2][i]);
       }
-      int64_t idx = ((int64_t)u * p.chunks_per_sec + ch) * D + i;
+      int64_t idx = ((int64_t)u * p.blks_per_sec + ch) * D + i;
       reinterpret_cast<double*>(p.ws + p.w.part_sum)[idx] = a;
       reinterpret_cast<double*>(p.ws + p.w.part_sq)[idx] = b;
       reinterpret_cast<float*>(p.ws + p.w.part_min)[idx] = c;
@@ -874,8 +874,8 @@ __global__ __launch_bounds__(256, MODE == 0 ? 3 : 1) void k_enc128(const Params 
   constexpr int D = 128;
   const int u = blockIdx.y + sec0, ch = blockIdx.x;
   const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
-  const int t0 = ch * p.chunk_tokens;
-  const int n = min(p.chunk_tokens, p.T_mid - t0);
+  const int t0 = ch * p.blk_tokens;
+  const int n = min(p.blk_tokens, p.T_mid - t0);
   if (n <= 0) return;
   if (MODE == 1 && (get_status(p.ws, p.w) & (1u << KVTC_ERR_NONFINITE))) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
@@ -925,7 +925,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? 3 : 1) void k_enc128(const Params 
       qmax[m] = (float)((1u << bl[m]) - 1u);
     }
     for (int i = 0; i < D; ++i) full_words += (uint32_t)((p.tile_tokens * (int)sd.bits[i] + 31) >> 5);
-    slot = reinterpret_cast<uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot);
+    slot = reinterpret_cast<uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.blks_per_sec + ch) * p.w.packed_slot);
   }
 
   // ---- staging registers and helpers
@@ -1219,7 +1219,7 @@ __global__ __launch_bounds__(256, MODE == 0 ? 3 : 1) void k_enc128(const Params 
         mx[m] = fmaxf(mx[m], __shfl_xor(mx[m], o, 64));
       }
       if (g == 0) {
-        const int64_t idx = ((int64_t)u * p.chunks_per_sec + ch) * D + (2 * wave + m) * 16 + r;
+        const int64_t idx = ((int64_t)u * p.blks_per_sec + ch) * D + (2 * wave + m) * 16 + r;
         reinterpret_cast<double*>(p.ws + p.w.part_sum)[idx] = sum[m];
         reinterpret_cast<double*>(p.ws + p.w.part_sq)[idx] = sq[m];
         reinterpret_cast<float*>(p.ws + p.w.part_min)[idx] = mn[m];
@@ -1246,7 +1246,7 @@ static size_t tile_lds_bytes(const Params& p) {
 }
 
 hipError_t launch_enc_transform(const Params& p, int mode, hipStream_t s) {
-  dim3 grid(p.chunks_per_sec, p.n_sections, seq_grid(p)), block(256);
+  dim3 grid(p.blks_per_sec, p.n_sections, seq_grid(p)), block(256);
   size_t lds = mode == 1 ? quant_lds_bytes(p, tile_lds_bytes(p)) : 0;
   if (p.transform == KVTC_WHT) {
     if (mode == 0) hipLaunchKernelGGL(k_enc_wht<0>, grid, block, 0, s, p, 0, (float*)nullptr, (float*)nullptr);
@@ -1282,7 +1282,7 @@ hipError_t launch_enc_transform(const Params& p, int mode, hipStream_t s) {
 
 hipError_t launch_coeffs(const Params& p, int sec_begin, int sec_end, float* out, float* r_out,
                          hipStream_t s) {
-  dim3 grid(p.chunks_per_sec, sec_end - sec_begin), block(256);
+  dim3 grid(p.blks_per_sec, sec_end - sec_begin), block(256);
   if (p.transform == KVTC_WHT) {
     hipLaunchKernelGGL(k_enc_wht<2>, grid, block, 0, s, p, sec_begin, out, r_out);
     return hipGetLastError();
@@ -1340,13 +1340,13 @@ __global__ __launch_bounds__(64) void k_enc_alloc(const Params p0) {
       double a = 0.0, b = 0.0;
       float lo = INFINITY, hi = -INFINITY;
       // the chunks' partials, eight chunks' loads in flight at a time
-      for (int c0 = 0; c0 < p.chunks_per_sec; c0 += 8) {
+      for (int c0 = 0; c0 < p.blks_per_sec; c0 += 8) {
         double pa[8], pb[8];
         float pl[8], ph[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const int ch = min(c0 + k, p.chunks_per_sec - 1);
-          const int64_t idx = ((int64_t)u * p.chunks_per_sec + ch) * D + i;
+          const int ch = min(c0 + k, p.blks_per_sec - 1);
+          const int64_t idx = ((int64_t)u * p.blks_per_sec + ch) * D + i;
           pa[k] = reinterpret_cast<const double*>(p.ws + p.w.part_sum)[idx];
           pb[k] = reinterpret_cast<const double*>(p.ws + p.w.part_sq)[idx];
           pl[k] = reinterpret_cast<const float*>(p.ws + p.w.part_min)[idx];
@@ -1354,7 +1354,7 @@ __global__ __launch_bounds__(64) void k_enc_alloc(const Params p0) {
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          if (c0 + k < p.chunks_per_sec) {
+          if (c0 + k < p.blks_per_sec) {
             a += pa[k];
             b += pb[k];
             lo = fminf(lo, pl[k]);

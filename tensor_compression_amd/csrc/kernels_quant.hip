@@ -185,14 +185,14 @@ __global__ __launch_bounds__(64 * kQWaves, 4) void k_quant128(const Params p0) {
   uint32_t refined = 0;
   // this wave's tile: the f-th tile of the section
   const int f = blockIdx.x * kQWaves + wave;
-  const int ch = f / p.tiles_per_chunk, tl = f % p.tiles_per_chunk;
-  const int t0 = ch * p.chunk_tokens;
-  const int n = min(p.chunk_tokens, p.T_mid - t0);
+  const int ch = f / p.tiles_per_blk, tl = f % p.tiles_per_blk;
+  const int t0 = ch * p.blk_tokens;
+  const int n = min(p.blk_tokens, p.T_mid - t0);
   const int ta = tl * p.tile_tokens;
-  if (ch < p.chunks_per_sec && ta < n) {
+  if (ch < p.blks_per_sec && ta < n) {
     const int nt = min(p.tile_tokens, n - ta);
     const int64_t row0 = ((int64_t)l * p.H + h) * (pre ? p.T_mid : p.T) + (pre ? 0 : p.mid_begin) + t0 + ta;
-    uint32_t* tile = reinterpret_cast<uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.chunks_per_sec + ch) * p.w.packed_slot) +
+    uint32_t* tile = reinterpret_cast<uint32_t*>(p.ws + p.w.packed + (int64_t)(u * p.blks_per_sec + ch) * p.w.packed_slot) +
                      (int64_t)tl * fw;
     // row offsets of this tile (natural order scan), by sorted position
     {
@@ -476,7 +476,7 @@ hipError_t launch_quant128(const Params& p, hipStream_t s) {
   if (segw > 2048) return hipErrorInvalidValue;
   const int segstride = (segw + 4 + 3) & ~3;
   const size_t lds = (size_t)8 * 4 * 64 * 16 + (size_t)kQWaves * segstride * 4;
-  const int tiles = p.chunks_per_sec * p.tiles_per_chunk;
+  const int tiles = p.blks_per_sec * p.tiles_per_blk;
   (void)hipFuncSetAttribute((const void*)k_quant128, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL(k_quant128, dim3((tiles + kQWaves - 1) / kQWaves, p.n_sections, seq_grid(p)), dim3(64 * kQWaves), lds, s, p);
   return hipGetLastError();

@@ -18,27 +18,25 @@ using namespace kvtc;
 
 namespace kvtc {
 
+// Worst-case container: the fixed part plus every record at its packed size
+// (a record never exceeds the packed form of its chunk, rounded to 16 bytes).
 int64_t max_container_bytes(const kvtc_config& c, const Layout& lo) {
   int64_t total = lo.chunks_off;
+  if (lo.recs_per_sec == 0) return total;
   for (int s = 0; s < 2; ++s) {
     int32_t budget = s == 0 ? lo.budget_k : lo.budget_v;
-    int64_t per_chunk_full = 0, per_chunk_last = 0;
+    int64_t per_rec[2] = {0, 0};
     for (int which = 0; which < 2; ++which) {
-      int32_t n = which == 0 ? c.chunk_tokens
-                             : lo.T_mid - (lo.chunks_per_sec - 1) * c.chunk_tokens;
-      if (lo.chunks_per_sec == 0) break;
-      int32_t ntiles = (n + c.tile_tokens - 1) / c.tile_tokens;
-      int64_t rec = 512 + 4 * (int64_t)ntiles;
-      for (int32_t t = 0; t < ntiles; ++t) {
-        int32_t m = n - t * c.tile_tokens;
-        if (m > c.tile_tokens) m = c.tile_tokens;
-        rec += 4 * (int64_t)c.rans_lanes + 2 * max_words(max_tile_bytes(c, m, budget), c) + 2;
+      int32_t n = which == 0 ? lo.rec_tokens : lo.T_mid - (lo.recs_per_sec - 1) * lo.rec_tokens;
+      int64_t P = 0;
+      for (int32_t a = 0; a < n; a += c.tile_tokens) {
+        int32_t m = n - a < c.tile_tokens ? n - a : c.tile_tokens;
+        P += max_tile_bytes(c, m, budget);
       }
-      (which == 0 ? per_chunk_full : per_chunk_last) = align16(rec);
+      per_rec[which] = align16(P);
     }
     int64_t secs = (int64_t)c.layers * c.kv_heads;
-    if (lo.chunks_per_sec > 0)
-      total += secs * ((lo.chunks_per_sec - 1) * per_chunk_full + per_chunk_last);
+    total += secs * ((lo.recs_per_sec - 1) * per_rec[0] + per_rec[1]);
   }
   return total;
 }
@@ -49,13 +47,15 @@ Params make_params(const PlanImpl& pl, const Layout& lo, const WsLayout& w) {
   p.L = c.layers; p.H = c.kv_heads; p.D = c.head_dim; p.dtype = c.dtype;
   p.transform = c.transform; p.rope_keys = c.rope_keys; p.rope_style = c.rope_style;
   p.max_bits = c.max_bits; p.sb = c.rans_scale_bits; p.lanes = c.rans_lanes;
-  p.chunk_tokens = c.chunk_tokens; p.tile_tokens = c.tile_tokens;
+  p.blk_tokens = lo.blk_tokens; p.tile_tokens = c.tile_tokens;
+  p.rec_tokens = lo.rec_tokens; p.recs_per_sec = lo.recs_per_sec; p.n_recs = lo.n_recs;
+  p.tiles_per_rec = lo.tiles_per_rec; p.blks_per_rec = lo.blks_per_rec;
   p.basis_per_head = c.basis_per_head; p.wht_keys = c.wht_keys;
   p.budget_k = lo.budget_k; p.budget_v = lo.budget_v;
   p.T = lo.T; p.s0 = lo.s0; p.mid_begin = lo.mid_begin; p.mid_end = lo.mid_end;
   p.T_mid = lo.T_mid; p.W_eff = lo.W_eff; p.n_sections = lo.n_sections;
-  p.chunks_per_sec = lo.chunks_per_sec; p.n_chunks = lo.n_chunks;
-  p.tiles_per_chunk = lo.tiles_per_chunk;
+  p.blks_per_sec = lo.blks_per_sec; p.n_blks = lo.n_blks;
+  p.tiles_per_blk = lo.tiles_per_blk;
   p.bits_k_uniform = floor_bits(c.bits_k); p.bits_v_uniform = floor_bits(c.bits_v);
   p.side_off = lo.side_off; p.r_off = lo.r_off; p.raw_off = lo.raw_off;
   p.raw_bytes = lo.raw_bytes; p.dir_off = lo.dir_off; p.chunks_off = lo.chunks_off;
@@ -79,7 +79,7 @@ void build_header(const PlanImpl& pl, const Layout& lo, uint8_t* h) {
   const kvtc_config& c = pl.cfg;
   memset(h, 0, kHeaderBytes);
   memcpy(h, "KVTC", 4);
-  put32(h + 4, 1);
+  put32(h + 4, kContainerVersion);
   put32(h + 8, kHeaderBytes);
   put32(h + 16, c.layers); put32(h + 20, c.kv_heads); put32(h + 24, c.head_dim);
   put32(h + 28, c.dtype); put32(h + 32, c.transform);
@@ -91,7 +91,7 @@ void build_header(const PlanImpl& pl, const Layout& lo, uint8_t* h) {
   put32(h + 80, c.chunk_tokens); put32(h + 84, c.tile_tokens);
   put32(h + 88, c.basis_per_head); put32(h + 92, c.wht_keys);
   put32(h + 96, lo.T); put32(h + 100, lo.s0); put32(h + 104, lo.mid_begin);
-  put32(h + 108, lo.mid_end); put32(h + 112, lo.n_sections); put32(h + 116, lo.chunks_per_sec);
+  put32(h + 108, lo.mid_end); put32(h + 112, lo.n_sections); put32(h + 116, lo.recs_per_sec);
   put64(h + 120, lo.side_off); put64(h + 128, lo.side_bytes); put64(h + 136, lo.raw_off);
   put64(h + 144, lo.raw_bytes); put64(h + 152, lo.dir_off); put64(h + 160, lo.chunks_off);
   put64(h + 176, pl.fingerprint);
@@ -125,7 +125,10 @@ static kvtc_status check_config(const kvtc_config* c) {
   if (c->rans_lanes != 16 && c->rans_lanes != 32) return KVTC_ERR_UNSUPPORTED;
   if (c->tile_tokens < 16 || c->tile_tokens > 256 || (c->tile_tokens % 16)) return KVTC_ERR_UNSUPPORTED;
   if (c->chunk_tokens < c->tile_tokens || (c->chunk_tokens % c->tile_tokens)) return KVTC_ERR_INVALID_ARG;
-  if (c->chunk_tokens / c->tile_tokens > 16) return KVTC_ERR_UNSUPPORTED;
+  // longer chunks split into work blocks of kBlkTokens tokens, whole tiles each
+  if (c->chunk_tokens > kBlkTokens && ((c->chunk_tokens % kBlkTokens) || (kBlkTokens % c->tile_tokens)))
+    return KVTC_ERR_UNSUPPORTED;
+  if (c->chunk_tokens / c->tile_tokens > kMaxTilesPerRec) return KVTC_ERR_UNSUPPORTED;
   if (c->basis_per_head != 0 && c->basis_per_head != 1) return KVTC_ERR_INVALID_ARG;
   if (c->wht_keys != 0 && c->wht_keys != 1) return KVTC_ERR_INVALID_ARG;
   return KVTC_OK;
@@ -357,7 +360,7 @@ kvtc_status kvtc_encode(kvtc_plan_t plan, const void* k, const void* v, int32_t 
   uint8_t hdr[kHeaderBytes];
   build_header(*pl, lo, hdr);
   ProfScope prof(pl, stream);
-  if (lo.n_chunks > 0) {
+  if (lo.n_blks > 0) {
     // the first pass clears the status block; the raw runs are copied by
     // extra workgroups of the rANS encoder
     HIP_TRY(launch_enc_transform(p, 0, stream));
@@ -368,7 +371,7 @@ kvtc_status kvtc_encode(kvtc_plan_t plan, const void* k, const void* v, int32_t 
   }
   HIP_TRY(launch_enc_alloc(p, stream));
   prof.phase("enc_alloc");
-  if (lo.n_chunks > 0) {
+  if (lo.n_blks > 0) {
     HIP_TRY(launch_enc_transform(p, 1, stream));
     prof.phase("enc_quant_pack");
     HIP_TRY(launch_rans_encode_chunks(p, stream, true));
@@ -399,7 +402,7 @@ kvtc_status kvtc_decode(kvtc_plan_t plan, const void* in, size_t in_bytes, int32
   ProfScope prof(pl, stream);
   HIP_TRY(launch_dec_check(p, hdr, stream));  // clears, then sets the status word
   prof.phase("dec_check");
-  if (lo.n_chunks > 0) {
+  if (lo.n_blks > 0) {
     // the raw runs are copied by extra workgroups of the rANS decoder
     HIP_TRY(launch_rans_decode_chunks(p, stream, true));
     prof.phase("rans_decode");
@@ -502,13 +505,13 @@ kvtc_status kvtc_encode_paged(kvtc_plan_t plan, const void* k_pool, const void* 
   HIP_TRY(launch_seq_setup(p, seq_lens_dev, sum_t, max_t, (int64_t)ws_bytes, 0, stream));
   HIP_TRY(launch_copy_raw(p, 1, stream));
   prof.phase("copy_raw");
-  if (p.n_chunks > 0) {
+  if (p.n_blks > 0) {
     HIP_TRY(launch_enc_transform(p, 0, stream));
     prof.phase("enc_stats");
   }
   HIP_TRY(launch_enc_alloc(p, stream));
   prof.phase("enc_alloc");
-  if (p.n_chunks > 0) {
+  if (p.n_blks > 0) {
     HIP_TRY(launch_enc_transform(p, 1, stream));
     prof.phase("enc_quant_pack");
     HIP_TRY(launch_rans_encode_chunks(p, stream));
@@ -541,7 +544,7 @@ kvtc_status kvtc_decode_paged(kvtc_plan_t plan, const void* in, size_t in_bytes,
   HIP_TRY(launch_seq_setup(p, seq_lens_dev, sum_t, max_t, (int64_t)ws_bytes, 1, stream));
   HIP_TRY(launch_dec_check(p, hdr, stream));
   prof.phase("dec_check");
-  if (p.n_chunks > 0) {
+  if (p.n_blks > 0) {
     HIP_TRY(launch_rans_decode_chunks(p, stream));
     prof.phase("rans_decode");
     HIP_TRY(launch_dec_transform(p, stream));
@@ -622,35 +625,30 @@ kvtc_status kvtc_test_coeffs(kvtc_plan_t plan, const void* k, const void* v, int
   return KVTC_OK;
 }
 
-kvtc_status kvtc_test_rans_encode(const uint8_t* sym, int64_t N, const uint16_t* freq,
-                                  int32_t scale_bits, int32_t lanes, uint32_t* states,
-                                  uint16_t* words, int64_t words_cap, int64_t* nwords,
-                                  hipStream_t stream) {
-  if ((N > 0 && !sym) || !freq || !states || !words || !nwords || N < 0) return KVTC_ERR_INVALID_ARG;
-  if (scale_bits < 8 || scale_bits > 12 || (lanes != 16 && lanes != 32)) return KVTC_ERR_UNSUPPORTED;
-  if (N >= (1ll << 30) || words_cap < 0) return KVTC_ERR_INVALID_ARG;
-  // the capacity is an upper bound on the words written: larger values act as 2^30
-  if (words_cap > (1ll << 30)) words_cap = 1ll << 30;
-  HIP_TRY(launch_test_rans_encode(sym, N, freq, scale_bits, lanes, states, words, words_cap,
-                                  nwords, stream));
-  return KVTC_OK;
-}
-
-kvtc_status kvtc_test_rans_decode(const uint32_t* states, const uint16_t* words, int64_t nwords,
-                                  const uint16_t* freq, int32_t scale_bits, int32_t lanes,
-                                  int64_t N, uint8_t* sym, int32_t* status, hipStream_t stream) {
-  if (!states || !freq || !status || (N > 0 && !sym) || N < 0 || nwords < 0) return KVTC_ERR_INVALID_ARG;
-  if (scale_bits < 8 || scale_bits > 12 || (lanes != 16 && lanes != 32)) return KVTC_ERR_UNSUPPORTED;
-  HIP_TRY(launch_test_rans_decode(states, words, nwords, freq, scale_bits, lanes, N, sym, status,
-                                  stream));
-  return KVTC_OK;
-}
-
-kvtc_status kvtc_test_freq_table(const uint32_t* counts, int32_t scale_bits, uint16_t* freq,
-                                 hipStream_t stream) {
-  if (!counts || !freq) return KVTC_ERR_INVALID_ARG;
+kvtc_status kvtc_test_freq_tables(const uint32_t* counts, const int32_t* alphabet, int32_t n,
+                                  int32_t scale_bits, uint16_t* freq, hipStream_t stream) {
+  if (n < 0 || (n > 0 && (!counts || !alphabet || !freq))) return KVTC_ERR_INVALID_ARG;
   if (scale_bits < 8 || scale_bits > 12) return KVTC_ERR_UNSUPPORTED;
-  HIP_TRY(launch_test_freq(counts, scale_bits, freq, stream));
+  HIP_TRY(launch_test_freq_tables(counts, alphabet, n, scale_bits, freq, stream));
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_test_packed_tiles(kvtc_plan_t plan, const void* ws, int32_t T, int32_t section,
+                                   void* out, size_t out_bytes, int32_t* blocks, size_t* slot_bytes,
+                                   hipStream_t stream) {
+  if (!plan || !ws) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* pl = (PlanImpl*)plan;
+  if (T < 0 || T > pl->cfg.max_tokens) return KVTC_ERR_INVALID_ARG;
+  Layout lo = make_layout(pl->cfg, T);
+  if (section < 0 || section >= lo.n_sections) return KVTC_ERR_INVALID_ARG;
+  WsLayout w = make_ws_layout(pl->cfg, lo);
+  if (blocks) *blocks = lo.blks_per_sec;
+  if (slot_bytes) *slot_bytes = (size_t)w.packed_slot;
+  const size_t n = (size_t)lo.blks_per_sec * (size_t)w.packed_slot;
+  if (!out || n == 0) return KVTC_OK;
+  if (out_bytes < n) return KVTC_ERR_CAPACITY;
+  HIP_TRY(hipMemcpyAsync(out, (const uint8_t*)ws + w.packed + (int64_t)section * lo.blks_per_sec * w.packed_slot, n,
+                         hipMemcpyDeviceToDevice, stream));
   return KVTC_OK;
 }
 

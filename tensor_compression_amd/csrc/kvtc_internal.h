@@ -11,14 +11,27 @@ namespace kvtc {
 
 constexpr uint32_t kRansL = 1u << 16;  // lower end of the normalised rANS state interval
 constexpr int kHeaderBytes = 256;
-constexpr int kDirEntry = 16;  // u64 offset, u32 size, u32 reserved
+constexpr int kDirEntry = 16;  // u64 offset, u32 size, u32 record mode
+constexpr int kContainerVersion = 2;
+constexpr int kBlkTokens = 1024;  // tokens of a transform work block (at most)
+constexpr int kMaxTilesPerRec = 32;
+
+// Two token granularities split a section's middle:
+//  * chunks (config.chunk_tokens): the container's records, each with its own
+//    frequency tables, stream word counts and directory entry;
+//  * work blocks of at most kBlkTokens tokens: the unit the transform kernels
+//    (statistics, quantise-and-pack, decode transform) take per workgroup and
+//    the unit of the packed buffer in the workspace.  A chunk is a whole
+//    number of blocks and a block a whole number of tiles.
 
 // Where each part of a container sits for a given T (all offsets in bytes
 // from the container start).  Only the chunk records have data-dependent
 // sizes; everything before chunks_off is fixed by the configuration and T.
 struct Layout {
   int32_t T, s0, mid_begin, mid_end, T_mid, W_eff;
-  int32_t n_sections, chunks_per_sec, n_chunks, tiles_per_chunk;
+  int32_t n_sections;
+  int32_t blk_tokens, blks_per_sec, n_blks, tiles_per_blk;             // work blocks
+  int32_t rec_tokens, recs_per_sec, n_recs, tiles_per_rec, blks_per_rec;  // chunk records
   int32_t n_r_sections;
   int32_t budget_k, budget_v;
   int64_t side_off, r_off, side_bytes, raw_off, raw_bytes, dir_off, chunks_off;
@@ -27,21 +40,23 @@ struct Layout {
 // Workspace carve-up (byte offsets from the workspace start).
 struct WsLayout {
   int64_t status;      // u32 status, u32 exact re-computations, u64 container bytes
-  int64_t part_sum;    // f64 [n_sections][chunks][D]
-  int64_t part_sq;     // f64 [n_sections][chunks][D]
-  int64_t part_min;    // f32 [n_sections][chunks][D]
-  int64_t part_max;    // f32 [n_sections][chunks][D]
+  int64_t part_sum;    // f64 [n_sections][blocks][D]
+  int64_t part_sq;     // f64 [n_sections][blocks][D]
+  int64_t part_min;    // f32 [n_sections][blocks][D]
+  int64_t part_max;    // f32 [n_sections][blocks][D]
   int64_t sec_stats;   // f32x4 [n_sections][D]: mean, variance, min, max
   int64_t side_rcp;    // f32 [n_sections][D]
   int64_t side_zero;   // f32 [n_sections][D]
   int64_t side_bits;   // u8  [n_sections][D]
-  int64_t packed;      // [n_chunks][packed_slot] packed tiles of each chunk
+  int64_t packed;      // [n_blks][packed_slot] packed tiles of each work block
   int64_t packed_slot;
-  int64_t rec;         // [n_chunks][rec_slot] encoder record slots
+  int64_t rec;         // [n_recs][rec_slot] encoder record slots
   int64_t rec_slot;
   int64_t tile_words_max;  // words capacity of one tile stream in a slot
-  int64_t rec_size;    // u32 [n_chunks]
-  int64_t rec_pos;     // u64 [n_chunks]
+  int64_t tile_raw_max;    // bytes of one tile's raw rows in a slot
+  int64_t rec_size;    // u32 [n_recs]
+  int64_t rec_mode;    // u32 [n_recs]: 0 coded, 1 packed
+  int64_t rec_pos;     // u64 [n_recs]
   int64_t kprime;      // bf16 [L][H][T_mid][D]: mid-region keys with RoPE removed (head_dim 128 bf16 path)
   int64_t fixed;       // paged batch: staging of the container's fixed part [chunks_off]
   int64_t total;
@@ -53,6 +68,20 @@ KVTC_HD inline int64_t align16(int64_t x) { return (x + 15) & ~(int64_t)15; }
 KVTC_HD inline int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
 
 KVTC_HD inline int32_t floor_bits(float b) { return (int32_t)floorf(b); }
+
+// Work-block size of a configuration: the chunk itself when it has at most
+// kBlkTokens tokens, otherwise kBlkTokens (the configuration check makes a
+// longer chunk a multiple of it).
+KVTC_HD inline int32_t blk_tokens_of(const kvtc_config& c) {
+  return c.chunk_tokens <= kBlkTokens ? c.chunk_tokens : kBlkTokens;
+}
+
+// Entropy-coding classes of a component of width b ("rANS Makes the Last Mile
+// Smaller"): codes of width >= 2 are coded one symbol per token, the symbol
+// being the top min(b, 4) bits with a frequency table per (chunk,
+// component); 1-bit codes and the low b - 4 bits of wider codes are raw.
+KVTC_HD inline int32_t sym_bits_of(int32_t b) { return b >= 2 ? (b < 4 ? b : 4) : 0; }
+KVTC_HD inline int32_t raw_bits_of(int32_t b) { return b == 1 ? 1 : (b >= 5 ? b - 4 : 0); }
 
 KVTC_HD inline bool section_has_r(const kvtc_config& c, int s) {
   return c.transform == KVTC_WHT && (s == 1 || c.wht_keys);
@@ -71,9 +100,15 @@ KVTC_HD inline Layout make_layout(const kvtc_config& c, int32_t T) {
   lo.T_mid = lo.mid_end - lo.mid_begin;
   lo.W_eff = T - lo.mid_end;
   lo.n_sections = c.layers * 2 * c.kv_heads;
-  lo.chunks_per_sec = lo.T_mid > 0 ? (lo.T_mid + c.chunk_tokens - 1) / c.chunk_tokens : 0;
-  lo.n_chunks = lo.n_sections * lo.chunks_per_sec;
-  lo.tiles_per_chunk = c.chunk_tokens / c.tile_tokens;
+  lo.blk_tokens = blk_tokens_of(c);
+  lo.blks_per_sec = lo.T_mid > 0 ? (lo.T_mid + lo.blk_tokens - 1) / lo.blk_tokens : 0;
+  lo.n_blks = lo.n_sections * lo.blks_per_sec;
+  lo.tiles_per_blk = lo.blk_tokens / c.tile_tokens;
+  lo.rec_tokens = c.chunk_tokens;
+  lo.recs_per_sec = lo.T_mid > 0 ? (lo.T_mid + c.chunk_tokens - 1) / c.chunk_tokens : 0;
+  lo.n_recs = lo.n_sections * lo.recs_per_sec;
+  lo.tiles_per_rec = c.chunk_tokens / c.tile_tokens;
+  lo.blks_per_rec = c.chunk_tokens / lo.blk_tokens;
   lo.n_r_sections = 0;
   for (int s = 0; s < 2; ++s)
     if (section_has_r(c, s)) lo.n_r_sections += c.layers * c.kv_heads;
@@ -85,7 +120,7 @@ KVTC_HD inline Layout make_layout(const kvtc_config& c, int32_t T) {
   lo.raw_off = lo.side_off + lo.side_bytes;
   lo.raw_bytes = align16(2 * (int64_t)c.layers * c.kv_heads * (lo.s0 + lo.W_eff) * D * eb);
   lo.dir_off = lo.raw_off + lo.raw_bytes;
-  lo.chunks_off = lo.dir_off + (int64_t)lo.n_chunks * kDirEntry;
+  lo.chunks_off = lo.dir_off + (int64_t)lo.n_recs * kDirEntry;
   if (c.transform == KVTC_PCA) {
     lo.budget_k = (int32_t)floorf(c.bits_k * (float)c.head_dim);
     lo.budget_v = (int32_t)floorf(c.bits_v * (float)c.head_dim);
@@ -96,15 +131,11 @@ KVTC_HD inline Layout make_layout(const kvtc_config& c, int32_t T) {
   return lo;
 }
 
+// Packed bytes of a tile of ntok tokens at most: ntok budget / 8 plus one
+// padding word per nonzero-width component row.
 KVTC_HD inline int64_t max_tile_bytes(const kvtc_config& c, int32_t ntok, int32_t budget) {
   int32_t nz = budget < c.head_dim ? budget : c.head_dim;
   return ((int64_t)ntok * budget + 7) / 8 + 4 * (int64_t)nz;
-}
-
-KVTC_HD inline int64_t max_words(int64_t P, const kvtc_config& c) {
-  // each coded symbol grows the state by at most scale_bits bits and each
-  // emitted word removes 16
-  return (P * (c.rans_scale_bits + 1)) / 16 + 2 * (int64_t)c.rans_lanes + 2;
 }
 
 // Status block at the start of every workspace: the status word (error
@@ -117,12 +148,15 @@ constexpr int64_t kCountOff = 256;
 constexpr int64_t kCountStride = 128;
 constexpr int64_t kStatusBlockBytes = kCountOff + kCountSlots * kCountStride;
 
+// Bytes of a record slot's table area: 16 u16 entries per component.
+KVTC_HD inline int64_t slot_table_bytes(const kvtc_config& c) { return 32 * (int64_t)c.head_dim; }
+
 // `paged`: the workspace of one sequence of a paged batch, which also stages
 // the fixed part of its container (everything before chunks_off).
 KVTC_HD inline WsLayout make_ws_layout(const kvtc_config& c, const Layout& lo, bool paged = false) {
   WsLayout w{};
   int64_t D = c.head_dim;
-  int64_t nsc = (int64_t)lo.n_sections * (lo.chunks_per_sec > 0 ? lo.chunks_per_sec : 1);
+  int64_t nsc = (int64_t)lo.n_sections * (lo.blks_per_sec > 0 ? lo.blks_per_sec : 1);
   auto take = [](int64_t& at, int64_t bytes) {
     int64_t o = at;
     at += (bytes + 255) & ~(int64_t)255;
@@ -140,23 +174,28 @@ KVTC_HD inline WsLayout make_ws_layout(const kvtc_config& c, const Layout& lo, b
   w.side_bits = take(at, (int64_t)lo.n_sections * D);
   int32_t bmax = lo.budget_k > lo.budget_v ? lo.budget_k : lo.budget_v;
   int64_t tile_max = max_tile_bytes(c, c.tile_tokens, bmax);
-  w.packed_slot = align16(tile_max * lo.tiles_per_chunk);
-  w.packed = take(at, (int64_t)lo.n_chunks * w.packed_slot);
-  // capacity rounded so that every tile piece of a slot starts 16-byte aligned
-  w.tile_words_max = ((max_words(tile_max, c) + 2 + 7) & ~(int64_t)7) - 2;
-  w.rec_slot = align16(align16(512 + 4 * (int64_t)lo.tiles_per_chunk) +
-                       (int64_t)lo.tiles_per_chunk * (4 * c.rans_lanes + 2 * w.tile_words_max + 4));
+  w.packed_slot = align16(tile_max * lo.tiles_per_blk);
+  w.packed = take(at, (int64_t)lo.n_blks * w.packed_slot);
+  // A tile stream whose words outgrow its packed size cannot make the record
+  // smaller than the packed form, so the record falls back to it; the word
+  // capacity (rounded so that every piece of a slot stays 16-byte aligned)
+  // only has to hold streams that can still win.
+  w.tile_words_max = ((tile_max / 2 + 2 * (int64_t)c.rans_lanes + 8 + 7) & ~(int64_t)7);
+  w.tile_raw_max = align16(tile_max);
+  w.rec_slot = align16(slot_table_bytes(c) + 4 * (int64_t)lo.tiles_per_rec) +
+               (int64_t)lo.tiles_per_rec * (4 * c.rans_lanes + 2 * w.tile_words_max + w.tile_raw_max);
   const bool fast128 = c.head_dim == 128 && c.dtype == KVTC_BF16 && c.transform == KVTC_PCA &&
                        c.tile_tokens % 64 == 0 && c.rope_keys;
   const int64_t kprime_bytes = fast128 ? (int64_t)c.layers * c.kv_heads * lo.T_mid * D * 2 : 0;
-  const int64_t rec_bytes = (int64_t)lo.n_chunks * w.rec_slot;
+  const int64_t rec_bytes = (int64_t)lo.n_recs * w.rec_slot;
   w.kprime = take(at, kprime_bytes);
   // the record slots are written by the rANS encoder, after the last reader
   // of the un-rotated keys (the quantiser): they share its memory when it is
   // large enough
   w.rec = (kprime_bytes > 0 && rec_bytes <= kprime_bytes) ? w.kprime : take(at, rec_bytes);
-  w.rec_size = take(at, (int64_t)lo.n_chunks * 4);
-  w.rec_pos = take(at, (int64_t)lo.n_chunks * 8 + 8);
+  w.rec_size = take(at, (int64_t)lo.n_recs * 4);
+  w.rec_mode = take(at, (int64_t)lo.n_recs * 4);
+  w.rec_pos = take(at, (int64_t)lo.n_recs * 8 + 8);
   w.fixed = take(at, paged ? lo.chunks_off : 0);
   w.total = at;
   return w;
@@ -185,10 +224,11 @@ struct PlanImpl {
 struct Params {
   // shape / config
   int32_t L, H, D, dtype, transform, rope_keys, rope_style, max_bits;
-  int32_t sb, lanes, chunk_tokens, tile_tokens, basis_per_head, wht_keys;
+  int32_t sb, lanes, blk_tokens, tile_tokens, basis_per_head, wht_keys;
   int32_t budget_k, budget_v;
-  int32_t T, s0, mid_begin, mid_end, T_mid, W_eff, n_sections, chunks_per_sec, n_chunks,
-      tiles_per_chunk;
+  int32_t T, s0, mid_begin, mid_end, T_mid, W_eff, n_sections, blks_per_sec, n_blks,
+      tiles_per_blk;
+  int32_t rec_tokens, recs_per_sec, n_recs, tiles_per_rec, blks_per_rec;
   int32_t bits_k_uniform, bits_v_uniform;
   float mfma_err;  // bound factor: |c_mfma - c_exact| <= mfma_err * ||x||_2
   int64_t side_off, r_off, raw_off, raw_bytes, dir_off, chunks_off;
@@ -254,7 +294,8 @@ __device__ inline Params at_seq(const Params& p0, int z) {
   const SeqInfo si = p0.seqs[z];
   const Layout lo = make_layout(p0.cfg, si.T);
   p.T = lo.T; p.s0 = lo.s0; p.mid_begin = lo.mid_begin; p.mid_end = lo.mid_end;
-  p.T_mid = lo.T_mid; p.W_eff = lo.W_eff; p.chunks_per_sec = lo.chunks_per_sec; p.n_chunks = lo.n_chunks;
+  p.T_mid = lo.T_mid; p.W_eff = lo.W_eff; p.blks_per_sec = lo.blks_per_sec; p.n_blks = lo.n_blks;
+  p.recs_per_sec = lo.recs_per_sec; p.n_recs = lo.n_recs;
   p.side_off = lo.side_off; p.r_off = lo.r_off; p.raw_off = lo.raw_off; p.raw_bytes = lo.raw_bytes;
   p.dir_off = lo.dir_off; p.chunks_off = lo.chunks_off;
   p.w = make_ws_layout(p0.cfg, lo, true);
@@ -300,13 +341,8 @@ hipError_t launch_seq_setup(const Params& p, const int32_t* seq_lens, int64_t su
                             int mode, hipStream_t s);  // mode 0 encode, 1 decode
 hipError_t launch_batch_place(const Params& p, hipStream_t s);
 hipError_t launch_batch_finish(const Params& p, hipStream_t s);
-hipError_t launch_test_rans_encode(const uint8_t* sym, int64_t N, const uint16_t* freq, int sb,
-                                   int lanes, uint32_t* states, uint16_t* words, int64_t cap,
-                                   int64_t* nwords, hipStream_t s);
-hipError_t launch_test_rans_decode(const uint32_t* states, const uint16_t* words, int64_t nwords,
-                                   const uint16_t* freq, int sb, int lanes, int64_t N,
-                                   uint8_t* sym, int32_t* status, hipStream_t s);
-hipError_t launch_test_freq(const uint32_t* counts, int sb, uint16_t* freq, hipStream_t s);
+hipError_t launch_test_freq_tables(const uint32_t* counts, const int32_t* alpha, int n, int sb, uint16_t* freq,
+                                   hipStream_t s);
 hipError_t launch_prep_basis(const float* src, void* basis_t, void* basis, int n_basis, int D,
                              int dtype, int32_t* bad, hipStream_t s);
 

@@ -85,16 +85,11 @@ EXPORTS = {
     "kvtc_test_coeffs": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
-    "kvtc_test_rans_encode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-                                             ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
-                                             ctypes.c_void_p]),
-    "kvtc_test_rans_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                             ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
-                                             ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
-                                             ctypes.c_void_p]),
-    "kvtc_test_freq_table": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
-                                            ctypes.c_void_p]),
+    "kvtc_test_freq_tables": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
+    "kvtc_test_packed_tiles": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -297,37 +292,25 @@ class Plan:
         torch.cuda.current_stream().synchronize()
         return out[:, :T_mid], r[:, :T_mid]
 
+    def packed_tiles(self, ws: torch.Tensor, T: int, section: int) -> torch.Tensor:
+        """The packed tiles of one section left in ws by the last encode (or
+        decode), as its work-block slots hold them: uint8 [blocks, slot bytes]."""
+        nb, sb = ctypes.c_int32(0), ctypes.c_size_t(0)
+        _check(lib().kvtc_test_packed_tiles(self.handle, _ptr(ws), T, section, None, 0, ctypes.byref(nb),
+                                            ctypes.byref(sb), _stream()), "kvtc_test_packed_tiles")
+        out = torch.zeros(max(nb.value * sb.value, 1), dtype=torch.uint8, device=self.device)
+        _check(lib().kvtc_test_packed_tiles(self.handle, _ptr(ws), T, section, _ptr(out), out.numel(), None, None,
+                                            _stream()), "kvtc_test_packed_tiles")
+        torch.cuda.current_stream().synchronize()
+        return out[: nb.value * sb.value].view(nb.value, sb.value)
 
-def rans_encode(sym: torch.Tensor, freq: torch.Tensor, scale_bits: int, lanes: int):
-    """Device single-stream coder (parity hook): returns (states, words)."""
-    N = sym.numel()
-    cap = (N * (scale_bits + 1)) // 16 + 2 * lanes + 2
-    dev = freq.device
-    states = torch.zeros(lanes, dtype=torch.int32, device=dev)
-    words = torch.zeros(max(cap, 1), dtype=torch.int16, device=dev)
-    nw = torch.zeros(1, dtype=torch.int64, device=dev)
-    symb = sym if N else torch.zeros(1, dtype=torch.uint8, device=dev)
-    _check(lib().kvtc_test_rans_encode(_ptr(symb), N, _ptr(freq), scale_bits, lanes, _ptr(states),
-                                       _ptr(words), cap, _ptr(nw), _stream()), "rans_encode")
+
+def freq_tables(counts: torch.Tensor, alphabet: torch.Tensor, scale_bits: int):
+    """Device normaliser of the record encoder on n tables: counts int32
+    [n, 16], alphabet sizes int32 [n] -> frequencies int16 [n, 16]."""
+    n = alphabet.numel()
+    f = torch.zeros((max(n, 1), 16), dtype=torch.int16, device=counts.device)
+    _check(lib().kvtc_test_freq_tables(_ptr(counts), _ptr(alphabet), n, scale_bits, _ptr(f), _stream()),
+           "freq_tables")
     torch.cuda.current_stream().synchronize()
-    n = int(nw.item())
-    return states, words[:max(n, 0)], n
-
-
-def rans_decode(states: torch.Tensor, words: torch.Tensor, freq: torch.Tensor, N: int,
-                scale_bits: int, lanes: int):
-    dev = freq.device
-    out = torch.zeros(max(N, 1), dtype=torch.uint8, device=dev)
-    st = torch.zeros(1, dtype=torch.int32, device=dev)
-    wb = words if words.numel() else torch.zeros(1, dtype=torch.int16, device=dev)
-    _check(lib().kvtc_test_rans_decode(_ptr(states), _ptr(wb), words.numel(), _ptr(freq), scale_bits,
-                                       lanes, N, _ptr(out), _ptr(st), _stream()), "rans_decode")
-    torch.cuda.current_stream().synchronize()
-    return out[:N], int(st.item())
-
-
-def freq_table(counts: torch.Tensor, scale_bits: int):
-    f = torch.zeros(256, dtype=torch.int16, device=counts.device)
-    _check(lib().kvtc_test_freq_table(_ptr(counts), scale_bits, _ptr(f), _stream()), "freq_table")
-    torch.cuda.current_stream().synchronize()
-    return f
+    return f[:n]

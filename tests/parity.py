@@ -11,9 +11,10 @@ Rules (per section, on identical inputs):
     coefficients with the GPU's side information, except where the oracle's
     pre-rounding value v lies within 1e-5 of a rounding boundary; such codes
     are counted and must stay at or below 0.01% of all codes;
-  * rANS: every chunk record of the GPU container is reproduced bit-for-bit
-    by the oracle coder from the record's own decoded bytes (same histogram,
-    same table, same states and words);
+  * records: every chunk record of the GPU container is reproduced
+    bit-for-bit by the oracle from the codes the record decodes to (same
+    tables, states, words, raw rows and mode), and the packed tiles the
+    kernels exchange equal the oracle's packing of the codes;
   * decode: the GPU decoder's fp32 output is within 1e-4 of the per-channel
     RMS of the oracle decoder's output on the same container.
 """
@@ -141,46 +142,45 @@ def compare_section(orc, cfg, T, k, v, basis, gpu_bytes, gpu_stats, u, gpu_coef=
 
 
 def check_records(orc, cfg, data, u, T, bits):
-    """Re-code every chunk record of section u with the oracle coder and
-    require the identical bytes."""
+    """Every chunk record of section u is the oracle's record of the codes it
+    decodes to: identical codes give identical tables, states, words, raw
+    rows and record mode."""
     pc = orc.parse_container(data, cfg, T)
     lo = pc["layout"]
     buf = np.frombuffer(data, np.uint8)
-    lanes, sb, D = cfg["rans_lanes"], cfg["rans_scale_bits"], cfg["head_dim"]
     n_rec = 0
     for ch in range(lo.chunks_per_sec):
         idx = u * lo.chunks_per_sec + ch
-        off, size = int(pc["offsets"][idx]), int(pc["sizes"][idx])
+        off, size, mode = int(pc["offsets"][idx]), int(pc["sizes"][idx]), int(pc["modes"][idx])
         n = min(cfg["chunk_tokens"], lo.T_mid - ch * cfg["chunk_tokens"])
-        ntiles = (n + cfg["tile_tokens"] - 1) // cfg["tile_tokens"]
-        tile_n = [min(cfg["tile_tokens"], n - t * cfg["tile_tokens"]) for t in range(ntiles)]
-        P = [orc.packed_bytes(bits, m) for m in tile_n]
-        if sum(P) == 0:
-            assert size == 0
-            continue
-        rec = buf[off: off + size]
-        freq = rec[:512].view(np.uint16)
-        nws = rec[512: 512 + 4 * ntiles].view(np.uint32)
-        at = 512 + 4 * ntiles
-        packed = []
-        streams = []
-        for t in range(ntiles):
-            st = rec[at: at + 4 * lanes].view(np.uint32)
-            nw = int(nws[t])
-            wd = rec[at + 4 * lanes: at + 4 * lanes + 2 * nw].view(np.uint16)
-            streams.append((st.copy(), wd.copy()))
-            packed.append(orc.rans_decode(st, wd, freq, P[t], sb, lanes))
-            at += 4 * lanes + 2 * nw + (2 if nw & 1 else 0)
-        assert (at + 15) // 16 * 16 == size
-        allp = np.concatenate(packed)
-        f2 = orc.freq_normalize(orc.byte_histogram(allp), sb)
-        assert np.array_equal(f2, freq), f"section {u} chunk {ch}: frequency table"
-        for t in range(ntiles):
-            st2, wd2 = orc.rans_encode(packed[t], freq, sb, lanes)
-            assert np.array_equal(st2, streams[t][0]) and np.array_equal(wd2, streams[t][1]), \
-                f"section {u} chunk {ch} tile {t}: rANS stream differs"
+        rec = buf[off: off + size].tobytes()
+        q = orc.chunk_decode(cfg, bits, rec, mode, n)
+        rec2, mode2 = orc.chunk_encode(cfg, bits, q)
+        assert mode2 == mode, f"section {u} chunk {ch}: record mode {mode}, oracle {mode2}"
+        assert rec2 == rec, f"section {u} chunk {ch}: record bytes differ from the oracle's"
         n_rec += 1
     return n_rec
+
+
+def blk_tokens(cfg):
+    """Tokens of a transform work block (the chunk, at most 1024 tokens)."""
+    return min(cfg["chunk_tokens"], 1024)
+
+
+def check_packed_tiles(orc, cfg, T, bits, q, slots):
+    """The packed tiles of a section in the workspace (`slots` [blocks, slot
+    bytes]) are the oracle's packing of its codes q [T_mid, D], padding bits
+    and words included."""
+    lo = orc.layout(cfg, T)
+    blk, tile = blk_tokens(cfg), cfg["tile_tokens"]
+    for b in range(slots.shape[0]):
+        at = 0
+        for a in range(b * blk, min(lo.T_mid, (b + 1) * blk), tile):
+            m = min(tile, lo.T_mid - a)
+            want = orc.pack(q[a: a + m], bits).tobytes()
+            got = slots[b, at: at + len(want)].tobytes()
+            assert got == want, f"block {b} tile at token {a}: packed bytes differ from the oracle's packing"
+            at += len(want)
 
 
 def channel_rms(x: np.ndarray) -> np.ndarray:

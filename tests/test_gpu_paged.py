@@ -97,8 +97,16 @@ def test_paged_batch_oracle_records_and_decode():
         pc = orc.parse_container(sub, cfg, T)
         Kz = synth.to_numpy_bits(synth.gather_paged(kp, table, z, T))
         Vz = synth.to_numpy_bits(synth.gather_paged(vp, table, z, T))
+        # the sequence's container is the contiguous encode of the gathered
+        # sequence (test above); the parity rules apply to it section by section
+        Kt = synth.gather_paged(kp, table, z, T)
+        Vt = synth.gather_paged(vp, table, z, T)
+        wsc = plan.workspace(T)
+        refc, stc = plan.encode(Kt, Vt, wsc)
+        assert stc == kvtc.OK and refc.cpu().numpy().tobytes() == sub
+        stats = plan.section_stats(wsc, T, lo.n_sections)
         for u in (0, H + 1, lo.n_sections - 1):
-            parity.check_records(orc, cfg, sub, u, T, pc["bits"][u])
+            parity.compare_section(orc, cfg, T, Kz, Vz, basis, sub, stats, u)
             l, s, h = u // (2 * H), (u // H) % 2, u % H
             src = Kz if s == 0 else Vz
             rms = np.sqrt((orc.bf16_bits_to_f32(src).reshape(src.shape)[l, h].astype(np.float64) ** 2).mean(axis=0))

@@ -50,9 +50,20 @@ def _full_parity(cfg, T, K, V, k, v, basis, plan, sections=None, decode_check=Tr
     total_codes = sum(r["codes"] for r in report)
     boundary = sum(r["boundary_codes"] for r in report)
     assert boundary <= parity.BOUNDARY_FRACTION * max(total_codes, 1)
+    # the packed tiles the encoder's kernels exchanged are the oracle's packing
+    # of the codes the container holds
+    pc = orc.parse_container(data, cfg, T)
+    codes = {u: orc.section_codes(cfg, data, basis, u, T) for u in secs} if lo.T_mid else {}
+    for u in codes:
+        parity.check_packed_tiles(orc, cfg, T, pc["bits"][u], codes[u], plan.packed_tiles(ws, T, u).cpu().numpy())
     if decode_check:
-        kd, vd, st2 = plan.decode(torch.frombuffer(bytearray(data), dtype=torch.uint8).cuda(), T, kvtc.FP32)
+        wsd = plan.workspace(T)
+        kd, vd, st2 = plan.decode(torch.frombuffer(bytearray(data), dtype=torch.uint8).cuda(), T, kvtc.FP32, ws=wsd)
         assert st2 == kvtc.OK
+        # and the record decoder rebuilds exactly those tiles
+        for u in codes:
+            parity.check_packed_tiles(orc, cfg, T, pc["bits"][u], codes[u],
+                                      plan.packed_tiles(wsd, T, u).cpu().numpy())
         kd, vd = kd.cpu().numpy(), vd.cpu().numpy()
         H = cfg["kv_heads"]
         ref = orc.decode_sections(cfg, data, basis, 0, lo.n_sections, lo.T_mid) if sections is None else None
@@ -77,52 +88,30 @@ def _full_parity(cfg, T, K, V, k, v, basis, plan, sections=None, decode_check=Tr
 
 # --------------------------------------------------------------------------- stages
 
-def test_freq_table_matches_oracle():
+def test_freq_tables_match_oracle():
+    """The record encoder's normaliser on alphabets of 1..16 symbols."""
     rng = np.random.default_rng(0)
-    cases = []
-    for _ in range(150):
-        k = int(rng.integers(1, 257))
-        c = np.zeros(256, np.uint32)
-        c[rng.choice(256, k, replace=False)] = rng.geometric(rng.uniform(0.0005, 0.9), k)
+    cases, alpha = [], []
+    for _ in range(400):
+        A = int(rng.integers(1, 17))
+        c = np.zeros(16, np.uint32)
+        k = int(rng.integers(1, A + 1))
+        c[rng.choice(A, k, replace=False)] = rng.geometric(rng.uniform(0.0005, 0.9), k)
         cases.append(c)
-    single = np.zeros(256, np.uint32)
-    single[200] = 77
-    cases += [single, np.full(256, 3, np.uint32), np.zeros(256, np.uint32)]
+        alpha.append(A)
+    for A in (1, 2, 4, 8, 16):  # single symbol, uniform, empty
+        for c in (np.eye(16, dtype=np.uint32)[A - 1] * 77, np.r_[np.full(A, 3), np.zeros(16 - A)].astype(np.uint32),
+                  np.zeros(16, np.uint32)):
+            cases.append(c)
+            alpha.append(A)
+    counts = torch.from_numpy(np.stack(cases).astype(np.int32)).cuda()
+    al = torch.tensor(alpha, dtype=torch.int32).cuda()
     for sb in (8, 10, 12):
-        for c in cases:
-            g = kvtc.freq_table(torch.from_numpy(c.astype(np.int32)).cuda(), sb).cpu().numpy().view(np.uint16)
-            assert np.array_equal(g, orc.freq_normalize(c, sb)), (sb, c)
-
-
-@pytest.mark.parametrize("lanes", [16, 32])
-@pytest.mark.parametrize("sb", [8, 12])
-def test_rans_streams_bit_exact(lanes, sb):
-    rng = np.random.default_rng(lanes + sb)
-    for N in (0, 1, 2, lanes - 1, lanes, lanes + 1, 1000, 8192, 12345):
-        for dist in ("gauss", "skew", "uniform", "single"):
-            if dist == "gauss":
-                sym = np.clip(np.rint(rng.standard_normal(N) * 15 + 100), 0, 255).astype(np.uint8)
-            elif dist == "skew":
-                p = np.exp(-np.arange(256) / 6.0)
-                sym = rng.choice(256, N, p=p / p.sum()).astype(np.uint8)
-            elif dist == "uniform":
-                sym = rng.integers(0, 256, N).astype(np.uint8)
-            else:
-                sym = np.full(N, 9, np.uint8)
-            freq = orc.freq_normalize(orc.byte_histogram(sym) if N else np.eye(256, dtype=np.uint32)[9], sb)
-            st_o, wd_o = orc.rans_encode(sym, freq, sb, lanes)
-            ft = torch.from_numpy(freq.view(np.int16)).cuda()
-            st_g, wd_g, n = kvtc.rans_encode(torch.from_numpy(sym).cuda(), ft, sb, lanes)
-            assert n == wd_o.size
-            assert np.array_equal(st_g.cpu().numpy().view(np.uint32), st_o)
-            assert np.array_equal(wd_g.cpu().numpy().view(np.uint16), wd_o)
-            out, status = kvtc.rans_decode(torch.from_numpy(st_o.view(np.int32)).cuda(),
-                                           torch.from_numpy(wd_o.view(np.int16)).cuda(), ft, N, sb, lanes)
-            assert status == kvtc.OK and np.array_equal(out.cpu().numpy(), sym)
-            if wd_o.size > 1:  # a missing word is detected
-                _, status = kvtc.rans_decode(torch.from_numpy(st_o.view(np.int32)).cuda(),
-                                             torch.from_numpy(wd_o[1:].view(np.int16)).cuda(), ft, N, sb, lanes)
-                assert status == kvtc.ERR_CORRUPT
+        g = kvtc.freq_tables(counts, al, sb).cpu().numpy().view(np.uint16)
+        for i, (c, A) in enumerate(zip(cases, alpha)):
+            want = orc.freq_normalize(c[:A], sb)
+            assert np.array_equal(g[i, :A], want), (sb, A, c)
+            assert not g[i, A:].any()
 
 
 # --------------------------------------------------------------------------- pipeline
@@ -240,12 +229,26 @@ def test_damaged_containers_are_refused():
     assert status(bad) == kvtc.ERR_CORRUPT                 # frequency table sum
     bad = bytearray(data); bad[pc["layout"].n_sections * 0 + 256] = 9  # a width above max_bits
     assert status(bad) == kvtc.ERR_CORRUPT
+    # flipped stream words of the first tile: the final-state and word-count
+    # checks catch nearly all of them
+    assert int(pc["modes"][0]) == 0
+    bits0 = pc["bits"][0]
+    tb = sum(2 * (1 << orc.sym_bits(int(b))) for b in bits0 if orc.sym_bits(int(b)))
+    tb = (tb + 3) // 4 * 4
+    ntiles = -(-min(cfg["chunk_tokens"], pc["layout"].T_mid) // cfg["tile_tokens"])
+    nw0 = int(np.frombuffer(data[rec + tb: rec + tb + 4], np.uint32)[0])
+    w0 = rec + tb + 4 * ntiles + 4 * cfg["rans_lanes"]
     rng = np.random.default_rng(0)
     caught = 0
-    for pos in rng.integers(rec + 700, rec + int(pc["sizes"][0]) - 8, 12):
+    for pos in rng.integers(w0, w0 + 2 * nw0, 12):
         bad = bytearray(data); bad[pos] ^= 0x5A
         caught += status(bad) == kvtc.ERR_CORRUPT
     assert caught >= 9
+    d0 = orc_dir_off(data)
+    for mode in (1, 2):  # a record mode that disagrees with the record, or none at all
+        bad = bytearray(data); bad[d0 + 12: d0 + 16] = np.uint32(mode).tobytes()
+        assert status(bad) == kvtc.ERR_CORRUPT
+        assert orc.decode_status(cfg, bytes(bad), basis, T) == orc.ERR_CORRUPT
     # a directory offset near 2^64 (16-byte aligned) would wrap an
     # offset + size bound; it is refused before the record is read
     bad = bytearray(data)
