@@ -69,9 +69,9 @@ def parse():
 PHASE_KERNELS = {
     "enc_stats": (("k_unrope128", "k_enc128"), ("kernels_encode.hip",)),
     "enc_quant_pack": (("k_quant128",), ("kernels_quant.hip",)),
-    "rans_encode": (("k_rans_enc_chunks",), ("kernels_rans.hip",)),
+    "rans_encode": (("k_rans_enc_recs",), ("kernels_rans.hip",)),
     "assemble": (("k_scan", "k_copy_records"), ("kernels_rans.hip",)),
-    "rans_decode": (("k_rans_dec_chunks",), ("kernels_rans.hip",)),
+    "rans_decode": (("k_rans_dec_recs",), ("kernels_rans.hip",)),
     "dec_transform": (("k_dec_pca128",), ("kernels_decode.hip",)),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_llama3_8b.md")

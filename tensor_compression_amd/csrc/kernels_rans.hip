@@ -53,26 +53,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(void* base, int32
 // symbol (lowest on ties), an excess is taken one unit at a time from the
 // largest frequency above 1 (lowest symbol on ties).  All zero when N = 0.
 __device__ void normalize_small(const uint32_t* cnt, int A, int sb, uint32_t* f) {
-  uint64_t N = 0;
+  // a chunk has at most 32 tiles of 256 tokens, so n 2M + N < 2^27 and the
+  // rounding division is exact in 32 bits
+  uint32_t N = 0;
   for (int s = 0; s < A; ++s) N += cnt[s];
   if (N == 0) {
     for (int s = 0; s < A; ++s) f[s] = 0;
     return;
   }
-  const uint64_t M = 1ull << sb;
-  int64_t sum = 0;
+  const uint32_t M = 1u << sb;
+  int32_t sum = 0;
   int best = 0;
   for (int s = 0; s < A; ++s) {
-    uint64_t r = 0;
+    uint32_t r = 0;
     if (cnt[s]) {
-      r = ((uint64_t)cnt[s] * (2 * M) + N) / (2 * N);
+      r = (cnt[s] * (2 * M) + N) / (2 * N);
       if (r < 1) r = 1;
     }
-    f[s] = (uint32_t)r;
-    sum += (int64_t)r;
+    f[s] = r;
+    sum += (int32_t)r;
     if (cnt[s] > cnt[best]) best = s;
   }
-  int64_t d = (int64_t)M - sum;
+  int32_t d = (int32_t)M - sum;
   if (d > 0) f[best] += (uint32_t)d;
   while (d < 0) {
     int bi = -1;
@@ -204,11 +206,17 @@ __device__ __forceinline__ uint32_t funnel(uint32_t lo, uint32_t hi, uint32_t sh
 // ---- record encoder ---------------------------------------------------------
 
 constexpr int kRowWords = 66;  // a staged component row of a 256-token tile (<= 64 words), zero-padded
+constexpr int kRawWords = 34;  // a raw row of a 256-token tile (<= 32 words), zero-padded
 
 // raw_runs > 0 (contiguous cache): workgroups past the chunks copy the raw
 // sink and recent runs into the container, on the bandwidth this
 // latency-bound pass leaves idle.
-template <int LANES>
+// STEPS = tile_tokens / LANES when the launch fixes it (0: from the tile at
+// run time).  With a fixed step count the loops unroll and every memory
+// operation of a component is issued unconditionally, so the wait for the
+// next component's prefetched row does not also wait for the stores issued
+// after it (loads and stores retire in order on one counter).
+template <int LANES, int STEPS>
 __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw_runs) {
   constexpr int SPW = 64 / LANES;  // streams per wave
   constexpr int NQ = 64 / LANES + 1;  // staged row words per lane
@@ -225,6 +233,7 @@ __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw
   __shared__ uint32_t hist[kMaxD * 17];
   __shared__ EncSym tab[kMaxD * 16];
   __shared__ uint32_t rowbuf[kMaxTilesPerRec][2][kRowWords];
+  __shared__ uint32_t rawrow[kMaxTilesPerRec][kRawWords];  // a component's raw row being assembled
   __shared__ int32_t s_nw[kMaxTilesPerRec];
   if (wave == 0) rec_setup(p, cr, p.ws + p.w.side_bits + (int64_t)u * p.D, g);
   for (int i = tid; i < kMaxD * 17; i += blockDim.x) hist[i] = 0;
@@ -237,38 +246,66 @@ __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw
   }
   const int nc = g.nc, ntiles = g.ntiles;
   uint8_t* slot = rec_slot(p, r);
-  // -- histograms: one (tile, coded component) row per thread, so that the
-  // lanes of a wave count into different components' bins
-  for (int it = tid; it < nc * ntiles; it += blockDim.x) {
-    const int t = it / nc, ci = it - t * nc;
-    const int i = g.coded[ci];
-    const uint32_t b = g.b[i], rr = b - (uint32_t)sym_bits_of((int)b);
-    const bool last = t == ntiles - 1;
-    const int m = last ? g.n_last : p.tile_tokens;
-    const uint32_t* row = reinterpret_cast<const uint32_t*>(packed_tile(p, u, cr, t, g.pf)) + g.roff[last][i];
-    const int W = (m * (int)b + 31) >> 5;
-    uint32_t* hc = hist + ci * 17;
-    uint64_t acc = 0;
-    uint32_t have = 0;
-    int wi = 0, k = 0;
-    while (k < m) {
-      // four words in flight, then their codes
-      uint32_t wv[4];
+  // -- streams: lane group grp of the wave codes tile t
+  const int grp = lane / LANES, j = lane % LANES;
+  const int t = wave * SPW + grp;
+  const bool valid = t < ntiles;
+  const bool last = valid && t == ntiles - 1;
+  const int m = !valid ? 0 : (last ? g.n_last : p.tile_tokens);
+  const int tt = valid ? t : 0;
+  const bool has_stream = wave * SPW < ntiles;  // wave-uniform
+  const uint32_t* tbase = reinterpret_cast<const uint32_t*>(packed_tile(p, u, cr, tt, g.pf));
+  uint32_t* rb = &rowbuf[tt][0][0];
+  int steps_max = (m + LANES - 1) / LANES;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) wv[q] = wi + q < W ? row[wi + q] : 0u;
-      wi += 4;
+  for (int o = 32; o > 0; o >>= 1) steps_max = max(steps_max, __shfl_xor(steps_max, o, 64));
+  steps_max = STEPS > 0 ? STEPS : __builtin_amdgcn_readfirstlane(steps_max);
+  // the record's packed tiles through one buffer resource: its work blocks
+  // are consecutive slots, and a lane's tile starts at tile_at
+  const int32_t prec_bytes = (int32_t)((int64_t)p.blks_per_rec * p.w.packed_slot);
+  const __amdgpu_buffer_rsrc_t prsrc = uniform_rsrc(packed_tile(p, u, cr, 0, g.pf), prec_bytes);
+  const int32_t tile_at = (int32_t)((int64_t)(tt / p.tiles_per_blk) * p.w.packed_slot + (int64_t)(tt % p.tiles_per_blk) * g.pf);
+  // the row of component i of this tile: NQ words per lane into registers
+  // (lanes past the row load zeros), then into this stream's LDS row buffer
+  uint32_t pre[NQ];
+  auto row_load = [&](int i) {
+    const int W = (m * (int)g.b[i] + 31) >> 5;
+    const int32_t at = tile_at + 4 * (int32_t)g.roff[last][i];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc |= (uint64_t)wv[q] << have;
-        have += 32;
-        while (have >= b && k < m) {
-          const uint32_t code = (uint32_t)acc & ((1u << b) - 1u);
-          acc >>= b;
-          have -= b;
+    for (int q = 0; q < NQ; ++q) {
+      const int w = j + q * LANES;
+      pre[q] = __builtin_amdgcn_raw_buffer_load_b32(prsrc, (valid && w < W) ? at + 4 * w : prec_bytes, 0, 0);
+    }
+  };
+  auto row_store = [&](int which) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int w = j + q * LANES;
+      if (valid && w < kRowWords) rb[which * kRowWords + w] = pre[q];
+    }
+  };
+  // -- histograms: each stream counts its tile's symbols component by
+  // component from the staged rows (the next row in flight meanwhile)
+  if (has_stream && nc > 0) {
+    row_load(g.coded[0]);
+    row_store(0);
+    for (int ci = 0; ci < nc; ++ci) {
+      const int i = g.coded[ci];
+      const uint32_t b = g.b[i], rr = b - (uint32_t)sym_bits_of((int)b);
+      if (ci + 1 < nc) row_load(g.coded[ci + 1]);
+      __builtin_amdgcn_wave_barrier();
+      const uint32_t* rw = rb + (ci & 1) * kRowWords;
+      uint32_t* hc = hist + ci * 17;
+#pragma unroll
+      for (int s = 0; s < (STEPS > 0 ? STEPS : steps_max); ++s) {
+        const int k = s * LANES + j;
+        if (valid && k < m) {
+          const uint32_t bp = (uint32_t)k * b;
+          const uint32_t code = funnel(rw[bp >> 5], rw[(bp >> 5) + 1], bp & 31) & ((1u << b) - 1u);
           atomicAdd(&hc[code >> rr], 1u);
-          ++k;
         }
       }
+      if (ci + 1 < nc) row_store((ci + 1) & 1);
     }
   }
   __syncthreads();
@@ -292,48 +329,21 @@ __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw
   }
   if (tid == 0 && g.tu < g.tb) *reinterpret_cast<uint16_t*>(slot + g.tu) = 0;  // padding to 4 bytes
   __syncthreads();
-  // -- streams: lane group grp of the wave codes tile t
-  const int grp = lane / LANES, j = lane % LANES;
-  const int t = wave * SPW + grp;
-  const bool valid = t < ntiles;
-  const bool last = valid && t == ntiles - 1;
-  const int m = !valid ? 0 : (last ? g.n_last : p.tile_tokens);
-  const int tt = valid ? t : 0;
   int32_t nw = 0;
-  if (wave * SPW < ntiles) {
+  if (has_stream) {
     const int64_t toff = slot_tile_off(p, tt);
     uint32_t* states = reinterpret_cast<uint32_t*>(slot + toff);
     const int32_t woff = (int32_t)(toff + 4 * LANES);
     const int32_t wcap = (int32_t)p.w.tile_words_max;
     const __amdgpu_buffer_rsrc_t wrsrc = uniform_rsrc(slot, (int32_t)p.w.rec_slot);
-    const uint32_t* tbase = reinterpret_cast<const uint32_t*>(packed_tile(p, u, cr, tt, g.pf));
     uint32_t* rawdst = reinterpret_cast<uint32_t*>(slot + slot_raw_off(p, tt));
     const uint64_t gm = ((1ull << LANES) - 1ull) << (grp * LANES);
     const uint32_t gm_lo = (uint32_t)gm, gm_hi = (uint32_t)(gm >> 32);
-    int steps_max = (m + LANES - 1) / LANES;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) steps_max = max(steps_max, __shfl_xor(steps_max, o, 64));
-    steps_max = __builtin_amdgcn_readfirstlane(steps_max);
-    uint32_t* rb = &rowbuf[tt][0][0];
-    // the row of component i of this tile: NQ words per lane into registers
-    uint32_t pre[NQ];
-    auto row_load = [&](int i) {
-      const int W = (m * (int)g.b[i] + 31) >> 5;
-      const uint32_t* row = tbase + g.roff[last][i];
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const int w = j + q * LANES;
-        pre[q] = (valid && w < W) ? row[w] : 0u;
-      }
-    };
-    auto row_store = [&](int which) {
-#pragma unroll
-      for (int q = 0; q < NQ; ++q) {
-        const int w = j + q * LANES;
-        if (valid && w < kRowWords) rb[which * kRowWords + w] = pre[q];
-      }
-    };
+    const uint32_t sbm = 32u - (uint32_t)p.sb, Mv = 1u << p.sb;
     uint32_t x = kRansL;
+    uint32_t* rrow = &rawrow[tt][0];
+    if (valid)
+      for (int w = j; w < kRawWords; w += LANES) rrow[w] = 0u;
     if (nc > 0) {
       row_load(g.coded[nc - 1]);
       row_store((nc - 1) & 1);
@@ -341,51 +351,69 @@ __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw
     for (int ci = nc - 1; ci >= 0; --ci) {
       const int i = g.coded[ci];
       const uint32_t b = g.b[i], rr = b - (uint32_t)sym_bits_of((int)b);
-      const uint32_t mask = (1u << b) - 1u;
+      const uint32_t mask = (1u << b) - 1u, rmask = (1u << rr) - 1u;
       if (ci > 0) row_load(g.coded[ci - 1]);  // the next component's row, in flight meanwhile
       __builtin_amdgcn_wave_barrier();
       const uint32_t* rw = rb + (ci & 1) * kRowWords;
-      const EncSym* tc = tab + ci * 16;
-      for (int s = steps_max - 1; s >= 0; --s) {
-        const int k = s * LANES + j;
-        const bool active = valid && k < m;
-        const uint32_t bp = active ? (uint32_t)k * b : 0u;
-        const uint32_t code = funnel(rw[bp >> 5], rw[(bp >> 5) + 1], bp & 31) & mask;
-        const uint32_t sym = code >> rr;
-        const uint4 q4 = reinterpret_cast<const uint4*>(tc)[sym];
-        const uint32_t f = q4.x, cum = q4.y;
-        const double rcp = __hiloint2double((int)q4.w, (int)q4.z);
-        // renormalise while x >= f 2^(32 - sb): one 16-bit word at most
-        const bool emit = active && (x >> (32 - p.sb)) >= f;
-        const uint64_t bl = __ballot(emit);
-        const uint32_t mlo = (uint32_t)bl & gm_lo, mhi = (uint32_t)(bl >> 32) & gm_hi;
-        const int32_t cnt = (int32_t)(__popc(mlo) + __popc(mhi));
-        // words are written in emission order, higher lanes first
-        const int32_t below = (int32_t)__builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
-        const int32_t at = nw + cnt - 1 - below;
-        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(x & 0xffffu), wrsrc,
-                                              (emit && at < wcap) ? woff + 2 * at : (int32_t)p.w.rec_slot, 0, 0);
-        const uint32_t xe = emit ? (x >> 16) : x;
-        nw += cnt;
-        // x = floor(x / f) M + (x mod f) + cum, via an exact fp64 quotient
-        const uint32_t qq = (uint32_t)__fma_rn((double)xe, rcp, 0x1p-20);
-        const uint32_t xn = xe + cum + __umul24(qq, (1u << p.sb) - f);
-        x = active ? xn : x;
-      }
-      // the component's raw row (its low bits), from the staged row
-      if (rr > 0 && valid) {
-        uint32_t* dst = rawdst + g.raoff[last][i];
-        const int Wr = (m * (int)rr + 31) >> 5;
-        for (int w = j; w < Wr; w += LANES) {
-          uint32_t acc = 0;
-          const int k0 = (32 * w) / (int)rr, k1 = min(m - 1, (32 * w + 31) / (int)rr);
-          for (int k = k0; k <= k1; ++k) {
-            const uint32_t bp = (uint32_t)k * b;
-            const uint32_t lo = funnel(rw[bp >> 5], rw[(bp >> 5) + 1], bp & 31) & ((1u << rr) - 1u);
-            const int pos = k * (int)rr - 32 * w;
-            acc |= pos >= 0 ? (lo << pos) : (lo >> (-pos));
+      const uint4* tc = reinterpret_cast<const uint4*>(tab + ci * 16);
+      // bit positions of token k = s LANES + j in the packed row and in the raw row
+      const uint32_t jb = (uint32_t)j * b, jr = (uint32_t)j * rr;
+      const uint32_t sb_step = (uint32_t)LANES * b, sr_step = (uint32_t)LANES * rr;
+      // steps from the last down, four at a time: the symbols and their table
+      // entries do not depend on the state, so they are all read first
+#pragma unroll
+      for (int s0 = (STEPS > 0 ? STEPS : steps_max) - 1; s0 >= 0; s0 -= 4) {
+        uint4 ent[4];
+        bool act[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const int st = s0 - d;
+          const int k = st * LANES + j;
+          act[d] = valid && st >= 0 && k < m;
+          const uint32_t bp = act[d] ? jb + (uint32_t)st * sb_step : 0u;
+          const uint32_t code = funnel(rw[bp >> 5], rw[(bp >> 5) + 1], bp & 31) & mask;
+          ent[d] = tc[code >> rr];
+          if (rr) {  // the low bits into the raw row (no field straddles a word unless rr = 3)
+            const uint32_t bq = act[d] ? jr + (uint32_t)st * sr_step : 0u;
+            const uint32_t lo = act[d] ? (code & rmask) : 0u;
+            atomicOr(&rrow[bq >> 5], lo << (bq & 31));
+            if (rr == 3) atomicOr(&rrow[(bq >> 5) + 1], (uint32_t)(((uint64_t)lo << (bq & 31)) >> 32));
           }
-          dst[w] = acc;
+        }
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const bool active = act[d];
+          const uint32_t f = ent[d].x, cum = ent[d].y;
+          const double rcp = __hiloint2double((int)ent[d].w, (int)ent[d].z);
+          // renormalise while x >= f 2^(32 - sb): one 16-bit word at most
+          const bool emit = active && (x >> sbm) >= f;
+          const uint64_t bl = __ballot(emit);
+          const uint32_t mlo = (uint32_t)bl & gm_lo, mhi = (uint32_t)(bl >> 32) & gm_hi;
+          const int32_t cnt = (int32_t)(__popc(mlo) + __popc(mhi));
+          // words are written in emission order, higher lanes first
+          const int32_t below = (int32_t)__builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
+          const int32_t at = nw + cnt - 1 - below;
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(x & 0xffffu), wrsrc,
+                                                (emit && at < wcap) ? woff + 2 * at : (int32_t)p.w.rec_slot, 0, 0);
+          const uint32_t xe = emit ? (x >> 16) : x;
+          nw += cnt;
+          // x = floor(x / f) M + (x mod f) + cum, via an exact fp64 quotient
+          const uint32_t qq = (uint32_t)__fma_rn((double)xe, rcp, 0x1p-20);
+          const uint32_t xn = xe + cum + __umul24(qq, Mv - f);
+          x = active ? xn : x;
+        }
+      }
+      // the component's raw row to the slot; the buffer is cleared for the next
+      if (rr) {
+        __builtin_amdgcn_wave_barrier();
+        const int Wr = (m * (int)rr + 31) >> 5;
+        const int32_t at = (int32_t)(slot_raw_off(p, tt) + 4 * (int64_t)g.raoff[last][i]);
+#pragma unroll
+        for (int q = 0; q < (kRawWords + LANES - 1) / LANES; ++q) {
+          const int w = j + q * LANES;
+          const uint32_t v = w < kRawWords ? rrow[w] : 0u;
+          __builtin_amdgcn_raw_buffer_store_b32(v, wrsrc, (valid && w < Wr) ? at + 4 * w : (int32_t)p.w.rec_slot, 0, 0);
+          if (valid && w < kRawWords) rrow[w] = 0u;
         }
       }
       if (ci > 0) row_store((ci - 1) & 1);
@@ -434,8 +462,16 @@ hipError_t launch_rans_encode_chunks(const Params& p, hipStream_t s, bool with_r
   if (waves < 1) waves = 1;
   const int raw_runs = with_raw && p.n_seqs == 0 ? 4 * p.L * p.H : 0;
   const dim3 grid(p.n_recs + raw_runs, 1, seq_grid(p)), block(64 * waves);
-  if (p.lanes == 16) hipLaunchKernelGGL(k_rans_enc_recs<16>, grid, block, 0, s, p, raw_runs);
-  else hipLaunchKernelGGL(k_rans_enc_recs<32>, grid, block, 0, s, p, raw_runs);
+  const int steps = p.tile_tokens / p.lanes;
+  if (p.lanes == 16) {
+    if (steps == 16) hipLaunchKernelGGL((k_rans_enc_recs<16, 16>), grid, block, 0, s, p, raw_runs);
+    else if (steps == 8) hipLaunchKernelGGL((k_rans_enc_recs<16, 8>), grid, block, 0, s, p, raw_runs);
+    else hipLaunchKernelGGL((k_rans_enc_recs<16, 0>), grid, block, 0, s, p, raw_runs);
+  } else {
+    if (steps == 8) hipLaunchKernelGGL((k_rans_enc_recs<32, 8>), grid, block, 0, s, p, raw_runs);
+    else if (steps == 4) hipLaunchKernelGGL((k_rans_enc_recs<32, 4>), grid, block, 0, s, p, raw_runs);
+    else hipLaunchKernelGGL((k_rans_enc_recs<32, 0>), grid, block, 0, s, p, raw_runs);
+  }
   return hipGetLastError();
 }
 
@@ -545,11 +581,14 @@ __global__ __launch_bounds__(1024) void k_scan(const Params p0, HeaderBytes hdr)
   finish_container(p, hdr, (uint64_t)p.chunks_off + s_total, tid);
 }
 
-// Copy of record r into the container.  scan = 1 (a contiguous call with few
-// records): each workgroup sums the sizes of the records before its own,
-// writes its directory entry, and the last one writes the header, the
-// container size and the status word, as k_scan does.
-__global__ __launch_bounds__(256) void k_copy_records(const Params p0, HeaderBytes hdr, int scan) {
+// Copy of record r into the container, one wave per tile piece (the waves'
+// copies overlap).  scan = 1 (a contiguous call with few records): each
+// workgroup sums the sizes of the records before its own, writes its
+// directory entry, and the last one writes the header, the container size and
+// the status word, as k_scan does.
+constexpr int kCopyWaves = 16;
+
+__global__ __launch_bounds__(64 * kCopyWaves) void k_copy_records(const Params p0, HeaderBytes hdr, int scan) {
   const Params p = at_seq(p0, blockIdx.z);
   const int r = blockIdx.x;
   if (r >= p.n_recs) return;
@@ -557,16 +596,19 @@ __global__ __launch_bounds__(256) void k_copy_records(const Params p0, HeaderByt
   const uint32_t* rec_size = reinterpret_cast<const uint32_t*>(p.ws + p.w.rec_size);
   const uint32_t size = rec_size[r];
   const uint32_t mode = reinterpret_cast<const uint32_t*>(p.ws + p.w.rec_mode)[r];
+  __shared__ uint64_t s_part[kCopyWaves];
+  __shared__ int64_t s_at[kMaxTilesPerRec + 1];
+  __shared__ RecGeo g;
   uint64_t pos;
   if (scan) {
     uint64_t part = 0;
-    for (int i = tid; i < r; i += 256) part += rec_size[i];
+    for (int i = tid; i < r; i += 64 * kCopyWaves) part += rec_size[i];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-    __shared__ uint64_t s_part[4];
     if (lane == 0) s_part[wave] = part;
     __syncthreads();
-    pos = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+    pos = 0;
+    for (int k = 0; k < kCopyWaves; ++k) pos += s_part[k];
     if (tid == 0) write_dir(p, r, pos, size, mode);
     if (r == p.n_recs - 1) finish_container(p, hdr, (uint64_t)p.chunks_off + pos + size, tid);
     // a record that does not fit is not copied (the last workgroup reports
@@ -578,56 +620,72 @@ __global__ __launch_bounds__(256) void k_copy_records(const Params p0, HeaderByt
   if (get_status(p.ws, p.w) & ((1u << KVTC_ERR_CAPACITY) | (1u << KVTC_ERR_NONFINITE))) return;
   if (size == 0) return;
   const int u = r / p.recs_per_sec, cr = r % p.recs_per_sec;
-  __shared__ RecGeo g;
   if (wave == 0) rec_setup(p, cr, p.ws + p.w.side_bits + (int64_t)u * p.D, g);
   __syncthreads();
-  uint8_t* dst = p.out_final + p.chunks_off + pos;  // 16-byte aligned record
-  // dword copy of n_dw dwords; the last one keeps only its low half when
-  // `half_last` (an odd word count padded with zeros)
-  auto copy_dw = [&](const uint32_t* src, uint32_t* d, int n_dw, bool half_last) {
-    for (int i0 = 0; i0 < n_dw; i0 += 4 * 256) {
-      uint32_t v[4];
+  const int ntiles = g.ntiles;
+  const uint8_t* slot = rec_slot(p, r);
+  const uint32_t* nwv = reinterpret_cast<const uint32_t*>(slot + slot_counts_off(p));
+  if (wave == 0) {  // where each tile's piece starts in the record
+    int64_t piece = 0;
+    if (lane < ntiles) {
+      const int64_t pt = lane == ntiles - 1 ? g.pl : g.pf;
+      if (mode == 1) {
+        piece = pt;
+      } else {
+        const uint32_t nw = nwv[lane];
+        piece = 4 * (int64_t)p.lanes + 2 * (int64_t)nw + ((nw & 1) ? 2 : 0) + (lane == ntiles - 1 ? g.rl : g.rf);
+      }
+    }
+    int64_t xs = piece;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = i0 + k * 256 + tid;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t y = __shfl_up(xs, o, 64);
+      if (lane >= o) xs += y;
+    }
+    const int64_t base = mode == 1 ? 0 : g.tb + 4 * (int64_t)ntiles;
+    if (lane < ntiles) s_at[lane] = base + xs - piece;
+    if (lane == ntiles - 1) s_at[ntiles] = base + xs;
+  }
+  __syncthreads();
+  uint8_t* dst = p.out_final + p.chunks_off + pos;  // 16-byte aligned record
+  // one wave copies n_dw dwords, eight in flight per lane; the last keeps only
+  // its low half when `half_last` (an odd word count padded with zeros)
+  auto copy_dw = [&](const uint32_t* src, uint32_t* d, int n_dw, bool half_last) {
+    for (int i0 = 0; i0 < n_dw; i0 += 8 * 64) {
+      uint32_t v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k * 64 + lane;
         v[k] = i < n_dw ? src[i] : 0u;
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = i0 + k * 256 + tid;
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k * 64 + lane;
         if (i < n_dw) d[i] = (half_last && i == n_dw - 1) ? (v[k] & 0xffffu) : v[k];
       }
     }
   };
-  int64_t at = 0;
-  const int ntiles = g.ntiles;
-  if (mode == 1) {
-    for (int t = 0; t < ntiles; ++t) {
+  for (int t = wave; t < ntiles; t += kCopyWaves) {
+    uint8_t* d = dst + s_at[t];
+    if (mode == 1) {
       const int32_t pt = t == ntiles - 1 ? g.pl : g.pf;
-      copy_dw(reinterpret_cast<const uint32_t*>(packed_tile(p, u, cr, t, g.pf)),
-              reinterpret_cast<uint32_t*>(dst + at), pt / 4, false);
-      at += pt;
-    }
-  } else {
-    const uint8_t* slot = rec_slot(p, r);
-    copy_dw(reinterpret_cast<const uint32_t*>(slot), reinterpret_cast<uint32_t*>(dst), g.tb / 4, false);
-    copy_dw(reinterpret_cast<const uint32_t*>(slot + slot_counts_off(p)), reinterpret_cast<uint32_t*>(dst + g.tb),
-            ntiles, false);
-    at = g.tb + 4 * (int64_t)ntiles;
-    const uint32_t* nwv = reinterpret_cast<const uint32_t*>(slot + slot_counts_off(p));
-    for (int t = 0; t < ntiles; ++t) {
+      copy_dw(reinterpret_cast<const uint32_t*>(packed_tile(p, u, cr, t, g.pf)), reinterpret_cast<uint32_t*>(d),
+              pt / 4, false);
+    } else {
       const uint32_t nw = nwv[t];
       const int n_dw = p.lanes + (int)((nw + 1) >> 1);  // states, words, zero pad to 4 bytes
-      copy_dw(reinterpret_cast<const uint32_t*>(slot + slot_tile_off(p, t)), reinterpret_cast<uint32_t*>(dst + at),
-              n_dw, (nw & 1) != 0);
-      at += 4 * (int64_t)n_dw;
+      copy_dw(reinterpret_cast<const uint32_t*>(slot + slot_tile_off(p, t)), reinterpret_cast<uint32_t*>(d), n_dw,
+              (nw & 1) != 0);
       const int32_t rbytes = t == ntiles - 1 ? g.rl : g.rf;
-      copy_dw(reinterpret_cast<const uint32_t*>(slot + slot_raw_off(p, t)), reinterpret_cast<uint32_t*>(dst + at),
+      copy_dw(reinterpret_cast<const uint32_t*>(slot + slot_raw_off(p, t)), reinterpret_cast<uint32_t*>(d + 4 * n_dw),
               rbytes / 4, false);
-      at += rbytes;
     }
   }
-  for (int64_t i = at + tid; i < size; i += 256) dst[i] = 0;
+  if (mode == 0 && wave == kCopyWaves - 1) {  // tables and word counts
+    copy_dw(reinterpret_cast<const uint32_t*>(slot), reinterpret_cast<uint32_t*>(dst), g.tb / 4, false);
+    copy_dw(nwv, reinterpret_cast<uint32_t*>(dst + g.tb), ntiles, false);
+  }
+  for (int64_t i = s_at[ntiles] + tid; i < size; i += 64 * kCopyWaves) dst[i] = 0;
 }
 
 hipError_t launch_assemble(const Params& p, const uint8_t* hdr, hipStream_t s) {
@@ -636,7 +694,7 @@ hipError_t launch_assemble(const Params& p, const uint8_t* hdr, hipStream_t s) {
   if (p.n_seqs == 0 && p.n_recs > 0 && p.n_recs <= 2048) {
     // one launch: offsets (each workgroup sums at most 2047 sizes), directory,
     // header and records
-    hipLaunchKernelGGL(k_copy_records, dim3(p.n_recs), dim3(256), 0, s, p, h, 1);
+    hipLaunchKernelGGL(k_copy_records, dim3(p.n_recs), dim3(64 * kCopyWaves), 0, s, p, h, 1);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_scan, dim3(1, 1, seq_grid(p)), dim3(1024), 0, s, p, h);
@@ -645,7 +703,8 @@ hipError_t launch_assemble(const Params& p, const uint8_t* hdr, hipStream_t s) {
     const hipError_t e = launch_batch_place(p, s);
     if (e != hipSuccess) return e;
   }
-  if (p.n_recs > 0) hipLaunchKernelGGL(k_copy_records, dim3(p.n_recs, 1, seq_grid(p)), dim3(256), 0, s, p, h, 0);
+  if (p.n_recs > 0)
+    hipLaunchKernelGGL(k_copy_records, dim3(p.n_recs, 1, seq_grid(p)), dim3(64 * kCopyWaves), 0, s, p, h, 0);
   return hipGetLastError();
 }
 
@@ -685,12 +744,11 @@ hipError_t launch_dec_check(const Params& p, const uint8_t* hdr, hipStream_t s) 
 
 constexpr int kRing = 512;  // words of a stream's LDS ring
 constexpr int kUnit = 256;  // words per refill
-constexpr int kRawWords = 34;  // a staged raw row of a 256-token tile (<= 32 words), zero-padded
 
 // raw_runs > 0 (contiguous cache): workgroups past the chunks copy the raw
 // sink and recent runs of the container to the outputs, which costs the
 // bandwidth this latency-bound pass leaves idle.
-template <int LANES>
+template <int LANES, int STEPS>
 __global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw_runs) {
   constexpr int SPW = 64 / LANES;
   constexpr int NR = 32 / LANES + 1;  // staged raw-row words per lane
@@ -709,6 +767,7 @@ __global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw
   __shared__ int s_ok;
   __shared__ uint32_t outbuf[kMaxTilesPerRec][kRowWords];
   __shared__ uint32_t rawbuf[kMaxTilesPerRec][2][kRawWords];
+  __shared__ uint8_t bucket[kMaxD * 256];  // symbol at the start of each 16-slot bucket, per coded component
   extern __shared__ uint16_t rings[];  // kRing words per tile
   if (wave == 0) rec_setup(p, cr, p.in + p.side_off + (int64_t)u * 9 * p.D, g);
   __syncthreads();
@@ -791,6 +850,21 @@ __global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw
     if (tid == 0) set_status(p.ws, p.w, KVTC_ERR_CORRUPT);
     return;
   }
+  // the symbol of the first slot of every 16-slot bucket (the last symbol
+  // whose cumulative start is at most that slot)
+  const int nbk = (int)(M >> 4);
+  for (int it = tid; it < nc * nbk; it += blockDim.x) {
+    const int ci = it / nbk, bk = it - ci * nbk;
+    const uint32_t* cm = cumt + ci * 17;
+    const uint32_t slot0 = (uint32_t)bk << 4;
+    uint32_t sy = 0;
+    sy += cm[sy + 8] <= slot0 ? 8u : 0u;
+    sy += cm[sy + 4] <= slot0 ? 4u : 0u;
+    sy += cm[sy + 2] <= slot0 ? 2u : 0u;
+    sy += cm[sy + 1] <= slot0 ? 1u : 0u;
+    bucket[ci * 256 + bk] = (uint8_t)sy;
+  }
+  __syncthreads();
   const int grp = lane / LANES, j = lane % LANES;
   const int t = wave * SPW + grp;
   const bool valid = t < ntiles;
@@ -840,21 +914,29 @@ __global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw
   int steps_max = (m + LANES - 1) / LANES;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) steps_max = max(steps_max, __shfl_xor(steps_max, o, 64));
-  steps_max = __builtin_amdgcn_readfirstlane(steps_max);
+  steps_max = STEPS > 0 ? STEPS : __builtin_amdgcn_readfirstlane(steps_max);
   uint32_t* ob = &outbuf[tt][0];
   uint32_t* rbb = &rawbuf[tt][0][0];
   if (valid)
     for (int w = j; w < kRowWords; w += LANES) ob[w] = 0u;
+  // the record (raw rows) and its packed tiles (the rows this kernel
+  // writes) through buffer resources, so that lanes past a row load zeros and
+  // drop their stores without a branch
+  const __amdgpu_buffer_rsrc_t rrsrc = uniform_rsrc(const_cast<uint8_t*>(rec), (int32_t)size);
+  const int32_t raws_at = (int32_t)(reinterpret_cast<const uint8_t*>(raws) - rec);
+  const int32_t prec_bytes = (int32_t)((int64_t)p.blks_per_rec * p.w.packed_slot);
+  const __amdgpu_buffer_rsrc_t prsrc = uniform_rsrc(packed_tile(p, u, cr, 0, g.pf), prec_bytes);
+  const int32_t tile_at = (int32_t)((int64_t)(tt / p.tiles_per_blk) * p.w.packed_slot + (int64_t)(tt % p.tiles_per_blk) * g.pf);
   // the raw row of component i of this tile: registers, then LDS
   uint32_t rpre[NR];
   auto raw_load = [&](int i) {
     const uint32_t rr = (uint32_t)raw_bits_of((int)g.b[i]);
     const int Wr = rr ? (m * (int)rr + 31) >> 5 : 0;
-    const uint32_t* src = raws + g.raoff[last][i];
+    const int32_t at = raws_at + 4 * (int32_t)g.raoff[last][i];
 #pragma unroll
     for (int q = 0; q < NR; ++q) {
       const int w = j + q * LANES;
-      rpre[q] = (valid && w < Wr) ? src[w] : 0u;
+      rpre[q] = __builtin_amdgcn_raw_buffer_load_b32(rrsrc, (valid && w < Wr) ? at + 4 * w : (int32_t)size, 0, 0);
     }
   };
   auto raw_store = [&](int which) {
@@ -871,36 +953,48 @@ __global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw
   for (int ci = 0; ci < nc; ++ci) {
     const int i = g.coded[ci];
     const uint32_t b = g.b[i], rr = b - (uint32_t)sym_bits_of((int)b);
+    const uint32_t rmask = (1u << rr) - 1u;
     if (ci + 1 < nc) raw_load(g.coded[ci + 1]);
+    // A component takes at most tile_tokens <= kUnit words, so one refill test
+    // per component keeps the ring ahead: after a refill at least kUnit
+    // committed words remain unread.
+    if (valid && clo > 0 && ptr - clo <= kUnit) {
+      // the ring slots of [plo, clo) held words >= clo + kUnit >= ptr: consumed
+#pragma unroll
+      for (int q2 = 0; q2 < PER; ++q2) {
+        const int32_t q = plo / 2 + j + LANES * q2;
+        if (q < clo / 2) ring32[q & (kRing / 2 - 1)] = pend[q2];
+      }
+      clo = plo;
+      plo = max(0, clo - kUnit);
+#pragma unroll
+      for (int q2 = 0; q2 < PER; ++q2) {
+        const int32_t q = plo / 2 + j + LANES * q2;
+        pend[q2] = q < clo / 2 ? wd[q] : 0u;
+      }
+    }
     __builtin_amdgcn_wave_barrier();
     const uint32_t* rw = rbb + (ci & 1) * kRawWords;
     const uint32_t* cm = cumt + ci * 17;
-    for (int s = 0; s < steps_max; ++s) {
-      if (valid && clo > 0 && ptr - clo <= kUnit) {
-        // the ring slots of [plo, clo) held words >= clo + kUnit >= ptr: consumed
+    const uint8_t* bkt = bucket + ci * 256;
+    const uint32_t jb = (uint32_t)j * b, jr = (uint32_t)j * rr;
+    const uint32_t sb_step = (uint32_t)LANES * b, sr_step = (uint32_t)LANES * rr;
+    const bool straddles = (b & (b - 1)) != 0;  // widths 3, 5, 6, 7: a code may cross a word
 #pragma unroll
-        for (int q2 = 0; q2 < PER; ++q2) {
-          const int32_t q = plo / 2 + j + LANES * q2;
-          if (q < clo / 2) ring32[q & (kRing / 2 - 1)] = pend[q2];
-        }
-        clo = plo;
-        plo = max(0, clo - kUnit);
-#pragma unroll
-        for (int q2 = 0; q2 < PER; ++q2) {
-          const int32_t q = plo / 2 + j + LANES * q2;
-          pend[q2] = q < clo / 2 ? wd[q] : 0u;
-        }
-      }
+    for (int s = 0; s < (STEPS > 0 ? STEPS : steps_max); ++s) {
       const int k = s * LANES + j;
       const bool active = valid && k < m;
       const uint32_t slot = x & (M - 1u);
-      // the symbol whose cumulative range holds the slot
-      uint32_t sy = 0;
-      sy += cm[sy + 8] <= slot ? 8u : 0u;
-      sy += cm[sy + 4] <= slot ? 4u : 0u;
-      sy += cm[sy + 2] <= slot ? 2u : 0u;
-      sy += cm[sy + 1] <= slot ? 1u : 0u;
-      const uint32_t c0 = cm[sy], c1 = cm[sy + 1];
+      // the symbol whose cumulative range holds the slot: the bucket's first
+      // symbol, moved past any range that ends inside the bucket (rare: it
+      // takes a frequency below 16); cm[16] = M ends the walk
+      uint32_t sy = bkt[slot >> 4];
+      uint32_t c0 = cm[sy], c1 = cm[sy + 1];
+      while (c1 <= slot) {
+        ++sy;
+        c0 = c1;
+        c1 = cm[sy + 1];
+      }
       const uint32_t xn = (c1 - c0) * (x >> p.sb) + slot - c0;
       x = active ? xn : x;
       const bool need = active && x < kRansL;
@@ -910,30 +1004,32 @@ __global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw
       const uint32_t wnext = ring[(uint32_t)(ptr - 1 - (int32_t)rank) & (kRing - 1)];
       x = need ? ((x << 16) | wnext) : x;
       ptr -= (int32_t)(__popc(mlo) + __popc(mhi));
-      if (active) {
-        uint32_t code = sy << rr;
-        if (rr) {
-          const uint32_t bq = (uint32_t)k * rr;
-          code |= funnel(rw[bq >> 5], rw[(bq >> 5) + 1], bq & 31) & ((1u << rr) - 1u);
-        }
-        const uint32_t bp = (uint32_t)k * b;
-        const uint32_t sh = bp & 31;
-        atomicOr(&ob[bp >> 5], code << sh);
-        if (sh + b > 32) atomicOr(&ob[(bp >> 5) + 1], code >> (32 - sh));
+      // the code into the component's packed row (inactive lanes OR zero)
+      uint32_t code = sy << rr;
+      if (rr) {
+        const uint32_t bq = active ? jr + (uint32_t)s * sr_step : 0u;
+        code |= funnel(rw[bq >> 5], rw[(bq >> 5) + 1], bq & 31) & rmask;
       }
+      code = active ? code : 0u;
+      const uint32_t bp = active ? jb + (uint32_t)s * sb_step : 0u;
+      const uint32_t sh = bp & 31;
+      atomicOr(&ob[bp >> 5], code << sh);
+      if (straddles) atomicOr(&ob[(bp >> 5) + 1], (uint32_t)(((uint64_t)code << sh) >> 32));
     }
-    // flush the component's packed row, clear the buffer
+    // the next component's raw row goes to LDS first (its loads were issued
+    // before this component's row stores, so the wait does not cover them);
+    // then the component's packed row is flushed and the buffer cleared
+    if (ci + 1 < nc) raw_store((ci + 1) & 1);
     __builtin_amdgcn_wave_barrier();
     const int W = (m * (int)b + 31) >> 5;
-    uint32_t* dst = tbase + g.roff[last][i];
-    if (valid) {
-      for (int w = j; w < kRowWords; w += LANES) {
-        const uint32_t v = ob[w];
-        if (w < W) dst[w] = v;
-        ob[w] = 0u;
-      }
+    const int32_t at = tile_at + 4 * (int32_t)g.roff[last][i];
+#pragma unroll
+    for (int q = 0; q < (kRowWords + LANES - 1) / LANES; ++q) {
+      const int w = j + q * LANES;
+      const uint32_t v = w < kRowWords ? ob[w] : 0u;
+      __builtin_amdgcn_raw_buffer_store_b32(v, prsrc, (valid && w < W) ? at + 4 * w : prec_bytes, 0, 0);
+      if (valid && w < kRowWords) ob[w] = 0u;
     }
-    if (ci + 1 < nc) raw_store((ci + 1) & 1);
   }
   const bool ok = !(bad0 || (valid && (x != kRansL || ptr != 0)));
   if (__ballot(!ok)) {
@@ -947,8 +1043,16 @@ hipError_t launch_rans_decode_chunks(const Params& p, hipStream_t s, bool with_r
   const size_t lds = (size_t)p.tiles_per_rec * kRing * 2;  // one word ring per tile
   const int raw_runs = with_raw && p.n_seqs == 0 ? 4 * p.L * p.H : 0;
   const dim3 grid(p.n_recs + raw_runs, 1, seq_grid(p)), block(64 * waves);
-  if (p.lanes == 16) hipLaunchKernelGGL(k_rans_dec_recs<16>, grid, block, lds, s, p, raw_runs);
-  else hipLaunchKernelGGL(k_rans_dec_recs<32>, grid, block, lds, s, p, raw_runs);
+  const int steps = p.tile_tokens / p.lanes;
+  if (p.lanes == 16) {
+    if (steps == 16) hipLaunchKernelGGL((k_rans_dec_recs<16, 16>), grid, block, lds, s, p, raw_runs);
+    else if (steps == 8) hipLaunchKernelGGL((k_rans_dec_recs<16, 8>), grid, block, lds, s, p, raw_runs);
+    else hipLaunchKernelGGL((k_rans_dec_recs<16, 0>), grid, block, lds, s, p, raw_runs);
+  } else {
+    if (steps == 8) hipLaunchKernelGGL((k_rans_dec_recs<32, 8>), grid, block, lds, s, p, raw_runs);
+    else if (steps == 4) hipLaunchKernelGGL((k_rans_dec_recs<32, 4>), grid, block, lds, s, p, raw_runs);
+    else hipLaunchKernelGGL((k_rans_dec_recs<32, 0>), grid, block, lds, s, p, raw_runs);
+  }
   return hipGetLastError();
 }
 
