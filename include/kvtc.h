@@ -27,7 +27,8 @@
  *    KVTC_ERR_INVALID_ARG.
  *  - The caller owns every buffer (device memory from any allocator, e.g.
  *    PyTorch).  The library never allocates device memory: plan memory and
- *    workspaces are passed in, sized by the *_size queries.
+ *    workspaces are passed in, sized by the *_size queries.  The one
+ *    exception is the fixed per-device array of kvtc_decode_noalloc.
  *  - Calls return a kvtc_status; no exception crosses the ABI.  Argument
  *    errors are reported synchronously and nothing is enqueued.  Errors found
  *    on the device (corrupt container, non-finite input, capacity) are
@@ -173,6 +174,35 @@ kvtc_status kvtc_encode(kvtc_plan_t plan, const void* k, const void* v, int32_t 
 kvtc_status kvtc_decode(kvtc_plan_t plan, const void* in, size_t in_bytes, int32_t T,
                         void* k_out, void* v_out, int32_t out_dtype, void* ws, size_t ws_bytes,
                         hipStream_t stream);
+
+/* ---- decode without allocation ----------------------------------------- */
+
+/* Bytes of the fixed device array kvtc_decode_noalloc works in. */
+#define KVTC_NOALLOC_SCRATCH_BYTES ((int64_t)128 << 20)
+
+/* For callers that cannot allocate device memory or hand in a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  kvtc_decode with its workspace replaced by a fixed array inside
+ * the library: KVTC_NOALLOC_SCRATCH_BYTES of device memory per device, held
+ * from the code object's load on that device until the process ends.  The
+ * decoder needs a 256-aligned status block of 8448 bytes plus its packed
+ * tiles there (about 71 MB for 32 layers x 8 KV heads x 4096 tokens x
+ * head_dim 128 at 2 bits per component); a call that needs more returns
+ * KVTC_ERR_CAPACITY and enqueues nothing.  The call allocates nothing:
+ * no hipMalloc, hipFree, event or library allocation.
+ *
+ * Arguments, outputs and device checks are those of kvtc_decode.  When
+ * status_dev (device, 4-byte aligned) is not NULL, the decode's status word
+ * is copied there after the last kernel: 0, or bit KVTC_ERR_CORRUPT set for a
+ * damaged container.
+ *
+ * Every call on a device works in that device's one array, which keeps the
+ * last call's contents (each call clears what it reads back).  Calls that
+ * overlap in time on one device -- different streams or host threads --
+ * race: the caller serialises them (one stream does). */
+kvtc_status kvtc_decode_noalloc(kvtc_plan_t plan, const void* in, size_t in_bytes, int32_t T,
+                                void* k_out, void* v_out, int32_t out_dtype, uint32_t* status_dev,
+                                hipStream_t stream);
 
 /* ---- paged ragged batches ---------------------------------------------- */
 

@@ -4,6 +4,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "kvtc_internal.h"
@@ -154,14 +155,14 @@ struct ProfScope {
   PlanImpl* pl;
   hipStream_t s;
   explicit ProfScope(PlanImpl* p, hipStream_t st) : pl(p), s(st) {
-    if (pl->prof_on) {
+    if (pl && pl->prof_on) {
       pl->prof_n = 0;
       (void)hipEventRecord(pl->prof_ev[0], s);
       pl->prof_n = 1;
     }
   }
   void phase(const char* name) {
-    if (!pl->prof_on || pl->prof_n >= 24) return;
+    if (!pl || !pl->prof_on || pl->prof_n >= 24) return;
     pl->prof_name[pl->prof_n - 1] = name;
     (void)hipEventRecord(pl->prof_ev[pl->prof_n], s);
     pl->prof_n += 1;
@@ -382,24 +383,26 @@ kvtc_status kvtc_encode(kvtc_plan_t plan, const void* k, const void* v, int32_t 
   return KVTC_OK;
 }
 
-kvtc_status kvtc_decode(kvtc_plan_t plan, const void* in, size_t in_bytes, int32_t T,
-                        void* k_out, void* v_out, int32_t out_dtype, void* ws, size_t ws_bytes,
-                        hipStream_t stream) {
-  if (!plan || !in || !ws) return KVTC_ERR_INVALID_ARG;
-  PlanImpl* pl = (PlanImpl*)plan;
+// Checks shared by the decode entry points (all but the workspace).
+static kvtc_status decode_args(const PlanImpl* pl, const void* in, int32_t T, const void* k_out,
+                               const void* v_out, int32_t out_dtype) {
   if (T < 0 || T > pl->cfg.max_tokens) return KVTC_ERR_INVALID_ARG;
   if (T > 0 && (!k_out || !v_out)) return KVTC_ERR_INVALID_ARG;
   if (out_dtype != KVTC_BF16 && out_dtype != KVTC_FP32) return KVTC_ERR_INVALID_ARG;
-  if (misaligned(in) || misaligned(k_out) || misaligned(v_out) || misaligned(ws)) return KVTC_ERR_INVALID_ARG;
-  Layout lo = make_layout(pl->cfg, T);
-  WsLayout w = make_ws_layout(pl->cfg, lo);
-  if ((int64_t)ws_bytes < w.total) return KVTC_ERR_CAPACITY;
+  if (misaligned(in) || misaligned(k_out) || misaligned(v_out)) return KVTC_ERR_INVALID_ARG;
+  return KVTC_OK;
+}
+
+// The decode launch sequence on a workspace laid out as `w`.
+static kvtc_status decode_launch(PlanImpl* pl, const Layout& lo, const WsLayout& w, const void* in,
+                                 size_t in_bytes, void* k_out, void* v_out, int32_t out_dtype, uint8_t* ws,
+                                 hipStream_t stream, bool profile) {
   Params p = make_params(*pl, lo, w);
-  p.in = (const uint8_t*)in; p.cap = (int64_t)in_bytes; p.ws = (uint8_t*)ws;
+  p.in = (const uint8_t*)in; p.cap = (int64_t)in_bytes; p.ws = ws;
   p.k_out = k_out; p.v_out = v_out; p.out_dtype = out_dtype;
   uint8_t hdr[kHeaderBytes];
   build_header(*pl, lo, hdr);
-  ProfScope prof(pl, stream);
+  ProfScope prof(profile ? pl : nullptr, stream);
   HIP_TRY(launch_dec_check(p, hdr, stream));  // clears, then sets the status word
   prof.phase("dec_check");
   if (lo.n_blks > 0) {
@@ -412,6 +415,83 @@ kvtc_status kvtc_decode(kvtc_plan_t plan, const void* in, size_t in_bytes, int32
     HIP_TRY(launch_copy_raw(p, 0, stream));
     prof.phase("copy_raw_out");
   }
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_decode(kvtc_plan_t plan, const void* in, size_t in_bytes, int32_t T,
+                        void* k_out, void* v_out, int32_t out_dtype, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  if (!plan || !in || !ws) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* pl = (PlanImpl*)plan;
+  const kvtc_status st = decode_args(pl, in, T, k_out, v_out, out_dtype);
+  if (st != KVTC_OK) return st;
+  if (misaligned(ws)) return KVTC_ERR_INVALID_ARG;
+  Layout lo = make_layout(pl->cfg, T);
+  WsLayout w = make_ws_layout(pl->cfg, lo);
+  if ((int64_t)ws_bytes < w.total) return KVTC_ERR_CAPACITY;
+  return decode_launch(pl, lo, w, in, in_bytes, k_out, v_out, out_dtype, (uint8_t*)ws, stream, true);
+}
+
+// ---- decode into a fixed device array ------------------------------------------
+
+// The decoder's only workspace is the status block and the packed tiles; the
+// variant below keeps both in this array (one copy per device, alive until
+// the process ends) instead of a caller's workspace.
+constexpr int64_t kScratchBytes = KVTC_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static uint8_t* g_scratch_at[kMaxDevices];  // device address of `scratch`, per device
+
+// The device address of the current device's copy of `scratch`, looked up on
+// the first call on that device.
+static kvtc_status scratch_of_current_device(uint8_t** at) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return KVTC_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return KVTC_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_at[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KVTC_ERR_HIP;
+    g_scratch_at[dev] = (uint8_t*)ptr;
+  }
+  *at = g_scratch_at[dev];
+  return KVTC_OK;
+}
+
+// The decoder's workspace inside the scratch array: the status block, then
+// the packed tiles; every other region is unused by the decode kernels and
+// points at the status block.
+static WsLayout decode_scratch_layout(const kvtc_config& c, const Layout& lo) {
+  const WsLayout full = make_ws_layout(c, lo);
+  WsLayout w{};
+  w.packed_slot = full.packed_slot;
+  w.tile_words_max = full.tile_words_max;
+  w.tile_raw_max = full.tile_raw_max;
+  w.rec_slot = full.rec_slot;
+  w.status = 0;
+  w.packed = align256(kStatusBlockBytes);
+  w.total = w.packed + align256((int64_t)lo.n_blks * w.packed_slot);
+  return w;
+}
+
+kvtc_status kvtc_decode_noalloc(kvtc_plan_t plan, const void* in, size_t in_bytes, int32_t T, void* k_out,
+                                void* v_out, int32_t out_dtype, uint32_t* status_dev, hipStream_t stream) {
+  if (!plan || !in) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* pl = (PlanImpl*)plan;
+  const kvtc_status st = decode_args(pl, in, T, k_out, v_out, out_dtype);
+  if (st != KVTC_OK) return st;
+  if ((uintptr_t)status_dev & 3u) return KVTC_ERR_INVALID_ARG;
+  Layout lo = make_layout(pl->cfg, T);
+  WsLayout w = decode_scratch_layout(pl->cfg, lo);
+  if (w.total > kScratchBytes) return KVTC_ERR_CAPACITY;
+  uint8_t* ws = nullptr;
+  const kvtc_status sst = scratch_of_current_device(&ws);
+  if (sst != KVTC_OK) return sst;
+  const kvtc_status lst = decode_launch(pl, lo, w, in, in_bytes, k_out, v_out, out_dtype, ws, stream, false);
+  if (lst != KVTC_OK) return lst;
+  if (status_dev) HIP_TRY(hipMemcpyAsync(status_dev, ws + w.status, 4, hipMemcpyDeviceToDevice, stream));
   return KVTC_OK;
 }
 

@@ -59,6 +59,9 @@ EXPORTS = {
     "kvtc_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                    ctypes.c_size_t, ctypes.c_void_p]),
+    "kvtc_decode_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_void_p]),
     "kvtc_workspace_size_paged": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                                  ctypes.POINTER(ctypes.c_size_t),
                                                  ctypes.POINTER(ctypes.c_size_t)]),
@@ -192,6 +195,14 @@ class Plan:
         od = out_dtype if out_dtype is not None else (BF16 if k_out.dtype == torch.bfloat16 else FP32)
         _check(lib().kvtc_decode(self.handle, _ptr(data), nbytes, T, _ptr(k_out), _ptr(v_out), od,
                                  _ptr(ws), ws.numel(), _stream(stream)), "kvtc_decode")
+
+    def decode_noalloc_async(self, data: torch.Tensor, nbytes: int, T: int, k_out: torch.Tensor,
+                             v_out: torch.Tensor, status: torch.Tensor | None, out_dtype: int = FP32,
+                             stream=None):
+        """kvtc_decode_noalloc: decode in the library's fixed device array;
+        the status word goes to `status` (device int32 [1]) when given."""
+        _check(lib().kvtc_decode_noalloc(self.handle, _ptr(data), nbytes, T, _ptr(k_out), _ptr(v_out),
+                                         out_dtype, _ptr(status), _stream(stream)), "kvtc_decode_noalloc")
 
     def result(self, ws: torch.Tensor):
         n = ctypes.c_uint64(0)
