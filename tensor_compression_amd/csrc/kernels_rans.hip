@@ -26,6 +26,8 @@
 // back into packed tiles for the decode transform).
 #include <string.h>
 
+#include <algorithm>
+
 #include "kvtc_internal.h"
 
 namespace kvtc {
@@ -266,33 +268,35 @@ __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw
   const __amdgpu_buffer_rsrc_t prsrc = uniform_rsrc(packed_tile(p, u, cr, 0, g.pf), prec_bytes);
   const int32_t tile_at = (int32_t)((int64_t)(tt / p.tiles_per_blk) * p.w.packed_slot + (int64_t)(tt % p.tiles_per_blk) * g.pf);
   // the row of component i of this tile: NQ words per lane into registers
-  // (lanes past the row load zeros), then into this stream's LDS row buffer
-  uint32_t pre[NQ];
-  auto row_load = [&](int i) {
+  // (lanes past the row load zeros), then into this stream's LDS row buffer.
+  // Two register sets alternate between even and odd components, so a row
+  // is loaded two components before its use and the load's latency hides
+  // behind a whole component.
+  uint32_t pre0[NQ], pre1[NQ];
+  auto row_load = [&](uint32_t(&pr)[NQ], int i) {
     const int W = (m * (int)g.b[i] + 31) >> 5;
     const int32_t at = tile_at + 4 * (int32_t)g.roff[last][i];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int w = j + q * LANES;
-      pre[q] = __builtin_amdgcn_raw_buffer_load_b32(prsrc, (valid && w < W) ? at + 4 * w : prec_bytes, 0, 0);
+      pr[q] = __builtin_amdgcn_raw_buffer_load_b32(prsrc, (valid && w < W) ? at + 4 * w : prec_bytes, 0, 0);
     }
   };
-  auto row_store = [&](int which) {
+  auto row_store = [&](const uint32_t(&pr)[NQ], int which) {
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int w = j + q * LANES;
-      if (valid && w < kRowWords) rb[which * kRowWords + w] = pre[q];
+      if (valid && w < kRowWords) rb[which * kRowWords + w] = pr[q];
     }
   };
   // -- histograms: each stream counts its tile's symbols component by
-  // component from the staged rows (the next row in flight meanwhile)
+  // component from the staged rows
   if (has_stream && nc > 0) {
-    row_load(g.coded[0]);
-    row_store(0);
-    for (int ci = 0; ci < nc; ++ci) {
+    auto hist_component = [&](int ci, uint32_t(&pr)[NQ]) {
       const int i = g.coded[ci];
       const uint32_t b = g.b[i], rr = b - (uint32_t)sym_bits_of((int)b);
-      if (ci + 1 < nc) row_load(g.coded[ci + 1]);
+      row_store(pr, ci & 1);  // its buffer was last read two components ago
+      if (ci + 2 < nc) row_load(pr, g.coded[ci + 2]);
       __builtin_amdgcn_wave_barrier();
       const uint32_t* rw = rb + (ci & 1) * kRowWords;
       uint32_t* hc = hist + ci * 17;
@@ -305,7 +309,12 @@ __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw
           atomicAdd(&hc[code >> rr], 1u);
         }
       }
-      if (ci + 1 < nc) row_store((ci + 1) & 1);
+    };
+    row_load(pre0, g.coded[0]);
+    if (nc > 1) row_load(pre1, g.coded[1]);
+    for (int ci = 0; ci < nc; ci += 2) {
+      hist_component(ci, pre0);
+      if (ci + 1 < nc) hist_component(ci + 1, pre1);
     }
   }
   __syncthreads();
@@ -344,15 +353,12 @@ __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw
     uint32_t* rrow = &rawrow[tt][0];
     if (valid)
       for (int w = j; w < kRawWords; w += LANES) rrow[w] = 0u;
-    if (nc > 0) {
-      row_load(g.coded[nc - 1]);
-      row_store((nc - 1) & 1);
-    }
-    for (int ci = nc - 1; ci >= 0; --ci) {
+    auto enc_component = [&](int ci, uint32_t(&pr)[NQ]) {
       const int i = g.coded[ci];
       const uint32_t b = g.b[i], rr = b - (uint32_t)sym_bits_of((int)b);
       const uint32_t mask = (1u << b) - 1u, rmask = (1u << rr) - 1u;
-      if (ci > 0) row_load(g.coded[ci - 1]);  // the next component's row, in flight meanwhile
+      row_store(pr, ci & 1);  // its buffer was last read two components ago
+      if (ci >= 2) row_load(pr, g.coded[ci - 2]);
       __builtin_amdgcn_wave_barrier();
       const uint32_t* rw = rb + (ci & 1) * kRowWords;
       const uint4* tc = reinterpret_cast<const uint4*>(tab + ci * 16);
@@ -416,7 +422,12 @@ __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw
           if (valid && w < kRawWords) rrow[w] = 0u;
         }
       }
-      if (ci > 0) row_store((ci - 1) & 1);
+    };
+    if (nc > 0) row_load(pre0, g.coded[nc - 1]);
+    if (nc > 1) row_load(pre1, g.coded[nc - 2]);
+    for (int ci = nc - 1; ci >= 0; ci -= 2) {
+      enc_component(ci, pre0);
+      if (ci >= 1) enc_component(ci - 1, pre1);
     }
     if (valid) states[j] = x;
     // 1-bit components: the packed row is the raw row
@@ -745,9 +756,56 @@ hipError_t launch_dec_check(const Params& p, const uint8_t* hdr, hipStream_t s) 
 constexpr int kRing = 512;  // words of a stream's LDS ring
 constexpr int kUnit = 256;  // words per refill
 
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
+// Decoder slot table of one component: entry s describes the symbol whose
+// cumulative range holds slot s -- its frequency f (bits 16..28), the symbol
+// (bits 12..15) and s minus the range's start (bits 0..11) -- so that one
+// LDS read per step gives x <- f (x >> sb) + offset and the symbol.
+__device__ __forceinline__ uint32_t slot_entry(uint32_t f, uint32_t sy, uint32_t off) {
+  return (f << 16) | (sy << 12) | off;
+}
+
+// Fills tab[0, M) from a component's cumulative frequencies cm[0..16]
+// (entries past the alphabet hold M; cm is non-decreasing and ends at M), 8
+// consecutive slots per thread: the last symbol whose range starts at or
+// before the first slot (binary search), then a walk over the run.
+__device__ __forceinline__ void build_slot_table(const uint32_t* cm, uint32_t M, uint32_t* tab, uint32_t tid,
+                                                 uint32_t nthreads) {
+  for (uint32_t s0 = tid * 8u; s0 < M; s0 += nthreads * 8u) {
+    uint32_t sy = 0;
+    sy += cm[sy + 8] <= s0 ? 8u : 0u;
+    sy += cm[sy + 4] <= s0 ? 4u : 0u;
+    sy += cm[sy + 2] <= s0 ? 2u : 0u;
+    sy += cm[sy + 1] <= s0 ? 1u : 0u;
+    uint32_t c0 = cm[sy], c1 = cm[sy + 1];
+    uint32_t e[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t sl = s0 + (uint32_t)q;
+      while (c1 <= sl) {
+        ++sy;
+        c0 = c1;
+        c1 = cm[sy + 1];
+      }
+      e[q] = slot_entry(c1 - c0, sy, sl - c0);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(tab + s0);
+    dst[0] = make_uint4(e[0], e[1], e[2], e[3]);
+    dst[1] = make_uint4(e[4], e[5], e[6], e[7]);
+  }
+}
+
 // raw_runs > 0 (contiguous cache): workgroups past the chunks copy the raw
 // sink and recent runs of the container to the outputs, which costs the
 // bandwidth this latency-bound pass leaves idle.
+//
+// The workgroup walks the coded components in lockstep: while its streams
+// decode component ci with ci's slot table, every thread helps build the
+// table of ci + 1 in the other buffer, and a barrier ends the component.
 template <int LANES, int STEPS>
 __global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw_runs) {
   constexpr int SPW = 64 / LANES;
@@ -767,8 +825,10 @@ __global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw
   __shared__ int s_ok;
   __shared__ uint32_t outbuf[kMaxTilesPerRec][kRowWords];
   __shared__ uint32_t rawbuf[kMaxTilesPerRec][2][kRawWords];
-  __shared__ uint8_t bucket[kMaxD * 256];  // symbol at the start of each 16-slot bucket, per coded component
-  extern __shared__ uint16_t rings[];  // kRing words per tile
+  // dynamic: one word ring per tile (kRing u16), then two slot tables of 2^sb u32
+  extern __shared__ __align__(16) uint8_t dyn[];
+  uint16_t* rings = reinterpret_cast<uint16_t*>(dyn);
+  uint32_t* stab = reinterpret_cast<uint32_t*>(dyn + (size_t)p.tiles_per_rec * kRing * 2);
   if (wave == 0) rec_setup(p, cr, p.in + p.side_off + (int64_t)u * 9 * p.D, g);
   __syncthreads();
   const uint8_t* dir = p.in + p.dir_off + (int64_t)r * kDirEntry;
@@ -830,8 +890,8 @@ __global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw
     }
     return;
   }
-  // tables -> cumulative frequencies (entries past the alphabet hold M, so a
-  // 16-entry search never selects them); each table must sum to M
+  // tables -> cumulative frequencies (entries past the alphabet hold M, so
+  // every search stops inside the alphabet); each table must sum to M
   const uint32_t M = 1u << p.sb;
   for (int ci = tid; ci < nc; ci += blockDim.x) {
     const int i = g.coded[ci];
@@ -850,41 +910,54 @@ __global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw
     if (tid == 0) set_status(p.ws, p.w, KVTC_ERR_CORRUPT);
     return;
   }
-  // the symbol of the first slot of every 16-slot bucket (the last symbol
-  // whose cumulative start is at most that slot)
-  const int nbk = (int)(M >> 4);
-  for (int it = tid; it < nc * nbk; it += blockDim.x) {
-    const int ci = it / nbk, bk = it - ci * nbk;
-    const uint32_t* cm = cumt + ci * 17;
-    const uint32_t slot0 = (uint32_t)bk << 4;
-    uint32_t sy = 0;
-    sy += cm[sy + 8] <= slot0 ? 8u : 0u;
-    sy += cm[sy + 4] <= slot0 ? 4u : 0u;
-    sy += cm[sy + 2] <= slot0 ? 2u : 0u;
-    sy += cm[sy + 1] <= slot0 ? 1u : 0u;
-    bucket[ci * 256 + bk] = (uint8_t)sy;
-  }
-  __syncthreads();
+  // waves past the streams' (when the launch adds them) build the slot
+  // tables of the components ahead while the streams decode; without them
+  // every thread builds
+  const int stream_waves = (p.tiles_per_rec * LANES + 63) / 64;
+  const bool builders = (int)(blockDim.x >> 6) > stream_waves;
+  const uint32_t btid = builders ? (uint32_t)(tid - 64 * stream_waves) : (uint32_t)tid;
+  const uint32_t bthreads = builders ? blockDim.x - 64u * stream_waves : blockDim.x;
+  const bool builds = !builders || wave >= stream_waves;
+  if (nc > 0) build_slot_table(cumt, M, stab, tid, blockDim.x);
   const int grp = lane / LANES, j = lane % LANES;
   const int t = wave * SPW + grp;
   const bool valid = t < ntiles;
   const bool last = valid && t == ntiles - 1;
   const int m = !valid ? 0 : (last ? g.n_last : p.tile_tokens);
   const int tt = valid ? t : 0;
+  const bool has_stream = wave * SPW < ntiles;  // wave-uniform
   uint32_t* tbase = reinterpret_cast<uint32_t*>(packed_tile(p, u, cr, tt, g.pf));
   const uint8_t* piece = rec + s_toff[tt];
   const uint32_t nw = reinterpret_cast<const uint32_t*>(rec + g.tb)[tt];
   const uint32_t* raws = reinterpret_cast<const uint32_t*>(piece + 4 * LANES + 2 * (int64_t)nw + ((nw & 1) ? 2 : 0));
-  // 1-bit components: the raw row is the packed row
-  if (valid) {
-    for (int q = 0; q < g.n1; ++q) {
-      const int i = g.raw1[q];
-      const uint32_t* src = raws + g.raoff[last][i];
-      uint32_t* dst = tbase + g.roff[last][i];
-      for (int w = j; w < ((m + 31) >> 5); w += LANES) dst[w] = src[w];
+  // the record (raw rows) and its packed tiles (the rows this kernel
+  // writes) through buffer resources, so that lanes past a row load zeros and
+  // drop their stores without a branch
+  const __amdgpu_buffer_rsrc_t rrsrc = uniform_rsrc(const_cast<uint8_t*>(rec), (int32_t)size);
+  const int32_t raws_at = (int32_t)(reinterpret_cast<const uint8_t*>(raws) - rec);
+  const int32_t prec_bytes = (int32_t)((int64_t)p.blks_per_rec * p.w.packed_slot);
+  const __amdgpu_buffer_rsrc_t prsrc = uniform_rsrc(packed_tile(p, u, cr, 0, g.pf), prec_bytes);
+  const int32_t tile_at = (int32_t)((int64_t)(tt / p.tiles_per_blk) * p.w.packed_slot + (int64_t)(tt % p.tiles_per_blk) * g.pf);
+  // 1-bit components: the raw row is the packed row; eight words per lane
+  // in flight at a time
+  if (valid && g.n1 > 0) {
+    const int W1 = (m + 31) >> 5;
+    const int n1w = g.n1 * W1;
+    for (int q0 = 0; q0 < n1w; q0 += 8 * LANES) {
+      uint32_t v[8];
+      int32_t dat[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int e = q0 + q * LANES + j;
+        const int c1 = e / W1, w = e - c1 * W1;
+        const int i = e < n1w ? g.raw1[c1] : 0;
+        v[q] = __builtin_amdgcn_raw_buffer_load_b32(rrsrc, e < n1w ? raws_at + 4 * ((int32_t)g.raoff[last][i] + w) : (int32_t)size, 0, 0);
+        dat[q] = e < n1w ? tile_at + 4 * ((int32_t)g.roff[last][i] + w) : prec_bytes;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) __builtin_amdgcn_raw_buffer_store_b32(v[q], prsrc, dat[q], 0, 0);
     }
   }
-  if (wave * SPW >= ntiles) return;  // no stream in this wave (no barrier follows)
   // -- streams
   const uint64_t gm = ((1ull << LANES) - 1ull) << (grp * LANES);
   const uint32_t gm_lo = (uint32_t)gm, gm_hi = (uint32_t)(gm >> 32);
@@ -915,124 +988,146 @@ __global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) steps_max = max(steps_max, __shfl_xor(steps_max, o, 64));
   steps_max = STEPS > 0 ? STEPS : __builtin_amdgcn_readfirstlane(steps_max);
+  // every step of both of the wave's streams codes a token (full tiles):
+  // the step loop then carries no activity masks
+  const bool wave_full = STEPS > 0 && __all(valid && m == STEPS * LANES);
   uint32_t* ob = &outbuf[tt][0];
   uint32_t* rbb = &rawbuf[tt][0][0];
   if (valid)
     for (int w = j; w < kRowWords; w += LANES) ob[w] = 0u;
-  // the record (raw rows) and its packed tiles (the rows this kernel
-  // writes) through buffer resources, so that lanes past a row load zeros and
-  // drop their stores without a branch
-  const __amdgpu_buffer_rsrc_t rrsrc = uniform_rsrc(const_cast<uint8_t*>(rec), (int32_t)size);
-  const int32_t raws_at = (int32_t)(reinterpret_cast<const uint8_t*>(raws) - rec);
-  const int32_t prec_bytes = (int32_t)((int64_t)p.blks_per_rec * p.w.packed_slot);
-  const __amdgpu_buffer_rsrc_t prsrc = uniform_rsrc(packed_tile(p, u, cr, 0, g.pf), prec_bytes);
-  const int32_t tile_at = (int32_t)((int64_t)(tt / p.tiles_per_blk) * p.w.packed_slot + (int64_t)(tt % p.tiles_per_blk) * g.pf);
-  // the raw row of component i of this tile: registers, then LDS
-  uint32_t rpre[NR];
-  auto raw_load = [&](int i) {
+  // the raw row of component i of this tile: registers, then LDS.  Two
+  // register sets alternate between even and odd components, so a row is
+  // loaded two components before its use and the load's latency hides
+  // behind a whole component.
+  uint32_t rpre0[NR], rpre1[NR];
+  auto raw_load = [&](uint32_t(&rp)[NR], int i) {
     const uint32_t rr = (uint32_t)raw_bits_of((int)g.b[i]);
     const int Wr = rr ? (m * (int)rr + 31) >> 5 : 0;
     const int32_t at = raws_at + 4 * (int32_t)g.raoff[last][i];
 #pragma unroll
     for (int q = 0; q < NR; ++q) {
       const int w = j + q * LANES;
-      rpre[q] = __builtin_amdgcn_raw_buffer_load_b32(rrsrc, (valid && w < Wr) ? at + 4 * w : (int32_t)size, 0, 0);
+      rp[q] = __builtin_amdgcn_raw_buffer_load_b32(rrsrc, (valid && w < Wr) ? at + 4 * w : (int32_t)size, 0, 0);
     }
   };
-  auto raw_store = [&](int which) {
+  auto raw_store = [&](const uint32_t(&rp)[NR], int which) {
 #pragma unroll
     for (int q = 0; q < NR; ++q) {
       const int w = j + q * LANES;
-      if (valid && w < kRawWords) rbb[which * kRawWords + w] = rpre[q];
+      if (valid && w < kRawWords) rbb[which * kRawWords + w] = rp[q];
     }
   };
-  if (nc > 0) {
-    raw_load(g.coded[0]);
-    raw_store(0);
+  if (has_stream) {
+    if (nc > 0) raw_load(rpre0, g.coded[0]);
+    if (nc > 1) raw_load(rpre1, g.coded[1]);
   }
-  for (int ci = 0; ci < nc; ++ci) {
-    const int i = g.coded[ci];
-    const uint32_t b = g.b[i], rr = b - (uint32_t)sym_bits_of((int)b);
-    const uint32_t rmask = (1u << rr) - 1u;
-    if (ci + 1 < nc) raw_load(g.coded[ci + 1]);
-    // A component takes at most tile_tokens <= kUnit words, so one refill test
-    // per component keeps the ring ahead: after a refill at least kUnit
-    // committed words remain unread.
-    if (valid && clo > 0 && ptr - clo <= kUnit) {
-      // the ring slots of [plo, clo) held words >= clo + kUnit >= ptr: consumed
+  __syncthreads();  // slot table 0 and the rings are complete
+  const uint32_t sb = (uint32_t)p.sb;
+  // one component of both streams: STEPS (or steps_max) steps, the codes
+  // OR-ed into the LDS row buffer at bit (k b) of token k = s LANES + j
+  auto decode_component = [&](auto full_tag, auto straddle_tag, const uint32_t* tab, uint32_t b, uint32_t rr,
+                              const uint32_t* rw) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    constexpr bool STRADDLES = decltype(straddle_tag)::value;  // widths 3, 5, 6, 7: a code may cross a word
+    // bit position of token k = s LANES + j: j b + s LANES b; with 32 lanes a
+    // step is b whole words, so the shift is the same at every step
+    const uint32_t jb = (uint32_t)j * b, jr = (uint32_t)j * rr;
+    const uint32_t sh0 = jb & 31u;
+    // the raw low bits of every step do not depend on the state: read first
+    constexpr int NS = STEPS > 0 ? STEPS : 16;
+    uint32_t rlow[NS];
+    {
+      const uint32_t rmask = (1u << rr) - 1u;
 #pragma unroll
-      for (int q2 = 0; q2 < PER; ++q2) {
-        const int32_t q = plo / 2 + j + LANES * q2;
-        if (q < clo / 2) ring32[q & (kRing / 2 - 1)] = pend[q2];
-      }
-      clo = plo;
-      plo = max(0, clo - kUnit);
-#pragma unroll
-      for (int q2 = 0; q2 < PER; ++q2) {
-        const int32_t q = plo / 2 + j + LANES * q2;
-        pend[q2] = q < clo / 2 ? wd[q] : 0u;
+      for (int s = 0; s < NS; ++s) {
+        if (s >= (STEPS > 0 ? STEPS : steps_max)) break;
+        const uint32_t bq = jr + (uint32_t)(s * LANES) * rr;
+        rlow[s] = rr ? (funnel(rw[bq >> 5], rw[(bq >> 5) + 1], bq & 31u) & rmask) : 0u;
       }
     }
-    __builtin_amdgcn_wave_barrier();
-    const uint32_t* rw = rbb + (ci & 1) * kRawWords;
-    const uint32_t* cm = cumt + ci * 17;
-    const uint8_t* bkt = bucket + ci * 256;
-    const uint32_t jb = (uint32_t)j * b, jr = (uint32_t)j * rr;
-    const uint32_t sb_step = (uint32_t)LANES * b, sr_step = (uint32_t)LANES * rr;
-    const bool straddles = (b & (b - 1)) != 0;  // widths 3, 5, 6, 7: a code may cross a word
 #pragma unroll
-    for (int s = 0; s < (STEPS > 0 ? STEPS : steps_max); ++s) {
-      const int k = s * LANES + j;
-      const bool active = valid && k < m;
-      const uint32_t slot = x & (M - 1u);
-      // the symbol whose cumulative range holds the slot: the bucket's first
-      // symbol, moved past any range that ends inside the bucket (rare: it
-      // takes a frequency below 16); cm[16] = M ends the walk
-      uint32_t sy = bkt[slot >> 4];
-      uint32_t c0 = cm[sy], c1 = cm[sy + 1];
-      while (c1 <= slot) {
-        ++sy;
-        c0 = c1;
-        c1 = cm[sy + 1];
-      }
-      const uint32_t xn = (c1 - c0) * (x >> p.sb) + slot - c0;
+    for (int s = 0; s < NS; ++s) {
+      if (s >= (STEPS > 0 ? STEPS : steps_max)) break;
+      const bool active = FULL || (valid && s * LANES + j < m);
+      const uint32_t e = tab[x & (M - 1u)];
+      const uint32_t xn = __umul24(e >> 16, x >> sb) + (e & 0xfffu);
       x = active ? xn : x;
       const bool need = active && x < kRansL;
-      const uint64_t bl = __ballot(need);
+      const uint64_t bl = __builtin_amdgcn_ballot_w64(need);
       const uint32_t mlo = (uint32_t)bl & gm_lo, mhi = (uint32_t)(bl >> 32) & gm_hi;
       const uint32_t rank = __builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
       const uint32_t wnext = ring[(uint32_t)(ptr - 1 - (int32_t)rank) & (kRing - 1)];
       x = need ? ((x << 16) | wnext) : x;
       ptr -= (int32_t)(__popc(mlo) + __popc(mhi));
-      // the code into the component's packed row (inactive lanes OR zero)
-      uint32_t code = sy << rr;
-      if (rr) {
-        const uint32_t bq = active ? jr + (uint32_t)s * sr_step : 0u;
-        code |= funnel(rw[bq >> 5], rw[(bq >> 5) + 1], bq & 31) & rmask;
-      }
-      code = active ? code : 0u;
-      const uint32_t bp = active ? jb + (uint32_t)s * sb_step : 0u;
-      const uint32_t sh = bp & 31;
-      atomicOr(&ob[bp >> 5], code << sh);
-      if (straddles) atomicOr(&ob[(bp >> 5) + 1], (uint32_t)(((uint64_t)code << sh) >> 32));
+      uint32_t code = (((e >> 12) & 15u) << rr) | rlow[s];
+      if (!FULL) code = active ? code : 0u;
+      const uint32_t bp = jb + (uint32_t)(s * LANES) * b;
+      const uint32_t sh = LANES == 32 ? sh0 : (bp & 31u);
+      uint32_t* ow = LANES == 32 ? ob + (jb >> 5) + s * b : ob + (bp >> 5);
+      const uint64_t c64 = (uint64_t)code << sh;  // the high word holds what crosses into the next word
+      atomicOr(ow, (uint32_t)c64);
+      if (STRADDLES) atomicOr(ow + 1, (uint32_t)(c64 >> 32));
     }
-    // the next component's raw row goes to LDS first (its loads were issued
-    // before this component's row stores, so the wait does not cover them);
-    // then the component's packed row is flushed and the buffer cleared
-    if (ci + 1 < nc) raw_store((ci + 1) & 1);
-    __builtin_amdgcn_wave_barrier();
-    const int W = (m * (int)b + 31) >> 5;
-    const int32_t at = tile_at + 4 * (int32_t)g.roff[last][i];
+  };
+  auto component = [&](int ci, uint32_t(&rp)[NR]) {
+    if (ci + 1 < nc && builds) build_slot_table(cumt + (ci + 1) * 17, M, stab + ((ci + 1) & 1) * M, btid, bthreads);
+    if (has_stream) {
+      const int i = g.coded[ci];
+      const uint32_t b = __builtin_amdgcn_readfirstlane((uint32_t)g.b[i]);
+      const uint32_t rr = b - (uint32_t)sym_bits_of((int)b);
+      // this component's raw row to LDS (its buffer was last read two
+      // components ago), then the row of ci + 2 into the same registers
+      raw_store(rp, ci & 1);
+      if (ci + 2 < nc) raw_load(rp, g.coded[ci + 2]);
+      // A component takes at most tile_tokens <= kUnit words, so one refill test
+      // per component keeps the ring ahead: after a refill at least kUnit
+      // committed words remain unread.
+      if (valid && clo > 0 && ptr - clo <= kUnit) {
+        // the ring slots of [plo, clo) held words >= clo + kUnit >= ptr: consumed
 #pragma unroll
-    for (int q = 0; q < (kRowWords + LANES - 1) / LANES; ++q) {
-      const int w = j + q * LANES;
-      const uint32_t v = w < kRowWords ? ob[w] : 0u;
-      __builtin_amdgcn_raw_buffer_store_b32(v, prsrc, (valid && w < W) ? at + 4 * w : prec_bytes, 0, 0);
-      if (valid && w < kRowWords) ob[w] = 0u;
+        for (int q2 = 0; q2 < PER; ++q2) {
+          const int32_t q = plo / 2 + j + LANES * q2;
+          if (q < clo / 2) ring32[q & (kRing / 2 - 1)] = pend[q2];
+        }
+        clo = plo;
+        plo = max(0, clo - kUnit);
+#pragma unroll
+        for (int q2 = 0; q2 < PER; ++q2) {
+          const int32_t q = plo / 2 + j + LANES * q2;
+          pend[q2] = q < clo / 2 ? wd[q] : 0u;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      const uint32_t* tab = stab + (ci & 1) * M;
+      const uint32_t* rw = rbb + (ci & 1) * kRawWords;
+      const bool straddles = (b & (b - 1u)) != 0u;
+      if (wave_full) {
+        if (straddles) decode_component(BoolTag<true>{}, BoolTag<true>{}, tab, b, rr, rw);
+        else decode_component(BoolTag<true>{}, BoolTag<false>{}, tab, b, rr, rw);
+      } else {
+        if (straddles) decode_component(BoolTag<false>{}, BoolTag<true>{}, tab, b, rr, rw);
+        else decode_component(BoolTag<false>{}, BoolTag<false>{}, tab, b, rr, rw);
+      }
+      // the component's packed row is flushed and the buffer cleared
+      __builtin_amdgcn_wave_barrier();
+      const int W = (m * (int)b + 31) >> 5;
+      const int32_t at = tile_at + 4 * (int32_t)g.roff[last][i];
+#pragma unroll
+      for (int q = 0; q < (kRowWords + LANES - 1) / LANES; ++q) {
+        const int w = j + q * LANES;
+        const uint32_t v = w < kRowWords ? ob[w] : 0u;
+        __builtin_amdgcn_raw_buffer_store_b32(v, prsrc, (valid && w < W) ? at + 4 * w : prec_bytes, 0, 0);
+        if (valid && w < kRowWords) ob[w] = 0u;
+      }
     }
+    __syncthreads();  // table ci + 1 is complete; table ci may be rebuilt
+  };
+  for (int ci = 0; ci < nc; ci += 2) {
+    component(ci, rpre0);
+    if (ci + 1 < nc) component(ci + 1, rpre1);
   }
   const bool ok = !(bad0 || (valid && (x != kRansL || ptr != 0)));
-  if (__ballot(!ok)) {
+  if (has_stream && __ballot(!ok)) {
     if (lane == 0) set_status(p.ws, p.w, KVTC_ERR_CORRUPT);
   }
 }
@@ -1040,7 +1135,10 @@ __global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw
 hipError_t launch_rans_decode_chunks(const Params& p, hipStream_t s, bool with_raw) {
   int waves = (p.tiles_per_rec * p.lanes + 63) / 64;
   if (waves < 1) waves = 1;
-  const size_t lds = (size_t)p.tiles_per_rec * kRing * 2;  // one word ring per tile
+  // plus table-building waves, half as many as the streams' (within 16)
+  waves += std::min(std::max(waves / 2, 1), 16 - waves);
+  // one word ring per tile, then two slot tables
+  const size_t lds = (size_t)p.tiles_per_rec * kRing * 2 + 2 * ((size_t)4 << p.sb);
   const int raw_runs = with_raw && p.n_seqs == 0 ? 4 * p.L * p.H : 0;
   const dim3 grid(p.n_recs + raw_runs, 1, seq_grid(p)), block(64 * waves);
   const int steps = p.tile_tokens / p.lanes;
