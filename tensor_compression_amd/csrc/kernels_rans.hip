@@ -207,6 +207,7 @@ __device__ __forceinline__ uint32_t funnel(uint32_t lo, uint32_t hi, uint32_t sh
 
 // ---- record encoder ---------------------------------------------------------
 
+constexpr int kHistCopies = 4;  // histogram copies per component in the record encoder
 constexpr int kRowWords = 66;  // a staged component row of a 256-token tile (<= 64 words), zero-padded
 constexpr int kRawWords = 34;  // a raw row of a 256-token tile (<= 32 words), zero-padded
 
@@ -232,13 +233,17 @@ __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (get_status(p.ws, p.w) & (1u << KVTC_ERR_NONFINITE)) return;
   __shared__ RecGeo g;
-  __shared__ uint32_t hist[kMaxD * 17];
-  __shared__ EncSym tab[kMaxD * 16];
+  // histograms (kHistCopies per component, picked by lane, so that fewer
+  // lanes add to one bin at once), later the encoder tables in the same LDS
+  __shared__ __align__(16) uint32_t histtab[kMaxD * kHistCopies * 17];
+  static_assert(sizeof(histtab) >= kMaxD * 16 * sizeof(EncSym), "tables fit in the histogram space");
+  uint32_t* const hist = histtab;
+  EncSym* const tab = reinterpret_cast<EncSym*>(histtab);
   __shared__ uint32_t rowbuf[kMaxTilesPerRec][2][kRowWords];
   __shared__ uint32_t rawrow[kMaxTilesPerRec][kRawWords];  // a component's raw row being assembled
   __shared__ int32_t s_nw[kMaxTilesPerRec];
   if (wave == 0) rec_setup(p, cr, p.ws + p.w.side_bits + (int64_t)u * p.D, g);
-  for (int i = tid; i < kMaxD * 17; i += blockDim.x) hist[i] = 0;
+  for (int i = tid; i < kMaxD * kHistCopies * 17; i += blockDim.x) hist[i] = 0;
   __syncthreads();
   uint32_t* rec_size = reinterpret_cast<uint32_t*>(p.ws + p.w.rec_size);
   uint32_t* rec_mode = reinterpret_cast<uint32_t*>(p.ws + p.w.rec_mode);
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw
       if (ci + 2 < nc) row_load(pr, g.coded[ci + 2]);
       __builtin_amdgcn_wave_barrier();
       const uint32_t* rw = rb + (ci & 1) * kRowWords;
-      uint32_t* hc = hist + ci * 17;
+      uint32_t* hc = hist + (ci * kHistCopies + (lane & (kHistCopies - 1))) * 17;
 #pragma unroll
       for (int s = 0; s < (STEPS > 0 ? STEPS : steps_max); ++s) {
         const int k = s * LANES + j;
@@ -318,22 +323,39 @@ __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw
     }
   }
   __syncthreads();
-  // -- tables: one thread per coded component
+  // -- tables: the histogram copies summed into the first, then one thread
+  // per coded component normalises its counts into the record's table; the
+  // encoder tables overwrite the histograms once every count has been read
+  for (int idx = tid; idx < nc * 16; idx += blockDim.x) {
+    uint32_t* hc = hist + (idx >> 4) * kHistCopies * 17 + (idx & 15);
+    uint32_t sum = 0;
+#pragma unroll
+    for (int c = 0; c < kHistCopies; ++c) sum += hc[c * 17];
+    hc[0] = sum;
+  }
+  __syncthreads();
   for (int ci = tid; ci < nc; ci += blockDim.x) {
     const int i = g.coded[ci];
     const int A = 1 << sym_bits_of((int)g.b[i]);
     uint32_t f[16];
-    normalize_small(hist + ci * 17, A, p.sb, f);
+    normalize_small(hist + ci * kHistCopies * 17, A, p.sb, f);
     uint16_t* ft = reinterpret_cast<uint16_t*>(slot) + g.toff[i];
+    for (int s = 0; s < A; ++s) ft[s] = (uint16_t)f[s];
+  }
+  __syncthreads();
+  for (int ci = tid; ci < nc; ci += blockDim.x) {
+    const int i = g.coded[ci];
+    const int A = 1 << sym_bits_of((int)g.b[i]);
+    const uint16_t* ft = reinterpret_cast<const uint16_t*>(slot) + g.toff[i];
     uint32_t cum = 0;
     for (int s = 0; s < A; ++s) {
-      ft[s] = (uint16_t)f[s];
+      const uint32_t fs = ft[s];
       EncSym e;
-      e.f = f[s];
+      e.f = fs;
       e.cum = cum;
-      e.rcp = f[s] ? __ddiv_rn(1.0, (double)f[s]) : 0.0;
+      e.rcp = fs ? __ddiv_rn(1.0, (double)fs) : 0.0;
       tab[ci * 16 + s] = e;
-      cum += f[s];
+      cum += fs;
     }
   }
   if (tid == 0 && g.tu < g.tb) *reinterpret_cast<uint16_t*>(slot + g.tu) = 0;  // padding to 4 bytes
