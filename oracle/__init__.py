@@ -52,7 +52,7 @@ class _Cfg(ctypes.Structure):
         ("rope_theta", ctypes.c_double), ("rans_scale_bits", ctypes.c_int32),
         ("rans_lanes", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
         ("tile_tokens", ctypes.c_int32), ("basis_per_head", ctypes.c_int32),
-        ("wht_keys", ctypes.c_int32),
+        ("wht_keys", ctypes.c_int32), ("alloc_scope", ctypes.c_int32),
     ]
 
 
@@ -91,6 +91,7 @@ def lib() -> ctypes.CDLL:
             "orc_stats": (None, [P, i64, i32, P, P, P, P]),
             "orc_budget": (i32, [f32, i32]),
             "orc_alloc_greedy": (None, [P, i32, i32, i32, P]),
+            "orc_alloc_greedy_heap": (None, [P, ctypes.c_int64, ctypes.c_int64, i32, P]),
             "orc_alloc_dp": (f64, [P, i32, i32, i32, P]),
             "orc_distortion": (f64, [P, P, i32]),
             "orc_side_info": (None, [P, P, P, P, i32, P, P, P]),
@@ -145,7 +146,7 @@ def make_cfg(cfg: dict) -> _Cfg:
     """Fill the oracle's config struct from a plain dict of its field names."""
     c = _Cfg()
     for f in CONFIG_FIELDS:
-        setattr(c, f, cfg[f])
+        setattr(c, f, cfg.get(f, 0) if f == "alloc_scope" else cfg[f])
     return c
 
 
@@ -249,6 +250,15 @@ def alloc_greedy(var: np.ndarray, budget_: int, max_bits: int) -> np.ndarray:
     var = np.ascontiguousarray(var, np.float32)
     bits = np.zeros(var.shape[0], np.uint8)
     lib().orc_alloc_greedy(_p(var), var.shape[0], budget_, max_bits, _p(bits))
+    return bits
+
+
+def alloc_greedy_heap(var: np.ndarray, budget_: int, max_bits: int) -> np.ndarray:
+    """Greedy allocation over any number of components (all sections of a
+    cache under one budget), heap-ordered; equal to alloc_greedy."""
+    var = np.ascontiguousarray(var, np.float32).reshape(-1)
+    bits = np.zeros(var.shape[0], np.uint8)
+    lib().orc_alloc_greedy_heap(_p(var), var.shape[0], int(budget_), max_bits, _p(bits))
     return bits
 
 

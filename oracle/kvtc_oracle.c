@@ -227,6 +227,57 @@ void orc_alloc_greedy(const float* var, int32_t D, int32_t budget, int32_t max_b
   }
 }
 
+/* The same greedy allocation over n components of any number of sections
+ * (one budget over all of them, "Bit Budget Is Not Fair": the budget moves
+ * toward the hard parts), with a binary max-heap holding each candidate's
+ * next marginal gain var * 4^-b (exact in fp64); ties go to the lowest index
+ * as in orc_alloc_greedy, which it equals on every input. */
+static int gain_before(const double* g, const int64_t* id, int64_t a, int64_t b) {
+  return g[a] > g[b] || (g[a] == g[b] && id[a] < id[b]);
+}
+
+static void gain_sift_down(double* g, int64_t* id, int64_t m, int64_t at) {
+  for (;;) {
+    int64_t l = 2 * at + 1, r = l + 1, top = at;
+    if (l < m && gain_before(g, id, l, top)) top = l;
+    if (r < m && gain_before(g, id, r, top)) top = r;
+    if (top == at) return;
+    double tg = g[at]; g[at] = g[top]; g[top] = tg;
+    int64_t ti = id[at]; id[at] = id[top]; id[top] = ti;
+    at = top;
+  }
+}
+
+void orc_alloc_greedy_heap(const float* var, int64_t n, int64_t budget, int32_t max_bits,
+                           uint8_t* bits) {
+  double* g = (double*)malloc(sizeof(double) * (size_t)(n + 1));
+  int64_t* id = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n + 1));
+  int64_t m = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    bits[i] = 0;
+    if (max_bits > 0 && var[i] > 0.0f) {
+      g[m] = (double)var[i];
+      id[m] = i;
+      ++m;
+    }
+  }
+  for (int64_t at = m / 2 - 1; at >= 0; --at) gain_sift_down(g, id, m, at);
+  for (int64_t step = 0; step < budget && m > 0; ++step) {
+    int64_t i = id[0];
+    bits[i] += 1;
+    if (bits[i] >= max_bits) { /* no further gain: drop the candidate */
+      --m;
+      g[0] = g[m];
+      id[0] = id[m];
+    } else {
+      g[0] = ldexp((double)var[i], -2 * (int)bits[i]);
+    }
+    gain_sift_down(g, id, m, 0);
+  }
+  free(g);
+  free(id);
+}
+
 double orc_distortion(const float* var, const uint8_t* bits, int32_t D) {
   double d = 0.0;
   for (int32_t i = 0; i < D; ++i) d += ldexp((double)var[i], -2 * (int)bits[i]);
@@ -848,6 +899,8 @@ int orc_check_config(const orc_config* c) {
   if (c->rope_keys && !(c->rope_theta > 1.0)) return ORC_ERR_INVALID_ARG;
   if (c->rans_scale_bits < 8 || c->rans_scale_bits > 15) return ORC_ERR_INVALID_ARG;
   if (c->rans_lanes < 1 || c->rans_lanes > 64) return ORC_ERR_INVALID_ARG;
+  if (c->alloc_scope != 0 && c->alloc_scope != 1) return ORC_ERR_INVALID_ARG;
+  if (c->alloc_scope == 1 && c->transform != ORC_PCA) return ORC_ERR_INVALID_ARG;
   if (c->tile_tokens < 1 || c->chunk_tokens < c->tile_tokens) return ORC_ERR_INVALID_ARG;
   if (c->chunk_tokens % c->tile_tokens) return ORC_ERR_INVALID_ARG;
   return ORC_OK;
@@ -891,6 +944,16 @@ static void make_layout(const orc_config* c, int32_t T, layout_t* lo) {
     lo->budget_k = uniform_bits(c->bits_k) * c->head_dim;
     lo->budget_v = uniform_bits(c->bits_v) * c->head_dim;
   }
+}
+
+/* The largest width sum one section of kind s (0 keys, 1 values) can have:
+ * its own budget, or with one budget over all sections every component at
+ * max_bits (within the total). */
+static int32_t sec_bits_max(const orc_config* c, const layout_t* lo, int32_t s) {
+  if (c->alloc_scope == 0) return s == 0 ? lo->budget_k : lo->budget_v;
+  int64_t total = (int64_t)c->layers * c->kv_heads * ((int64_t)lo->budget_k + lo->budget_v);
+  int64_t cap = (int64_t)c->head_dim * c->max_bits;
+  return (int32_t)(total < cap ? total : cap);
 }
 
 /* r-area index of section u, or -1 */
@@ -966,7 +1029,7 @@ int64_t orc_max_container_bytes(const orc_config* c, int32_t T) {
   int64_t total = lo.chunks_off;
   for (int32_t u = 0; u < lo.n_sections; ++u) {
     int32_t s = (u / c->kv_heads) % 2;
-    int32_t budget = s == 0 ? lo.budget_k : lo.budget_v;
+    int32_t budget = sec_bits_max(c, &lo, s);
     for (int32_t ch = 0; ch < lo.chunks_per_sec; ++ch) {
       int32_t n = lo.T_mid - ch * c->chunk_tokens;
       if (n > c->chunk_tokens) n = c->chunk_tokens;
@@ -1078,6 +1141,7 @@ static void write_header(const orc_config* c, const layout_t* lo, uint64_t fp,
   put64(out + 176, fp);
   put32(out + 184, (uint32_t)lo->budget_k);
   put32(out + 188, (uint32_t)lo->budget_v);
+  put32(out + 192, (uint32_t)c->alloc_scope);
 }
 
 /* Copy the sink and recent windows bit-exactly ([KVTC] "How the Pipeline
@@ -1113,13 +1177,16 @@ typedef struct {
 
 /* Allocation and side information of one section from its coefficients. */
 static void section_side(const orc_config* c, const layout_t* lo, int32_t u,
-                         const float* coef, side_t* si) {
+                         const float* coef, const uint8_t* bits_given, side_t* si) {
   int32_t D = c->head_dim, s = (u / c->kv_heads) % 2;
   int32_t N = lo->T_mid;
   float mu[256], var[256], mn[256], mx[256];
   orc_stats(coef, N, D, mu, var, mn, mx);
   if (c->transform == ORC_PCA) {
-    orc_alloc_greedy(var, D, s == 0 ? lo->budget_k : lo->budget_v, c->max_bits, si->bits);
+    if (bits_given)
+      memcpy(si->bits, bits_given, (size_t)D);
+    else
+      orc_alloc_greedy(var, D, s == 0 ? lo->budget_k : lo->budget_v, c->max_bits, si->bits);
     orc_side_info(si->bits, mu, mn, mx, D, si->zero, si->scale, si->rcp);
     return;
   }
@@ -1226,12 +1293,30 @@ int orc_encode(const orc_config* c, const void* k, const void* v, int32_t T,
   uint8_t* q = (uint8_t*)malloc((size_t)c->chunk_tokens * D + 1);
   int64_t pos = lo.chunks_off;
   side_t si;
+  /* one budget over all sections: the variances of every section first,
+   * then the greedy allocation over all of their components at once */
+  uint8_t* bits_all = NULL;
+  if (c->alloc_scope == 1 && lo.T_mid > 0) {
+    float* var_all = (float*)malloc(sizeof(float) * (size_t)lo.n_sections * D);
+    bits_all = (uint8_t*)malloc((size_t)lo.n_sections * D);
+    int64_t budget = 0;
+    for (int32_t u = 0; u < lo.n_sections && st == ORC_OK; ++u) {
+      st = gather_section(c, k, v, &lo, u, cos_t, sin_t, x);
+      if (st != ORC_OK) break;
+      transform_section(c, basis, u, lo.T_mid, x, coef, r);
+      float mu[256], mn[256], mx[256];
+      orc_stats(coef, lo.T_mid, D, mu, var_all + (int64_t)u * D, mn, mx);
+      budget += ((u / H) % 2) == 0 ? lo.budget_k : lo.budget_v;
+    }
+    if (st == ORC_OK) orc_alloc_greedy_heap(var_all, (int64_t)lo.n_sections * D, budget, c->max_bits, bits_all);
+    free(var_all);
+  }
   for (int32_t u = 0; u < lo.n_sections && st == ORC_OK; ++u) {
     st = gather_section(c, k, v, &lo, u, cos_t, sin_t, x);
     if (st != ORC_OK) break;
     if (lo.T_mid == 0) continue;
     transform_section(c, basis, u, lo.T_mid, x, coef, r);
-    section_side(c, &lo, u, coef, &si);
+    section_side(c, &lo, u, coef, bits_all ? bits_all + (int64_t)u * D : NULL, &si);
     /* section record */
     uint8_t* rec = out + lo.side_off + (int64_t)u * SEC_REC(D);
     memcpy(rec, si.bits, (size_t)D);
@@ -1263,6 +1348,7 @@ int orc_encode(const orc_config* c, const void* k, const void* v, int32_t T,
   }
   free(x); free(coef); free(r); free(q);
   free(cos_t); free(sin_t);
+  free(bits_all);
   return st;
 }
 
@@ -1294,6 +1380,7 @@ static int parse_header(const orc_config* c, const float* basis, const uint8_t* 
   h.tile_tokens = (int32_t)get32(in + 84);
   h.basis_per_head = (int32_t)get32(in + 88);
   h.wht_keys = (int32_t)get32(in + 92);
+  h.alloc_scope = (int32_t)get32(in + 192);
   if (h.layers != c->layers || h.kv_heads != c->kv_heads || h.head_dim != c->head_dim ||
       h.dtype != c->dtype || h.transform != c->transform || h.sink_tokens != c->sink_tokens ||
       h.recent_tokens != c->recent_tokens || memcmp(&h.bits_k, &c->bits_k, 4) ||
@@ -1302,7 +1389,7 @@ static int parse_header(const orc_config* c, const float* basis, const uint8_t* 
       memcmp(&h.rope_theta, &c->rope_theta, 8) || h.rans_scale_bits != c->rans_scale_bits ||
       h.rans_lanes != c->rans_lanes || h.chunk_tokens != c->chunk_tokens ||
       h.tile_tokens != c->tile_tokens || h.basis_per_head != c->basis_per_head ||
-      h.wht_keys != c->wht_keys)
+      h.wht_keys != c->wht_keys || h.alloc_scope != c->alloc_scope)
     return ORC_ERR_CORRUPT;
   int32_t T = (int32_t)get32(in + 96);
   if (T < 0) return ORC_ERR_CORRUPT;

@@ -67,6 +67,7 @@ typedef struct {
   int32_t tile_tokens;    /* tokens per packed tile = one rANS stream */
   int32_t basis_per_head; /* 0: basis [L,2,D,D]; 1: [L,2,H,D,D] */
   int32_t wht_keys;       /* WHT path: 1 = keys get RMS+WHT too */
+  int32_t alloc_scope;    /* PCA path: 0 = one budget per section; 1 = one budget over all sections */
 } orc_config;
 
 /* ---- numeric primitives ---------------------------------------------- */
@@ -90,6 +91,8 @@ void orc_alloc_greedy(const float* var, int32_t D, int32_t budget, int32_t max_b
                       uint8_t* bits);
 double orc_alloc_dp(const float* var, int32_t D, int32_t budget, int32_t max_bits,
                     uint8_t* bits);
+void orc_alloc_greedy_heap(const float* var, int64_t n, int64_t budget, int32_t max_bits,
+                           uint8_t* bits);
 double orc_distortion(const float* var, const uint8_t* bits, int32_t D);
 void orc_side_info(const uint8_t* bits, const float* mu, const float* cmin,
                    const float* cmax, int32_t D, float* zero, float* scale, float* rcp);
