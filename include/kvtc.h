@@ -101,6 +101,16 @@ enum { KVTC_ROPE_HALF = 0, KVTC_ROPE_INTERLEAVED = 1 };
  *                   0 = keys are quantised directly
  *  max_tokens       largest T any call on the plan may use (sizes the RoPE
  *                   table)
+ *  alloc_scope      PCA path: 0 = each section spends its own budget
+ *                   (floor(bits D) bits per token); 1 = one budget, the
+ *                   sum of those, over all sections of the cache (of each
+ *                   sequence of a paged batch), spent by the same greedy
+ *                   marginal rule over every component at once, lowest
+ *                   (section, component) first on ties ("KVTC: The
+ *                   Open-Source KV Cache Codec That Treats LLM Memory Like
+ *                   Media", Bit Budget Is Not Fair, and That Is the Point:
+ *                   the budget moves toward the sections that need it).
+ *                   Needs n_sections * head_dim <= 2^20.
  */
 typedef struct kvtc_config {
   int32_t layers, kv_heads, head_dim;
@@ -119,6 +129,7 @@ typedef struct kvtc_config {
   int32_t basis_per_head;
   int32_t wht_keys;
   int32_t max_tokens;
+  int32_t alloc_scope;
 } kvtc_config;
 
 typedef struct kvtc_plan_s* kvtc_plan_t;

@@ -404,7 +404,7 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 
 // Words of the LDS tile buffer: the packed tile and four zero words past it.
 __host__ __device__ inline int dec_tile_words(const Params& p) {
-  const int32_t bmax = p.budget_k > p.budget_v ? p.budget_k : p.budget_v;
+  const int32_t bmax = p.sec_bits_max;
   return (int)(((int64_t)p.tile_tokens * bmax + 31) / 32) + 4;
 }
 
@@ -906,7 +906,7 @@ hipError_t launch_dec_transform(const Params& p, hipStream_t s) {
     return hipGetLastError();
   }
   const int ob = p.out_dtype == KVTC_BF16 ? 2 : 4;
-  const int32_t bmax = p.budget_k > p.budget_v ? p.budget_k : p.budget_v;
+  const int32_t bmax = p.sec_bits_max;
   const int32_t nz = bmax < p.D ? bmax : p.D;
   const size_t tile_words = (size_t)(((int64_t)p.tile_tokens * bmax + 31) / 32 + nz) + 4;
   if (p.D == 128 && p.dtype == KVTC_BF16 && p.tile_tokens % 64 == 0 &&

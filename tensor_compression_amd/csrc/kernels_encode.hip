@@ -1236,7 +1236,7 @@ static size_t quant_lds_bytes(const Params& p, size_t tile) {
 }
 
 static size_t tile_lds_bytes(const Params& p) {
-  int32_t bmax = p.budget_k > p.budget_v ? p.budget_k : p.budget_v;
+  int32_t bmax = p.sec_bits_max;
   if (p.transform == KVTC_WHT) {
     int32_t b = p.bits_k_uniform > p.bits_v_uniform ? p.bits_k_uniform : p.bits_v_uniform;
     return (size_t)((p.tile_tokens * b + 31) / 32) * p.D * 4;
@@ -1321,7 +1321,30 @@ __device__ __forceinline__ uint64_t alloc_key(float var, int k, int i) {
   return (((e2 << 23) | man) << 8) | (uint64_t)(255 - i);
 }
 
+// Ordering key of var * 4^-k for the one-budget allocation over all
+// sections: (extended exponent, significand, then the (section, component)
+// index reversed in 20 bits so that lower indices win ties), 53 bits.
+__device__ __forceinline__ void var_exp_man(float var, int32_t& ex, uint32_t& man) {
+  const uint32_t bits = __float_as_uint(var);
+  ex = (int32_t)(bits >> 23);
+  man = bits & 0x7fffffu;
+  if (ex == 0) {  // subnormal: normalise the significand
+    const int sh = __clz(man) - 8;
+    man = (man << sh) & 0x7fffffu;
+    ex = 1 - sh;
+  }
+}
+constexpr int kGKeyLow = 43;  // bits below the exponent field: 23 significand + 20 index
+__device__ __forceinline__ uint64_t global_key(int32_t ex, uint32_t man, int k, int64_t idx) {
+  const uint64_t e2 = (uint64_t)(ex - 2 * k + 256);  // in [220, 510]
+  return (e2 << kGKeyLow) | ((uint64_t)man << 20) | (uint64_t)(0xfffffu - (uint32_t)idx);
+}
+
 // One wave per section; lane l holds components l and l + 64 (head_dim 128).
+// MODE 0: statistics, the section's own greedy widths and side information.
+// MODE 1 (one budget over all sections): statistics only, for k_alloc_global.
+// MODE 2: statistics, widths from the global threshold key, side information.
+template <int MODE>
 __global__ __launch_bounds__(64) void k_enc_alloc(const Params p0) {
   const Params p = at_seq(p0, blockIdx.z);
   const int u = blockIdx.x;
@@ -1373,9 +1396,29 @@ __global__ __launch_bounds__(64) void k_enc_alloc(const Params p0) {
     }
   }
   if (__ballot(nonfinite) && lane == 0) set_status(p.ws, p.w, KVTC_ERR_NONFINITE);
+  if (MODE == 1) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      if (c < NC)
+        reinterpret_cast<float4*>(p.ws + p.w.sec_stats)[(int64_t)u * D + lane + 64 * c] =
+            make_float4(mu[c], var[c], mn[c], mx[c]);
+    return;
+  }
   // ---- bit widths ----
   uint32_t bits[2] = {0u, 0u};
-  if (p.transform == KVTC_PCA) {
+  if (MODE == 2) {
+    // every k whose key reaches the threshold (keys fall as k grows)
+    const uint64_t thr = *reinterpret_cast<const uint64_t*>(p.ws + p.w.status + kGlobalThrOff);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      if (c >= NC || !(var[c] > 0.0f)) continue;
+      int32_t ex;
+      uint32_t man;
+      var_exp_man(var[c], ex, man);
+      const int64_t idx = (int64_t)u * D + lane + 64 * c;
+      for (int k = 0; k < p.max_bits; ++k) bits[c] += global_key(ex, man, k, idx) >= thr ? 1u : 0u;
+    }
+  } else if (p.transform == KVTC_PCA) {
     const int budget = s == 0 ? p.budget_k : p.budget_v;
     // greedy marginal allocation == the `budget` largest var_i 4^-k (k < max_bits),
     // ranked by exact value then lowest index: find the budget-th largest key
@@ -1452,8 +1495,154 @@ __global__ __launch_bounds__(64) void k_enc_alloc(const Params p0) {
   }
 }
 
+// One budget over all sections of a cache (of each sequence of a batch): the
+// greedy marginal allocation over every component at once takes exactly the
+// total_budget largest keys var * 4^-k (k < max_bits), so the widths follow
+// from the total_budget-th largest key.  One workgroup finds that key by a
+// most-significant-digit-first radix selection: the exponent field from a
+// histogram of the variances' exponents (each variance contributes the
+// exponents e - 2k of its keys), then the 43 low bits in four digits over the
+// keys in the chosen exponent (at most one per component).
+constexpr int kGDigits = 4;
+__device__ __forceinline__ int gdigit_shift(int d) { return d < 3 ? 32 - 11 * d : 0; }
+__device__ __forceinline__ int gdigit_bits(int d) { return d < 3 ? 11 : 10; }
+
+__global__ __launch_bounds__(1024) void k_alloc_global(const Params p0) {
+  const Params p = at_seq(p0, blockIdx.z);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t n = (int64_t)p.n_sections * p.D;
+  const float4* st = reinterpret_cast<const float4*>(p.ws + p.w.sec_stats);
+  uint64_t* thr_out = reinterpret_cast<uint64_t*>(p.ws + p.w.status + kGlobalThrOff);
+  const int64_t B = p.T_mid > 0 ? p.total_budget : 0;
+  const int mb = p.max_bits;
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t wsum[16];
+  __shared__ int64_t s_total;
+  __shared__ int32_t s_sel;
+  __shared__ int64_t s_need;
+  // -- exponents of the variances (fp32 exponent + 32, subnormals included)
+  for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0u;
+  if (tid == 0) s_total = 0;
+  __syncthreads();
+  uint32_t cand = 0;
+  for (int64_t i = tid; i < n; i += blockDim.x) {
+    const float v = st[i].y;
+    if (!(v > 0.0f)) continue;
+    int32_t ex;
+    uint32_t man;
+    var_exp_man(v, ex, man);
+    atomicAdd(&hist[ex + 32], 1u);
+    cand += (uint32_t)mb;
+  }
+  for (int o = 32; o > 0; o >>= 1) cand += __shfl_xor(cand, o, 64);
+  if (lane == 0) atomicAdd((unsigned long long*)&s_total, (unsigned long long)cand);
+  __syncthreads();
+  if (B <= 0 || s_total <= B) {  // nothing to spend, or every candidate fits
+    if (tid == 0) *thr_out = B <= 0 ? ~0ull : 1ull;
+    return;
+  }
+  // -- the exponent field E = e - 2k + 256 of the B-th largest key: thread
+  // t evaluates count(E >= t) over the exponent histogram
+  {
+    const int t = tid;  // candidate E values 0 .. 1023
+    int64_t cnt = 0;
+    for (int e = 0; e < 320; ++e) {
+      const uint32_t h = hist[e];
+      if (!h) continue;
+      const int32_t top = (e - 32) + 256;  // E of k = 0
+      // k in [0, mb) with top - 2k >= t
+      const int32_t kk = top >= t ? (top - t) / 2 + 1 : 0;
+      cnt += (int64_t)h * (kk < mb ? kk : mb);
+    }
+    // the largest t with count(E >= t) >= B; count(E >= t + 1) < B then
+    const bool ok = cnt >= B;
+    const uint64_t bl = __ballot(ok);
+    // counts fall as t grows, so the largest qualifying t is the last set lane
+    if (lane == 0) wsum[wave] = bl ? (uint32_t)(63 - __clzll(bl)) + 1u : 0u;
+    __syncthreads();
+    if (tid == 0) {
+      int best = -1;
+      for (int w = 0; w < (int)(blockDim.x >> 6); ++w)
+        if (wsum[w]) best = 64 * w + (int)wsum[w] - 1;
+      s_sel = best;
+    }
+    __syncthreads();
+  }
+  const int32_t Et = s_sel;
+  // keys above the chosen exponent, and what is still needed inside it
+  if (tid == 0) s_need = 0;
+  __syncthreads();
+  {
+    int64_t above = 0;
+    for (int e = tid; e < 320; e += blockDim.x) {
+      const uint32_t h = hist[e];
+      const int32_t top = (e - 32) + 256;
+      const int32_t kk = top >= Et + 1 ? (top - Et - 1) / 2 + 1 : 0;
+      above += (int64_t)h * (kk < mb ? kk : mb);
+    }
+    for (int o = 32; o > 0; o >>= 1) above += __shfl_xor(above, o, 64);
+    if (lane == 0) atomicAdd((unsigned long long*)&s_need, (unsigned long long)above);
+  }
+  __syncthreads();
+  int64_t need = B - s_need;  // 1 <= need <= keys with E == Et
+  uint64_t prefix = 0;        // low bits chosen so far (above the current digit)
+  for (int d = 0; d < kGDigits; ++d) {
+    const int sh = gdigit_shift(d), nb = gdigit_bits(d);
+    for (int i = tid; i < 2048; i += blockDim.x) hist[i] = 0u;
+    __syncthreads();
+    for (int64_t i = tid; i < n; i += blockDim.x) {
+      const float v = st[i].y;
+      if (!(v > 0.0f)) continue;
+      int32_t ex;
+      uint32_t man;
+      var_exp_man(v, ex, man);
+      const int32_t diff = ex + 256 - Et;  // = 2k for the key in the chosen exponent
+      if (diff < 0 || (diff & 1) || diff / 2 >= mb) continue;
+      const uint64_t low = global_key(ex, man, diff / 2, i) & ((1ull << kGKeyLow) - 1ull);
+      if ((low >> (sh + nb)) != prefix) continue;
+      atomicAdd(&hist[(low >> sh) & ((1u << nb) - 1u)], 1u);
+    }
+    __syncthreads();
+    // suffix sums over the digit's bins (two per thread, high bins first)
+    const int nbins = 1 << nb;
+    const int b0 = nbins - 1 - 2 * tid;  // this thread's higher bin
+    uint32_t c0 = 0, c1 = 0;
+    if (2 * tid < nbins) {
+      c0 = hist[b0];
+      c1 = b0 - 1 >= 0 ? hist[b0 - 1] : 0u;
+    }
+    uint32_t x = c0 + c1;  // inclusive scan in descending bin order
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const uint32_t incl = before + x;          // keys in bins >= b0 - 1
+    const uint32_t excl = incl - c0 - c1;      // keys in bins > b0
+    if (2 * tid < nbins) {
+      if (excl < need && excl + c0 >= need) { s_sel = b0; s_need = need - excl; }
+      else if (excl + c0 < need && incl >= need) { s_sel = b0 - 1; s_need = need - excl - c0; }
+    }
+    __syncthreads();
+    prefix = (prefix << nb) | (uint64_t)s_sel;
+    need = s_need;
+    __syncthreads();
+  }
+  if (tid == 0) *thr_out = ((uint64_t)Et << kGKeyLow) | prefix;
+}
+
 hipError_t launch_enc_alloc(const Params& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_enc_alloc, dim3(p.n_sections, 1, seq_grid(p)), dim3(64), 0, s, p);
+  if (p.alloc_scope == 1 && p.transform == KVTC_PCA) {
+    hipLaunchKernelGGL(k_enc_alloc<1>, dim3(p.n_sections, 1, seq_grid(p)), dim3(64), 0, s, p);
+    hipLaunchKernelGGL(k_alloc_global, dim3(1, 1, seq_grid(p)), dim3(1024), 0, s, p);
+    hipLaunchKernelGGL(k_enc_alloc<2>, dim3(p.n_sections, 1, seq_grid(p)), dim3(64), 0, s, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_enc_alloc<0>, dim3(p.n_sections, 1, seq_grid(p)), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -470,7 +470,7 @@ __global__ __launch_bounds__(64 * kQWaves, 4) void k_quant128(const Params p0) {
 }
 
 hipError_t launch_quant128(const Params& p, hipStream_t s) {
-  const int32_t bmax = p.budget_k > p.budget_v ? p.budget_k : p.budget_v;
+  const int32_t bmax = p.sec_bits_max;
   // segment buffer: 64 tokens of every row, 2 b words per component
   const int segw = 2 * (bmax < 8 * p.D ? bmax : 8 * p.D);
   if (segw > 2048) return hipErrorInvalidValue;

@@ -872,7 +872,8 @@ __global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw
       if (p.transform == KVTC_WHT && b != (s == 0 ? p.bits_k_uniform : p.bits_v_uniform)) okl = false;
     }
     bool ok = __ballot(!okl) == 0ull;
-    if (p.transform == KVTC_PCA && g.sum_b > (s == 0 ? p.budget_k : p.budget_v)) ok = false;
+    if (p.transform == KVTC_PCA && g.sum_b > (p.alloc_scope == 1 ? p.sec_bits_max : (s == 0 ? p.budget_k : p.budget_v)))
+      ok = false;
     if (ok && mode > 1) ok = false;
     if (ok && g.P == 0 && (size != 0 || mode != 0)) ok = false;
     if (ok && g.P > 0 && (off < (uint64_t)p.chunks_off || (off & 15) || off > total || size > total - off)) ok = false;

@@ -25,7 +25,7 @@ int64_t max_container_bytes(const kvtc_config& c, const Layout& lo) {
   int64_t total = lo.chunks_off;
   if (lo.recs_per_sec == 0) return total;
   for (int s = 0; s < 2; ++s) {
-    int32_t budget = s == 0 ? lo.budget_k : lo.budget_v;
+    int32_t budget = c.alloc_scope == 1 ? lo.sec_bits_max : (s == 0 ? lo.budget_k : lo.budget_v);
     int64_t per_rec[2] = {0, 0};
     for (int which = 0; which < 2; ++which) {
       int32_t n = which == 0 ? lo.rec_tokens : lo.T_mid - (lo.recs_per_sec - 1) * lo.rec_tokens;
@@ -53,6 +53,7 @@ Params make_params(const PlanImpl& pl, const Layout& lo, const WsLayout& w) {
   p.tiles_per_rec = lo.tiles_per_rec; p.blks_per_rec = lo.blks_per_rec;
   p.basis_per_head = c.basis_per_head; p.wht_keys = c.wht_keys;
   p.budget_k = lo.budget_k; p.budget_v = lo.budget_v;
+  p.sec_bits_max = lo.sec_bits_max; p.alloc_scope = c.alloc_scope; p.total_budget = lo.total_budget;
   p.T = lo.T; p.s0 = lo.s0; p.mid_begin = lo.mid_begin; p.mid_end = lo.mid_end;
   p.T_mid = lo.T_mid; p.W_eff = lo.W_eff; p.n_sections = lo.n_sections;
   p.blks_per_sec = lo.blks_per_sec; p.n_blks = lo.n_blks;
@@ -97,6 +98,7 @@ void build_header(const PlanImpl& pl, const Layout& lo, uint8_t* h) {
   put64(h + 144, lo.raw_bytes); put64(h + 152, lo.dir_off); put64(h + 160, lo.chunks_off);
   put64(h + 176, pl.fingerprint);
   put32(h + 184, lo.budget_k); put32(h + 188, lo.budget_v);
+  put32(h + 192, c.alloc_scope);
 }
 
 }  // namespace kvtc
@@ -132,6 +134,11 @@ static kvtc_status check_config(const kvtc_config* c) {
   if (c->chunk_tokens / c->tile_tokens > kMaxTilesPerRec) return KVTC_ERR_UNSUPPORTED;
   if (c->basis_per_head != 0 && c->basis_per_head != 1) return KVTC_ERR_INVALID_ARG;
   if (c->wht_keys != 0 && c->wht_keys != 1) return KVTC_ERR_INVALID_ARG;
+  if (c->alloc_scope != 0 && c->alloc_scope != 1) return KVTC_ERR_INVALID_ARG;
+  if (c->alloc_scope == 1 && c->transform != KVTC_PCA) return KVTC_ERR_INVALID_ARG;
+  // one-budget keys carry the (section, component) index in 20 bits
+  if (c->alloc_scope == 1 && (int64_t)c->layers * 2 * c->kv_heads * c->head_dim > (1 << 20))
+    return KVTC_ERR_UNSUPPORTED;
   return KVTC_OK;
 }
 

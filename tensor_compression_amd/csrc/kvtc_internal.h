@@ -34,6 +34,8 @@ struct Layout {
   int32_t rec_tokens, recs_per_sec, n_recs, tiles_per_rec, blks_per_rec;  // chunk records
   int32_t n_r_sections;
   int32_t budget_k, budget_v;
+  int32_t sec_bits_max;  // largest width sum of one section (its budget, or all components at max_bits)
+  int64_t total_budget;  // the budget of all sections together (one-budget allocation)
   int64_t side_off, r_off, side_bytes, raw_off, raw_bytes, dir_off, chunks_off;
 };
 
@@ -128,6 +130,12 @@ KVTC_HD inline Layout make_layout(const kvtc_config& c, int32_t T) {
     lo.budget_k = floor_bits(c.bits_k) * c.head_dim;
     lo.budget_v = floor_bits(c.bits_v) * c.head_dim;
   }
+  lo.total_budget = (int64_t)c.layers * c.kv_heads * ((int64_t)lo.budget_k + lo.budget_v);
+  lo.sec_bits_max = lo.budget_k > lo.budget_v ? lo.budget_k : lo.budget_v;
+  if (c.alloc_scope == 1) {
+    const int64_t cap = (int64_t)c.head_dim * c.max_bits;
+    lo.sec_bits_max = (int32_t)(lo.total_budget < cap ? lo.total_budget : cap);
+  }
   return lo;
 }
 
@@ -147,6 +155,7 @@ constexpr int kCountSlots = 64;
 constexpr int64_t kCountOff = 256;
 constexpr int64_t kCountStride = 128;
 constexpr int64_t kStatusBlockBytes = kCountOff + kCountSlots * kCountStride;
+constexpr int64_t kGlobalThrOff = 16;  // u64 threshold key of the one-budget allocation
 
 // Bytes of a record slot's table area: 16 u16 entries per component.
 KVTC_HD inline int64_t slot_table_bytes(const kvtc_config& c) { return 32 * (int64_t)c.head_dim; }
@@ -172,8 +181,7 @@ KVTC_HD inline WsLayout make_ws_layout(const kvtc_config& c, const Layout& lo, b
   w.side_rcp = take(at, (int64_t)lo.n_sections * D * 4);
   w.side_zero = take(at, (int64_t)lo.n_sections * D * 4);
   w.side_bits = take(at, (int64_t)lo.n_sections * D);
-  int32_t bmax = lo.budget_k > lo.budget_v ? lo.budget_k : lo.budget_v;
-  int64_t tile_max = max_tile_bytes(c, c.tile_tokens, bmax);
+  int64_t tile_max = max_tile_bytes(c, c.tile_tokens, lo.sec_bits_max);
   w.packed_slot = align16(tile_max * lo.tiles_per_blk);
   w.packed = take(at, (int64_t)lo.n_blks * w.packed_slot);
   // A tile stream whose words outgrow its packed size cannot make the record
@@ -226,6 +234,8 @@ struct Params {
   int32_t L, H, D, dtype, transform, rope_keys, rope_style, max_bits;
   int32_t sb, lanes, blk_tokens, tile_tokens, basis_per_head, wht_keys;
   int32_t budget_k, budget_v;
+  int32_t sec_bits_max, alloc_scope;
+  int64_t total_budget;
   int32_t T, s0, mid_begin, mid_end, T_mid, W_eff, n_sections, blks_per_sec, n_blks,
       tiles_per_blk;
   int32_t rec_tokens, recs_per_sec, n_recs, tiles_per_rec, blks_per_rec;

@@ -39,6 +39,7 @@ class Config(ctypes.Structure):
         ("rans_lanes", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
         ("tile_tokens", ctypes.c_int32), ("basis_per_head", ctypes.c_int32),
         ("wht_keys", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
+        ("alloc_scope", ctypes.c_int32),
     ]
 
 
@@ -136,6 +137,8 @@ def make_config(cfg: dict, max_tokens: int) -> Config:
     for f, _ in Config._fields_:
         if f == "max_tokens":
             c.max_tokens = max_tokens
+        elif f == "alloc_scope":
+            c.alloc_scope = cfg.get("alloc_scope", 0)
         else:
             setattr(c, f, cfg[f])
     return c

@@ -96,8 +96,9 @@ def compare_section(orc, cfg, T, k, v, basis, gpu_bytes, gpu_stats, u, gpu_coef=
     vo = var_o.astype(np.float64)
     vtol = 2 * np.sqrt(vo) * bmax + bmax ** 2 + 1e-6 * vo + tiny ** 2
     assert np.all(np.abs(var_g.astype(np.float64) - vo) <= vtol), f"section {u}: var"
-    # -- widths
-    if not wht:
+    # -- widths (one budget over all sections: checked over the whole cache
+    # by check_global_widths)
+    if not wht and cfg.get("alloc_scope", 0) == 0:
         budget = orc.budget(cfg["bits_k"] if s == 0 else cfg["bits_v"], D)
         assert np.array_equal(orc.alloc_greedy(var_g, budget, cfg["max_bits"]), bits_g), \
             f"section {u}: GPU allocation differs from greedy on its own variances"
@@ -139,6 +140,23 @@ def compare_section(orc, cfg, T, k, v, basis, gpu_bytes, gpu_stats, u, gpu_coef=
     if report is not None:
         report.append(out)
     return out
+
+
+def check_global_widths(orc, cfg, T, gpu_bytes, gpu_stats, k, v, basis):
+    """One budget over all sections: the GPU's widths equal the greedy
+    allocation over every component of the cache run on the GPU's own
+    variances (exact), and agree with it on the oracle's variances up to a
+    near-tie of equal modelled distortion."""
+    lo = orc.layout(cfg, T)
+    D = cfg["head_dim"]
+    pc = orc.parse_container(gpu_bytes, cfg, T)
+    bits_g = pc["bits"][: lo.n_sections].astype(np.uint8)
+    var_g = gpu_stats[1][: lo.n_sections]
+    budget = sum(orc.budget(cfg["bits_k"] if (u // cfg["kv_heads"]) % 2 == 0 else cfg["bits_v"], D)
+                 for u in range(lo.n_sections))
+    want = orc.alloc_greedy_heap(var_g, budget, cfg["max_bits"]).reshape(lo.n_sections, D)
+    assert np.array_equal(want, bits_g), "GPU widths differ from the global greedy on its own variances"
+    return bits_g, budget
 
 
 def check_records(orc, cfg, data, u, T, bits):

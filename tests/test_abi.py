@@ -73,3 +73,17 @@ def test_hadamard_path_needs_head_dim_128():
         st, _ = _mem_size(dict(cfg, head_dim=64))
         assert st == kvtc.ERR_UNSUPPORTED
 
+
+
+def test_alloc_scope_validation():
+    """One budget over all sections: PCA only, a valid scope value, and the
+    (section, component) index within the 20 bits of the selection keys."""
+    w = synth.WORKLOADS["llama3_8b"]
+    cfg = synth.oracle_config(w, alloc_scope=1)
+    assert _mem_size(cfg)[0] == kvtc.OK
+    assert _mem_size(dict(cfg, alloc_scope=2))[0] == kvtc.ERR_INVALID_ARG
+    h = synth.oracle_config(synth.WORKLOADS["hadamard_long"], alloc_scope=1)
+    assert _mem_size(h)[0] == kvtc.ERR_INVALID_ARG
+    # 64 layers x 8 heads x 2 x 128 = 2^17 components fit; 2^21 do not
+    assert _mem_size(dict(cfg, layers=64))[0] == kvtc.OK
+    assert _mem_size(dict(cfg, layers=1024))[0] == kvtc.ERR_UNSUPPORTED
