@@ -92,6 +92,7 @@ def lib() -> ctypes.CDLL:
             "orc_budget": (i32, [f32, i32]),
             "orc_alloc_greedy": (None, [P, i32, i32, i32, P]),
             "orc_alloc_greedy_heap": (None, [P, ctypes.c_int64, ctypes.c_int64, i32, P]),
+            "orc_checksum": (None, [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P]),
             "orc_alloc_dp": (f64, [P, i32, i32, i32, P]),
             "orc_distortion": (f64, [P, P, i32]),
             "orc_side_info": (None, [P, P, P, P, i32, P, P, P]),
@@ -472,6 +473,15 @@ def check_config(cfg: dict) -> int:
     return int(lib().orc_check_config(ctypes.byref(c)))
 
 
+def checksum(data: bytes, skip_from: int = 0, skip_to: int = 0) -> tuple[int, int]:
+    """(A, B): plain and position-weighted sums of the 32-bit words mod 2^61 - 1."""
+    buf = np.frombuffer(bytes(data), np.uint8).copy()
+    a = ctypes.c_uint64(0)
+    b = ctypes.c_uint64(0)
+    lib().orc_checksum(_p(buf), len(buf), skip_from, skip_to, ctypes.byref(a), ctypes.byref(b))
+    return a.value, b.value
+
+
 def fnv1a64(data: bytes, h: int = 0xCBF29CE484222325) -> int:
     buf = np.frombuffer(bytes(data), np.uint8).copy()
     return int(lib().orc_fnv1a64(h, _p(buf) if buf.size else None, buf.size))
@@ -622,11 +632,13 @@ def parse_container(data: bytes, cfg: dict, T: int) -> dict:
     zero = recs[:, D: 5 * D].copy().view(np.float32)
     scale = recs[:, 5 * D: 9 * D].copy().view(np.float32)
     nch = lo.n_sections * lo.chunks_per_sec
-    d = buf[dir_off: dir_off + 16 * nch].reshape(max(nch, 0), 16)
+    d = buf[dir_off: dir_off + 32 * nch].reshape(max(nch, 0), 32)
     offs = d[:, :8].copy().view(np.uint64).ravel()
     sizes = d[:, 8:12].copy().view(np.uint32).ravel()
     modes = d[:, 12:16].copy().view(np.uint32).ravel()
-    return dict(bits=bits, zero=zero, scale=scale, offsets=offs, sizes=sizes, modes=modes,
+    csums = d[:, 16:32].copy().view(np.uint64).reshape(-1, 2)
+    return dict(bits=bits, zero=zero, scale=scale, offsets=offs, sizes=sizes, modes=modes, csums=csums,
+                fixed_csum=(int(hdr[200:208].view(np.uint64)[0]), int(hdr[208:216].view(np.uint64)[0])),
                 chunks_off=chunks_off, total=total, layout=lo,
                 fingerprint=int(hdr[176:184].view(np.uint64)[0]))
 

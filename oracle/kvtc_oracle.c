@@ -871,7 +871,8 @@ int orc_chunk_decode(const orc_config* c, const uint8_t* bits, const uint8_t* re
 
 #define HDR_BYTES 256
 #define SEC_REC(D) (9 * (int64_t)(D))
-#define DIR_ENTRY 16
+#define DIR_ENTRY 32
+#define CSUM_FIELD 200 /* header bytes [200, 216): checksum of the fixed part */
 
 typedef struct {
   int32_t T, s0, mid_begin, mid_end, T_mid, W_eff;
@@ -881,6 +882,30 @@ typedef struct {
 } layout_t;
 
 static int64_t align16(int64_t x) { return (x + 15) & ~(int64_t)15; }
+
+/* Integrity checksum of a byte range whose length is a multiple of 4
+ * ("Quantum-Aware Tensor Compression", QATC transport: bounded chunks with an
+ * aggregate checksum, and a damaged or truncated payload is refused before
+ * restore).  Over the little-endian 32-bit words w_0 .. w_{n-1}, with the
+ * prime P = 2^61 - 1: A = sum w_j mod P and B = sum (j + 1) w_j mod P -- the
+ * plain and the position-weighted sum of Fletcher's construction, taken
+ * modulo a prime so that every change of one or two words is caught.  Words
+ * in [skip_from, skip_to) count as zero (the field that holds the result). */
+#define CSUM_P ((uint64_t)0x1fffffffffffffffull)
+
+void orc_checksum(const uint8_t* data, int64_t n_bytes, int64_t skip_from, int64_t skip_to,
+                  uint64_t* a_out, uint64_t* b_out) {
+  unsigned __int128 A = 0, B = 0;
+  for (int64_t j = 0; j < n_bytes / 4; ++j) {
+    uint64_t w = (uint64_t)data[4 * j] | ((uint64_t)data[4 * j + 1] << 8) |
+                 ((uint64_t)data[4 * j + 2] << 16) | ((uint64_t)data[4 * j + 3] << 24);
+    if (4 * j >= skip_from && 4 * j < skip_to) w = 0;
+    A = (A + w) % CSUM_P;
+    B = (B + (unsigned __int128)(j + 1) * w) % CSUM_P;
+  }
+  *a_out = (uint64_t)A;
+  *b_out = (uint64_t)B;
+}
 
 int orc_check_config(const orc_config* c) {
   if (c->layers < 1 || c->kv_heads < 1) return ORC_ERR_INVALID_ARG;
@@ -1103,7 +1128,7 @@ static void write_header(const orc_config* c, const layout_t* lo, uint64_t fp,
                          int64_t total, uint8_t* out) {
   memset(out, 0, HDR_BYTES);
   memcpy(out + 0, "KVTC", 4);
-  put32(out + 4, 2);
+  put32(out + 4, 3);
   put32(out + 8, HDR_BYTES);
   put32(out + 12, 0);
   put32(out + 16, (uint32_t)c->layers);
@@ -1338,12 +1363,21 @@ int orc_encode(const orc_config* c, const void* k, const void* v, int32_t T,
       put64(out + dir, (uint64_t)pos);
       put32(out + dir + 8, (uint32_t)size);
       put32(out + dir + 12, (uint32_t)mode);
+      uint64_t ca, cb;
+      orc_checksum(out + pos, size, 0, 0, &ca, &cb);
+      put64(out + dir + 16, ca);
+      put64(out + dir + 24, cb);
       pos += size;
     }
   }
   if (st == ORC_OK) {
     copy_raw(c, &lo, k, v, out + lo.raw_off, 1);
     write_header(c, &lo, orc_fingerprint(c, basis), pos, out);
+    /* last: the checksum of everything before the records */
+    uint64_t fa, fb;
+    orc_checksum(out, lo.chunks_off, CSUM_FIELD, CSUM_FIELD + 16, &fa, &fb);
+    put64(out + CSUM_FIELD, fa);
+    put64(out + CSUM_FIELD + 8, fb);
     *out_bytes = pos;
   }
   free(x); free(coef); free(r); free(q);
@@ -1357,7 +1391,7 @@ int orc_encode(const orc_config* c, const void* k, const void* v, int32_t T,
 static int parse_header(const orc_config* c, const float* basis, const uint8_t* in,
                         int64_t n, layout_t* lo) {
   if (n < HDR_BYTES) return ORC_ERR_CORRUPT;
-  if (memcmp(in, "KVTC", 4) != 0 || get32(in + 4) != 2 || get32(in + 8) != HDR_BYTES)
+  if (memcmp(in, "KVTC", 4) != 0 || get32(in + 4) != 3 || get32(in + 8) != HDR_BYTES)
     return ORC_ERR_CORRUPT;
   orc_config h;
   memset(&h, 0, sizeof h);
@@ -1405,6 +1439,9 @@ static int parse_header(const orc_config* c, const float* basis, const uint8_t* 
   uint64_t total = get64(in + 168);
   if (total > (uint64_t)n || total < (uint64_t)lo->chunks_off) return ORC_ERR_CORRUPT;
   if (get64(in + 176) != orc_fingerprint(c, basis)) return ORC_ERR_CORRUPT;
+  uint64_t fa, fb;
+  orc_checksum(in, lo->chunks_off, CSUM_FIELD, CSUM_FIELD + 16, &fa, &fb);
+  if (fa != get64(in + CSUM_FIELD) || fb != get64(in + CSUM_FIELD + 8)) return ORC_ERR_CORRUPT;
   return ORC_OK;
 }
 
@@ -1422,6 +1459,9 @@ static int decode_chunk_codes(const orc_config* c, const layout_t* lo, const uin
   if (size > 0 && (off < (uint64_t)lo->chunks_off || (off & 15) || off > (uint64_t)total ||
                    size > (uint64_t)total - off))
     return ORC_ERR_CORRUPT;
+  uint64_t ca, cb;
+  orc_checksum(size > 0 ? in + off : in, size, 0, 0, &ca, &cb);
+  if (ca != get64(in + dir + 16) || cb != get64(in + dir + 24)) return ORC_ERR_CORRUPT;
   return orc_chunk_decode(c, bits, size > 0 ? in + off : in, size, (int32_t)mode, n, q);
 }
 

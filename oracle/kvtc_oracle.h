@@ -93,6 +93,8 @@ double orc_alloc_dp(const float* var, int32_t D, int32_t budget, int32_t max_bit
                     uint8_t* bits);
 void orc_alloc_greedy_heap(const float* var, int64_t n, int64_t budget, int32_t max_bits,
                            uint8_t* bits);
+void orc_checksum(const uint8_t* data, int64_t n_bytes, int64_t skip_from, int64_t skip_to,
+                  uint64_t* a_out, uint64_t* b_out);
 double orc_distortion(const float* var, const uint8_t* bits, int32_t D);
 void orc_side_info(const uint8_t* bits, const float* mu, const float* cmin,
                    const float* cmax, int32_t D, float* zero, float* scale, float* rcp);
