@@ -71,6 +71,8 @@ PHASE_KERNELS = {
     "enc_quant_pack": (("k_quant128",), ("kernels_quant.hip",)),
     "rans_encode": (("k_rans_enc_recs",), ("kernels_rans.hip",)),
     "assemble": (("k_scan", "k_copy_records"), ("kernels_rans.hip",)),
+    "enc_checksum": (("k_csum_part", "k_csum_final"), ("kernels_rans.hip",)),
+    "dec_checksum": (("k_csum_part", "k_csum_final"), ("kernels_rans.hip",)),
     "rans_decode": (("k_rans_dec_recs",), ("kernels_rans.hip",)),
     "dec_transform": (("k_dec_pca128",), ("kernels_decode.hip",)),
 }

@@ -168,20 +168,41 @@ kvtc_status kvtc_workspace_size(kvtc_plan_t plan, int32_t T, size_t* ws_bytes,
                                 size_t* max_container_bytes);
 
 /* Encode one cache of T tokens (T <= max_tokens) into a container at `out`
- * (device, `cap` bytes).  k, v: device [L,H,T,D] in the cache dtype.  ws:
+ * (device, `cap` bytes): the steps of "KVTC: The Open-Source KV Cache Codec
+ * That Treats LLM Memory Like Media", How the Pipeline Works (regions, RoPE
+ * undo, PCA or Hadamard transform, bit allocation, quantisation, entropy
+ * coding), each section carrying its widths, zero points and scales as in
+ * its CompressedSection.  k, v: device [L,H,T,D] in the cache dtype.  ws:
  * device workspace of ws_bytes >= kvtc_workspace_size().  Asynchronous; the
  * container size and the device status (OK, NONFINITE, CAPACITY) are read
  * with kvtc_result() after the stream has been synchronised.  The container
- * is deterministic: the same inputs give the same bytes. */
+ * is deterministic: the same inputs give the same bytes.
+ *
+ * Container (version 3, little-endian): a 256-byte header (config echo, T,
+ * region offsets, total bytes, basis fingerprint, and at bytes 200..215 the
+ * checksum of everything before the records); per section u8 widths[D],
+ * f32 zero[D], f32 scale[D] (and per-token RMS on the Hadamard path); the
+ * raw sink and recent windows; a directory of 32-byte entries (u64 offset,
+ * u32 size, u32 mode, u64 x 2 checksum of the record); the chunk records.
+ * Checksums ("Quantum-Aware Tensor Compression", QATC transport: an
+ * aggregate checksum over bounded chunks) are A = sum w_j and
+ * B = sum (j + 1) w_j modulo 2^61 - 1 over the range's 32-bit words, the
+ * header's own field counting as zero. */
 kvtc_status kvtc_encode(kvtc_plan_t plan, const void* k, const void* v, int32_t T, void* out,
                         size_t cap, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Decode a container of T tokens (the T it was encoded with; the header is
  * checked against it on the device) from `in` (device, in_bytes) into k_out,
- * v_out (device [L,H,T,D] in out_dtype, KVTC_BF16 or KVTC_FP32: RNE cast).
- * Sink and recent windows are restored bit-exactly (converted when out_dtype
- * differs from the cache dtype).  Asynchronous; a corrupt container sets
- * KVTC_ERR_CORRUPT in the workspace status and leaves the outputs undefined. */
+ * v_out (device [L,H,T,D] in out_dtype, KVTC_BF16 or KVTC_FP32: RNE cast):
+ * the inverse steps of the same pipeline (entropy decode, dequantise,
+ * inverse transform, RoPE re-applied), which "returns the same native tensor
+ * bytes" for the raw windows ("Compress the most expensive bytes in AI", KV
+ * & tensor mode).  Sink and recent windows are restored bit-exactly
+ * (converted when out_dtype differs from the cache dtype).  The header, the
+ * checksum of the fixed part and every record's checksum are verified; a
+ * damaged or truncated container (QATC: rejected before restore) sets
+ * KVTC_ERR_CORRUPT in the workspace status and leaves the outputs
+ * undefined.  Asynchronous. */
 kvtc_status kvtc_decode(kvtc_plan_t plan, const void* in, size_t in_bytes, int32_t T,
                         void* k_out, void* v_out, int32_t out_dtype, void* ws, size_t ws_bytes,
                         hipStream_t stream);
@@ -196,8 +217,8 @@ kvtc_status kvtc_decode(kvtc_plan_t plan, const void* in, size_t in_bytes, int32
  * hipMalloc.  kvtc_decode with its workspace replaced by a fixed array inside
  * the library: KVTC_NOALLOC_SCRATCH_BYTES of device memory per device, held
  * from the code object's load on that device until the process ends.  The
- * decoder needs a 256-aligned status block of 8448 bytes plus its packed
- * tiles there (about 71 MB for 32 layers x 8 KV heads x 4096 tokens x
+ * decoder needs a 256-aligned status block of 8448 bytes, 16 KiB of
+ * partial checksums and its packed tiles there (about 71 MB for 32 layers x 8 KV heads x 4096 tokens x
  * head_dim 128 at 2 bits per component); a call that needs more returns
  * KVTC_ERR_CAPACITY and enqueues nothing.  The call allocates nothing:
  * no hipMalloc, hipFree, event or library allocation.

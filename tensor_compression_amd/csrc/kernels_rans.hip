@@ -651,7 +651,10 @@ __global__ __launch_bounds__(64 * kCopyWaves) void k_copy_records(const Params p
     pos = reinterpret_cast<const uint64_t*>(p.ws + p.w.rec_pos)[r];
   }
   if (get_status(p.ws, p.w) & ((1u << KVTC_ERR_CAPACITY) | (1u << KVTC_ERR_NONFINITE))) return;
-  if (size == 0) return;
+  if (size == 0) {  // an empty record: the checksum of no words
+    if (tid < 2) reinterpret_cast<uint64_t*>(p.out_final + p.dir_off + (int64_t)r * kDirEntry + 16)[tid] = 0;
+    return;
+  }
   const int u = r / p.recs_per_sec, cr = r % p.recs_per_sec;
   if (wave == 0) rec_setup(p, cr, p.ws + p.w.side_bits + (int64_t)u * p.D, g);
   __syncthreads();
@@ -681,9 +684,13 @@ __global__ __launch_bounds__(64 * kCopyWaves) void k_copy_records(const Params p
   }
   __syncthreads();
   uint8_t* dst = p.out_final + p.chunks_off + pos;  // 16-byte aligned record
+  // the record's checksum, summed over the words as they are copied (the
+  // zero padding adds nothing)
+  uint64_t ca = 0, cb = 0;
   // one wave copies n_dw dwords, eight in flight per lane; the last keeps only
   // its low half when `half_last` (an odd word count padded with zeros)
   auto copy_dw = [&](const uint32_t* src, uint32_t* d, int n_dw, bool half_last) {
+    const uint64_t j0 = (uint64_t)(reinterpret_cast<uint8_t*>(d) - dst) >> 2;  // record word index of d[0]
     for (int i0 = 0; i0 < n_dw; i0 += 8 * 64) {
       uint32_t v[8];
 #pragma unroll
@@ -694,7 +701,11 @@ __global__ __launch_bounds__(64 * kCopyWaves) void k_copy_records(const Params p
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int i = i0 + k * 64 + lane;
-        if (i < n_dw) d[i] = (half_last && i == n_dw - 1) ? (v[k] & 0xffffu) : v[k];
+        if (i < n_dw) {
+          const uint32_t w = (half_last && i == n_dw - 1) ? (v[k] & 0xffffu) : v[k];
+          d[i] = w;
+          csum_add(ca, cb, j0 + (uint64_t)i, w);
+        }
       }
     }
   };
@@ -719,6 +730,93 @@ __global__ __launch_bounds__(64 * kCopyWaves) void k_copy_records(const Params p
     copy_dw(nwv, reinterpret_cast<uint32_t*>(dst + g.tb), ntiles, false);
   }
   for (int64_t i = s_at[ntiles] + tid; i < size; i += 64 * kCopyWaves) dst[i] = 0;
+  __shared__ uint64_t s_cs[32];
+  csum_block_reduce(ca, cb, s_cs);
+  if (tid == 0) {
+    uint64_t* d = reinterpret_cast<uint64_t*>(p.out_final + p.dir_off + (int64_t)r * kDirEntry + 16);
+    d[0] = ca;
+    d[1] = cb;
+  }
+}
+
+// ---- checksum of the fixed part ----------------------------------------------
+
+// Partial checksums of the words [0, chunks_off / 4) of a container (the
+// header's checksum field counts as zero), one contiguous range per
+// workgroup; k_csum_final sums them.
+constexpr int kCsumThreads = 256;
+
+__global__ __launch_bounds__(kCsumThreads) void k_csum_part(const Params p0, int encode) {
+  const Params p = at_seq(p0, blockIdx.z);
+  const uint32_t* w32 = reinterpret_cast<const uint32_t*>(encode ? p.out_final : p.in);
+  // 16-byte units (chunks_off is a multiple of 16), four in flight per thread
+  const int64_t nq = p.chunks_off / 16;
+  const int64_t per = (nq + kCsumParts - 1) / kCsumParts;
+  const int64_t a = (int64_t)blockIdx.x * per, b = min(nq, a + per);
+  const uint4* q4 = reinterpret_cast<const uint4*>(w32);
+  uint64_t A = 0, B = 0;
+  if (!encode && (uint64_t)p.cap < (uint64_t)p.chunks_off) {
+    // a truncated container: k_dec_check reports it, nothing is read
+  } else {
+    for (int64_t q0 = a + threadIdx.x; q0 < b; q0 += 4 * kCsumThreads) {
+      uint4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int64_t q = q0 + k * kCsumThreads;
+        v[k] = q < b ? q4[q] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int64_t q = q0 + k * kCsumThreads;
+        if (q >= b) continue;
+        const uint32_t e[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int64_t j = 4 * q + c;
+          const bool field = j >= kCsumField / 4 && j < kCsumField / 4 + 4;
+          csum_add(A, B, (uint64_t)j, field ? 0u : e[c]);
+        }
+      }
+    }
+  }
+  __shared__ uint64_t s_cs[32];
+  csum_block_reduce(A, B, s_cs);
+  if (threadIdx.x == 0) {
+    uint64_t* out = reinterpret_cast<uint64_t*>(p.ws + p.w.csum) + 2 * blockIdx.x;
+    out[0] = A;
+    out[1] = B;
+  }
+}
+
+// Encode: the sum of the partials into the header's checksum field.
+// Decode: the sum against that field; a mismatch marks the container corrupt.
+__global__ __launch_bounds__(kCsumThreads) void k_csum_final(const Params p0, int encode) {
+  const Params p = at_seq(p0, blockIdx.z);
+  const uint64_t* part = reinterpret_cast<const uint64_t*>(p.ws + p.w.csum);
+  uint64_t A = 0, B = 0;
+  for (int k = threadIdx.x; k < kCsumParts; k += kCsumThreads) {
+    A = mod61(A + part[2 * k]);
+    B = mod61(B + part[2 * k + 1]);
+  }
+  __shared__ uint64_t s_cs[32];
+  csum_block_reduce(A, B, s_cs);
+  if (threadIdx.x != 0) return;
+  if (encode) {
+    if (get_status(p.ws, p.w) & ((1u << KVTC_ERR_CAPACITY) | (1u << KVTC_ERR_NONFINITE))) return;
+    uint64_t* f = reinterpret_cast<uint64_t*>(p.out_final + kCsumField);
+    f[0] = A;
+    f[1] = B;
+  } else {
+    if ((uint64_t)p.cap < (uint64_t)p.chunks_off) return;
+    const uint64_t* f = reinterpret_cast<const uint64_t*>(p.in + kCsumField);
+    if (f[0] != A || f[1] != B) set_status(p.ws, p.w, KVTC_ERR_CORRUPT);
+  }
+}
+
+hipError_t launch_csum(const Params& p, int encode, hipStream_t s) {
+  hipLaunchKernelGGL(k_csum_part, dim3(kCsumParts, 1, seq_grid(p)), dim3(kCsumThreads), 0, s, p, encode);
+  hipLaunchKernelGGL(k_csum_final, dim3(1, 1, seq_grid(p)), dim3(kCsumThreads), 0, s, p, encode);
+  return hipGetLastError();
 }
 
 hipError_t launch_assemble(const Params& p, const uint8_t* hdr, hipStream_t s) {
@@ -751,7 +849,7 @@ __global__ void k_dec_check(const Params p0, HeaderBytes hdr) {
   __syncthreads();
   if (p.cap < p.chunks_off || p.cap < kHeaderBytes) {
     if (tid == 0) s_bad = 1;
-  } else if (tid < kHeaderBytes / 4 && tid != 42 && tid != 43) {
+  } else if (tid < kHeaderBytes / 4 && tid != 42 && tid != 43 && (tid < kCsumField / 4 || tid >= kCsumField / 4 + 4)) {
     const uint32_t want = header_word(p, hdr, tid);
     if (reinterpret_cast<const uint32_t*>(p.in)[tid] != want) atomicOr(&s_bad, 1);
   }
@@ -828,8 +926,11 @@ __device__ __forceinline__ void build_slot_table(const uint32_t* cm, uint32_t M,
 // The workgroup walks the coded components in lockstep: while its streams
 // decode component ci with ci's slot table, every thread helps build the
 // table of ci + 1 in the other buffer, and a barrier ends the component.
-template <int LANES, int STEPS>
-__global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw_runs) {
+// BIG: workgroups of more than 768 threads (more than 24 tiles per record);
+// otherwise two workgroups of up to 12 waves share a CU: six waves per SIMD,
+// which caps the registers at 80.
+template <int LANES, int STEPS, bool BIG>
+__global__ __launch_bounds__(BIG ? 1024 : 768, BIG ? 4 : 6) void k_rans_dec_recs(const Params p0, int raw_runs) {
   constexpr int SPW = 64 / LANES;
   constexpr int NR = 32 / LANES + 1;  // staged raw-row words per lane
   const Params p = at_seq(p0, blockIdx.z);
@@ -901,7 +1002,37 @@ __global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw
     if (tid == 0) set_status(p.ws, p.w, KVTC_ERR_CORRUPT);
     return;
   }
-  if (g.P == 0) return;
+  // The record against its directory checksum (its range was checked
+  // above).  Threads add 16-byte units [q0, q1) of the record to their
+  // partial sums -- at once on the short paths, after the decode on the coded
+  // path -- and the block total is compared; a mismatch marks the container
+  // corrupt (the decode of a damaged record stays in bounds).
+  const uint4* r4 = reinterpret_cast<const uint4*>(rec);
+  const uint32_t nq = size / 16;
+  uint64_t csA = 0, csB = 0;
+  auto csum_units = [&](uint32_t q0, uint32_t q1, uint32_t t, uint32_t nt) {
+    for (uint32_t q = q0 + t; q < q1; q += nt) {
+      const uint4 v = r4[q];
+      const uint64_t j = 4ull * q;
+      csum_add(csA, csB, j, v.x);
+      csum_add(csA, csB, j + 1, v.y);
+      csum_add(csA, csB, j + 2, v.z);
+      csum_add(csA, csB, j + 3, v.w);
+    }
+  };
+  auto verify_record = [&]() {
+    __shared__ uint64_t s_cs[32];
+    csum_block_reduce(csA, csB, s_cs);
+    if (tid == 0) {
+      const uint64_t* d = reinterpret_cast<const uint64_t*>(dir + 16);
+      if (d[0] != csA || d[1] != csB) set_status(p.ws, p.w, KVTC_ERR_CORRUPT);
+    }
+  };
+  if (g.P == 0) {
+    csum_units(0, nq, tid, blockDim.x);
+    verify_record();
+    return;
+  }
   if (mode == 1) {  // the packed rows themselves
     int64_t at = 0;
     for (int t = 0; t < ntiles; ++t) {
@@ -911,6 +1042,8 @@ __global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw
       for (int i = tid; i < pt / 4; i += blockDim.x) dst[i] = src[i];
       at += pt;
     }
+    csum_units(0, nq, tid, blockDim.x);
+    verify_record();
     return;
   }
   // tables -> cumulative frequencies (entries past the alphabet hold M, so
@@ -1153,6 +1286,10 @@ __global__ __launch_bounds__(1024) void k_rans_dec_recs(const Params p0, int raw
   if (has_stream && __ballot(!ok)) {
     if (lane == 0) set_status(p.ws, p.w, KVTC_ERR_CORRUPT);
   }
+  // the record's checksum by the table-building waves (by every thread
+  // when the launch has none); the streams meet them in the reduction
+  if (builds) csum_units(0, nq, btid, bthreads);
+  verify_record();
 }
 
 hipError_t launch_rans_decode_chunks(const Params& p, hipStream_t s, bool with_raw) {
@@ -1165,14 +1302,17 @@ hipError_t launch_rans_decode_chunks(const Params& p, hipStream_t s, bool with_r
   const int raw_runs = with_raw && p.n_seqs == 0 ? 4 * p.L * p.H : 0;
   const dim3 grid(p.n_recs + raw_runs, 1, seq_grid(p)), block(64 * waves);
   const int steps = p.tile_tokens / p.lanes;
-  if (p.lanes == 16) {
-    if (steps == 16) hipLaunchKernelGGL((k_rans_dec_recs<16, 16>), grid, block, lds, s, p, raw_runs);
-    else if (steps == 8) hipLaunchKernelGGL((k_rans_dec_recs<16, 8>), grid, block, lds, s, p, raw_runs);
-    else hipLaunchKernelGGL((k_rans_dec_recs<16, 0>), grid, block, lds, s, p, raw_runs);
+  if (64 * waves > 768) {
+    if (p.lanes == 16) hipLaunchKernelGGL((k_rans_dec_recs<16, 0, true>), grid, block, lds, s, p, raw_runs);
+    else hipLaunchKernelGGL((k_rans_dec_recs<32, 0, true>), grid, block, lds, s, p, raw_runs);
+  } else if (p.lanes == 16) {
+    if (steps == 16) hipLaunchKernelGGL((k_rans_dec_recs<16, 16, false>), grid, block, lds, s, p, raw_runs);
+    else if (steps == 8) hipLaunchKernelGGL((k_rans_dec_recs<16, 8, false>), grid, block, lds, s, p, raw_runs);
+    else hipLaunchKernelGGL((k_rans_dec_recs<16, 0, false>), grid, block, lds, s, p, raw_runs);
   } else {
-    if (steps == 8) hipLaunchKernelGGL((k_rans_dec_recs<32, 8>), grid, block, lds, s, p, raw_runs);
-    else if (steps == 4) hipLaunchKernelGGL((k_rans_dec_recs<32, 4>), grid, block, lds, s, p, raw_runs);
-    else hipLaunchKernelGGL((k_rans_dec_recs<32, 0>), grid, block, lds, s, p, raw_runs);
+    if (steps == 8) hipLaunchKernelGGL((k_rans_dec_recs<32, 8, false>), grid, block, lds, s, p, raw_runs);
+    else if (steps == 4) hipLaunchKernelGGL((k_rans_dec_recs<32, 4, false>), grid, block, lds, s, p, raw_runs);
+    else hipLaunchKernelGGL((k_rans_dec_recs<32, 0, false>), grid, block, lds, s, p, raw_runs);
   }
   return hipGetLastError();
 }

@@ -387,6 +387,8 @@ kvtc_status kvtc_encode(kvtc_plan_t plan, const void* k, const void* v, int32_t 
   }
   HIP_TRY(launch_assemble(p, hdr, stream));
   prof.phase("assemble");
+  HIP_TRY(launch_csum(p, 1, stream));
+  prof.phase("enc_checksum");
   return KVTC_OK;
 }
 
@@ -412,6 +414,8 @@ static kvtc_status decode_launch(PlanImpl* pl, const Layout& lo, const WsLayout&
   ProfScope prof(profile ? pl : nullptr, stream);
   HIP_TRY(launch_dec_check(p, hdr, stream));  // clears, then sets the status word
   prof.phase("dec_check");
+  HIP_TRY(launch_csum(p, 0, stream));
+  prof.phase("dec_checksum");
   if (lo.n_blks > 0) {
     // the raw runs are copied by extra workgroups of the rANS decoder
     HIP_TRY(launch_rans_decode_chunks(p, stream, true));
@@ -441,7 +445,8 @@ kvtc_status kvtc_decode(kvtc_plan_t plan, const void* in, size_t in_bytes, int32
 
 // ---- decode into a fixed device array ------------------------------------------
 
-// The decoder's only workspace is the status block and the packed tiles; the
+// The decoder's only workspace is the status block, the partial checksums
+// of the fixed part and the packed tiles; the
 // variant below keeps both in this array (one copy per device, alive until
 // the process ends) instead of a caller's workspace.
 constexpr int64_t kScratchBytes = KVTC_NOALLOC_SCRATCH_BYTES;
@@ -467,9 +472,9 @@ static kvtc_status scratch_of_current_device(uint8_t** at) {
   return KVTC_OK;
 }
 
-// The decoder's workspace inside the scratch array: the status block, then
-// the packed tiles; every other region is unused by the decode kernels and
-// points at the status block.
+// The decoder's workspace inside the scratch array: the status block, the
+// partial checksums, then the packed tiles; every other region is unused by
+// the decode kernels and points at the status block.
 static WsLayout decode_scratch_layout(const kvtc_config& c, const Layout& lo) {
   const WsLayout full = make_ws_layout(c, lo);
   WsLayout w{};
@@ -478,7 +483,8 @@ static WsLayout decode_scratch_layout(const kvtc_config& c, const Layout& lo) {
   w.tile_raw_max = full.tile_raw_max;
   w.rec_slot = full.rec_slot;
   w.status = 0;
-  w.packed = align256(kStatusBlockBytes);
+  w.csum = align256(kStatusBlockBytes);
+  w.packed = w.csum + align256((int64_t)kCsumParts * 16);
   w.total = w.packed + align256((int64_t)lo.n_blks * w.packed_slot);
   return w;
 }
@@ -605,6 +611,7 @@ kvtc_status kvtc_encode_paged(kvtc_plan_t plan, const void* k_pool, const void* 
     prof.phase("rans_encode");
   }
   HIP_TRY(launch_assemble(p, hdr, stream));
+  HIP_TRY(launch_csum(p, 1, stream));
   HIP_TRY(launch_batch_finish(p, stream));
   prof.phase("assemble");
   return KVTC_OK;
@@ -630,6 +637,7 @@ kvtc_status kvtc_decode_paged(kvtc_plan_t plan, const void* in, size_t in_bytes,
   ProfScope prof(pl, stream);
   HIP_TRY(launch_seq_setup(p, seq_lens_dev, sum_t, max_t, (int64_t)ws_bytes, 1, stream));
   HIP_TRY(launch_dec_check(p, hdr, stream));
+  HIP_TRY(launch_csum(p, 0, stream));
   prof.phase("dec_check");
   if (p.n_blks > 0) {
     HIP_TRY(launch_rans_decode_chunks(p, stream));

@@ -11,8 +11,10 @@ namespace kvtc {
 
 constexpr uint32_t kRansL = 1u << 16;  // lower end of the normalised rANS state interval
 constexpr int kHeaderBytes = 256;
-constexpr int kDirEntry = 16;  // u64 offset, u32 size, u32 record mode
-constexpr int kContainerVersion = 2;
+constexpr int kDirEntry = 32;  // u64 offset, u32 size, u32 record mode, u64 x 2 record checksum
+constexpr int kContainerVersion = 3;
+constexpr int kCsumField = 200;     // header bytes [200, 216): checksum of the fixed part
+constexpr int kCsumParts = 1024;    // workgroups (partial sums) of a fixed-part checksum
 constexpr int kBlkTokens = 1024;  // tokens of a transform work block (at most)
 constexpr int kMaxTilesPerRec = 32;
 
@@ -61,6 +63,7 @@ struct WsLayout {
   int64_t rec_pos;     // u64 [n_recs]
   int64_t kprime;      // bf16 [L][H][T_mid][D]: mid-region keys with RoPE removed (head_dim 128 bf16 path)
   int64_t fixed;       // paged batch: staging of the container's fixed part [chunks_off]
+  int64_t csum;        // u64 x 2 [kCsumParts]: partial checksums of the fixed part
   int64_t total;
 };
 
@@ -205,6 +208,7 @@ KVTC_HD inline WsLayout make_ws_layout(const kvtc_config& c, const Layout& lo, b
   w.rec_mode = take(at, (int64_t)lo.n_recs * 4);
   w.rec_pos = take(at, (int64_t)lo.n_recs * 8 + 8);
   w.fixed = take(at, paged ? lo.chunks_off : 0);
+  w.csum = take(at, (int64_t)kCsumParts * 16);
   w.total = at;
   return w;
 }
@@ -343,6 +347,9 @@ hipError_t launch_quant128(const Params& p, hipStream_t s);  // head_dim 128 bf1
 hipError_t launch_rans_encode_chunks(const Params& p, hipStream_t s, bool with_raw = false);
 hipError_t launch_assemble(const Params& p, const uint8_t* hdr, hipStream_t s);
 hipError_t launch_dec_check(const Params& p, const uint8_t* hdr, hipStream_t s);
+// checksum of the fixed part: written into the header (encode = 1) or
+// checked against it (encode = 0)
+hipError_t launch_csum(const Params& p, int encode, hipStream_t s);
 hipError_t launch_rans_decode_chunks(const Params& p, hipStream_t s, bool with_raw = false);
 hipError_t launch_dec_transform(const Params& p, hipStream_t s);
 hipError_t launch_coeffs(const Params& p, int sec_begin, int sec_end, float* out, float* r_out,
@@ -372,6 +379,49 @@ __device__ inline uint16_t f32_to_bf16(float f) {
 }
 
 __device__ inline float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+// ---- integrity checksum ("Quantum-Aware Tensor Compression", QATC
+// transport: an aggregate checksum; damaged payloads are refused before
+// restore).  Over the little-endian 32-bit words w_j of a range:
+// A = sum w_j and B = sum (j + 1) w_j, both modulo the prime 2^61 - 1.
+constexpr uint64_t kCsumP = (1ull << 61) - 1;
+
+__device__ __forceinline__ uint64_t mod61(uint64_t x) {  // x < 2^64 -> [0, P)
+  x = (x & kCsumP) + (x >> 61);
+  return x >= kCsumP ? x - kCsumP : x;
+}
+
+__device__ __forceinline__ uint64_t mulmod61(uint64_t a, uint64_t b) {  // a, b < 2^61
+  const uint64_t lo = a * b, hi = __umul64hi(a, b);
+  // a b = hi 2^64 + lo = (8 hi) 2^61 + lo, and 2^61 = 1 (mod P)
+  return mod61((lo & kCsumP) + (lo >> 61) + (hi << 3));
+}
+
+// Adds word w at index j of the range to a thread's partial sums.
+__device__ __forceinline__ void csum_add(uint64_t& A, uint64_t& B, uint64_t j, uint32_t w) {
+  A = mod61(A + w);
+  B = mod61(B + mulmod61(j + 1, w));
+}
+
+// Sum of the partials of a whole workgroup (at most 16 waves) in thread 0;
+// `sh` holds 32 u64 of LDS.  Every thread of the workgroup must call it.
+__device__ inline void csum_block_reduce(uint64_t& A, uint64_t& B, uint64_t* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    A = mod61(A + __shfl_xor(A, o, 64));
+    B = mod61(B + __shfl_xor(B, o, 64));
+  }
+  if (lane == 0) { sh[wave] = A; sh[16 + wave] = B; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < (int)((blockDim.x + 63) >> 6); ++k) {
+      A = mod61(A + sh[k]);
+      B = mod61(B + sh[16 + k]);
+    }
+  }
+  __syncthreads();
+}
 
 __device__ inline void set_status(uint8_t* ws, const WsLayout& w, uint32_t code) {
   atomicOr(reinterpret_cast<uint32_t*>(ws + w.status), 1u << code);

@@ -243,7 +243,20 @@ def test_damaged_containers_are_refused():
     for pos in rng.integers(w0, w0 + 2 * nw0, 12):
         bad = bytearray(data); bad[pos] ^= 0x5A
         caught += status(bad) == kvtc.ERR_CORRUPT
-    assert caught >= 9
+    assert caught == 12  # the record checksum catches every one
+    # every byte of the container is under a checksum: the side information
+    # (zero points and scales), the raw windows, the directory, the records
+    # and the checksum field itself; the oracle refuses the same damage
+    h = np.frombuffer(data[:256], np.uint8)
+    side_off, raw_off, raw_bytes, dir_off, chunks_off = (
+        int(h[a: a + 8].view(np.uint64)[0]) for a in (120, 136, 144, 152, 160))
+    regions = [(side_off + 128, raw_off), (raw_off, raw_off + raw_bytes), (dir_off, chunks_off),
+               (chunks_off, len(data)), (200, 216)]
+    for a, b in regions:
+        for pos in rng.integers(a, b, 3):
+            bad = bytearray(data); bad[int(pos)] ^= 1 << int(rng.integers(0, 8))
+            assert status(bad) == kvtc.ERR_CORRUPT, (a, b, int(pos))
+            assert orc.decode_status(cfg, bytes(bad), basis, T) == orc.ERR_CORRUPT
     d0 = orc_dir_off(data)
     for mode in (1, 2):  # a record mode that disagrees with the record, or none at all
         bad = bytearray(data); bad[d0 + 12: d0 + 16] = np.uint32(mode).tobytes()
