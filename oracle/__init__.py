@@ -133,7 +133,10 @@ def _p(a: np.ndarray | None):
     if a is None:
         return None
     assert a.flags["C_CONTIGUOUS"]
-    return ctypes.c_void_p(a.ctypes.data)
+    # data_as keeps a reference to the array, so a temporary passed straight
+    # into a call (np.ascontiguousarray(...) of a strided view) stays alive
+    # until the call returns
+    return a.ctypes.data_as(ctypes.c_void_p)
 
 
 # --------------------------------------------------------------------------

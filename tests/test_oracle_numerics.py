@@ -325,3 +325,16 @@ def test_pack_round_trip(orc):
         data = orc.pack(q, bits)
         assert data.size == sum(4 * ((n * int(b) + 31) // 32) for b in bits if b)
         assert np.array_equal(orc.unpack(data, n, bits), q)
+
+
+def test_binding_keeps_strided_arguments_alive(orc):
+    """Strided views are copied to contiguous temporaries on their way into
+    the C routines; each temporary must outlive the call (three of them at
+    once here, whose memory would otherwise be reused by the next)."""
+    rng = np.random.default_rng(3)
+    st = rng.normal(size=(64, 4)).astype(np.float32)
+    st[:, 3] = st[:, 2] + np.abs(st[:, 3]) + 1
+    bits = np.full(64, 3, np.uint8)
+    z, s, _ = orc.side_info(bits, st[:, 0], st[:, 2], st[:, 3])
+    assert np.array_equal(z, st[:, 2])
+    assert np.array_equal(s, ((st[:, 3].astype(np.float64) - st[:, 2]) / 7).astype(np.float32))
