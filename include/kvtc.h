@@ -342,6 +342,47 @@ kvtc_status kvtc_test_packed_tiles(kvtc_plan_t plan, const void* ws, int32_t T, 
                                    void* out, size_t out_bytes, int32_t* blocks, size_t* slot_bytes,
                                    hipStream_t stream);
 
+/* Stage hook, RoPE undo ("KVTC: The Open-Source KV Cache Codec That Treats
+ * LLM Memory Like Media", Why RoPE Has to Be Reversed First): the middle
+ * keys of k (device [L,H,T,D] bf16) with the rotation removed and rounded to
+ * bf16, as the encoder's first pass computes them, into out (device,
+ * [L,H,T_mid,D] bf16, out_bytes >= L H T_mid D 2).  ws: a workspace of
+ * kvtc_workspace_size() bytes.  Only the bf16 head_dim-128 PCA path with
+ * RoPE keys runs this as a pass of its own (elsewhere it is fused):
+ * KVTC_ERR_UNSUPPORTED otherwise. */
+kvtc_status kvtc_test_rope(kvtc_plan_t plan, const void* k, int32_t T, void* ws, size_t ws_bytes, void* out,
+                           size_t out_bytes, hipStream_t stream);
+
+/* Stage hook, bit allocation and side information (same page, Bit Budget Is
+ * Not Fair; How the Pipeline Works: widths, scales and zero points per
+ * section): from per-component statistics stats (host, [n_sections][D][4]
+ * f32: mean, variance, min, max) to the section records written to side_out
+ * (device, >= n_sections 9 D bytes: u8 widths[D], f32 zero[D], f32
+ * scale[D] per section) by the allocation kernels of the plan's scope.  ws:
+ * a workspace of kvtc_workspace_size(T) bytes (T fixes T_mid, which decides
+ * the empty-middle case). */
+kvtc_status kvtc_test_alloc(kvtc_plan_t plan, int32_t T, const float* stats, void* ws, size_t ws_bytes,
+                            void* side_out, size_t side_bytes, hipStream_t stream);
+
+/* Stage hook, the encoder up to quantisation and packing (same page, How the
+ * Pipeline Works: RoPE undo -> transform -> bit allocation -> quantization):
+ * the encode passes before entropy coding.  The section records go to out
+ * (device, cap >= the raw-window offset of the layout) at their container
+ * offsets, the packed tiles stay in ws (read them with
+ * kvtc_test_packed_tiles). */
+kvtc_status kvtc_test_quant_pack(kvtc_plan_t plan, const void* k, const void* v, int32_t T, void* out, size_t cap,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Stage hook, dequantisation and inverse projection ("Codec-Gauge", Problem
+ * Statement and Overview: Z^ = D(B_c), X^ = G^-1 Z^; RoPE re-applied to
+ * keys): the decode transform alone, from the packed tiles in ws (as
+ * kvtc_test_quant_pack or a record decode left them) and the section records
+ * of in (device, in_bytes >= the raw-window offset) into the middle rows of
+ * k_out, v_out (device [L,H,T,D] in out_dtype); other rows are untouched. */
+kvtc_status kvtc_test_dequant_project(kvtc_plan_t plan, const void* in, size_t in_bytes, int32_t T, void* ws,
+                                      size_t ws_bytes, void* k_out, void* v_out, int32_t out_dtype,
+                                      hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

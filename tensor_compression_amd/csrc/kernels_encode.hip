@@ -1344,8 +1344,12 @@ __device__ __forceinline__ uint64_t global_key(int32_t ex, uint32_t man, int k, 
 // MODE 0: statistics, the section's own greedy widths and side information.
 // MODE 1 (one budget over all sections): statistics only, for k_alloc_global.
 // MODE 2: statistics, widths from the global threshold key, side information.
+// MODE 3 / 4: as 0 / 2 from statistics already in the workspace (the
+// allocation stage hook).
 template <int MODE>
 __global__ __launch_bounds__(64) void k_enc_alloc(const Params p0) {
+  constexpr bool FROM_STATS = MODE >= 3;
+  constexpr bool GLOBAL_W = MODE == 2 || MODE == 4;
   const Params p = at_seq(p0, blockIdx.z);
   const int u = blockIdx.x;
   const int D = p.D;
@@ -1359,6 +1363,13 @@ __global__ __launch_bounds__(64) void k_enc_alloc(const Params p0) {
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const int i = lane + 64 * c;
+    if (FROM_STATS) {
+      if (c < NC) {
+        const float4 st4 = reinterpret_cast<const float4*>(p.ws + p.w.sec_stats)[(int64_t)u * D + i];
+        mu[c] = st4.x; var[c] = st4.y; mn[c] = st4.z; mx[c] = st4.w;
+      }
+      continue;
+    }
     if (c < NC && N > 0) {
       double a = 0.0, b = 0.0;
       float lo = INFINITY, hi = -INFINITY;
@@ -1406,7 +1417,7 @@ __global__ __launch_bounds__(64) void k_enc_alloc(const Params p0) {
   }
   // ---- bit widths ----
   uint32_t bits[2] = {0u, 0u};
-  if (MODE == 2) {
+  if (GLOBAL_W) {
     // every k whose key reaches the threshold (keys fall as k grows)
     const uint64_t thr = *reinterpret_cast<const uint64_t*>(p.ws + p.w.status + kGlobalThrOff);
 #pragma unroll
@@ -1633,6 +1644,23 @@ __global__ __launch_bounds__(1024) void k_alloc_global(const Params p0) {
     __syncthreads();
   }
   if (tid == 0) *thr_out = ((uint64_t)Et << kGKeyLow) | prefix;
+}
+
+hipError_t launch_alloc_from_stats(const Params& p, hipStream_t s) {
+  if (p.alloc_scope == 1 && p.transform == KVTC_PCA) {
+    hipLaunchKernelGGL(k_alloc_global, dim3(1, 1, seq_grid(p)), dim3(1024), 0, s, p);
+    hipLaunchKernelGGL(k_enc_alloc<4>, dim3(p.n_sections, 1, seq_grid(p)), dim3(64), 0, s, p);
+  } else {
+    hipLaunchKernelGGL(k_enc_alloc<3>, dim3(p.n_sections, 1, seq_grid(p)), dim3(64), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_unrope(const Params& p, hipStream_t s) {
+  if (!(p.D == 128 && p.dtype == KVTC_BF16 && p.transform == KVTC_PCA && p.rope_keys && (p.tile_tokens % 64) == 0))
+    return hipErrorInvalidValue;
+  if (p.T_mid > 0) hipLaunchKernelGGL(k_unrope128, dim3((p.T_mid + 15) / 16, p.L, seq_grid(p)), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_enc_alloc(const Params& p, hipStream_t s) {

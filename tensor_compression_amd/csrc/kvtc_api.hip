@@ -747,4 +747,78 @@ kvtc_status kvtc_test_packed_tiles(kvtc_plan_t plan, const void* ws, int32_t T, 
   return KVTC_OK;
 }
 
+kvtc_status kvtc_test_rope(kvtc_plan_t plan, const void* k, int32_t T, void* ws, size_t ws_bytes, void* out,
+                           size_t out_bytes, hipStream_t stream) {
+  if (!plan || !k || !ws || !out) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* pl = (PlanImpl*)plan;
+  if (T < 0 || T > pl->cfg.max_tokens) return KVTC_ERR_INVALID_ARG;
+  const kvtc_config& c = pl->cfg;
+  if (!(c.head_dim == 128 && c.dtype == KVTC_BF16 && c.transform == KVTC_PCA && c.rope_keys && c.tile_tokens % 64 == 0))
+    return KVTC_ERR_UNSUPPORTED;
+  Layout lo = make_layout(c, T);
+  WsLayout w = make_ws_layout(c, lo);
+  if ((int64_t)ws_bytes < w.total) return KVTC_ERR_CAPACITY;
+  const size_t n = (size_t)c.layers * c.kv_heads * lo.T_mid * c.head_dim * 2;
+  if (out_bytes < n) return KVTC_ERR_CAPACITY;
+  Params p = make_params(*pl, lo, w);
+  p.k = k; p.ws = (uint8_t*)ws;
+  HIP_TRY(launch_unrope(p, stream));
+  if (n) HIP_TRY(hipMemcpyAsync(out, (const uint8_t*)ws + w.kprime, n, hipMemcpyDeviceToDevice, stream));
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_test_alloc(kvtc_plan_t plan, int32_t T, const float* stats, void* ws, size_t ws_bytes,
+                            void* side_out, size_t side_bytes, hipStream_t stream) {
+  if (!plan || !stats || !ws || !side_out) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* pl = (PlanImpl*)plan;
+  if (T < 0 || T > pl->cfg.max_tokens) return KVTC_ERR_INVALID_ARG;
+  Layout lo = make_layout(pl->cfg, T);
+  WsLayout w = make_ws_layout(pl->cfg, lo);
+  if ((int64_t)ws_bytes < w.total) return KVTC_ERR_CAPACITY;
+  const size_t n = (size_t)lo.n_sections * pl->cfg.head_dim;
+  if (side_bytes < n * 9) return KVTC_ERR_CAPACITY;
+  HIP_TRY(hipMemcpyAsync((uint8_t*)ws + w.sec_stats, stats, n * 16, hipMemcpyHostToDevice, stream));
+  Params p = make_params(*pl, lo, w);
+  p.ws = (uint8_t*)ws;
+  p.out = (uint8_t*)side_out - lo.side_off;  // the section records land at side_out
+  HIP_TRY(launch_alloc_from_stats(p, stream));
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_test_quant_pack(kvtc_plan_t plan, const void* k, const void* v, int32_t T, void* out, size_t cap,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!plan || !k || !v || !out || !ws) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* pl = (PlanImpl*)plan;
+  if (T < 0 || T > pl->cfg.max_tokens) return KVTC_ERR_INVALID_ARG;
+  if (misaligned(k) || misaligned(v) || misaligned(out) || misaligned(ws)) return KVTC_ERR_INVALID_ARG;
+  Layout lo = make_layout(pl->cfg, T);
+  WsLayout w = make_ws_layout(pl->cfg, lo);
+  if ((int64_t)ws_bytes < w.total || (int64_t)cap < lo.raw_off) return KVTC_ERR_CAPACITY;
+  Params p = make_params(*pl, lo, w);
+  p.k = k; p.v = v; p.out = (uint8_t*)out; p.out_final = p.out; p.cap = (int64_t)cap; p.ws = (uint8_t*)ws;
+  if (lo.n_blks == 0) return KVTC_OK;
+  HIP_TRY(launch_enc_transform(p, 0, stream));
+  HIP_TRY(launch_enc_alloc(p, stream));
+  HIP_TRY(launch_enc_transform(p, 1, stream));
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_test_dequant_project(kvtc_plan_t plan, const void* in, size_t in_bytes, int32_t T, void* ws,
+                                      size_t ws_bytes, void* k_out, void* v_out, int32_t out_dtype,
+                                      hipStream_t stream) {
+  if (!plan || !in || !ws || !k_out || !v_out) return KVTC_ERR_INVALID_ARG;
+  PlanImpl* pl = (PlanImpl*)plan;
+  const kvtc_status st = decode_args(pl, in, T, k_out, v_out, out_dtype);
+  if (st != KVTC_OK) return st;
+  Layout lo = make_layout(pl->cfg, T);
+  WsLayout w = make_ws_layout(pl->cfg, lo);
+  if ((int64_t)ws_bytes < w.total || (int64_t)in_bytes < lo.raw_off) return KVTC_ERR_CAPACITY;
+  Params p = make_params(*pl, lo, w);
+  p.in = (const uint8_t*)in; p.cap = (int64_t)in_bytes; p.ws = (uint8_t*)ws;
+  p.k_out = k_out; p.v_out = v_out; p.out_dtype = out_dtype;
+  if (lo.n_blks == 0) return KVTC_OK;
+  HIP_TRY(launch_dec_transform(p, stream));
+  return KVTC_OK;
+}
+
 }  // extern "C"

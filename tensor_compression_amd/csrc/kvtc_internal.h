@@ -350,6 +350,11 @@ hipError_t launch_dec_check(const Params& p, const uint8_t* hdr, hipStream_t s);
 // checksum of the fixed part: written into the header (encode = 1) or
 // checked against it (encode = 0)
 hipError_t launch_csum(const Params& p, int encode, hipStream_t s);
+// stage hooks: allocation and side information from the statistics in the
+// workspace; RoPE undo of the middle keys into the workspace (bf16 head_dim
+// 128 path)
+hipError_t launch_alloc_from_stats(const Params& p, hipStream_t s);
+hipError_t launch_unrope(const Params& p, hipStream_t s);
 hipError_t launch_rans_decode_chunks(const Params& p, hipStream_t s, bool with_raw = false);
 hipError_t launch_dec_transform(const Params& p, hipStream_t s);
 hipError_t launch_coeffs(const Params& p, int sec_begin, int sec_end, float* out, float* r_out,

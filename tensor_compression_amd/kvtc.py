@@ -94,6 +94,16 @@ EXPORTS = {
     "kvtc_test_packed_tiles": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                               ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "kvtc_test_rope": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "kvtc_test_alloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "kvtc_test_quant_pack": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                            ctypes.c_void_p]),
+    "kvtc_test_dequant_project": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                                 ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
+                                                 ctypes.c_int32, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -317,6 +327,45 @@ class Plan:
                                             _stream()), "kvtc_test_packed_tiles")
         torch.cuda.current_stream().synchronize()
         return out[: nb.value * sb.value].view(nb.value, sb.value)
+
+
+    def rope_stage(self, K: torch.Tensor, ws: torch.Tensor, T_mid: int) -> torch.Tensor:
+        """kvtc_test_rope: the middle keys un-rotated, bf16 bits int16 [L, H, T_mid, D]."""
+        L, H, T, D = K.shape
+        out = torch.zeros((L, H, max(T_mid, 1), D), dtype=torch.int16, device=self.device)
+        _check(lib().kvtc_test_rope(self.handle, _ptr(K), T, _ptr(ws), ws.numel(), _ptr(out), out.numel() * 2,
+                                    _stream()), "kvtc_test_rope")
+        torch.cuda.current_stream().synchronize()
+        return out[:, :, :T_mid]
+
+    def alloc_stage(self, T: int, stats, ws: torch.Tensor):
+        """kvtc_test_alloc: host stats float32 [n_sections, D, 4] -> (widths u8,
+        zero f32, scale f32), each [n_sections, D]."""
+        import numpy as np
+        st = np.ascontiguousarray(stats, np.float32)
+        n, D = st.shape[0], st.shape[1]
+        side = torch.zeros(n * 9 * D, dtype=torch.uint8, device=self.device)
+        _check(lib().kvtc_test_alloc(self.handle, T, st.ctypes.data_as(ctypes.c_void_p), _ptr(ws), ws.numel(),
+                                     _ptr(side), side.numel(), _stream()), "kvtc_test_alloc")
+        torch.cuda.current_stream().synchronize()
+        rec = side.cpu().numpy().reshape(n, 9 * D)
+        return rec[:, :D].copy(), rec[:, D: 5 * D].copy().view(np.float32), rec[:, 5 * D:].copy().view(np.float32)
+
+    def quant_pack_stage(self, K: torch.Tensor, V: torch.Tensor, ws: torch.Tensor, out: torch.Tensor):
+        """kvtc_test_quant_pack: encode passes up to packing; section records
+        into `out`, packed tiles left in ws."""
+        _check(lib().kvtc_test_quant_pack(self.handle, _ptr(K), _ptr(V), K.shape[2], _ptr(out), out.numel(),
+                                          _ptr(ws), ws.numel(), _stream()), "kvtc_test_quant_pack")
+        torch.cuda.current_stream().synchronize()
+
+    def dequant_project_stage(self, side: torch.Tensor, T: int, ws: torch.Tensor, k_out: torch.Tensor,
+                              v_out: torch.Tensor, out_dtype: int):
+        """kvtc_test_dequant_project: the decode transform from ws's packed
+        tiles and the section records in `side` into the middle rows."""
+        _check(lib().kvtc_test_dequant_project(self.handle, _ptr(side), side.numel(), T, _ptr(ws), ws.numel(),
+                                               _ptr(k_out), _ptr(v_out), out_dtype, _stream()),
+               "kvtc_test_dequant_project")
+        torch.cuda.current_stream().synchronize()
 
 
 def freq_tables(counts: torch.Tensor, alphabet: torch.Tensor, scale_bits: int):
