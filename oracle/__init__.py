@@ -678,6 +678,64 @@ def fit_pca_basis(cfg: dict, k, v, t0: int | None = None, t1: int | None = None)
     return out
 
 
+def gauge_block(A: np.ndarray) -> np.ndarray:
+    """One orthogonal gauge block G = exp(A - A^T) ("Codec-Gauge: Learning
+    Compression-Friendly Gauges for Transformer KV Caches", Gauge
+    Parameterization and Training: a skew-symmetric generator per channel
+    group), in fp64 by the matrix exponential of scipy."""
+    from scipy.linalg import expm
+    A = np.asarray(A, np.float64)
+    return expm(A - A.T)
+
+
+def grouped_gauge(D: int, g: int, generators) -> np.ndarray:
+    """Block-diagonal gauge G = diag(exp(A_k - A_k^T)) over D / g groups of g
+    consecutive channels (same page, Gauge Parameterization: groups of g
+    channels, g in {8, 16, 32}); `generators` is [D / g, g, g] (the learned
+    parameters; here any given matrices, training is not part of the codec).
+    The frame is Z = G X, so as a basis (column i = component i) it enters
+    the pipeline as B = G^T.  Returns fp64 [D, D]."""
+    assert D % g == 0
+    G = np.zeros((D, D), np.float64)
+    for k in range(D // g):
+        G[k * g:(k + 1) * g, k * g:(k + 1) * g] = gauge_block(generators[k])
+    return G
+
+
+def random_gauge_generators(D: int, g: int, scale: float, seed: int) -> np.ndarray:
+    """Seeded normal generators [D / g, g, g] of standard deviation `scale`:
+    the random-gauge control of the same page (Compression Conditions)."""
+    rng = np.random.default_rng(seed)
+    return rng.normal(0.0, scale, (D // g, g, g))
+
+
+def grouped_klt_basis(cfg: dict, k, v, g: int, t0: int | None = None, t1: int | None = None) -> np.ndarray:
+    """The PCA/KLT control at group granularity (same page, Compression
+    Conditions: the uncentered second-moment eigenbasis computed per layer,
+    K/V and group): within each group of g consecutive channels the
+    eigenvectors of that group's block of the second moment, descending.
+    Block-diagonal fp32 [L, 2, D, D] like fit_pca_basis."""
+    full = fit_pca_basis(dict(cfg, basis_per_head=0), k, v, t0, t1)  # only for the shape
+    L, D = cfg["layers"], cfg["head_dim"]
+    H, T = cfg["kv_heads"], k.shape[2]
+    t0 = 0 if t0 is None else t0
+    t1 = T if t1 is None else t1
+    out = np.zeros_like(full)
+    for l in range(L):
+        for s in range(2):
+            acc = np.zeros((D, D), np.float64)
+            n = 0
+            for h in range(H):
+                x = section_rows(cfg, k, v, (l * 2 + s) * H + h, t0, t1).astype(np.float64)
+                acc += x.T @ x
+                n += x.shape[0]
+            S = acc / max(n, 1)
+            for q in range(D // g):
+                sl = slice(q * g, (q + 1) * g)
+                out[l, s, sl, sl] = _eig_basis(S[sl, sl])
+    return out
+
+
 def _eig_basis(S: np.ndarray) -> np.ndarray:
     w, V = np.linalg.eigh(S)
     order = np.argsort(-w, kind="stable")
