@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 METRIC = "encode+decode GB/s of raw bf16 KV at 2 bits/comp; ratio; % HBM roofline"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA of the MI355X
 
 
 def parse():
@@ -44,6 +45,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--chunk-tokens", type=int, default=4096)
     ap.add_argument("--tile-tokens", type=int, default=256)
+    ap.add_argument("--alloc-scope", type=int, default=0,
+                    help="0: each section spends its own bit budget; 1: one budget over all sections")
     ap.add_argument("--cpu-layers", type=int, default=8,
                     help="layers of the workload the CPU oracle baseline codes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -304,7 +307,7 @@ def run_paged(args, w):
 
     n_seqs = args.seqs if args.seqs is not None else w.n_seqs
     lens = synth.ragged_lengths(w, n_seqs)
-    over = dict(chunk_tokens=args.chunk_tokens, tile_tokens=args.tile_tokens)
+    over = dict(chunk_tokens=args.chunk_tokens, tile_tokens=args.tile_tokens, alloc_scope=args.alloc_scope)
     if args.bits is not None:
         over.update(bits_k=args.bits, bits_v=args.bits)
     kp, vp, table, lens = synth.generate_paged(w, device="cuda", lengths=lens, layers=args.layers)
@@ -499,8 +502,8 @@ def main():
         plan.profile(False)
     ph_ms = {k: float(np.mean(v)) for k, v in phases.items()}
     t_enc = sum(ph_ms.get(k, 0.0) for k in ("copy_raw", "enc_stats", "enc_alloc", "enc_quant_pack",
-                                             "rans_encode", "assemble"))
-    t_dec = sum(ph_ms.get(k, 0.0) for k in ("dec_check", "rans_decode", "dec_transform",
+                                             "rans_encode", "assemble", "enc_checksum"))
+    t_dec = sum(ph_ms.get(k, 0.0) for k in ("dec_check", "dec_checksum", "rans_decode", "dec_transform",
                                              "copy_raw_out"))
 
     # container accounting from the side records (bits) and the header
@@ -549,7 +552,7 @@ def main():
             "layers": L, "kv_heads": H, "tokens": T, "head_dim": D,
             "bits_per_component": cfg["bits_k"], "chunk_tokens": cfg["chunk_tokens"],
             "tile_tokens": cfg["tile_tokens"], "rans_lanes": cfg["rans_lanes"],
-            "rans_scale_bits": cfg["rans_scale_bits"],
+            "rans_scale_bits": cfg["rans_scale_bits"], "alloc_scope": cfg.get("alloc_scope", 0),
         },
         "raw_bytes": raw,
         "container_bytes": nbytes,
@@ -575,6 +578,20 @@ def main():
                            "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBPS, "traffic": traffic_from_profile(dom),
                            "algorithmic_bytes": alg[dom], "avg_ms": ph_ms[dom]}
+    if cfg["transform"] == 0 and ph_ms:
+        # the projections are the path's dense contractions: 2 D flops per
+        # coefficient (bf16 MFMA, fp32 accumulation) in the statistics pass,
+        # again in the quantiser (it recomputes rather than stores them) and
+        # in the inverse projection of the decoder
+        # (the quantiser and the decoder project only the components that
+        # carry codes: 2 D flops per coded coefficient)
+        coded = int((bits > 0).sum()) * T_mid
+        flops = {"enc_stats": 2 * D * N_mid, "enc_quant_pack": 2 * D * coded, "dec_transform": 2 * D * coded}
+        res["mfma_roofline"] = {
+            k: {"flops": flops[k], "achieved_tflops": flops[k] / (ph_ms[k] * 1e-3) / 1e12,
+                "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                "frac": flops[k] / (ph_ms[k] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+            for k in flops if k in ph_ms}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, cfg, K, V, basis, args.cpu_layers) \
             if basis is not None else None
