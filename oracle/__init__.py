@@ -93,6 +93,11 @@ def lib() -> ctypes.CDLL:
             "orc_alloc_greedy": (None, [P, i32, i32, i32, P]),
             "orc_alloc_greedy_heap": (None, [P, ctypes.c_int64, ctypes.c_int64, i32, P]),
             "orc_checksum": (None, [P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P, P]),
+            "orc_sq_check": (i32, [P, P]),
+            "orc_sq_code_bytes": (ctypes.c_int64, [P, P, i32]),
+            "orc_sq_range_pairs": (ctypes.c_int64, [P, P, i32]),
+            "orc_sq_encode": (i32, [P, P, P, P, i32, P, P, P]),
+            "orc_sq_decode": (i32, [P, P, P, P, i32, P, P, P]),
             "orc_alloc_dp": (f64, [P, i32, i32, i32, P]),
             "orc_distortion": (f64, [P, P, i32]),
             "orc_side_info": (None, [P, P, P, P, i32, P, P, P]),
@@ -144,6 +149,13 @@ def _p(a: np.ndarray | None):
 # --------------------------------------------------------------------------
 
 CONFIG_FIELDS = [f for f, _ in _Cfg._fields_]
+
+SQ_BLOCK, SQ_KIVI = 1, 2
+
+
+class _SqCfg(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("group", ctypes.c_int32), ("tile", ctypes.c_int32),
+                ("bits_k", ctypes.c_int32), ("bits_v", ctypes.c_int32)]
 
 
 def make_cfg(cfg: dict) -> _Cfg:
@@ -483,6 +495,44 @@ def checksum(data: bytes, skip_from: int = 0, skip_to: int = 0) -> tuple[int, in
     b = ctypes.c_uint64(0)
     lib().orc_checksum(_p(buf), len(buf), skip_from, skip_to, ctypes.byref(a), ctypes.byref(b))
     return a.value, b.value
+
+
+def sq_sizes(cfg: dict, sq: dict, T: int) -> tuple[int, int]:
+    """(code bytes, (zero, scale) pairs) of the scalar-quantiser path."""
+    c, q = make_cfg(cfg), _SqCfg(**sq)
+    return (int(lib().orc_sq_code_bytes(ctypes.byref(c), ctypes.byref(q), T)),
+            int(lib().orc_sq_range_pairs(ctypes.byref(c), ctypes.byref(q), T)))
+
+
+def sq_encode(cfg: dict, sq: dict, k, v, basis) -> tuple[np.ndarray, np.ndarray]:
+    """Scalar quantisers on gauge coordinates ([CG] Compression Conditions):
+    (codes uint8, ranges float32 [pairs, 2])."""
+    c, q = make_cfg(cfg), _SqCfg(**sq)
+    T = k.shape[2]
+    nb, nr = sq_sizes(cfg, sq, T)
+    if nb < 0:
+        raise OracleError(ERR_INVALID_ARG, "sq_encode")
+    codes = np.zeros(max(nb, 1), np.uint8)
+    ranges = np.zeros((max(nr, 1), 2), np.float32)
+    kk, vv = np.ascontiguousarray(k), np.ascontiguousarray(v)
+    b = np.ascontiguousarray(basis, np.float32)
+    st = lib().orc_sq_encode(ctypes.byref(c), ctypes.byref(q), _p(kk), _p(vv), T, _p(b), _p(codes), _p(ranges))
+    if st != OK:
+        raise OracleError(st, "sq_encode")
+    return codes[:nb], ranges[:nr]
+
+
+def sq_decode(cfg: dict, sq: dict, codes, ranges, T: int, basis) -> tuple[np.ndarray, np.ndarray]:
+    c, q = make_cfg(cfg), _SqCfg(**sq)
+    shape = (cfg["layers"], cfg["kv_heads"], T, cfg["head_dim"])
+    ko, vo = np.zeros(shape, np.float32), np.zeros(shape, np.float32)
+    cs = np.ascontiguousarray(codes, np.uint8)
+    rg = np.ascontiguousarray(ranges, np.float32)
+    b = np.ascontiguousarray(basis, np.float32)
+    st = lib().orc_sq_decode(ctypes.byref(c), ctypes.byref(q), _p(cs), _p(rg), T, _p(b), _p(ko), _p(vo))
+    if st != OK:
+        raise OracleError(st, "sq_decode")
+    return ko, vo
 
 
 def fnv1a64(data: bytes, h: int = 0xCBF29CE484222325) -> int:

@@ -1322,7 +1322,7 @@ int orc_encode(const orc_config* c, const void* k, const void* v, int32_t T,
    * then the greedy allocation over all of their components at once */
   uint8_t* bits_all = NULL;
   if (c->alloc_scope == 1 && lo.T_mid > 0) {
-    float* var_all = (float*)malloc(sizeof(float) * (size_t)lo.n_sections * D);
+    float* var_all = (float*)calloc((size_t)lo.n_sections * D, sizeof(float));
     bits_all = (uint8_t*)malloc((size_t)lo.n_sections * D);
     int64_t budget = 0;
     for (int32_t u = 0; u < lo.n_sections && st == ORC_OK; ++u) {
@@ -1640,4 +1640,182 @@ int orc_section_codes(const orc_config* c, const float* basis, const uint8_t* in
   for (int32_t ch = 0; ch < lo.chunks_per_sec && st == ORC_OK; ++ch)
     st = decode_chunk_codes(c, &lo, in, total, u, ch, bits, q_out + (int64_t)ch * c->chunk_tokens * D);
   return st;
+}
+
+/* ===================================================================== */
+/* Scalar quantisers on gauge coordinates ("Codec-Gauge", Compression     */
+/* Conditions: block-uniform ranges per T_b x d_l block; KIVI-style        */
+/* per-channel key and per-token value ranges; the same bit settings).    */
+/* ===================================================================== */
+
+int orc_sq_check(const orc_config* c, const orc_sq_config* q) {
+  int st = orc_check_config(c);
+  if (st != ORC_OK) return st;
+  if (c->transform != ORC_PCA) return ORC_ERR_INVALID_ARG;
+  if (q->kind != ORC_SQ_BLOCK && q->kind != ORC_SQ_KIVI) return ORC_ERR_INVALID_ARG;
+  if (q->group < 1 || c->head_dim % q->group) return ORC_ERR_INVALID_ARG;
+  if (q->tile < 1) return ORC_ERR_INVALID_ARG;
+  if (q->bits_k < 1 || q->bits_k > 8 || q->bits_v < 1 || q->bits_v > 8) return ORC_ERR_INVALID_ARG;
+  return ORC_OK;
+}
+
+/* Code bytes and (zero, scale) pairs of one section of kind s (0 keys,
+ * 1 values) over T tokens. */
+static int64_t sq_sec_codes(const orc_config* c, const orc_sq_config* q, int32_t T, int32_t s) {
+  return (int64_t)T * c->head_dim * (s == 0 ? q->bits_k : q->bits_v) / 8;
+}
+
+static int64_t sq_sec_ranges(const orc_config* c, const orc_sq_config* q, int32_t T, int32_t s) {
+  int64_t nt = ((int64_t)T + q->tile - 1) / q->tile, D = c->head_dim, g = q->group;
+  if (q->kind == ORC_SQ_BLOCK) return nt * (D / g);
+  return s == 0 ? nt * D : (int64_t)T * (D / g);
+}
+
+/* Offset of section u = (l 2 + s) H + h among sections whose sizes depend
+ * only on s. */
+static int64_t sq_sec_off(const orc_config* c, int32_t u, int64_t x0, int64_t x1) {
+  int32_t H = c->kv_heads, h = u % H, s = (u / H) % 2, l = u / (2 * H);
+  return (int64_t)l * H * (x0 + x1) + (s ? (int64_t)H * x0 : 0) + (int64_t)h * (s ? x1 : x0);
+}
+
+int64_t orc_sq_code_bytes(const orc_config* c, const orc_sq_config* q, int32_t T) {
+  if (orc_sq_check(c, q) != ORC_OK || T < 0) return -1;
+  return (int64_t)c->layers * c->kv_heads * (sq_sec_codes(c, q, T, 0) + sq_sec_codes(c, q, T, 1));
+}
+
+int64_t orc_sq_range_pairs(const orc_config* c, const orc_sq_config* q, int32_t T) {
+  if (orc_sq_check(c, q) != ORC_OK || T < 0) return -1;
+  return (int64_t)c->layers * c->kv_heads * (sq_sec_ranges(c, q, T, 0) + sq_sec_ranges(c, q, T, 1));
+}
+
+/* The range index (within its section) of coefficient (t, i) of kind s. */
+static int64_t sq_range_of(const orc_config* c, const orc_sq_config* q, int32_t s, int32_t t, int32_t i) {
+  int32_t D = c->head_dim, g = q->group;
+  int64_t ti = t / q->tile;
+  if (q->kind == ORC_SQ_BLOCK) return ti * (D / g) + i / g;
+  return s == 0 ? ti * D + i : (int64_t)t * (D / g) + i / g;
+}
+
+/* zero = min, scale = (max - min) / (2^b - 1) in fp64 rounded once, rcp =
+ * 1 / scale (0 for an empty step), as for a component's side information. */
+static void sq_range(float mn, float mx, int32_t b, float* zero, float* scale, float* rcp) {
+  float sc = (float)(((double)mx - (double)mn) / (double)((1u << b) - 1u));
+  float r = sc > 0.0f ? 1.0f / sc : 0.0f;
+  if (!(sc > 0.0f) || isinf(r)) {
+    sc = 0.0f;
+    r = 0.0f;
+  }
+  *zero = mn;
+  *scale = sc;
+  *rcp = r;
+}
+
+int orc_sq_encode(const orc_config* c, const orc_sq_config* q, const void* k, const void* v, int32_t T,
+                  const float* basis, uint8_t* codes, float* ranges) {
+  int st = orc_sq_check(c, q);
+  if (st != ORC_OK) return st;
+  if (T < 0 || !basis) return ORC_ERR_INVALID_ARG;
+  int32_t D = c->head_dim, H = c->kv_heads, n_sec = c->layers * 2 * H;
+  int64_t cb0 = sq_sec_codes(c, q, T, 0), cb1 = sq_sec_codes(c, q, T, 1);
+  int64_t nr0 = sq_sec_ranges(c, q, T, 0), nr1 = sq_sec_ranges(c, q, T, 1);
+  float* x = (float*)malloc(sizeof(float) * ((size_t)T * D + 1));
+  float* coef = (float*)malloc(sizeof(float) * ((size_t)T * D + 1));
+  float* Bp = (float*)malloc(sizeof(float) * (size_t)D * D);
+  float* mn = (float*)malloc(sizeof(float) * (size_t)(nr0 > nr1 ? nr0 : nr1) + 4);
+  float* mx = (float*)malloc(sizeof(float) * (size_t)(nr0 > nr1 ? nr0 : nr1) + 4);
+  for (int32_t u = 0; u < n_sec && st == ORC_OK; ++u) {
+    int32_t h = u % H, s = (u / H) % 2, l = u / (2 * H);
+    int32_t b = s == 0 ? q->bits_k : q->bits_v;
+    int64_t nr = s == 0 ? nr0 : nr1;
+    st = orc_section_rows(c, k, v, T, u, 0, T, x);
+    if (st != ORC_OK) break;
+    const float* B = basis_of(c, basis, l, s, h);
+    for (int64_t a = 0; a < (int64_t)D * D; ++a) Bp[a] = round_p(B[a], c->dtype);
+    for (int32_t t = 0; t < T; ++t) orc_project(x + (int64_t)t * D, Bp, D, coef + (int64_t)t * D);
+    /* ranges: min and max of each range's coefficients */
+    for (int64_t r = 0; r < nr; ++r) {
+      mn[r] = INFINITY;
+      mx[r] = -INFINITY;
+    }
+    for (int32_t t = 0; t < T; ++t)
+      for (int32_t i = 0; i < D; ++i) {
+        float cv = coef[(int64_t)t * D + i];
+        if (!isfinite(cv)) st = ORC_ERR_NONFINITE;
+        int64_t r = sq_range_of(c, q, s, t, i);
+        if (cv < mn[r]) mn[r] = cv;
+        if (cv > mx[r]) mx[r] = cv;
+      }
+    if (st != ORC_OK) break;
+    float* rg = ranges + 2 * sq_sec_off(c, u, nr0, nr1);
+    for (int64_t r = 0; r < nr; ++r) {
+      float z, sc, rc;
+      sq_range(mn[r], mx[r], b, &z, &sc, &rc);
+      rg[2 * r] = z;
+      rg[2 * r + 1] = sc;
+    }
+    /* codes: v = (c - zero) * rcp in fp32, q = clamp(rint(v), 0, 2^b - 1),
+     * token rows of D b bits, channel i at bits [i b, i b + b), LSB-first */
+    uint8_t* cs = codes + sq_sec_off(c, u, cb0, cb1);
+    memset(cs, 0, (size_t)(s == 0 ? cb0 : cb1));
+    for (int32_t t = 0; t < T; ++t)
+      for (int32_t i = 0; i < D; ++i) {
+        int64_t r = sq_range_of(c, q, s, t, i);
+        float z, sc, rc;
+        sq_range(mn[r], mx[r], b, &z, &sc, &rc);
+        float d = coef[(int64_t)t * D + i] - z;
+        float vv = d * rc;
+        float rq = nearbyintf(vv);
+        float hi = (float)((1u << b) - 1u);
+        if (rq < 0.0f) rq = 0.0f;
+        if (rq > hi) rq = hi;
+        uint32_t code = (uint32_t)rq;
+        int64_t bit = ((int64_t)t * D + i) * b;
+        for (int32_t e = 0; e < b; ++e)
+          if ((code >> e) & 1u) cs[(bit + e) >> 3] |= (uint8_t)(1u << ((bit + e) & 7));
+      }
+  }
+  free(x); free(coef); free(Bp); free(mn); free(mx);
+  return st;
+}
+
+int orc_sq_decode(const orc_config* c, const orc_sq_config* q, const uint8_t* codes, const float* ranges,
+                  int32_t T, const float* basis, float* k_out, float* v_out) {
+  int st = orc_sq_check(c, q);
+  if (st != ORC_OK) return st;
+  if (T < 0 || !basis) return ORC_ERR_INVALID_ARG;
+  int32_t D = c->head_dim, H = c->kv_heads, n_sec = c->layers * 2 * H;
+  int64_t cb0 = sq_sec_codes(c, q, T, 0), cb1 = sq_sec_codes(c, q, T, 1);
+  int64_t nr0 = sq_sec_ranges(c, q, T, 0), nr1 = sq_sec_ranges(c, q, T, 1);
+  float* Bp = (float*)malloc(sizeof(float) * (size_t)D * D);
+  float* cos_t = (float*)malloc(sizeof(float) * ((size_t)T * D / 2 + 1));
+  float* sin_t = (float*)malloc(sizeof(float) * ((size_t)T * D / 2 + 1));
+  orc_rope_table(T, D, c->rope_theta, cos_t, sin_t);
+  float chat[256], xr[256], y[256];
+  for (int32_t u = 0; u < n_sec; ++u) {
+    int32_t h = u % H, s = (u / H) % 2, l = u / (2 * H);
+    int32_t b = s == 0 ? q->bits_k : q->bits_v;
+    const float* B = basis_of(c, basis, l, s, h);
+    for (int64_t a = 0; a < (int64_t)D * D; ++a) Bp[a] = round_p(B[a], c->dtype);
+    const float* rg = ranges + 2 * sq_sec_off(c, u, nr0, nr1);
+    const uint8_t* cs = codes + sq_sec_off(c, u, cb0, cb1);
+    float* out = s == 0 ? k_out : v_out;
+    for (int32_t t = 0; t < T; ++t) {
+      for (int32_t i = 0; i < D; ++i) {
+        int64_t bit = ((int64_t)t * D + i) * b;
+        uint32_t code = 0;
+        for (int32_t e = 0; e < b; ++e) code |= (uint32_t)((cs[(bit + e) >> 3] >> ((bit + e) & 7)) & 1u) << e;
+        int64_t r = sq_range_of(c, q, s, t, i);
+        chat[i] = round_p(fmaf((float)code, rg[2 * r + 1], rg[2 * r]), c->dtype);
+      }
+      orc_unproject(chat, Bp, D, xr);
+      if (s == 0 && c->rope_keys) {
+        orc_rope_forward(xr, y, D, c->rope_style, cos_t + (int64_t)t * (D / 2), sin_t + (int64_t)t * (D / 2));
+      } else {
+        memcpy(y, xr, sizeof(float) * D);
+      }
+      memcpy(out + (((int64_t)l * H + h) * T + t) * D, y, sizeof(float) * D);
+    }
+  }
+  free(Bp); free(cos_t); free(sin_t);
+  return ORC_OK;
 }

@@ -161,6 +161,28 @@ int orc_section_rows(const orc_config* cfg, const void* k, const void* v, int32_
 int orc_section_coeffs(const orc_config* cfg, const void* k, const void* v, int32_t T,
                        const float* basis, int32_t section, float* c_out, float* r_out);
 
+/* ---- scalar quantisers on gauge coordinates --------------------------- */
+/* ("Codec-Gauge: Learning Compression-Friendly Gauges for Transformer KV
+ * Caches", Compression Conditions: block-uniform uses one range per
+ * T_b x d_l block; the KIVI-style path uses per-channel key and per-token
+ * value ranges; both at a fixed bit setting.)  Every token of the cache is
+ * coded; keys are un-rotated first and rotated back on decode. */
+#define ORC_SQ_BLOCK 1
+#define ORC_SQ_KIVI 2
+typedef struct {
+  int32_t kind;    /* ORC_SQ_BLOCK or ORC_SQ_KIVI */
+  int32_t group;   /* channels per range (d_l); divides head_dim */
+  int32_t tile;    /* tokens per range block (T_b) */
+  int32_t bits_k, bits_v;  /* code widths, 1..8 */
+} orc_sq_config;
+int orc_sq_check(const orc_config* c, const orc_sq_config* q);
+int64_t orc_sq_code_bytes(const orc_config* c, const orc_sq_config* q, int32_t T);
+int64_t orc_sq_range_pairs(const orc_config* c, const orc_sq_config* q, int32_t T);
+int orc_sq_encode(const orc_config* c, const orc_sq_config* q, const void* k, const void* v, int32_t T,
+                  const float* basis, uint8_t* codes, float* ranges);
+int orc_sq_decode(const orc_config* c, const orc_sq_config* q, const uint8_t* codes, const float* ranges,
+                  int32_t T, const float* basis, float* k_out, float* v_out);
+
 #ifdef __cplusplus
 }
 #endif
