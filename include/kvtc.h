@@ -383,6 +383,75 @@ kvtc_status kvtc_test_dequant_project(kvtc_plan_t plan, const void* in, size_t i
                                       size_t ws_bytes, void* k_out, void* v_out, int32_t out_dtype,
                                       hipStream_t stream);
 
+/* ---- scalar quantisers on gauge coordinates ------------------------------ */
+
+/* "Codec-Gauge: Learning Compression-Friendly Gauges for Transformer KV
+ * Caches", Compression Conditions: the gauge coordinates Z = G X also feed
+ * two scalar quantisers with one bit setting per cache type.  The plan's
+ * basis is the gauge (component i is column i of B = G^T: a grouped
+ * block-diagonal gauge, PCA/KLT or the identity); the plan's transform must
+ * be KVTC_PCA.  Every token of [0, T) is coded (no raw windows); keys are
+ * un-rotated first when the plan's keys carry RoPE.
+ *
+ *  KVTC_SQ_BLOCK  block-uniform: one range per block of `tile` tokens x
+ *                 `group` channels, keys and values alike (group = head_dim
+ *                 gives one range per T_b x d_l block)
+ *  KVTC_SQ_KIVI   KIVI-style: keys one range per channel over `tile`
+ *                 tokens, values one range per token over `group` channels
+ *
+ * A range over coefficients c has zero = min c and scale = (max c - min c) /
+ * (2^b - 1) (fp64, rounded once to fp32); rcp = 1 / scale in fp32, or 0 when
+ * scale is 0 or the reciprocal overflows.  A code is
+ * clamp(rint((c - zero) * rcp), 0, 2^b - 1) in fp32; decoding takes
+ * fma(code, scale, zero) rounded to bf16, applies X = B c and re-applies
+ * RoPE.  The coefficients come from bf16 MFMA products with fp32
+ * accumulation; a code whose pre-rounding value lies within the
+ * accumulation error of a rounding boundary is re-computed from the exact
+ * coefficient.
+ *
+ * Layout, sections u = (l 2 + s) H + h in order (s 0 keys, 1 values):
+ *  codes   per section T head_dim b_s / 8 bytes: token-major rows of
+ *          head_dim b_s bits, channel i at bits [i b, i b + b) of its row,
+ *          least significant bit first;
+ *  ranges  per section ceil(T / te) (head_dim / ce) fp32 (zero, scale)
+ *          pairs, index (t / te) (head_dim / ce) + i / ce, where (te, ce) is
+ *          (tile, group) for block-uniform, (tile, 1) for KIVI keys and
+ *          (1, group) for KIVI values.
+ *
+ * Supported: bf16 head_dim-128 plans with tile dividing 64 (otherwise
+ * KVTC_ERR_UNSUPPORTED).  group must divide head_dim, tile >= 1, bits 1..8
+ * (otherwise KVTC_ERR_INVALID_ARG). */
+enum { KVTC_SQ_BLOCK = 1, KVTC_SQ_KIVI = 2 };
+
+typedef struct kvtc_sq_config {
+  int32_t kind;    /* KVTC_SQ_BLOCK or KVTC_SQ_KIVI */
+  int32_t group;   /* channels per range (see above) */
+  int32_t tile;    /* tokens per range, T_b (see above) */
+  int32_t bits_k;  /* bits per key coefficient, 1..8 */
+  int32_t bits_v;  /* bits per value coefficient, 1..8 */
+} kvtc_sq_config;
+
+/* Code bytes and (zero, scale) pairs of a call over T tokens (host only). */
+kvtc_status kvtc_sq_sizes(kvtc_plan_t plan, const kvtc_sq_config* q, int32_t T, size_t* code_bytes,
+                          size_t* range_pairs);
+
+/* Quantise k, v (device [L,H,T,D] bf16) into codes (device, code_cap bytes)
+ * and ranges (device, range_cap pairs of fp32), laid out as above.  When
+ * status_dev (device, 4-byte aligned) is not NULL it is cleared and then
+ * gets bit KVTC_ERR_NONFINITE if a coefficient is NaN or infinite (codes
+ * and ranges are then undefined).  Asynchronous on `stream`. */
+kvtc_status kvtc_sq_encode(kvtc_plan_t plan, const kvtc_sq_config* q, const void* k, const void* v, int32_t T,
+                           void* codes, size_t code_cap, float* ranges, size_t range_cap, uint32_t* status_dev,
+                           hipStream_t stream);
+
+/* Reconstruct k_out, v_out (device [L,H,T,D] in out_dtype, KVTC_BF16 or
+ * KVTC_FP32 with a round-to-nearest-even cast) from codes (code_bytes) and
+ * ranges (range_pairs) written by kvtc_sq_encode under the same plan, sq
+ * configuration and T.  Asynchronous on `stream`. */
+kvtc_status kvtc_sq_decode(kvtc_plan_t plan, const kvtc_sq_config* q, const void* codes, size_t code_bytes,
+                           const float* ranges, size_t range_pairs, int32_t T, void* k_out, void* v_out,
+                           int32_t out_dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

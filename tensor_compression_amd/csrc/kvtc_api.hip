@@ -821,4 +821,89 @@ kvtc_status kvtc_test_dequant_project(kvtc_plan_t plan, const void* in, size_t i
   return KVTC_OK;
 }
 
+// ---- scalar quantisers on gauge coordinates --------------------------------
+
+static kvtc_status sq_params(const PlanImpl* pl, const kvtc_sq_config* q, int32_t T, SqParams* sp) {
+  if (!q) return KVTC_ERR_INVALID_ARG;
+  const kvtc_config& c = pl->cfg;
+  if (c.transform != KVTC_PCA) return KVTC_ERR_INVALID_ARG;
+  if (q->kind != KVTC_SQ_BLOCK && q->kind != KVTC_SQ_KIVI) return KVTC_ERR_INVALID_ARG;
+  if (q->group < 1 || c.head_dim % q->group) return KVTC_ERR_INVALID_ARG;
+  if (q->tile < 1) return KVTC_ERR_INVALID_ARG;
+  if (q->bits_k < 1 || q->bits_k > 8 || q->bits_v < 1 || q->bits_v > 8) return KVTC_ERR_INVALID_ARG;
+  if (T < 0 || T > c.max_tokens) return KVTC_ERR_INVALID_ARG;
+  // the kernels run 64-token spans of head_dim 128 bf16 rows on MFMA; a
+  // range may not straddle a span
+  if (c.head_dim != 128 || c.dtype != KVTC_BF16 || (64 % q->tile)) return KVTC_ERR_UNSUPPORTED;
+  SqParams p{};
+  p.L = c.layers; p.H = c.kv_heads; p.T = T;
+  p.basis_per_head = c.basis_per_head; p.rope_keys = c.rope_keys; p.rope_style = c.rope_style;
+  p.bits[0] = q->bits_k; p.bits[1] = q->bits_v;
+  const bool block = q->kind == KVTC_SQ_BLOCK;
+  p.te[0] = q->tile; p.ce[0] = block ? q->group : 1;          // keys
+  p.te[1] = block ? q->tile : 1; p.ce[1] = q->group;          // values
+  for (int s = 0; s < 2; ++s) {
+    p.code_bytes[s] = (int64_t)T * c.head_dim * p.bits[s] / 8;
+    p.n_ranges[s] = ((int64_t)T + p.te[s] - 1) / p.te[s] * (c.head_dim / p.ce[s]);
+  }
+  p.mfma_err = 24.0f * 0x1p-24f * pl->max_col_norm;  // as for the codec's projection
+  p.basis_t = (const uint16_t*)pl->basis_t;
+  p.basis = (const uint16_t*)pl->basis;
+  p.rope = pl->rope;
+  *sp = p;
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_sq_sizes(kvtc_plan_t plan, const kvtc_sq_config* q, int32_t T, size_t* code_bytes,
+                          size_t* range_pairs) {
+  if (!plan || !code_bytes || !range_pairs) return KVTC_ERR_INVALID_ARG;
+  SqParams p;
+  const kvtc_status st = sq_params((const PlanImpl*)plan, q, T, &p);
+  if (st != KVTC_OK) return st;
+  const int64_t LH = (int64_t)p.L * p.H;
+  *code_bytes = (size_t)(LH * (p.code_bytes[0] + p.code_bytes[1]));
+  *range_pairs = (size_t)(LH * (p.n_ranges[0] + p.n_ranges[1]));
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_sq_encode(kvtc_plan_t plan, const kvtc_sq_config* q, const void* k, const void* v, int32_t T,
+                           void* codes, size_t code_cap, float* ranges, size_t range_cap, uint32_t* status_dev,
+                           hipStream_t stream) {
+  if (!plan) return KVTC_ERR_INVALID_ARG;
+  SqParams p;
+  const kvtc_status st = sq_params((const PlanImpl*)plan, q, T, &p);
+  if (st != KVTC_OK) return st;
+  if (T > 0 && (!k || !v || !codes || !ranges)) return KVTC_ERR_INVALID_ARG;
+  if (misaligned(k) || misaligned(v) || misaligned(codes) || misaligned(ranges) || ((uintptr_t)status_dev & 3u))
+    return KVTC_ERR_INVALID_ARG;
+  const int64_t LH = (int64_t)p.L * p.H;
+  if ((int64_t)code_cap < LH * (p.code_bytes[0] + p.code_bytes[1]) ||
+      (int64_t)range_cap < LH * (p.n_ranges[0] + p.n_ranges[1]))
+    return KVTC_ERR_CAPACITY;
+  p.k = (const uint16_t*)k; p.v = (const uint16_t*)v;
+  p.codes = (uint8_t*)codes; p.ranges = ranges; p.status = status_dev;
+  HIP_TRY(launch_sq_encode(p, stream));
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_sq_decode(kvtc_plan_t plan, const kvtc_sq_config* q, const void* codes, size_t code_bytes,
+                           const float* ranges, size_t range_pairs, int32_t T, void* k_out, void* v_out,
+                           int32_t out_dtype, hipStream_t stream) {
+  if (!plan) return KVTC_ERR_INVALID_ARG;
+  SqParams p;
+  const kvtc_status st = sq_params((const PlanImpl*)plan, q, T, &p);
+  if (st != KVTC_OK) return st;
+  if (out_dtype != KVTC_BF16 && out_dtype != KVTC_FP32) return KVTC_ERR_INVALID_ARG;
+  if (T > 0 && (!codes || !ranges || !k_out || !v_out)) return KVTC_ERR_INVALID_ARG;
+  if (misaligned(codes) || misaligned(ranges) || misaligned(k_out) || misaligned(v_out)) return KVTC_ERR_INVALID_ARG;
+  const int64_t LH = (int64_t)p.L * p.H;
+  if ((int64_t)code_bytes < LH * (p.code_bytes[0] + p.code_bytes[1]) ||
+      (int64_t)range_pairs < LH * (p.n_ranges[0] + p.n_ranges[1]))
+    return KVTC_ERR_CAPACITY;
+  p.codes = (uint8_t*)codes; p.ranges = (float*)ranges;
+  p.k_out = k_out; p.v_out = v_out; p.out_dtype = out_dtype;
+  HIP_TRY(launch_sq_decode(p, stream));
+  return KVTC_OK;
+}
+
 }  // extern "C"

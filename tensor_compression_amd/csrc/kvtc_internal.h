@@ -277,6 +277,28 @@ struct Params {
 
 constexpr int kPageTokens = 16;
 
+// One call of the scalar quantisers on gauge coordinates (kernels_sq.hip).
+// Every token of [0, T) is coded.  A range is a block of te tokens x ce
+// channels of one section: block-uniform (tile, group), KIVI keys (tile, 1),
+// KIVI values (1, group).  Index [s]: the section kind, 0 keys, 1 values.
+struct SqParams {
+  int32_t L, H, T, basis_per_head, rope_keys, rope_style, out_dtype;
+  int32_t bits[2], te[2], ce[2];
+  int64_t code_bytes[2];  // bytes of one section's codes
+  int64_t n_ranges[2];    // (zero, scale) pairs of one section
+  float mfma_err;         // |c_mfma - c_exact| <= mfma_err * ||x||_2
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* basis_t;  // component-major [n_basis][i][j] = B[j][i], bf16
+  const uint16_t* basis;    // channel-major   [n_basis][j][i], bf16
+  const float2* rope;
+  uint8_t* codes;
+  float* ranges;
+  void* k_out;
+  void* v_out;
+  uint32_t* status;  // device word or null
+};
+
 // Per-sequence placement of a paged batch, written on the device.
 struct SeqInfo {
   int32_t T;        // tokens of the sequence
@@ -365,6 +387,9 @@ hipError_t launch_batch_place(const Params& p, hipStream_t s);
 hipError_t launch_batch_finish(const Params& p, hipStream_t s);
 hipError_t launch_test_freq_tables(const uint32_t* counts, const int32_t* alpha, int n, int sb, uint16_t* freq,
                                    hipStream_t s);
+// scalar quantisers (head_dim 128, bf16): encode clears *status first
+hipError_t launch_sq_encode(const SqParams& q, hipStream_t s);
+hipError_t launch_sq_decode(const SqParams& q, hipStream_t s);
 hipError_t launch_prep_basis(const float* src, void* basis_t, void* basis, int n_basis, int D,
                              int dtype, int32_t* bad, hipStream_t s);
 

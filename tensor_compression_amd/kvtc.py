@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libkvtc.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_CORRUPT, ERR_NONFINITE, ERR_HIP = range(7)
 FP32, BF16 = 0, 1
 PCA, WHT = 0, 1
+SQ_BLOCK, SQ_KIVI = 1, 2
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "CAPACITY", 4: "CORRUPT",
           5: "NONFINITE", 6: "HIP"}
 
@@ -41,6 +42,15 @@ class Config(ctypes.Structure):
         ("wht_keys", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
         ("alloc_scope", ctypes.c_int32),
     ]
+
+
+class SqConfig(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("group", ctypes.c_int32), ("tile", ctypes.c_int32),
+                ("bits_k", ctypes.c_int32), ("bits_v", ctypes.c_int32)]
+
+
+def make_sq_config(sq: dict) -> SqConfig:
+    return SqConfig(sq["kind"], sq["group"], sq["tile"], sq["bits_k"], sq["bits_v"])
 
 
 EXPORTS = {
@@ -104,6 +114,14 @@ EXPORTS = {
     "kvtc_test_dequant_project": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
                                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
                                                  ctypes.c_int32, ctypes.c_void_p]),
+    "kvtc_sq_sizes": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                     ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
+    "kvtc_sq_encode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    "kvtc_sq_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
 }
 
 _lib = None
@@ -366,6 +384,53 @@ class Plan:
                                                _ptr(k_out), _ptr(v_out), out_dtype, _stream()),
                "kvtc_test_dequant_project")
         torch.cuda.current_stream().synchronize()
+
+    # ---- scalar quantisers on gauge coordinates (kvtc_sq_*)
+
+    def sq_sizes(self, sq: dict, T: int):
+        """(code bytes, range pairs) of a kvtc_sq_encode call over T tokens."""
+        c = make_sq_config(sq)
+        nb, nr = ctypes.c_size_t(0), ctypes.c_size_t(0)
+        _check(lib().kvtc_sq_sizes(self.handle, ctypes.byref(c), T, ctypes.byref(nb), ctypes.byref(nr)),
+               "kvtc_sq_sizes")
+        return nb.value, nr.value
+
+    def sq_encode_async(self, sq: dict, K: torch.Tensor, V: torch.Tensor, codes: torch.Tensor,
+                        ranges: torch.Tensor, status: torch.Tensor | None, stream=None):
+        c = make_sq_config(sq)
+        _check(lib().kvtc_sq_encode(self.handle, ctypes.byref(c), _ptr(K), _ptr(V), K.shape[2], _ptr(codes),
+                                    codes.numel(), _ptr(ranges), ranges.numel() // 2, _ptr(status),
+                                    _stream(stream)), "kvtc_sq_encode")
+
+    def sq_encode(self, sq: dict, K: torch.Tensor, V: torch.Tensor):
+        """kvtc_sq_encode: returns (codes uint8, ranges float32 [pairs, 2],
+        status word)."""
+        T = K.shape[2]
+        nb, nr = self.sq_sizes(sq, T)
+        codes = torch.empty(max(nb, 16), dtype=torch.uint8, device=self.device)
+        ranges = torch.empty((max(nr, 1), 2), dtype=torch.float32, device=self.device)
+        status = torch.zeros(4, dtype=torch.int32, device=self.device)
+        self.sq_encode_async(sq, K, V, codes, ranges, status)
+        torch.cuda.synchronize(self.device)
+        return codes[:nb], ranges[:nr], int(status[0].item())
+
+    def sq_decode_async(self, sq: dict, codes: torch.Tensor, ranges: torch.Tensor, T: int,
+                        k_out: torch.Tensor, v_out: torch.Tensor, out_dtype: int = FP32, stream=None):
+        c = make_sq_config(sq)
+        _check(lib().kvtc_sq_decode(self.handle, ctypes.byref(c), _ptr(codes), codes.numel(), _ptr(ranges),
+                                    ranges.numel() // 2, T, _ptr(k_out), _ptr(v_out), out_dtype,
+                                    _stream(stream)), "kvtc_sq_decode")
+
+    def sq_decode(self, sq: dict, codes: torch.Tensor, ranges: torch.Tensor, T: int, out_dtype: int = FP32):
+        """kvtc_sq_decode into new [L, H, T, D] tensors of out_dtype."""
+        c = self.cfg
+        shape = (c["layers"], c["kv_heads"], T, c["head_dim"])
+        dt = torch.float32 if out_dtype == FP32 else torch.bfloat16
+        k_out = torch.empty(shape, dtype=dt, device=self.device)
+        v_out = torch.empty(shape, dtype=dt, device=self.device)
+        self.sq_decode_async(sq, codes, ranges, T, k_out, v_out, out_dtype)
+        torch.cuda.synchronize(self.device)
+        return k_out, v_out
 
 
 def freq_tables(counts: torch.Tensor, alphabet: torch.Tensor, scale_bits: int):

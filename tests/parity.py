@@ -217,3 +217,93 @@ def nrmse(a, b) -> float:
     a = a.astype(np.float64)
     b = b.astype(np.float64)
     return math.sqrt(float(((a - b) ** 2).sum() / max((a ** 2).sum(), 1e-300)))
+
+
+# ---- scalar quantisers on gauge coordinates ------------------------------------
+
+def sq_extents(sq, s):
+    """(tokens, channels) of a range of section kind s (0 keys, 1 values)."""
+    if sq["kind"] == 1:
+        return sq["tile"], sq["group"]
+    return (sq["tile"], 1) if s == 0 else (1, sq["group"])
+
+
+def sq_section_offsets(cfg, sq, T, u):
+    """(code byte offset, range offset) of section u."""
+    D, H = cfg["head_dim"], cfg["kv_heads"]
+    h, s, l = u % H, (u // H) % 2, u // (2 * H)
+    cb = [T * D * sq["bits_k"] // 8, T * D * sq["bits_v"] // 8]
+    nr = []
+    for kind in (0, 1):
+        te, ce = sq_extents(sq, kind)
+        nr.append(-(-T // te) * (D // ce))
+
+    def off(x):
+        return l * H * (x[0] + x[1]) + (H * x[0] if s else 0) + h * x[s]
+    return off(cb), off(nr)
+
+
+def unpack_rows(buf, T, D, b):
+    """Token-major rows of D b-bit codes, least significant bit first."""
+    bits = np.unpackbits(np.asarray(buf, np.uint8), bitorder="little")[: T * D * b].reshape(T, D, b)
+    return (bits.astype(np.uint32) << np.arange(b, dtype=np.uint32)).sum(axis=2)
+
+
+def check_sq(orc, cfg, sq, k, v, basis, codes_g, ranges_g, T, report=None):
+    """Parity rules of the scalar quantisers, per section:
+      * ranges: zero within the coefficient bound of the range's exact
+        minimum, scale within twice that bound / (2^b - 1) (plus fp32
+        rounding) of the exact (max - min) / (2^b - 1);
+      * codes: equal to the oracle's quantiser on the oracle's exact
+        coefficients with the GPU's ranges, except where its pre-rounding
+        value lies within 1e-5 of a rounding boundary (at most 0.01%)."""
+    D, H = cfg["head_dim"], cfg["kv_heads"]
+    full = dict(cfg, sink_tokens=0, recent_tokens=0)
+    codes_g = np.asarray(codes_g, np.uint8)
+    ranges_g = np.asarray(ranges_g, np.float32).reshape(-1, 2)
+    n_sec = cfg["layers"] * 2 * H
+    n_codes = n_boundary = 0
+    for u in range(n_sec):
+        s = (u // H) % 2
+        b = sq["bits_k"] if s == 0 else sq["bits_v"]
+        te, ce = sq_extents(sq, s)
+        co, ro = sq_section_offsets(cfg, sq, T, u)
+        nr = -(-T // te) * (D // ce)
+        rg = ranges_g[ro: ro + nr]
+        c, _ = orc.section_coeffs(full, k, v, basis, u)
+        c = c[:T].astype(np.float32)
+        bound = coeff_bound(orc, full, k, v, basis, u, T)[:T]
+        tt, ii = np.meshgrid(np.arange(T), np.arange(D), indexing="ij")
+        ridx = (tt // te) * (D // ce) + ii // ce
+        mn = np.full(nr, np.inf)
+        mx = np.full(nr, -np.inf)
+        bm = np.zeros(nr)
+        np.minimum.at(mn, ridx.ravel(), c.astype(np.float64).ravel())
+        np.maximum.at(mx, ridx.ravel(), c.astype(np.float64).ravel())
+        np.maximum.at(bm, ridx.ravel(), bound.ravel())
+        tiny = 1e-7 * np.maximum(np.abs(mn), np.abs(mx)) + 1e-30
+        zg, sg = rg[:, 0].astype(np.float64), rg[:, 1].astype(np.float64)
+        assert np.all(np.abs(zg - mn) <= bm + tiny), f"section {u}: zero points"
+        qm = float((1 << b) - 1)
+        sref = (mx - mn) / qm
+        assert np.all(np.abs(sg - sref) <= 2 * bm / qm + 2.0 ** -22 * sref + tiny / qm), f"section {u}: scales"
+        # codes
+        rcp = rcp_of(rg[:, 1])
+        z32 = rg[:, 0][ridx]
+        vref = ((c - z32).astype(np.float32) * rcp[ridx]).astype(np.float32)
+        qref = np.clip(np.rint(vref), 0, qm).astype(np.uint32)
+        nb = T * D * b // 8
+        qg = unpack_rows(codes_g[co: co + nb], T, D, b)
+        diff = qg != qref
+        if diff.any():
+            vb = vref[diff].astype(np.float64)
+            dist = np.abs(vb - (np.floor(vb) + 0.5))
+            assert np.all(dist < BOUNDARY_TOL), \
+                f"section {u}: {int(diff.sum())} codes differ, worst boundary distance {dist.max()}"
+            assert np.all(np.abs(qg[diff].astype(int) - qref[diff].astype(int)) == 1)
+        n_codes += qg.size
+        n_boundary += int(diff.sum())
+    assert n_boundary <= BOUNDARY_FRACTION * max(n_codes, 1), f"{n_boundary} boundary codes of {n_codes}"
+    if report is not None:
+        report.append(dict(codes=n_codes, boundary_codes=n_boundary))
+    return n_codes, n_boundary

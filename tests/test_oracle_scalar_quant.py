@@ -136,3 +136,24 @@ def test_kivi_outlier_stays_in_its_ranges(orc):
     assert np.array_equal(r0[:nrk], r1[:nrk])
     changed = np.nonzero((r0[nrk:] != r1[nrk:]).any(axis=1))[0]
     assert changed.size > 0 and np.all(changed // (D // g) == 100)
+
+
+@pytest.mark.parametrize("kind", [1, 2])
+def test_parity_rules_refuse_planted_mistakes(orc, kind):
+    """The GPU parity rules accept the oracle's own output and refuse a code
+    moved by one step away from a rounding boundary, a zero point moved
+    beyond the coefficient bound and a scale off by more than its bound."""
+    import parity
+    cfg, sq, k, v, basis = _tiny(orc, kind)
+    T = k.shape[2]
+    codes, ranges = orc.sq_encode(cfg, sq, k, v, basis)
+    parity.check_sq(orc, cfg, sq, k, v, basis, codes, ranges, T)
+    bad = codes.copy()
+    bad[100] ^= 0x10
+    with pytest.raises(AssertionError):
+        parity.check_sq(orc, cfg, sq, k, v, basis, bad, ranges, T)
+    for col in (0, 1):
+        r2 = ranges.copy()
+        r2[3, col] += np.float32(1e-3) * max(abs(float(r2[3, 1])), 1e-3)
+        with pytest.raises(AssertionError):
+            parity.check_sq(orc, cfg, sq, k, v, basis, codes, r2, T)
