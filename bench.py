@@ -52,6 +52,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-phase event pass")
     ap.add_argument("--seqs", type=int, default=None, help="sequences of a paged workload")
+    ap.add_argument("--sq", choices=("block", "kivi"), default=None,
+                    help="time the scalar quantisers on gauge coordinates instead of the codec")
+    ap.add_argument("--sq-group", type=int, default=16, help="channels per range (block, KIVI values)")
+    ap.add_argument("--sq-tile", type=int, default=16, help="tokens per range (block, KIVI keys)")
+    ap.add_argument("--sq-bits", type=int, default=4, help="bits per coefficient (keys and values)")
     ap.add_argument("--ceilings", action="store_true",
                     help="time plain read, write and copy kernels over 520 MB (the practical HBM ceilings) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -78,8 +83,12 @@ PHASE_KERNELS = {
     "dec_checksum": (("k_csum_part", "k_csum_final"), ("kernels_rans.hip",)),
     "rans_decode": (("k_rans_dec_recs",), ("kernels_rans.hip",)),
     "dec_transform": (("k_dec_pca128",), ("kernels_decode.hip",)),
+    # scalar quantisers on gauge coordinates (bench.py --sq)
+    "sq_encode": (("k_sq_clear", "k_sq_enc128"), ("kernels_sq.hip",)),
+    "sq_decode": (("k_sq_dec128",), ("kernels_sq.hip",)),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_llama3_8b.md")
+TRAFFIC_FILE_SQ = os.path.join(ROOT, "profiles", "hbm_traffic_sq_llama3_8b.md")
 COPY_CAL_BYTES = 1 << 28  # fp32 elements read and written by the calibration copy
 
 
@@ -92,14 +101,14 @@ def source_digest(files) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(phase):
+def traffic_from_profile(phase, path=TRAFFIC_FILE):
     """HBM bytes per launch of the phase's kernels from the committed counter
     summary (rows `| phase | ... | bytes | digest |`), or None when absent or
     taken on different kernel sources."""
-    if phase not in PHASE_KERNELS or not os.path.exists(TRAFFIC_FILE):
+    if phase not in PHASE_KERNELS or not os.path.exists(path):
         return None
     want = source_digest(PHASE_KERNELS[phase][1])
-    with open(TRAFFIC_FILE) as fh:
+    with open(path) as fh:
         for line in fh:
             cells = [c.strip() for c in line.strip().strip("|").split("|")]
             if len(cells) >= 6 and cells[0] == phase:
@@ -172,6 +181,8 @@ def traffic_table(fetch_dir, write_dir):
     print("|---|---|---|---|---|---|")
     for ph, (kernels, files) in PHASE_KERNELS.items():
         names = [k for k in fetch if any(k == b or k.startswith(b + "<") for b in kernels)]
+        if not names:
+            continue
         fb = sum(fetch[k] for k in names) * ff * 1024
         wb = sum(write.get(k, 0.0) for k in names) * fw * 1024
         print(f"| {ph} | {' + '.join(sorted(names))} | {fb:.0f} | {wb:.0f} | {fb + wb:.0f} | "
@@ -410,6 +421,124 @@ def run_paged(args, w):
     print(json.dumps(res), flush=True)
 
 
+def run_sq(args, w):
+    """The scalar quantisers on gauge coordinates: one step = kvtc_sq_encode
+    + kvtc_sq_decode of the whole cache with a grouped random gauge (g = 16)
+    as the basis.  Each call is one launch (plus a one-word status clear
+    before the encoder), timed with HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from tensor_compression_amd import kvtc, synth
+
+    K, V = synth.generate(w, device="cuda", tokens=args.tokens, layers=args.layers)
+    L, H, T, D = K.shape
+    cfg = synth.oracle_config(w, layers=L)
+    B = np.zeros((L, 2, D, D), np.float32)
+    for l in range(L):
+        for s in range(2):
+            G = oracle.grouped_gauge(D, 16, oracle.random_gauge_generators(D, 16, 0.5, seed=100 * l + 10 * s))
+            B[l, s] = G.T.astype(np.float32)
+    basis = torch.from_numpy(B)
+    plan = kvtc.Plan(cfg, basis, max_tokens=T)
+    sq = dict(kind=kvtc.SQ_BLOCK if args.sq == "block" else kvtc.SQ_KIVI, group=args.sq_group,
+              tile=args.sq_tile, bits_k=args.sq_bits, bits_v=args.sq_bits)
+    nb, nr = plan.sq_sizes(sq, T)
+    codes = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    ranges = torch.empty((nr, 2), dtype=torch.float32, device="cuda")
+    status = torch.zeros(4, dtype=torch.int32, device="cuda")
+    kd, vd = torch.empty_like(K), torch.empty_like(V)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+    def step(times=None):
+        ev[0].record(stream)
+        plan.sq_encode_async(sq, K, V, codes, ranges, status, stream)
+        ev[1].record(stream)
+        plan.sq_decode_async(sq, codes, ranges, T, kd, vd, kvtc.BF16, stream)
+        ev[2].record(stream)
+        if times is not None:
+            torch.cuda.synchronize()
+            times.append((ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        plan.sq_encode_async(sq, K, V, codes, ranges, status, stream)
+        plan.sq_decode_async(sq, codes, ranges, T, kd, vd, kvtc.BF16, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    if int(status[0].item()) != 0:
+        raise SystemExit(f"device status {int(status[0].item())}")
+    times = []
+    for _ in range(args.steps):
+        step(times)
+    t_enc = float(np.mean([t[0] for t in times]))
+    t_dec = float(np.mean([t[1] for t in times]))
+    raw = (K.numel() + V.numel()) * K.element_size()
+    stored = nb + 8 * nr
+    alg = {"sq_encode": raw + stored, "sq_decode": stored + raw}
+    ms = {"sq_encode": t_enc, "sq_decode": t_dec}
+    dom = max(ms, key=lambda k: ms[k])
+    ach = alg[dom] / (ms[dom] * 1e-3) / 1e9
+
+    def nrmse(a, b):
+        a, b = a.float(), b.float()
+        return math.sqrt(float(((a - b) ** 2).sum()) / max(float((a ** 2).sum()), 1e-300))
+
+    res = {
+        "metric": f"scalar-quantiser ({args.sq}) encode+decode GB/s of raw bf16 KV",
+        "value": raw / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {L} layers x {H} KV heads x {T} tokens x head_dim {D}, bf16, "
+                        f"{args.sq} quantiser, {args.sq_bits} bits, group {args.sq_group}, tile {args.sq_tile}, "
+                        "grouped random gauge g = 16",
+            "layers": L, "kv_heads": H, "tokens": T, "head_dim": D, "sq": sq,
+        },
+        "raw_bytes": raw, "code_bytes": nb, "range_bytes": 8 * nr, "compression_ratio": raw / stored,
+        "bits_per_value": 8.0 * stored / (K.numel() + V.numel()),
+        "nrmse_k": nrmse(K, kd), "nrmse_v": nrmse(V, vd),
+        "phases_ms": ms,
+        "roofline": {"bound": "hbm", "kernel": dom, "kernels": ["k_sq_enc128" if dom == "sq_encode" else "k_sq_dec128"],
+                     "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                     "traffic": traffic_from_profile(dom, TRAFFIC_FILE_SQ), "algorithmic_bytes": alg[dom],
+                     "avg_ms": ms[dom]},
+        "path_roofline": {"bound": "hbm", "algorithmic_bytes": 2 * (raw + stored),
+                          "achieved": 2 * (raw + stored) / (ms_per_step * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                          "unit": "GB/s",
+                          "frac": 2 * (raw + stored) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+        "mfma_roofline": {k: {"flops": 2 * D * (K.numel() + V.numel()),
+                              "achieved_tflops": 2 * D * (K.numel() + V.numel()) / (ms[k] * 1e-3) / 1e12,
+                              "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                              "frac": 2 * D * (K.numel() + V.numel()) / (ms[k] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+                          for k in ms},
+    }
+    if not args.no_cpu_baseline:
+        nl = max(1, min(2, L))
+        k = synth.to_numpy_bits(K[:nl])
+        v = synth.to_numpy_bits(V[:nl])
+        c1 = dict(cfg, layers=nl)
+        oracle.lib()
+        t_a = time.perf_counter()
+        cg, rg = oracle.sq_encode(c1, sq, k, v, B[:nl])
+        t_b = time.perf_counter()
+        oracle.sq_decode(c1, sq, cg, rg, T, B[:nl])
+        t_c = time.perf_counter()
+        res["cpu_baseline"] = {
+            "value": (k.nbytes + v.nbytes) / (t_c - t_a) / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nl} of {L} layers: oracle encode {t_b - t_a:.2f} s + decode {t_c - t_b:.2f} s, "
+                      "single thread",
+        }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -442,6 +571,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
     w = synth.WORKLOADS[args.workload]
+    if args.sq:
+        run_sq(args, w)
+        return
     if w.n_seqs > 0:
         run_paged(args, w)
         return
