@@ -429,18 +429,14 @@ def run_sq(args, w):
     import numpy as np
     import torch
 
-    import oracle
     from tensor_compression_amd import kvtc, synth
+    from tensor_compression_amd.calibrate import grouped_random_gauge
 
     K, V = synth.generate(w, device="cuda", tokens=args.tokens, layers=args.layers)
     L, H, T, D = K.shape
     cfg = synth.oracle_config(w, layers=L)
-    B = np.zeros((L, 2, D, D), np.float32)
-    for l in range(L):
-        for s in range(2):
-            G = oracle.grouped_gauge(D, 16, oracle.random_gauge_generators(D, 16, 0.5, seed=100 * l + 10 * s))
-            B[l, s] = G.T.astype(np.float32)
-    basis = torch.from_numpy(B)
+    basis = grouped_random_gauge(L, D, 16, 0.5, seed=1)
+    B = basis.numpy()
     plan = kvtc.Plan(cfg, basis, max_tokens=T)
     sq = dict(kind=kvtc.SQ_BLOCK if args.sq == "block" else kvtc.SQ_KIVI, group=args.sq_group,
               tile=args.sq_tile, bits_k=args.sq_bits, bits_v=args.sq_bits)
@@ -521,6 +517,7 @@ def run_sq(args, w):
                           for k in ms},
     }
     if not args.no_cpu_baseline:
+        import oracle
         nl = max(1, min(2, L))
         k = synth.to_numpy_bits(K[:nl])
         v = synth.to_numpy_bits(V[:nl])

@@ -62,3 +62,20 @@ def _eig(S: torch.Tensor) -> torch.Tensor:
     sign = torch.sign(V[idx, torch.arange(V.shape[1], device=V.device)])
     sign[sign == 0] = 1
     return (V * sign).to(torch.float32)
+
+
+def grouped_random_gauge(layers: int, D: int, g: int, scale: float = 0.5, seed: int = 0) -> torch.Tensor:
+    """A seeded grouped gauge as a basis [layers, 2, D, D] (Codec-Gauge,
+    Gauge Parameterization: block-diagonal exp(A - A^T) over groups of g
+    channels; the random-gauge control of Compression Conditions).  The
+    frame is Z = G X, so the basis (column i = component i) is B = G^T.  The
+    generators A are N(0, scale^2); learning them is not part of the codec."""
+    gen = torch.Generator().manual_seed(seed)
+    out = torch.zeros((layers, 2, D, D), dtype=torch.float64)
+    for l in range(layers):
+        for s in range(2):
+            A = torch.randn((D // g, g, g), generator=gen, dtype=torch.float64) * scale
+            G = torch.matrix_exp(A - A.transpose(1, 2))
+            for k in range(D // g):
+                out[l, s, k * g:(k + 1) * g, k * g:(k + 1) * g] = G[k].T
+    return out.to(torch.float32)
