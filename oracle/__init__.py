@@ -98,6 +98,12 @@ def lib() -> ctypes.CDLL:
             "orc_sq_range_pairs": (ctypes.c_int64, [P, P, i32]),
             "orc_sq_encode": (i32, [P, P, P, P, i32, P, P, P]),
             "orc_sq_decode": (i32, [P, P, P, P, i32, P, P, P]),
+            "orc_pq_check": (i32, [P, P]),
+            "orc_pq_row_words": (i32, [P, P]),
+            "orc_pq_outlier_slots": (ctypes.c_int64, [P, P, i32]),
+            "orc_pq_nearest": (i32, [P, P, i32, i32]),
+            "orc_pq_encode": (i32, [P, P, P, i32, P, P, P, P, P]),
+            "orc_pq_decode": (i32, [P, P, P, P, P, i32, P, P, P]),
             "orc_alloc_dp": (f64, [P, i32, i32, i32, P]),
             "orc_distortion": (f64, [P, P, i32]),
             "orc_side_info": (None, [P, P, P, P, i32, P, P, P]),
@@ -533,6 +539,62 @@ def sq_decode(cfg: dict, sq: dict, codes, ranges, T: int, basis) -> tuple[np.nda
     if st != OK:
         raise OracleError(st, "sq_decode")
     return ko, vo
+
+
+class _PqCfg(ctypes.Structure):
+    _fields_ = [("sub_dim", ctypes.c_int32), ("k1", ctypes.c_int32), ("k2", ctypes.c_int32),
+                ("outliers", ctypes.c_int32), ("block_tokens", ctypes.c_int32)]
+
+
+def pq_sizes(cfg: dict, pq: dict, T: int) -> tuple[int, int]:
+    """(u32 words per token row, outlier slots) of the TTAS-X2 value path."""
+    c, q = make_cfg(cfg), _PqCfg(**pq)
+    rw = int(lib().orc_pq_row_words(ctypes.byref(c), ctypes.byref(q)))
+    ns = int(lib().orc_pq_outlier_slots(ctypes.byref(c), ctypes.byref(q), T))
+    if rw < 0 or ns < 0:
+        raise OracleError(ERR_INVALID_ARG, "pq_sizes")
+    return rw, ns
+
+
+def pq_nearest(y, cb) -> int:
+    """Index of the nearest bf16-rounded centroid of cb [k, d] to y [d]
+    ([TTAS] 2.2 product quantisation; fp64 distance, lowest index on ties)."""
+    y = np.ascontiguousarray(y, np.float32)
+    cb = np.ascontiguousarray(cb, np.float32)
+    return int(lib().orc_pq_nearest(_p(y), _p(cb), cb.shape[0], cb.shape[1]))
+
+
+def pq_encode(cfg: dict, pq: dict, v, cb1, cb2):
+    """TTAS-X2 value path ([TTAS] 2.2): (codes u32 [L,H,T,row_words], rms f32
+    [L,H,T], outliers u32 [L,H,blocks,budget,2])."""
+    c, q = make_cfg(cfg), _PqCfg(**pq)
+    L, H, T = cfg["layers"], cfg["kv_heads"], v.shape[2]
+    rw, ns = pq_sizes(cfg, pq, T)
+    nblk = -(-T // pq["block_tokens"])
+    codes = np.zeros((L, H, T, rw), np.uint32)
+    rms_ = np.zeros((L, H, T), np.float32)
+    outl = np.zeros((L, H, nblk, pq["outliers"], 2), np.uint32)
+    vv = np.ascontiguousarray(v)
+    a1, a2 = np.ascontiguousarray(cb1, np.float32), np.ascontiguousarray(cb2, np.float32)
+    st = lib().orc_pq_encode(ctypes.byref(c), ctypes.byref(q), _p(vv), T, _p(a1), _p(a2), _p(codes), _p(rms_),
+                             _p(outl) if outl.size else None)
+    if st != OK:
+        raise OracleError(st, "pq_encode")
+    return codes, rms_, outl
+
+
+def pq_decode(cfg: dict, pq: dict, codes, rms_, outl, T: int, cb1, cb2) -> np.ndarray:
+    c, q = make_cfg(cfg), _PqCfg(**pq)
+    out = np.zeros((cfg["layers"], cfg["kv_heads"], T, cfg["head_dim"]), np.float32)
+    cs = np.ascontiguousarray(codes, np.uint32)
+    rs = np.ascontiguousarray(rms_, np.float32)
+    ol = np.ascontiguousarray(outl, np.uint32)
+    a1, a2 = np.ascontiguousarray(cb1, np.float32), np.ascontiguousarray(cb2, np.float32)
+    st = lib().orc_pq_decode(ctypes.byref(c), ctypes.byref(q), _p(cs), _p(rs), _p(ol) if ol.size else None, T,
+                             _p(a1), _p(a2), _p(out))
+    if st != OK:
+        raise OracleError(st, "pq_decode")
+    return out
 
 
 def fnv1a64(data: bytes, h: int = 0xCBF29CE484222325) -> int:

@@ -1819,3 +1819,245 @@ int orc_sq_decode(const orc_config* c, const orc_sq_config* q, const uint8_t* co
   free(Bp); free(cos_t); free(sin_t);
   return ORC_OK;
 }
+
+/* ===================================================================== */
+/* TTAS-X2 value path ([TTAS] 2.2 V Compression: RMS normalisation per     */
+/* vector, Hadamard transform, two-level product quantisation with         */
+/* K1 = 256 and K2 = 64..512, fixed-budget outliers per head).             */
+/* ===================================================================== */
+
+static int pq_pow2_in(int32_t k, int32_t lo, int32_t hi) { return k >= lo && k <= hi && (k & (k - 1)) == 0; }
+
+static int32_t pq_log2(int32_t k) {
+  int32_t b = 0;
+  while ((1 << b) < k) ++b;
+  return b;
+}
+
+int orc_pq_check(const orc_config* c, const orc_pq_config* q) {
+  int st = orc_check_config(c);
+  if (st != ORC_OK) return st;
+  if (!q || (c->head_dim & (c->head_dim - 1))) return ORC_ERR_INVALID_ARG; /* the WHT needs 2^n */
+  if (q->sub_dim < 1 || c->head_dim % q->sub_dim) return ORC_ERR_INVALID_ARG;
+  if (!pq_pow2_in(q->k1, 2, 512) || !pq_pow2_in(q->k2, 2, 512)) return ORC_ERR_INVALID_ARG;
+  if (q->outliers < 0 || q->block_tokens < 1) return ORC_ERR_INVALID_ARG;
+  return ORC_OK;
+}
+
+/* A token's row: the M level-1 indices of log2(k1) bits, then the M level-2
+ * indices of log2(k2) bits, least significant bit first, padded to 32. */
+int32_t orc_pq_row_words(const orc_config* c, const orc_pq_config* q) {
+  if (orc_pq_check(c, q) != ORC_OK) return -1;
+  int32_t M = c->head_dim / q->sub_dim;
+  return (M * (pq_log2(q->k1) + pq_log2(q->k2)) + 31) / 32;
+}
+
+int64_t orc_pq_outlier_slots(const orc_config* c, const orc_pq_config* q, int32_t T) {
+  if (orc_pq_check(c, q) != ORC_OK || T < 0) return -1;
+  int64_t nblk = ((int64_t)T + q->block_tokens - 1) / q->block_tokens;
+  return (int64_t)c->layers * c->kv_heads * nblk * q->outliers;
+}
+
+/* The nearest of k centroids (already bf16-valued) to y: fp64 squared
+ * distance summed in channel order, lowest index on ties. */
+static int32_t pq_nearest_r(const float* y, const float* cb, int32_t k, int32_t d) {
+  int32_t best = 0;
+  double bd = INFINITY;
+  for (int32_t i = 0; i < k; ++i) {
+    double acc = 0.0;
+    for (int32_t j = 0; j < d; ++j) {
+      double e = (double)y[j] - (double)cb[(int64_t)i * d + j];
+      acc += e * e;
+    }
+    if (acc < bd) {
+      bd = acc;
+      best = i;
+    }
+  }
+  return best;
+}
+
+int32_t orc_pq_nearest(const float* y, const float* cb, int32_t k, int32_t d) {
+  float* r = (float*)malloc(sizeof(float) * (size_t)k * d);
+  for (int64_t a = 0; a < (int64_t)k * d; ++a) r[a] = orc_bf16_to_f32(orc_f32_to_bf16(cb[a]));
+  int32_t i = pq_nearest_r(y, r, k, d);
+  free(r);
+  return i;
+}
+
+static void pq_put(uint32_t* row, int64_t bit, int32_t nb, uint32_t v) {
+  for (int32_t e = 0; e < nb; ++e)
+    if ((v >> e) & 1u) row[(bit + e) >> 5] |= 1u << ((bit + e) & 31);
+}
+
+static uint32_t pq_get(const uint32_t* row, int64_t bit, int32_t nb) {
+  uint32_t v = 0;
+  for (int32_t e = 0; e < nb; ++e) v |= ((row[(bit + e) >> 5] >> ((bit + e) & 31)) & 1u) << e;
+  return v;
+}
+
+/* The layer's codebooks with every entry rounded to bf16. */
+static void pq_round_codebooks(const orc_config* c, const orc_pq_config* q, int32_t l, const float* cb1,
+                               const float* cb2, float* c1, float* c2) {
+  int32_t M = c->head_dim / q->sub_dim, d = q->sub_dim;
+  int64_t n1 = (int64_t)M * q->k1 * d, n2 = (int64_t)M * q->k2 * d;
+  for (int64_t a = 0; a < n1; ++a) c1[a] = orc_bf16_to_f32(orc_f32_to_bf16(cb1[(int64_t)l * n1 + a]));
+  for (int64_t a = 0; a < n2; ++a) c2[a] = orc_bf16_to_f32(orc_f32_to_bf16(cb2[(int64_t)l * n2 + a]));
+}
+
+typedef struct {
+  float mag;
+  uint32_t idx;
+} pq_cand;
+
+/* |y - y^| descending, then the lower index first. */
+static int pq_cmp_mag(const void* a, const void* b) {
+  const pq_cand* x = (const pq_cand*)a;
+  const pq_cand* y = (const pq_cand*)b;
+  if (x->mag != y->mag) return x->mag > y->mag ? -1 : 1;
+  return x->idx < y->idx ? -1 : (x->idx > y->idx);
+}
+
+static int pq_cmp_idx(const void* a, const void* b) {
+  const pq_cand* x = (const pq_cand*)a;
+  const pq_cand* y = (const pq_cand*)b;
+  return x->idx < y->idx ? -1 : (x->idx > y->idx);
+}
+
+int orc_pq_encode(const orc_config* c, const orc_pq_config* q, const void* v, int32_t T, const float* cb1,
+                  const float* cb2, uint32_t* codes, float* rms, uint32_t* outliers) {
+  int st = orc_pq_check(c, q);
+  if (st != ORC_OK) return st;
+  if (T < 0) return ORC_ERR_INVALID_ARG;
+  if (T == 0) return ORC_OK;
+  if (!v || !cb1 || !cb2 || !codes || !rms || (q->outliers > 0 && !outliers)) return ORC_ERR_INVALID_ARG;
+  const int32_t D = c->head_dim, H = c->kv_heads, d = q->sub_dim, M = D / d;
+  const int32_t b1 = pq_log2(q->k1), b2 = pq_log2(q->k2), rw = orc_pq_row_words(c, q);
+  const int32_t B = q->outliers, bt = q->block_tokens;
+  const int32_t nblk = (T + bt - 1) / bt;
+  float* c1 = (float*)malloc(sizeof(float) * (size_t)M * q->k1 * d);
+  float* c2 = (float*)malloc(sizeof(float) * (size_t)M * q->k2 * d);
+  float* y = (float*)malloc(sizeof(float) * (size_t)T * D);
+  float* del = (float*)malloc(sizeof(float) * (size_t)T * D);
+  pq_cand* cand = (pq_cand*)malloc(sizeof(pq_cand) * ((size_t)(bt < T ? bt : T) * D + 1));
+  float x[256], xn[256], e[256];
+  for (int32_t l = 0; l < c->layers && st == ORC_OK; ++l) {
+    pq_round_codebooks(c, q, l, cb1, cb2, c1, c2);
+    for (int32_t h = 0; h < H && st == ORC_OK; ++h) {
+      const int64_t sec = (int64_t)l * H + h;
+      for (int32_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < D; ++j) {
+          x[j] = load_elem(v, c->dtype, (sec * T + t) * D + j);
+          if (!isfinite(x[j])) st = ORC_ERR_NONFINITE;
+        }
+        if (st != ORC_OK) break;
+        /* RMS normalisation and the orthonormal Hadamard transform */
+        float r = orc_rms(x, D);
+        rms[sec * T + t] = r;
+        for (int32_t j = 0; j < D; ++j) xn[j] = r == 0.0f ? 0.0f : x[j] / r;
+        float* yt = y + (int64_t)t * D;
+        orc_wht(xn, D, yt);
+        uint32_t* row = codes + (sec * T + t) * rw;
+        memset(row, 0, sizeof(uint32_t) * (size_t)rw);
+        for (int32_t s = 0; s < M; ++s) {
+          const float* ys = yt + s * d;
+          const float* cs1 = c1 + (int64_t)s * q->k1 * d;
+          const float* cs2 = c2 + (int64_t)s * q->k2 * d;
+          /* level 1, then level 2 on the fp32 residual */
+          int32_t i1 = pq_nearest_r(ys, cs1, q->k1, d);
+          for (int32_t j = 0; j < d; ++j) e[j] = ys[j] - cs1[(int64_t)i1 * d + j];
+          int32_t i2 = pq_nearest_r(e, cs2, q->k2, d);
+          for (int32_t j = 0; j < d; ++j) {
+            float yh = cs1[(int64_t)i1 * d + j] + cs2[(int64_t)i2 * d + j];
+            del[(int64_t)t * D + s * d + j] = ys[j] - yh;
+          }
+          pq_put(row, (int64_t)s * b1, b1, (uint32_t)i1);
+          pq_put(row, (int64_t)M * b1 + (int64_t)s * b2, b2, (uint32_t)i2);
+        }
+      }
+      if (st != ORC_OK || B == 0) continue;
+      /* per block: the B coefficients with the largest |y - y^|, kept exactly */
+      for (int32_t k = 0; k < nblk; ++k) {
+        int32_t ta = k * bt, tb = ta + bt < T ? ta + bt : T;
+        int64_t n = (int64_t)(tb - ta) * D;
+        for (int64_t a = 0; a < n; ++a) {
+          cand[a].idx = (uint32_t)((int64_t)ta * D + a);
+          cand[a].mag = fabsf(del[(int64_t)ta * D + a]);
+        }
+        qsort(cand, (size_t)n, sizeof(pq_cand), pq_cmp_mag);
+        int64_t nsel = n < B ? n : B;
+        qsort(cand, (size_t)nsel, sizeof(pq_cand), pq_cmp_idx);
+        uint32_t* o = outliers + ((sec * nblk + k) * B) * 2;
+        for (int64_t a = 0; a < B; ++a) {
+          if (a < nsel) {
+            uint32_t bits;
+            memcpy(&bits, &y[cand[a].idx], 4);
+            o[2 * a] = cand[a].idx;
+            o[2 * a + 1] = bits;
+          } else {
+            o[2 * a] = 0xFFFFFFFFu;
+            o[2 * a + 1] = 0u;
+          }
+        }
+      }
+    }
+  }
+  free(c1); free(c2); free(y); free(del); free(cand);
+  return st;
+}
+
+int orc_pq_decode(const orc_config* c, const orc_pq_config* q, const uint32_t* codes, const float* rms,
+                  const uint32_t* outliers, int32_t T, const float* cb1, const float* cb2, float* v_out) {
+  int st = orc_pq_check(c, q);
+  if (st != ORC_OK) return st;
+  if (T < 0) return ORC_ERR_INVALID_ARG;
+  if (T == 0) return ORC_OK;
+  if (!codes || !rms || !cb1 || !cb2 || !v_out || (q->outliers > 0 && !outliers)) return ORC_ERR_INVALID_ARG;
+  const int32_t D = c->head_dim, H = c->kv_heads, d = q->sub_dim, M = D / d;
+  const int32_t b1 = pq_log2(q->k1), b2 = pq_log2(q->k2), rw = orc_pq_row_words(c, q);
+  const int32_t B = q->outliers, bt = q->block_tokens;
+  const int32_t nblk = (T + bt - 1) / bt;
+  float* c1 = (float*)malloc(sizeof(float) * (size_t)M * q->k1 * d);
+  float* c2 = (float*)malloc(sizeof(float) * (size_t)M * q->k2 * d);
+  float* yh = (float*)malloc(sizeof(float) * ((size_t)(bt < T ? bt : T) * D + 1));
+  float tmp[256];
+  for (int32_t l = 0; l < c->layers && st == ORC_OK; ++l) {
+    pq_round_codebooks(c, q, l, cb1, cb2, c1, c2);
+    for (int32_t h = 0; h < H && st == ORC_OK; ++h) {
+      const int64_t sec = (int64_t)l * H + h;
+      for (int32_t k = 0; k < nblk && st == ORC_OK; ++k) {
+        int32_t ta = k * bt, tb = ta + bt < T ? ta + bt : T;
+        for (int32_t t = ta; t < tb; ++t) {
+          const uint32_t* row = codes + (sec * T + t) * rw;
+          for (int32_t s = 0; s < M; ++s) {
+            uint32_t i1 = pq_get(row, (int64_t)s * b1, b1);
+            uint32_t i2 = pq_get(row, (int64_t)M * b1 + (int64_t)s * b2, b2);
+            for (int32_t j = 0; j < d; ++j)
+              yh[(int64_t)(t - ta) * D + s * d + j] =
+                  c1[((int64_t)s * q->k1 + i1) * d + j] + c2[((int64_t)s * q->k2 + i2) * d + j];
+          }
+        }
+        /* the block's outliers replace their coefficients */
+        const uint32_t* o = B > 0 ? outliers + ((sec * nblk + k) * B) * 2 : NULL;
+        for (int32_t a = 0; a < B; ++a) {
+          uint32_t idx = o[2 * a];
+          if (idx == 0xFFFFFFFFu) continue;
+          if ((int64_t)idx < (int64_t)ta * D || (int64_t)idx >= (int64_t)tb * D) {
+            st = ORC_ERR_CORRUPT;
+            break;
+          }
+          memcpy(&yh[idx - (int64_t)ta * D], &o[2 * a + 1], 4);
+        }
+        if (st != ORC_OK) break;
+        /* inverse transform (the orthonormal WHT is its own inverse), times r */
+        for (int32_t t = ta; t < tb; ++t) {
+          float r = rms[sec * T + t];
+          orc_wht(yh + (int64_t)(t - ta) * D, D, tmp);
+          for (int32_t j = 0; j < D; ++j) v_out[(sec * T + t) * D + j] = tmp[j] * r;
+        }
+      }
+    }
+  }
+  free(c1); free(c2); free(yh);
+  return st;
+}

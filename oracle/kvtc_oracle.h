@@ -183,6 +183,39 @@ int orc_sq_encode(const orc_config* c, const orc_sq_config* q, const void* k, co
 int orc_sq_decode(const orc_config* c, const orc_sq_config* q, const uint8_t* codes, const float* ranges,
                   int32_t T, const float* basis, float* k_out, float* v_out);
 
+/* ---- TTAS-X2 value path: two-level product quantisation ---------------- */
+/* ("TTAS-X2: Extreme KV Cache Compression for Large Language Models", 2.2 V
+ * Compression: per-vector RMS normalisation, Hadamard transform, two-level
+ * product quantisation with K1 = 256 and K2 = 64..512 centroids, a fixed
+ * budget of outliers per head; 3 Experiments: the budget and K2 per layer.)
+ * Value sections only.  Each value vector x: r = rms(x), y = WHT(x / r);
+ * y is split into head_dim / sub_dim subvectors; level 1 takes the nearest
+ * of k1 centroids, level 2 the nearest of k2 centroids to the level-1
+ * residual; per (layer, head) and block of block_tokens tokens the
+ * `outliers` coefficients with the largest |y - y^| are stored exactly. */
+typedef struct {
+  int32_t sub_dim;       /* channels per subvector; divides head_dim */
+  int32_t k1, k2;        /* centroids per subspace, powers of two in [2, 512] */
+  int32_t outliers;      /* budget per (layer, head) and block, >= 0 */
+  int32_t block_tokens;  /* tokens per outlier block, >= 1 */
+} orc_pq_config;
+int orc_pq_check(const orc_config* c, const orc_pq_config* q);
+int32_t orc_pq_row_words(const orc_config* c, const orc_pq_config* q);
+int64_t orc_pq_outlier_slots(const orc_config* c, const orc_pq_config* q, int32_t T);
+/* Nearest of k centroids cb[k][d] (entries rounded to bf16) to y[d]: the
+ * smallest sum_j (y_j - c_j)^2 in fp64, summed in j order; ties go to the
+ * lowest index. */
+int32_t orc_pq_nearest(const float* y, const float* cb, int32_t k, int32_t d);
+/* v: [L,H,T,D] in the cache dtype; cb1 [L][M][k1][d], cb2 [L][M][k2][d]
+ * fp32 (rounded to bf16 on use).  codes [L][H][T][row_words] u32, rms
+ * [L][H][T] f32, outliers [L][H][blocks][outliers][2] u32 (index t D + j
+ * within the section, fp32 bits of y), index-ascending per block, unused
+ * slots (0xFFFFFFFF, 0). */
+int orc_pq_encode(const orc_config* c, const orc_pq_config* q, const void* v, int32_t T, const float* cb1,
+                  const float* cb2, uint32_t* codes, float* rms, uint32_t* outliers);
+int orc_pq_decode(const orc_config* c, const orc_pq_config* q, const uint32_t* codes, const float* rms,
+                  const uint32_t* outliers, int32_t T, const float* cb1, const float* cb2, float* v_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,6 +9,8 @@ linear algebra; it is not part of the coded path.
 """
 from __future__ import annotations
 
+import math
+
 import torch
 
 
@@ -79,3 +81,66 @@ def grouped_random_gauge(layers: int, D: int, g: int, scale: float = 0.5, seed: 
             for k in range(D // g):
                 out[l, s, k * g:(k + 1) * g, k * g:(k + 1) * g] = G[k].T
     return out.to(torch.float32)
+
+
+def hadamard(D: int, dtype=torch.float64, device="cpu") -> torch.Tensor:
+    """Orthonormal Walsh-Hadamard matrix in Sylvester order."""
+    i = torch.arange(D, device=device)
+    bits = (i[:, None] & i[None, :]).to(torch.int64)
+    par = torch.zeros_like(bits)
+    while bool(bits.any()):
+        par ^= bits & 1
+        bits >>= 1
+    return (1 - 2 * par).to(dtype) / math.sqrt(D)
+
+
+def _kmeans(x: torch.Tensor, k: int, iters: int, gen: torch.Generator) -> torch.Tensor:
+    """Lloyd's k-means with k-means++ seeding on rows of x [N, d] (fp32)."""
+    N = x.shape[0]
+    cent = torch.empty((k, x.shape[1]), dtype=x.dtype, device=x.device)
+    first = int(torch.randint(N, (1,), generator=gen))
+    cent[0] = x[first]
+    d2 = ((x - cent[0]) ** 2).sum(1)
+    for j in range(1, k):
+        p = (d2 / d2.sum()).cpu() if float(d2.sum()) > 0 else torch.full((N,), 1.0 / N)
+        idx = int(torch.multinomial(p, 1, generator=gen))
+        cent[j] = x[idx]
+        d2 = torch.minimum(d2, ((x - cent[j]) ** 2).sum(1))
+    for _ in range(iters):
+        a = torch.cdist(x, cent).argmin(1)
+        s = torch.zeros_like(cent).index_add_(0, a, x)
+        n = torch.bincount(a, minlength=k).to(x.dtype)
+        keep = n > 0
+        cent[keep] = s[keep] / n[keep, None]
+    return cent
+
+
+def train_pq_codebooks(V: torch.Tensor, pq: dict, iters: int = 8, seed: int = 0, max_rows: int = 65536):
+    """Two-level product-quantisation codebooks for the TTAS-X2 value path
+    (TTAS-X2 2.2: per-vector RMS normalisation, Hadamard transform, then
+    product quantisation with K1 and K2 centroids per subspace), trained by
+    k-means per layer and subspace on V [L, H, T, D]; level 2 on the level-1
+    residuals (centroids rounded to bf16, as the codec holds them).  Returns
+    fp32 (cb1 [L, M, k1, d], cb2 [L, M, k2, d]).  Set-up, not the coded path."""
+    L, H, T, D = V.shape
+    d, k1, k2 = pq["sub_dim"], pq["k1"], pq["k2"]
+    M = D // d
+    gen = torch.Generator().manual_seed(seed)
+    Hm = hadamard(D, torch.float64, V.device)
+    cb1 = torch.empty((L, M, k1, d), dtype=torch.float32)
+    cb2 = torch.empty((L, M, k2, d), dtype=torch.float32)
+    for l in range(L):
+        x = V[l].reshape(-1, D).to(torch.float64)
+        if x.shape[0] > max_rows:
+            x = x[torch.randperm(x.shape[0], generator=gen)[:max_rows].to(x.device)]
+        r = torch.sqrt((x * x).mean(1, keepdim=True))
+        xn = torch.where(r > 0, x / torch.where(r > 0, r, torch.ones_like(r)), torch.zeros_like(x))
+        y = (xn @ Hm.T).to(torch.float32)
+        for s in range(M):
+            ys = y[:, s * d:(s + 1) * d].contiguous()
+            c1 = _kmeans(ys, k1, iters, gen).to(torch.bfloat16).to(torch.float32)
+            e = ys - c1[torch.cdist(ys, c1).argmin(1)]
+            c2 = _kmeans(e, k2, iters, gen)
+            cb1[l, s] = c1.cpu()
+            cb2[l, s] = c2.cpu()
+    return cb1, cb2
