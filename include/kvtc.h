@@ -452,6 +452,81 @@ kvtc_status kvtc_sq_decode(kvtc_plan_t plan, const kvtc_sq_config* q, const void
                            const float* ranges, size_t range_pairs, int32_t T, void* k_out, void* v_out,
                            int32_t out_dtype, hipStream_t stream);
 
+/* ---- TTAS-X2 value path: two-level product quantisation ------------------ */
+
+/* "TTAS-X2: Extreme KV Cache Compression for Large Language Models", 2.2 V
+ * Compression: every value vector x (value sections only) is RMS-normalised,
+ * r = sqrt(sum x^2 / D), and Hadamard-transformed, y = WHT(x / r) (the
+ * orthonormal Sylvester transform); y is split into D / sub_dim subvectors,
+ * each coded by two-level product quantisation -- the nearest of k1
+ * centroids, then the nearest of k2 centroids to the fp32 residual -- and
+ * per (layer, head) and block of block_tokens tokens the `outliers`
+ * coefficients with the largest |y - y^| (then the lowest index) are kept
+ * exactly; 3 Experiments: K1 = 256, K2 = 64..512, 32..256 outliers per
+ * head.  The keys' 4-bit scalar path of 2.1 is kvtc_encode with the WHT
+ * transform and wht_keys = 0.
+ *
+ * Definitions: r in fp64 rounded to fp32; the transform in fp64, rounded
+ * once; centroids are held in bf16 (the given fp32 codebooks are rounded to
+ * nearest even); the nearest centroid minimises sum_j (y_j - c_j)^2 in fp64
+ * summed in channel order, lowest index on ties; y^ = c1 + c2 in fp32;
+ * decoding puts the outliers back into y^ and returns WHT(y^) r.  The
+ * encoder's scores come from bf16 MFMA products of y split into two bf16
+ * parts; a choice whose two best scores lie within their error bound is
+ * re-decided by the exact distances, so the indices are the exact ones.
+ *
+ * Codebooks (device, fp32, 16-byte aligned, owned by the caller): cb1
+ * [L][D / sub_dim][k1][sub_dim], cb2 [L][D / sub_dim][k2][sub_dim], per
+ * layer and subspace (shared by the layer's heads).
+ *
+ * Layout, value sections (l, h) = l H + h in order:
+ *  codes     [L H][T][row_words] u32: per token the level-1 indices of
+ *            log2(k1) bits, then the level-2 indices of log2(k2) bits, in
+ *            subspace order, least significant bit first, zero-padded;
+ *  rms       [L H][T] fp32;
+ *  outliers  [L H][blocks][outliers] slots of two u32: index t D + j within
+ *            the section (t the token, j the channel) and the fp32 bits of
+ *            y; index-ascending within a block, unused slots
+ *            (0xFFFFFFFF, 0); blocks = ceil(T / block_tokens).
+ *
+ * Supported: bf16 head_dim-128 plans with sub_dim 8, k1 and k2 in
+ * {32, ..., 512}, outliers <= 256, block_tokens a multiple of 64 with
+ * (block_tokens / 64) outliers <= 4096 (otherwise KVTC_ERR_UNSUPPORTED).
+ * sub_dim must divide head_dim, k1 and k2 be powers of two in [2, 512],
+ * outliers >= 0 and block_tokens >= 1 (otherwise KVTC_ERR_INVALID_ARG). */
+typedef struct kvtc_pq_config {
+  int32_t sub_dim;       /* channels per subvector */
+  int32_t k1, k2;        /* centroids per subspace, levels 1 and 2 */
+  int32_t outliers;      /* budget per (layer, head) and block */
+  int32_t block_tokens;  /* tokens per outlier block */
+} kvtc_pq_config;
+
+/* Bytes of codes, outlier slots and workspace bytes of a call over T tokens
+ * (host only).  rms holds L H T floats. */
+kvtc_status kvtc_pq_sizes(kvtc_plan_t plan, const kvtc_pq_config* q, int32_t T, size_t* code_bytes,
+                          size_t* outlier_slots, size_t* ws_bytes);
+
+/* Encode the values v (device [L,H,T,D] bf16) into codes (code_cap bytes),
+ * rms (rms_cap floats) and outliers (outlier_cap slots), all device.  ws:
+ * device workspace of kvtc_pq_sizes() bytes.  When status_dev (device,
+ * 4-byte aligned) is not NULL it is cleared and then gets bit
+ * KVTC_ERR_NONFINITE for a NaN or infinite value (the outputs are then
+ * undefined).  Asynchronous on `stream`. */
+kvtc_status kvtc_pq_encode(kvtc_plan_t plan, const kvtc_pq_config* q, const float* cb1, const float* cb2,
+                           const void* v, int32_t T, uint32_t* codes, size_t code_cap, float* rms, size_t rms_cap,
+                           uint32_t* outliers, size_t outlier_cap, void* ws, size_t ws_bytes, uint32_t* status_dev,
+                           hipStream_t stream);
+
+/* Reconstruct the values into v_out (device [L,H,T,D] in out_dtype,
+ * KVTC_BF16 or KVTC_FP32) from what kvtc_pq_encode wrote under the same
+ * plan, configuration, codebooks and T.  An outlier index outside its block
+ * sets bit KVTC_ERR_CORRUPT in status_dev (cleared first; may be NULL) and
+ * is ignored.  Asynchronous on `stream`. */
+kvtc_status kvtc_pq_decode(kvtc_plan_t plan, const kvtc_pq_config* q, const float* cb1, const float* cb2,
+                           const uint32_t* codes, size_t code_bytes, const float* rms, const uint32_t* outliers,
+                           size_t outlier_slots, int32_t T, void* v_out, int32_t out_dtype, void* ws, size_t ws_bytes,
+                           uint32_t* status_dev, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

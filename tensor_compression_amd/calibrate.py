@@ -95,17 +95,13 @@ def hadamard(D: int, dtype=torch.float64, device="cpu") -> torch.Tensor:
 
 
 def _kmeans(x: torch.Tensor, k: int, iters: int, gen: torch.Generator) -> torch.Tensor:
-    """Lloyd's k-means with k-means++ seeding on rows of x [N, d] (fp32)."""
+    """Lloyd's k-means on rows of x [N, d] (fp32), seeded with k distinct rows
+    (repeated when N < k)."""
     N = x.shape[0]
-    cent = torch.empty((k, x.shape[1]), dtype=x.dtype, device=x.device)
-    first = int(torch.randint(N, (1,), generator=gen))
-    cent[0] = x[first]
-    d2 = ((x - cent[0]) ** 2).sum(1)
-    for j in range(1, k):
-        p = (d2 / d2.sum()).cpu() if float(d2.sum()) > 0 else torch.full((N,), 1.0 / N)
-        idx = int(torch.multinomial(p, 1, generator=gen))
-        cent[j] = x[idx]
-        d2 = torch.minimum(d2, ((x - cent[j]) ** 2).sum(1))
+    pick = torch.randperm(N, generator=gen)[:k]
+    if pick.numel() < k:
+        pick = pick.repeat((k + N - 1) // N)[:k]
+    cent = x[pick.to(x.device)].clone()
     for _ in range(iters):
         a = torch.cdist(x, cent).argmin(1)
         s = torch.zeros_like(cent).index_add_(0, a, x)

@@ -906,4 +906,114 @@ kvtc_status kvtc_sq_decode(kvtc_plan_t plan, const kvtc_sq_config* q, const void
   return KVTC_OK;
 }
 
+// ---- TTAS-X2 value path -------------------------------------------------------
+
+static bool pq_pow2(int32_t k) { return k >= 2 && k <= 512 && (k & (k - 1)) == 0; }
+
+static int32_t pq_log2(int32_t k) {
+  int32_t b = 0;
+  while ((1 << b) < k) ++b;
+  return b;
+}
+
+// Checks, parameters and the workspace layout of a call; ws_at == null only sizes it.
+static kvtc_status pq_params(const PlanImpl* pl, const kvtc_pq_config* q, int32_t T, uint8_t* ws_at,
+                             PqParams* pp, int64_t* ws_need) {
+  if (!q) return KVTC_ERR_INVALID_ARG;
+  const kvtc_config& c = pl->cfg;
+  if (q->sub_dim < 1 || c.head_dim % q->sub_dim) return KVTC_ERR_INVALID_ARG;
+  if (!pq_pow2(q->k1) || !pq_pow2(q->k2) || q->outliers < 0 || q->block_tokens < 1) return KVTC_ERR_INVALID_ARG;
+  if (T < 0 || T > c.max_tokens) return KVTC_ERR_INVALID_ARG;
+  // the kernels: head_dim 128 bf16 rows, 8-channel subvectors on 32 x 32 x 8
+  // MFMA blocks of 32 centroids, 64-token spans inside a block, at most 4096
+  // candidates per block merge
+  if (c.head_dim != 128 || c.dtype != KVTC_BF16 || q->sub_dim != 8 || q->k1 < 32 || q->k2 < 32 ||
+      q->outliers > 256 || (q->block_tokens % 64) || (int64_t)(q->block_tokens / 64) * q->outliers > 4096)
+    return KVTC_ERR_UNSUPPORTED;
+  PqParams p{};
+  p.L = c.layers; p.H = c.kv_heads; p.T = T;
+  p.k1 = q->k1; p.k2 = q->k2; p.b1 = pq_log2(q->k1); p.b2 = pq_log2(q->k2);
+  p.B = q->outliers; p.bt = q->block_tokens;
+  p.rw = (16 * (p.b1 + p.b2) + 31) / 32;
+  p.nspan = (T + 63) / 64;
+  p.nblk = (T + q->block_tokens - 1) / q->block_tokens;
+  int64_t at = 0;
+  auto take = [&](int64_t bytes) { const int64_t o = at; at += align256(bytes); return o; };
+  const int64_t o1 = take((int64_t)c.layers * 16 * p.k1 * 8 * 2);
+  const int64_t o2 = take((int64_t)c.layers * 16 * p.k2 * 8 * 2);
+  const int64_t o3 = take((int64_t)c.layers * 16 * (p.k1 + p.k2) * 4);
+  const int64_t o4 = take((int64_t)c.layers * 16 * 2 * 4);
+  const int64_t o5 = take((int64_t)c.layers * c.kv_heads * p.nspan * p.B * 16);
+  *ws_need = at;
+  if (ws_at) {
+    p.cb1h = (uint16_t*)(ws_at + o1);
+    p.cb2h = (uint16_t*)(ws_at + o2);
+    p.cn2 = (float*)(ws_at + o3);
+    p.cmax = (float*)(ws_at + o4);
+    p.cand = (uint4*)(ws_at + o5);
+  }
+  *pp = p;
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_pq_sizes(kvtc_plan_t plan, const kvtc_pq_config* q, int32_t T, size_t* code_bytes,
+                          size_t* outlier_slots, size_t* ws_bytes) {
+  if (!plan || !code_bytes || !outlier_slots || !ws_bytes) return KVTC_ERR_INVALID_ARG;
+  PqParams p;
+  int64_t ws = 0;
+  const kvtc_status st = pq_params((const PlanImpl*)plan, q, T, nullptr, &p, &ws);
+  if (st != KVTC_OK) return st;
+  *code_bytes = (size_t)((int64_t)p.L * p.H * T * p.rw * 4);
+  *outlier_slots = (size_t)((int64_t)p.L * p.H * p.nblk * p.B);
+  *ws_bytes = (size_t)ws;
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_pq_encode(kvtc_plan_t plan, const kvtc_pq_config* q, const float* cb1, const float* cb2,
+                           const void* v, int32_t T, uint32_t* codes, size_t code_cap, float* rms, size_t rms_cap,
+                           uint32_t* outliers, size_t outlier_cap, void* ws, size_t ws_bytes, uint32_t* status_dev,
+                           hipStream_t stream) {
+  if (!plan || !ws) return KVTC_ERR_INVALID_ARG;
+  PqParams p;
+  int64_t need = 0;
+  const kvtc_status st = pq_params((const PlanImpl*)plan, q, T, (uint8_t*)ws, &p, &need);
+  if (st != KVTC_OK) return st;
+  if (!cb1 || !cb2 || (T > 0 && (!v || !codes || !rms)) || (T > 0 && p.B > 0 && !outliers)) return KVTC_ERR_INVALID_ARG;
+  if (misaligned(cb1) || misaligned(cb2) || misaligned(v) || misaligned(codes) || misaligned(rms) ||
+      misaligned(outliers) || misaligned(ws) || ((uintptr_t)status_dev & 3u))
+    return KVTC_ERR_INVALID_ARG;
+  const int64_t LH = (int64_t)p.L * p.H;
+  if ((int64_t)ws_bytes < need || (int64_t)code_cap < LH * T * p.rw * 4 || (int64_t)rms_cap < LH * T ||
+      (int64_t)outlier_cap < LH * p.nblk * p.B)
+    return KVTC_ERR_CAPACITY;
+  p.cb1 = cb1; p.cb2 = cb2; p.v = (const uint16_t*)v;
+  p.codes = codes; p.rms = rms; p.outl = outliers; p.status = status_dev;
+  HIP_TRY(launch_pq_encode(p, stream));
+  return KVTC_OK;
+}
+
+kvtc_status kvtc_pq_decode(kvtc_plan_t plan, const kvtc_pq_config* q, const float* cb1, const float* cb2,
+                           const uint32_t* codes, size_t code_bytes, const float* rms, const uint32_t* outliers,
+                           size_t outlier_slots, int32_t T, void* v_out, int32_t out_dtype, void* ws, size_t ws_bytes,
+                           uint32_t* status_dev, hipStream_t stream) {
+  if (!plan || !ws) return KVTC_ERR_INVALID_ARG;
+  PqParams p;
+  int64_t need = 0;
+  const kvtc_status st = pq_params((const PlanImpl*)plan, q, T, (uint8_t*)ws, &p, &need);
+  if (st != KVTC_OK) return st;
+  if (out_dtype != KVTC_BF16 && out_dtype != KVTC_FP32) return KVTC_ERR_INVALID_ARG;
+  if (!cb1 || !cb2 || (T > 0 && (!codes || !rms || !v_out)) || (T > 0 && p.B > 0 && !outliers))
+    return KVTC_ERR_INVALID_ARG;
+  if (misaligned(cb1) || misaligned(cb2) || misaligned(codes) || misaligned(rms) || misaligned(outliers) ||
+      misaligned(v_out) || misaligned(ws) || ((uintptr_t)status_dev & 3u))
+    return KVTC_ERR_INVALID_ARG;
+  const int64_t LH = (int64_t)p.L * p.H;
+  if ((int64_t)ws_bytes < need || (int64_t)code_bytes < LH * T * p.rw * 4 || (int64_t)outlier_slots < LH * p.nblk * p.B)
+    return KVTC_ERR_CAPACITY;
+  p.cb1 = cb1; p.cb2 = cb2; p.codes = (uint32_t*)codes; p.rms = (float*)rms; p.outl = (uint32_t*)outliers;
+  p.v_out = v_out; p.out_dtype = out_dtype; p.status = status_dev;
+  HIP_TRY(launch_pq_decode(p, stream));
+  return KVTC_OK;
+}
+
 }  // extern "C"

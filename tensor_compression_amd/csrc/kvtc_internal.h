@@ -387,6 +387,32 @@ hipError_t launch_batch_place(const Params& p, hipStream_t s);
 hipError_t launch_batch_finish(const Params& p, hipStream_t s);
 hipError_t launch_test_freq_tables(const uint32_t* counts, const int32_t* alpha, int n, int sb, uint16_t* freq,
                                    hipStream_t s);
+// One call of the TTAS-X2 value path (kernels_pq.hip): value sections
+// (layer l, head h) = l H + h, head_dim 128, subvectors of 8 channels.
+struct PqParams {
+  int32_t L, H, T;
+  int32_t k1, k2, b1, b2;  // centroids per subspace and their index bits
+  int32_t B, bt;           // outliers per (section, block), tokens per block
+  int32_t rw;              // u32 words of a token's code row
+  int32_t nspan, nblk;     // 64-token spans and outlier blocks per section
+  int32_t out_dtype;
+  const float* cb1;  // [L][16][k1][8] fp32 (caller's)
+  const float* cb2;  // [L][16][k2][8]
+  uint16_t* cb1h;    // workspace: the codebooks in bf16
+  uint16_t* cb2h;
+  float* cn2;        // workspace: [L][16][k1 + k2] squared norms of the bf16 centroids
+  float* cmax;       // workspace: [L][16][2] largest centroid norm per level
+  uint4* cand;       // workspace: [L H][nspan][B] candidates (|err| bits, index, y bits, 0)
+  const uint16_t* v;
+  uint32_t* codes;        // [L H][T][rw]
+  float* rms;             // [L H][T]
+  uint32_t* outl;         // [L H][nblk][B][2]
+  void* v_out;
+  uint32_t* status;       // device word or null
+};
+hipError_t launch_pq_encode(const PqParams& q, hipStream_t s);
+hipError_t launch_pq_decode(const PqParams& q, hipStream_t s);
+
 // scalar quantisers (head_dim 128, bf16): encode clears *status first
 hipError_t launch_sq_encode(const SqParams& q, hipStream_t s);
 hipError_t launch_sq_decode(const SqParams& q, hipStream_t s);

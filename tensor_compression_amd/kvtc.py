@@ -49,6 +49,15 @@ class SqConfig(ctypes.Structure):
                 ("bits_k", ctypes.c_int32), ("bits_v", ctypes.c_int32)]
 
 
+class PqConfig(ctypes.Structure):
+    _fields_ = [("sub_dim", ctypes.c_int32), ("k1", ctypes.c_int32), ("k2", ctypes.c_int32),
+                ("outliers", ctypes.c_int32), ("block_tokens", ctypes.c_int32)]
+
+
+def make_pq_config(pq: dict) -> PqConfig:
+    return PqConfig(pq["sub_dim"], pq["k1"], pq["k2"], pq["outliers"], pq["block_tokens"])
+
+
 def make_sq_config(sq: dict) -> SqConfig:
     return SqConfig(sq["kind"], sq["group"], sq["tile"], sq["bits_k"], sq["bits_v"])
 
@@ -114,6 +123,17 @@ EXPORTS = {
     "kvtc_test_dequant_project": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
                                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
                                                  ctypes.c_int32, ctypes.c_void_p]),
+    "kvtc_pq_sizes": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                     ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t),
+                                     ctypes.POINTER(ctypes.c_size_t)]),
+    "kvtc_pq_encode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    "kvtc_pq_decode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     "kvtc_sq_sizes": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                      ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]),
     "kvtc_sq_encode": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -431,6 +451,68 @@ class Plan:
         self.sq_decode_async(sq, codes, ranges, T, k_out, v_out, out_dtype)
         torch.cuda.synchronize(self.device)
         return k_out, v_out
+
+    # ---- TTAS-X2 value path (kvtc_pq_*)
+
+    def pq_sizes(self, pq: dict, T: int):
+        """(code bytes, outlier slots, workspace bytes) of a call over T tokens."""
+        c = make_pq_config(pq)
+        a, b, w = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+        _check(lib().kvtc_pq_sizes(self.handle, ctypes.byref(c), T, ctypes.byref(a), ctypes.byref(b),
+                                   ctypes.byref(w)), "kvtc_pq_sizes")
+        return a.value, b.value, w.value
+
+    def pq_buffers(self, pq: dict, T: int):
+        """Fresh device buffers (codes u32, rms f32, outliers u32 [slots, 2], workspace)."""
+        nb, ns, wb = self.pq_sizes(pq, T)
+        L, H = self.cfg["layers"], self.cfg["kv_heads"]
+        codes = torch.zeros(max(nb // 4, 4), dtype=torch.int32, device=self.device)
+        rms = torch.zeros(max(L * H * T, 4), dtype=torch.float32, device=self.device)
+        outl = torch.zeros((max(ns, 2), 2), dtype=torch.int32, device=self.device)
+        ws = torch.empty(max(wb, 256), dtype=torch.uint8, device=self.device)
+        return codes, rms, outl, ws
+
+    def pq_encode_async(self, pq: dict, cb1, cb2, V, codes, rms, outl, ws, status, stream=None):
+        c = make_pq_config(pq)
+        _check(lib().kvtc_pq_encode(self.handle, ctypes.byref(c), _ptr(cb1), _ptr(cb2), _ptr(V), V.shape[2],
+                                    _ptr(codes), codes.numel() * 4, _ptr(rms), rms.numel(), _ptr(outl),
+                                    outl.numel() // 2, _ptr(ws), ws.numel(), _ptr(status), _stream(stream)),
+               "kvtc_pq_encode")
+
+    def pq_decode_async(self, pq: dict, cb1, cb2, codes, rms, outl, T, v_out, ws, status, out_dtype=FP32,
+                        stream=None):
+        c = make_pq_config(pq)
+        _check(lib().kvtc_pq_decode(self.handle, ctypes.byref(c), _ptr(cb1), _ptr(cb2), _ptr(codes),
+                                    codes.numel() * 4, _ptr(rms), _ptr(outl), outl.numel() // 2, T, _ptr(v_out),
+                                    out_dtype, _ptr(ws), ws.numel(), _ptr(status), _stream(stream)),
+               "kvtc_pq_decode")
+
+    def pq_encode(self, pq: dict, cb1, cb2, V):
+        """kvtc_pq_encode: (codes [L,H,T,row_words] u32 as int32, rms [L,H,T],
+        outliers [L,H,blocks,budget,2] as int32, status word)."""
+        L, H, T = V.shape[0], V.shape[1], V.shape[2]
+        nb, ns, _ = self.pq_sizes(pq, T)
+        codes, rms, outl, ws = self.pq_buffers(pq, T)
+        status = torch.zeros(4, dtype=torch.int32, device=self.device)
+        self.pq_encode_async(pq, cb1, cb2, V, codes, rms, outl, ws, status)
+        torch.cuda.synchronize(self.device)
+        nblk = -(-T // pq["block_tokens"])
+        rw = nb // (4 * L * H * T) if T else 0
+        return (codes[: nb // 4].reshape(L, H, T, rw), rms[: L * H * T].reshape(L, H, T),
+                outl[:ns].reshape(L, H, nblk, pq["outliers"], 2), int(status[0].item()))
+
+    def pq_decode(self, pq: dict, cb1, cb2, codes, rms, outl, T: int, out_dtype: int = FP32):
+        """kvtc_pq_decode into a new [L, H, T, D] tensor; returns (values, status word)."""
+        c = self.cfg
+        dt = torch.float32 if out_dtype == FP32 else torch.bfloat16
+        v_out = torch.empty((c["layers"], c["kv_heads"], T, c["head_dim"]), dtype=dt, device=self.device)
+        _, _, wb = self.pq_sizes(pq, T)
+        ws = torch.empty(max(wb, 256), dtype=torch.uint8, device=self.device)
+        status = torch.zeros(4, dtype=torch.int32, device=self.device)
+        o = outl.contiguous() if outl.numel() else torch.zeros((2, 2), dtype=torch.int32, device=self.device)
+        self.pq_decode_async(pq, cb1, cb2, codes.contiguous(), rms.contiguous(), o, T, v_out, ws, status, out_dtype)
+        torch.cuda.synchronize(self.device)
+        return v_out, int(status[0].item())
 
 
 def freq_tables(counts: torch.Tensor, alphabet: torch.Tensor, scale_bits: int):

@@ -1,0 +1,153 @@
+"""GPU parity of the TTAS-X2 value path ("TTAS-X2: Extreme KV Cache
+Compression for Large Language Models", 2.2 V Compression: RMS normalisation,
+Hadamard transform, two-level product quantisation, fixed-budget outliers)
+through the C ABI (kvtc_pq_encode / kvtc_pq_decode) against the oracle.
+
+Rules: the per-token RMS, every level-1 and level-2 index and every outlier
+(index and value) are bit-exact; the decode of the GPU's output is within
+1e-4 of the per-channel RMS of the oracle's decode of the same output, and
+its bf16 form is the round-to-nearest-even cast of its fp32 form."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import parity
+from tensor_compression_amd import calibrate, kvtc, synth
+
+pytestmark = pytest.mark.gpu
+
+PQ = dict(sub_dim=8, k1=256, k2=64, outliers=64, block_tokens=1024)
+
+
+def _setup(tokens=1100, layers=2, seed=21, trained=True, pq=PQ):
+    w = synth.WORKLOADS["llama3_8b"]
+    K, V = synth.generate(w, device="cuda", tokens=tokens, layers=layers, seed=seed)
+    # the TTAS-X2 configuration: keys 4-bit with a per-head scale (WHT plan, keys untransformed)
+    cfg = synth.oracle_config(w, layers=layers, transform=1, bits_k=4.0, bits_v=2.0, wht_keys=0)
+    plan = kvtc.Plan(cfg, None, max_tokens=max(tokens, 1))
+    if trained:
+        cb1, cb2 = calibrate.train_pq_codebooks(V, pq, iters=4, seed=seed)
+    else:
+        rng = np.random.default_rng(seed)
+        cb1 = torch.from_numpy(rng.normal(size=(layers, 16, pq["k1"], 8)).astype(np.float32))
+        cb2 = torch.from_numpy((0.3 * rng.normal(size=(layers, 16, pq["k2"], 8))).astype(np.float32))
+    return cfg, plan, V, cb1, cb2
+
+
+def _check(cfg, plan, pq, V, cb1, cb2):
+    T = V.shape[2]
+    c1, c2 = cb1.cuda(), cb2.cuda()
+    codes, rms, outl, st = plan.pq_encode(pq, c1, c2, V)
+    assert st == 0, st
+    v = synth.to_numpy_bits(V)
+    oc, orms, oo = orc.pq_encode(cfg, pq, v, cb1.numpy(), cb2.numpy())
+    g_codes = codes.cpu().numpy().view(np.uint32)
+    assert np.array_equal(rms.cpu().numpy().view(np.uint32), orms.view(np.uint32)), "rms"
+    diff = g_codes != oc
+    assert not diff.any(), f"{int(diff.any(axis=-1).sum())} token rows differ"
+    g_out = outl.cpu().numpy().view(np.uint32)
+    assert np.array_equal(g_out, oo), "outliers"
+    vd, st = plan.pq_decode(pq, c1, c2, codes, rms, outl, T, kvtc.FP32)
+    assert st == 0
+    ref = orc.pq_decode(cfg, pq, g_codes, rms.cpu().numpy(), g_out, T, cb1.numpy(), cb2.numpy())
+    x = orc.bf16_bits_to_f32(v).reshape(v.shape)
+    parity.compare_decode(vd.cpu().numpy(), ref, parity.channel_rms(x))
+    vb, _ = plan.pq_decode(pq, c1, c2, codes, rms, outl, T, kvtc.BF16)
+    assert torch.equal(vd.to(torch.bfloat16), vb)
+    return codes, rms, outl, vd
+
+
+@pytest.mark.parametrize("pq,trained", [
+    (PQ, True),
+    (dict(PQ, k2=512, outliers=256), True),   # the widest level 2, the largest budget
+    (dict(PQ, k1=128, k2=32, outliers=32, block_tokens=64), False),
+    (dict(PQ, outliers=0), True),
+])
+def test_pq_parity(pq, trained):
+    cfg, plan, V, cb1, cb2 = _setup(pq=pq, trained=trained)
+    _check(cfg, plan, pq, V, cb1, cb2)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 200])
+def test_pq_short_and_ragged(T):
+    pq = dict(PQ, block_tokens=128)
+    cfg, plan, V, cb1, cb2 = _setup(tokens=T, layers=1, seed=T, trained=False, pq=pq)
+    _check(cfg, plan, pq, V, cb1, cb2)
+
+
+def test_pq_zero_cache_ties():
+    """All-zero values: every distance to the zero centroids ties (the lowest
+    index wins) and every error is zero (each block keeps its first
+    coefficients)."""
+    pq = dict(PQ, block_tokens=64, outliers=40)
+    cfg, plan, V, cb1, cb2 = _setup(tokens=150, layers=1, trained=False, pq=pq)
+    cb1[:, :, 5] = 0.0
+    cb1[:, :, 9] = 0.0
+    cb2[:, :, 2] = 0.0
+    codes, rms, outl, vd = _check(cfg, plan, pq, torch.zeros_like(V), cb1, cb2)
+    assert not rms.any() and not vd.any()
+
+
+def test_pq_nonfinite_and_corrupt_outliers():
+    cfg, plan, V, cb1, cb2 = _setup(tokens=200, layers=1, trained=False)
+    c1, c2 = cb1.cuda(), cb2.cuda()
+    V2 = V.clone()
+    V2[0, 2, 77, 5] = float("nan")
+    _, _, _, st = plan.pq_encode(PQ, c1, c2, V2)
+    assert st & (1 << kvtc.ERR_NONFINITE)
+    codes, rms, outl, st = plan.pq_encode(PQ, c1, c2, V)
+    assert st == 0
+    bad = outl.clone()
+    bad[0, 3, 0, 5, 0] = 200 * 128  # past the section's last token
+    _, st = plan.pq_decode(PQ, c1, c2, codes, rms, bad, 200)
+    assert st & (1 << kvtc.ERR_CORRUPT)
+    _, st = plan.pq_decode(PQ, c1, c2, codes, rms, outl, 200)
+    assert st == 0
+
+
+def test_pq_argument_checks():
+    cfg, plan, V, cb1, cb2 = _setup(tokens=128, layers=1, trained=False)
+    for bad, want in ((dict(PQ, k1=24), kvtc.ERR_INVALID_ARG), (dict(PQ, sub_dim=3), kvtc.ERR_INVALID_ARG),
+                      (dict(PQ, outliers=-1), kvtc.ERR_INVALID_ARG), (dict(PQ, block_tokens=0), kvtc.ERR_INVALID_ARG),
+                      (dict(PQ, sub_dim=16), kvtc.ERR_UNSUPPORTED), (dict(PQ, k2=16), kvtc.ERR_UNSUPPORTED),
+                      (dict(PQ, outliers=300), kvtc.ERR_UNSUPPORTED), (dict(PQ, block_tokens=100), kvtc.ERR_UNSUPPORTED),
+                      (dict(PQ, block_tokens=4096, outliers=256), kvtc.ERR_UNSUPPORTED)):
+        with pytest.raises(kvtc.KvtcError) as e:
+            plan.pq_sizes(bad, 128)
+        assert e.value.status == want, bad
+    nb, ns, wb = plan.pq_sizes(PQ, 128)
+    assert nb == 8 * 128 * 4 * ((16 * (8 + 6) + 31) // 32) and ns == 8 * PQ["outliers"]
+    codes, rms, outl, ws = plan.pq_buffers(PQ, 128)
+    with pytest.raises(kvtc.KvtcError) as e:
+        plan.pq_encode_async(PQ, cb1.cuda(), cb2.cuda(), V, codes, rms, outl, ws[: wb - 256], None)
+    assert e.value.status == kvtc.ERR_CAPACITY
+
+
+def test_pq_full_size_sampled_layers():
+    """The Llama-3-8B-shaped cache (32 layers x 8 KV heads x 4096 tokens,
+    bf16) with k-means codebooks, in the benchmark's launch configuration;
+    layers 0 and 31 checked against the oracle on one-layer slices."""
+    w = synth.WORKLOADS["llama3_8b"]
+    K, V = synth.generate(w, device="cuda")
+    cfg = synth.oracle_config(w, transform=1, bits_k=4.0, bits_v=2.0, wht_keys=0)
+    T = V.shape[2]
+    plan = kvtc.Plan(cfg, None, max_tokens=T)
+    cb1, cb2 = calibrate.train_pq_codebooks(V, PQ, iters=4, seed=3)
+    c1, c2 = cb1.cuda(), cb2.cuda()
+    codes, rms, outl, st = plan.pq_encode(PQ, c1, c2, V)
+    assert st == 0
+    vd, st = plan.pq_decode(PQ, c1, c2, codes, rms, outl, T, kvtc.BF16)
+    assert st == 0
+    c_one = dict(cfg, layers=1)
+    for l in (0, 31):
+        v1 = synth.to_numpy_bits(V[l:l + 1].contiguous())
+        oc, orms, oo = orc.pq_encode(c_one, PQ, v1, cb1[l:l + 1].numpy(), cb2[l:l + 1].numpy())
+        assert np.array_equal(codes[l:l + 1].cpu().numpy().view(np.uint32), oc)
+        assert np.array_equal(rms[l:l + 1].cpu().numpy().view(np.uint32), orms.view(np.uint32))
+        assert np.array_equal(outl[l:l + 1].cpu().numpy().view(np.uint32), oo)
+        ref = orc.pq_decode(c_one, PQ, oc, orms, oo, T, cb1[l:l + 1].numpy(), cb2[l:l + 1].numpy())
+        x = orc.bf16_bits_to_f32(v1).reshape(v1.shape)
+        g = vd[l:l + 1].float().cpu().numpy()
+        err = np.abs(g.astype(np.float64) - ref)
+        assert np.all(err <= 1e-4 * parity.channel_rms(x) + 2.0 ** -8 * np.abs(ref) + 1e-30)
