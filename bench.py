@@ -57,6 +57,12 @@ def parse():
     ap.add_argument("--sq-group", type=int, default=16, help="channels per range (block, KIVI values)")
     ap.add_argument("--sq-tile", type=int, default=16, help="tokens per range (block, KIVI keys)")
     ap.add_argument("--sq-bits", type=int, default=4, help="bits per coefficient (keys and values)")
+    ap.add_argument("--pq", action="store_true",
+                    help="time the TTAS-X2 value path (two-level product quantisation) instead of the codec")
+    ap.add_argument("--pq-k1", type=int, default=256)
+    ap.add_argument("--pq-k2", type=int, default=64)
+    ap.add_argument("--pq-outliers", type=int, default=64, help="outliers per (layer, head) and block")
+    ap.add_argument("--pq-block", type=int, default=1024, help="tokens per outlier block")
     ap.add_argument("--ceilings", action="store_true",
                     help="time plain read, write and copy kernels over 520 MB (the practical HBM ceilings) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -86,9 +92,15 @@ PHASE_KERNELS = {
     # scalar quantisers on gauge coordinates (bench.py --sq)
     "sq_encode": (("k_sq_clear", "k_sq_enc128"), ("kernels_sq.hip",)),
     "sq_decode": (("k_sq_dec128",), ("kernels_sq.hip",)),
+    # TTAS-X2 value path (bench.py --pq)
+    "pq_encode": (("k_pq_prep", "k_pq_enc", "k_pq_merge"), ("kernels_pq.hip",)),
+    "pq_decode": (("k_pq_prep", "k_pq_dec"), ("kernels_pq.hip",)),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_llama3_8b.md")
 TRAFFIC_FILE_SQ = os.path.join(ROOT, "profiles", "hbm_traffic_sq_llama3_8b.md")
+TRAFFIC_FILE_PQ = os.path.join(ROOT, "profiles", "hbm_traffic_pq_llama3_8b.md")
+# plain VALU lane operations per second: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 COPY_CAL_BYTES = 1 << 28  # fp32 elements read and written by the calibration copy
 
 
@@ -536,6 +548,116 @@ def run_sq(args, w):
     print(json.dumps(res), flush=True)
 
 
+def run_pq(args, w):
+    """The TTAS-X2 value path: one step = kvtc_pq_encode + kvtc_pq_decode of
+    the whole cache's values with k-means codebooks fitted on them before
+    timing (keys take the codec's 4-bit path, not timed here).  Each call is a
+    prep launch plus the encoder and the outlier merge (or the decoder),
+    timed with HIP events on the launch stream."""
+    import numpy as np
+    import torch
+
+    from tensor_compression_amd import calibrate, kvtc, synth
+
+    K, V = synth.generate(w, device="cuda", tokens=args.tokens, layers=args.layers)
+    del K
+    L, H, T, D = V.shape
+    cfg = synth.oracle_config(w, layers=L, transform=1, bits_k=4.0, bits_v=2.0, wht_keys=0)
+    plan = kvtc.Plan(cfg, None, max_tokens=T)
+    pq = dict(sub_dim=8, k1=args.pq_k1, k2=args.pq_k2, outliers=args.pq_outliers, block_tokens=args.pq_block)
+    cb1, cb2 = calibrate.train_pq_codebooks(V, pq, iters=6, seed=0)
+    c1, c2 = cb1.cuda(), cb2.cuda()
+    nb, ns, wb = plan.pq_sizes(pq, T)
+    codes, rms, outl, ws = plan.pq_buffers(pq, T)
+    ws_d = torch.empty_like(ws)
+    status = torch.zeros(4, dtype=torch.int32, device="cuda")
+    status_d = torch.zeros(4, dtype=torch.int32, device="cuda")
+    vd = torch.empty_like(V)
+    stream = torch.cuda.current_stream()
+
+    def enc():
+        plan.pq_encode_async(pq, c1, c2, V, codes, rms, outl, ws, status, stream)
+
+    def dec():
+        plan.pq_decode_async(pq, c1, c2, codes, rms, outl, T, vd, ws_d, status_d, kvtc.BF16, stream)
+
+    for _ in range(args.warmup):
+        enc()
+        dec()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        enc()
+        dec()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    if int(status[0].item()) or int(status_d[0].item()):
+        raise SystemExit(f"device status {int(status[0].item())} / {int(status_d[0].item())}")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    te, td = [], []
+    for _ in range(args.steps):
+        ev[0].record(stream)
+        enc()
+        ev[1].record(stream)
+        dec()
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        te.append(ev[0].elapsed_time(ev[1]))
+        td.append(ev[1].elapsed_time(ev[2]))
+    ms = {"pq_encode": float(np.mean(te)), "pq_decode": float(np.mean(td))}
+    raw = V.numel() * V.element_size()
+    stored = nb + 4 * L * H * T + 8 * ns
+    N = L * H * T
+    # the search is VALU work: at least one fused score and one running
+    # minimum per candidate centroid, per subvector and level
+    ops = 2 * N * (D // 8) * (pq["k1"] + pq["k2"])
+    ach = ops / (ms["pq_encode"] * 1e-3) / 1e12
+    dec_bytes = stored + raw
+    vf = V.float()
+    nrmse_v = math.sqrt(float(((vf - vd.float()) ** 2).sum()) / max(float((vf ** 2).sum()), 1e-300))
+    res = {
+        "metric": "TTAS-X2 value path encode+decode GB/s of raw bf16 V",
+        "value": raw / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": f"{w.name} values: {L} layers x {H} KV heads x {T} tokens x head_dim {D}, bf16, "
+                        f"RMS + WHT + two-level PQ (8-channel subvectors, K1 {pq['k1']}, K2 {pq['k2']}), "
+                        f"{pq['outliers']} outliers per head and {pq['block_tokens']} tokens, k-means codebooks",
+            "layers": L, "kv_heads": H, "tokens": T, "head_dim": D, "pq": pq,
+        },
+        "raw_bytes": raw, "code_bytes": nb, "rms_bytes": 4 * N, "outlier_bytes": 8 * ns,
+        "compression_ratio": raw / stored, "bits_per_value": 8.0 * stored / V.numel(), "nrmse_v": nrmse_v,
+        "phases_ms": ms,
+        "roofline": {"bound": "alu", "kernel": "pq_encode", "kernels": ["k_pq_enc"], "achieved": ach,
+                     "peak": VALU_PEAK_TOPS, "unit": "T VALU op/s", "frac": ach / VALU_PEAK_TOPS,
+                     "traffic": traffic_from_profile("pq_encode", TRAFFIC_FILE_PQ), "algorithmic_ops": ops,
+                     "avg_ms": ms["pq_encode"]},
+        "decode_roofline": {"bound": "hbm", "kernel": "pq_decode", "algorithmic_bytes": dec_bytes,
+                            "achieved": dec_bytes / (ms["pq_decode"] * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": dec_bytes / (ms["pq_decode"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                            "traffic": traffic_from_profile("pq_decode", TRAFFIC_FILE_PQ)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        v1 = synth.to_numpy_bits(V[:1])
+        c_one = dict(cfg, layers=1)
+        oracle.lib()
+        t_a = time.perf_counter()
+        oc, orms, oo = oracle.pq_encode(c_one, pq, v1, cb1[:1].numpy(), cb2[:1].numpy())
+        t_b = time.perf_counter()
+        oracle.pq_decode(c_one, pq, oc, orms, oo, T, cb1[:1].numpy(), cb2[:1].numpy())
+        t_c = time.perf_counter()
+        res["cpu_baseline"] = {
+            "value": v1.nbytes / (t_c - t_a) / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"layer 0 of {L} ({H} heads x {T} tokens of values): oracle encode {t_b - t_a:.2f} s + "
+                      f"decode {t_c - t_b:.2f} s, single thread",
+        }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -570,6 +692,9 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if args.sq:
         run_sq(args, w)
+        return
+    if args.pq:
+        run_pq(args, w)
         return
     if w.n_seqs > 0:
         run_paged(args, w)
