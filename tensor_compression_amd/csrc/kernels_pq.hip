@@ -20,9 +20,10 @@
 //  k_pq_prep   per (layer, subspace): bf16 codebooks, centroid squared
 //              norms, largest norm per level.
 //  k_pq_enc    stage + RMS + WHT (fp64 butterflies, 16 lanes a token) ->
-//              level 1: v_mfma_f32_32x32x8_bf16 scores ||c||^2 - 2 y.c for 32
-//              centroids x 32 tokens at a time, y split into bf16 hi + lo
-//              operands, running best / second-best per token with the index
+//              level 1: v_mfma_f32_32x32x16_bf16 scores ||c||^2 - 2 y.c for 32
+//              centroids x 32 tokens at a time (a wave takes one subspace
+//              and both 32-token groups of the span), y split into bf16 hi + lo
+//              halves of K, running best / second-best per token with the index
 //              packed into the score's low bits; a token whose best two
 //              scores lie within the score error bound is decided again by
 //              one wave-wide exact fp64 scan -> residual -> level 2 alike ->
@@ -37,7 +38,7 @@ namespace kvtc {
 
 namespace {
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int D = 128;
@@ -103,37 +104,72 @@ __device__ __forceinline__ float rms_wht(const float (&x)[8], int q, float (&c)[
 }
 
 // Best and second-best packed keys (score with the candidate index in its
-// low 9 bits) over k centroids for token 32 g2 + lane % 32 in subspace s;
-// both lane halves end with the same pair.
-__device__ __forceinline__ void search32(const uint16_t* OPH, const uint16_t* OPL, int g2, int s,
-                                         const uint16_t* cbh, const float* cn2, int k, float& best,
-                                         float& second) {
+// low 9 bits) over k centroids for tokens g 32 + lane % 32 (g = 0, 1) in
+// subspace s; both lane halves end with the same pairs.  One 32 x 32 x 16
+// MFMA per block of 32 centroids and token group: K = the subvector's 8
+// channels twice, y's bf16 high part from the lower lane half and its low
+// part from the upper half against the centroid's 8 values in both.  The
+// next block's operands are loaded during this block's scores, which run in
+// four independent min chains per group.
+__device__ __forceinline__ void search64(const uint16_t* OPH, const uint16_t* OPL, int s, const uint16_t* cbh,
+                                         const float* cn2, int k, float (&best)[2], float (&second)[2]) {
   const int lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
-  const int tok = g2 * 32 + n32;
-  const s16x4_t bh = *reinterpret_cast<const s16x4_t*>(&OPH[tok * kHS + s * SD + 4 * hf]);
-  const s16x4_t bl = *reinterpret_cast<const s16x4_t*>(&OPL[tok * kHS + s * SD + 4 * hf]);
-  float b1 = INFINITY, b2 = INFINITY;
-  for (int blk = 0; blk < (k >> 5); ++blk) {
-    const s16x4_t a = *reinterpret_cast<const s16x4_t*>(cbh + (blk * 32 + n32) * SD + 4 * hf);
+  const uint16_t* opr = hf ? OPL : OPH;
+  const bf16x8_t bop0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&opr[n32 * kHS + s * SD]));
+  const bf16x8_t bop1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&opr[(32 + n32) * kHS + s * SD]));
+  float b1[2][4], b2[2][4];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) b1[g][c] = b2[g][c] = INFINITY;
+  const int nb = k >> 5;
+  uint4 an = *reinterpret_cast<const uint4*>(cbh + n32 * SD);
+  float4 cnn[4];
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) cnn[r4] = *reinterpret_cast<const float4*>(cn2 + 8 * r4 + 4 * hf);
+  for (int blk = 0; blk < nb; ++blk) {
+    const uint4 a = an;
     float4 cn[4];
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) cn[r4] = *reinterpret_cast<const float4*>(cn2 + blk * 32 + 8 * r4 + 4 * hf);
-    f32x16_t acc = {};
-    acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, bh, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, bl, acc, 0, 0, 0);
+    for (int r4 = 0; r4 < 4; ++r4) cn[r4] = cnn[r4];
+    if (blk + 1 < nb) {
+      an = *reinterpret_cast<const uint4*>(cbh + ((blk + 1) * 32 + n32) * SD);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        cnn[r4] = *reinterpret_cast<const float4*>(cn2 + (blk + 1) * 32 + 8 * r4 + 4 * hf);
+    }
+    f32x16_t acc[2];
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), bop0, f32x16_t{}, 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), bop1, f32x16_t{}, 0, 0, 0);
+    const uint32_t base = (uint32_t)(blk * 32 + 4 * hf);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const float4 c4 = cn[i >> 2];
       const float cni = (i & 3) == 0 ? c4.x : (i & 3) == 1 ? c4.y : (i & 3) == 2 ? c4.z : c4.w;
-      const float sc = __fmaf_rn(-2.0f, acc[i], cni);
-      const float key = __uint_as_float((__float_as_uint(sc) & ~0x1FFu) | (uint32_t)(blk * 32 + acc_row(i, hf)));
-      b2 = __builtin_amdgcn_fmed3f(b1, b2, key);
-      b1 = fminf(b1, key);
+      const uint32_t idx = base + (uint32_t)(8 * (i >> 2) + (i & 3));
+      const int c = i & 3;
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const float sc = __fmaf_rn(-2.0f, acc[g][i], cni);
+        const float key = __uint_as_float((__float_as_uint(sc) & ~0x1FFu) | idx);
+        b2[g][c] = __builtin_amdgcn_fmed3f(b1[g][c], b2[g][c], key);
+        b1[g][c] = fminf(b1[g][c], key);
+      }
     }
   }
-  const float o1 = __shfl_xor(b1, 32, 64), o2 = __shfl_xor(b2, 32, 64);
-  second = fminf(fmaxf(b1, o1), fminf(b2, o2));
-  best = fminf(b1, o1);
+  // the four chains, then the other lane half
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    float x1 = b1[g][0], x2 = b2[g][0];
+#pragma unroll
+    for (int c = 1; c < 4; ++c) {
+      x2 = fminf(fmaxf(x1, b1[g][c]), fminf(x2, b2[g][c]));
+      x1 = fminf(x1, b1[g][c]);
+    }
+    const float o1 = __shfl_xor(x1, 32, 64), o2 = __shfl_xor(x2, 32, 64);
+    second[g] = fminf(fmaxf(x1, o1), fminf(x2, o2));
+    best[g] = fminf(x1, o1);
+  }
 }
 
 // The exact nearest of k bf16 centroids to the wave-uniform subvector ys:
@@ -170,59 +206,69 @@ __device__ __forceinline__ int exact_nearest(const float (&ys)[SD], const uint16
   return bi < k ? bi : 0;
 }
 
-// The largest key among the `B` largest of nel distinct keys key(e) of
-// `bits` bits (the B-th largest), 11 bits per pass from the top.  Every
-// thread of the (256-thread) workgroup calls it; HIST holds 2048 words of
-// LDS, SM 8.
+// One radix pass of a block-wide selection (256 threads): among the nel
+// keys key(e) that match `prefix` on `pmask`, the digit d of bits
+// [sh, sh + w) holding the need-th largest, and how many of the keys with
+// that digit are still needed.  HIST holds 2048 words of LDS, SM 8.
 template <class KeyFn>
-__device__ uint64_t radix_kth(KeyFn key, int nel, int bits, uint32_t B, uint32_t* HIST, uint32_t* SM) {
+__device__ void radix_pass(KeyFn key, int nel, int sh, int w, uint64_t prefix, uint64_t pmask, uint32_t need,
+                           uint32_t* HIST, uint32_t* SM, uint32_t& digit, uint32_t& need_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint64_t prefix = 0, pmask = 0;
-  uint32_t need = B;
-  for (int top = bits; top > 0; top -= 11) {
-    const int w = top < 11 ? top : 11, sh = top - w;
-    const uint32_t dmask = (1u << w) - 1u;
-    for (int i = tid; i < 2048; i += 256) HIST[i] = 0u;
-    __syncthreads();
-    for (int e = tid; e < nel; e += 256) {
-      const uint64_t kk = key(e);
-      if ((kk & pmask) == prefix) atomicAdd(&HIST[(uint32_t)(kk >> sh) & dmask], 1u);
-    }
-    __syncthreads();
-    uint32_t c[8], loc = 0;
+  const uint32_t dmask = (1u << w) - 1u;
+  for (int i = tid; i < 2048; i += 256) HIST[i] = 0u;
+  __syncthreads();
+  for (int e = tid; e < nel; e += 256) {
+    const uint64_t kk = key(e);
+    if ((kk & pmask) == prefix) atomicAdd(&HIST[(uint32_t)(kk >> sh) & dmask], 1u);
+  }
+  __syncthreads();
+  uint32_t c[8], loc = 0;
 #pragma unroll
-    for (int z = 0; z < 8; ++z) {
-      c[z] = HIST[8 * tid + z];
-      loc += c[z];
-    }
-    // counts in the bins above this thread's: a suffix sum over the threads
-    uint32_t x = loc;
+  for (int z = 0; z < 8; ++z) {
+    c[z] = HIST[8 * tid + z];
+    loc += c[z];
+  }
+  // counts in the bins above this thread's: a suffix sum over the threads
+  uint32_t x = loc;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_down(x, o, 64);
-      if (lane + o < 64) x += y;
-    }
-    if (lane == 0) SM[wave] = x;
-    __syncthreads();
-    uint32_t above = x - loc;
-    for (int w2 = wave + 1; w2 < 4; ++w2) above += SM[w2];
-    __syncthreads();
-    if (above < need && above + loc >= need) {
-      uint32_t run = above;
-      for (int z = 7; z >= 0; --z) {
-        if (run + c[z] >= need) {
-          SM[4] = (uint32_t)(8 * tid + z);
-          SM[5] = need - run;
-          break;
-        }
-        run += c[z];
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_down(x, o, 64);
+    if (lane + o < 64) x += y;
+  }
+  if (lane == 0) SM[wave] = x;
+  __syncthreads();
+  uint32_t above = x - loc;
+  for (int w2 = wave + 1; w2 < 4; ++w2) above += SM[w2];
+  __syncthreads();
+  if (above < need && above + loc >= need) {
+    uint32_t run = above;
+    for (int z = 7; z >= 0; --z) {
+      if (run + c[z] >= need) {
+        SM[4] = (uint32_t)(8 * tid + z);
+        SM[5] = need - run;
+        break;
       }
+      run += c[z];
     }
-    __syncthreads();
-    prefix |= (uint64_t)SM[4] << sh;
-    pmask |= (uint64_t)dmask << sh;
-    need = SM[5];
-    __syncthreads();
+  }
+  __syncthreads();
+  digit = SM[4];
+  need_out = SM[5];
+  __syncthreads();
+}
+
+// The B-th largest of nel distinct keys key(e) below bit `top` that match
+// `prefix` on `pmask`, 11 bits per pass from the top.
+template <class KeyFn>
+__device__ uint64_t radix_kth(KeyFn key, int nel, int top, uint32_t B, uint32_t* HIST, uint32_t* SM,
+                              uint64_t prefix = 0, uint64_t pmask = 0) {
+  uint32_t need = B;
+  for (; top > 0; top -= 11) {
+    const int w = top < 11 ? top : 11, sh = top - w;
+    uint32_t d;
+    radix_pass(key, nel, sh, w, prefix, pmask, need, HIST, SM, d, need);
+    prefix |= (uint64_t)d << sh;
+    pmask |= (uint64_t)((1u << w) - 1u) << sh;
   }
   return prefix;
 }
@@ -284,11 +330,19 @@ __global__ __launch_bounds__(256) void k_pq_enc(const PqParams q) {
   {
     const int q16 = lane & 15, grp = tid >> 4;
     bool bad = false;
+    uint4 raw[4];
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {  // every row of the span in flight at once
+      const int tok = pass * 16 + grp;
+      raw[pass] = tok < n ? *reinterpret_cast<const uint4*>(q.v + ((int64_t)sec * q.T + t0 + tok) * D + 8 * q16)
+                          : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
       const int tok = pass * 16 + grp;
       const bool valid = tok < n;
-      float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (valid) unpack8(*reinterpret_cast<const uint4*>(q.v + ((int64_t)sec * q.T + t0 + tok) * D + 8 * q16), x);
+      float x[8];
+      unpack8(raw[pass], x);
 #pragma unroll
       for (int e = 0; e < 8; ++e) bad |= !finite_f(x[e]);
       float c[8];
@@ -320,36 +374,40 @@ __global__ __launch_bounds__(256) void k_pq_enc(const PqParams q) {
   for (int level = 0; level < 2; ++level) {
     const int k = level ? q.k2 : q.k1;
     uint32_t* const I = level ? I2 : I1;
-    for (int it = 0; it < 8; ++it) {
-      const int unit = wave + 4 * it, s = unit >> 1, g2 = unit & 1;
+    for (int it = 0; it < 4; ++it) {
+      const int s = wave + 4 * it;
       const int64_t ls = ls0 + s;
       const uint16_t* cbh = (level ? q.cb2h : q.cb1h) + ls * k * SD;
       const float* cn2 = q.cn2 + ls * (q.k1 + q.k2) + (level ? q.k1 : 0);
       const float cm = q.cmax[ls * 2 + level];
-      float best, second;
-      search32(OPH, OPL, g2, s, cbh, cn2, k, best, second);
-      const int tok = g2 * 32 + n32;
-      const float thr = 0x1p-13f * (YN[tok * NS + s] * cm + cm * cm) + 0x1p-12f * (fabsf(best) + fabsf(second));
-      const bool owner = hf == 0 && tok < n;
-      // every token gets an index (tokens past the span keep a valid one)
-      if (hf == 0) I[tok * NS + s] = __float_as_uint(best) & 0x1FFu;
-      // near ties: decided again exactly, one wave-wide scan each
-      uint64_t pend = __ballot(owner && !(__fsub_rn(second, best) > thr));
-      while (pend) {
-        const int L = __ffsll((unsigned long long)pend) - 1;
-        const int tk = g2 * 32 + (L & 31);
-        float ys[SD];
+      float best[2], second[2];
+      search64(OPH, OPL, s, cbh, cn2, k, best, second);
 #pragma unroll
-        for (int j = 0; j < SD; ++j) ys[j] = Y[tk * kYS + s * SD + j];
-        if (level) {
-          float c1[8];
-          unpack8(*reinterpret_cast<const uint4*>(q.cb1h + (ls * q.k1 + (I1[tk * NS + s] & (q.k1 - 1))) * SD), c1);
+      for (int g2 = 0; g2 < 2; ++g2) {
+        const int tok = g2 * 32 + n32;
+        const float thr =
+            0x1p-13f * (YN[tok * NS + s] * cm + cm * cm) + 0x1p-12f * (fabsf(best[g2]) + fabsf(second[g2]));
+        const bool owner = hf == 0 && tok < n;
+        // every token gets an index (tokens past the span keep a valid one)
+        if (hf == 0) I[tok * NS + s] = __float_as_uint(best[g2]) & 0x1FFu;
+        // near ties: decided again exactly, one wave-wide scan each
+        uint64_t pend = __ballot(owner && !(__fsub_rn(second[g2], best[g2]) > thr));
+        while (pend) {
+          const int L = __ffsll((unsigned long long)pend) - 1;
+          const int tk = g2 * 32 + (L & 31);
+          float ys[SD];
 #pragma unroll
-          for (int j = 0; j < SD; ++j) ys[j] = __fsub_rn(ys[j], c1[j]);
+          for (int j = 0; j < SD; ++j) ys[j] = Y[tk * kYS + s * SD + j];
+          if (level) {
+            float c1[8];
+            unpack8(*reinterpret_cast<const uint4*>(q.cb1h + (ls * q.k1 + (I1[tk * NS + s] & (q.k1 - 1))) * SD), c1);
+#pragma unroll
+            for (int j = 0; j < SD; ++j) ys[j] = __fsub_rn(ys[j], c1[j]);
+          }
+          const int bi = exact_nearest(ys, cbh, k);
+          if (lane == L) I[tk * NS + s] = (uint32_t)bi;
+          pend &= pend - 1;
         }
-        const int bi = exact_nearest(ys, cbh, k);
-        if (lane == L) I[tk * NS + s] = (uint32_t)bi;
-        pend &= pend - 1;
       }
     }
     __syncthreads();
@@ -418,18 +476,45 @@ __global__ __launch_bounds__(256) void k_pq_enc(const PqParams q) {
     return ((uint64_t)(__float_as_uint(DEL[e]) & 0x7fffffffu) << 13) | (uint64_t)(8191 - e);
   };
   const uint32_t B = (uint32_t)q.B;
-  uint64_t tau = 0;
-  if ((uint32_t)nel > B) tau = radix_kth(key, nel, 44, B, HIST, SM);
-  if (tid == 0) SM[6] = 0u;
-  __syncthreads();
   uint4* cand = q.cand + ((int64_t)sec * q.nspan + span) * q.B;
-  for (int e = tid; e < nel; e += 256) {
-    if ((uint32_t)nel <= B || key(e) >= tau) {
-      const uint32_t slot = atomicAdd(&SM[6], 1u);
-      const int tok = e >> 7, j = e & 127;
-      if (slot < B)
-        cand[slot] = make_uint4(__float_as_uint(DEL[e]) & 0x7fffffffu, (uint32_t)((t0 + tok) * D + j),
-                              __float_as_uint(Y[tok * kYS + j]), 0u);
+  auto put = [&](uint64_t kk, uint32_t slot) {
+    const int e = 8191 - (int)(kk & 8191u);
+    const int tok = e >> 7, j = e & 127;
+    if (slot < B)
+      cand[slot] = make_uint4((uint32_t)(kk >> 13), (uint32_t)((t0 + tok) * D + j), __float_as_uint(Y[tok * kYS + j]), 0u);
+  };
+  if ((uint32_t)nel <= B) {
+    for (int e = tid; e < nel; e += 256) put(key(e), (uint32_t)e);
+    return;
+  }
+  // the top 11 bits over every key; keys above the threshold digit are
+  // selected outright, those on it go to a short list for the remaining passes
+  uint32_t d0, need;
+  radix_pass(key, nel, 33, 11, 0, 0, B, HIST, SM, d0, need);
+  const uint32_t on_digit = HIST[d0];
+  uint64_t* const LIST = reinterpret_cast<uint64_t*>(AUX + 2048);  // 512 keys past HIST
+  constexpr uint32_t kList = 512;
+  if (tid == 0) { SM[6] = 0u; SM[7] = 0u; }
+  __syncthreads();
+  if (on_digit <= kList) {
+    for (int e = tid; e < nel; e += 256) {
+      const uint64_t kk = key(e);
+      const uint32_t dg = (uint32_t)(kk >> 33);
+      if (dg > d0) put(kk, atomicAdd(&SM[6], 1u));
+      else if (dg == d0) LIST[atomicAdd(&SM[7], 1u)] = kk;
+    }
+    __syncthreads();
+    const int nl = (int)SM[7];
+    const uint64_t tau = radix_kth([&](int e) { return LIST[e]; }, nl, 33, need, HIST, SM, (uint64_t)d0 << 33,
+                                   (uint64_t)0x7FF << 33);
+    for (int e = tid; e < nl; e += 256)
+      if (LIST[e] >= tau) put(LIST[e], atomicAdd(&SM[6], 1u));
+  } else {
+    // many equal top digits (e.g. an all-zero error): the remaining passes over every key
+    const uint64_t tau = radix_kth(key, nel, 33, need, HIST, SM, (uint64_t)d0 << 33, (uint64_t)0x7FF << 33);
+    for (int e = tid; e < nel; e += 256) {
+      const uint64_t kk = key(e);
+      if (kk >= tau) put(kk, atomicAdd(&SM[6], 1u));
     }
   }
 }

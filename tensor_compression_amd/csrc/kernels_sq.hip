@@ -39,10 +39,9 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kSpan = 64;   // tokens per workgroup
+constexpr int kSpan = 64;   // tokens per span
 constexpr int kXS = 136;    // bf16 row stride of staged rows (16-B aligned, 4-bank shift)
 constexpr int kCS = 132;    // fp32 row stride of the coefficient / output tile
-constexpr int kPS = 65;     // row stride of the per-(token, run) partials
 
 __device__ __forceinline__ void unpack8(uint4 a, float* o) {
   o[0] = __uint_as_float(a.x << 16); o[1] = __uint_as_float(a.x & 0xffff0000u);
@@ -85,12 +84,11 @@ __device__ __forceinline__ void make_range(float mn, float mx, int b, float* zer
 
 }  // namespace
 
-// Dynamic LDS of the encoder: the per-(token, run) partials, later the packed
-// rows, then the span's range table (zero, reciprocal).
+// Dynamic LDS of the encoder: the packed rows, then the span's range table
+// (zero, reciprocal).
 __host__ __device__ inline int sq_enc_part_bytes(int b, int ce) {
-  const int part = ce > 1 ? (128 / ce) * kPS * 8 : 0;
-  const int pack = kSpan * 4 * b * 4;
-  return ((part > pack ? part : pack) + 15) & ~15;
+  (void)ce;
+  return (kSpan * 4 * b * 4 + 15) & ~15;
 }
 __host__ __device__ inline int sq_span_ranges(int te, int ce) { return (kSpan / te) * (128 / ce); }
 
@@ -98,10 +96,103 @@ __global__ void k_sq_clear(uint32_t* status) {
   if (threadIdx.x == 0) *status = 0u;
 }
 
+// Quantise and pack the 32 channels [32 w, 32 w + 32) of token t = lane of
+// the span (wave w): codes clamp(rint((c - zero) rcp)) into B whole words at
+// word (t 4 + w) B.  A coarse test per value flags the lane when some
+// pre-rounding value v may lie within its error bound of a rounding
+// boundary (the bound taken at its largest, |v| <= 2^B); such lanes find
+// their values one by one, and each is recomputed from the exact
+// coefficient (one wave-wide fp64 dot product of the staged row and the
+// basis row).
+template <int B>
+__device__ __forceinline__ void quant_pack(const SqParams& q, const float* C, const uint16_t* X, const uint16_t* bt,
+                                           const float2* R, const float* nrm, uint32_t* PK, int n, int lte, int lce,
+                                           int lncg) {
+  constexpr int D = 128;
+  constexpr float QM = (float)((1u << B) - 1u);
+  constexpr uint32_t MASK = (1u << B) - 1u;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = lane;
+  const bool valid = t < n;
+  const int rrow = (t >> lte) << lncg;
+  const float ecm = valid ? q.mfma_err * nrm[t] : 0.0f;
+  const float slack = 3.0f * 0x1p-23f * (QM + 1.0f);
+  uint32_t w[B];
+#pragma unroll
+  for (int i = 0; i < B; ++i) w[i] = 0u;
+  float worst = -1.0f;  // max over values of |v - rint(v)| - (1/2 - bound)
+  if (valid) {
+#pragma unroll
+    for (int k4 = 0; k4 < 8; ++k4) {
+      const float4 v4 = *reinterpret_cast<const float4*>(&C[t * kCS + 32 * wave + 4 * k4]);
+      const float cv[4] = {v4.x, v4.y, v4.z, v4.w};
+      float2 zr[4];
+      if (lce >= 2) {
+        zr[0] = zr[1] = zr[2] = zr[3] = R[rrow + ((32 * wave + 4 * k4) >> lce)];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zr[e] = R[rrow + ((32 * wave + 4 * k4 + e) >> lce)];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 4 * k4 + e;
+        const float v = __fmul_rn(__fsub_rn(cv[e], zr[e].x), zr[e].y);
+        const float rv = __builtin_rintf(v);
+        const uint32_t code = (uint32_t)__builtin_amdgcn_fmed3f(rv, 0.0f, QM);
+        const float hth = 0.5f - __fmaf_rn(ecm, zr[e].y, slack);
+        worst = fmaxf(worst, fabsf(__fsub_rn(v, rv)) - hth);
+        const int bit = c * B;
+        w[bit >> 5] |= code << (bit & 31);
+        if ((bit & 31) + B > 32) w[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
+      }
+    }
+  }
+  // the lanes that may hold a near-boundary value list them precisely
+  uint32_t flags = 0u;
+  if (worst >= 0.0f) {
+    for (int c = 0; c < 32; ++c) {
+      const float cvv = C[t * kCS + 32 * wave + c];
+      const float2 zr = R[rrow + ((32 * wave + c) >> lce)];
+      const float v = __fmul_rn(__fsub_rn(cvv, zr.x), zr.y);
+      const float hth = 0.5f - __fmaf_rn(ecm, zr.y, slack);
+      if (fabsf(__fsub_rn(v, __builtin_rintf(v))) >= hth) flags |= 1u << c;
+    }
+  }
+  uint64_t pend = __ballot(flags != 0u);
+  while (pend) {
+    const int L = __ffsll((unsigned long long)pend) - 1;
+    const uint32_t fl = __shfl(flags, L, 64);
+    const int c = __ffs(fl) - 1;
+    const int i = 32 * wave + c;
+    const uint32_t xw = *reinterpret_cast<const uint32_t*>(&X[L * kXS + 2 * lane]);
+    const uint32_t bw = *reinterpret_cast<const uint32_t*>(bt + (int64_t)i * D + 2 * lane);
+    double part = __fma_rn((double)__uint_as_float(xw << 16), (double)__uint_as_float(bw << 16),
+                           (double)__uint_as_float(xw & 0xffff0000u) * (double)__uint_as_float(bw & 0xffff0000u));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
+    if (lane == L) {
+      const float2 zr = R[rrow + (i >> lce)];
+      const float v = __fmul_rn(__fsub_rn((float)part, zr.x), zr.y);
+      const uint32_t code = (uint32_t)__builtin_amdgcn_fmed3f(__builtin_rintf(v), 0.0f, QM);
+      const int bit = c * B, wi = bit >> 5, sh = bit & 31;
+#pragma unroll
+      for (int k = 0; k < B; ++k) {
+        if (k == wi) w[k] = (w[k] & ~(MASK << sh)) | (code << sh);
+        if (sh + B > 32 && k == wi + 1) w[k] = (w[k] & ~(MASK >> (32 - sh))) | (code >> (32 - sh));
+      }
+      flags &= ~(1u << c);
+    }
+    pend = __ballot(flags != 0u);
+  }
+  if (valid) {
+    uint32_t* dst = PK + (t * 4 + wave) * B;
+#pragma unroll
+    for (int k = 0; k < B; ++k) dst[k] = w[k];
+  }
+}
+
 __global__ __launch_bounds__(256) void k_sq_enc128(const SqParams q) {
   constexpr int D = 128;
-  const int u = blockIdx.y, t0 = blockIdx.x * kSpan;
-  const int n = min(kSpan, q.T - t0);
+  const int u = blockIdx.y;
   const int H = q.H, h = u % H, s = (u / H) & 1, l = u / (2 * H);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r = lane & 15;
   const int b = q.bits[s], te = q.te[s], ce = q.ce[s];
@@ -116,9 +207,7 @@ __global__ __launch_bounds__(256) void k_sq_enc128(const SqParams q) {
   __shared__ float nrm[kSpan];
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
   const int part_bytes = sq_enc_part_bytes(b, ce);
-  float* const Pmn = reinterpret_cast<float*>(dyn);  // [ncg][kPS]
-  float* const Pmx = Pmn + ncg * kPS;
-  uint32_t* const PK = reinterpret_cast<uint32_t*>(dyn);  // packed rows (after the ranges)
+  uint32_t* const PK = reinterpret_cast<uint32_t*>(dyn);          // packed rows
   float2* const R = reinterpret_cast<float2*>(dyn + part_bytes);  // (zero, rcp) per range
 
   const uint16_t* bt = q.basis_t + basis_of(q, l, s, h) * D * D;
@@ -132,13 +221,14 @@ __global__ __launch_bounds__(256) void k_sq_enc128(const SqParams q) {
 
   // ---- stage: thread (token tid / 4, quarter tid % 4) holds channel runs
   // [16 q, 16 q + 16) and [64 + 16 q, +16): both members of every RoPE pair
-  {
-    const int st_t = tid >> 2, st_q = tid & 3;
-    const bool valid = st_t < n;
-    const int pos = t0 + st_t;
-    const bool rope = s == 0 && q.rope_keys;
-    uint4 y[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-    float4 cs[8];
+  const int st_t = tid >> 2, st_q = tid & 3;
+  const bool rope = s == 0 && q.rope_keys;
+  uint4 y[4];
+  float4 cs[8];
+  auto load_rows = [&](int ts, int ns) {
+    const bool valid = st_t < ns;
+    const int pos = ts + st_t;
+    y[0] = y[1] = y[2] = y[3] = make_uint4(0, 0, 0, 0);
     if (valid) {
       const uint16_t* row = (s ? q.v : q.k) + (((int64_t)l * H + h) * q.T + pos) * D;
       y[0] = *reinterpret_cast<const uint4*>(row + 16 * st_q);
@@ -158,6 +248,12 @@ __global__ __launch_bounds__(256) void k_sq_enc128(const SqParams q) {
         }
       }
     }
+  };
+  const int t0 = blockIdx.x * kSpan;
+  const int n = min(kSpan, q.T - t0);
+  load_rows(t0, n);
+  {
+    const bool valid = st_t < n;
     float lo[16], hi[16];
     unpack8(y[0], lo); unpack8(y[1], lo + 8);
     unpack8(y[2], hi); unpack8(y[3], hi + 8);
@@ -241,128 +337,90 @@ __global__ __launch_bounds__(256) void k_sq_enc128(const SqParams q) {
 
   // ---- ranges
   bool bad = false;
-  if (ce > 1) {
-    // per (token, run): lanes take consecutive tokens
-    for (int it = tid; it < kSpan * ncg; it += 256) {
-      const int t = it & (kSpan - 1), cg = it >> 6;
-      const float* c = &C[t * kCS + cg * ce];
-      float mn = INFINITY, mx = -INFINITY;
-      if (ce >= 4) {
-        for (int j = 0; j < ce; j += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(c + j);
-          mn = fminf(fminf(mn, v.x), fminf(v.y, fminf(v.z, v.w)));
-          mx = fmaxf(fmaxf(mx, v.x), fmaxf(v.y, fmaxf(v.z, v.w)));
-          if (t < n) bad |= !(finite(v.x) && finite(v.y) && finite(v.z) && finite(v.w));
-        }
-      } else {
-        for (int j = 0; j < ce; ++j) {
-          mn = fminf(mn, c[j]);
-          mx = fmaxf(mx, c[j]);
-          if (t < n) bad |= !finite(c[j]);
-        }
-      }
-      Pmn[cg * kPS + t] = mn;
-      Pmx[cg * kPS + t] = mx;
-    }
-    __syncthreads();
-  }
   {
     const int64_t rbase = sec_off(u, H, q.n_ranges[0], q.n_ranges[1]) + (int64_t)(t0 >> lte) * ncg;
-    for (int it = tid; it < nrs; it += 256) {
-      const int cg = it & (ncg - 1), tj = it >> lncg;
-      const int ta = tj * te, tb = min(ta + te, n);
-      float mn = INFINITY, mx = -INFINITY;
-      if (ce > 1) {
-        for (int t = ta; t < tb; ++t) {
-          mn = fminf(mn, Pmn[cg * kPS + t]);
-          mx = fmaxf(mx, Pmx[cg * kPS + t]);
+    if (ce > 1) {
+      // lane = token, wave = channel runs wave, wave + 4, ...: the run's
+      // extremes, then across the te tokens of a range with lane shuffles
+      for (int cg = wave; cg < ncg; cg += 4) {
+        const int t = lane;
+        const float* c = &C[t * kCS + cg * ce];
+        float mn = INFINITY, mx = -INFINITY;
+        if (ce >= 4) {
+          for (int j = 0; j < ce; j += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(c + j);
+            mn = fminf(fminf(mn, v.x), fminf(v.y, fminf(v.z, v.w)));
+            mx = fmaxf(fmaxf(mx, v.x), fmaxf(v.y, fmaxf(v.z, v.w)));
+            bad |= !(finite(v.x) && finite(v.y) && finite(v.z) && finite(v.w));
+          }
+        } else {
+          for (int j = 0; j < ce; ++j) {
+            mn = fminf(mn, c[j]);
+            mx = fmaxf(mx, c[j]);
+            bad |= !finite(c[j]);
+          }
         }
-      } else {
-        for (int t = ta; t < tb; ++t) {
+        if (t >= n) {  // tokens past the span take no part
+          mn = INFINITY;
+          mx = -INFINITY;
+          bad = false;
+        }
+        for (int o = 1; o < te; o <<= 1) {
+          mn = fminf(mn, __shfl_xor(mn, o, 64));
+          mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        }
+        if ((t & (te - 1)) == 0) {
+          const int it = ((t >> lte) << lncg) + cg;
+          float zero = 0.f, scale = 0.f, rcp = 0.f;
+          if (t < n) {
+            make_range(mn, mx, b, &zero, &scale, &rcp);
+            *reinterpret_cast<float2*>(q.ranges + 2 * (rbase + it)) = make_float2(zero, scale);
+          }
+          R[it] = make_float2(zero, rcp);
+        }
+      }
+    } else {
+      // one channel a range: a column scan of te tokens, four loads in flight
+      for (int it = tid; it < nrs; it += 256) {
+        const int cg = it & (ncg - 1), tj = it >> lncg;
+        const int ta = tj * te, tb = min(ta + te, n);
+        float mn = INFINITY, mx = -INFINITY;
+        int t = ta;
+        for (; t + 4 <= tb; t += 4) {
+          const float c0 = C[t * kCS + cg], c1 = C[(t + 1) * kCS + cg];
+          const float c2 = C[(t + 2) * kCS + cg], c3 = C[(t + 3) * kCS + cg];
+          mn = fminf(fminf(mn, c0), fminf(c1, fminf(c2, c3)));
+          mx = fmaxf(fmaxf(mx, c0), fmaxf(c1, fmaxf(c2, c3)));
+          bad |= !(finite(c0) && finite(c1) && finite(c2) && finite(c3));
+        }
+        for (; t < tb; ++t) {
           const float c = C[t * kCS + cg];
           mn = fminf(mn, c);
           mx = fmaxf(mx, c);
           bad |= !finite(c);
         }
+        float zero = 0.f, scale = 0.f, rcp = 0.f;
+        if (ta < n) {
+          make_range(mn, mx, b, &zero, &scale, &rcp);
+          *reinterpret_cast<float2*>(q.ranges + 2 * (rbase + it)) = make_float2(zero, scale);
+        }
+        R[it] = make_float2(zero, rcp);
       }
-      float zero = 0.f, scale = 0.f, rcp = 0.f;
-      if (ta < n) {
-        make_range(mn, mx, b, &zero, &scale, &rcp);
-        *reinterpret_cast<float2*>(q.ranges + 2 * (rbase + it)) = make_float2(zero, scale);
-      }
-      R[it] = make_float2(zero, rcp);
     }
   }
   if (bad && q.status) atomicOr(q.status, 1u << KVTC_ERR_NONFINITE);
-  __syncthreads();  // the range table is complete; the partials are free
+  __syncthreads();  // the range table is complete
 
   // ---- quantise and pack: lane = token, wave = channel quarter [32 w, 32 w + 32)
-  {
-    const int t = lane;
-    const float qmax = (float)((1u << b) - 1u);
-    uint32_t c8[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};  // four 8-bit codes per word
-    uint32_t flags = 0u;
-    const int rrow = (t >> lte) << lncg;
-    if (t < n) {
-      const float ecm = q.mfma_err * nrm[t];
-#pragma unroll
-      for (int k4 = 0; k4 < 8; ++k4) {
-        const float4 v4 = *reinterpret_cast<const float4*>(&C[t * kCS + 32 * wave + 4 * k4]);
-        const float cv[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = 4 * k4 + e;
-          const float2 zr = R[rrow + ((32 * wave + c) >> lce)];
-          const float v = __fmul_rn(__fsub_rn(cv[e], zr.x), zr.y);
-          const float rv = __builtin_rintf(v);
-          const float qf = fminf(fmaxf(rv, 0.0f), qmax);
-          c8[k4] |= (uint32_t)qf << (8 * e);
-          const float ev = __fmaf_rn(ecm, zr.y, 3.0f * 0x1p-23f * fmaxf(fabsf(v), 1.0f));
-          if (fabsf(fabsf(__fsub_rn(v, rv)) - 0.5f) < ev) flags |= 1u << c;
-        }
-      }
-    }
-    // values near a rounding boundary: the exact coefficient, one wave-wide
-    // fp64 dot product of the staged row and the basis row each
-    uint64_t pend = __ballot(flags != 0u);
-    while (pend) {
-      const int L = __ffsll((unsigned long long)pend) - 1;
-      const uint32_t fl = __shfl(flags, L, 64);
-      const int bit = __ffs(fl) - 1;
-      const int i = 32 * wave + bit;
-      const uint32_t xw = *reinterpret_cast<const uint32_t*>(&X[L * kXS + 2 * lane]);
-      const uint32_t bw = *reinterpret_cast<const uint32_t*>(bt + (int64_t)i * D + 2 * lane);
-      double part = __fma_rn((double)__uint_as_float(xw << 16), (double)__uint_as_float(bw << 16),
-                             (double)__uint_as_float(xw & 0xffff0000u) * (double)__uint_as_float(bw & 0xffff0000u));
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) part += __shfl_xor(part, o, 64);
-      if (lane == L) {
-        const float2 zr = R[rrow + (i >> lce)];
-        const float v = __fmul_rn(__fsub_rn((float)part, zr.x), zr.y);
-        const float qf = fminf(fmaxf(__builtin_rintf(v), 0.0f), qmax);
-#pragma unroll
-        for (int k4 = 0; k4 < 8; ++k4)
-          if (k4 == (bit >> 2)) c8[k4] = (c8[k4] & ~(0xffu << (8 * (bit & 3)))) | ((uint32_t)qf << (8 * (bit & 3)));
-        flags &= ~(1u << bit);
-      }
-      pend = __ballot(flags != 0u);
-    }
-    // 32 codes of b bits = b whole words at word (t 4 + w) b of the span
-    if (t < n) {
-      uint32_t* dst = PK + (t * 4 + wave) * b;
-      uint64_t acc = 0;
-      int nb = 0, wo = 0;
-#pragma unroll
-      for (int c = 0; c < 32; ++c) {
-        acc |= (uint64_t)((c8[c >> 2] >> (8 * (c & 3))) & 0xffu) << nb;
-        nb += b;
-        if (nb >= 32) {
-          dst[wo++] = (uint32_t)acc;
-          acc >>= 32;
-          nb -= 32;
-        }
-      }
-    }
+  switch (b) {
+    case 1: quant_pack<1>(q, C, X, bt, R, nrm, PK, n, lte, lce, lncg); break;
+    case 2: quant_pack<2>(q, C, X, bt, R, nrm, PK, n, lte, lce, lncg); break;
+    case 3: quant_pack<3>(q, C, X, bt, R, nrm, PK, n, lte, lce, lncg); break;
+    case 4: quant_pack<4>(q, C, X, bt, R, nrm, PK, n, lte, lce, lncg); break;
+    case 5: quant_pack<5>(q, C, X, bt, R, nrm, PK, n, lte, lce, lncg); break;
+    case 6: quant_pack<6>(q, C, X, bt, R, nrm, PK, n, lte, lce, lncg); break;
+    case 7: quant_pack<7>(q, C, X, bt, R, nrm, PK, n, lte, lce, lncg); break;
+    default: quant_pack<8>(q, C, X, bt, R, nrm, PK, n, lte, lce, lncg); break;
   }
   __syncthreads();
   {
