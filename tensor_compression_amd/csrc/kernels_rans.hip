@@ -305,6 +305,24 @@ __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw
       __builtin_amdgcn_wave_barrier();
       const uint32_t* rw = rb + (ci & 1) * kRowWords;
       uint32_t* hc = hist + (ci * kHistCopies + (lane & (kHistCopies - 1))) * 17;
+      if constexpr (LANES == 32 && STEPS > 0) {
+        // token k = 32 s + j sits at word s b + (j b >> 5) of the row, at the
+        // lane's constant shift (j b) & 31: every word of the component first
+        const uint32_t jb = (uint32_t)j * b, sh = jb & 31u, mask = (1u << b) - 1u;
+        const uint32_t* rwl = rw + (jb >> 5);
+        uint32_t lo[STEPS], hi[STEPS];
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+          lo[s] = rwl[s * b];
+          hi[s] = rwl[s * b + 1];
+        }
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+          const uint32_t code = __builtin_amdgcn_alignbit(hi[s], lo[s], sh) & mask;
+          if (valid && s * LANES + j < m) atomicAdd(&hc[code >> rr], 1u);
+        }
+        return;
+      }
 #pragma unroll
       for (int s = 0; s < (STEPS > 0 ? STEPS : steps_max); ++s) {
         const int k = s * LANES + j;
@@ -384,6 +402,66 @@ __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw
       __builtin_amdgcn_wave_barrier();
       const uint32_t* rw = rb + (ci & 1) * kRowWords;
       const uint4* tc = reinterpret_cast<const uint4*>(tab + ci * 16);
+      if constexpr (LANES == 32 && STEPS > 0 && STEPS % 4 == 0) {
+        // token k = 32 s + j: its code at word s b + (j b >> 5) of the row and
+        // its raw bits at word s rr + (j rr >> 5) of the raw row, each at the
+        // lane's constant shift; a step's words for the ring are placed by a
+        // ballot over the wave split into its two streams (lanes 0-31, 32-63)
+        const uint32_t jb = (uint32_t)j * b, shb = jb & 31u;
+        const uint32_t jr = (uint32_t)j * rr, shr = jr & 31u;
+        const uint32_t* rwl = rw + (jb >> 5);
+        uint32_t* rrl = rrow + (jr >> 5);
+        const bool upper = grp != 0;
+#pragma unroll
+        for (int s0 = STEPS - 1; s0 >= 0; s0 -= 4) {
+          uint32_t lo[4], hi[4], code[4];
+          uint4 ent[4];
+          bool act[4];
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            lo[d] = rwl[(s0 - d) * b];
+            hi[d] = rwl[(s0 - d) * b + 1];
+          }
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            act[d] = valid && (s0 - d) * LANES + j < m;
+            code[d] = __builtin_amdgcn_alignbit(hi[d], lo[d], shb) & mask;
+            ent[d] = tc[code[d] >> rr];
+          }
+          if (rr) {  // the low bits into the raw row (a field straddles a word only when rr = 3)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              const uint32_t v = act[d] ? (code[d] & rmask) : 0u;
+              uint32_t* wp = rrl + (s0 - d) * rr;
+              atomicOr(wp, v << shr);
+              if (rr == 3 && shr > 29) atomicOr(wp + 1, v >> (32 - shr));
+            }
+          }
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const uint32_t f = ent[d].x, cum = ent[d].y;
+            const double rcp = __hiloint2double((int)ent[d].w, (int)ent[d].z);
+            // renormalise while x >= f 2^(32 - sb): one 16-bit word at most
+            const bool emit = act[d] && (x >> sbm) >= f;
+            const uint64_t bl = __ballot(emit);
+            const uint32_t blo = (uint32_t)bl, bhi = (uint32_t)(bl >> 32);
+            const uint32_t nlo = (uint32_t)__popc(blo), nhi = (uint32_t)__popc(bhi);
+            const int32_t cnt = (int32_t)(upper ? nhi : nlo);
+            // words are written in emission order, higher lanes first
+            const int32_t below =
+                (int32_t)__builtin_amdgcn_mbcnt_hi(bhi, __builtin_amdgcn_mbcnt_lo(blo, 0u)) - (upper ? (int32_t)nlo : 0);
+            const int32_t at = nw + cnt - 1 - below;
+            if (emit && at < wcap)
+              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(x & 0xffffu), wrsrc, woff + 2 * at, 0, 0);
+            const uint32_t xe = emit ? (x >> 16) : x;
+            nw += cnt;
+            // x = floor(x / f) M + (x mod f) + cum, via an exact fp64 quotient
+            const uint32_t qq = (uint32_t)__fma_rn((double)xe, rcp, 0x1p-20);
+            const uint32_t xn = xe + cum + __umul24(qq, Mv - f);
+            x = act[d] ? xn : x;
+          }
+        }
+      } else {
       // bit positions of token k = s LANES + j in the packed row and in the raw row
       const uint32_t jb = (uint32_t)j * b, jr = (uint32_t)j * rr;
       const uint32_t sb_step = (uint32_t)LANES * b, sr_step = (uint32_t)LANES * rr;
@@ -431,6 +509,7 @@ __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw
           x = active ? xn : x;
         }
       }
+      }  // generic steps
       // the component's raw row to the slot; the buffer is cleared for the next
       if (rr) {
         __builtin_amdgcn_wave_barrier();
