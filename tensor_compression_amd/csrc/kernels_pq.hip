@@ -46,7 +46,6 @@ constexpr int SD = 8;        // channels per subvector
 constexpr int NS = D / SD;   // subspaces
 constexpr int kSpan = 64;
 constexpr int kYS = 132;     // fp32 row stride of the coefficient tile
-constexpr int kHS = 136;     // bf16 row stride of the operand rows
 constexpr int kMaxRow = 9;   // code row words: 16 (9 + 9) bits
 
 __device__ __forceinline__ bool finite_f(float x) { return fabsf(x) <= 3.402823466e38f; }
@@ -64,6 +63,33 @@ __device__ __forceinline__ int acc_row(int i, int hf) { return 8 * (i >> 2) + 4 
 
 // The orthonormal WHT butterflies of a 16-lane group (lane q holds channels
 // 8 q .. 8 q + 7), in fp64, unscaled.
+// Lane i of every 16-lane row takes v from lane i ^ O, O = 1, 2, 4, 8:
+// DPP quad permutations for 1 and 2, a swizzle for 4, a row rotation for 8.
+template <int O>
+__device__ __forceinline__ uint32_t xor16_u32(uint32_t v) {
+  if constexpr (O == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (O == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (O == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (4 << 10) | 0x1F);
+  else return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
+}
+template <int O>
+__device__ __forceinline__ double xor16(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = xor16_u32<O>((uint32_t)u), hi = xor16_u32<O>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(lo | (hi << 32)));
+}
+
+// One fp64 butterfly stage across lanes: the lane with bit O of q set keeps
+// (partner - own), the other (own + partner); fma by +-1 rounds each once.
+template <int O>
+__device__ __forceinline__ void wht_lane_stage(double (&y)[8], int q) {
+  const double sg = (q & O) ? -1.0 : 1.0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = __fma_rn(sg, y[e], xor16<O>(y[e]));
+}
+
+// Butterflies over the 128 channels of a token: bits 0-2 of the channel
+// index in a lane's registers, bits 3-6 across its 16-lane row.
 __device__ __forceinline__ void wht_fp64(double (&y)[8], int q) {
 #pragma unroll
   for (int st = 1; st < 8; st <<= 1)
@@ -74,86 +100,175 @@ __device__ __forceinline__ void wht_fp64(double (&y)[8], int q) {
         y[e] = a + b;
         y[e + st] = a - b;
       }
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const double other = __shfl_xor(y[e], o, 16);
-      y[e] = (q & o) ? other - y[e] : y[e] + other;
-    }
-  }
+  wht_lane_stage<1>(y, q);
+  wht_lane_stage<2>(y, q);
+  wht_lane_stage<4>(y, q);
+  wht_lane_stage<8>(y, q);
+}
+
+// True when z (an fp64 value within 2 of its units in the last place of a
+// real number u) cannot be trusted to round to fp32 as u does: z lies within
+// 8 fp64 units of an fp32 rounding midpoint of its binade, or below the fp32
+// normal range, where that grid changes.  Zero is exact.
+__device__ __forceinline__ bool f32_round_unsure(double z) {
+  const uint32_t lo = (uint32_t)__double_as_longlong(z);
+  const bool mid = ((lo + 8u - 0x10000000u) & 0x1FFFFFFFu) <= 16u;
+  return mid || (fabs(z) < 0x1p-125 && z != 0.0);
 }
 
 // y = WHT(x / r) of 16 tokens at a time: lane q = lane % 16 of a 16-lane
-// group holds channels 8 q .. 8 q + 7.  Returns r.
+// group holds channels 8 q .. 8 q + 7.  Returns r.  Each x / r (an fp32
+// quotient) and each y / sqrt(D) (an fp64 quotient, then fp32) is first
+// taken from one fp64 product with the reciprocal, which is within 2 fp64
+// units of the quotient; where that cannot decide the fp32 rounding the
+// division is done outright, so every result is the correctly rounded one.
 __device__ __forceinline__ float rms_wht(const float (&x)[8], int q, float (&c)[8]) {
+  static_assert((D & (D - 1)) == 0, "sum / D is a power-of-two scaling");
   double ss = 0.0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss = __fma_rn((double)x[e], (double)x[e], ss);
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o, 16);
-  const float rt = (float)__dsqrt_rn(__ddiv_rn(ss, (double)D));
+  ss += xor16<1>(ss);
+  ss += xor16<2>(ss);
+  ss += xor16<4>(ss);
+  ss += xor16<8>(ss);
+  const float rt = (float)__dsqrt_rn(ss * (1.0 / D));
   double y[8];
+  const double inv = __ddiv_rn(1.0, (double)rt);
+  float xn[8];
+  uint32_t unsure = 0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) y[e] = rt == 0.0f ? 0.0 : (double)__fdiv_rn(x[e], rt);
+  for (int e = 0; e < 8; ++e) {
+    const double z = (double)x[e] * inv;
+    xn[e] = (float)z;
+    unsure |= f32_round_unsure(z) ? 1u << e : 0u;
+  }
+  if (__builtin_amdgcn_ballot_w64(unsure != 0)) {  // rare: the divisions only where a lane needs them
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (unsure & (1u << e)) xn[e] = __fdiv_rn(x[e], rt);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = rt == 0.0f ? 0.0 : (double)xn[e];
   wht_fp64(y, q);
   const double rs = __dsqrt_rn((double)D);
+  const double irs = __ddiv_rn(1.0, rs);
+  unsure = 0;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) c[e] = (float)__ddiv_rn(y[e], rs);
+  for (int e = 0; e < 8; ++e) {
+    const double w = y[e] * irs;
+    c[e] = (float)w;
+    unsure |= f32_round_unsure(w) ? 1u << e : 0u;
+  }
+  if (__builtin_amdgcn_ballot_w64(unsure != 0)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (unsure & (1u << e)) c[e] = (float)__ddiv_rn(y[e], rs);
+  }
   return rt;
+}
+
+// Minimum and median of packed keys.  The keys are built with integer
+// operations, so the compiler would quiet each one before a float min; a
+// key is a NaN only when its score is, and then it is already quiet.
+__device__ __forceinline__ float key_min(float a, float b) {
+  float d;
+  asm("v_min_f32 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ float key_med3(float a, float b, float c) {
+  float d;
+  asm("v_med3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
 }
 
 // Best and second-best packed keys (score with the candidate index in its
 // low 9 bits) over k centroids for tokens g 32 + lane % 32 (g = 0, 1) in
-// subspace s; both lane halves end with the same pairs.  One 32 x 32 x 16
-// MFMA per block of 32 centroids and token group: K = the subvector's 8
-// channels twice, y's bf16 high part from the lower lane half and its low
-// part from the upper half against the centroid's 8 values in both.  The
-// next block's operands are loaded during this block's scores, which run in
-// four independent min chains per group.
-__device__ __forceinline__ void search64(const uint16_t* OPH, const uint16_t* OPL, int s, const uint16_t* cbh,
-                                         const float* cn2, int k, float (&best)[2], float (&second)[2]) {
+// subspace s; both lane halves end with the same pairs, and with the norm
+// of each token's subvector.  The subvector is y (c1 == null) or the level-1
+// residual y - c1 (c1: the level-1 codebook of the subspace, idx1 its
+// chosen rows), formed in registers and split into bf16 high and low parts.
+// One 32 x 32 x 16 MFMA per block of 32 centroids and token group gives
+// ||c||^2 - 2 y.c outright: K = the subvector's 8 channels twice, -2 y's
+// high part from the lower lane half and its low part from the upper half
+// against the centroid's 8 values in both, and ||c||^2 as the accumulator's
+// input.  The next block's operands are loaded during this block's scores,
+// which run in four independent min chains per group.
+__device__ __forceinline__ void search64(const float* Y, int s, const uint16_t* c1, const uint16_t* idx1,
+                                         const uint16_t* cbh, const float* cn2, int k, float (&best)[2],
+                                         float (&second)[2], float (&norm)[2]) {
   const int lane = threadIdx.x & 63, n32 = lane & 31, hf = lane >> 5;
-  const uint16_t* opr = hf ? OPL : OPH;
-  const bf16x8_t bop0 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&opr[n32 * kHS + s * SD]));
-  const bf16x8_t bop1 = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&opr[(32 + n32) * kHS + s * SD]));
+  bf16x8_t bop[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int tok = g * 32 + n32;
+    const float4 a = *reinterpret_cast<const float4*>(&Y[tok * kYS + s * SD]);
+    const float4 b = *reinterpret_cast<const float4*>(&Y[tok * kYS + s * SD + 4]);
+    float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    if (c1) {
+      float cv[8];
+      unpack8(*reinterpret_cast<const uint4*>(c1 + (uint32_t)idx1[tok * NS + s] * SD), cv);
+#pragma unroll
+      for (int j = 0; j < SD; ++j) v[j] = __fsub_rn(v[j], cv[j]);
+    }
+    uint32_t w[8];
+    float n2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < SD; ++j) {
+      const float m2 = -2.0f * v[j];  // exact
+      const uint32_t h = (uint32_t)f32_to_bf16(m2);
+      w[j] = hf ? (uint32_t)f32_to_bf16(__fsub_rn(m2, __uint_as_float(h << 16))) : h;
+      n2 = __fmaf_rn(v[j], v[j], n2);
+    }
+    norm[g] = __fsqrt_rn(n2);
+    bop[g] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16),
+                                                     w[6] | (w[7] << 16)));
+  }
   float b1[2][4], b2[2][4];
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
     for (int c = 0; c < 4; ++c) b1[g][c] = b2[g][c] = INFINITY;
   const int nb = k >> 5;
-  uint4 an = *reinterpret_cast<const uint4*>(cbh + n32 * SD);
-  float4 cnn[4];
+  const uint4 an = *reinterpret_cast<const uint4*>(cbh + n32 * SD);
+  // accumulator input: output row i of a lane is centroid 8 (i / 4) + 4 (lane / 32) + i % 4
+  auto load_cn = [&](int blk) {
+    f32x16_t c;
 #pragma unroll
-  for (int r4 = 0; r4 < 4; ++r4) cnn[r4] = *reinterpret_cast<const float4*>(cn2 + 8 * r4 + 4 * hf);
-  for (int blk = 0; blk < nb; ++blk) {
-    const uint4 a = an;
-    float4 cn[4];
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) cn[r4] = cnn[r4];
-    if (blk + 1 < nb) {
-      an = *reinterpret_cast<const uint4*>(cbh + ((blk + 1) * 32 + n32) * SD);
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4)
-        cnn[r4] = *reinterpret_cast<const float4*>(cn2 + (blk + 1) * 32 + 8 * r4 + 4 * hf);
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const float4 v4 = *reinterpret_cast<const float4*>(cn2 + blk * 32 + 8 * r4 + 4 * hf);
+      c[4 * r4] = v4.x;
+      c[4 * r4 + 1] = v4.y;
+      c[4 * r4 + 2] = v4.z;
+      c[4 * r4 + 3] = v4.w;
     }
+    return c;
+  };
+  // the score bits kept above the index, from a scalar register so that one
+  // and-or per key packs it
+  uint32_t kmask;
+  asm volatile("s_mov_b32 %0, 0xfffffe00" : "=s"(kmask));
+  // the next block's operands are loaded once both products have read this block's
+  uint4 a = an;
+  f32x16_t cn = load_cn(0);
+  for (int blk = 0; blk < nb; ++blk) {
     f32x16_t acc[2];
-    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), bop0, f32x16_t{}, 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), bop1, f32x16_t{}, 0, 0, 0);
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), bop[0], cn, 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), bop[1], cn, 0, 0, 0);
+    if (blk + 1 < nb) {
+      a = *reinterpret_cast<const uint4*>(cbh + ((blk + 1) * 32 + n32) * SD);
+      cn = load_cn(blk + 1);
+    }
     const uint32_t base = (uint32_t)(blk * 32 + 4 * hf);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float4 c4 = cn[i >> 2];
-      const float cni = (i & 3) == 0 ? c4.x : (i & 3) == 1 ? c4.y : (i & 3) == 2 ? c4.z : c4.w;
-      const uint32_t idx = base + (uint32_t)(8 * (i >> 2) + (i & 3));
+      uint32_t idx = base | (uint32_t)(8 * (i >> 2) + (i & 3));  // disjoint bits
+      asm("" : "+v"(idx));  // one index per row, shared by both groups' and-or
       const int c = i & 3;
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        const float sc = __fmaf_rn(-2.0f, acc[g][i], cni);
-        const float key = __uint_as_float((__float_as_uint(sc) & ~0x1FFu) | idx);
-        b2[g][c] = __builtin_amdgcn_fmed3f(b1[g][c], b2[g][c], key);
-        b1[g][c] = fminf(b1[g][c], key);
+        const float key = __uint_as_float((__float_as_uint(acc[g][i]) & kmask) | idx);
+        b2[g][c] = key_med3(b1[g][c], b2[g][c], key);
+        b1[g][c] = key_min(b1[g][c], key);
       }
     }
   }
@@ -206,21 +321,21 @@ __device__ __forceinline__ int exact_nearest(const float (&ys)[SD], const uint16
   return bi < k ? bi : 0;
 }
 
-// One radix pass of a block-wide selection (256 threads): among the nel
-// keys key(e) that match `prefix` on `pmask`, the digit d of bits
-// [sh, sh + w) holding the need-th largest, and how many of the keys with
-// that digit are still needed.  HIST holds 2048 words of LDS, SM 8.
-template <class KeyFn>
-__device__ void radix_pass(KeyFn key, int nel, int sh, int w, uint64_t prefix, uint64_t pmask, uint32_t need,
+// One radix pass of a block-wide selection (256 threads): among the keys
+// that match `prefix` on `pmask`, the digit d of bits [sh, sh + w) holding
+// the need-th largest, and how many of the keys with that digit are still
+// needed.  each(f) calls f(key) on every key the thread holds.  HIST holds
+// 2048 words of LDS, SM 8.
+template <class EachFn>
+__device__ void radix_pass(EachFn each, int sh, int w, uint64_t prefix, uint64_t pmask, uint32_t need,
                            uint32_t* HIST, uint32_t* SM, uint32_t& digit, uint32_t& need_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t dmask = (1u << w) - 1u;
   for (int i = tid; i < 2048; i += 256) HIST[i] = 0u;
   __syncthreads();
-  for (int e = tid; e < nel; e += 256) {
-    const uint64_t kk = key(e);
+  each([&](uint64_t kk) {
     if ((kk & pmask) == prefix) atomicAdd(&HIST[(uint32_t)(kk >> sh) & dmask], 1u);
-  }
+  });
   __syncthreads();
   uint32_t c[8], loc = 0;
 #pragma unroll
@@ -257,16 +372,16 @@ __device__ void radix_pass(KeyFn key, int nel, int sh, int w, uint64_t prefix, u
   __syncthreads();
 }
 
-// The B-th largest of nel distinct keys key(e) below bit `top` that match
-// `prefix` on `pmask`, 11 bits per pass from the top.
-template <class KeyFn>
-__device__ uint64_t radix_kth(KeyFn key, int nel, int top, uint32_t B, uint32_t* HIST, uint32_t* SM,
+// The B-th largest of the distinct keys each(f) visits that lie below bit
+// `top` and match `prefix` on `pmask`, 11 bits per pass from the top.
+template <class EachFn>
+__device__ uint64_t radix_kth(EachFn each, int top, uint32_t B, uint32_t* HIST, uint32_t* SM,
                               uint64_t prefix = 0, uint64_t pmask = 0) {
   uint32_t need = B;
   for (; top > 0; top -= 11) {
     const int w = top < 11 ? top : 11, sh = top - w;
     uint32_t d;
-    radix_pass(key, nel, sh, w, prefix, pmask, need, HIST, SM, d, need);
+    radix_pass(each, sh, w, prefix, pmask, need, HIST, SM, d, need);
     prefix |= (uint64_t)d << sh;
     pmask |= (uint64_t)((1u << w) - 1u) << sh;
   }
@@ -306,25 +421,21 @@ __global__ __launch_bounds__(256) void k_pq_prep(const PqParams q) {
   if (tid < 2) q.cmax[ls * 2 + tid] = __uint_as_float(smax[tid]);
 }
 
-__global__ __launch_bounds__(256) void k_pq_enc(const PqParams q) {
+__global__ __launch_bounds__(256, 3) void k_pq_enc(const PqParams q) {
   const int sec = blockIdx.y, span = blockIdx.x;
   const int l = sec / q.H;
   const int t0 = span * kSpan, n = min(kSpan, q.T - t0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hf = lane >> 5, n32 = lane & 31;
 
+  // 50 KB of LDS (three workgroups a CU): the span's coefficients, the chosen
+  // indices, the radix histogram (first the code rows) and the short list
   __shared__ __attribute__((aligned(16))) float Y[kSpan * kYS];
-  __shared__ __attribute__((aligned(16))) uint16_t OP[2 * kSpan * kHS];  // hi, lo operand rows; later y - y^
-  __shared__ __attribute__((aligned(16))) uint32_t AUX[3 * kSpan * NS];  // I1, I2, norms; later HIST
+  __shared__ uint16_t I1[kSpan * NS], I2[kSpan * NS];
+  __shared__ __attribute__((aligned(16))) uint32_t HIST[2048];
+  __shared__ __attribute__((aligned(16))) uint64_t LIST[512];
   __shared__ uint32_t SM[8];
-  uint16_t* const OPH = OP;
-  uint16_t* const OPL = OP + kSpan * kHS;
-  float* const DEL = reinterpret_cast<float*>(OP);
-  uint32_t* const I1 = AUX;
-  uint32_t* const I2 = AUX + kSpan * NS;
-  float* const YN = reinterpret_cast<float*>(AUX + 2 * kSpan * NS);
-  uint32_t* const ROW = AUX + 2 * kSpan * NS;  // after level 2, over the norms
-  uint32_t* const HIST = AUX;                   // after the code rows
+  uint32_t* const ROW = HIST;  // the code rows, before the selection
 
   // ---- stage, RMS, WHT: 16 lanes a token, 16 tokens a pass
   {
@@ -351,45 +462,32 @@ __global__ __launch_bounds__(256) void k_pq_enc(const PqParams q) {
       float* yr = &Y[tok * kYS + 8 * q16];
       *reinterpret_cast<float4*>(yr) = make_float4(c[0], c[1], c[2], c[3]);
       *reinterpret_cast<float4*>(yr + 4) = make_float4(c[4], c[5], c[6], c[7]);
-      uint32_t hb[8], lb[8];
-      float n2 = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        hb[e] = (uint32_t)f32_to_bf16(c[e]);
-        lb[e] = (uint32_t)f32_to_bf16(__fsub_rn(c[e], __uint_as_float(hb[e] << 16)));
-        n2 = __fmaf_rn(c[e], c[e], n2);
-      }
-      *reinterpret_cast<uint4*>(&OPH[tok * kHS + 8 * q16]) =
-          make_uint4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16));
-      *reinterpret_cast<uint4*>(&OPL[tok * kHS + 8 * q16]) =
-          make_uint4(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16), lb[6] | (lb[7] << 16));
-      YN[tok * NS + q16] = __fsqrt_rn(n2);
     }
     if (bad && q.status) atomicOr(q.status, 1u << KVTC_ERR_NONFINITE);
   }
   __syncthreads();
 
   const int64_t ls0 = (int64_t)l * NS;  // first (layer, subspace) row of the tables
-  // ---- levels 1 and 2: unit (s, g2) = subspace s, tokens 32 g2 .. +31; eight units a wave
+  // ---- levels 1 and 2: a wave takes subspaces wave, wave + 4, ... with both token groups
   for (int level = 0; level < 2; ++level) {
     const int k = level ? q.k2 : q.k1;
-    uint32_t* const I = level ? I2 : I1;
+    uint16_t* const I = level ? I2 : I1;
     for (int it = 0; it < 4; ++it) {
       const int s = wave + 4 * it;
       const int64_t ls = ls0 + s;
       const uint16_t* cbh = (level ? q.cb2h : q.cb1h) + ls * k * SD;
+      const uint16_t* c1 = level ? q.cb1h + ls * q.k1 * SD : nullptr;
       const float* cn2 = q.cn2 + ls * (q.k1 + q.k2) + (level ? q.k1 : 0);
       const float cm = q.cmax[ls * 2 + level];
-      float best[2], second[2];
-      search64(OPH, OPL, s, cbh, cn2, k, best, second);
+      float best[2], second[2], norm[2];
+      search64(Y, s, c1, I1, cbh, cn2, k, best, second, norm);
 #pragma unroll
       for (int g2 = 0; g2 < 2; ++g2) {
         const int tok = g2 * 32 + n32;
-        const float thr =
-            0x1p-13f * (YN[tok * NS + s] * cm + cm * cm) + 0x1p-12f * (fabsf(best[g2]) + fabsf(second[g2]));
+        const float thr = 0x1p-13f * (norm[g2] * cm + cm * cm) + 0x1p-12f * (fabsf(best[g2]) + fabsf(second[g2]));
         const bool owner = hf == 0 && tok < n;
         // every token gets an index (tokens past the span keep a valid one)
-        if (hf == 0) I[tok * NS + s] = __float_as_uint(best[g2]) & 0x1FFu;
+        if (hf == 0) I[tok * NS + s] = (uint16_t)(__float_as_uint(best[g2]) & 0x1FFu & (uint32_t)(k - 1));
         // near ties: decided again exactly, one wave-wide scan each
         uint64_t pend = __ballot(owner && !(__fsub_rn(second[g2], best[g2]) > thr));
         while (pend) {
@@ -399,68 +497,35 @@ __global__ __launch_bounds__(256) void k_pq_enc(const PqParams q) {
 #pragma unroll
           for (int j = 0; j < SD; ++j) ys[j] = Y[tk * kYS + s * SD + j];
           if (level) {
-            float c1[8];
-            unpack8(*reinterpret_cast<const uint4*>(q.cb1h + (ls * q.k1 + (I1[tk * NS + s] & (q.k1 - 1))) * SD), c1);
+            float cv[8];
+            unpack8(*reinterpret_cast<const uint4*>(c1 + ((uint32_t)I1[tk * NS + s] & (q.k1 - 1)) * SD), cv);
 #pragma unroll
-            for (int j = 0; j < SD; ++j) ys[j] = __fsub_rn(ys[j], c1[j]);
+            for (int j = 0; j < SD; ++j) ys[j] = __fsub_rn(ys[j], cv[j]);
           }
           const int bi = exact_nearest(ys, cbh, k);
-          if (lane == L) I[tk * NS + s] = (uint32_t)bi;
+          if (lane == L) I[tk * NS + s] = (uint16_t)bi;
           pend &= pend - 1;
         }
       }
     }
     __syncthreads();
-    if (level == 0) {
-      // level-2 operands: the residual e = y - c1 (fp32), split into bf16 hi + lo
-      for (int it = tid; it < kSpan * NS; it += 256) {
-        const int tok = it >> 4, s = it & 15;
-        float c1[8];
-        unpack8(*reinterpret_cast<const uint4*>(q.cb1h + ((ls0 + s) * q.k1 + (I1[tok * NS + s] & (q.k1 - 1))) * SD), c1);
-        uint32_t hb[8], lb[8];
-        float n2 = 0.f;
-#pragma unroll
-        for (int j = 0; j < SD; ++j) {
-          const float e = __fsub_rn(Y[tok * kYS + s * SD + j], c1[j]);
-          hb[j] = (uint32_t)f32_to_bf16(e);
-          lb[j] = (uint32_t)f32_to_bf16(__fsub_rn(e, __uint_as_float(hb[j] << 16)));
-          n2 = __fmaf_rn(e, e, n2);
-        }
-        *reinterpret_cast<uint4*>(&OPH[tok * kHS + s * SD]) =
-            make_uint4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16));
-        *reinterpret_cast<uint4*>(&OPL[tok * kHS + s * SD]) =
-            make_uint4(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16), lb[6] | (lb[7] << 16));
-        YN[tok * NS + s] = __fsqrt_rn(n2);
-      }
-      __syncthreads();
-    }
   }
 
-  // ---- code rows (level-1 fields, then level-2 fields) and y - y^
+  // ---- code rows: level-1 fields, then level-2 fields
   for (int i = tid; i < kSpan * q.rw; i += 256) ROW[i] = 0u;
   __syncthreads();
   for (int it = tid; it < kSpan * NS; it += 256) {
     const int tok = it >> 4, s = it & 15;
+    if (tok >= n) continue;
     const uint32_t i1 = I1[tok * NS + s] & (q.k1 - 1), i2 = I2[tok * NS + s] & (q.k2 - 1);
-    if (tok < n) {
-      const int bits[2] = {s * q.b1, NS * q.b1 + s * q.b2};
-      const uint32_t vals[2] = {i1, i2}, nbs[2] = {(uint32_t)q.b1, (uint32_t)q.b2};
+    const int bits[2] = {s * q.b1, NS * q.b1 + s * q.b2};
+    const uint32_t vals[2] = {i1, i2}, nbs[2] = {(uint32_t)q.b1, (uint32_t)q.b2};
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const int w = bits[f] >> 5, sh = bits[f] & 31;
-        atomicOr(&ROW[tok * q.rw + w], vals[f] << sh);
-        if (sh + (int)nbs[f] > 32) atomicOr(&ROW[tok * q.rw + w + 1], vals[f] >> (32 - sh));
-      }
+    for (int f = 0; f < 2; ++f) {
+      const int w = bits[f] >> 5, sh = bits[f] & 31;
+      atomicOr(&ROW[tok * q.rw + w], vals[f] << sh);
+      if (sh + (int)nbs[f] > 32) atomicOr(&ROW[tok * q.rw + w + 1], vals[f] >> (32 - sh));
     }
-    float c1[8], c2[8];
-    unpack8(*reinterpret_cast<const uint4*>(q.cb1h + ((ls0 + s) * q.k1 + i1) * SD), c1);
-    unpack8(*reinterpret_cast<const uint4*>(q.cb2h + ((ls0 + s) * q.k2 + i2) * SD), c2);
-    float dv[8];
-#pragma unroll
-    for (int j = 0; j < SD; ++j) dv[j] = __fsub_rn(Y[tok * kYS + s * SD + j], __fadd_rn(c1[j], c2[j]));
-    // DEL overwrites the operand rows: every wave is past its searches
-    *reinterpret_cast<float4*>(&DEL[tok * D + s * SD]) = make_float4(dv[0], dv[1], dv[2], dv[3]);
-    *reinterpret_cast<float4*>(&DEL[tok * D + s * SD + 4]) = make_float4(dv[4], dv[5], dv[6], dv[7]);
   }
   __syncthreads();
   {
@@ -470,12 +535,42 @@ __global__ __launch_bounds__(256) void k_pq_enc(const PqParams q) {
   if (q.B == 0) return;
   __syncthreads();  // the rows are read; HIST reuses their memory
 
-  // ---- the span's B largest |y - y^|, then the lowest index: distinct 44-bit keys
+  // ---- the span's B largest |y - y^|, then the lowest index: distinct
+  // 44-bit keys (|y - y^| bits << 13) | (8191 - e), e = 128 token + channel.
+  // Thread tid holds the keys of channel tid % 128 for tokens 2 i + tid / 128
+  // (i < 32).  Slots past the span's last token hold |y - y^| = 0 and an
+  // index past every real one, so their keys lie below all real keys: they
+  // are never among the B largest while there are more than B real keys.
+  constexpr int kSel = kSpan / 2;
   const int nel = n * D;
-  auto key = [&](int e) -> uint64_t {
-    return ((uint64_t)(__float_as_uint(DEL[e]) & 0x7fffffffu) << 13) | (uint64_t)(8191 - e);
-  };
   const uint32_t B = (uint32_t)q.B;
+  uint32_t mag[kSel];
+  {
+    const int j = tid & 127, s = j >> 3, jj = j & 7;
+    const uint16_t* c1 = q.cb1h + (ls0 + s) * q.k1 * SD + jj;
+    const uint16_t* c2 = q.cb2h + (ls0 + s) * q.k2 * SD + jj;
+#pragma unroll
+    for (int i = 0; i < kSel; ++i) {
+      const int tok = 2 * i + (tid >> 7);  // every token of the span has indices, so reads stay in bounds
+      const uint32_t i1 = I1[tok * NS + s] & (q.k1 - 1), i2 = I2[tok * NS + s] & (q.k2 - 1);
+      const float yh = __fadd_rn(__uint_as_float((uint32_t)c1[i1 * SD] << 16), __uint_as_float((uint32_t)c2[i2 * SD] << 16));
+      const uint32_t m = __float_as_uint(__fsub_rn(Y[tok * kYS + j], yh)) & 0x7fffffffu;
+      mag[i] = tok < n ? m : 0u;
+    }
+  }
+  // the key of element e = 128 token + channel (e < nel), from LDS and the
+  // codebooks: for the rare walks that need every key in full
+  auto key_of = [&](int e) -> uint64_t {
+    const int tok = e >> 7, j = e & 127, s = j >> 3, jj = j & 7;
+    const uint32_t i1 = I1[tok * NS + s] & (q.k1 - 1), i2 = I2[tok * NS + s] & (q.k2 - 1);
+    const float c1v = __uint_as_float((uint32_t)q.cb1h[((ls0 + s) * q.k1 + i1) * SD + jj] << 16);
+    const float c2v = __uint_as_float((uint32_t)q.cb2h[((ls0 + s) * q.k2 + i2) * SD + jj] << 16);
+    const float dv = __fsub_rn(Y[tok * kYS + j], __fadd_rn(c1v, c2v));
+    return ((uint64_t)(__float_as_uint(dv) & 0x7fffffffu) << 13) | (uint64_t)(8191 - e);
+  };
+  auto each_full = [&](auto f) {
+    for (int e = tid; e < nel; e += 256) f(key_of(e));
+  };
   uint4* cand = q.cand + ((int64_t)sec * q.nspan + span) * q.B;
   auto put = [&](uint64_t kk, uint32_t slot) {
     const int e = 8191 - (int)(kk & 8191u);
@@ -484,38 +579,47 @@ __global__ __launch_bounds__(256) void k_pq_enc(const PqParams q) {
       cand[slot] = make_uint4((uint32_t)(kk >> 13), (uint32_t)((t0 + tok) * D + j), __float_as_uint(Y[tok * kYS + j]), 0u);
   };
   if ((uint32_t)nel <= B) {
-    for (int e = tid; e < nel; e += 256) put(key(e), (uint32_t)e);
+    each_full([&](uint64_t kk) { put(kk, (uint32_t)(8191 - (int)(kk & 8191u))); });
     return;
   }
-  // the top 11 bits over every key; keys above the threshold digit are
-  // selected outright, those on it go to a short list for the remaining passes
+  // the top 11 bits over every slot (bits 30..20 of |y - y^|; the index
+  // bits play no part); keys above the threshold digit are selected
+  // outright, those on it go to a short list for the remaining passes
   uint32_t d0, need;
-  radix_pass(key, nel, 33, 11, 0, 0, B, HIST, SM, d0, need);
+  radix_pass(
+      [&](auto f) {
+#pragma unroll
+        for (int i = 0; i < kSel; ++i) f((uint64_t)mag[i] << 13);
+      },
+      33, 11, 0, 0, B, HIST, SM, d0, need);
   const uint32_t on_digit = HIST[d0];
-  uint64_t* const LIST = reinterpret_cast<uint64_t*>(AUX + 2048);  // 512 keys past HIST
   constexpr uint32_t kList = 512;
   if (tid == 0) { SM[6] = 0u; SM[7] = 0u; }
   __syncthreads();
   if (on_digit <= kList) {
-    for (int e = tid; e < nel; e += 256) {
-      const uint64_t kk = key(e);
-      const uint32_t dg = (uint32_t)(kk >> 33);
-      if (dg > d0) put(kk, atomicAdd(&SM[6], 1u));
-      else if (dg == d0) LIST[atomicAdd(&SM[7], 1u)] = kk;
+#pragma unroll
+    for (int i = 0; i < kSel; ++i) {
+      const uint32_t dg = mag[i] >> 20;
+      if (dg >= d0) {
+        const uint64_t kk = ((uint64_t)mag[i] << 13) | (uint64_t)(8191 - (tid + 256 * i));
+        if (dg > d0) put(kk, atomicAdd(&SM[6], 1u));
+        else LIST[atomicAdd(&SM[7], 1u)] = kk;
+      }
     }
     __syncthreads();
     const int nl = (int)SM[7];
-    const uint64_t tau = radix_kth([&](int e) { return LIST[e]; }, nl, 33, need, HIST, SM, (uint64_t)d0 << 33,
-                                   (uint64_t)0x7FF << 33);
+    auto each_list = [&](auto f) {
+      for (int e = tid; e < nl; e += 256) f(LIST[e]);
+    };
+    const uint64_t tau = radix_kth(each_list, 33, need, HIST, SM, (uint64_t)d0 << 33, (uint64_t)0x7FF << 33);
     for (int e = tid; e < nl; e += 256)
       if (LIST[e] >= tau) put(LIST[e], atomicAdd(&SM[6], 1u));
   } else {
     // many equal top digits (e.g. an all-zero error): the remaining passes over every key
-    const uint64_t tau = radix_kth(key, nel, 33, need, HIST, SM, (uint64_t)d0 << 33, (uint64_t)0x7FF << 33);
-    for (int e = tid; e < nel; e += 256) {
-      const uint64_t kk = key(e);
+    const uint64_t tau = radix_kth(each_full, 33, need, HIST, SM, (uint64_t)d0 << 33, (uint64_t)0x7FF << 33);
+    each_full([&](uint64_t kk) {
       if (kk >= tau) put(kk, atomicAdd(&SM[6], 1u));
-    }
+    });
   }
 }
 
@@ -553,7 +657,10 @@ __global__ __launch_bounds__(256) void k_pq_merge(const PqParams q) {
   __syncthreads();
   const uint32_t B = (uint32_t)q.B;
   uint64_t tau = 0;
-  if ((uint32_t)nc > B) tau = radix_kth([&](int e) { return CK[e]; }, nc, 63, B, HIST, SM);
+  auto each_cand = [&](auto f) {
+    for (int e = tid; e < nc; e += 256) f(CK[e]);
+  };
+  if ((uint32_t)nc > B) tau = radix_kth(each_cand, 63, B, HIST, SM);
   if (tid == 0) SM[6] = 0u;
   __syncthreads();
   for (int e = tid; e < nc; e += 256) {
