@@ -1300,8 +1300,21 @@ __global__ __launch_bounds__(BIG ? 1024 : 768, BIG ? 4 : 6) void k_rans_dec_recs
       const uint32_t sh = LANES == 32 ? sh0 : (bp & 31u);
       uint32_t* ow = LANES == 32 ? ob + (jb >> 5) + s * b : ob + (bp >> 5);
       const uint64_t c64 = (uint64_t)code << sh;  // the high word holds what crosses into the next word
-      atomicOr(ow, (uint32_t)c64);
-      if (STRADDLES) atomicOr(ow + 1, (uint32_t)(c64 >> 32));
+      if constexpr (!STRADDLES) {
+        // widths 2, 4, 8: a word holds the codes of an aligned run of 32 / b
+        // lanes of one step, so the run ORs its codes across lanes and its
+        // first lane stores the word (no atomics on the state's critical path)
+        uint32_t v = (uint32_t)c64;
+        v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+        v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // lane ^ 2
+        if (b <= 4u) v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);  // 7 - lane % 8
+        if (b <= 2u) v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);  // 15 - lane % 16
+        if (valid && (j & ((32u / b) - 1u)) == 0u) *ow = v;
+      } else {
+        atomicOr(ow, (uint32_t)c64);
+        const uint32_t hi = (uint32_t)(c64 >> 32);
+        if (hi) atomicOr(ow + 1, hi);  // only lanes whose code crosses the word
+      }
     }
   };
   auto component = [&](int ci, uint32_t(&rp)[NR]) {
