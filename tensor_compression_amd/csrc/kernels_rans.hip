@@ -428,13 +428,29 @@ __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw
             code[d] = __builtin_amdgcn_alignbit(hi[d], lo[d], shb) & mask;
             ent[d] = tc[code[d] >> rr];
           }
-          if (rr) {  // the low bits into the raw row (a field straddles a word only when rr = 3)
+          if (rr == 3) {  // the low bits into the raw row (a 3-bit field may straddle a word)
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
               const uint32_t v = act[d] ? (code[d] & rmask) : 0u;
               uint32_t* wp = rrl + (s0 - d) * rr;
               atomicOr(wp, v << shr);
-              if (rr == 3 && shr > 29) atomicOr(wp + 1, v >> (32 - shr));
+              if (shr > 29) atomicOr(wp + 1, v >> (32 - shr));
+            }
+          } else if (rr) {
+            // rr = 1, 2, 4: a raw word holds the fields of an aligned run of
+            // 32 / rr lanes of one step; the run ORs them across lanes (quad
+            // swaps, half-row and row mirrors, then row 0's total into row 1)
+            // and one lane of the run stores the word
+            const bool leader = rr == 1 ? j == 31 : (j & ((32u / rr) - 1u)) == 0u;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              uint32_t v = (act[d] ? (code[d] & rmask) : 0u) << shr;
+              v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+              v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // lane ^ 2
+              v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);  // 7 - lane % 8
+              if (rr <= 2u) v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);  // 15 - lane % 16
+              if (rr == 1u) v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // lane 15 into the next row
+              if (valid && leader) rrl[(s0 - d) * rr] = v;
             }
           }
 #pragma unroll
