@@ -316,11 +316,37 @@ __global__ __launch_bounds__(1024) void k_rans_enc_recs(const Params p0, int raw
           lo[s] = rwl[s * b];
           hi[s] = rwl[s * b + 1];
         }
+        // the lane's STEPS <= 8 symbols counted in 4-bit fields (symbol y at
+        // bits 4y), widened to bytes (B0: even symbols 0-6, B1: odd 1-7, B2:
+        // even 8-14, B3: odd 9-15) and summed over each 16-lane row by DPP
+        // adds (at most 128 a byte); then lane k of a row adds the row's count
+        // of symbol k to the first histogram copy
+        static_assert(STEPS <= 8, "4-bit per-lane counts");
+        uint64_t nib = 0;
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) {
           const uint32_t code = __builtin_amdgcn_alignbit(hi[s], lo[s], sh) & mask;
-          if (valid && s * LANES + j < m) atomicAdd(&hc[code >> rr], 1u);
+          if (valid && s * LANES + j < m) nib += 1ull << (4u * (code >> rr));
         }
+        const uint32_t A = 1u << (b - rr);  // symbols: 4, 8 or 16
+        auto row_sum = [](uint32_t v) {
+          v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // lane ^ 1
+          v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // lane ^ 2
+          v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false);  // 7 - lane % 8
+          v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false);  // 15 - lane % 16
+          return v;
+        };
+        const uint32_t nlo = (uint32_t)nib, nhi = (uint32_t)(nib >> 32);
+        const uint32_t B0 = row_sum(nlo & 0x0F0F0F0Fu), B1 = row_sum((nlo >> 4) & 0x0F0F0F0Fu);
+        uint32_t B2 = 0u, B3 = 0u;
+        if (A > 8u) {
+          B2 = row_sum(nhi & 0x0F0F0F0Fu);
+          B3 = row_sum((nhi >> 4) & 0x0F0F0F0Fu);
+        }
+        const uint32_t k = (uint32_t)j & 15u;
+        const uint32_t reg = k < 8u ? ((k & 1u) ? B1 : B0) : ((k & 1u) ? B3 : B2);
+        const uint32_t cnt = (reg >> (8u * ((k >> 1) & 3u))) & 0xFFu;
+        if (valid && k < A && cnt) atomicAdd(&hist[ci * kHistCopies * 17 + k], cnt);
         return;
       }
 #pragma unroll
