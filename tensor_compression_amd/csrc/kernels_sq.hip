@@ -84,12 +84,7 @@ __device__ __forceinline__ void make_range(float mn, float mx, int b, float* zer
 
 }  // namespace
 
-// Dynamic LDS of the encoder: the packed rows, then the span's range table
-// (zero, reciprocal).
-__host__ __device__ inline int sq_enc_part_bytes(int b, int ce) {
-  (void)ce;
-  return (kSpan * 4 * b * 4 + 15) & ~15;
-}
+// Dynamic LDS of the encoder: the span's range table (zero, reciprocal).
 __host__ __device__ inline int sq_span_ranges(int te, int ce) { return (kSpan / te) * (128 / ce); }
 
 __global__ void k_sq_clear(uint32_t* status) {
@@ -106,7 +101,7 @@ __global__ void k_sq_clear(uint32_t* status) {
 // basis row).
 template <int B>
 __device__ __forceinline__ void quant_pack(const SqParams& q, const float* C, const uint16_t* X, const uint16_t* bt,
-                                           const float2* R, const float* nrm, uint32_t* PK, int n, int lte, int lce,
+                                           const float2* R, const float* nrm, uint32_t* out, int n, int lte, int lce,
                                            int lncg) {
   constexpr int D = 128;
   constexpr float QM = (float)((1u << B) - 1u);
@@ -183,10 +178,18 @@ __device__ __forceinline__ void quant_pack(const SqParams& q, const float* C, co
     }
     pend = __ballot(flags != 0u);
   }
-  if (valid) {
-    uint32_t* dst = PK + (t * 4 + wave) * B;
+  if (valid) {  // the lane's B words of its token's row, in the widest aligned stores
+    uint32_t* dst = out + (t * 4 + wave) * B;
+    if constexpr (B % 4 == 0) {
 #pragma unroll
-    for (int k = 0; k < B; ++k) dst[k] = w[k];
+      for (int k = 0; k < B; k += 4) *reinterpret_cast<uint4*>(dst + k) = make_uint4(w[k], w[k + 1], w[k + 2], w[k + 3]);
+    } else if constexpr (B % 2 == 0) {
+#pragma unroll
+      for (int k = 0; k < B; k += 2) *reinterpret_cast<uint2*>(dst + k) = make_uint2(w[k], w[k + 1]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < B; ++k) dst[k] = w[k];
+    }
   }
 }
 
@@ -206,9 +209,7 @@ __global__ __launch_bounds__(256) void k_sq_enc128(const SqParams q) {
   __shared__ __attribute__((aligned(16))) float C[kSpan * kCS];
   __shared__ float nrm[kSpan];
   extern __shared__ __attribute__((aligned(16))) uint8_t dyn[];
-  const int part_bytes = sq_enc_part_bytes(b, ce);
-  uint32_t* const PK = reinterpret_cast<uint32_t*>(dyn);          // packed rows
-  float2* const R = reinterpret_cast<float2*>(dyn + part_bytes);  // (zero, rcp) per range
+  float2* const R = reinterpret_cast<float2*>(dyn);  // (zero, rcp) per range
 
   const uint16_t* bt = q.basis_t + basis_of(q, l, s, h) * D * D;
   // B operands: component (2 wave + m) 16 + r, channels 32 kb + 8 g .. +7
@@ -412,22 +413,19 @@ __global__ __launch_bounds__(256) void k_sq_enc128(const SqParams q) {
   __syncthreads();  // the range table is complete
 
   // ---- quantise and pack: lane = token, wave = channel quarter [32 w, 32 w + 32)
+  // the span's rows go straight to the output (16-byte aligned: a section's
+  // rows are 16 b bytes each)
+  uint32_t* const out = reinterpret_cast<uint32_t*>(q.codes + sec_off(u, H, q.code_bytes[0], q.code_bytes[1]) +
+                                                    (int64_t)t0 * 16 * b);
   switch (b) {
-    case 1: quant_pack<1>(q, C, X, bt, R, nrm, PK, n, lte, lce, lncg); break;
-    case 2: quant_pack<2>(q, C, X, bt, R, nrm, PK, n, lte, lce, lncg); break;
-    case 3: quant_pack<3>(q, C, X, bt, R, nrm, PK, n, lte, lce, lncg); break;
-    case 4: quant_pack<4>(q, C, X, bt, R, nrm, PK, n, lte, lce, lncg); break;
-    case 5: quant_pack<5>(q, C, X, bt, R, nrm, PK, n, lte, lce, lncg); break;
-    case 6: quant_pack<6>(q, C, X, bt, R, nrm, PK, n, lte, lce, lncg); break;
-    case 7: quant_pack<7>(q, C, X, bt, R, nrm, PK, n, lte, lce, lncg); break;
-    default: quant_pack<8>(q, C, X, bt, R, nrm, PK, n, lte, lce, lncg); break;
-  }
-  __syncthreads();
-  {
-    uint32_t* dst = reinterpret_cast<uint32_t*>(q.codes + sec_off(u, H, q.code_bytes[0], q.code_bytes[1]) +
-                                                (int64_t)t0 * 16 * b);
-    const int nw = n * 4 * b;
-    for (int i = tid; i < nw; i += 256) dst[i] = PK[i];
+    case 1: quant_pack<1>(q, C, X, bt, R, nrm, out, n, lte, lce, lncg); break;
+    case 2: quant_pack<2>(q, C, X, bt, R, nrm, out, n, lte, lce, lncg); break;
+    case 3: quant_pack<3>(q, C, X, bt, R, nrm, out, n, lte, lce, lncg); break;
+    case 4: quant_pack<4>(q, C, X, bt, R, nrm, out, n, lte, lce, lncg); break;
+    case 5: quant_pack<5>(q, C, X, bt, R, nrm, out, n, lte, lce, lncg); break;
+    case 6: quant_pack<6>(q, C, X, bt, R, nrm, out, n, lte, lce, lncg); break;
+    case 7: quant_pack<7>(q, C, X, bt, R, nrm, out, n, lte, lce, lncg); break;
+    default: quant_pack<8>(q, C, X, bt, R, nrm, out, n, lte, lce, lncg); break;
   }
 }
 
@@ -585,7 +583,7 @@ hipError_t launch_sq_encode(const SqParams& q, hipStream_t s) {
   if (q.T == 0) return hipSuccess;
   int lds = 0;
   for (int k = 0; k < 2; ++k)
-    lds = max2(lds, sq_enc_part_bytes(q.bits[k], q.ce[k]) + 8 * sq_span_ranges(q.te[k], q.ce[k]));
+    lds = max2(lds, 8 * sq_span_ranges(q.te[k], q.ce[k]));
   (void)hipFuncSetAttribute((const void*)k_sq_enc128, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   const dim3 grid((unsigned)((q.T + kSpan - 1) / kSpan), (unsigned)(q.L * 2 * q.H));
   k_sq_enc128<<<grid, 256, lds, s>>>(q);
