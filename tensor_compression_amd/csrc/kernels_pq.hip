@@ -116,6 +116,25 @@ __device__ __forceinline__ bool f32_round_unsure(double z) {
   return mid || (fabs(z) < 0x1p-125 && z != 0.0);
 }
 
+// c = (float)(y / rs), the fp64 quotient rounded to fp32, for 8 values:
+// from the product with irs = 1 / rs (within 2 fp64 units of the quotient),
+// with the division itself only where that product cannot decide the
+// rounding (behind a wave-level branch).
+__device__ __forceinline__ void quot_f32(const double (&y)[8], double rs, double irs, float (&c)[8]) {
+  uint32_t unsure = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const double w = y[e] * irs;
+    c[e] = (float)w;
+    unsure |= f32_round_unsure(w) ? 1u << e : 0u;
+  }
+  if (__builtin_amdgcn_ballot_w64(unsure != 0)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (unsure & (1u << e)) c[e] = (float)__ddiv_rn(y[e], rs);
+  }
+}
+
 // y = WHT(x / r) of 16 tokens at a time: lane q = lane % 16 of a 16-lane
 // group holds channels 8 q .. 8 q + 7.  Returns r.  Each x / r (an fp32
 // quotient) and each y / sqrt(D) (an fp64 quotient, then fp32) is first
@@ -151,19 +170,7 @@ __device__ __forceinline__ float rms_wht(const float (&x)[8], int q, float (&c)[
   for (int e = 0; e < 8; ++e) y[e] = rt == 0.0f ? 0.0 : (double)xn[e];
   wht_fp64(y, q);
   const double rs = __dsqrt_rn((double)D);
-  const double irs = __ddiv_rn(1.0, rs);
-  unsure = 0;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const double w = y[e] * irs;
-    c[e] = (float)w;
-    unsure |= f32_round_unsure(w) ? 1u << e : 0u;
-  }
-  if (__builtin_amdgcn_ballot_w64(unsure != 0)) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (unsure & (1u << e)) c[e] = (float)__ddiv_rn(y[e], rs);
-  }
+  quot_f32(y, rs, __ddiv_rn(1.0, rs), c);
   return rt;
 }
 
@@ -744,7 +751,7 @@ __global__ __launch_bounds__(256) void k_pq_dec(const PqParams q) {
   __syncthreads();
   // inverse transform (the orthonormal WHT is its own inverse), times r
   const int q16 = lane & 15, grp = tid >> 4;
-  const double rs = __dsqrt_rn((double)D);
+  const double rs = __dsqrt_rn((double)D), irs = __ddiv_rn(1.0, rs);
   for (int pass = 0; pass < 4; ++pass) {
     const int tok = pass * 16 + grp;
     double y[8];
@@ -755,8 +762,9 @@ __global__ __launch_bounds__(256) void k_pq_dec(const PqParams q) {
     if (tok >= n) continue;
     const float rt = q.rms[(int64_t)sec * q.T + t0 + tok];
     float o[8];
+    quot_f32(y, rs, irs, o);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = __fmul_rn((float)__ddiv_rn(y[e], rs), rt);
+    for (int e = 0; e < 8; ++e) o[e] = __fmul_rn(o[e], rt);
     const int64_t row = ((int64_t)sec * q.T + t0 + tok) * D + 8 * q16;
     if (q.out_dtype == KVTC_FP32) {
       float* dst = reinterpret_cast<float*>(q.v_out) + row;
