@@ -293,26 +293,12 @@ __global__ __launch_bounds__(256) void k_dec_wht(const Params p) {
         double y[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = (double)c[e];
-#pragma unroll
-        for (int st = 1; st < 8; st <<= 1)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (!(e & st)) {
-              double a = y[e], bb = y[e + st];
-              y[e] = a + bb;
-              y[e + st] = a - bb;
-            }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            double other = __shfl_xor(y[e], o, 16);
-            y[e] = (q & o) ? other - y[e] : y[e] + other;
-          }
+        wht_fp64(y, q);  // channel strides 1, 2, 4 in the lane, then 8 .. 64 across the row
         const double rs = __dsqrt_rn((double)D);
         const float rt = rarea[r_index * p.T_mid + t0 + tok];
+        quot_f32(y, rs, __ddiv_rn(1.0, rs), x);  // y / sqrt(D), exactly rounded
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = __fmul_rn((float)__ddiv_rn(y[e], rs), rt);
+        for (int e = 0; e < 8; ++e) x[e] = __fmul_rn(x[e], rt);
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = c[e];

@@ -642,37 +642,23 @@ __global__ __launch_bounds__(256) void k_enc_wht(const Params p, int sec0, float
       }
       float c[8];
       if (transform) {
+        static_assert((D & (D - 1)) == 0, "sum / D is a power-of-two scaling");
         double ss = 0.0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss = __fma_rn((double)x[e], (double)x[e], ss);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o, 16);
-        const float rt = (float)__dsqrt_rn(__ddiv_rn(ss, (double)D));
+        ss += xor16<1>(ss);
+        ss += xor16<2>(ss);
+        ss += xor16<4>(ss);
+        ss += xor16<8>(ss);
+        const float rt = (float)__dsqrt_rn(ss * (1.0 / D));
         double y[8];
+        float xn[8];
+        div_f32(x, rt, xn);  // x / r, exactly rounded
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = rt == 0.0f ? 0.0 : (double)__fdiv_rn(x[e], rt);
-        // in-lane stages (channel strides 1, 2, 4)
-#pragma unroll
-        for (int st = 1; st < 8; st <<= 1)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (!(e & st)) {
-              double a = y[e], b = y[e + st];
-              y[e] = a + b;
-              y[e + st] = a - b;
-            }
-        // cross-lane stages (channel strides 8, 16, 32, 64)
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            double other = __shfl_xor(y[e], o, 16);
-            y[e] = (q & o) ? other - y[e] : y[e] + other;
-          }
-        }
+        for (int e = 0; e < 8; ++e) y[e] = rt == 0.0f ? 0.0 : (double)xn[e];
+        wht_fp64(y, q);  // channel strides 1, 2, 4 in the lane, then 8 .. 64 across the row
         const double rs = __dsqrt_rn((double)D);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) c[e] = (float)__ddiv_rn(y[e], rs);
+        quot_f32(y, rs, __ddiv_rn(1.0, rs), c);  // y / sqrt(D), exactly rounded
         if (q == 0) {
           if (MODE == 0) reinterpret_cast<float*>(p.out + p.r_off)[r_index * p.T_mid + t0 + tok] = rt;
           if (MODE == 2 && r_out) r_out[(int64_t)(u - sec0) * p.T_mid + t0 + tok] = rt;

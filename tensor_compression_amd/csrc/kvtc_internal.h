@@ -599,4 +599,103 @@ __device__ inline void copy_raw_run(const Params& p, int run, int to_container, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// fp64 Walsh-Hadamard butterflies over 16-lane rows and exactly rounded
+// quotients (the RMS / Hadamard value paths)
+// ---------------------------------------------------------------------------
+
+// Lane i of every 16-lane row takes v from lane i ^ O, O = 1, 2, 4, 8:
+// DPP quad permutations for 1 and 2, a swizzle for 4, a row rotation for 8.
+template <int O>
+__device__ __forceinline__ uint32_t xor16_u32(uint32_t v) {
+  if constexpr (O == 1) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+  else if constexpr (O == 2) return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);
+  else if constexpr (O == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, (4 << 10) | 0x1F);
+  else return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);
+}
+template <int O>
+__device__ __forceinline__ double xor16(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = xor16_u32<O>((uint32_t)u), hi = xor16_u32<O>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)(lo | (hi << 32)));
+}
+
+// One fp64 butterfly stage across lanes: the lane with bit O of q set keeps
+// (partner - own), the other (own + partner); fma by +-1 rounds each once.
+template <int O>
+__device__ __forceinline__ void wht_lane_stage(double (&y)[8], int q) {
+  const double sg = (q & O) ? -1.0 : 1.0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = __fma_rn(sg, y[e], xor16<O>(y[e]));
+}
+
+// Butterflies over the 128 channels of a token (the orthonormal transform
+// without its 1 / sqrt(128)): bits 0-2 of the channel index in a lane's
+// registers, bits 3-6 across its 16-lane row (lane q holds channels
+// 8 q .. 8 q + 7).  Every sum is one fp64 rounding, stage by stage.
+__device__ __forceinline__ void wht_fp64(double (&y)[8], int q) {
+#pragma unroll
+  for (int st = 1; st < 8; st <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (!(e & st)) {
+        const double a = y[e], b = y[e + st];
+        y[e] = a + b;
+        y[e + st] = a - b;
+      }
+  wht_lane_stage<1>(y, q);
+  wht_lane_stage<2>(y, q);
+  wht_lane_stage<4>(y, q);
+  wht_lane_stage<8>(y, q);
+}
+
+// True when z (an fp64 value within 2 of its units in the last place of a
+// real number u) cannot be trusted to round to fp32 as u does: z lies within
+// 8 fp64 units of an fp32 rounding midpoint of its binade, or below the fp32
+// normal range, where that grid changes.  Zero is exact.
+__device__ __forceinline__ bool f32_round_unsure(double z) {
+  const uint32_t lo = (uint32_t)__double_as_longlong(z);
+  const bool mid = ((lo + 8u - 0x10000000u) & 0x1FFFFFFFu) <= 16u;
+  return mid || (fabs(z) < 0x1p-125 && z != 0.0);
+}
+
+// c = (float)(y / rs), the fp64 quotient rounded to fp32, for 8 values:
+// from the product with irs = 1 / rs (within 2 fp64 units of the quotient),
+// with the division itself only where that product cannot decide the
+// rounding (behind a wave-level branch).
+__device__ __forceinline__ void quot_f32(const double (&y)[8], double rs, double irs, float (&c)[8]) {
+  uint32_t unsure = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const double w = y[e] * irs;
+    c[e] = (float)w;
+    unsure |= f32_round_unsure(w) ? 1u << e : 0u;
+  }
+  if (__builtin_amdgcn_ballot_w64(unsure != 0)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (unsure & (1u << e)) c[e] = (float)__ddiv_rn(y[e], rs);
+  }
+}
+
+// xn = (float)(x / rt), the correctly rounded fp32 quotient, for 8 values:
+// from the fp64 product with 1 / rt (within 2 fp64 units of the quotient),
+// with the division itself only where that product cannot decide the
+// rounding (behind a wave-level branch).
+__device__ __forceinline__ void div_f32(const float (&x)[8], float rt, float (&xn)[8]) {
+  const double inv = __ddiv_rn(1.0, (double)rt);
+  uint32_t unsure = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const double z = (double)x[e] * inv;
+    xn[e] = (float)z;
+    unsure |= f32_round_unsure(z) ? 1u << e : 0u;
+  }
+  if (__builtin_amdgcn_ballot_w64(unsure != 0)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (unsure & (1u << e)) xn[e] = __fdiv_rn(x[e], rt);
+  }
+}
+
 }  // namespace kvtc
