@@ -212,13 +212,6 @@ __global__ __launch_bounds__(256) void k_sq_enc128(const SqParams q) {
   float2* const R = reinterpret_cast<float2*>(dyn);  // (zero, rcp) per range
 
   const uint16_t* bt = q.basis_t + basis_of(q, l, s, h) * D * D;
-  // B operands: component (2 wave + m) 16 + r, channels 32 kb + 8 g .. +7
-  uint4 bq[2][4];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      bq[m][kb] = *reinterpret_cast<const uint4*>(bt + (int64_t)((2 * wave + m) * 16 + r) * D + kb * 32 + 8 * g);
 
   // ---- stage: thread (token tid / 4, quarter tid % 4) holds channel runs
   // [16 q, 16 q + 16) and [64 + 16 q, +16): both members of every RoPE pair
@@ -253,6 +246,14 @@ __global__ __launch_bounds__(256) void k_sq_enc128(const SqParams q) {
   const int t0 = blockIdx.x * kSpan;
   const int n = min(kSpan, q.T - t0);
   load_rows(t0, n);
+  // B operands: component (2 wave + m) 16 + r, channels 32 kb + 8 g .. +7,
+  // requested after the rows so that waiting for the rows does not wait for them
+  uint4 bq[2][4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      bq[m][kb] = *reinterpret_cast<const uint4*>(bt + (int64_t)((2 * wave + m) * 16 + r) * D + kb * 32 + 8 * g);
   {
     const bool valid = st_t < n;
     float lo[16], hi[16];
@@ -452,13 +453,6 @@ __global__ __launch_bounds__(256) void k_sq_dec128(const SqParams q) {
   float2* const R = reinterpret_cast<float2*>(dyn + sq_dec_code_bytes(b));
 
   const uint16_t* bc = q.basis + basis_of(q, l, s, h) * D * D;
-  // A operands: channel 16 (wave + 4 nbi) + r, components 32 kb + 8 g .. +7
-  uint4 A[2][4];
-#pragma unroll
-  for (int nbi = 0; nbi < 2; ++nbi)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      A[nbi][kb] = *reinterpret_cast<const uint4*>(bc + (int64_t)(16 * (wave + 4 * nbi) + r) * D + kb * 32 + 8 * g);
 
   {
     const uint32_t* src = reinterpret_cast<const uint32_t*>(q.codes + sec_off(u, H, q.code_bytes[0], q.code_bytes[1]) +
@@ -469,6 +463,14 @@ __global__ __launch_bounds__(256) void k_sq_dec128(const SqParams q) {
                        (int64_t)(t0 >> lte) * ncg;
     for (int i = tid; i < nrv; i += 256) R[i] = rs[i];
   }
+  // A operands: channel 16 (wave + 4 nbi) + r, components 32 kb + 8 g .. +7,
+  // requested after the codes so that they arrive during the dequantisation
+  uint4 A[2][4];
+#pragma unroll
+  for (int nbi = 0; nbi < 2; ++nbi)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      A[nbi][kb] = *reinterpret_cast<const uint4*>(bc + (int64_t)(16 * (wave + 4 * nbi) + r) * D + kb * 32 + 8 * g);
   __syncthreads();
 
   // ---- dequantise: item = (token, component octet), lanes on consecutive tokens
