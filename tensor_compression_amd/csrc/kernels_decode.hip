@@ -731,6 +731,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_pca128(const Params p0) {
   __shared__ uint4 s_kw[D];          // sorted order: {b, row byte offset in the tile, scale, zero}
   __shared__ uint8_t s_rank[D];      // natural component -> sorted position
   __shared__ __attribute__((aligned(16))) float s_const[D];
+  __shared__ __attribute__((aligned(16))) float s_zr[D];  // bf16-rounded zero points, sorted order
   __shared__ uint32_t s_b[D];
   __shared__ int32_t s_misc[4];      // [1] corrupt flag, [2] full tile words
   // dynamic: [MFMA operands of the sub-tile: KBMAX x 4 KB][tile buffer][bf16
@@ -776,6 +777,8 @@ __global__ __launch_bounds__(256, 3) void k_dec_pca128(const Params p0) {
     const float* sc = reinterpret_cast<const float*>(rec + 5 * D);
     s_ki[r0] = DecKInfo{b0, (uint32_t)(2 * lane), sc[2 * lane], zr[2 * lane]};
     s_ki[r1] = DecKInfo{b1, (uint32_t)(2 * lane + 1), sc[2 * lane + 1], zr[2 * lane + 1]};
+    s_zr[r0] = round_bf16(zr[2 * lane]);
+    s_zr[r1] = round_bf16(zr[2 * lane + 1]);
     uint32_t fw = ((uint32_t)(p.tile_tokens * (int)b0 + 31) >> 5) + ((uint32_t)(p.tile_tokens * (int)b1 + 31) >> 5);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) fw += __shfl_xor(fw, o, 64);
@@ -821,15 +824,21 @@ __global__ __launch_bounds__(256, 3) void k_dec_pca128(const Params p0) {
   __syncthreads();
   if (tid >= 128) {
     // constant of the b = 0 components (sorted positions nnz .. D-1):
-    // sum_i B[j][i] bf16(zero_i), fp64 (four partial sums), one rounding
+    // sum_i B[j][i] bf16(zero_i), fp64 (four partial sums), one rounding;
+    // eight basis entries and zero points per step from 16-byte LDS reads
     const int j = tid - 128;
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int k = nnz; k < D; k += 4) {
+    for (int k8 = nnz & ~7; k8 < D; k8 += 8) {
+      const uint4 bw = *reinterpret_cast<const uint4*>(&bst[j * kBS + k8]);
+      const float4 z0 = *reinterpret_cast<const float4*>(&s_zr[k8]);
+      const float4 z1 = *reinterpret_cast<const float4*>(&s_zr[k8 + 4]);
+      const uint32_t bv[4] = {bw.x, bw.y, bw.z, bw.w};
+      const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int kk = min(k + e, D - 1);
-        const double t = (double)bf16_to_f32(bst[j * kBS + kk]) * (double)round_bf16(s_ki[kk].zero);
-        acc[e] += (k + e < D) ? t : 0.0;
+      for (int e = 0; e < 8; ++e) {
+        const float bf = __uint_as_float((e & 1) ? (bv[e >> 1] & 0xffff0000u) : (bv[e >> 1] << 16));
+        const double t = (double)bf * (double)zv[e];
+        acc[e & 3] += (k8 + e >= nnz) ? t : 0.0;
       }
     }
     s_const[j] = (float)((acc[0] + acc[1]) + (acc[2] + acc[3]));
