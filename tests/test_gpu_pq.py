@@ -76,6 +76,16 @@ def test_pq_short_and_ragged(T):
     _check(cfg, plan, pq, V, cb1, cb2)
 
 
+@pytest.mark.parametrize("T", [1, 2, 66, 130])
+def test_pq_span_takes_every_error(T):
+    """A last span of one or two tokens with a 256-outlier budget: its
+    n * 128 <= 256 errors are all candidates (no selection), and the block
+    merge keeps the 256 largest of its spans' candidates."""
+    pq = dict(PQ, outliers=256, block_tokens=128)
+    cfg, plan, V, cb1, cb2 = _setup(tokens=T, layers=1, seed=40 + T, trained=False, pq=pq)
+    _check(cfg, plan, pq, V, cb1, cb2)
+
+
 def test_pq_zero_cache_ties():
     """All-zero values: every distance to the zero centroids ties (the lowest
     index wins) and every error is zero (each block keeps its first
