@@ -858,7 +858,11 @@ __global__ __launch_bounds__(256, MODE == 0 ? 3 : 1) void k_enc128(const Params 
   const Params p = at_seq(p0, blockIdx.z);
   if (MODE == 0 && p0.n_seqs == 0 && !p.rope_keys && blockIdx.x == 0 && blockIdx.y == 0) clear_status_block(p);
   constexpr int D = 128;
-  const int u = blockIdx.y + sec0, ch = blockIdx.x;
+  // the statistics pass walks the sections backwards: the RoPE pass has just
+  // written the last layers' keys, and the quantiser, which walks forwards,
+  // then starts on the rows read last; both find more of them in the
+  // memory-side cache
+  const int u = (MODE == 0 ? (int)gridDim.y - 1 - (int)blockIdx.y : (int)blockIdx.y) + sec0, ch = blockIdx.x;
   const int h = u % p.H, s = (u / p.H) & 1, l = u / (2 * p.H);
   const int t0 = ch * p.blk_tokens;
   const int n = min(p.blk_tokens, p.T_mid - t0);
