@@ -742,7 +742,9 @@ __global__ __launch_bounds__(1024) void k_scan(const Params p0, HeaderBytes hdr)
 // the status word, as k_scan does.
 constexpr int kCopyWaves = 16;
 
-__global__ __launch_bounds__(64 * kCopyWaves) void k_copy_records(const Params p0, HeaderBytes hdr, int scan) {
+// at least 8 waves per SIMD (64 VGPRs): two 16-wave workgroups share a CU, so
+// the 512 records of a 32-layer, 8-head cache are copied in one round
+__global__ __launch_bounds__(64 * kCopyWaves, 8) void k_copy_records(const Params p0, HeaderBytes hdr, int scan) {
   const Params p = at_seq(p0, blockIdx.z);
   const int r = blockIdx.x;
   if (r >= p.n_recs) return;
