@@ -383,6 +383,11 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// Decoded rows are stored non-temporally (the cache policy's nt bit): nothing
+// in the codec reads them again, and streaming them past the caches keeps
+// the packed tiles that later workgroups read in the memory-side cache.
+constexpr int kNtStore = 2;
+
 // two fp32 values rounded to bf16 (nearest even) in one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
@@ -684,8 +689,8 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
             const int pp = hf + 2 * pq;
             const f32x4_t x0 = acc[2 * pq], x1 = acc[2 * pq + 1];
             const int c0 = 32 * pp + 8 * g;
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x0), orsrc, vo + 4 * c0, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x1), orsrc, vo + 4 * c0 + 16, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x0), orsrc, vo + 4 * c0, 0, kNtStore);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x1), orsrc, vo + 4 * c0 + 16, 0, kNtStore);
           }
         }
       }
@@ -704,10 +709,10 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
             const int64_t page = p.page_row[min(pos, p.T - 1) >> 4];
             uint8_t* rowp = valid ? obase + ((((page + (int64_t)l * p.pool_pages) * p.H + h) << 4) + (pos & 15)) * D * 2
                                   : dummy;
-            *reinterpret_cast<uint4*>(rowp + 16 * un) = v;
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t*>(rowp + 16 * un));
           } else {
             const int32_t vo = valid ? (int32_t)((int64_t)pos * D * 2) : slab_bytes;
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), orsrc, vo + 16 * un, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), orsrc, vo + 16 * un, 0, kNtStore);
           }
         }
       }
