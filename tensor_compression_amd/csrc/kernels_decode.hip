@@ -335,11 +335,11 @@ __global__ __launch_bounds__(256) void k_dec_wht(const Params p) {
         o.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
         o.z = (uint32_t)f32_to_bf16(x[4]) | ((uint32_t)f32_to_bf16(x[5]) << 16);
         o.w = (uint32_t)f32_to_bf16(x[6]) | ((uint32_t)f32_to_bf16(x[7]) << 16);
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(dst) + base) = o;
+        store_out16(reinterpret_cast<uint16_t*>(dst) + base, o);
       } else {
         float* d = reinterpret_cast<float*>(dst) + base;
-        *reinterpret_cast<float4*>(d) = make_float4(x[0], x[1], x[2], x[3]);
-        *reinterpret_cast<float4*>(d + 4) = make_float4(x[4], x[5], x[6], x[7]);
+        store_out16(d, make_float4(x[0], x[1], x[2], x[3]));
+        store_out16(d + 4, make_float4(x[4], x[5], x[6], x[7]));
       }
     }
   }
@@ -709,7 +709,7 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
             const int64_t page = p.page_row[min(pos, p.T - 1) >> 4];
             uint8_t* rowp = valid ? obase + ((((page + (int64_t)l * p.pool_pages) * p.H + h) << 4) + (pos & 15)) * D * 2
                                   : dummy;
-            __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), reinterpret_cast<u32x4_t*>(rowp + 16 * un));
+            store_out16(rowp + 16 * un, v);
           } else {
             const int32_t vo = valid ? (int32_t)((int64_t)pos * D * 2) : slab_bytes;
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), orsrc, vo + 16 * un, 0, kNtStore);

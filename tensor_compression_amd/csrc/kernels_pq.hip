@@ -684,14 +684,14 @@ __global__ __launch_bounds__(256) void k_pq_dec(const PqParams q) {
     const int64_t row = ((int64_t)sec * q.T + t0 + tok) * D + 8 * q16;
     if (q.out_dtype == KVTC_FP32) {
       float* dst = reinterpret_cast<float*>(q.v_out) + row;
-      reinterpret_cast<float4*>(dst)[0] = make_float4(o[0], o[1], o[2], o[3]);
-      reinterpret_cast<float4*>(dst)[1] = make_float4(o[4], o[5], o[6], o[7]);
+      store_out16(dst, make_float4(o[0], o[1], o[2], o[3]));
+      store_out16(dst + 4, make_float4(o[4], o[5], o[6], o[7]));
     } else {
       uint32_t h[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) h[e] = (uint32_t)f32_to_bf16(o[e]);
-      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(q.v_out) + row) =
-          make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16));
+      store_out16(reinterpret_cast<uint16_t*>(q.v_out) + row,
+                  make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)));
     }
   }
 }

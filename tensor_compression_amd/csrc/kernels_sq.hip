@@ -560,7 +560,7 @@ __global__ __launch_bounds__(256) void k_sq_dec128(const SqParams q) {
     float* o = reinterpret_cast<float*>(out) + (((int64_t)l * H + h) * q.T + t0) * D;
     for (int it = tid; it < n * 32; it += 256) {
       const int t = it >> 5, un = it & 31;
-      *reinterpret_cast<float4*>(o + (int64_t)t * D + 4 * un) = *reinterpret_cast<const float4*>(&OS[t * kCS + 4 * un]);
+      store_out16(o + (int64_t)t * D + 4 * un, *reinterpret_cast<const float4*>(&OS[t * kCS + 4 * un]));
     }
   } else {
     uint16_t* o = reinterpret_cast<uint16_t*>(out) + (((int64_t)l * H + h) * q.T + t0) * D;
@@ -568,8 +568,7 @@ __global__ __launch_bounds__(256) void k_sq_dec128(const SqParams q) {
       const int t = it >> 4, un = it & 15;
       const float4 a = *reinterpret_cast<const float4*>(&OS[t * kCS + 8 * un]);
       const float4 c = *reinterpret_cast<const float4*>(&OS[t * kCS + 8 * un + 4]);
-      *reinterpret_cast<uint4*>(o + (int64_t)t * D + 8 * un) =
-          make_uint4(pk2(a.x, a.y), pk2(a.z, a.w), pk2(c.x, c.y), pk2(c.z, c.w));
+      store_out16(o + (int64_t)t * D + 8 * un, make_uint4(pk2(a.x, a.y), pk2(a.z, a.w), pk2(c.x, c.y), pk2(c.z, c.w)));
     }
   }
 }

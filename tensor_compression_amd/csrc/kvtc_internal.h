@@ -436,6 +436,15 @@ __device__ inline uint16_t f32_to_bf16(float f) {
 
 __device__ inline float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 
+// A decoder's output rows: 16 bytes stored with the non-temporal cache policy
+// (nothing in the codec reads them again, and they then do not fill the
+// caches with dirty lines that the next launch would have to write back)
+typedef uint32_t u32x4_out __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_out16(void* dst, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4_out, v), reinterpret_cast<u32x4_out*>(dst));
+}
+__device__ __forceinline__ void store_out16(void* dst, float4 v) { store_out16(dst, __builtin_bit_cast(uint4, v)); }
+
 // ---- integrity checksum ("Quantum-Aware Tensor Compression", QATC
 // transport: an aggregate checksum; damaged payloads are refused before
 // restore).  Over the little-endian 32-bit words w_j of a range:
