@@ -396,6 +396,40 @@ def test_llama3_8b_full_size_sampled():
 
 
 @pytest.mark.timeout(900)
+def test_llama3_8b_full_size_every_section_decoded():
+    """The full Llama-3-8B-shaped cache in the benchmark's launch configuration:
+    every one of its 512 sections, decoded on the GPU, is within the decode
+    bound of the oracle's decode of the same container, and the raw windows
+    come back bit-exactly."""
+    w = synth.WORKLOADS["llama3_8b"]
+    K, V = synth.generate(w, device="cuda")
+    T = K.shape[2]
+    cfg = synth.oracle_config(w)
+    lo = orc.layout(cfg, T)
+    basis_t = fit_pca_basis(K, V, cfg, lo.mid_begin, lo.mid_end)
+    basis = basis_t.cpu().numpy()
+    plan = kvtc.Plan(cfg, basis_t, max_tokens=T)
+    data_t, st = plan.encode(K, V, plan.workspace(T))
+    assert st == kvtc.OK, kvtc.STATUS[st]
+    data = data_t.cpu().numpy().tobytes()
+    kd, vd, st = plan.decode(data_t, T, kvtc.FP32)
+    assert st == kvtc.OK, kvtc.STATUS[st]
+    kd, vd = kd.cpu().numpy(), vd.cpu().numpy()
+    k, v = synth.to_numpy_bits(K), synth.to_numpy_bits(V)
+    del K, V, data_t
+    ref = orc.decode_sections(cfg, data, basis, 0, lo.n_sections, lo.T_mid)
+    L, H = w.layers, w.kv_heads
+    for l in range(L):
+        for s, (src, dec) in enumerate(((k, kd), (v, vd))):
+            srcf = orc.bf16_bits_to_f32(src[l]).reshape(src.shape[1:])  # [H, T, D]
+            rms = np.sqrt((srcf.astype(np.float64) ** 2).mean(axis=1))  # [H, D]
+            for h in range(H):
+                u = (l * 2 + s) * H + h
+                parity.compare_decode(dec[l, h, lo.mid_begin: lo.mid_end], ref[u], rms[h][None, :])
+            assert np.array_equal(srcf[:, : lo.s0], dec[l, :, : lo.s0])
+            assert np.array_equal(srcf[:, lo.mid_end:], dec[l, :, lo.mid_end:])
+
+
 def test_qwen3_32b_full_size_sampled():
     """64 layers x 8 heads x 32768 tokens bf16 at 2 bits/comp (the 8.6 GB
     cache); first, last and layer-boundary sections plus random ones."""
