@@ -844,6 +844,12 @@ def main():
                            "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                            "frac": ach / HBM_PEAK_GBPS, "traffic": traffic_from_profile(dom),
                            "algorithmic_bytes": alg[dom], "avg_ms": ph_ms[dom]}
+        # the same measure for every phase with a defined minimum traffic
+        res["phase_roofline"] = {
+            k: {"algorithmic_bytes": alg[k], "avg_ms": ph_ms[k],
+                "frac": alg[k] / (ph_ms[k] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                "traffic": traffic_from_profile(k)}
+            for k in alg if k in ph_ms}
     if cfg["transform"] == 0 and ph_ms:
         # the projections are the path's dense contractions: 2 D flops per
         # coefficient (bf16 MFMA, fp32 accumulation) in the statistics pass,
