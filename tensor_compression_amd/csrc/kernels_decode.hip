@@ -387,6 +387,9 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // in the codec reads them again, and streaming them past the caches keeps
 // the packed tiles that later workgroups read in the memory-side cache.
 constexpr int kNtStore = 2;
+// The packed tiles are read here for the last time: their direct-to-LDS
+// loads carry the same policy.
+constexpr int kNtLoad = 2;
 
 // two fp32 values rounded to bf16 (nearest even) in one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
@@ -612,7 +615,7 @@ __device__ __forceinline__ void dec_chunk128(const Params& p, int u, int ch, con
             if (c * 64 + (uint32_t)lane < n4n)
               __builtin_amdgcn_global_load_lds(
                   (const void __attribute__((address_space(1)))*)(nsrc + 4 * (c * 64 + lane)),
-                  (void __attribute__((address_space(3)))*)(tbn + 256 * c), 16, 0, 0);
+                  (void __attribute__((address_space(3)))*)(tbn + 256 * c), 16, 0, kNtLoad);
           pf = true;
         }
       }
@@ -807,7 +810,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_pca128(const Params p0) {
       for (uint32_t c = (uint32_t)wave; c * 64 < n4; c += 4)
         if (c * 64 + (uint32_t)lane < n4)
           __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(slot0 + 4 * (c * 64 + lane)),
-                                           (void __attribute__((address_space(3)))*)(tb2 + 256 * c), 16, 0, 0);
+                                           (void __attribute__((address_space(3)))*)(tb2 + 256 * c), 16, 0, kNtLoad);
       pf0 = true;
     }
   }
